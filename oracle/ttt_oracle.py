@@ -1,0 +1,179 @@
+"""CPU oracle for the In-Place TTT fast-weight gated-MLP prefill.
+
+TEST INFRASTRUCTURE ONLY. This is a plain, slow, float64 NumPy statement of
+what the layer computes. Only the test suite, the package's smoke check and
+the benchmark's CPU-baseline leg may import or call it; the HIP library never
+does, and shares no code with it.
+
+Sources (page title, then section / equation):
+  [notes]  "论文精读：In-Place Test-Time Training" reading notes (jindou-blog):
+           "In-Place 设计" gated-MLP equation; "Chunk-Wise 更新机制" update
+           equation; "LM-Aligned 目标函数" target equation.
+  [forum]  "In-Place TTT: ByteDance Seed's Test-Time Training Framework Gives
+           LLMs On-the-Fly Memory" (zhichai): "Three Core Designs" 1-3.
+  [iplex]  iplexlaw explainer of "In-Place Test-Time Training": §2 (W_down as
+           fast weight), §3 (apply, then update), §4 (LM-aligned target),
+           §6 (prefix scan, chunk-boundary padding, document reset).
+
+Readings where the pages leave a step open (each is a choice, stated here and
+tested by the pins in tests/test_oracle.py):
+  * phi is SiLU, x * sigmoid(x).
+  * Tap k of the depthwise conv reads X0[t + k]; so taps [0, 1, 0, ...] with
+    W_target = I give the next token's embedding ([forum] design 3). Rows past
+    the end of the sequence are zero ("sequence" padding). The [iplex] §6
+    remark that the conv must not pull information across chunk boundaries
+    is the optional "chunk" padding: reads stop at the end of the token's own
+    chunk.
+  * V = conv(X0) @ W_target, W_target[i, j] maps input channel i to output
+    channel j (right multiplication, no transpose).
+  * W_down is [d, f]; the output is O = Z W_down^T and the update is
+    W += eta * V_i^T Z_i, with no 1/C factor and no clipping.
+  * Each sequence of the batch has its own state, starting from W_down0.
+  * A last chunk shorter than C is allowed. The returned final state includes
+    the last chunk's update.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["silu", "gated_activation", "conv_target_input", "lm_target",
+           "ttt_prefill", "activation_rows", "target_rows",
+           "final_state_entries"]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """phi(x) = x * sigmoid(x) = x / (1 + exp(-x))."""
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def gated_activation(H, Wg, Wu) -> np.ndarray:
+    """Z = phi(H Wg^T) * (H Wu^T), elementwise product.
+
+    [notes] "In-Place 设计": the gated MLP's intermediate activation, the part
+    of O = (phi(H W_gate^T) . (H W_up^T)) W_down^T that stays frozen; [iplex] §2.
+    H [T, d], Wg and Wu [f, d] -> Z [T, f].
+    """
+    H, Wg, Wu = _f64(H), _f64(Wg), _f64(Wu)
+    return silu(H @ Wg.T) * (H @ Wu.T)
+
+
+def conv_target_input(X0, taps, pad="sequence", chunk=None, n_out=None):
+    """Depthwise conv of the token embeddings, the Conv1D(X0) of the target.
+
+    [notes] "LM-Aligned 目标函数" target equation; [iplex] §4, §6 (depthwise).
+    Y[t, c] = sum_k taps[k, c] * X0[t + k, c], where the read X0[t + k]
+    counts only if t + k is inside the sequence (pad="sequence") or inside
+    t's own chunk of `chunk` tokens (pad="chunk"). X0 may carry extra
+    look-ahead rows past the n_out outputs wanted.
+    """
+    X0, taps = _f64(X0), _f64(taps)
+    T_in, d = X0.shape
+    T = T_in if n_out is None else n_out
+    K = taps.shape[0]
+    Y = np.zeros((T, d))
+    for k in range(K):
+        if pad == "sequence":
+            # output t reads row t + k while t + k < T_in
+            hi = min(T, T_in - k)
+            if hi > 0:
+                Y[:hi] += taps[k] * X0[k:hi + k]
+        elif pad == "chunk":
+            # output t in chunk [a, a + chunk) reads row t + k while it is in
+            # that chunk (and inside X0)
+            for a in range(0, T, chunk):
+                hi = min(a + chunk, T, min(a + chunk, T_in) - k)
+                if hi > a:
+                    Y[a:hi] += taps[k] * X0[a + k:hi + k]
+        else:
+            raise ValueError(pad)
+    return Y
+
+
+def lm_target(X0, taps, W_target, pad="sequence", chunk=None, n_out=None):
+    """V = Conv1D(X0) W_target, the LM-aligned target ([notes] target
+    equation; [forum] design 3; [iplex] §4)."""
+    return conv_target_input(X0, taps, pad, chunk, n_out) @ _f64(W_target)
+
+
+def ttt_prefill(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
+                pad="sequence"):
+    """The layer's prefill: per-chunk apply, then update, over the sequence.
+
+    [notes] "Chunk-Wise 更新机制": the sequence is cut into non-overlapping
+    chunks; each chunk first produces its output with the current fast
+    weight, then the fast weight takes the step
+    W^(i+1) = W^(i) + eta * V_[i]^T Z_[i]. [iplex] §3: a chunk's output always
+    uses the state from before its own update. [iplex] §6: the state starts
+    at the pretrained W_down for each document (here: each batch row).
+
+    H [B, T, d]; X0 [B, T + L, d] (L >= 0 look-ahead rows, read by the conv
+    only); Wg, Wu [f, d]; W_down0 [d, f] shared, or [B, d, f] per sequence;
+    taps [K, d]; W_target [d, d]. Returns O [B, T, d] and the final state
+    W [B, d, f], float64.
+    """
+    H, X0, W_down0 = _f64(H), _f64(X0), _f64(W_down0)
+    B, T, d = H.shape
+    f = Wg.shape[0]
+    if X0.shape[0] != B or X0.shape[1] < T or X0.shape[2] != d:
+        raise ValueError("X0 must be [B, >=T, d]")
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    O = np.zeros((B, T, d))
+    W_final = np.zeros((B, d, f))
+    for b in range(B):
+        Z = gated_activation(H[b], Wg, Wu)                       # [T, f]
+        V = lm_target(X0[b], taps, W_target, pad, chunk, n_out=T)  # [T, d]
+        W = (W_down0[b] if W_down0.ndim == 3 else W_down0).copy()
+        for start in range(0, T, chunk):
+            rows = slice(start, min(start + chunk, T))
+            O[b, rows] = Z[rows] @ W.T                 # apply: pre-update state
+            W = W + eta * (V[rows].T @ Z[rows])        # then update
+        W_final[b] = W
+    return O, W_final
+
+
+# ---------------------------------------------------------------------------
+# Sampled forms, for checking outputs of sizes the full recurrence is too slow
+# for. Each is the same definition restricted to a few output elements.
+# ---------------------------------------------------------------------------
+
+def activation_rows(H_b, Wg, Wu, rows) -> np.ndarray:
+    """Z[rows] of one sequence (the gated activation is row-local)."""
+    return gated_activation(_f64(H_b)[rows], Wg, Wu)
+
+
+def target_rows(X0_b, taps, W_target, rows, pad="sequence", chunk=None):
+    """V[rows] of one sequence; each row reads X0 rows t..t+K-1 only."""
+    X0_b, taps = _f64(X0_b), _f64(taps)
+    T, d = X0_b.shape
+    K = taps.shape[0]
+    rows = np.asarray(rows)
+    Y = np.zeros((len(rows), d))
+    for i, t in enumerate(rows):
+        end = T if pad == "sequence" else min(T, (t // chunk + 1) * chunk)
+        for k in range(K):
+            if t + k < end:
+                Y[i] += taps[k] * X0_b[t + k]
+    return Y @ _f64(W_target)
+
+
+def final_state_entries(H_b, X0_b, Wg, Wu, W0_b, taps, W_target, eta, cs, js,
+                        pad="sequence", chunk=None) -> np.ndarray:
+    """Entries W_final[c, j] for c in cs, j in js of one sequence.
+
+    Summing the update equation over all chunks gives
+    W_final = W_down0 + eta * sum_i V_i^T Z_i = W_down0 + eta * V^T Z, since
+    the chunks partition the tokens; each entry needs only column j of Z and
+    column c of V over all tokens.
+    """
+    H_b, Wg, Wu = _f64(H_b), _f64(Wg), _f64(Wu)
+    cs, js = np.asarray(cs), np.asarray(js)
+    Zc = silu(H_b @ Wg[js].T) * (H_b @ Wu[js].T)                  # [T, |js|]
+    Y = conv_target_input(X0_b, taps, pad, chunk)                  # [T, d]
+    Vc = Y @ _f64(W_target)[:, cs]                                  # [T, |cs|]
+    return _f64(W0_b)[np.ix_(cs, js)] + eta * (Vc.T @ Zc)

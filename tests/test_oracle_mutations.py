@@ -1,0 +1,102 @@
+"""CPU-only: plant a plausible mistake in the oracle, rerun every pin, and
+check that at least one pin catches it. This is what shows the pins are
+strong enough to trust the oracle; every mutation lives here, on the CPU.
+"""
+import numpy as np
+import pytest
+
+import oracle.ttt_oracle as ora
+import oracle_pins
+
+_real_prefill = ora.ttt_prefill
+_real_target = ora.lm_target
+_real_conv = ora.conv_target_input
+
+
+def _prefill_variant(order="apply_first", scale=1.0, skip_last=False,
+                     shared_state=False, sign=1.0, chunk_extra=0):
+    """A copy of the recurrence with one knob turned away from the pages."""
+    def prefill(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
+                pad="sequence"):
+        H, X0, W_down0 = (np.asarray(a, np.float64) for a in (H, X0, W_down0))
+        B, T, d = H.shape
+        f = Wg.shape[0]
+        O = np.zeros((B, T, d))
+        Wf = np.zeros((B, d, f))
+        W = None
+        step = chunk + chunk_extra
+        for b in range(B):
+            Z = ora.gated_activation(H[b], Wg, Wu)
+            V = ora.lm_target(X0[b], taps, W_target, pad, chunk, n_out=T)
+            if W is None or not shared_state:
+                W = (W_down0[b] if W_down0.ndim == 3 else W_down0).copy()
+            starts = list(range(0, T, step))
+            for n, s in enumerate(starts):
+                r = slice(s, min(s + step, T))
+                upd = sign * eta * scale * (V[r].T @ Z[r])
+                if skip_last and n == len(starts) - 1:
+                    upd = 0.0
+                if order == "update_first":
+                    W = W + upd
+                    O[b, r] = Z[r] @ W.T
+                else:
+                    O[b, r] = Z[r] @ W.T
+                    W = W + upd
+            Wf[b] = W
+        return O, Wf
+    return prefill
+
+
+def _target_transposed(X0, taps, W_target, pad="sequence", chunk=None, n_out=None):
+    return _real_conv(X0, taps, pad, chunk, n_out) @ np.asarray(W_target, np.float64).T
+
+
+def _conv_backward(X0, taps, pad="sequence", chunk=None, n_out=None):
+    X0 = np.asarray(X0, np.float64)
+    return _real_conv(X0[::-1], taps, pad, chunk, n_out)[::-1].copy()
+
+
+def _conv_wraps(X0, taps, pad="sequence", chunk=None, n_out=None):
+    X0 = np.asarray(X0, np.float64)
+    T = X0.shape[0] if n_out is None else n_out
+    Y = np.zeros((T, X0.shape[1]))
+    for k in range(taps.shape[0]):
+        Y += np.asarray(taps[k], np.float64) * np.roll(X0, -k, axis=0)[:T]
+    return Y
+
+
+def _conv_ignores_chunk(X0, taps, pad="sequence", chunk=None, n_out=None):
+    return _real_conv(X0, taps, "sequence", chunk, n_out)
+
+
+MUTATIONS = {
+    "inclusive_prefix_leak": ("ttt_prefill", _prefill_variant(order="update_first")),
+    "skip_update": ("ttt_prefill", _prefill_variant(scale=0.0)),
+    "normalise_by_chunk": ("ttt_prefill", _prefill_variant(scale=1.0 / 8)),
+    "wrong_sign": ("ttt_prefill", _prefill_variant(sign=-1.0)),
+    "drop_last_update": ("ttt_prefill", _prefill_variant(skip_last=True)),
+    "state_shared_across_batch": ("ttt_prefill", _prefill_variant(shared_state=True)),
+    "chunk_off_by_one": ("ttt_prefill", _prefill_variant(chunk_extra=1)),
+    "w_target_transposed": ("lm_target", _target_transposed),
+    "conv_reads_backward": ("conv_target_input", _conv_backward),
+    "conv_wraps_around": ("conv_target_input", _conv_wraps),
+    "chunk_padding_ignored": ("conv_target_input", _conv_ignores_chunk),
+    "phi_is_sigmoid": ("silu", lambda x: 1.0 / (1.0 + np.exp(-x))),
+    "phi_is_identity": ("silu", lambda x: x),
+    "gate_up_swapped": ("gated_activation",
+                        lambda H, Wg, Wu: ora.silu(np.asarray(H, np.float64) @ np.asarray(Wu, np.float64).T)
+                        * (np.asarray(H, np.float64) @ np.asarray(Wg, np.float64).T)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(ora, attr, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutation {name} passed every pin"
