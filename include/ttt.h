@@ -1,0 +1,157 @@
+/*
+ * ttt.h - C ABI of the In-Place TTT fast-weight gated-MLP prefill for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (page citations name the page title and the section / equation):
+ *   Z   = SiLU(H Wg^T) * (H Wu^T)
+ *         "论文精读：In-Place Test-Time Training" reading notes, "In-Place 设计",
+ *         gated-MLP equation: W_gate and W_up are frozen, W_down is the fast
+ *         weight.
+ *   V   = Conv1D(X0) W_target, a depthwise conv whose tap k reads X0[t + k]
+ *         reading notes, "LM-Aligned 目标函数", target equation; zhichai
+ *         summary "In-Place TTT: ByteDance Seed's Test-Time Training Framework
+ *         Gives LLMs On-the-Fly Memory", "Three Core Designs" 3 (taps
+ *         [0, 1, 0, ...] with W_target = I give the next token's embedding).
+ *   for each chunk i of C tokens, in order:
+ *     O_i      = Z_i W^(i)^T                       (apply with the pre-update state)
+ *     W^(i+1)  = W^(i) + eta * V_i^T Z_i            (then update)
+ *         reading notes, "Chunk-Wise 更新机制", update equation; iplexlaw
+ *         explainer of In-Place Test-Time Training, §3 (apply, then update)
+ *         and §6 (the exclusive prefix scan over chunk deltas, and the state
+ *         starting from the pretrained W_down for every document).
+ *   W^(0) = W_down0 for every sequence of the batch; the call returns every
+ *   O and the final state W^(k) (after the last chunk's update).
+ *
+ * Layouts are row-major. Sizes: B batch, T tokens, d = d_model, f = d_ff,
+ * K conv taps, C chunk, k = ceil(T / C) chunks.
+ *
+ * Memory ownership: every pointer argument is device memory owned by the
+ * caller. The library never allocates or frees device memory in these calls;
+ * scratch space is the caller's workspace of ttt_workspace_size() bytes.
+ * Inputs are only read. Calls are asynchronous on the given HIP stream
+ * (a hipStream_t passed as void*, NULL = the default stream) and never
+ * synchronise the device; results are valid after the stream completes.
+ *
+ * Errors: every argument is checked on the host before anything is
+ * launched; on an error nothing is launched and no output is written.
+ * Launch failures return TTT_ERR_HIP. ttt_last_error() gives a
+ * human-readable reason for the most recent failure on the calling thread.
+ * NaN and Inf inputs are propagated, not checked. The library keeps no
+ * global state other than the optional per-launch timing record
+ * (ttt_profile_*), which is not thread-safe.
+ */
+#ifndef TTT_H_
+#define TTT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ttt_status {
+  TTT_OK = 0,
+  TTT_ERR_INVALID_ARG = -1, /* bad size, null or misaligned pointer, bad flag */
+  TTT_ERR_UNSUPPORTED = -2, /* valid for the method, not supported by the kernels */
+  TTT_ERR_WORKSPACE = -3,   /* workspace smaller than ttt_workspace_size() */
+  TTT_ERR_ALIAS = -4,       /* an output overlaps an input, the other output or the workspace */
+  TTT_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} ttt_status;
+
+typedef enum ttt_dtype { TTT_BF16 = 0, TTT_F32 = 1 } ttt_dtype;
+
+enum {
+  /* Chunk-local conv padding: the conv of a token reads no row past the end
+   * of the token's own chunk (iplexlaw explainer §6, chunk boundaries must
+   * not let the target pull future information from other chunks). Without
+   * the flag, rows past the end of the sequence read as zero. */
+  TTT_FLAG_PAD_CHUNK = 1u << 0,
+  /* Chunk schedule. Default (neither flag) is the materialised exclusive
+   * prefix: one update launch over the whole sequence writes a bf16 snapshot
+   * of W^(i) for every chunk, then one apply launch covers every chunk.
+   * RUNNING keeps one fp32 state and alternates apply / update per chunk. */
+  TTT_FLAG_SCHED_RUNNING = 1u << 1,
+  TTT_FLAG_SCHED_PREFIX = 1u << 2
+};
+
+typedef struct ttt_desc {
+  int32_t batch;       /* B >= 1 */
+  int32_t seq_len;     /* T >= 1 */
+  int32_t d_model;     /* d: multiple of 64 */
+  int32_t d_ff;        /* f: multiple of 64 */
+  int32_t conv_k;      /* K: 1 .. 64 */
+  int32_t act_dtype;   /* ttt_dtype of H, X0 and O */
+  int32_t weight_dtype;/* ttt_dtype of Wg, Wu, W_down0, taps, W_target */
+  int32_t reserved;    /* must be 0 */
+  int64_t w0_batch_stride; /* elements between sequences' W_down0; 0 = one shared [d, f] */
+  uint32_t flags;      /* TTT_FLAG_* */
+  uint32_t reserved2;  /* must be 0 */
+} ttt_desc;
+
+/* Workspace bytes ttt_layer_forward needs for this descriptor and chunk.
+ * Host only. Returns TTT_OK and writes *bytes, or an error for an invalid
+ * descriptor. */
+ttt_status ttt_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes);
+
+/* The layer's prefill.
+ *   H         [B, T, d]  act_dtype   hidden states entering the MLP
+ *   X0        [B, T, d]  act_dtype   token embeddings
+ *   Wg, Wu    [f, d]     weight_dtype frozen gate / up projections
+ *   W_down0   [d, f]     weight_dtype (one per sequence at w0_batch_stride)
+ *   conv_taps [K, d]     weight_dtype depthwise taps, tap k reads X0[t + k]
+ *   W_target  [d, d]     weight_dtype row = input channel, V = conv(X0) W_target
+ *   eta                  update step, finite
+ *   chunk                C: a multiple of 64, >= 64
+ *   O         [B, T, d]  act_dtype   out
+ *   W_down_final [B, d, f] float32   out, the state after the last chunk
+ *   workspace            >= ttt_workspace_size() bytes, 256-byte aligned
+ * Every pointer must be 16-byte aligned. Arithmetic: bf16 operands with
+ * fp32 accumulation; Z and V are stored in bf16, the state in fp32, and the
+ * apply reads a bf16 copy of each chunk's state. */
+ttt_status ttt_layer_forward(const ttt_desc* desc,
+                             const void* H, const void* X0,
+                             const void* Wg, const void* Wu,
+                             const void* W_down0, const void* conv_taps,
+                             const void* W_target, float eta, int32_t chunk,
+                             void* O, float* W_down_final,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Step entry points: one step of the layer each, for per-step checks.
+ * ttt_gated_activation writes Z [B, T, d_ff] in bf16.
+ * ttt_lm_target writes V [B, T, d_model] in bf16 (unscaled, eta not applied).
+ * Workspace sizes come from ttt_step_workspace_size(). Same conventions as
+ * ttt_layer_forward. */
+ttt_status ttt_step_workspace_size(const ttt_desc* desc, size_t* bytes);
+ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H,
+                                const void* Wg, const void* Wu, void* Z,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0,
+                         const void* conv_taps, const void* W_target, int32_t chunk,
+                         void* V, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+const char* ttt_status_string(int32_t status);
+const char* ttt_last_error(void);
+
+/* Optional per-launch timing. While enabled, every kernel the library
+ * launches is bracketed by HIP events on its stream. ttt_profile_read()
+ * synchronises those events and reports, per kernel name, the number of
+ * launches and the summed device time, writing at most max_entries of them
+ * to `out`, and returns the number of distinct kernel names; the record is
+ * then cleared. Not thread-safe. */
+typedef struct ttt_kernel_stat {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} ttt_kernel_stat;
+
+ttt_status ttt_profile_enable(int32_t on); /* on: clears the record */
+int32_t ttt_profile_read(ttt_kernel_stat* out, int32_t max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_H_ */

@@ -1,0 +1,26 @@
+"""In-Place TTT fast-weight gated-MLP prefill on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libttt_layer.so, whose C ABI is include/ttt.h.
+PyTorch supplies device memory and the stream; every step of the layer runs
+in the library's HIP kernels. There is no fallback: if the library is not
+built, or a call fails, an exception is raised.
+
+    O, W_final = layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target,
+                               eta, chunk)
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH,
+    TTTError,
+    gated_activation,
+    layer_forward,
+    lib,
+    lm_target,
+    make_desc,
+    profile_enable,
+    profile_read,
+    workspace_size,
+)
+
+__all__ = ["layer_forward", "gated_activation", "lm_target", "workspace_size",
+           "make_desc", "profile_enable", "profile_read", "TTTError", "lib",
+           "LIB_PATH"]

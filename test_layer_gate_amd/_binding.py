@@ -1,0 +1,228 @@
+"""ctypes marshalling for libttt_layer.so (C ABI: include/ttt.h).
+
+Only argument checking and marshalling live here: tensors are passed to the
+library as raw device pointers, together with torch's current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libttt_layer.so")
+
+TTT_BF16, TTT_F32 = 0, 1
+FLAG_PAD_CHUNK = 1 << 0
+FLAG_SCHED_RUNNING = 1 << 1
+FLAG_SCHED_PREFIX = 1 << 2
+
+
+class TTTError(RuntimeError):
+    """A non-OK status from libttt_layer, with its name and message."""
+
+    def __init__(self, status: int, name: str, message: str):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("conv_k", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("weight_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("w0_batch_stride", ctypes.c_int64), ("flags", ctypes.c_uint32),
+                ("reserved2", ctypes.c_uint32)]
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_S = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libttt_layer.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m test_layer_gate_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    DP = ctypes.POINTER(Desc)
+    L.ttt_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
+    L.ttt_step_workspace_size.argtypes = [DP, ctypes.POINTER(_S)]
+    L.ttt_layer_forward.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                    ctypes.c_int32, _P, _P, _P, _S, _P]
+    L.ttt_gated_activation.argtypes = [DP, _P, _P, _P, _P, _P, _S, _P]
+    L.ttt_lm_target.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _S, _P]
+    for fn in ("ttt_workspace_size", "ttt_step_workspace_size", "ttt_layer_forward",
+               "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
+        getattr(L, fn).restype = ctypes.c_int
+    L.ttt_status_string.argtypes = [ctypes.c_int32]
+    L.ttt_status_string.restype = ctypes.c_char_p
+    L.ttt_last_error.argtypes = []
+    L.ttt_last_error.restype = ctypes.c_char_p
+    L.ttt_profile_enable.argtypes = [ctypes.c_int32]
+    L.ttt_profile_read.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int32]
+    L.ttt_profile_read.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise TTTError(status, L.ttt_status_string(status).decode(),
+                       L.ttt_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype == torch.bfloat16:
+        return TTT_BF16
+    if t.dtype == torch.float32:
+        return TTT_F32
+    raise TypeError(f"{what} must be bfloat16 or float32, got {t.dtype}")
+
+
+def make_desc(batch, seq_len, d_model, d_ff, conv_k, act_dtype=TTT_BF16,
+              weight_dtype=TTT_BF16, w0_batch_stride=0, flags=0) -> Desc:
+    return Desc(batch, seq_len, d_model, d_ff, conv_k, act_dtype, weight_dtype, 0,
+                w0_batch_stride, flags, 0)
+
+
+def _flags(schedule, pad):
+    fl = 0
+    if pad == "chunk":
+        fl |= FLAG_PAD_CHUNK
+    elif pad != "sequence":
+        raise ValueError(f"pad must be 'sequence' or 'chunk', got {pad!r}")
+    if schedule == "running":
+        fl |= FLAG_SCHED_RUNNING
+    elif schedule == "prefix":
+        fl |= FLAG_SCHED_PREFIX
+    elif schedule is not None:
+        raise ValueError(f"schedule must be None, 'prefix' or 'running', got {schedule!r}")
+    return fl
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def workspace_size(desc: Desc, chunk: int) -> int:
+    n = _S(0)
+    _check(lib().ttt_workspace_size(ctypes.byref(desc), chunk, ctypes.byref(n)))
+    return n.value
+
+
+def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
+                  schedule=None, pad="sequence", out=None, W_down_final=None,
+                  workspace=None, stream=None):
+    """O, W_final for H, X0 [B, T, d]; Wg, Wu [f, d]; W_down0 [d, f] or
+    [B, d, f]; conv_taps [K, d]; W_target [d, d] (see include/ttt.h).
+
+    schedule: None (library default), "prefix" or "running". pad:
+    "sequence" (conv reads zero past the sequence end) or "chunk".
+    """
+    _require_cuda(H, X0, Wg, Wu, W_down0, conv_taps, W_target)
+    if H.dim() != 3 or X0.shape != H.shape:
+        raise ValueError("H and X0 must both be [B, T, d]")
+    B, T, d = H.shape
+    f = Wg.shape[0]
+    K = conv_taps.shape[0]
+    if Wg.shape != (f, d) or Wu.shape != (f, d):
+        raise ValueError("Wg and Wu must be [d_ff, d_model]")
+    if W_down0.shape not in ((d, f), (B, d, f)):
+        raise ValueError("W_down0 must be [d_model, d_ff] or [B, d_model, d_ff]")
+    if conv_taps.shape != (K, d) or W_target.shape != (d, d):
+        raise ValueError("conv_taps must be [K, d_model] and W_target [d_model, d_model]")
+    act = _dtype_code(H, "H")
+    wt = _dtype_code(Wg, "Wg")
+    if X0.dtype != H.dtype:
+        raise TypeError("X0 must have H's dtype")
+    for t, n in ((Wu, "Wu"), (W_down0, "W_down0"), (conv_taps, "conv_taps"),
+                 (W_target, "W_target")):
+        if t.dtype != Wg.dtype:
+            raise TypeError(f"{n} must have Wg's dtype")
+    if not math.isfinite(float(eta)):
+        raise ValueError("eta must be finite")
+    stride = d * f if W_down0.dim() == 3 else 0
+    desc = make_desc(B, T, d, f, K, act, wt, stride, _flags(schedule, pad))
+    ws_bytes = workspace_size(desc, int(chunk))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
+    O = torch.empty_like(H) if out is None else out
+    Wf = (torch.empty((B, d, f), dtype=torch.float32, device=H.device)
+          if W_down_final is None else W_down_final)
+    _require_cuda(O, Wf, workspace)
+    _check(lib().ttt_layer_forward(
+        ctypes.byref(desc), _ptr(H), _ptr(X0), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
+        _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk),
+        _ptr(O), _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return O, Wf
+
+
+def _step_ws(desc, device):
+    n = _S(0)
+    _check(lib().ttt_step_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+
+
+def gated_activation(H, Wg, Wu, *, stream=None):
+    """Z = SiLU(H Wg^T) * (H Wu^T) in bf16, [B, T, d_ff]."""
+    _require_cuda(H, Wg, Wu)
+    B, T, d = H.shape
+    f = Wg.shape[0]
+    desc = make_desc(B, T, d, f, 1, _dtype_code(H, "H"), _dtype_code(Wg, "Wg"))
+    ws = _step_ws(desc, H.device)
+    Z = torch.empty((B, T, f), dtype=torch.bfloat16, device=H.device)
+    _check(lib().ttt_gated_activation(ctypes.byref(desc), _ptr(H), _ptr(Wg), _ptr(Wu),
+                                      _ptr(Z), _ptr(ws), ws.numel(), _stream(stream)))
+    return Z
+
+
+def lm_target(X0, conv_taps, W_target, *, chunk=64, pad="sequence", stream=None):
+    """V = conv(X0) W_target in bf16, [B, T, d_model]."""
+    _require_cuda(X0, conv_taps, W_target)
+    B, T, d = X0.shape
+    desc = make_desc(B, T, d, 64, conv_taps.shape[0], _dtype_code(X0, "X0"),
+                     _dtype_code(conv_taps, "conv_taps"), 0, _flags(None, pad))
+    ws = _step_ws(desc, X0.device)
+    V = torch.empty((B, T, d), dtype=torch.bfloat16, device=X0.device)
+    _check(lib().ttt_lm_target(ctypes.byref(desc), _ptr(X0), _ptr(conv_taps),
+                               _ptr(W_target), int(chunk), _ptr(V), _ptr(ws),
+                               ws.numel(), _stream(stream)))
+    return V
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(lib().ttt_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total ms)} for launches since profile_enable."""
+    cap = 64
+    arr = (KernelStat * cap)()
+    n = min(lib().ttt_profile_read(arr, cap), cap)
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}

@@ -1,0 +1,511 @@
+// C ABI of libttt_layer: argument checking, workspace layout, the chunk
+// schedule and optional per-launch timing. Declarations and the contract of
+// every entry point are in include/ttt.h.
+#include "ttt.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ttt_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ttt_status fail(ttt_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+constexpr uint32_t kKnownFlags =
+    TTT_FLAG_PAD_CHUNK | TTT_FLAG_SCHED_RUNNING | TTT_FLAG_SCHED_PREFIX;
+constexpr int kMaxTaps = 64;
+constexpr int64_t kMaxDim = 1 << 20;
+
+// ------------------------------------------------------------ timing
+
+struct TimingRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  bool on = false;
+  std::vector<TimingRecord> recs;
+  std::vector<hipEvent_t> pool;
+};
+Timing g_timing;
+
+hipEvent_t take_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_timing.on) return launch();
+  hipEvent_t a = take_event(), b = take_event();
+  if (a && b) hipEventRecord(a, s);
+  hipError_t e = launch();
+  if (a && b) {
+    hipEventRecord(b, s);
+    g_timing.recs.push_back({name, a, b});
+  }
+  return e;
+}
+
+// ------------------------------------------------------------ geometry
+
+struct Geo {
+  int64_t B, T, d, f, K, C, T_pad, nchunks;
+  bool act_f32, w_f32, pad_chunk, running;
+  int64_t w0_stride;  // elements
+  size_t act_bytes() const { return act_f32 ? 4 : 2; }
+  size_t w_bytes() const { return w_f32 ? 4 : 2; }
+};
+
+struct Layout {
+  size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgb = 0, wub = 0;
+  size_t total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout forward_layout(const Geo& g) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.y = take(g.B * g.T_pad * g.d * 2);
+  L.wtt = take(g.d * g.d * 2);
+  L.z = take(g.B * g.T * g.f * 2);
+  L.zt = take(g.B * g.f * g.T_pad * 2);
+  L.vt = take(g.B * g.d * g.T_pad * 2);
+  L.snap = take(g.running ? g.B * g.d * g.f * 2 : g.B * g.nchunks * g.d * g.f * 2);
+  if (g.act_f32) {
+    L.hb = take(g.B * g.T * g.d * 2);
+    L.x0b = take(g.B * g.T * g.d * 2);
+  }
+  if (g.w_f32) {
+    L.wgb = take(g.f * g.d * 2);
+    L.wub = take(g.f * g.d * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+// Step entry points: gated activation needs bf16 copies of fp32 inputs;
+// the target needs Y, WtT and a bf16 copy of fp32 X0.
+Layout step_layout(const Geo& g) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.y = take(g.B * g.T_pad * g.d * 2);
+  L.wtt = take(g.d * g.d * 2);
+  if (g.act_f32) {
+    L.hb = take(g.B * g.T * g.d * 2);
+    L.x0b = take(g.B * g.T * g.d * 2);
+  }
+  if (g.w_f32) {
+    L.wgb = take(g.f * g.d * 2);
+    L.wub = take(g.f * g.d * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+ttt_status check_desc(const ttt_desc* desc, Geo* g) {
+  if (desc == nullptr) return fail(TTT_ERR_INVALID_ARG, "desc is NULL");
+  const ttt_desc& D = *desc;
+  if (D.batch < 1) return fail(TTT_ERR_INVALID_ARG, "batch must be >= 1");
+  if (D.seq_len < 1) return fail(TTT_ERR_INVALID_ARG, "seq_len must be >= 1");
+  if (D.d_model < 1 || D.d_ff < 1)
+    return fail(TTT_ERR_INVALID_ARG, "d_model and d_ff must be >= 1");
+  if (D.conv_k < 1) return fail(TTT_ERR_INVALID_ARG, "conv_k must be >= 1");
+  if ((D.act_dtype != TTT_BF16 && D.act_dtype != TTT_F32) ||
+      (D.weight_dtype != TTT_BF16 && D.weight_dtype != TTT_F32))
+    return fail(TTT_ERR_INVALID_ARG, "act_dtype / weight_dtype must be TTT_BF16 or TTT_F32");
+  if (D.reserved != 0 || D.reserved2 != 0)
+    return fail(TTT_ERR_INVALID_ARG, "reserved fields must be 0");
+  if (D.flags & ~kKnownFlags) return fail(TTT_ERR_INVALID_ARG, "unknown flag bits");
+  if ((D.flags & TTT_FLAG_SCHED_RUNNING) && (D.flags & TTT_FLAG_SCHED_PREFIX))
+    return fail(TTT_ERR_INVALID_ARG, "at most one schedule flag");
+  if (D.d_model % 64 != 0 || D.d_ff % 64 != 0)
+    return fail(TTT_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
+  if (D.d_model > kMaxDim || D.d_ff > kMaxDim)
+    return fail(TTT_ERR_UNSUPPORTED, "d_model / d_ff above 2^20");
+  if (D.conv_k > kMaxTaps) return fail(TTT_ERR_UNSUPPORTED, "conv_k above 64");
+  const int64_t df = (int64_t)D.d_model * D.d_ff;
+  if (D.w0_batch_stride < 0) return fail(TTT_ERR_INVALID_ARG, "w0_batch_stride < 0");
+  if (D.w0_batch_stride != 0) {
+    if (D.w0_batch_stride < df)
+      return fail(TTT_ERR_INVALID_ARG, "w0_batch_stride must be 0 or >= d_model * d_ff");
+    const int64_t granule = D.weight_dtype == TTT_F32 ? 4 : 8;
+    if (D.w0_batch_stride % granule != 0)
+      return fail(TTT_ERR_INVALID_ARG, "w0_batch_stride must keep every W_down0 16-byte aligned");
+  }
+  const int64_t T_pad =
+      (D.seq_len + tttk::kTokenPad - 1) / tttk::kTokenPad * tttk::kTokenPad;
+  // Largest per-launch tile counts must fit a 32-bit grid.
+  if ((int64_t)D.batch * (T_pad / 256) * (D.d_ff / 64 + 1) >= (int64_t)1 << 31)
+    return fail(TTT_ERR_UNSUPPORTED, "problem too large for one launch");
+  g->B = D.batch;
+  g->T = D.seq_len;
+  g->d = D.d_model;
+  g->f = D.d_ff;
+  g->K = D.conv_k;
+  g->T_pad = T_pad;
+  g->act_f32 = D.act_dtype == TTT_F32;
+  g->w_f32 = D.weight_dtype == TTT_F32;
+  g->pad_chunk = (D.flags & TTT_FLAG_PAD_CHUNK) != 0;
+  g->running = (D.flags & TTT_FLAG_SCHED_RUNNING) != 0;
+  g->w0_stride = D.w0_batch_stride;
+  g->C = 0;
+  g->nchunks = 0;
+  return TTT_OK;
+}
+
+ttt_status check_chunk(int32_t chunk, Geo* g) {
+  if (chunk < 1) return fail(TTT_ERR_INVALID_ARG, "chunk must be >= 1");
+  if (chunk % 64 != 0) return fail(TTT_ERR_UNSUPPORTED, "chunk must be a multiple of 64");
+  g->C = chunk;
+  g->nchunks = (g->T + chunk - 1) / chunk;
+  return TTT_OK;
+}
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;
+};
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+ttt_status check_ptr(const void* p, const char* name, size_t align = 16) {
+  if (p == nullptr) return fail(TTT_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (reinterpret_cast<uintptr_t>(p) % align != 0)
+    return fail(TTT_ERR_INVALID_ARG,
+                std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return TTT_OK;
+}
+
+Range range_of(const char* name, const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {name, lo, lo + bytes};
+}
+
+ttt_status check_aliasing(const std::vector<Range>& inputs, const std::vector<Range>& outputs) {
+  for (size_t i = 0; i < outputs.size(); ++i) {
+    for (const Range& in : inputs)
+      if (overlaps(outputs[i], in))
+        return fail(TTT_ERR_ALIAS,
+                    std::string(outputs[i].name) + " overlaps input " + in.name);
+    for (size_t j = i + 1; j < outputs.size(); ++j)
+      if (overlaps(outputs[i], outputs[j]))
+        return fail(TTT_ERR_ALIAS,
+                    std::string(outputs[i].name) + " overlaps " + outputs[j].name);
+  }
+  return TTT_OK;
+}
+
+#define TTT_TRY(expr)                 \
+  do {                                \
+    ttt_status _s = (expr);           \
+    if (_s != TTT_OK) return _s;      \
+  } while (0)
+
+#define TTT_LAUNCH(name, stream, call)                                            \
+  do {                                                                            \
+    hipError_t _e = timed(name, stream, [&]() { return (call); });                \
+    if (_e != hipSuccess)                                                         \
+      return fail(TTT_ERR_HIP, std::string(name) + ": " + hipGetErrorString(_e)); \
+  } while (0)
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttt_status_string(int32_t s) {
+  switch (s) {
+    case TTT_OK: return "TTT_OK";
+    case TTT_ERR_INVALID_ARG: return "TTT_ERR_INVALID_ARG";
+    case TTT_ERR_UNSUPPORTED: return "TTT_ERR_UNSUPPORTED";
+    case TTT_ERR_WORKSPACE: return "TTT_ERR_WORKSPACE";
+    case TTT_ERR_ALIAS: return "TTT_ERR_ALIAS";
+    case TTT_ERR_HIP: return "TTT_ERR_HIP";
+    default: return "TTT_ERR_UNKNOWN";
+  }
+}
+
+const char* ttt_last_error(void) { return g_err.c_str(); }
+
+ttt_status ttt_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = forward_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_step_workspace_size(const ttt_desc* desc, size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = step_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0,
+                             const void* Wg, const void* Wu, const void* W_down0,
+                             const void* conv_taps, const void* W_target, float eta,
+                             int32_t chunk, void* O, float* W_down_final, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
+  TTT_TRY(check_ptr(H, "H"));
+  TTT_TRY(check_ptr(X0, "X0"));
+  TTT_TRY(check_ptr(Wg, "Wg"));
+  TTT_TRY(check_ptr(Wu, "Wu"));
+  TTT_TRY(check_ptr(W_down0, "W_down0"));
+  TTT_TRY(check_ptr(conv_taps, "conv_taps"));
+  TTT_TRY(check_ptr(W_target, "W_target"));
+  TTT_TRY(check_ptr(O, "O"));
+  TTT_TRY(check_ptr(W_down_final, "W_down_final"));
+  TTT_TRY(check_ptr(workspace, "workspace", 256));
+  const Layout L = forward_layout(g);
+  if (workspace_bytes < L.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                       " bytes, needs " + std::to_string(L.total));
+  const size_t ab = g.act_bytes(), wb = g.w_bytes();
+  const size_t w0_bytes =
+      g.w0_stride == 0 ? g.d * g.f * wb : ((g.B - 1) * g.w0_stride + g.d * g.f) * wb;
+  const std::vector<Range> inputs = {
+      range_of("H", H, g.B * g.T * g.d * ab),
+      range_of("X0", X0, g.B * g.T * g.d * ab),
+      range_of("Wg", Wg, g.f * g.d * wb),
+      range_of("Wu", Wu, g.f * g.d * wb),
+      range_of("W_down0", W_down0, w0_bytes),
+      range_of("conv_taps", conv_taps, g.K * g.d * wb),
+      range_of("W_target", W_target, g.d * g.d * wb)};
+  const std::vector<Range> outputs = {range_of("O", O, g.B * g.T * g.d * ab),
+                                      range_of("W_down_final", W_down_final, g.B * g.d * g.f * 4),
+                                      range_of("workspace", workspace, L.total)};
+  TTT_TRY(check_aliasing(inputs, outputs));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int B = (int)g.B, T = (int)g.T, T_pad = (int)g.T_pad, d = (int)g.d, f = (int)g.f;
+  const int64_t df = g.d * g.f;
+
+  // bf16 operands
+  const uint16_t* Hb = static_cast<const uint16_t*>(H);
+  const uint16_t* X0b = static_cast<const uint16_t*>(X0);
+  const uint16_t* Wgb = static_cast<const uint16_t*>(Wg);
+  const uint16_t* Wub = static_cast<const uint16_t*>(Wu);
+  if (g.act_f32) {
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(H),
+                                                      at<uint16_t>(workspace, L.hb), g.B * g.T * g.d, s));
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(X0),
+                                                      at<uint16_t>(workspace, L.x0b), g.B * g.T * g.d, s));
+    Hb = at<uint16_t>(workspace, L.hb);
+    X0b = at<uint16_t>(workspace, L.x0b);
+  }
+  if (g.w_f32) {
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(Wg),
+                                                      at<uint16_t>(workspace, L.wgb), g.f * g.d, s));
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(Wu),
+                                                      at<uint16_t>(workspace, L.wub), g.f * g.d, s));
+    Wgb = at<uint16_t>(workspace, L.wgb);
+    Wub = at<uint16_t>(workspace, L.wub);
+  }
+  uint16_t* Y = at<uint16_t>(workspace, L.y);
+  uint16_t* WtT = at<uint16_t>(workspace, L.wtt);
+  uint16_t* Z = at<uint16_t>(workspace, L.z);
+  uint16_t* ZT = at<uint16_t>(workspace, L.zt);
+  uint16_t* VT = at<uint16_t>(workspace, L.vt);
+  uint16_t* snap = at<uint16_t>(workspace, L.snap);
+
+  TTT_LAUNCH("transpose_w_target", s,
+             tttk::launch_transpose(W_target, g.w_f32, WtT, d, d, s));
+  TTT_LAUNCH("conv", s,
+             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, B, T, T_pad, d, (int)g.K,
+                               (int)g.C, g.pad_chunk, s));
+  TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgb, Wub, Z, ZT, B, T, T_pad, d, f, s));
+  TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, eta, B, T, T_pad, d, s));
+
+  const int steps_per_chunk = (int)(g.C / 64);
+  const int nk_total = (int)((g.T + 63) / 64);
+  if (!g.running) {
+    // Materialised exclusive prefix: snapshot i = bf16(W^(i)) for every chunk,
+    // W_down_final = W^(k); then every chunk's output in one launch.
+    TTT_LAUNCH("update_prefix", s,
+               tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, snap,
+                                   g.nchunks * df, W_down_final, nullptr, B, T_pad, d, f, 0,
+                                   nk_total, steps_per_chunk, s));
+    TTT_LAUNCH("apply", s,
+               tttk::launch_apply(Z, snap, g.nchunks * df, df, O, g.act_f32, B, T, d, f, 0, T,
+                                  (int)g.C, s));
+  } else {
+    // Running state: W_down_final holds W^(i) in fp32, `snap` its bf16 copy.
+    TTT_LAUNCH("update_running", s,
+               tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, nullptr, 0,
+                                   W_down_final, snap, B, T_pad, d, f, 0, 0, steps_per_chunk, s));
+    for (int64_t i = 0; i < g.nchunks; ++i) {
+      const int t0 = (int)(i * g.C), t1 = (int)std::min<int64_t>(g.T, (i + 1) * g.C);
+      TTT_LAUNCH("apply", s,
+                 tttk::launch_apply(Z, snap, df, 0, O, g.act_f32, B, T, d, f, t0, t1,
+                                    (int)g.C, s));
+      const int nk = (t1 - t0 + 63) / 64;
+      TTT_LAUNCH("update_running", s,
+                 tttk::launch_update(ZT, VT, W_down_final, true, df, nullptr, 0, W_down_final,
+                                     snap, B, T_pad, d, f, t0, nk, steps_per_chunk, s));
+    }
+  }
+  return TTT_OK;
+}
+
+ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void* Wg,
+                                const void* Wu, void* Z, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_ptr(H, "H"));
+  TTT_TRY(check_ptr(Wg, "Wg"));
+  TTT_TRY(check_ptr(Wu, "Wu"));
+  TTT_TRY(check_ptr(Z, "Z"));
+  const Layout L = step_layout(g);
+  if (L.total > 0) TTT_TRY(check_ptr(workspace, "workspace", 256));
+  if (workspace_bytes < L.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                       " bytes, needs " + std::to_string(L.total));
+  const size_t ab = g.act_bytes(), wb = g.w_bytes();
+  TTT_TRY(check_aliasing({range_of("H", H, g.B * g.T * g.d * ab),
+                          range_of("Wg", Wg, g.f * g.d * wb),
+                          range_of("Wu", Wu, g.f * g.d * wb)},
+                         {range_of("Z", Z, g.B * g.T * g.f * 2),
+                          range_of("workspace", workspace, L.total)}));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* Hb = static_cast<const uint16_t*>(H);
+  const uint16_t* Wgb = static_cast<const uint16_t*>(Wg);
+  const uint16_t* Wub = static_cast<const uint16_t*>(Wu);
+  if (g.act_f32) {
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(H),
+                                                      at<uint16_t>(workspace, L.hb), g.B * g.T * g.d, s));
+    Hb = at<uint16_t>(workspace, L.hb);
+  }
+  if (g.w_f32) {
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(Wg),
+                                                      at<uint16_t>(workspace, L.wgb), g.f * g.d, s));
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(Wu),
+                                                      at<uint16_t>(workspace, L.wub), g.f * g.d, s));
+    Wgb = at<uint16_t>(workspace, L.wgb);
+    Wub = at<uint16_t>(workspace, L.wub);
+  }
+  TTT_LAUNCH("gate_up", s,
+             tttk::launch_gate_up(Hb, Wgb, Wub, static_cast<uint16_t*>(Z), nullptr, (int)g.B,
+                                  (int)g.T, (int)g.T_pad, (int)g.d, (int)g.f, s));
+  return TTT_OK;
+}
+
+ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0, const void* conv_taps,
+                         const void* W_target, int32_t chunk, void* V, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  TTT_TRY(check_ptr(X0, "X0"));
+  TTT_TRY(check_ptr(conv_taps, "conv_taps"));
+  TTT_TRY(check_ptr(W_target, "W_target"));
+  TTT_TRY(check_ptr(V, "V"));
+  TTT_TRY(check_ptr(workspace, "workspace", 256));
+  const Layout L = step_layout(g);
+  if (workspace_bytes < L.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                       " bytes, needs " + std::to_string(L.total));
+  const size_t ab = g.act_bytes(), wb = g.w_bytes();
+  TTT_TRY(check_aliasing({range_of("X0", X0, g.B * g.T * g.d * ab),
+                          range_of("conv_taps", conv_taps, g.K * g.d * wb),
+                          range_of("W_target", W_target, g.d * g.d * wb)},
+                         {range_of("V", V, g.B * g.T * g.d * 2),
+                          range_of("workspace", workspace, L.total)}));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* X0b = static_cast<const uint16_t*>(X0);
+  if (g.act_f32) {
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(X0),
+                                                      at<uint16_t>(workspace, L.x0b), g.B * g.T * g.d, s));
+    X0b = at<uint16_t>(workspace, L.x0b);
+  }
+  uint16_t* Y = at<uint16_t>(workspace, L.y);
+  uint16_t* WtT = at<uint16_t>(workspace, L.wtt);
+  TTT_LAUNCH("transpose_w_target", s,
+             tttk::launch_transpose(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, s));
+  TTT_LAUNCH("conv", s,
+             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, (int)g.B, (int)g.T, (int)g.T_pad,
+                               (int)g.d, (int)g.K, (int)g.C, g.pad_chunk, s));
+  TTT_LAUNCH("target", s,
+             tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), 1.0f, (int)g.B,
+                                 (int)g.T, (int)g.T_pad, (int)g.d, s));
+  return TTT_OK;
+}
+
+ttt_status ttt_profile_enable(int32_t on) {
+  for (auto& r : g_timing.recs) {
+    g_timing.pool.push_back(r.start);
+    g_timing.pool.push_back(r.stop);
+  }
+  g_timing.recs.clear();
+  g_timing.on = on != 0;
+  return TTT_OK;
+}
+
+int32_t ttt_profile_read(ttt_kernel_stat* out, int32_t max_entries) {
+  std::vector<ttt_kernel_stat> stats;
+  for (auto& r : g_timing.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) == hipSuccess &&
+        hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      ttt_kernel_stat* st = nullptr;
+      for (auto& x : stats)
+        if (std::strcmp(x.name, r.name) == 0) st = &x;
+      if (st == nullptr) {
+        stats.push_back({});
+        st = &stats.back();
+        std::snprintf(st->name, sizeof(st->name), "%s", r.name);
+      }
+      st->launches += 1;
+      st->total_ms += ms;
+    }
+    g_timing.pool.push_back(r.start);
+    g_timing.pool.push_back(r.stop);
+  }
+  g_timing.recs.clear();
+  const int32_t n = (int32_t)stats.size();
+  for (int32_t i = 0; i < n && i < max_entries && out != nullptr; ++i) out[i] = stats[i];
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+"""CPU-only: the C-ABI library loads, exports every function include/ttt.h
+declares, and rejects bad arguments on the host before launching anything.
+
+No call here reaches a kernel launch: every call fails argument checking,
+which runs before any HIP call. Pointers are fake, aligned addresses that the
+library never dereferences on an error path.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+from test_layer_gate_amd import _binding as bnd  # noqa: E402
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, ALIAS = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    names = set(re.findall(r"\b(ttt_[a-z_]+)\s*\(", src))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bnd.LIB_PATH):
+        pytest.fail("libttt_layer.so is not built (run __graft_entry__.build())")
+    return bnd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in ttt.h but not exported"
+
+
+def test_status_strings(L):
+    for code, name in [(0, "TTT_OK"), (-1, "TTT_ERR_INVALID_ARG"), (-2, "TTT_ERR_UNSUPPORTED"),
+                       (-3, "TTT_ERR_WORKSPACE"), (-4, "TTT_ERR_ALIAS"), (-5, "TTT_ERR_HIP")]:
+        assert L.ttt_status_string(code).decode() == name
+
+
+def qwen_desc(**kw):
+    a = dict(batch=1, seq_len=65536, d_model=2560, d_ff=9728, conv_k=4)
+    a.update(kw)
+    return bnd.make_desc(**a)
+
+
+def ws_size(L, desc, chunk):
+    n = ctypes.c_size_t(0)
+    st = L.ttt_workspace_size(ctypes.byref(desc), chunk, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_matches_layout(L):
+    st, n = ws_size(L, qwen_desc(), 1024)
+    assert st == OK
+    B, T, d, f, k = 1, 65536, 2560, 9728, 64
+    expect = (B * T * d * 2 + d * d * 2 + B * T * f * 2 + B * f * T * 2 + B * d * T * 2
+              + B * k * d * f * 2)
+    assert expect <= n <= expect + 16 * 256
+    st, n_run = ws_size(L, qwen_desc(flags=bnd.FLAG_SCHED_RUNNING), 1024)
+    assert st == OK and n_run < n      # running schedule keeps one bf16 copy
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, INVALID), ("seq_len", 0, INVALID), ("d_model", 0, INVALID),
+    ("d_ff", -64, INVALID), ("conv_k", 0, INVALID), ("act_dtype", 7, INVALID),
+    ("weight_dtype", -1, INVALID), ("flags", 1 << 9, INVALID),
+    ("flags", bnd.FLAG_SCHED_RUNNING | bnd.FLAG_SCHED_PREFIX, INVALID),
+    ("w0_batch_stride", -1, INVALID), ("w0_batch_stride", 100, INVALID),
+    ("d_model", 2500, UNSUPPORTED), ("d_ff", 9700, UNSUPPORTED), ("conv_k", 65, UNSUPPORTED),
+])
+def test_bad_descriptor(L, field, value, code):
+    desc = qwen_desc()
+    setattr(desc, field, value)
+    st, _ = ws_size(L, desc, 1024)
+    assert st == code, (field, value, st, L.ttt_last_error())
+    assert L.ttt_last_error().decode()
+
+
+@pytest.mark.parametrize("chunk,code", [(0, INVALID), (-64, INVALID), (100, UNSUPPORTED),
+                                        (64, OK), (1024, OK)])
+def test_chunk_validation(L, chunk, code):
+    st, _ = ws_size(L, qwen_desc(), chunk)
+    assert st == code
+
+
+class FakeBuffers:
+    """Distinct, 256-byte aligned fake device addresses, far apart."""
+
+    def __init__(self):
+        self.base = 1 << 40
+        self.step = 1 << 36
+
+    def __getitem__(self, i):
+        return ctypes.c_void_p(self.base + i * self.step)
+
+
+def forward(L, desc, ptrs, eta=1e-3, chunk=1024, ws_bytes=1 << 62):
+    return L.ttt_layer_forward(ctypes.byref(desc), *ptrs[:7], ctypes.c_float(eta), chunk,
+                               ptrs[7], ptrs[8], ptrs[9], ctypes.c_size_t(ws_bytes), None)
+
+
+def good_ptrs():
+    fb = FakeBuffers()
+    return [fb[i] for i in range(10)]
+
+
+def test_forward_rejects_nonfinite_eta(L):
+    assert forward(L, qwen_desc(), good_ptrs(), eta=float("nan")) == INVALID
+    assert forward(L, qwen_desc(), good_ptrs(), eta=float("inf")) == INVALID
+
+
+@pytest.mark.parametrize("idx", range(10))
+def test_forward_rejects_null(L, idx):
+    p = good_ptrs()
+    p[idx] = ctypes.c_void_p(0)
+    assert forward(L, qwen_desc(), p) == INVALID
+    assert "NULL" in L.ttt_last_error().decode()
+
+
+@pytest.mark.parametrize("idx", range(10))
+def test_forward_rejects_misaligned(L, idx):
+    p = good_ptrs()
+    p[idx] = ctypes.c_void_p(p[idx].value + 8)
+    assert forward(L, qwen_desc(), p) == INVALID
+    assert "aligned" in L.ttt_last_error().decode()
+
+
+def test_forward_rejects_small_workspace(L):
+    _, need = ws_size(L, qwen_desc(), 1024)
+    assert forward(L, qwen_desc(), good_ptrs(), ws_bytes=need - 1) == WORKSPACE
+
+
+@pytest.mark.parametrize("out_idx,in_idx", [(7, 0), (7, 1), (8, 4), (8, 2), (9, 6), (7, 8),
+                                            (9, 7)])
+def test_forward_rejects_aliasing(L, out_idx, in_idx):
+    p = good_ptrs()
+    p[out_idx] = ctypes.c_void_p(p[in_idx].value + 4096)
+    st = forward(L, qwen_desc(), p)
+    assert st == ALIAS, L.ttt_last_error()
+
+
+def test_step_entry_points_validate(L):
+    desc = qwen_desc()
+    fb = FakeBuffers()
+    st = L.ttt_gated_activation(ctypes.byref(desc), fb[0], fb[1], ctypes.c_void_p(0), fb[3],
+                                fb[4], ctypes.c_size_t(1 << 62), None)
+    assert st == INVALID
+    st = L.ttt_lm_target(ctypes.byref(desc), fb[0], fb[1], fb[2], 100, fb[3], fb[4],
+                         ctypes.c_size_t(1 << 62), None)
+    assert st == UNSUPPORTED
+    st = L.ttt_lm_target(ctypes.byref(desc), fb[0], fb[1], fb[2], 1024, fb[3], fb[4],
+                         ctypes.c_size_t(16), None)
+    assert st == WORKSPACE
+
+
+def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bnd, "_lib", None)
+    monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        bnd.lib()
