@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -71,6 +72,7 @@ struct Geo {
   int64_t B, T, d, f, K, C, T_pad, nchunks;
   bool act_f32, w_f32, pad_chunk, running;
   int64_t w0_stride;  // elements
+  tttk::Dims dims;
   size_t act_bytes() const { return act_f32 ? 4 : 2; }
   size_t w_bytes() const { return w_f32 ? 4 : 2; }
 };
@@ -90,12 +92,13 @@ Layout forward_layout(const Geo& g) {
     off = align256(off + bytes);
     return o;
   };
-  L.y = take(g.B * g.T_pad * g.d * 2);
-  L.wtt = take(g.d * g.d * 2);
-  L.z = take(g.B * g.T * g.f * 2);
-  L.zt = take(g.B * g.f * g.T_pad * 2);
-  L.vt = take(g.B * g.d * g.T_pad * 2);
-  L.snap = take(g.running ? g.B * g.d * g.f * 2 : g.B * g.nchunks * g.d * g.f * 2);
+  const tttk::Dims& D = g.dims;
+  L.y = take(g.B * g.T_pad * D.ld_y * 2);
+  L.wtt = take(g.d * D.ld_y * 2);
+  L.z = take(g.B * g.T * D.ld_z * 2);
+  L.zt = take(g.B * g.f * D.ld_t * 2);
+  L.vt = take(g.B * g.d * D.ld_t * 2);
+  L.snap = take(g.running ? g.B * g.d * D.ld_s * 2 : g.B * g.nchunks * g.d * D.ld_s * 2);
   if (g.act_f32) {
     L.hb = take(g.B * g.T * g.d * 2);
     L.x0b = take(g.B * g.T * g.d * 2);
@@ -118,8 +121,8 @@ Layout step_layout(const Geo& g) {
     off = align256(off + bytes);
     return o;
   };
-  L.y = take(g.B * g.T_pad * g.d * 2);
-  L.wtt = take(g.d * g.d * 2);
+  L.y = take(g.B * g.T_pad * g.dims.ld_y * 2);
+  L.wtt = take(g.d * g.dims.ld_y * 2);
   if (g.act_f32) {
     L.hb = take(g.B * g.T * g.d * 2);
     L.x0b = take(g.B * g.T * g.d * 2);
@@ -180,6 +183,7 @@ ttt_status check_desc(const ttt_desc* desc, Geo* g) {
   g->w0_stride = D.w0_batch_stride;
   g->C = 0;
   g->nchunks = 0;
+  g->dims = tttk::make_dims((int)g->B, (int)g->T, (int)g->d, (int)g->f);
   return TTT_OK;
 }
 
@@ -318,7 +322,7 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
   TTT_TRY(check_aliasing(inputs, outputs));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int B = (int)g.B, T = (int)g.T, T_pad = (int)g.T_pad, d = (int)g.d, f = (int)g.f;
+  const tttk::Dims& D = g.dims;
   const int64_t df = g.d * g.f;
 
   // bf16 operands
@@ -349,40 +353,52 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
   uint16_t* VT = at<uint16_t>(workspace, L.vt);
   uint16_t* snap = at<uint16_t>(workspace, L.snap);
 
+  // The update's operands are fp16 with the target scaled by vscale = eta *
+  // 2^p, p = round(-log2 |eta|), so that eta * V sits at V's own magnitude;
+  // the state is carried as 2^p * W in fp32 and every output is multiplied
+  // back by 2^-p. Powers of two make both scalings exact.
+  float vscale = 0.0f, acc_scale = 1.0f;
+  if (eta != 0.0f) {
+    long p = std::lround(-std::log2(std::fabs((double)eta)));
+    p = std::max(-60L, std::min(60L, p));
+    acc_scale = std::ldexp(1.0f, (int)p);
+    vscale = eta * acc_scale;
+  }
+
   TTT_LAUNCH("transpose_w_target", s,
-             tttk::launch_transpose(W_target, g.w_f32, WtT, d, d, s));
+             tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, D.ld_y, s));
   TTT_LAUNCH("conv", s,
-             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, B, T, T_pad, d, (int)g.K,
-                               (int)g.C, g.pad_chunk, s));
-  TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgb, Wub, Z, ZT, B, T, T_pad, d, f, s));
-  TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, eta, B, T, T_pad, d, s));
+             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, D, (int)g.K, (int)g.C, g.pad_chunk, s));
+  TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgb, Wub, Z, ZT, D, s));
+  TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, vscale, D, s));
 
   const int steps_per_chunk = (int)(g.C / 64);
   const int nk_total = (int)((g.T + 63) / 64);
+  const int64_t snap_cstride = g.d * D.ld_s;
   if (!g.running) {
     // Materialised exclusive prefix: snapshot i = bf16(W^(i)) for every chunk,
     // W_down_final = W^(k); then every chunk's output in one launch.
     TTT_LAUNCH("update_prefix", s,
-               tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, snap,
-                                   g.nchunks * df, W_down_final, nullptr, B, T_pad, d, f, 0,
+               tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale, snap,
+                                   g.nchunks * snap_cstride, W_down_final, nullptr, D, 0,
                                    nk_total, steps_per_chunk, s));
     TTT_LAUNCH("apply", s,
-               tttk::launch_apply(Z, snap, g.nchunks * df, df, O, g.act_f32, B, T, d, f, 0, T,
-                                  (int)g.C, s));
+               tttk::launch_apply(Z, snap, g.nchunks * snap_cstride, snap_cstride, O, g.act_f32,
+                                  D, 0, (int)g.T, (int)g.C, s));
   } else {
     // Running state: W_down_final holds W^(i) in fp32, `snap` its bf16 copy.
     TTT_LAUNCH("update_running", s,
-               tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, nullptr, 0,
-                                   W_down_final, snap, B, T_pad, d, f, 0, 0, steps_per_chunk, s));
+               tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale,
+                                   nullptr, 0, W_down_final, snap, D, 0, 0, steps_per_chunk, s));
     for (int64_t i = 0; i < g.nchunks; ++i) {
       const int t0 = (int)(i * g.C), t1 = (int)std::min<int64_t>(g.T, (i + 1) * g.C);
       TTT_LAUNCH("apply", s,
-                 tttk::launch_apply(Z, snap, df, 0, O, g.act_f32, B, T, d, f, t0, t1,
-                                    (int)g.C, s));
+                 tttk::launch_apply(Z, snap, snap_cstride, 0, O, g.act_f32, D, t0, t1, (int)g.C,
+                                    s));
       const int nk = (t1 - t0 + 63) / 64;
       TTT_LAUNCH("update_running", s,
-                 tttk::launch_update(ZT, VT, W_down_final, true, df, nullptr, 0, W_down_final,
-                                     snap, B, T_pad, d, f, t0, nk, steps_per_chunk, s));
+                 tttk::launch_update(ZT, VT, W_down_final, true, df, g.f, acc_scale, nullptr, 0,
+                                     W_down_final, snap, D, t0, nk, steps_per_chunk, s));
     }
   }
   return TTT_OK;
@@ -425,9 +441,10 @@ ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void*
     Wgb = at<uint16_t>(workspace, L.wgb);
     Wub = at<uint16_t>(workspace, L.wub);
   }
+  tttk::Dims D = g.dims;
+  D.ld_z = g.f;  // the caller's Z is dense [B, T, d_ff]
   TTT_LAUNCH("gate_up", s,
-             tttk::launch_gate_up(Hb, Wgb, Wub, static_cast<uint16_t*>(Z), nullptr, (int)g.B,
-                                  (int)g.T, (int)g.T_pad, (int)g.d, (int)g.f, s));
+             tttk::launch_gate_up(Hb, Wgb, Wub, static_cast<uint16_t*>(Z), nullptr, D, s));
   return TTT_OK;
 }
 
@@ -462,13 +479,13 @@ ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0, const void* conv_
   uint16_t* Y = at<uint16_t>(workspace, L.y);
   uint16_t* WtT = at<uint16_t>(workspace, L.wtt);
   TTT_LAUNCH("transpose_w_target", s,
-             tttk::launch_transpose(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, s));
+             tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, g.dims.ld_y,
+                                        s));
   TTT_LAUNCH("conv", s,
-             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, (int)g.B, (int)g.T, (int)g.T_pad,
-                               (int)g.d, (int)g.K, (int)g.C, g.pad_chunk, s));
+             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, g.dims, (int)g.K, (int)g.C,
+                               g.pad_chunk, s));
   TTT_LAUNCH("target", s,
-             tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), 1.0f, (int)g.B,
-                                 (int)g.T, (int)g.T_pad, (int)g.d, s));
+             tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), 1.0f, g.dims, s));
   return TTT_OK;
 }
 

@@ -1,13 +1,16 @@
 // gfx950 (CDNA4) kernels of the In-Place TTT gated-MLP prefill.
 //
-// The dense contractions (gate/up projection, target projection, the
-// per-chunk fast-weight update and the apply) run on one bf16 MFMA GEMM core:
-// C[M][N] = sum_k A[m][k] * B[n][k], both operands K-contiguous in HBM,
-// staged through LDS in 64-wide K slices with two LDS buffers, and
-// multiplied with v_mfma_f32_32x32x16_bf16 (fp32 accumulation). A workgroup
-// has 4 wave64s in a 2 x 2 grid; each wave owns (BM/2) x (BN/2) outputs.
-// The depthwise conv, W_target transpose and fp32->bf16 casts are small
-// bandwidth-bound kernels.
+// The four dense contractions (gate/up projection, target projection, the
+// fast-weight update and the apply) share one MFMA GEMM core:
+//   C[M][N] = sum_k A[m][k] * B[n][k],  both operands K-contiguous in HBM.
+// A workgroup is 4 wave64s in a 2 x 2 grid; wave (wm, wn) owns a
+// (BM/2) x (BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16},
+// fp32 accumulation, accumulators in AGPRs). K advances 64 elements per step
+// through two LDS stages: buffer_load ... lds moves each 16-byte chunk from
+// HBM straight into LDS (no VGPR staging), bounds-checked by the buffer
+// descriptor (rows past the tile's valid rows read as zero), while the MFMAs
+// run on the other stage. Fragments are read with ds_read_b128 one K-substep
+// ahead of the MFMAs that use them.
 //
 // Method sources: "论文精读：In-Place Test-Time Training" reading notes —
 // "In-Place 设计" (gated MLP), "Chunk-Wise 更新机制" (update equation),
@@ -24,10 +27,15 @@ namespace {
 
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kThreads = 256;  // 4 wave64s
-constexpr int kBK = 64;        // K elements per LDS stage (128 bytes per row)
+constexpr int kThreads = 256;      // small kernels
+constexpr int kGemmWaves = 8;      // GEMM workgroups: 8 wave64s, 2 per SIMD
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kBK = 64;            // K elements per LDS stage (128 bytes per row)
+constexpr int kRsrcWord3 = 0x00020000;
 
 // ---------------------------------------------------------------- helpers
 
@@ -38,59 +46,85 @@ __device__ __forceinline__ u16 bf16_rne(float x) {
   return (u16)(u >> 16);
 }
 
-__device__ __forceinline__ float bf16_f32(u16 h) {
-  return __uint_as_float((uint32_t)h << 16);
+__device__ __forceinline__ float bf16_f32(u16 h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ u16 f16_rne(float x) {
+  return __builtin_bit_cast(u16, (_Float16)x);  // v_cvt_f16_f32: round to nearest even
 }
 
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)bf16_rne(lo) | ((uint32_t)bf16_rne(hi) << 16);
 }
 
-__device__ __forceinline__ float silu(float x) {
-  return x / (1.0f + __expf(-x));
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return (uint32_t)f16_rne(lo) | ((uint32_t)f16_rne(hi) << 16);
 }
 
-// LDS tile of `rows` x 64 bf16, row stride 128 B. The eight 16-byte chunks of
-// a row are XOR-permuted by (row ^ row >> 3) & 7 so that the 32 rows of an
-// MFMA fragment read, and the eight rows of a cooperative store, fall on
-// distinct banks.
-__device__ __forceinline__ int lds_off(int row, int kc) {
-  return row * kBK + (((kc ^ row ^ (row >> 3)) & 7) << 3);
-}
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-__device__ __forceinline__ bf16x8 frag(const u16* lds, int row, int kc) {
-  return __builtin_bit_cast(bf16x8,
-                            *reinterpret_cast<const uint4*>(lds + lds_off(row, kc)));
-}
-
-// One 64-wide K slice of ROWS rows, moved HBM -> registers -> LDS by the
-// whole workgroup, 16 bytes per thread per step. Rows at or past rows_valid
-// read as zero.
-template <int ROWS>
-struct GTile {
-  static constexpr int N = ROWS * 8 / kThreads;
-  static_assert(N >= 1 && ROWS * 8 % kThreads == 0, "tile rows");
-  uint4 v[N];
-  __device__ __forceinline__ void load(const u16* __restrict__ base, int64_t ld,
-                                       int rows_valid, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 3;
-      if (r < rows_valid)
-        v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)r * ld + (c & 7) * 8);
-      else
-        v[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  __device__ __forceinline__ void store(u16* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + i * kThreads;
-      *reinterpret_cast<uint4*>(lds + lds_off(c >> 3, c & 7)) = v[i];
-    }
+struct Bf16Mma {
+  static __device__ __forceinline__ f32x16 mma(const uint4& a, const uint4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
 };
+
+struct F16Mma {
+  static __device__ __forceinline__ f32x16 mma(const uint4& a, const uint4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+// LDS tile of `rows` x 64 16-bit elements, 128 B per row. The eight 16-byte
+// chunks of a row are XOR-permuted by swz(row), so that the 32 rows of one
+// fragment read fall on distinct banks. swz depends on row % 32 only, so a
+// lane's permutation is the same for every 32-row fragment it reads and each
+// read is one per-lane register plus an immediate offset.
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 3)) & 7; }
+__device__ __forceinline__ int lds_off(int row, int kc) { return row * kBK + ((kc ^ swz(row)) << 3); }
+
+__device__ __forceinline__ uint4 lds_frag(const u16* lds, int row, int kc) {
+  return *reinterpret_cast<const uint4*>(lds + lds_off(row, kc));
+}
+
+// One operand tile of ROWS rows. Each of the 8 waves issues ROWS / 64
+// direct-to-LDS loads per K step; load i of wave w fills LDS rows
+// [(8i + w) * 8, +8), lane l the 16 bytes at physical chunk l % 8 of row
+// l / 8, which is the row's logical chunk (l % 8) ^ swz(row). The per-lane
+// byte offsets are fixed; the K step enters as the scalar offset.
+template <int ROWS>
+struct DmaTile {
+  static constexpr int NI = ROWS / (8 * kGemmWaves);
+  static_assert(ROWS % (8 * kGemmWaves) == 0, "rows");
+  uint32_t voff[NI];
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ void init(const u16* base, int64_t ld, int rows_valid, int wave,
+                                       int lane) {
+    int64_t bytes = rows_valid > 0 ? (int64_t)rows_valid * ld * 2 : 0;
+    if (bytes > 0xffffffffLL) bytes = 0xffffffffLL;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(base), (short)0, (int)(uint32_t)bytes,
+                                             kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (kGemmWaves * i + wave) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(row);
+      voff[i] = (uint32_t)((int64_t)row * ld * 2 + kc * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(u16* lds_region, int wave, uint32_t soff) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (lds_ptr_t)(lds_region + (kGemmWaves * i + wave) * 8 * kBK), 16, voff[i], soff,
+          0, 0);
+  }
+};
+
+__device__ __forceinline__ void wait_dma_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 
 // Maps the linear workgroup id to (batch, tile_m, tile_n). Workgroups are
 // handed to the 8 XCDs in turn, so ids are first renumbered so that each XCD
@@ -122,80 +156,8 @@ __device__ __forceinline__ TileIdx tile_index(int tiles_m, int tiles_n, int grou
 }
 
 struct NoHook {
-  __device__ __forceinline__ void operator()(int) const {}
+  __device__ __forceinline__ void operator()(int, const f32x16*) const {}
 };
-
-// The GEMM core. acc[m][n] is the 32x32 MFMA tile (m, n) of this wave:
-// output rows wm*BM/2 + m*32 + 8*(r/4) + 4*(lane/32) + r%4 for register r,
-// output column wn*BN/2 + n*32 + lane%32 (for SPLITB see brow()).
-// SPLITB: the B tile is BN/2 rows of B0 followed by BN/2 rows of B1 (the
-// gate and up projections); wave wn then owns the same BN/4 columns of each,
-// in acc[.][0, TN/2) (B0) and acc[.][TN/2, TN) (B1).
-// hook(kt) runs before the MFMAs of K step kt, when acc holds steps < kt.
-template <int BM, int BN, bool SPLITB, class Hook>
-__device__ __forceinline__ void gemm_mainloop(
-    const u16* __restrict__ A, int64_t lda, int a_valid,
-    const u16* __restrict__ B0, const u16* __restrict__ B1, int64_t ldb,
-    int b_valid, int nk, f32x16 (&acc)[BM / 64][BN / 64], u16* smem,
-    const Hook& hook) {
-  constexpr int TM = BM / 64, TN = BN / 64;
-  constexpr int STAGE = (BM + BN) * kBK;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  if (nk <= 0) return;
-
-  GTile<BM> ga;
-  GTile<SPLITB ? BN / 2 : BN> gb0;
-  GTile<SPLITB ? BN / 2 : 64> gb1;  // used only when SPLITB
-
-  auto gload = [&](int kt) {
-    const int64_t k = (int64_t)kt * kBK;
-    ga.load(A + k, lda, a_valid, tid);
-    gb0.load(B0 + k, ldb, b_valid, tid);
-    if constexpr (SPLITB) gb1.load(B1 + k, ldb, b_valid, tid);
-  };
-  auto sstore = [&](int buf) {
-    u16* s = smem + buf * STAGE;
-    ga.store(s, tid);
-    gb0.store(s + BM * kBK, tid);
-    if constexpr (SPLITB) gb1.store(s + BM * kBK + (BN / 2) * kBK, tid);
-  };
-  auto brow = [&](int n) {
-    if constexpr (SPLITB) {
-      constexpr int H = TN / 2;
-      return n < H ? wn * H * 32 + n * 32 : BN / 2 + wn * H * 32 + (n - H) * 32;
-    } else {
-      return wn * TN * 32 + n * 32;
-    }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    hook(kt);
-    const u16* sA = smem + cur * STAGE;
-    const u16* sB = sA + BM * kBK;
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int kc = 2 * s + (lane >> 5);
-      bf16x8 a[TM], b[TN];
-#pragma unroll
-      for (int m = 0; m < TM; ++m) a[m] = frag(sA, wm * TM * 32 + m * 32 + (lane & 31), kc);
-#pragma unroll
-      for (int n = 0; n < TN; ++n) b[n] = frag(sB, brow(n) + (lane & 31), kc);
-#pragma unroll
-      for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int n = 0; n < TN; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
-}
 
 template <int TM, int TN>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM][TN]) {
@@ -205,110 +167,273 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM][TN]) {
     for (int n = 0; n < TN; ++n) acc[m][n] = f32x16{};
 }
 
+// Wave layout of a BM x BN GEMM tile: WGM x WGN waves (WGM * WGN = 8), each
+// owning TM x TN MFMA tiles of 32 x 32.
+template <int BM, int BN, int WGM>
+struct Layout {
+  static constexpr int WGN = kGemmWaves / WGM;
+  static constexpr int TM = BM / (32 * WGM);
+  static constexpr int TN = BN / (32 * WGN);
+  static_assert(TM >= 1 && TN >= 1 && TM * 32 * WGM == BM && TN * 32 * WGN == BN, "layout");
+};
+
+// The GEMM core. acc[m * TN + n] is the 32x32 MFMA tile (m, n) of this wave
+// (wave w = (wm, wn) with wm = w / WGN, wn = w % WGN); its register r holds
+// output row wm*TM*32 + m*32 + 8*(r/4) + 4*(lane/32) + r%4 and column
+// wn*TN*32 + n*32 + lane%32.
+// SPLITB: the B tile is BN/2 rows of B0 followed by BN/2 rows of B1 (the
+// gate and up projections); wave wn then owns the same TN/2 * 32 columns of
+// each, in acc[.][0, TN/2) (B0) and acc[.][TN/2, TN) (B1).
+// hook(kt, acc) runs at the start of K step kt, when acc holds steps < kt.
+// lds0 / lds1 are the two LDS stages, each (BM + BN) * 64 elements, kept as
+// distinct arrays so the compiler can tell a stage being filled from the
+// stage being read.
+template <int BM, int BN, int WGM, class Op, bool SPLITB, class Hook>
+__device__ __forceinline__ void gemm_core(const u16* __restrict__ A, int64_t lda, int a_valid,
+                                          const u16* __restrict__ B0,
+                                          const u16* __restrict__ B1, int64_t ldb, int b_valid,
+                                          int nk, f32x16* acc, u16* lds0, u16* lds1,
+                                          const Hook& hook) {
+  using L = Layout<BM, BN, WGM>;
+  constexpr int TM = L::TM, TN = L::TN, WGN = L::WGN;
+  constexpr int BROWS = SPLITB ? BN / 2 : BN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  if (nk <= 0) return;
+
+  DmaTile<BM> ta;
+  DmaTile<BROWS> tb0;
+  DmaTile<SPLITB ? BN / 2 : 64> tb1;
+  ta.init(A, lda, a_valid, w, lane);
+  tb0.init(B0, ldb, b_valid, w, lane);
+  if constexpr (SPLITB) tb1.init(B1, ldb, b_valid, w, lane);
+
+  auto issue = [&](u16* stage, int kt) {
+    const uint32_t soff = (uint32_t)kt * (kBK * 2);
+    ta.issue(stage, w, soff);
+    tb0.issue(stage + BM * kBK, w, soff);
+    if constexpr (SPLITB) tb1.issue(stage + BM * kBK + (BN / 2) * kBK, w, soff);
+  };
+
+  // Rows of this lane's fragments within the stage.
+  int arow[TM], brow[TN];
+#pragma unroll
+  for (int m = 0; m < TM; ++m) arow[m] = wm * TM * 32 + m * 32 + (lane & 31);
+#pragma unroll
+  for (int n = 0; n < TN; ++n) {
+    if constexpr (SPLITB) {
+      constexpr int H = TN / 2;
+      brow[n] = BM + (n < H ? wn * H * 32 + n * 32 : BN / 2 + wn * H * 32 + (n - H) * 32) +
+                (lane & 31);
+    } else {
+      brow[n] = BM + wn * TN * 32 + n * 32 + (lane & 31);
+    }
+  }
+  const int khalf = lane >> 5;
+
+  auto compute = [&](const u16* st) {
+    uint4 fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int m = 0; m < TM; ++m) fa[0][m] = lds_frag(st, arow[m], khalf);
+#pragma unroll
+    for (int n = 0; n < TN; ++n) fb[0][n] = lds_frag(st, brow[n], khalf);
+#pragma unroll
+    for (int s = 0; s < kBK / 16; ++s) {
+      const int cb = s & 1, nb = cb ^ 1;
+      if (s + 1 < kBK / 16) {
+#pragma unroll
+        for (int m = 0; m < TM; ++m) fa[nb][m] = lds_frag(st, arow[m], 2 * (s + 1) + khalf);
+#pragma unroll
+        for (int n = 0; n < TN; ++n) fb[nb][n] = lds_frag(st, brow[n], 2 * (s + 1) + khalf);
+      }
+#pragma unroll
+      for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n)
+          acc[m * TN + n] = Op::mma(fa[cb][m], fb[cb][n], acc[m * TN + n]);
+    }
+  };
+
+  issue(lds0, 0);
+  wait_dma_and_barrier();
+  for (int kt = 0; kt < nk; kt += 2) {
+    hook(kt, acc);
+    if (kt + 1 < nk) issue(lds1, kt + 1);
+    compute(lds0);
+    wait_dma_and_barrier();
+    if (kt + 1 < nk) {
+      hook(kt + 1, acc);
+      if (kt + 2 < nk) issue(lds0, kt + 2);
+      compute(lds1);
+      wait_dma_and_barrier();
+    }
+  }
+}
+
+// Output coordinates of register group q (registers 4q..4q+3) of MFMA tile
+// (m, n): four consecutive rows starting at row(), one column col().
+template <class L>
+struct Frag {
+  int wm, wn, lane;
+  __device__ __forceinline__ Frag() {
+    const int w = threadIdx.x >> 6;
+    wm = w / L::WGN;
+    wn = w % L::WGN;
+    lane = threadIdx.x & 63;
+  }
+  __device__ __forceinline__ int row(int m, int q) const {
+    return wm * L::TM * 32 + m * 32 + 8 * q + 4 * (lane >> 5);
+  }
+  __device__ __forceinline__ int col(int n) const { return wn * L::TN * 32 + n * 32 + (lane & 31); }
+};
+
 // ------------------------------------------------ gate/up + SiLU*mul (K1)
 // M = tokens (256), N = 128 columns of Wg and the same 128 of Wu, K = d.
-constexpr int K1_BM = 256, K1_BN = 256, K1_LDZ = K1_BN / 2 + 8;
+// Waves 2 x 4: each wave owns 128 tokens x 32 columns of Wg and of Wu.
+constexpr int K1_BM = 256, K1_BN = 256, K1_WGM = 2, K1_LDZ = K1_BN / 2 + 8;
 
-__global__ __launch_bounds__(kThreads) void gate_up_kernel(
-    const u16* __restrict__ H, const u16* __restrict__ Wg,
-    const u16* __restrict__ Wu, u16* __restrict__ Z, u16* __restrict__ ZT,
-    int T, int T_pad, int d, int f, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * (K1_BM + K1_BN) * kBK];
+__global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
+    const u16* __restrict__ H, const u16* __restrict__ Wg, const u16* __restrict__ Wu,
+    u16* __restrict__ Z, u16* __restrict__ ZT, Dims g, int tiles_m, int tiles_n) {
+  using L = Layout<K1_BM, K1_BN, K1_WGM>;
+  static_assert(L::TN == 2, "one gate and one up tile per wave");
+  __shared__ __attribute__((aligned(16))) u16 lds0[(K1_BM + K1_BN) * kBK];
+  __shared__ __attribute__((aligned(16))) u16 lds1[(K1_BM + K1_BN) * kBK];
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K1_BM, j0 = ti.tn * (K1_BN / 2);
-  f32x16 acc[4][4];
+  const int d = g.d, f = g.f;
+  f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  gemm_mainloop<K1_BM, K1_BN, true>(H + ((int64_t)ti.b * T + t0) * d, d, min(K1_BM, T - t0),
-                                     Wg + (int64_t)j0 * d, Wu + (int64_t)j0 * d, d,
-                                     min(K1_BN / 2, f - j0), d / kBK, acc, smem, NoHook{});
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  u16* sZ = smem;  // [256][K1_LDZ] staging for the token-major store
+  gemm_core<K1_BM, K1_BN, K1_WGM, Bf16Mma, true>(
+      H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0), Wg + (int64_t)j0 * d,
+      Wu + (int64_t)j0 * d, d, min(K1_BN / 2, f - j0), d / kBK, &acc[0][0], lds0, lds1,
+      NoHook{});
+  const Frag<L> fr;
+  // Token-major Z goes through LDS (rows 0-127 in lds0, 128-255 in lds1) so
+  // that its stores are whole 16-byte row segments.
+  u16* sZ = fr.wm == 0 ? lds0 : lds1;
+  const int jl = fr.wn * 32 + (fr.lane & 31);
+  const int j = j0 + jl;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < L::TM; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
+    for (int q = 0; q < 4; ++q) {
+      const int tl = m * 32 + 8 * q + 4 * (fr.lane >> 5);  // row within this wave's half
+      float z[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int tl = wm * 128 + m * 32 + 8 * q + 4 * (lane >> 5);
-        const int jl = wn * 64 + n * 32 + (lane & 31);
-        float z[4];
+      for (int e = 0; e < 4; ++e) z[e] = silu(acc[m][0][4 * q + e]) * acc[m][1][4 * q + e];
+      const int t = t0 + fr.wm * 128 + tl;
+      if (ZT != nullptr && j < f)
+        *reinterpret_cast<uint2*>(ZT + ((int64_t)ti.b * f + j) * g.ld_t + t) =
+            make_uint2(pack_f16(z[0], z[1]), pack_f16(z[2], z[3]));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = silu(acc[m][n][4 * q + e]) * acc[m][n + 2][4 * q + e];
-        const int t = t0 + tl, j = j0 + jl;
-        if (ZT != nullptr && j < f)
-          *reinterpret_cast<uint2*>(ZT + ((int64_t)ti.b * f + j) * T_pad + t) =
-              make_uint2(pack2(z[0], z[1]), pack2(z[2], z[3]));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sZ[(tl + e) * K1_LDZ + jl] = bf16_rne(z[e]);
-      }
+      for (int e = 0; e < 4; ++e) sZ[(tl + e) * K1_LDZ + jl] = bf16_rne(z[e]);
+    }
   if (Z == nullptr) return;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = tid + i * kThreads;
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + i * kGemmThreads;
     const int row = c >> 4, cc = c & 15;
-    const int t = t0 + row, j = j0 + cc * 8;
-    if (t < T && j < f)
-      *reinterpret_cast<uint4*>(Z + ((int64_t)ti.b * T + t) * f + j) =
-          *reinterpret_cast<const uint4*>(sZ + row * K1_LDZ + cc * 8);
+    const u16* src = (row < 128 ? lds0 : lds1) + (row & 127) * K1_LDZ + cc * 8;
+    const int t = t0 + row, jj = j0 + cc * 8;
+    if (t < g.T && jj < f)
+      *reinterpret_cast<uint4*>(Z + ((int64_t)ti.b * g.T + t) * g.ld_z + jj) =
+          *reinterpret_cast<const uint4*>(src);
   }
 }
 
 // ------------------------------------------------------ target GEMM (K2)
-// M = tokens (256), N = output channels (256), K = d.
-__global__ __launch_bounds__(kThreads) void target_kernel(
+// M = tokens (256), N = output channels (256), K = d; fp16 operands.
+constexpr int K2_BM = 256, K2_BN = 256, K2_WGM = 2;
+
+__global__ __launch_bounds__(kGemmThreads) void target_kernel(
     const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
-    u16* __restrict__ Vtok, float scale, int T, int T_pad, int d, int tiles_m,
-    int tiles_n) {
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * (256 + 256) * kBK];
+    u16* __restrict__ Vtok, float vscale, Dims g, int tiles_m, int tiles_n) {
+  using L = Layout<K2_BM, K2_BN, K2_WGM>;
+  __shared__ __attribute__((aligned(16))) u16 lds0[(K2_BM + K2_BN) * kBK];
+  __shared__ __attribute__((aligned(16))) u16 lds1[(K2_BM + K2_BN) * kBK];
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
-  const int t0 = ti.tm * 256, c0 = ti.tn * 256;
-  f32x16 acc[4][4];
+  const int t0 = ti.tm * K2_BM, c0 = ti.tn * K2_BN;
+  const int d = g.d;
+  f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  gemm_mainloop<256, 256, false>(Y + ((int64_t)ti.b * T_pad + t0) * d, d, 256,
-                                 WtT + (int64_t)c0 * d, nullptr, d, min(256, d - c0),
-                                 d / kBK, acc, smem, NoHook{});
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  gemm_core<K2_BM, K2_BN, K2_WGM, F16Mma, false>(
+      Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM, WtT + (int64_t)c0 * g.ld_y,
+      nullptr, g.ld_y, min(K2_BN, d - c0), d / kBK, &acc[0][0], lds0, lds1, NoHook{});
+  const Frag<L> fr;
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < L::TM; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < L::TN; ++n)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int t = t0 + wm * 128 + m * 32 + 8 * q + 4 * (lane >> 5);
-        const int c = c0 + wn * 128 + n * 32 + (lane & 31);
+        const int t = t0 + fr.row(m, q);
+        const int c = c0 + fr.col(n);
         if (c >= d) continue;
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[m][n][4 * q + e] * scale;
+        for (int e = 0; e < 4; ++e) v[e] = acc[m][n][4 * q + e] * vscale;
         if (VT != nullptr)
-          *reinterpret_cast<uint2*>(VT + ((int64_t)ti.b * d + c) * T_pad + t) =
-              make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+          *reinterpret_cast<uint2*>(VT + ((int64_t)ti.b * d + c) * g.ld_t + t) =
+              make_uint2(pack_f16(v[0], v[1]), pack_f16(v[2], v[3]));
         if (Vtok != nullptr) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (t + e < T) Vtok[((int64_t)ti.b * T + t + e) * d + c] = bf16_rne(v[e]);
+            if (t + e < g.T) Vtok[((int64_t)ti.b * g.T + t + e) * d + c] = bf16_rne(v[e]);
         }
       }
 }
 
 // ------------------------------------------ fast-weight update (K3)
-// M = d_ff (256), N = d_model (BN), K = tokens. acc starts at the state and
-// absorbs (eta V)^T Z one 64-token step at a time; at every chunk start the
-// state before that chunk is stored as a bf16 snapshot (exclusive prefix).
-template <int BN, bool WINIT_F32>
-__global__ __launch_bounds__(kThreads) void update_kernel(
-    const u16* __restrict__ ZT, const u16* __restrict__ VT,
-    const void* __restrict__ Winit, int64_t winit_bstride, u16* __restrict__ snap,
-    int64_t snap_bstride, float* __restrict__ Wf, u16* __restrict__ shadow,
-    int T_pad, int d, int f, int tok_begin, int nk, int steps_per_chunk,
-    int tiles_m, int tiles_n) {
-  constexpr int BM = 256, TM = BM / 64, TN = BN / 64;
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * (BM + BN) * kBK];
+// M = d_ff (192), N = d_model (256), K = tokens; fp16 operands. acc starts
+// at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
+// time; at every chunk start the state before that chunk is stored as a
+// bf16 snapshot (the exclusive prefix).
+constexpr int K3_BM = 192, K3_BN = 256, K3_WGM = 2;
+
+// Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
+// into a [d][ld] bf16 matrix (row c = d_model index, column j = d_ff index).
+template <class L>
+struct SnapshotStore {
+  int j0, c0, d, f;
+  int64_t ld;
+  float out_scale;
+  __device__ __forceinline__ void operator()(u16* dst, const f32x16* acc) const {
+    const Frag<L> fr;
+#pragma unroll
+    for (int m = 0; m < L::TM; ++m)
+#pragma unroll
+      for (int n = 0; n < L::TN; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = j0 + fr.row(m, q);
+          const int c = c0 + fr.col(n);
+          const f32x16& a = acc[m * L::TN + n];
+          if (c < d && j < f)
+            *reinterpret_cast<uint2*>(dst + (int64_t)c * ld + j) =
+                make_uint2(pack_bf16(a[4 * q] * out_scale, a[4 * q + 1] * out_scale),
+                           pack_bf16(a[4 * q + 2] * out_scale, a[4 * q + 3] * out_scale));
+        }
+  }
+};
+
+template <bool WINIT_F32>
+__global__ __launch_bounds__(kGemmThreads) void update_kernel(
+    const u16* __restrict__ ZT, const u16* __restrict__ VT, const void* __restrict__ Winit,
+    int64_t winit_bstride, int64_t winit_ld, float acc_scale, u16* __restrict__ snap,
+    int64_t snap_bstride, float* __restrict__ Wf, u16* __restrict__ shadow, Dims g,
+    int tok_begin, int nk, int steps_per_chunk, int tiles_m, int tiles_n) {
+  using L = Layout<K3_BM, K3_BN, K3_WGM>;
+  constexpr int TM = L::TM, TN = L::TN;
+  __shared__ __attribute__((aligned(16))) u16 lds0[(K3_BM + K3_BN) * kBK];
+  __shared__ __attribute__((aligned(16))) u16 lds1[(K3_BM + K3_BN) * kBK];
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
-  const int j0 = ti.tm * BM, c0 = ti.tn * BN;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-  const int64_t df = (int64_t)d * f;
+  const int j0 = ti.tm * K3_BM, c0 = ti.tn * K3_BN;
+  const int d = g.d, f = g.f;
+  const Frag<L> fr;
+  const int64_t chunk_stride = (int64_t)d * g.ld_s;
+  const float out_scale = 1.0f / acc_scale;
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -317,11 +442,11 @@ __global__ __launch_bounds__(kThreads) void update_kernel(
     for (int n = 0; n < TN; ++n)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = j0 + wm * TM * 32 + m * 32 + 8 * q + 4 * (lane >> 5);
-        const int c = c0 + wn * TN * 32 + n * 32 + (lane & 31);
+        const int j = j0 + fr.row(m, q);
+        const int c = c0 + fr.col(n);
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (c < d && j < f) {
-          const int64_t o = ti.b * winit_bstride + (int64_t)c * f + j;
+          const int64_t o = ti.b * winit_bstride + (int64_t)c * winit_ld + j;
           if constexpr (WINIT_F32) {
             const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(Winit) + o);
             v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
@@ -334,79 +459,74 @@ __global__ __launch_bounds__(kThreads) void update_kernel(
           }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[m][n][4 * q + e] = v[e];
+        for (int e = 0; e < 4; ++e) acc[m][n][4 * q + e] = v[e] * acc_scale;
       }
 
-  auto store_bf16 = [&](u16* dst) {
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
-#pragma unroll
-      for (int n = 0; n < TN; ++n)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = j0 + wm * TM * 32 + m * 32 + 8 * q + 4 * (lane >> 5);
-          const int c = c0 + wn * TN * 32 + n * 32 + (lane & 31);
-          if (c < d && j < f)
-            *reinterpret_cast<uint2*>(dst + (int64_t)c * f + j) =
-                make_uint2(pack2(acc[m][n][4 * q], acc[m][n][4 * q + 1]),
-                           pack2(acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]));
-        }
-  };
-
+  SnapshotStore<L> snapshot{j0, c0, d, f, g.ld_s, out_scale};
   u16* snap_b = snap ? snap + ti.b * snap_bstride : nullptr;
-  auto hook = [&](int kt) {
+  auto hook = [=](int kt, const f32x16* a) {
     if (snap_b != nullptr && kt % steps_per_chunk == 0)
-      store_bf16(snap_b + (int64_t)(kt / steps_per_chunk) * df);
+      snapshot(snap_b + (int64_t)(kt / steps_per_chunk) * chunk_stride, a);
   };
-  gemm_mainloop<BM, BN, false>(ZT + ((int64_t)ti.b * f + j0) * T_pad + tok_begin, T_pad,
-                               min(BM, f - j0),
-                               VT + ((int64_t)ti.b * d + c0) * T_pad + tok_begin, nullptr,
-                               T_pad, min(BN, d - c0), nk, acc, smem, hook);
+  gemm_core<K3_BM, K3_BN, K3_WGM, F16Mma, false>(
+      ZT + ((int64_t)ti.b * f + j0) * g.ld_t + tok_begin, g.ld_t, min(K3_BM, f - j0),
+      VT + ((int64_t)ti.b * d + c0) * g.ld_t + tok_begin, nullptr, g.ld_t, min(K3_BN, d - c0), nk,
+      &acc[0][0], lds0, lds1, hook);
 
-  float* wf_b = Wf + ti.b * df;
+  float* wf_b = Wf + (int64_t)ti.b * d * f;
 #pragma unroll
   for (int m = 0; m < TM; ++m)
 #pragma unroll
     for (int n = 0; n < TN; ++n)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = j0 + wm * TM * 32 + m * 32 + 8 * q + 4 * (lane >> 5);
-        const int c = c0 + wn * TN * 32 + n * 32 + (lane & 31);
+        const int j = j0 + fr.row(m, q);
+        const int c = c0 + fr.col(n);
         if (c < d && j < f)
           *reinterpret_cast<float4*>(wf_b + (int64_t)c * f + j) =
-              make_float4(acc[m][n][4 * q], acc[m][n][4 * q + 1], acc[m][n][4 * q + 2],
-                          acc[m][n][4 * q + 3]);
+              make_float4(acc[m][n][4 * q] * out_scale, acc[m][n][4 * q + 1] * out_scale,
+                          acc[m][n][4 * q + 2] * out_scale, acc[m][n][4 * q + 3] * out_scale);
       }
-  if (shadow != nullptr) store_bf16(shadow + ti.b * df);
+  if (shadow != nullptr) snapshot(shadow + (int64_t)ti.b * chunk_stride, &acc[0][0]);
 }
 
 // ------------------------------------------------------------ apply (K4)
 // M = d_model (256), N = tokens (BN, which divides the chunk), K = d_ff.
 // The tile's tokens all lie in one chunk i and read snapshot i.
+template <int BN>
+struct ApplyCfg {
+  static constexpr int WGM = BN == 256 ? 2 : (BN == 128 ? 4 : 8);
+};
+
 template <int BN, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) void apply_kernel(
+__global__ __launch_bounds__(kGemmThreads) void apply_kernel(
     const u16* __restrict__ Z, const u16* __restrict__ snap, int64_t snap_bstride,
-    int64_t snap_cstride, void* __restrict__ O, int T, int d, int f, int tok_begin,
-    int chunk, int tiles_m, int tiles_n) {
-  constexpr int BM = 256, TM = BM / 64, TN = BN / 64;
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * (BM + BN) * kBK];
+    int64_t snap_cstride, void* __restrict__ O, Dims g, int tok_begin, int chunk, int tiles_m,
+    int tiles_n) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  constexpr int BM = 256, WGM = ApplyCfg<BN>::WGM;
+  using L = Layout<BM, BN, WGM>;
+  __shared__ __attribute__((aligned(16))) u16 lds0[(BM + BN) * kBK];
+  __shared__ __attribute__((aligned(16))) u16 lds1[(BM + BN) * kBK];
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int c0 = ti.tm * BM, t0 = tok_begin + ti.tn * BN;
   const int i = t0 / chunk;
-  f32x16 acc[TM][TN];
+  const int d = g.d, f = g.f, T = g.T;
+  f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  gemm_mainloop<BM, BN, false>(snap + ti.b * snap_bstride + i * snap_cstride + (int64_t)c0 * f,
-                               f, min(BM, d - c0), Z + ((int64_t)ti.b * T + t0) * f, nullptr,
-                               f, min(BN, T - t0), f / kBK, acc, smem, NoHook{});
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  gemm_core<BM, BN, WGM, Bf16Mma, false>(
+      snap + ti.b * snap_bstride + i * snap_cstride + (int64_t)c0 * g.ld_s, g.ld_s,
+      min(BM, d - c0), Z + ((int64_t)ti.b * T + t0) * g.ld_z, nullptr, g.ld_z, min(BN, T - t0),
+      f / kBK, &acc[0][0], lds0, lds1, NoHook{});
+  const Frag<L> fr;
 #pragma unroll
-  for (int m = 0; m < TM; ++m)
+  for (int m = 0; m < L::TM; ++m)
 #pragma unroll
-    for (int n = 0; n < TN; ++n)
+    for (int n = 0; n < L::TN; ++n)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int c = c0 + wm * TM * 32 + m * 32 + 8 * q + 4 * (lane >> 5);
-        const int t = t0 + wn * TN * 32 + n * 32 + (lane & 31);
+        const int c = c0 + fr.row(m, q);
+        const int t = t0 + fr.col(n);
         if (t >= T || c >= d) continue;
         const int64_t o = ((int64_t)ti.b * T + t) * d + c;
         if constexpr (OUT_F32) {
@@ -415,10 +535,11 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(
                           acc[m][n][4 * q + 3]);
         } else {
           *reinterpret_cast<uint2*>(static_cast<u16*>(O) + o) =
-              make_uint2(pack2(acc[m][n][4 * q], acc[m][n][4 * q + 1]),
-                         pack2(acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]));
+              make_uint2(pack_bf16(acc[m][n][4 * q], acc[m][n][4 * q + 1]),
+                         pack_bf16(acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]));
         }
       }
+#endif
 }
 
 // --------------------------------------------------- small kernels
@@ -428,14 +549,14 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const float* __restrict_
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * kThreads) {
     const float4 x = reinterpret_cast<const float4*>(src)[i];
-    reinterpret_cast<uint2*>(dst)[i] = make_uint2(pack2(x.x, x.y), pack2(x.z, x.w));
+    reinterpret_cast<uint2*>(dst)[i] = make_uint2(pack_bf16(x.x, x.y), pack_bf16(x.z, x.w));
   }
 }
 
 template <bool F32>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(const void* __restrict__ src,
                                                              u16* __restrict__ dst, int rows,
-                                                             int cols) {
+                                                             int cols, int64_t ld_dst) {
   __shared__ float tile[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -450,21 +571,23 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const void* __restr
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) dst[(int64_t)c * rows + r] = bf16_rne(tile[tx][i]);
+    if (c < cols && r < rows) dst[(int64_t)c * ld_dst + r] = f16_rne(tile[tx][i]);
   }
 }
 
 template <bool TAPS_F32>
-__global__ __launch_bounds__(kThreads) void conv_kernel(
-    const u16* __restrict__ X0, const void* __restrict__ taps, u16* __restrict__ Y, int T,
-    int T_pad, int d, int K, int chunk, int pad_chunk, int64_t total) {
+__global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ X0,
+                                                        const void* __restrict__ taps,
+                                                        u16* __restrict__ Y, Dims g, int K,
+                                                        int chunk, int pad_chunk, int64_t total) {
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (gid >= total) return;
+  const int d = g.d, T = g.T;
   const int d8 = d >> 3;
   const int c = (int)(gid % d8) * 8;
   const int64_t bt = gid / d8;
-  const int t = (int)(bt % T_pad);
-  const int b = (int)(bt / T_pad);
+  const int t = (int)(bt % g.T_pad);
+  const int b = (int)(bt / g.T_pad);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int end = pad_chunk ? min(T, (t / chunk + 1) * chunk) : T;
   for (int k = 0; k < K && t + k < end; ++k) {
@@ -472,12 +595,14 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
     float tp[8];
     if constexpr (TAPS_F32) {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(taps) + (int64_t)k * d + c);
+      const float4* p =
+          reinterpret_cast<const float4*>(static_cast<const float*>(taps) + (int64_t)k * d + c);
       const float4 a = p[0], bq = p[1];
       tp[0] = a.x; tp[1] = a.y; tp[2] = a.z; tp[3] = a.w;
       tp[4] = bq.x; tp[5] = bq.y; tp[6] = bq.z; tp[7] = bq.w;
     } else {
-      const uint4 tv = *reinterpret_cast<const uint4*>(static_cast<const u16*>(taps) + (int64_t)k * d + c);
+      const uint4 tv =
+          *reinterpret_cast<const uint4*>(static_cast<const u16*>(taps) + (int64_t)k * d + c);
       const uint32_t tw[4] = {tv.x, tv.y, tv.z, tv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -491,9 +616,9 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(
       acc[2 * e + 1] = fmaf(tp[2 * e + 1], __uint_as_float(xw[e] & 0xffff0000u), acc[2 * e + 1]);
     }
   }
-  *reinterpret_cast<uint4*>(Y + ((int64_t)b * T_pad + t) * d + c) =
-      make_uint4(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]), pack2(acc[4], acc[5]),
-                 pack2(acc[6], acc[7]));
+  *reinterpret_cast<uint4*>(Y + ((int64_t)b * g.T_pad + t) * g.ld_y + c) =
+      make_uint4(pack_f16(acc[0], acc[1]), pack_f16(acc[2], acc[3]), pack_f16(acc[4], acc[5]),
+                 pack_f16(acc[6], acc[7]));
 }
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -509,94 +634,93 @@ hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(const void* src, bool src_f32, uint16_t* dst, int rows, int cols,
-                            hipStream_t s) {
+hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, int rows, int cols,
+                                int64_t ld_dst, hipStream_t s) {
   dim3 grid(ceil_div(cols, 64), ceil_div(rows, 64));
   if (src_f32)
-    transpose_kernel<true><<<grid, kThreads, 0, s>>>(src, dst, rows, cols);
+    transpose_kernel<true><<<grid, kThreads, 0, s>>>(src, dst, rows, cols, ld_dst);
   else
-    transpose_kernel<false><<<grid, kThreads, 0, s>>>(src, dst, rows, cols);
+    transpose_kernel<false><<<grid, kThreads, 0, s>>>(src, dst, rows, cols, ld_dst);
   return hipGetLastError();
 }
 
-hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint16_t* Y, int B,
-                       int T, int T_pad, int d, int K, int chunk, bool pad_chunk, hipStream_t s) {
-  const int64_t total = (int64_t)B * T_pad * (d / 8);
+hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint16_t* Y,
+                       const Dims& g, int K, int chunk, bool pad_chunk, hipStream_t s) {
+  const int64_t total = (int64_t)g.B * g.T_pad * (g.d / 8);
   const int blocks = ceil_div(total, kThreads);
   if (taps_f32)
-    conv_kernel<true><<<blocks, kThreads, 0, s>>>(X0, taps, Y, T, T_pad, d, K, chunk,
-                                                  pad_chunk ? 1 : 0, total);
+    conv_kernel<true><<<blocks, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
+                                                  total);
   else
-    conv_kernel<false><<<blocks, kThreads, 0, s>>>(X0, taps, Y, T, T_pad, d, K, chunk,
-                                                   pad_chunk ? 1 : 0, total);
+    conv_kernel<false><<<blocks, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
+                                                   total);
   return hipGetLastError();
 }
 
 hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wg, const uint16_t* Wu, uint16_t* Z,
-                          uint16_t* ZT, int B, int T, int T_pad, int d, int f, hipStream_t s) {
-  const int tiles_m = T_pad / K1_BM, tiles_n = ceil_div(f, K1_BN / 2);
-  gate_up_kernel<<<tiles_m * tiles_n * B, kThreads, 0, s>>>(H, Wg, Wu, Z, ZT, T, T_pad, d, f,
-                                                            tiles_m, tiles_n);
+                          uint16_t* ZT, const Dims& g, hipStream_t s) {
+  const int tiles_m = g.T_pad / K1_BM, tiles_n = ceil_div(g.f, K1_BN / 2);
+  gate_up_kernel<<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(H, Wg, Wu, Z, ZT, g, tiles_m,
+                                                              tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
-                         float scale, int B, int T, int T_pad, int d, hipStream_t s) {
-  const int tiles_m = T_pad / 256, tiles_n = ceil_div(d, 256);
-  target_kernel<<<tiles_m * tiles_n * B, kThreads, 0, s>>>(Y, WtT, VT, Vtok, scale, T, T_pad, d,
-                                                           tiles_m, tiles_n);
+                         float vscale, const Dims& g, hipStream_t s) {
+  const int tiles_m = g.T_pad / K2_BM, tiles_n = ceil_div(g.d, K2_BN);
+  target_kernel<<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(Y, WtT, VT, Vtok, vscale, g, tiles_m,
+                                                             tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
-                         bool winit_f32, int64_t winit_bstride, uint16_t* snap,
-                         int64_t snap_bstride, float* Wf, uint16_t* shadow, int B, int T_pad,
-                         int d, int f, int tok_begin, int nk, int steps_per_chunk,
-                         hipStream_t s) {
-  constexpr int BN = 128;
-  const int tiles_m = ceil_div(f, 256), tiles_n = ceil_div(d, BN);
-  const int grid = tiles_m * tiles_n * B;
+                         bool winit_f32, int64_t winit_bstride, int64_t winit_ld,
+                         float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
+                         uint16_t* shadow, const Dims& g, int tok_begin, int nk,
+                         int steps_per_chunk, hipStream_t s) {
+  const int tiles_m = ceil_div(g.f, K3_BM), tiles_n = ceil_div(g.d, K3_BN);
+  const int grid = tiles_m * tiles_n * g.B;
   if (winit_f32)
-    update_kernel<BN, true><<<grid, kThreads, 0, s>>>(ZT, VT, Winit, winit_bstride, snap,
-                                                     snap_bstride, Wf, shadow, T_pad, d, f,
-                                                     tok_begin, nk, steps_per_chunk, tiles_m,
-                                                     tiles_n);
+    update_kernel<true><<<grid, kGemmThreads, 0, s>>>(ZT, VT, Winit, winit_bstride, winit_ld,
+                                                  acc_scale, snap, snap_bstride, Wf, shadow, g,
+                                                  tok_begin, nk, steps_per_chunk, tiles_m,
+                                                  tiles_n);
   else
-    update_kernel<BN, false><<<grid, kThreads, 0, s>>>(ZT, VT, Winit, winit_bstride, snap,
-                                                      snap_bstride, Wf, shadow, T_pad, d, f,
-                                                      tok_begin, nk, steps_per_chunk, tiles_m,
-                                                      tiles_n);
+    update_kernel<false><<<grid, kGemmThreads, 0, s>>>(ZT, VT, Winit, winit_bstride, winit_ld,
+                                                   acc_scale, snap, snap_bstride, Wf, shadow, g,
+                                                   tok_begin, nk, steps_per_chunk, tiles_m,
+                                                   tiles_n);
   return hipGetLastError();
 }
 
 template <int BN>
 static void apply_dispatch(const uint16_t* Z, const uint16_t* snap, int64_t sb, int64_t sc,
-                           void* O, bool out_f32, int B, int T, int d, int f, int tok_begin,
-                           int tok_end, int chunk, hipStream_t s) {
-  const int tiles_m = ceil_div(d, 256), tiles_n = ceil_div(tok_end - tok_begin, BN);
-  const int grid = tiles_m * tiles_n * B;
+                           void* O, bool out_f32, const Dims& g, int tok_begin, int tok_end,
+                           int chunk, hipStream_t s) {
+  const int tiles_m = ceil_div(g.d, 256), tiles_n = ceil_div(tok_end - tok_begin, BN);
+  const int grid = tiles_m * tiles_n * g.B;
   if (out_f32)
-    apply_kernel<BN, true><<<grid, kThreads, 0, s>>>(Z, snap, sb, sc, O, T, d, f, tok_begin,
-                                                     chunk, tiles_m, tiles_n);
+    apply_kernel<BN, true><<<grid, kGemmThreads, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin, chunk,
+                                                     tiles_m, tiles_n);
   else
-    apply_kernel<BN, false><<<grid, kThreads, 0, s>>>(Z, snap, sb, sc, O, T, d, f, tok_begin,
-                                                      chunk, tiles_m, tiles_n);
+    apply_kernel<BN, false><<<grid, kGemmThreads, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin, chunk,
+                                                      tiles_m, tiles_n);
 }
 
 hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bstride,
-                        int64_t snap_cstride, void* O, bool out_f32, int B, int T, int d, int f,
+                        int64_t snap_cstride, void* O, bool out_f32, const Dims& g,
                         int tok_begin, int tok_end, int chunk, hipStream_t s) {
   // The token tile must not straddle a chunk: take the largest of 256, 128,
   // 64 that divides the chunk (the chunk is a multiple of 64).
   if (chunk % 256 == 0)
-    apply_dispatch<256>(Z, snap, snap_bstride, snap_cstride, O, out_f32, B, T, d, f, tok_begin,
-                        tok_end, chunk, s);
+    apply_dispatch<256>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
+                        chunk, s);
   else if (chunk % 128 == 0)
-    apply_dispatch<128>(Z, snap, snap_bstride, snap_cstride, O, out_f32, B, T, d, f, tok_begin,
-                        tok_end, chunk, s);
+    apply_dispatch<128>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
+                        chunk, s);
   else
-    apply_dispatch<64>(Z, snap, snap_bstride, snap_cstride, O, out_f32, B, T, d, f, tok_begin,
-                       tok_end, chunk, s);
+    apply_dispatch<64>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
+                       chunk, s);
   return hipGetLastError();
 }
 
