@@ -2,6 +2,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule prefix|running] [--no-cpu-baseline]
+    python bench.py --summarize DIR [--fetch DIR2 --write DIR3]
+                    --summary-out FILE.md --command "..."
+
+The second form turns rocprofv3 output (a --kernel-trace --stats run, and
+optionally --pmc FETCH_SIZE / WRITE_SIZE runs) of the first form into the
+text summaries kept under profiles/.
 
 One step is one call of ttt_layer_forward on the whole workload (gate/up,
 target, update with per-chunk snapshots, apply), with inputs resident in HBM.
@@ -30,6 +36,13 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "test_layer_gate_amd", "csrc", "ttt_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CALIB_BYTES = 256 << 20      # the known-size copy run before the timed region
+# library timing names -> kernel names in rocprofv3 traces
+KERNEL_NAMES = {"gate_up": "gate_up_kernel", "target": "target_kernel",
+                "update_prefix": "update_kernel", "update_running": "update_kernel",
+                "apply": "apply_kernel", "conv": "conv_kernel",
+                "transpose_w_target": "transpose_kernel", "cast_bf16": "cast_kernel",
+                "calibration_copy": "calibration_copy_kernel"}
 
 
 def kernel_work(name, cfg, T_pad):
@@ -96,6 +109,74 @@ def cpu_baseline(cfg, x, budget_s=15.0):
                       f"({j * C} tokens, batch row 0) of {cfg.name}; {tj:.1f} s"}
 
 
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find(d, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[-1]
+
+
+def summarize(args):
+    """Write a markdown summary of rocprofv3 results (and, with --fetch and
+    --write, the per-launch HBM traffic record used by the bench line)."""
+    stats = _read_csv(_find(args.summarize, "kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel summary: {args.title}", "",
+             f"Command: `{args.command}`", "",
+             f"Kernel source sha256[:16]: `{source_hash()}`", "",
+             "| kernel | calls | avg us | min us | max us | total ms | share |",
+             "|---|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("| {} | {} | {:.1f} | {:.1f} | {:.1f} | {:.3f} | {:.1f}% |".format(
+            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    if args.fetch and args.write:
+        per = {}
+        for which, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
+            for r in _read_csv(_find(d, "counter_collection.csv")):
+                if r["Counter_Name"] != which:
+                    continue
+                per.setdefault(r["Kernel_Name"], {}).setdefault(which, []).append(
+                    float(r["Counter_Value"]) * 1024.0)
+        cal = per.get("calibration_copy_kernel")
+        if not cal:
+            raise SystemExit("no calibration_copy_kernel dispatch in the counter runs")
+        f_fac = CALIB_BYTES / (sum(cal["FETCH_SIZE"]) / len(cal["FETCH_SIZE"]))
+        w_fac = CALIB_BYTES / (sum(cal["WRITE_SIZE"]) / len(cal["WRITE_SIZE"]))
+        lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE)", "",
+                  f"Fetch command: `{args.fetch_command}`", "",
+                  f"Write command: `{args.write_command}`", "",
+                  f"Calibration: calibration_copy_kernel moves {CALIB_BYTES} bytes each way; "
+                  f"counter-to-byte factors: fetch {f_fac:.4f}, write {w_fac:.4f}.", "",
+                  "| kernel | dispatches | fetch MB | write MB | HBM MB (scaled) |",
+                  "|---|---|---|---|---|"]
+        rec = {"kernel_source_sha256_16": source_hash(), "workload": args.workload,
+               "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {args.workload: {}}}
+        for name, v in sorted(per.items()):
+            fe = sum(v.get("FETCH_SIZE", [0])) / max(len(v.get("FETCH_SIZE", [])), 1)
+            wr = sum(v.get("WRITE_SIZE", [0])) / max(len(v.get("WRITE_SIZE", [])), 1)
+            tot = fe * f_fac + wr * w_fac
+            lines.append(f"| {name} | {len(v.get('FETCH_SIZE', []))} | {fe / 1e6:.1f} | "
+                         f"{wr / 1e6:.1f} | {tot / 1e6:.1f} |")
+            for lib_name, kname in KERNEL_NAMES.items():
+                if kname == name:
+                    rec["kernels"][args.workload][lib_name] = {
+                        "hbm_bytes_per_launch": tot, "fetch_bytes": fe * f_fac,
+                        "write_bytes": wr * w_fac}
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(rec, fh, indent=1)
+    os.makedirs(os.path.dirname(args.summary_out) or ".", exist_ok=True)
+    with open(args.summary_out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +185,18 @@ def main():
     ap.add_argument("--workload", default=synth.BENCH_CONFIG, choices=sorted(synth.CONFIGS))
     ap.add_argument("--schedule", default="prefix", choices=["prefix", "running"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
+    ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
+    ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory")
+    ap.add_argument("--summary-out")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--fetch-command", default="")
+    ap.add_argument("--write-command", default="")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -134,6 +226,13 @@ def main():
                           t["W_target"], cfg.eta, cfg.chunk, schedule=args.schedule,
                           out=O, W_down_final=Wf, workspace=ws)
 
+    # A plain copy of known size, outside the timed region: the reference that
+    # converts hardware traffic counters to bytes in profiled runs.
+    calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    calib_dst = torch.empty_like(calib_src)
+    ttt.copy_calibration(calib_dst, calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -181,7 +280,7 @@ def main():
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "bf16+fp16", "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "seq_len": T, "chunk": cfg.chunk,
                    "d_model": d, "d_ff": f, "conv_k": cfg.conv_k, "eta": cfg.eta,
                    "schedule": args.schedule},

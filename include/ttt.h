@@ -149,6 +149,13 @@ typedef struct ttt_kernel_stat {
 } ttt_kernel_stat;
 
 ttt_status ttt_profile_enable(int32_t on); /* on: clears the record */
+
+/* Copies `bytes` bytes (a multiple of 16; both pointers 16-byte aligned,
+ * not overlapping) with one plain streaming kernel, named
+ * calibration_copy_kernel in profiles. It moves a known number of bytes, so
+ * hardware traffic counters read on it convert counter units to bytes for
+ * the layer's kernels measured in the same run. */
+ttt_status ttt_copy_calibration(void* dst, const void* src, size_t bytes, void* stream);
 int32_t ttt_profile_read(ttt_kernel_stat* out, int32_t max_entries);
 
 #ifdef __cplusplus

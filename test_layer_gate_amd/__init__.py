@@ -11,6 +11,7 @@ built, or a call fails, an exception is raised.
 from ._binding import (  # noqa: F401
     LIB_PATH,
     TTTError,
+    copy_calibration,
     gated_activation,
     layer_forward,
     lib,
@@ -22,5 +23,6 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["layer_forward", "gated_activation", "lm_target", "workspace_size",
+           "copy_calibration",
            "make_desc", "profile_enable", "profile_read", "TTTError", "lib",
            "LIB_PATH"]

@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_last_error.argtypes = []
     L.ttt_last_error.restype = ctypes.c_char_p
     L.ttt_profile_enable.argtypes = [ctypes.c_int32]
+    L.ttt_copy_calibration.argtypes = [_P, _P, _S, _P]
+    L.ttt_copy_calibration.restype = ctypes.c_int
     L.ttt_profile_read.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int32]
     L.ttt_profile_read.restype = ctypes.c_int32
     _lib = L
@@ -226,3 +228,13 @@ def profile_read() -> dict:
     arr = (KernelStat * cap)()
     n = min(lib().ttt_profile_read(arr, cap), cap)
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
+
+
+def copy_calibration(dst, src, *, stream=None):
+    """dst <- src (same byte size, a multiple of 16) with the library's plain
+    copy kernel, a known-size reference for hardware traffic counters."""
+    _require_cuda(dst, src)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("dst and src must have the same size in bytes")
+    _check(lib().ttt_copy_calibration(_ptr(dst), _ptr(src), n, _stream(stream)))

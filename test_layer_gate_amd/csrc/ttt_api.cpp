@@ -372,8 +372,6 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
   TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgb, Wub, Z, ZT, D, s));
   TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, vscale, D, s));
 
-  const int steps_per_chunk = (int)(g.C / 64);
-  const int nk_total = (int)((g.T + 63) / 64);
   const int64_t snap_cstride = g.d * D.ld_s;
   if (!g.running) {
     // Materialised exclusive prefix: snapshot i = bf16(W^(i)) for every chunk,
@@ -381,7 +379,7 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
     TTT_LAUNCH("update_prefix", s,
                tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale, snap,
                                    g.nchunks * snap_cstride, W_down_final, nullptr, D, 0,
-                                   nk_total, steps_per_chunk, s));
+                                   (int)g.T, (int)g.C, s));
     TTT_LAUNCH("apply", s,
                tttk::launch_apply(Z, snap, g.nchunks * snap_cstride, snap_cstride, O, g.act_f32,
                                   D, 0, (int)g.T, (int)g.C, s));
@@ -389,16 +387,15 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
     // Running state: W_down_final holds W^(i) in fp32, `snap` its bf16 copy.
     TTT_LAUNCH("update_running", s,
                tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale,
-                                   nullptr, 0, W_down_final, snap, D, 0, 0, steps_per_chunk, s));
+                                   nullptr, 0, W_down_final, snap, D, 0, 0, (int)g.C, s));
     for (int64_t i = 0; i < g.nchunks; ++i) {
       const int t0 = (int)(i * g.C), t1 = (int)std::min<int64_t>(g.T, (i + 1) * g.C);
       TTT_LAUNCH("apply", s,
                  tttk::launch_apply(Z, snap, snap_cstride, 0, O, g.act_f32, D, t0, t1, (int)g.C,
                                     s));
-      const int nk = (t1 - t0 + 63) / 64;
       TTT_LAUNCH("update_running", s,
                  tttk::launch_update(ZT, VT, W_down_final, true, df, g.f, acc_scale, nullptr, 0,
-                                     W_down_final, snap, D, t0, nk, steps_per_chunk, s));
+                                     W_down_final, snap, D, t0, t1 - t0, (int)g.C, s));
     }
   }
   return TTT_OK;
@@ -486,6 +483,16 @@ ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0, const void* conv_
                                g.pad_chunk, s));
   TTT_LAUNCH("target", s,
              tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), 1.0f, g.dims, s));
+  return TTT_OK;
+}
+
+ttt_status ttt_copy_calibration(void* dst, const void* src, size_t bytes, void* stream) {
+  TTT_TRY(check_ptr(dst, "dst"));
+  TTT_TRY(check_ptr(src, "src"));
+  if (bytes % 16 != 0) return fail(TTT_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  TTT_TRY(check_aliasing({range_of("src", src, bytes)}, {range_of("dst", dst, bytes)}));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TTT_LAUNCH("calibration_copy", s, tttk::launch_copy(src, dst, (int64_t)bytes, s));
   return TTT_OK;
 }
 

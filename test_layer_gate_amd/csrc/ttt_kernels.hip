@@ -35,6 +35,8 @@ constexpr int kThreads = 256;      // small kernels
 constexpr int kGemmWaves = 8;      // GEMM workgroups: 8 wave64s, 2 per SIMD
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kBK = 64;            // K elements per LDS stage (128 bytes per row)
+constexpr int kSub = kBK / 16;     // MFMA K-substeps per stage
+constexpr int kMaxStages = 3;      // LDS stages per workgroup (all but one in flight)
 constexpr int kRsrcWord3 = 0x00020000;
 
 // ---------------------------------------------------------------- helpers
@@ -60,7 +62,11 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return (uint32_t)f16_rne(lo) | ((uint32_t)f16_rne(hi) << 16);
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU(x) = x * sigmoid(x), with the hardware reciprocal (1 ulp) in place of
+// a full division.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 struct Bf16Mma {
   static __device__ __forceinline__ f32x16 mma(const uint4& a, const uint4& b, const f32x16& c) {
@@ -76,11 +82,12 @@ struct F16Mma {
   }
 };
 
-// LDS tile of `rows` x 64 16-bit elements, 128 B per row. The eight 16-byte
-// chunks of a row are XOR-permuted by swz(row), so that the 32 rows of one
-// fragment read fall on distinct banks. swz depends on row % 32 only, so a
-// lane's permutation is the same for every 32-row fragment it reads and each
-// read is one per-lane register plus an immediate offset.
+// LDS tile of `rows` x 64 16-bit elements, 128 B per row, eight 16-byte
+// chunks. Chunk kc of row r sits at physical chunk kc ^ swz(r), so that the
+// 32 rows of one fragment read (and any 8 or 16 consecutive ones) fall on
+// distinct banks. swz depends on row % 32 only, so a lane's permutation is
+// the same for every 32-row fragment it reads and each read is one per-lane
+// register plus an immediate offset.
 __device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 3)) & 7; }
 __device__ __forceinline__ int lds_off(int row, int kc) { return row * kBK + ((kc ^ swz(row)) << 3); }
 
@@ -88,42 +95,97 @@ __device__ __forceinline__ uint4 lds_frag(const u16* lds, int row, int kc) {
   return *reinterpret_cast<const uint4*>(lds + lds_off(row, kc));
 }
 
-// One operand tile of ROWS rows. Each of the 8 waves issues ROWS / 64
-// direct-to-LDS loads per K step; load i of wave w fills LDS rows
-// [(8i + w) * 8, +8), lane l the 16 bytes at physical chunk l % 8 of row
-// l / 8, which is the row's logical chunk (l % 8) ^ swz(row). The per-lane
-// byte offsets are fixed; the K step enters as the scalar offset.
+// One operand tile of ROWS rows (a multiple of 8), loaded in blocks of 8
+// rows: one direct-to-LDS load fills block b, lane l the 16 bytes at
+// physical chunk l % 8 of row 8b + l / 8, which is that row's logical chunk
+// (l % 8) ^ swz(row). Every wave issues NI = ceil(blocks / 8) loads per K
+// step, load i of wave w covering block (8i + w) mod blocks; when the blocks
+// do not divide evenly the extra loads repeat a block, writing the same
+// bytes to the same place. The per-lane byte offsets are fixed; the K step
+// enters as the scalar offset.
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of `bytes` bytes at `base` (raw, no stride): reads at
+// offsets >= bytes return zero.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r.x = (uint32_t)a;
+  r.y = (uint32_t)(a >> 32) & 0xffffu;
+  r.z = bytes;
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// Direct-to-LDS loads, written as inline asm so that the compiler does not
+// track them: it would otherwise wait for every such load before any later
+// LDS read, which serialises the pipeline. They have no register results;
+// completion is tracked only by the explicit vmcnt waits in the pipeline.
+// M0 holds the LDS byte address of lane 0; one wait state separates the M0
+// write from the load.
+__device__ __forceinline__ void lds_dma_b128(const u32x4& rsrc, uint32_t lds_addr,
+                                             uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+
+// LDS byte address of p, which must be the same in every lane of the wave
+// (it becomes M0).
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
 template <int ROWS>
 struct DmaTile {
-  static constexpr int NI = ROWS / (8 * kGemmWaves);
-  static_assert(ROWS % (8 * kGemmWaves) == 0, "rows");
+  static constexpr int NB = ROWS / 8;
+  static constexpr int NI = (NB + kGemmWaves - 1) / kGemmWaves;
+  static_assert(ROWS % 8 == 0, "rows");
   uint32_t voff[NI];
-  __amdgpu_buffer_rsrc_t rsrc;
+  int block[NI];
+  u32x4 rsrc;
   __device__ __forceinline__ void init(const u16* base, int64_t ld, int rows_valid, int wave,
                                        int lane) {
     int64_t bytes = rows_valid > 0 ? (int64_t)rows_valid * ld * 2 : 0;
     if (bytes > 0xffffffffLL) bytes = 0xffffffffLL;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(base), (short)0, (int)(uint32_t)bytes,
-                                             kRsrcWord3);
+    rsrc = make_rsrc(base, (uint32_t)bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = (kGemmWaves * i + wave) * 8 + (lane >> 3);
+      block[i] = (kGemmWaves * i + wave) % NB;
+      const int row = block[i] * 8 + (lane >> 3);
       const int kc = (lane & 7) ^ swz(row);
       voff[i] = (uint32_t)((int64_t)row * ld * 2 + kc * 16);
     }
   }
-  __device__ __forceinline__ void issue(u16* lds_region, int wave, uint32_t soff) const {
+  __device__ __forceinline__ void issue(u16* lds_region, uint32_t soff) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (lds_ptr_t)(lds_region + (kGemmWaves * i + wave) * 8 * kBK), 16, voff[i], soff,
-          0, 0);
+      lds_dma_b128(rsrc, lds_addr_of(lds_region + block[i] * 8 * kBK), voff[i], soff);
   }
 };
 
-__device__ __forceinline__ void wait_dma_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+// The LDS stages of a GEMM workgroup.
+struct LdsStages {
+  u16* s[kMaxStages];
+};
+
+#define TTT_STAGE_ELEMS(BM_, BN_, NST_, i) ((i) < (NST_) ? ((BM_) + (BN_)) * kBK : 8)
+#define TTT_GEMM_LDS(var, BM_, BN_, NST_)                                                        \
+  static_assert((NST_) >= 2 && (NST_) <= kMaxStages, "stages");                                  \
+  __shared__ __attribute__((aligned(16))) u16 var##0[TTT_STAGE_ELEMS(BM_, BN_, NST_, 0)];        \
+  __shared__ __attribute__((aligned(16))) u16 var##1[TTT_STAGE_ELEMS(BM_, BN_, NST_, 1)];        \
+  __shared__ __attribute__((aligned(16))) u16 var##2[TTT_STAGE_ELEMS(BM_, BN_, NST_, 2)];        \
+  const LdsStages var = {{var##0, var##1, var##2}};
+
+// Waits until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order) and all of its LDS reads have
+// returned, then joins the workgroup barrier. This replaces __syncthreads()
+// in the pipeline: that one carries a release fence, which waits for every
+// outstanding load, including the stages meant to stay in flight. The
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // Maps the linear workgroup id to (batch, tile_m, tile_n). Workgroups are
@@ -185,17 +247,16 @@ struct Layout {
 // gate and up projections); wave wn then owns the same TN/2 * 32 columns of
 // each, in acc[.][0, TN/2) (B0) and acc[.][TN/2, TN) (B1).
 // hook(kt, acc) runs at the start of K step kt, when acc holds steps < kt.
-// lds0 / lds1 are the two LDS stages, each (BM + BN) * 64 elements, kept as
-// distinct arrays so the compiler can tell a stage being filled from the
-// stage being read.
-template <int BM, int BN, int WGM, class Op, bool SPLITB, class Hook>
+// nk is the number of 64-wide K steps; L holds NST LDS stages, each
+// (BM + BN) * 64 elements.
+template <int BM, int BN, int WGM, int NST, class Op, bool SPLITB, class Hook>
 __device__ __forceinline__ void gemm_core(const u16* __restrict__ A, int64_t lda, int a_valid,
                                           const u16* __restrict__ B0,
                                           const u16* __restrict__ B1, int64_t ldb, int b_valid,
-                                          int nk, f32x16* acc, u16* lds0, u16* lds1,
+                                          int nk, f32x16* acc, const LdsStages& L,
                                           const Hook& hook) {
-  using L = Layout<BM, BN, WGM>;
-  constexpr int TM = L::TM, TN = L::TN, WGN = L::WGN;
+  using Lay = Layout<BM, BN, WGM>;
+  constexpr int TM = Lay::TM, TN = Lay::TN, WGN = Lay::WGN;
   constexpr int BROWS = SPLITB ? BN / 2 : BN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / WGN, wn = w % WGN;
@@ -203,16 +264,16 @@ __device__ __forceinline__ void gemm_core(const u16* __restrict__ A, int64_t lda
 
   DmaTile<BM> ta;
   DmaTile<BROWS> tb0;
-  DmaTile<SPLITB ? BN / 2 : 64> tb1;
+  DmaTile<SPLITB ? BN / 2 : 8> tb1;
   ta.init(A, lda, a_valid, w, lane);
   tb0.init(B0, ldb, b_valid, w, lane);
   if constexpr (SPLITB) tb1.init(B1, ldb, b_valid, w, lane);
 
   auto issue = [&](u16* stage, int kt) {
     const uint32_t soff = (uint32_t)kt * (kBK * 2);
-    ta.issue(stage, w, soff);
-    tb0.issue(stage + BM * kBK, w, soff);
-    if constexpr (SPLITB) tb1.issue(stage + BM * kBK + (BN / 2) * kBK, w, soff);
+    ta.issue(stage, soff);
+    tb0.issue(stage + BM * kBK, soff);
+    if constexpr (SPLITB) tb1.issue(stage + BM * kBK + (BN / 2) * kBK, soff);
   };
 
   // Rows of this lane's fragments within the stage.
@@ -231,43 +292,74 @@ __device__ __forceinline__ void gemm_core(const u16* __restrict__ A, int64_t lda
   }
   const int khalf = lane >> 5;
 
-  auto compute = [&](const u16* st) {
-    uint4 fa[2][TM], fb[2][TN];
+  // Software pipeline over NST LDS stages. While stage kt is read, the
+  // loads of stages kt + 1 .. kt + NST - 1 are in flight; the load of stage
+  // kt + NST - 1 goes into the stage read at kt - 1, which the barrier ending
+  // step kt - 1 released. A stage holds four 16-wide substeps: the fragments
+  // of substep s + 1 are read between the MFMAs of substep s, and the MFMAs
+  // of the last substep run after the barrier, between the reads of the next
+  // stage's first substep.
+  constexpr int R = NST - 1;  // load distance in stages
+  uint4 fa[2][TM], fb[2][TN];
+  auto load_sub = [&](const u16* st, int sub, int set) {
 #pragma unroll
-    for (int m = 0; m < TM; ++m) fa[0][m] = lds_frag(st, arow[m], khalf);
+    for (int m = 0; m < TM; ++m) fa[set][m] = lds_frag(st, arow[m], 2 * sub + khalf);
 #pragma unroll
-    for (int n = 0; n < TN; ++n) fb[0][n] = lds_frag(st, brow[n], khalf);
+    for (int n = 0; n < TN; ++n) fb[set][n] = lds_frag(st, brow[n], 2 * sub + khalf);
+  };
+  auto mma_sub = [&](int set) {
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int cb = s & 1, nb = cb ^ 1;
-      if (s + 1 < kBK / 16) {
+    for (int m = 0; m < TM; ++m)
 #pragma unroll
-        for (int m = 0; m < TM; ++m) fa[nb][m] = lds_frag(st, arow[m], 2 * (s + 1) + khalf);
+      for (int n = 0; n < TN; ++n)
+        acc[m * TN + n] = Op::mma(fa[set][m], fb[set][n], acc[m * TN + n]);
+  };
+  constexpr int NPS = DmaTile<BM>::NI + (SPLITB ? 2 * DmaTile<BN / 2>::NI : DmaTile<BN>::NI);
+  // The loads issued after those of stage kt + 1 are the (R - 1) stage
+  // loads that follow it.
+  constexpr int WAIT = (R - 1) * NPS;
+  // One MFMA, then one fragment read while reads remain, then loads.
+  auto interleave = [&](int nvmem) {
 #pragma unroll
-        for (int n = 0; n < TN; ++n) fb[nb][n] = lds_frag(st, brow[n], 2 * (s + 1) + khalf);
-      }
-#pragma unroll
-      for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int n = 0; n < TN; ++n)
-          acc[m * TN + n] = Op::mma(fa[cb][m], fb[cb][n], acc[m * TN + n]);
+    for (int i = 0; i < TM * TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < nvmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   };
-
-  issue(lds0, 0);
-  wait_dma_and_barrier();
-  for (int kt = 0; kt < nk; kt += 2) {
-    hook(kt, acc);
-    if (kt + 1 < nk) issue(lds1, kt + 1);
-    compute(lds0);
-    wait_dma_and_barrier();
-    if (kt + 1 < nk) {
-      hook(kt + 1, acc);
-      if (kt + 2 < nk) issue(lds0, kt + 2);
-      compute(lds1);
-      wait_dma_and_barrier();
+  // Loads and reads past the last stage are unconditional (clamped to the
+  // last stage, in bounds, into released stages; reads of stale LDS) so a
+  // step's MFMA section stays one basic block; nothing uses their results.
+  auto step = [&](const u16* cur, const u16* nxt, u16* refill, int kt) {
+    issue(refill, min(kt + R, nk - 1));
+    load_sub(cur, 1, 1);
+    mma_sub(0);
+    interleave(NPS);
+#pragma unroll
+    for (int sub = 1; sub + 1 < kSub; ++sub) {
+      load_sub(cur, sub + 1, (sub + 1) & 1);
+      mma_sub(sub & 1);
+      interleave(0);
     }
+    wait_and_barrier<WAIT>();  // stage kt + 1 landed everywhere; stage kt released
+    load_sub(nxt, 0, 0);
+    mma_sub((kSub - 1) & 1);
+    interleave(0);
+    if (kt + 1 < nk) hook(kt + 1, acc);
+  };
+
+  hook(0, acc);
+#pragma unroll
+  for (int i = 0; i < R; ++i) issue(L.s[i], min(i, nk - 1));
+  wait_and_barrier<WAIT>();
+  load_sub(L.s[0], 0, 0);
+  for (int kt = 0; kt < nk; kt += NST) {
+#pragma unroll
+    for (int i = 0; i < NST; ++i)
+      if (kt + i < nk) step(L.s[i], L.s[(i + 1) % NST], L.s[(i + NST - 1) % NST], kt + i);
   }
+  // Drain the trailing loads before the caller reuses LDS.
+  wait_and_barrier<0>();
 }
 
 // Output coordinates of register group q (registers 4q..4q+3) of MFMA tile
@@ -290,28 +382,25 @@ struct Frag {
 // ------------------------------------------------ gate/up + SiLU*mul (K1)
 // M = tokens (256), N = 128 columns of Wg and the same 128 of Wu, K = d.
 // Waves 2 x 4: each wave owns 128 tokens x 32 columns of Wg and of Wu.
-constexpr int K1_BM = 256, K1_BN = 256, K1_WGM = 2, K1_LDZ = K1_BN / 2 + 8;
+constexpr int K1_BM = 256, K1_BN = 256, K1_WGM = 2, K1_NST = 2, K1_LDZ = K1_BN / 2 + 8;
 
 __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
     const u16* __restrict__ H, const u16* __restrict__ Wg, const u16* __restrict__ Wu,
     u16* __restrict__ Z, u16* __restrict__ ZT, Dims g, int tiles_m, int tiles_n) {
   using L = Layout<K1_BM, K1_BN, K1_WGM>;
   static_assert(L::TN == 2, "one gate and one up tile per wave");
-  __shared__ __attribute__((aligned(16))) u16 lds0[(K1_BM + K1_BN) * kBK];
-  __shared__ __attribute__((aligned(16))) u16 lds1[(K1_BM + K1_BN) * kBK];
+  TTT_GEMM_LDS(lds, K1_BM, K1_BN, K1_NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K1_BM, j0 = ti.tn * (K1_BN / 2);
   const int d = g.d, f = g.f;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  gemm_core<K1_BM, K1_BN, K1_WGM, Bf16Mma, true>(
+  gemm_core<K1_BM, K1_BN, K1_WGM, K1_NST, Bf16Mma, true>(
       H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0), Wg + (int64_t)j0 * d,
-      Wu + (int64_t)j0 * d, d, min(K1_BN / 2, f - j0), d / kBK, &acc[0][0], lds0, lds1,
-      NoHook{});
+      Wu + (int64_t)j0 * d, d, min(K1_BN / 2, f - j0), d / kBK, &acc[0][0], lds, NoHook{});
   const Frag<L> fr;
-  // Token-major Z goes through LDS (rows 0-127 in lds0, 128-255 in lds1) so
-  // that its stores are whole 16-byte row segments.
-  u16* sZ = fr.wm == 0 ? lds0 : lds1;
+  // Token-major Z goes through LDS (rows 0-127 in stage 0, 128-255 in stage
+  // 1) so that its stores are whole 16-byte row segments.
   const int jl = fr.wn * 32 + (fr.lane & 31);
   const int j = j0 + jl;
 #pragma unroll
@@ -326,8 +415,9 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
       if (ZT != nullptr && j < f)
         *reinterpret_cast<uint2*>(ZT + ((int64_t)ti.b * f + j) * g.ld_t + t) =
             make_uint2(pack_f16(z[0], z[1]), pack_f16(z[2], z[3]));
+      u16* sZ = (fr.wm == 0 ? lds.s[0] : lds.s[1]) + tl * K1_LDZ + jl;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sZ[(tl + e) * K1_LDZ + jl] = bf16_rne(z[e]);
+      for (int e = 0; e < 4; ++e) sZ[e * K1_LDZ] = bf16_rne(z[e]);
     }
   if (Z == nullptr) return;
   __syncthreads();
@@ -335,7 +425,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
   for (int i = 0; i < 8; ++i) {
     const int c = threadIdx.x + i * kGemmThreads;
     const int row = c >> 4, cc = c & 15;
-    const u16* src = (row < 128 ? lds0 : lds1) + (row & 127) * K1_LDZ + cc * 8;
+    const u16* src = lds.s[i >> 2] + (row & 127) * K1_LDZ + cc * 8;  // row >> 7 == i >> 2
     const int t = t0 + row, jj = j0 + cc * 8;
     if (t < g.T && jj < f)
       *reinterpret_cast<uint4*>(Z + ((int64_t)ti.b * g.T + t) * g.ld_z + jj) =
@@ -345,22 +435,21 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
 
 // ------------------------------------------------------ target GEMM (K2)
 // M = tokens (256), N = output channels (256), K = d; fp16 operands.
-constexpr int K2_BM = 256, K2_BN = 256, K2_WGM = 2;
+constexpr int K2_BM = 256, K2_BN = 256, K2_WGM = 2, K2_NST = 2;
 
 __global__ __launch_bounds__(kGemmThreads) void target_kernel(
     const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
     u16* __restrict__ Vtok, float vscale, Dims g, int tiles_m, int tiles_n) {
   using L = Layout<K2_BM, K2_BN, K2_WGM>;
-  __shared__ __attribute__((aligned(16))) u16 lds0[(K2_BM + K2_BN) * kBK];
-  __shared__ __attribute__((aligned(16))) u16 lds1[(K2_BM + K2_BN) * kBK];
+  TTT_GEMM_LDS(lds, K2_BM, K2_BN, K2_NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K2_BM, c0 = ti.tn * K2_BN;
   const int d = g.d;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  gemm_core<K2_BM, K2_BN, K2_WGM, F16Mma, false>(
+  gemm_core<K2_BM, K2_BN, K2_WGM, K2_NST, F16Mma, false>(
       Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM, WtT + (int64_t)c0 * g.ld_y,
-      nullptr, g.ld_y, min(K2_BN, d - c0), d / kBK, &acc[0][0], lds0, lds1, NoHook{});
+      nullptr, g.ld_y, min(K2_BN, d - c0), d / kBK, &acc[0][0], lds, NoHook{});
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -386,11 +475,11 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 }
 
 // ------------------------------------------ fast-weight update (K3)
-// M = d_ff (192), N = d_model (256), K = tokens; fp16 operands. acc starts
+// M = d_ff (256), N = d_model (128), K = tokens; fp16 operands. acc starts
 // at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
 // time; at every chunk start the state before that chunk is stored as a
 // bf16 snapshot (the exclusive prefix).
-constexpr int K3_BM = 192, K3_BN = 256, K3_WGM = 2;
+constexpr int K3_BM = 256, K3_BN = 128, K3_WGM = 4, K3_NST = 3;
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
 // into a [d][ld] bf16 matrix (row c = d_model index, column j = d_ff index).
@@ -426,8 +515,7 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
     int tok_begin, int nk, int steps_per_chunk, int tiles_m, int tiles_n) {
   using L = Layout<K3_BM, K3_BN, K3_WGM>;
   constexpr int TM = L::TM, TN = L::TN;
-  __shared__ __attribute__((aligned(16))) u16 lds0[(K3_BM + K3_BN) * kBK];
-  __shared__ __attribute__((aligned(16))) u16 lds1[(K3_BM + K3_BN) * kBK];
+  TTT_GEMM_LDS(lds, K3_BM, K3_BN, K3_NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int j0 = ti.tm * K3_BM, c0 = ti.tn * K3_BN;
   const int d = g.d, f = g.f;
@@ -468,10 +556,10 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
     if (snap_b != nullptr && kt % steps_per_chunk == 0)
       snapshot(snap_b + (int64_t)(kt / steps_per_chunk) * chunk_stride, a);
   };
-  gemm_core<K3_BM, K3_BN, K3_WGM, F16Mma, false>(
+  gemm_core<K3_BM, K3_BN, K3_WGM, K3_NST, F16Mma, false>(
       ZT + ((int64_t)ti.b * f + j0) * g.ld_t + tok_begin, g.ld_t, min(K3_BM, f - j0),
       VT + ((int64_t)ti.b * d + c0) * g.ld_t + tok_begin, nullptr, g.ld_t, min(K3_BN, d - c0), nk,
-      &acc[0][0], lds0, lds1, hook);
+      &acc[0][0], lds, hook);
 
   float* wf_b = Wf + (int64_t)ti.b * d * f;
 #pragma unroll
@@ -506,18 +594,17 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int BM = 256, WGM = ApplyCfg<BN>::WGM;
   using L = Layout<BM, BN, WGM>;
-  __shared__ __attribute__((aligned(16))) u16 lds0[(BM + BN) * kBK];
-  __shared__ __attribute__((aligned(16))) u16 lds1[(BM + BN) * kBK];
+  TTT_GEMM_LDS(lds, BM, BN, 2)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int c0 = ti.tm * BM, t0 = tok_begin + ti.tn * BN;
   const int i = t0 / chunk;
   const int d = g.d, f = g.f, T = g.T;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  gemm_core<BM, BN, WGM, Bf16Mma, false>(
+  gemm_core<BM, BN, WGM, 2, Bf16Mma, false>(
       snap + ti.b * snap_bstride + i * snap_cstride + (int64_t)c0 * g.ld_s, g.ld_s,
       min(BM, d - c0), Z + ((int64_t)ti.b * T + t0) * g.ld_z, nullptr, g.ld_z, min(BN, T - t0),
-      f / kBK, &acc[0][0], lds0, lds1, NoHook{});
+      f / kBK, &acc[0][0], lds, NoHook{});
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -621,11 +708,28 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
                  pack_f16(acc[6], acc[7]));
 }
 
+__global__ __launch_bounds__(kThreads) void calibration_copy_kernel(const uint4* __restrict__ src,
+                                                                    uint4* __restrict__ dst,
+                                                                    int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads)
+    dst[i] = src[i];
+}
+
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
 // ------------------------------------------------------------ launchers
+
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  const int blocks = (int)std::min<int64_t>((n16 + kThreads - 1) / kThreads, 8192);
+  if (blocks > 0)
+    calibration_copy_kernel<<<blocks, kThreads, 0, s>>>(static_cast<const uint4*>(src),
+                                                        static_cast<uint4*>(dst), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
   const int64_t n4 = n / 4;
@@ -676,8 +780,9 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
 hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
                          bool winit_f32, int64_t winit_bstride, int64_t winit_ld,
                          float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
-                         uint16_t* shadow, const Dims& g, int tok_begin, int nk,
-                         int steps_per_chunk, hipStream_t s) {
+                         uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
+                         int chunk, hipStream_t s) {
+  const int nk = (tok_count + kBK - 1) / kBK, steps_per_chunk = chunk / kBK;
   const int tiles_m = ceil_div(g.f, K3_BM), tiles_n = ceil_div(g.d, K3_BN);
   const int grid = tiles_m * tiles_n * g.B;
   if (winit_f32)

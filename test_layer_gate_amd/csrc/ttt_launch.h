@@ -45,6 +45,9 @@ inline Dims make_dims(int B, int T, int d, int f) {
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 
+// dst[0, bytes) = src[0, bytes) with a plain 16-byte-per-thread copy.
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
 // dst[c * ld_dst + r] = fp16(src[r][c]) for a rows x cols matrix (bf16 or fp32).
 hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, int rows,
                                 int cols, int64_t ld_dst, hipStream_t s);
@@ -63,18 +66,19 @@ hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wg, const uint16_t*
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
                          float vscale, const Dims& g, hipStream_t s);
 
-// Fast-weight update over tokens [tok_begin, tok_begin + 64 * nk).
-// acc = acc_scale * Winit; for each 64-token step kt: if snap != null and
-// kt % steps_per_chunk == 0, snapshot kt / steps_per_chunk = bf16(acc /
-// acc_scale); acc += ZT-slice^T-contracted-with VT-slice. Then Wf = acc /
-// acc_scale and, if shadow != null, shadow = bf16(acc / acc_scale).
+// Fast-weight update over tokens [tok_begin, tok_begin + tok_count), in
+// 32-token steps (columns past T read as zero). acc = acc_scale * Winit;
+// before each step that starts a chunk (every chunk / 32 steps), if snap !=
+// null, that chunk's snapshot = bf16(acc / acc_scale); then acc += the
+// step's ZT x VT contraction over tokens. Finally Wf = acc / acc_scale and,
+// if shadow != null, shadow = bf16(acc / acc_scale). tok_count may be 0.
 // Winit element (b, c, j) is at b * winit_bstride + c * winit_ld + j.
 // acc_scale must be a power of two (the scalings are then exact). nk may be 0.
 hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
                          bool winit_f32, int64_t winit_bstride, int64_t winit_ld,
                          float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
-                         uint16_t* shadow, const Dims& g, int tok_begin, int nk,
-                         int steps_per_chunk, hipStream_t s);
+                         uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
+                         int chunk, hipStream_t s);
 
 // O[b][t] = Z[b][t] W_i^T for tokens t in [tok_begin, tok_end), where W_i is
 // the bf16 state at snap + b * snap_bstride + (t / chunk) * snap_cstride,
