@@ -32,7 +32,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;      // small kernels
-constexpr int kGemmWaves = 8;      // GEMM workgroups: 8 wave64s, 2 per SIMD
+#ifndef TTT_GEMM_WAVES
+#define TTT_GEMM_WAVES 8
+#endif
+constexpr int kGemmWaves = TTT_GEMM_WAVES;  // wave64s per GEMM workgroup (4 or 8)
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kBK = 64;            // K elements per LDS stage (128 bytes per row)
 constexpr int kSub = kBK / 16;     // MFMA K-substeps per stage
@@ -110,10 +113,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // offsets >= bytes return zero.
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
+  // The descriptor must sit in SGPRs: every lane holds the same value.
   u32x4 r;
-  r.x = (uint32_t)a;
-  r.y = (uint32_t)(a >> 32) & 0xffffu;
-  r.z = bytes;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
   r.w = kRsrcWord3;
   return r;
 }
@@ -383,12 +387,14 @@ struct Frag {
 // M = tokens (256), N = 128 columns of Wg and the same 128 of Wu, K = d.
 // Waves 2 x 4: each wave owns 128 tokens x 32 columns of Wg and of Wu.
 constexpr int K1_BM = 256, K1_BN = 256, K1_WGM = 2, K1_NST = 2, K1_LDZ = K1_BN / 2 + 8;
+static_assert(kGemmWaves == 4 || kGemmWaves == 8, "wave count");
 
 __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
     const u16* __restrict__ H, const u16* __restrict__ Wg, const u16* __restrict__ Wu,
     u16* __restrict__ Z, u16* __restrict__ ZT, Dims g, int tiles_m, int tiles_n) {
   using L = Layout<K1_BM, K1_BN, K1_WGM>;
-  static_assert(L::TN == 2, "one gate and one up tile per wave");
+  constexpr int NG = L::TN / 2;  // gate tiles per wave (and as many up tiles)
+  static_assert(NG >= 1 && L::TN == 2 * NG, "gate and up tiles pair up");
   TTT_GEMM_LDS(lds, K1_BM, K1_BN, K1_NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K1_BM, j0 = ti.tn * (K1_BN / 2);
@@ -401,31 +407,36 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
   const Frag<L> fr;
   // Token-major Z goes through LDS (rows 0-127 in stage 0, 128-255 in stage
   // 1) so that its stores are whole 16-byte row segments.
-  const int jl = fr.wn * 32 + (fr.lane & 31);
-  const int j = j0 + jl;
+  constexpr int WROWS = K1_BM / K1_WGM;  // tile rows per wave row
+  static_assert(WROWS <= 128 && 128 % WROWS == 0, "a wave's rows stay in one stage");
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int tl = m * 32 + 8 * q + 4 * (fr.lane >> 5);  // row within this wave's half
-      float z[4];
+    for (int n = 0; n < NG; ++n)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] = silu(acc[m][0][4 * q + e]) * acc[m][1][4 * q + e];
-      const int t = t0 + fr.wm * 128 + tl;
-      if (ZT != nullptr && j < f)
-        *reinterpret_cast<uint2*>(ZT + ((int64_t)ti.b * f + j) * g.ld_t + t) =
-            make_uint2(pack_f16(z[0], z[1]), pack_f16(z[2], z[3]));
-      u16* sZ = (fr.wm == 0 ? lds.s[0] : lds.s[1]) + tl * K1_LDZ + jl;
+      for (int q = 0; q < 4; ++q) {
+        const int row = fr.wm * WROWS + m * 32 + 8 * q + 4 * (fr.lane >> 5);  // tile row
+        const int jl = fr.wn * NG * 32 + n * 32 + (fr.lane & 31);
+        const int j = j0 + jl;
+        float z[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sZ[e * K1_LDZ] = bf16_rne(z[e]);
-    }
+        for (int e = 0; e < 4; ++e) z[e] = silu(acc[m][n][4 * q + e]) * acc[m][n + NG][4 * q + e];
+        const int t = t0 + row;
+        if (ZT != nullptr && j < f)
+          *reinterpret_cast<uint2*>(ZT + ((int64_t)ti.b * f + j) * g.ld_t + t) =
+              make_uint2(pack_f16(z[0], z[1]), pack_f16(z[2], z[3]));
+        u16* sZ = (row < 128 ? lds.s[0] : lds.s[1]) + (row & 127) * K1_LDZ + jl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sZ[e * K1_LDZ] = bf16_rne(z[e]);
+      }
   if (Z == nullptr) return;
   __syncthreads();
+  constexpr int CHUNKS = K1_BM * (K1_BN / 2) / 8;  // 16-byte row segments in the tile
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < CHUNKS / kGemmThreads; ++i) {
     const int c = threadIdx.x + i * kGemmThreads;
     const int row = c >> 4, cc = c & 15;
-    const u16* src = lds.s[i >> 2] + (row & 127) * K1_LDZ + cc * 8;  // row >> 7 == i >> 2
+    const u16* src = (row < 128 ? lds.s[0] : lds.s[1]) + (row & 127) * K1_LDZ + cc * 8;
     const int t = t0 + row, jj = j0 + cc * 8;
     if (t < g.T && jj < f)
       *reinterpret_cast<uint4*>(Z + ((int64_t)ti.b * g.T + t) * g.ld_z + jj) =
@@ -479,7 +490,7 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 // at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
 // time; at every chunk start the state before that chunk is stored as a
 // bf16 snapshot (the exclusive prefix).
-constexpr int K3_BM = 256, K3_BN = 128, K3_WGM = 4, K3_NST = 3;
+constexpr int K3_BM = 256, K3_BN = 128, K3_WGM = kGemmWaves == 8 ? 4 : 2, K3_NST = 3;
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
 // into a [d][ld] bf16 matrix (row c = d_model index, column j = d_ff index).
@@ -583,7 +594,8 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
 // The tile's tokens all lie in one chunk i and read snapshot i.
 template <int BN>
 struct ApplyCfg {
-  static constexpr int WGM = BN == 256 ? 2 : (BN == 128 ? 4 : 8);
+  static constexpr int WGM =
+      kGemmWaves == 8 ? (BN == 256 ? 2 : (BN == 128 ? 4 : 8)) : (BN == 64 ? 4 : 2);
 };
 
 template <int BN, bool OUT_F32>
