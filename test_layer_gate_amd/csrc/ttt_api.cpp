@@ -96,8 +96,8 @@ Layout forward_layout(const Geo& g) {
   L.y = take(g.B * g.T_pad * D.ld_y * 2);
   L.wtt = take(g.d * D.ld_y * 2);
   L.z = take(g.B * g.T * D.ld_z * 2);
-  L.zt = take(g.B * g.f * D.ld_t * 2);
-  L.vt = take(g.B * g.d * D.ld_t * 2);
+  L.zt = take(tttk::zt_elems(D) * 2);
+  L.vt = take(tttk::vt_elems(D) * 2);
   L.snap = take(g.running ? g.B * g.d * D.ld_s * 2 : g.B * g.nchunks * g.d * D.ld_s * 2);
   if (g.act_f32) {
     L.hb = take(g.B * g.T * g.d * 2);

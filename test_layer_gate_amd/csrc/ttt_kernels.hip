@@ -140,6 +140,29 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)p));
 }
 
+// A GEMM operand in HBM as the core reads it: row r of K step kt (64
+// elements, 128 bytes) starts at byte r * row_bytes + kt * step_bytes from
+// base; reads at or past `bytes` from base return zero.
+struct Operand {
+  const u16* base;
+  uint32_t row_bytes, step_bytes, bytes;
+};
+
+// Row-major [rows][ld] with K contiguous; rows at or past rows_valid read as
+// zero.
+__device__ __forceinline__ Operand row_major(const u16* base, int64_t ld, int rows_valid) {
+  int64_t bytes = rows_valid > 0 ? (int64_t)rows_valid * ld * 2 : 0;
+  if (bytes > 0xffffffffLL) bytes = 0xffffffffLL;
+  return {base, (uint32_t)(ld * 2), (uint32_t)(kBK * 2), (uint32_t)bytes};
+}
+
+// Blocked [nk][rows][64]: each K step of the tile is one contiguous slab.
+__device__ __forceinline__ Operand blocked(const u16* base, int rows, int nk) {
+  int64_t bytes = (int64_t)nk * rows * (kBK * 2);
+  if (bytes > 0xffffffffLL) bytes = 0xffffffffLL;
+  return {base, (uint32_t)(kBK * 2), (uint32_t)(rows * kBK * 2), (uint32_t)bytes};
+}
+
 template <int ROWS>
 struct DmaTile {
   static constexpr int NB = ROWS / 8;
@@ -147,21 +170,21 @@ struct DmaTile {
   static_assert(ROWS % 8 == 0, "rows");
   uint32_t voff[NI];
   int block[NI];
+  uint32_t step_bytes;
   u32x4 rsrc;
-  __device__ __forceinline__ void init(const u16* base, int64_t ld, int rows_valid, int wave,
-                                       int lane) {
-    int64_t bytes = rows_valid > 0 ? (int64_t)rows_valid * ld * 2 : 0;
-    if (bytes > 0xffffffffLL) bytes = 0xffffffffLL;
-    rsrc = make_rsrc(base, (uint32_t)bytes);
+  __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
+    rsrc = make_rsrc(op.base, op.bytes);
+    step_bytes = op.step_bytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       block[i] = (kGemmWaves * i + wave) % NB;
       const int row = block[i] * 8 + (lane >> 3);
       const int kc = (lane & 7) ^ swz(row);
-      voff[i] = (uint32_t)((int64_t)row * ld * 2 + kc * 16);
+      voff[i] = (uint32_t)row * op.row_bytes + kc * 16;
     }
   }
-  __device__ __forceinline__ void issue(u16* lds_region, uint32_t soff) const {
+  __device__ __forceinline__ void issue(u16* lds_region, int kt) const {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)kt * step_bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       lds_dma_b128(rsrc, lds_addr_of(lds_region + block[i] * 8 * kBK), voff[i], soff);
@@ -254,9 +277,7 @@ struct Layout {
 // nk is the number of 64-wide K steps; L holds NST LDS stages, each
 // (BM + BN) * 64 elements.
 template <int BM, int BN, int WGM, int NST, class Op, bool SPLITB, class Hook>
-__device__ __forceinline__ void gemm_core(const u16* __restrict__ A, int64_t lda, int a_valid,
-                                          const u16* __restrict__ B0,
-                                          const u16* __restrict__ B1, int64_t ldb, int b_valid,
+__device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, const Operand& B1,
                                           int nk, f32x16* acc, const LdsStages& L,
                                           const Hook& hook) {
   using Lay = Layout<BM, BN, WGM>;
@@ -269,15 +290,14 @@ __device__ __forceinline__ void gemm_core(const u16* __restrict__ A, int64_t lda
   DmaTile<BM> ta;
   DmaTile<BROWS> tb0;
   DmaTile<SPLITB ? BN / 2 : 8> tb1;
-  ta.init(A, lda, a_valid, w, lane);
-  tb0.init(B0, ldb, b_valid, w, lane);
-  if constexpr (SPLITB) tb1.init(B1, ldb, b_valid, w, lane);
+  ta.init(A, w, lane);
+  tb0.init(B0, w, lane);
+  if constexpr (SPLITB) tb1.init(B1, w, lane);
 
   auto issue = [&](u16* stage, int kt) {
-    const uint32_t soff = (uint32_t)kt * (kBK * 2);
-    ta.issue(stage, soff);
-    tb0.issue(stage + BM * kBK, soff);
-    if constexpr (SPLITB) tb1.issue(stage + BM * kBK + (BN / 2) * kBK, soff);
+    ta.issue(stage, kt);
+    tb0.issue(stage + BM * kBK, kt);
+    if constexpr (SPLITB) tb1.issue(stage + BM * kBK + (BN / 2) * kBK, kt);
   };
 
   // Rows of this lane's fragments within the stage.
@@ -402,8 +422,10 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
   gemm_core<K1_BM, K1_BN, K1_WGM, K1_NST, Bf16Mma, true>(
-      H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0), Wg + (int64_t)j0 * d,
-      Wu + (int64_t)j0 * d, d, min(K1_BN / 2, f - j0), d / kBK, &acc[0][0], lds, NoHook{});
+      row_major(H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0)),
+      row_major(Wg + (int64_t)j0 * d, d, min(K1_BN / 2, f - j0)),
+      row_major(Wu + (int64_t)j0 * d, d, min(K1_BN / 2, f - j0)), d / kBK, &acc[0][0], lds,
+      NoHook{});
   const Frag<L> fr;
   // Token-major Z goes through LDS (rows 0-127 in stage 0, 128-255 in stage
   // 1) so that its stores are whole 16-byte row segments.
@@ -423,7 +445,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
         for (int e = 0; e < 4; ++e) z[e] = silu(acc[m][n][4 * q + e]) * acc[m][n + NG][4 * q + e];
         const int t = t0 + row;
         if (ZT != nullptr && j < f)
-          *reinterpret_cast<uint2*>(ZT + ((int64_t)ti.b * f + j) * g.ld_t + t) =
+          *reinterpret_cast<uint2*>(ZT + zt_offset(g, ti.b, j, t)) =
               make_uint2(pack_f16(z[0], z[1]), pack_f16(z[2], z[3]));
         u16* sZ = (row < 128 ? lds.s[0] : lds.s[1]) + (row & 127) * K1_LDZ + jl;
 #pragma unroll
@@ -458,9 +480,10 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
   const int d = g.d;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
+  const Operand wt = row_major(WtT + (int64_t)c0 * g.ld_y, g.ld_y, min(K2_BN, d - c0));
   gemm_core<K2_BM, K2_BN, K2_WGM, K2_NST, F16Mma, false>(
-      Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM, WtT + (int64_t)c0 * g.ld_y,
-      nullptr, g.ld_y, min(K2_BN, d - c0), d / kBK, &acc[0][0], lds, NoHook{});
+      row_major(Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM), wt, wt, d / kBK,
+      &acc[0][0], lds, NoHook{});
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -475,7 +498,7 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[m][n][4 * q + e] * vscale;
         if (VT != nullptr)
-          *reinterpret_cast<uint2*>(VT + ((int64_t)ti.b * d + c) * g.ld_t + t) =
+          *reinterpret_cast<uint2*>(VT + vt_offset(g, ti.b, c, t)) =
               make_uint2(pack_f16(v[0], v[1]), pack_f16(v[2], v[3]));
         if (Vtok != nullptr) {
 #pragma unroll
@@ -490,7 +513,7 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 // at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
 // time; at every chunk start the state before that chunk is stored as a
 // bf16 snapshot (the exclusive prefix).
-constexpr int K3_BM = 256, K3_BN = 128, K3_WGM = kGemmWaves == 8 ? 4 : 2, K3_NST = 3;
+constexpr int K3_BM = kZtRows, K3_BN = kVtRows, K3_WGM = kGemmWaves == 8 ? 4 : 2, K3_NST = 3;
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
 // into a [d][ld] bf16 matrix (row c = d_model index, column j = d_ff index).
@@ -567,10 +590,12 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
     if (snap_b != nullptr && kt % steps_per_chunk == 0)
       snapshot(snap_b + (int64_t)(kt / steps_per_chunk) * chunk_stride, a);
   };
+  // Rows past d_ff / d_model in the last slabs are never written; they only
+  // feed output rows / columns that are not stored.
+  const Operand vt = blocked(VT + vt_offset(g, ti.b, c0, tok_begin), K3_BN, nk);
   gemm_core<K3_BM, K3_BN, K3_WGM, K3_NST, F16Mma, false>(
-      ZT + ((int64_t)ti.b * f + j0) * g.ld_t + tok_begin, g.ld_t, min(K3_BM, f - j0),
-      VT + ((int64_t)ti.b * d + c0) * g.ld_t + tok_begin, nullptr, g.ld_t, min(K3_BN, d - c0), nk,
-      &acc[0][0], lds, hook);
+      blocked(ZT + zt_offset(g, ti.b, j0, tok_begin), K3_BM, nk), vt, vt, nk, &acc[0][0], lds,
+      hook);
 
   float* wf_b = Wf + (int64_t)ti.b * d * f;
 #pragma unroll
@@ -613,10 +638,11 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
   const int d = g.d, f = g.f, T = g.T;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
+  const Operand z = row_major(Z + ((int64_t)ti.b * T + t0) * g.ld_z, g.ld_z, min(BN, T - t0));
   gemm_core<BM, BN, WGM, 2, Bf16Mma, false>(
-      snap + ti.b * snap_bstride + i * snap_cstride + (int64_t)c0 * g.ld_s, g.ld_s,
-      min(BM, d - c0), Z + ((int64_t)ti.b * T + t0) * g.ld_z, nullptr, g.ld_z, min(BN, T - t0),
-      f / kBK, &acc[0][0], lds, NoHook{});
+      row_major(snap + ti.b * snap_bstride + i * snap_cstride + (int64_t)c0 * g.ld_s, g.ld_s,
+                min(BM, d - c0)),
+      z, z, f / kBK, &acc[0][0], lds, NoHook{});
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)

@@ -7,9 +7,12 @@
 //   Y   fp16 [B][T_pad][ld_y]   conv(X0); rows >= T are zero
 //   WtT fp16 [d][ld_y]          W_target transposed: WtT[o][i] = W_target[i][o]
 //   Z   bf16 [B][T][ld_z]       gated activation, token-major (the apply reads it)
-//   ZT  fp16 [B][f][ld_t]       the same, feature-major (the update reads it);
-//                               columns >= T are zero
-//   VT  fp16 [B][d][ld_t]       vscale * V, feature-major; columns >= T are zero
+//   ZT  fp16 [B][f/256][T_pad/64][256][64]   the same, feature-major and blocked
+//                               for the update: each (256 d_ff rows x 64 tokens)
+//                               block is one contiguous 32 KB slab; tokens >= T
+//                               are zero
+//   VT  fp16 [B][d/128][T_pad/64][128][64]   vscale * V, blocked the same way
+//                               (128 d_model rows per slab); tokens >= T zero
 //   S   bf16 [B][k][d][ld_s]    per-chunk snapshots of the state
 // T_pad = T rounded up to a multiple of 256.
 #pragma once
@@ -19,6 +22,9 @@
 namespace tttk {
 
 constexpr int kTokenPad = 256;
+constexpr int kZtRows = 256;  // d_ff rows per ZT slab = the update tile's M
+constexpr int kVtRows = 128;  // d_model rows per VT slab = the update tile's N
+constexpr int kTokStep = 64;  // tokens per slab = one K step
 
 // n (a multiple of 64) padded so that n * 2 bytes is an odd number of
 // 128-byte lines.
@@ -26,7 +32,8 @@ inline int64_t pad_ld(int64_t n) { return ((n / 64) % 2 == 0) ? n + 64 : n; }
 
 struct Dims {
   int B, T, T_pad, d, f;
-  int64_t ld_t, ld_y, ld_z, ld_s;
+  int nts, nfb, ndb;  // token steps, ZT row blocks, VT row blocks
+  int64_t ld_y, ld_z, ld_s;
 };
 
 inline Dims make_dims(int B, int T, int d, int f) {
@@ -36,12 +43,26 @@ inline Dims make_dims(int B, int T, int d, int f) {
   g.T_pad = (T + kTokenPad - 1) / kTokenPad * kTokenPad;
   g.d = d;
   g.f = f;
-  g.ld_t = pad_ld(g.T_pad);
+  g.nts = g.T_pad / kTokStep;
+  g.nfb = (f + kZtRows - 1) / kZtRows;
+  g.ndb = (d + kVtRows - 1) / kVtRows;
   g.ld_y = pad_ld(d);
   g.ld_z = pad_ld(f);
   g.ld_s = pad_ld(f);
   return g;
 }
+
+// Element offsets in the blocked ZT / VT buffers.
+__host__ __device__ inline int64_t zt_offset(const Dims& g, int b, int j, int t) {
+  return (((int64_t)b * g.nfb + j / kZtRows) * g.nts + t / kTokStep) * (kZtRows * kTokStep) +
+         (int64_t)(j % kZtRows) * kTokStep + t % kTokStep;
+}
+__host__ __device__ inline int64_t vt_offset(const Dims& g, int b, int c, int t) {
+  return (((int64_t)b * g.ndb + c / kVtRows) * g.nts + t / kTokStep) * (kVtRows * kTokStep) +
+         (int64_t)(c % kVtRows) * kTokStep + t % kTokStep;
+}
+inline int64_t zt_elems(const Dims& g) { return (int64_t)g.B * g.nfb * kZtRows * g.T_pad; }
+inline int64_t vt_elems(const Dims& g) { return (int64_t)g.B * g.ndb * kVtRows * g.T_pad; }
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 
