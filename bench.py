@@ -42,6 +42,7 @@ KERNEL_NAMES = {"gate_up": "gate_up_kernel", "target": "target_kernel",
                 "update_prefix": "update_kernel", "update_running": "update_kernel",
                 "apply": "apply_kernel", "conv": "conv_kernel",
                 "transpose_w_target": "transpose_kernel", "cast_bf16": "cast_kernel",
+                "pack_weights": "pack_weight_kernel",
                 "calibration_copy": "calibration_copy_kernel"}
 
 
@@ -60,6 +61,8 @@ def kernel_work(name, cfg, T_pad):
         return "hbm", 2.0 * B * T * d + 2.0 * B * T_pad * d + 2.0 * K * d
     if name == "transpose_w_target":
         return "hbm", 4.0 * d * d
+    if name == "pack_weights":  # one of W_g / W_u per launch: read d*f, write the packed copy
+        return "hbm", 2.0 * d * f + 2.0 * d * (-(-f // 128) * 128)
     return None, None
 
 

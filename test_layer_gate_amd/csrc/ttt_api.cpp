@@ -78,7 +78,7 @@ struct Geo {
 };
 
 struct Layout {
-  size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgb = 0, wub = 0;
+  size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgp = 0, wup = 0;
   size_t total = 0;
 };
 
@@ -103,16 +103,14 @@ Layout forward_layout(const Geo& g) {
     L.hb = take(g.B * g.T * g.d * 2);
     L.x0b = take(g.B * g.T * g.d * 2);
   }
-  if (g.w_f32) {
-    L.wgb = take(g.f * g.d * 2);
-    L.wub = take(g.f * g.d * 2);
-  }
+  L.wgp = take(tttk::wpack_elems(D) * 2);
+  L.wup = take(tttk::wpack_elems(D) * 2);
   L.total = off;
   return L;
 }
 
-// Step entry points: gated activation needs bf16 copies of fp32 inputs;
-// the target needs Y, WtT and a bf16 copy of fp32 X0.
+// Step entry points: gated activation needs the packed weights and a bf16
+// copy of fp32 H; the target needs Y, WtT and a bf16 copy of fp32 X0.
 Layout step_layout(const Geo& g) {
   Layout L;
   size_t off = 0;
@@ -127,10 +125,8 @@ Layout step_layout(const Geo& g) {
     L.hb = take(g.B * g.T * g.d * 2);
     L.x0b = take(g.B * g.T * g.d * 2);
   }
-  if (g.w_f32) {
-    L.wgb = take(g.f * g.d * 2);
-    L.wub = take(g.f * g.d * 2);
-  }
+  L.wgp = take(tttk::wpack_elems(g.dims) * 2);
+  L.wup = take(tttk::wpack_elems(g.dims) * 2);
   L.total = off;
   return L;
 }
@@ -328,8 +324,6 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
   // bf16 operands
   const uint16_t* Hb = static_cast<const uint16_t*>(H);
   const uint16_t* X0b = static_cast<const uint16_t*>(X0);
-  const uint16_t* Wgb = static_cast<const uint16_t*>(Wg);
-  const uint16_t* Wub = static_cast<const uint16_t*>(Wu);
   if (g.act_f32) {
     TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(H),
                                                       at<uint16_t>(workspace, L.hb), g.B * g.T * g.d, s));
@@ -338,14 +332,10 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
     Hb = at<uint16_t>(workspace, L.hb);
     X0b = at<uint16_t>(workspace, L.x0b);
   }
-  if (g.w_f32) {
-    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(Wg),
-                                                      at<uint16_t>(workspace, L.wgb), g.f * g.d, s));
-    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(Wu),
-                                                      at<uint16_t>(workspace, L.wub), g.f * g.d, s));
-    Wgb = at<uint16_t>(workspace, L.wgb);
-    Wub = at<uint16_t>(workspace, L.wub);
-  }
+  uint16_t* Wgp = at<uint16_t>(workspace, L.wgp);
+  uint16_t* Wup = at<uint16_t>(workspace, L.wup);
+  TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wg, g.w_f32, Wgp, D, s));
+  TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wu, g.w_f32, Wup, D, s));
   uint16_t* Y = at<uint16_t>(workspace, L.y);
   uint16_t* WtT = at<uint16_t>(workspace, L.wtt);
   uint16_t* Z = at<uint16_t>(workspace, L.z);
@@ -369,7 +359,7 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
              tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, D.ld_y, s));
   TTT_LAUNCH("conv", s,
              tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, D, (int)g.K, (int)g.C, g.pad_chunk, s));
-  TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgb, Wub, Z, ZT, D, s));
+  TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, s));
   TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, vscale, D, s));
 
   const int64_t snap_cstride = g.d * D.ld_s;
@@ -423,25 +413,19 @@ ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void*
                           range_of("workspace", workspace, L.total)}));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* Hb = static_cast<const uint16_t*>(H);
-  const uint16_t* Wgb = static_cast<const uint16_t*>(Wg);
-  const uint16_t* Wub = static_cast<const uint16_t*>(Wu);
   if (g.act_f32) {
     TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(H),
                                                       at<uint16_t>(workspace, L.hb), g.B * g.T * g.d, s));
     Hb = at<uint16_t>(workspace, L.hb);
   }
-  if (g.w_f32) {
-    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(Wg),
-                                                      at<uint16_t>(workspace, L.wgb), g.f * g.d, s));
-    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(Wu),
-                                                      at<uint16_t>(workspace, L.wub), g.f * g.d, s));
-    Wgb = at<uint16_t>(workspace, L.wgb);
-    Wub = at<uint16_t>(workspace, L.wub);
-  }
   tttk::Dims D = g.dims;
   D.ld_z = g.f;  // the caller's Z is dense [B, T, d_ff]
+  uint16_t* Wgp = at<uint16_t>(workspace, L.wgp);
+  uint16_t* Wup = at<uint16_t>(workspace, L.wup);
+  TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wg, g.w_f32, Wgp, D, s));
+  TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wu, g.w_f32, Wup, D, s));
   TTT_LAUNCH("gate_up", s,
-             tttk::launch_gate_up(Hb, Wgb, Wub, static_cast<uint16_t*>(Z), nullptr, D, s));
+             tttk::launch_gate_up(Hb, Wgp, Wup, static_cast<uint16_t*>(Z), nullptr, D, s));
   return TTT_OK;
 }
 

@@ -3,14 +3,14 @@
 // The four dense contractions (gate/up projection, target projection, the
 // fast-weight update and the apply) share one MFMA GEMM core:
 //   C[M][N] = sum_k A[m][k] * B[n][k],  both operands K-contiguous in HBM.
-// A workgroup is 4 wave64s in a 2 x 2 grid; wave (wm, wn) owns a
-// (BM/2) x (BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16},
-// fp32 accumulation, accumulators in AGPRs). K advances 64 elements per step
-// through two LDS stages: buffer_load ... lds moves each 16-byte chunk from
-// HBM straight into LDS (no VGPR staging), bounds-checked by the buffer
-// descriptor (rows past the tile's valid rows read as zero), while the MFMAs
-// run on the other stage. Fragments are read with ds_read_b128 one K-substep
-// ahead of the MFMAs that use them.
+// A workgroup is 8 wave64s (two per SIMD) in a WGM x WGN grid; each wave
+// owns a block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}, fp32
+// accumulation). K advances BK elements (32 or 64) per step through NST LDS
+// stages: buffer_load ... lds moves each 16-byte chunk from HBM straight
+// into LDS (no VGPR staging), bounds-checked by the buffer descriptor (rows
+// past the tile's valid rows read as zero), while the MFMAs run on a stage
+// that has landed; NST - 1 stages are in flight at once. Fragments are read
+// with ds_read_b128 one K-substep ahead of the MFMAs that use them.
 //
 // Method sources: "论文精读：In-Place Test-Time Training" reading notes —
 // "In-Place 设计" (gated MLP), "Chunk-Wise 更新机制" (update equation),
@@ -37,9 +37,7 @@ constexpr int kThreads = 256;      // small kernels
 #endif
 constexpr int kGemmWaves = TTT_GEMM_WAVES;  // wave64s per GEMM workgroup (4 or 8)
 constexpr int kGemmThreads = 64 * kGemmWaves;
-constexpr int kBK = 64;            // K elements per LDS stage (128 bytes per row)
-constexpr int kSub = kBK / 16;     // MFMA K-substeps per stage
-constexpr int kMaxStages = 3;      // LDS stages per workgroup (all but one in flight)
+constexpr int kMaxStages = 6;      // LDS stages per workgroup (all but one in flight)
 constexpr int kRsrcWord3 = 0x00020000;
 
 // ---------------------------------------------------------------- helpers
@@ -85,27 +83,33 @@ struct F16Mma {
   }
 };
 
-// LDS tile of `rows` x 64 16-bit elements, 128 B per row, eight 16-byte
-// chunks. Chunk kc of row r sits at physical chunk kc ^ swz(r), so that the
-// 32 rows of one fragment read (and any 8 or 16 consecutive ones) fall on
-// distinct banks. swz depends on row % 32 only, so a lane's permutation is
-// the same for every 32-row fragment it reads and each read is one per-lane
+// LDS tile of `rows` x BK 16-bit elements, 2 * BK bytes per row, CPR = BK / 8
+// 16-byte chunks per row. Chunk kc of row r sits at physical chunk
+// kc ^ swz(r), chosen so that any 8 consecutive rows read at one logical
+// chunk fall on 8 distinct 16-byte bank groups of the 128-byte bank line
+// (one ds_read_b128 pass): with 128-byte rows the 8 rows need 8 distinct
+// chunk positions; with 64-byte rows, rows 2i and 2i + 1 share a bank line
+// at opposite halves, so the 4 even (and the 4 odd) rows need 4 distinct
+// positions. swz depends on row % 32 only, so a lane's permutation is the
+// same for every 32-row fragment it reads and each read is one per-lane
 // register plus an immediate offset.
-__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int kc) { return row * kBK + ((kc ^ swz(row)) << 3); }
+template <int BK>
+struct Swz {
+  static_assert(BK == 32 || BK == 64, "BK");
+  static constexpr int CPR = BK / 8;   // 16-byte chunks per row
+  static constexpr int RPB = 64 / CPR;  // rows per 1 KB direct-to-LDS block
+  static __device__ __forceinline__ int swz(int row) {
+    return BK == 64 ? (row ^ ((row >> 3) & 3)) & 7 : (row >> 1) & 3;
+  }
+  static __device__ __forceinline__ int off(int row, int kc) {
+    return row * BK + ((kc ^ swz(row)) << 3);
+  }
+};
 
+template <int BK>
 __device__ __forceinline__ uint4 lds_frag(const u16* lds, int row, int kc) {
-  return *reinterpret_cast<const uint4*>(lds + lds_off(row, kc));
+  return *reinterpret_cast<const uint4*>(lds + Swz<BK>::off(row, kc));
 }
-
-// One operand tile of ROWS rows (a multiple of 8), loaded in blocks of 8
-// rows: one direct-to-LDS load fills block b, lane l the 16 bytes at
-// physical chunk l % 8 of row 8b + l / 8, which is that row's logical chunk
-// (l % 8) ^ swz(row). Every wave issues NI = ceil(blocks / 8) loads per K
-// step, load i of wave w covering block (8i + w) mod blocks; when the blocks
-// do not divide evenly the extra loads repeat a block, writing the same
-// bytes to the same place. The per-lane byte offsets are fixed; the K step
-// enters as the scalar offset.
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -140,9 +144,9 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)p));
 }
 
-// A GEMM operand in HBM as the core reads it: row r of K step kt (64
-// elements, 128 bytes) starts at byte r * row_bytes + kt * step_bytes from
-// base; reads at or past `bytes` from base return zero.
+// A GEMM operand in HBM as the core reads it: row r of K step kt (BK
+// elements) starts at byte r * row_bytes + kt * step_bytes from base; reads
+// at or past `bytes` from base return zero.
 struct Operand {
   const u16* base;
   uint32_t row_bytes, step_bytes, bytes;
@@ -150,24 +154,35 @@ struct Operand {
 
 // Row-major [rows][ld] with K contiguous; rows at or past rows_valid read as
 // zero.
+template <int BK>
 __device__ __forceinline__ Operand row_major(const u16* base, int64_t ld, int rows_valid) {
   int64_t bytes = rows_valid > 0 ? (int64_t)rows_valid * ld * 2 : 0;
   if (bytes > 0xffffffffLL) bytes = 0xffffffffLL;
-  return {base, (uint32_t)(ld * 2), (uint32_t)(kBK * 2), (uint32_t)bytes};
+  return {base, (uint32_t)(ld * 2), (uint32_t)(BK * 2), (uint32_t)bytes};
 }
 
-// Blocked [nk][rows][64]: each K step of the tile is one contiguous slab.
+// Blocked [nk][rows][BK]: each K step of the tile is one contiguous slab.
+template <int BK>
 __device__ __forceinline__ Operand blocked(const u16* base, int rows, int nk) {
-  int64_t bytes = (int64_t)nk * rows * (kBK * 2);
+  int64_t bytes = (int64_t)nk * rows * (BK * 2);
   if (bytes > 0xffffffffLL) bytes = 0xffffffffLL;
-  return {base, (uint32_t)(kBK * 2), (uint32_t)(rows * kBK * 2), (uint32_t)bytes};
+  return {base, (uint32_t)(BK * 2), (uint32_t)(rows * BK * 2), (uint32_t)bytes};
 }
 
-template <int ROWS>
+// One operand tile of ROWS rows, loaded in blocks of RPB rows: one
+// direct-to-LDS load (64 lanes x 16 bytes) fills block b, lane l the 16
+// bytes at physical chunk l % CPR of row RPB * b + l / CPR, which is that
+// row's logical chunk (l % CPR) ^ swz(row). Every wave issues
+// NI = ceil(blocks / waves) loads per K step, load i of wave w covering block
+// (waves * i + w) mod blocks; when the blocks do not divide evenly the extra
+// loads repeat a block, writing the same bytes to the same place. The
+// per-lane byte offsets are fixed; the K step enters as the scalar offset.
+template <int ROWS, int BK>
 struct DmaTile {
-  static constexpr int NB = ROWS / 8;
+  using S = Swz<BK>;
+  static constexpr int NB = ROWS / S::RPB;
   static constexpr int NI = (NB + kGemmWaves - 1) / kGemmWaves;
-  static_assert(ROWS % 8 == 0, "rows");
+  static_assert(ROWS % S::RPB == 0, "rows");
   uint32_t voff[NI];
   int block[NI];
   uint32_t step_bytes;
@@ -178,8 +193,8 @@ struct DmaTile {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       block[i] = (kGemmWaves * i + wave) % NB;
-      const int row = block[i] * 8 + (lane >> 3);
-      const int kc = (lane & 7) ^ swz(row);
+      const int row = block[i] * S::RPB + lane / S::CPR;
+      const int kc = (lane % S::CPR) ^ S::swz(row);
       voff[i] = (uint32_t)row * op.row_bytes + kc * 16;
     }
   }
@@ -187,22 +202,15 @@ struct DmaTile {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)kt * step_bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      lds_dma_b128(rsrc, lds_addr_of(lds_region + block[i] * 8 * kBK), voff[i], soff);
+      lds_dma_b128(rsrc, lds_addr_of(lds_region + block[i] * S::RPB * BK), voff[i], soff);
   }
 };
 
-// The LDS stages of a GEMM workgroup.
-struct LdsStages {
-  u16* s[kMaxStages];
-};
-
-#define TTT_STAGE_ELEMS(BM_, BN_, NST_, i) ((i) < (NST_) ? ((BM_) + (BN_)) * kBK : 8)
-#define TTT_GEMM_LDS(var, BM_, BN_, NST_)                                                        \
-  static_assert((NST_) >= 2 && (NST_) <= kMaxStages, "stages");                                  \
-  __shared__ __attribute__((aligned(16))) u16 var##0[TTT_STAGE_ELEMS(BM_, BN_, NST_, 0)];        \
-  __shared__ __attribute__((aligned(16))) u16 var##1[TTT_STAGE_ELEMS(BM_, BN_, NST_, 1)];        \
-  __shared__ __attribute__((aligned(16))) u16 var##2[TTT_STAGE_ELEMS(BM_, BN_, NST_, 2)];        \
-  const LdsStages var = {{var##0, var##1, var##2}};
+// The LDS of a GEMM workgroup: NST stages of (BM + BN) * BK elements back to
+// back (the epilogues reuse the whole array once the core has returned).
+#define TTT_GEMM_LDS(var, BM_, BN_, BK_, NST_)                                  \
+  static_assert((NST_) >= 2 && (NST_) <= kMaxStages, "stages");                 \
+  __shared__ __attribute__((aligned(16))) u16 var[(NST_) * ((BM_) + (BN_)) * (BK_)];
 
 // Waits until at most N of this wave's vector-memory operations are
 // outstanding (they complete in issue order) and all of its LDS reads have
@@ -274,30 +282,39 @@ struct Layout {
 // gate and up projections); wave wn then owns the same TN/2 * 32 columns of
 // each, in acc[.][0, TN/2) (B0) and acc[.][TN/2, TN) (B1).
 // hook(kt, acc) runs at the start of K step kt, when acc holds steps < kt.
-// nk is the number of 64-wide K steps; L holds NST LDS stages, each
-// (BM + BN) * 64 elements.
-template <int BM, int BN, int WGM, int NST, class Op, bool SPLITB, class Hook>
+// nk is the number of BK-wide K steps; lds holds NST stages, each
+// (BM + BN) * BK elements. Step kt reads K block (kt + k0) mod nk (k0 in
+// [0, nk)): tiles that share an operand slab but start at different k0 reach
+// it at different times, so one of them misses in L2 and the others then
+// hit, instead of all waiting on the same miss. A hook needs k0 = 0.
+template <int BM, int BN, int WGM, int BK, int NST, class Op, bool SPLITB, class Hook>
 __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, const Operand& B1,
-                                          int nk, f32x16* acc, const LdsStages& L,
-                                          const Hook& hook) {
+                                          int nk, f32x16* acc, u16* lds, const Hook& hook,
+                                          int k0 = 0) {
   using Lay = Layout<BM, BN, WGM>;
   constexpr int TM = Lay::TM, TN = Lay::TN, WGN = Lay::WGN;
   constexpr int BROWS = SPLITB ? BN / 2 : BN;
+  constexpr int KSUB = BK / 16;  // MFMA K-substeps per stage
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(NST >= 2 && NST <= kMaxStages && KSUB >= 2, "pipeline");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / WGN, wn = w % WGN;
   if (nk <= 0) return;
 
-  DmaTile<BM> ta;
-  DmaTile<BROWS> tb0;
-  DmaTile<SPLITB ? BN / 2 : 8> tb1;
+  DmaTile<BM, BK> ta;
+  DmaTile<BROWS, BK> tb0;
+  DmaTile<SPLITB ? BN / 2 : Swz<BK>::RPB, BK> tb1;
   ta.init(A, w, lane);
   tb0.init(B0, w, lane);
   if constexpr (SPLITB) tb1.init(B1, w, lane);
 
-  auto issue = [&](u16* stage, int kt) {
-    ta.issue(stage, kt);
-    tb0.issue(stage + BM * kBK, kt);
-    if constexpr (SPLITB) tb1.issue(stage + BM * kBK + (BN / 2) * kBK, kt);
+  auto stage = [&](int i) { return lds + i * STAGE; };
+  auto issue = [&](u16* st, int kt) {
+    kt += k0;
+    if (kt >= nk) kt -= nk;
+    ta.issue(st, kt);
+    tb0.issue(st + BM * BK, kt);
+    if constexpr (SPLITB) tb1.issue(st + BM * BK + (BN / 2) * BK, kt);
   };
 
   // Rows of this lane's fragments within the stage.
@@ -319,7 +336,7 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
   // Software pipeline over NST LDS stages. While stage kt is read, the
   // loads of stages kt + 1 .. kt + NST - 1 are in flight; the load of stage
   // kt + NST - 1 goes into the stage read at kt - 1, which the barrier ending
-  // step kt - 1 released. A stage holds four 16-wide substeps: the fragments
+  // step kt - 1 released. A stage holds KSUB 16-wide substeps: the fragments
   // of substep s + 1 are read between the MFMAs of substep s, and the MFMAs
   // of the last substep run after the barrier, between the reads of the next
   // stage's first substep.
@@ -327,9 +344,9 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
   uint4 fa[2][TM], fb[2][TN];
   auto load_sub = [&](const u16* st, int sub, int set) {
 #pragma unroll
-    for (int m = 0; m < TM; ++m) fa[set][m] = lds_frag(st, arow[m], 2 * sub + khalf);
+    for (int m = 0; m < TM; ++m) fa[set][m] = lds_frag<BK>(st, arow[m], 2 * sub + khalf);
 #pragma unroll
-    for (int n = 0; n < TN; ++n) fb[set][n] = lds_frag(st, brow[n], 2 * sub + khalf);
+    for (int n = 0; n < TN; ++n) fb[set][n] = lds_frag<BK>(st, brow[n], 2 * sub + khalf);
   };
   auto mma_sub = [&](int set) {
 #pragma unroll
@@ -338,10 +355,12 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
       for (int n = 0; n < TN; ++n)
         acc[m * TN + n] = Op::mma(fa[set][m], fb[set][n], acc[m * TN + n]);
   };
-  constexpr int NPS = DmaTile<BM>::NI + (SPLITB ? 2 * DmaTile<BN / 2>::NI : DmaTile<BN>::NI);
+  constexpr int NPS =
+      DmaTile<BM, BK>::NI + (SPLITB ? 2 * DmaTile<BN / 2, BK>::NI : DmaTile<BN, BK>::NI);
   // The loads issued after those of stage kt + 1 are the (R - 1) stage
   // loads that follow it.
   constexpr int WAIT = (R - 1) * NPS;
+  static_assert(WAIT + NPS <= 63, "outstanding loads exceed the vmcnt range");
   // One MFMA, then one fragment read while reads remain, then loads.
   auto interleave = [&](int nvmem) {
 #pragma unroll
@@ -360,27 +379,27 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
     mma_sub(0);
     interleave(NPS);
 #pragma unroll
-    for (int sub = 1; sub + 1 < kSub; ++sub) {
+    for (int sub = 1; sub + 1 < KSUB; ++sub) {
       load_sub(cur, sub + 1, (sub + 1) & 1);
       mma_sub(sub & 1);
       interleave(0);
     }
     wait_and_barrier<WAIT>();  // stage kt + 1 landed everywhere; stage kt released
     load_sub(nxt, 0, 0);
-    mma_sub((kSub - 1) & 1);
+    mma_sub((KSUB - 1) & 1);
     interleave(0);
     if (kt + 1 < nk) hook(kt + 1, acc);
   };
 
   hook(0, acc);
 #pragma unroll
-  for (int i = 0; i < R; ++i) issue(L.s[i], min(i, nk - 1));
+  for (int i = 0; i < R; ++i) issue(stage(i), min(i, nk - 1));
   wait_and_barrier<WAIT>();
-  load_sub(L.s[0], 0, 0);
+  load_sub(stage(0), 0, 0);
   for (int kt = 0; kt < nk; kt += NST) {
 #pragma unroll
     for (int i = 0; i < NST; ++i)
-      if (kt + i < nk) step(L.s[i], L.s[(i + 1) % NST], L.s[(i + NST - 1) % NST], kt + i);
+      if (kt + i < nk) step(stage(i), stage((i + 1) % NST), stage((i + NST - 1) % NST), kt + i);
   }
   // Drain the trailing loads before the caller reuses LDS.
   wait_and_barrier<0>();
@@ -403,34 +422,45 @@ struct Frag {
   __device__ __forceinline__ int col(int n) const { return wn * L::TN * 32 + n * 32 + (lane & 31); }
 };
 
+// K-step rotation of the tile at absolute tile coordinates (tm, tn): the
+// workgroups resident on one XCD cover 4 tile rows x 8 tile columns (see
+// tile_index), and offsets that differ along both directions stagger every
+// shared A and B slab.
+__device__ __forceinline__ int k_rotation(int tm, int tn, int nk) {
+  return ((tm & 3) + (tn & 7)) % nk;
+}
+
 // ------------------------------------------------ gate/up + SiLU*mul (K1)
 // M = tokens (256), N = 128 columns of Wg and the same 128 of Wu, K = d.
-// Waves 2 x 4: each wave owns 128 tokens x 32 columns of Wg and of Wu.
-constexpr int K1_BM = 256, K1_BN = 256, K1_WGM = 2, K1_NST = 2, K1_LDZ = K1_BN / 2 + 8;
+// Waves 2 x 4: each wave owns 128 tokens x 32 columns of Wg and of Wu. The
+// weights come packed (Wgp / Wup: one contiguous slab per tile and K step).
+constexpr int K1_BM = 256, K1_BN = 2 * kWRows, K1_WGM = 2, K1_BK = kGateBK, K1_NST = 2;
+constexpr int K1_LDZ = K1_BN / 2 + 8;  // row stride of the Z staging tile in LDS
+static_assert(K1_BM * K1_LDZ <= K1_NST * (K1_BM + K1_BN) * K1_BK, "Z staging fits the stages");
 static_assert(kGemmWaves == 4 || kGemmWaves == 8, "wave count");
 
 __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
-    const u16* __restrict__ H, const u16* __restrict__ Wg, const u16* __restrict__ Wu,
+    const u16* __restrict__ H, const u16* __restrict__ Wgp, const u16* __restrict__ Wup,
     u16* __restrict__ Z, u16* __restrict__ ZT, Dims g, int tiles_m, int tiles_n) {
   using L = Layout<K1_BM, K1_BN, K1_WGM>;
   constexpr int NG = L::TN / 2;  // gate tiles per wave (and as many up tiles)
   static_assert(NG >= 1 && L::TN == 2 * NG, "gate and up tiles pair up");
-  TTT_GEMM_LDS(lds, K1_BM, K1_BN, K1_NST)
+  TTT_GEMM_LDS(lds, K1_BM, K1_BN, K1_BK, K1_NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K1_BM, j0 = ti.tn * (K1_BN / 2);
   const int d = g.d, f = g.f;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  gemm_core<K1_BM, K1_BN, K1_WGM, K1_NST, Bf16Mma, true>(
-      row_major(H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0)),
-      row_major(Wg + (int64_t)j0 * d, d, min(K1_BN / 2, f - j0)),
-      row_major(Wu + (int64_t)j0 * d, d, min(K1_BN / 2, f - j0)), d / kBK, &acc[0][0], lds,
-      NoHook{});
+  const int nk = d / K1_BK;
+  const int64_t wslab = (int64_t)ti.tn * kWRows * d;  // tile tn's packed rows
+  gemm_core<K1_BM, K1_BN, K1_WGM, K1_BK, K1_NST, Bf16Mma, true>(
+      row_major<K1_BK>(H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0)),
+      blocked<K1_BK>(Wgp + wslab, kWRows, nk), blocked<K1_BK>(Wup + wslab, kWRows, nk), nk,
+      &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, ti.tn, nk));
   const Frag<L> fr;
-  // Token-major Z goes through LDS (rows 0-127 in stage 0, 128-255 in stage
-  // 1) so that its stores are whole 16-byte row segments.
+  // Token-major Z goes through LDS so that its stores are whole 16-byte row
+  // segments.
   constexpr int WROWS = K1_BM / K1_WGM;  // tile rows per wave row
-  static_assert(WROWS <= 128 && 128 % WROWS == 0, "a wave's rows stay in one stage");
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
 #pragma unroll
@@ -447,7 +477,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
         if (ZT != nullptr && j < f)
           *reinterpret_cast<uint2*>(ZT + zt_offset(g, ti.b, j, t)) =
               make_uint2(pack_f16(z[0], z[1]), pack_f16(z[2], z[3]));
-        u16* sZ = (row < 128 ? lds.s[0] : lds.s[1]) + (row & 127) * K1_LDZ + jl;
+        u16* sZ = lds + row * K1_LDZ + jl;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sZ[e * K1_LDZ] = bf16_rne(z[e]);
       }
@@ -458,7 +488,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
   for (int i = 0; i < CHUNKS / kGemmThreads; ++i) {
     const int c = threadIdx.x + i * kGemmThreads;
     const int row = c >> 4, cc = c & 15;
-    const u16* src = (row < 128 ? lds.s[0] : lds.s[1]) + (row & 127) * K1_LDZ + cc * 8;
+    const u16* src = lds + row * K1_LDZ + cc * 8;
     const int t = t0 + row, jj = j0 + cc * 8;
     if (t < g.T && jj < f)
       *reinterpret_cast<uint4*>(Z + ((int64_t)ti.b * g.T + t) * g.ld_z + jj) =
@@ -468,22 +498,23 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
 
 // ------------------------------------------------------ target GEMM (K2)
 // M = tokens (256), N = output channels (256), K = d; fp16 operands.
-constexpr int K2_BM = 256, K2_BN = 256, K2_WGM = 2, K2_NST = 2;
+constexpr int K2_BM = 256, K2_BN = 256, K2_WGM = 2, K2_BK = 64, K2_NST = 2;
 
 __global__ __launch_bounds__(kGemmThreads) void target_kernel(
     const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
     u16* __restrict__ Vtok, float vscale, Dims g, int tiles_m, int tiles_n) {
   using L = Layout<K2_BM, K2_BN, K2_WGM>;
-  TTT_GEMM_LDS(lds, K2_BM, K2_BN, K2_NST)
+  TTT_GEMM_LDS(lds, K2_BM, K2_BN, K2_BK, K2_NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K2_BM, c0 = ti.tn * K2_BN;
   const int d = g.d;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  const Operand wt = row_major(WtT + (int64_t)c0 * g.ld_y, g.ld_y, min(K2_BN, d - c0));
-  gemm_core<K2_BM, K2_BN, K2_WGM, K2_NST, F16Mma, false>(
-      row_major(Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM), wt, wt, d / kBK,
-      &acc[0][0], lds, NoHook{});
+  const Operand wt = row_major<K2_BK>(WtT + (int64_t)c0 * g.ld_y, g.ld_y, min(K2_BN, d - c0));
+  const int nk = d / K2_BK;
+  gemm_core<K2_BM, K2_BN, K2_WGM, K2_BK, K2_NST, F16Mma, false>(
+      row_major<K2_BK>(Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM), wt, wt, nk,
+      &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, ti.tn, nk));
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -513,7 +544,8 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 // at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
 // time; at every chunk start the state before that chunk is stored as a
 // bf16 snapshot (the exclusive prefix).
-constexpr int K3_BM = kZtRows, K3_BN = kVtRows, K3_WGM = kGemmWaves == 8 ? 4 : 2, K3_NST = 3;
+constexpr int K3_BM = kZtRows, K3_BN = kVtRows, K3_WGM = kGemmWaves == 8 ? 4 : 2,
+              K3_BK = kTokStep, K3_NST = 3;
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
 // into a [d][ld] bf16 matrix (row c = d_model index, column j = d_ff index).
@@ -549,7 +581,7 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
     int tok_begin, int nk, int steps_per_chunk, int tiles_m, int tiles_n) {
   using L = Layout<K3_BM, K3_BN, K3_WGM>;
   constexpr int TM = L::TM, TN = L::TN;
-  TTT_GEMM_LDS(lds, K3_BM, K3_BN, K3_NST)
+  TTT_GEMM_LDS(lds, K3_BM, K3_BN, K3_BK, K3_NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int j0 = ti.tm * K3_BM, c0 = ti.tn * K3_BN;
   const int d = g.d, f = g.f;
@@ -592,10 +624,10 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
   };
   // Rows past d_ff / d_model in the last slabs are never written; they only
   // feed output rows / columns that are not stored.
-  const Operand vt = blocked(VT + vt_offset(g, ti.b, c0, tok_begin), K3_BN, nk);
-  gemm_core<K3_BM, K3_BN, K3_WGM, K3_NST, F16Mma, false>(
-      blocked(ZT + zt_offset(g, ti.b, j0, tok_begin), K3_BM, nk), vt, vt, nk, &acc[0][0], lds,
-      hook);
+  const Operand vt = blocked<K3_BK>(VT + vt_offset(g, ti.b, c0, tok_begin), K3_BN, nk);
+  gemm_core<K3_BM, K3_BN, K3_WGM, K3_BK, K3_NST, F16Mma, false>(
+      blocked<K3_BK>(ZT + zt_offset(g, ti.b, j0, tok_begin), K3_BM, nk), vt, vt, nk, &acc[0][0],
+      lds, hook);
 
   float* wf_b = Wf + (int64_t)ti.b * d * f;
 #pragma unroll
@@ -621,6 +653,7 @@ template <int BN>
 struct ApplyCfg {
   static constexpr int WGM =
       kGemmWaves == 8 ? (BN == 256 ? 2 : (BN == 128 ? 4 : 8)) : (BN == 64 ? 4 : 2);
+  static constexpr int BK = 64, NST = 2;
 };
 
 template <int BN, bool OUT_F32>
@@ -629,20 +662,25 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
     int64_t snap_cstride, void* __restrict__ O, Dims g, int tok_begin, int chunk, int tiles_m,
     int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int BM = 256, WGM = ApplyCfg<BN>::WGM;
+  constexpr int BM = 256, WGM = ApplyCfg<BN>::WGM, BK = ApplyCfg<BN>::BK,
+                NST = ApplyCfg<BN>::NST;
   using L = Layout<BM, BN, WGM>;
-  TTT_GEMM_LDS(lds, BM, BN, 2)
+  TTT_GEMM_LDS(lds, BM, BN, BK, NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int c0 = ti.tm * BM, t0 = tok_begin + ti.tn * BN;
   const int i = t0 / chunk;
   const int d = g.d, f = g.f, T = g.T;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
-  const Operand z = row_major(Z + ((int64_t)ti.b * T + t0) * g.ld_z, g.ld_z, min(BN, T - t0));
-  gemm_core<BM, BN, WGM, 2, Bf16Mma, false>(
-      row_major(snap + ti.b * snap_bstride + i * snap_cstride + (int64_t)c0 * g.ld_s, g.ld_s,
-                min(BM, d - c0)),
-      z, z, f / kBK, &acc[0][0], lds, NoHook{});
+  const Operand z =
+      row_major<BK>(Z + ((int64_t)ti.b * T + t0) * g.ld_z, g.ld_z, min(BN, T - t0));
+  // The rotation uses the absolute token tile, so that every schedule runs
+  // the same tile with the same summation order.
+  const int nk = f / BK;
+  gemm_core<BM, BN, WGM, BK, NST, Bf16Mma, false>(
+      row_major<BK>(snap + ti.b * snap_bstride + i * snap_cstride + (int64_t)c0 * g.ld_s,
+                    g.ld_s, min(BM, d - c0)),
+      z, z, nk, &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, t0 / BN, nk));
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -746,6 +784,34 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
                  pack_f16(acc[6], acc[7]));
 }
 
+// One thread per 8 packed elements, in packed (destination) order: row
+// jb * 128 + r, columns kt * 64 + 8 * c8 .. + 8 of W -> slab (jb, kt).
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void pack_weight_kernel(const void* __restrict__ W,
+                                                              u16* __restrict__ dst, int f, int d,
+                                                              int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const int nk = d / kGateBK;
+  const int c8 = (int)(i & 7), r = (int)((i >> 3) % kWRows);
+  const int64_t slab = i / (8 * kWRows);
+  const int kt = (int)(slab % nk), jb = (int)(slab / nk);
+  const int row = jb * kWRows + r;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < f) {
+    const int64_t o = (int64_t)row * d + kt * kGateBK + c8 * 8;
+    if constexpr (F32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(W) + o);
+      const float4 a = p[0], b = p[1];
+      v = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y),
+                     pack_bf16(b.z, b.w));
+    } else {
+      v = *reinterpret_cast<const uint4*>(static_cast<const u16*>(W) + o);
+    }
+  }
+  reinterpret_cast<uint4*>(dst)[i] = v;
+}
+
 __global__ __launch_bounds__(kThreads) void calibration_copy_kernel(const uint4* __restrict__ src,
                                                                     uint4* __restrict__ dst,
                                                                     int64_t n16) {
@@ -799,10 +865,21 @@ hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wg, const uint16_t* Wu, uint16_t* Z,
-                          uint16_t* ZT, const Dims& g, hipStream_t s) {
+hipError_t launch_pack_weight(const void* W, bool w_f32, uint16_t* dst, const Dims& g,
+                              hipStream_t s) {
+  const int64_t total = wpack_elems(g) / 8;
+  const int blocks = ceil_div(total, kThreads);
+  if (w_f32)
+    pack_weight_kernel<true><<<blocks, kThreads, 0, s>>>(W, dst, g.f, g.d, total);
+  else
+    pack_weight_kernel<false><<<blocks, kThreads, 0, s>>>(W, dst, g.f, g.d, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
+                          uint16_t* Z, uint16_t* ZT, const Dims& g, hipStream_t s) {
   const int tiles_m = g.T_pad / K1_BM, tiles_n = ceil_div(g.f, K1_BN / 2);
-  gate_up_kernel<<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(H, Wg, Wu, Z, ZT, g, tiles_m,
+  gate_up_kernel<<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(H, Wgp, Wup, Z, ZT, g, tiles_m,
                                                               tiles_n);
   return hipGetLastError();
 }
@@ -820,7 +897,7 @@ hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Win
                          float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
                          uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
                          int chunk, hipStream_t s) {
-  const int nk = (tok_count + kBK - 1) / kBK, steps_per_chunk = chunk / kBK;
+  const int nk = (tok_count + K3_BK - 1) / K3_BK, steps_per_chunk = chunk / K3_BK;
   const int tiles_m = ceil_div(g.f, K3_BM), tiles_n = ceil_div(g.d, K3_BN);
   const int grid = tiles_m * tiles_n * g.B;
   if (winit_f32)

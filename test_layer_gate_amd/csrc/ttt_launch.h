@@ -7,13 +7,18 @@
 //   Y   fp16 [B][T_pad][ld_y]   conv(X0); rows >= T are zero
 //   WtT fp16 [d][ld_y]          W_target transposed: WtT[o][i] = W_target[i][o]
 //   Z   bf16 [B][T][ld_z]       gated activation, token-major (the apply reads it)
-//   ZT  fp16 [B][f/256][T_pad/64][256][64]   the same, feature-major and blocked
-//                               for the update: each (256 d_ff rows x 64 tokens)
-//                               block is one contiguous 32 KB slab; tokens >= T
-//                               are zero
-//   VT  fp16 [B][d/128][T_pad/64][128][64]   vscale * V, blocked the same way
+//   ZT  fp16 [B][f/256][T_pad/S][256][S]   the same, feature-major and blocked
+//                               for the update: each (256 d_ff rows x S tokens)
+//                               block is one contiguous slab, S = kTokStep, the
+//                               update's K step; tokens >= T are zero
+//   VT  fp16 [B][d/128][T_pad/S][128][S]   vscale * V, blocked the same way
 //                               (128 d_model rows per slab); tokens >= T zero
 //   S   bf16 [B][k][d][ld_s]    per-chunk snapshots of the state
+//   Wgp, Wup  bf16 [f_pad/128][d/64][128][64]   W_g and W_u packed for the
+//                               gate/up GEMM: each (128 rows x 64 columns) block
+//                               is one contiguous 16 KB slab, one K step of one
+//                               tile's B operand; f_pad = f rounded up to 128,
+//                               rows >= f are zero
 // T_pad = T rounded up to a multiple of 256.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -24,7 +29,9 @@ namespace tttk {
 constexpr int kTokenPad = 256;
 constexpr int kZtRows = 256;  // d_ff rows per ZT slab = the update tile's M
 constexpr int kVtRows = 128;  // d_model rows per VT slab = the update tile's N
-constexpr int kTokStep = 64;  // tokens per slab = one K step
+constexpr int kTokStep = 64;  // tokens per slab = one K step of the update
+constexpr int kWRows = 128;   // W_g / W_u rows per packed slab = half the gate/up tile's N
+constexpr int kGateBK = 64;   // d_model elements per packed slab = one K step of gate/up
 
 // n (a multiple of 64) padded so that n * 2 bytes is an odd number of
 // 128-byte lines.
@@ -62,6 +69,9 @@ __host__ __device__ inline int64_t vt_offset(const Dims& g, int b, int c, int t)
          (int64_t)(c % kVtRows) * kTokStep + t % kTokStep;
 }
 inline int64_t zt_elems(const Dims& g) { return (int64_t)g.B * g.nfb * kZtRows * g.T_pad; }
+inline int64_t wpack_elems(const Dims& g) {
+  return (int64_t)((g.f + kWRows - 1) / kWRows) * kWRows * g.d;
+}
 inline int64_t vt_elems(const Dims& g) { return (int64_t)g.B * g.ndb * kVtRows * g.T_pad; }
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
@@ -78,8 +88,13 @@ hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, in
 hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint16_t* Y,
                        const Dims& g, int K, int chunk, bool pad_chunk, hipStream_t s);
 
-// Z = SiLU(H Wg^T) * (H Wu^T): bf16 Z (token-major) and fp16 ZT; either may be null.
-hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wg, const uint16_t* Wu,
+// dst = W ([f][d], bf16 or fp32, rounded to bf16) in the packed Wgp layout.
+hipError_t launch_pack_weight(const void* W, bool w_f32, uint16_t* dst, const Dims& g,
+                              hipStream_t s);
+
+// Z = SiLU(H Wg^T) * (H Wu^T) from packed Wgp / Wup: bf16 Z (token-major) and
+// fp16 ZT; either may be null.
+hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
                           uint16_t* Z, uint16_t* ZT, const Dims& g, hipStream_t s);
 
 // V = Y WtT^T (conv(X0) W_target): fp16 VT = vscale * V (feature-major) and
@@ -88,8 +103,8 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
                          float vscale, const Dims& g, hipStream_t s);
 
 // Fast-weight update over tokens [tok_begin, tok_begin + tok_count), in
-// 32-token steps (columns past T read as zero). acc = acc_scale * Winit;
-// before each step that starts a chunk (every chunk / 32 steps), if snap !=
+// kTokStep-token steps (columns past T read as zero). acc = acc_scale * Winit;
+// before each step that starts a chunk (every chunk / kTokStep steps), if snap !=
 // null, that chunk's snapshot = bf16(acc / acc_scale); then acc += the
 // step's ZT x VT contraction over tokens. Finally Wf = acc / acc_scale and,
 // if shadow != null, shadow = bf16(acc / acc_scale). tok_count may be 0.
