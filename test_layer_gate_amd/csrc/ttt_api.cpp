@@ -98,7 +98,8 @@ Layout forward_layout(const Geo& g) {
   L.z = take(g.B * g.T * D.ld_z * 2);
   L.zt = take(tttk::zt_elems(D) * 2);
   L.vt = take(tttk::vt_elems(D) * 2);
-  L.snap = take(g.running ? g.B * g.d * D.ld_s * 2 : g.B * g.nchunks * g.d * D.ld_s * 2);
+  const int64_t snap_elems = tttk::snap_elems(D);
+  L.snap = take(g.running ? g.B * snap_elems * 2 : g.B * g.nchunks * snap_elems * 2);
   if (g.act_f32) {
     L.hb = take(g.B * g.T * g.d * 2);
     L.x0b = take(g.B * g.T * g.d * 2);
@@ -362,7 +363,7 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
   TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, s));
   TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, vscale, D, s));
 
-  const int64_t snap_cstride = g.d * D.ld_s;
+  const int64_t snap_cstride = tttk::snap_elems(D);
   if (!g.running) {
     // Materialised exclusive prefix: snapshot i = bf16(W^(i)) for every chunk,
     // W_down_final = W^(k); then every chunk's output in one launch.

@@ -39,6 +39,8 @@ constexpr int kGemmWaves = TTT_GEMM_WAVES;  // wave64s per GEMM workgroup (4 or 
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kMaxStages = 6;      // LDS stages per workgroup (all but one in flight)
 constexpr int kRsrcWord3 = 0x00020000;
+enum { kRowMajor = 0, kSlab = 1 };  // LDS / HBM layouts of a GEMM operand (see Operand)
+constexpr int kCpolNt = 2, kCpolSc1 = 16;  // cache-policy bits of buffer instructions
 
 // ---------------------------------------------------------------- helpers
 
@@ -106,9 +108,18 @@ struct Swz {
   }
 };
 
-template <int BK>
+// A slab operand keeps its HBM image in LDS: piece kc of row r at element
+// (r / 32) * 2048 + (kc / 2) * 512 + ((kc % 2) * 32 + r % 32) * 8. A
+// fragment read (32 consecutive rows from a multiple of 32, lanes 32-63 at
+// kc + 1 with kc even) is then one contiguous, conflict-free 1 KB.
+__device__ __forceinline__ int slab_off(int row, int kc) {
+  return (row >> 5) * 2048 + (kc >> 1) * 512 + ((kc & 1) * 32 + (row & 31)) * 8;
+}
+
+template <int BK, int LAY>
 __device__ __forceinline__ uint4 lds_frag(const u16* lds, int row, int kc) {
-  return *reinterpret_cast<const uint4*>(lds + Swz<BK>::off(row, kc));
+  return *reinterpret_cast<const uint4*>(lds + (LAY == kSlab ? slab_off(row, kc)
+                                                             : Swz<BK>::off(row, kc)));
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -144,9 +155,14 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)p));
 }
 
-// A GEMM operand in HBM as the core reads it: row r of K step kt (BK
-// elements) starts at byte r * row_bytes + kt * step_bytes from base; reads
-// at or past `bytes` from base return zero.
+// A GEMM operand in HBM as the core reads it: the tile's rows of K step kt
+// (BK elements) start at byte kt * step_bytes from base. Row-major (kRowMajor):
+// the 16-byte piece kc (K elements 8kc .. 8kc + 7) of row r is at
+// r * row_bytes + kc * 16 from there. Slab (kSlab, the sb layout of
+// ttt_launch.h, BK = 64): the step is one contiguous slab of rows * 128
+// bytes, with piece kc of row r at (r / 32) * 4096 + (kc / 2) * 1024 +
+// ((kc % 2) * 32 + r % 32) * 16. Reads at or past `bytes` from base return
+// zero.
 struct Operand {
   const u16* base;
   uint32_t row_bytes, step_bytes, bytes;
@@ -169,20 +185,32 @@ __device__ __forceinline__ Operand blocked(const u16* base, int rows, int nk) {
   return {base, (uint32_t)(BK * 2), (uint32_t)(rows * BK * 2), (uint32_t)bytes};
 }
 
-// One operand tile of ROWS rows, loaded in blocks of RPB rows: one
-// direct-to-LDS load (64 lanes x 16 bytes) fills block b, lane l the 16
-// bytes at physical chunk l % CPR of row RPB * b + l / CPR, which is that
-// row's logical chunk (l % CPR) ^ swz(row). Every wave issues
+// The SR-row slab row of an sb<SR> matrix at m (K columns) that starts at
+// row r0 (a multiple of SR), from column k0 (a multiple of 64) on; the GEMM
+// tile is the SR rows and steps 64 columns at a time.
+template <int SR>
+__device__ __forceinline__ Operand slab_blocked(const u16* m, int64_t K, int r0, int64_t k0) {
+  int64_t bytes = (K - k0) / 64 * (SR * 128);
+  if (bytes > 0xffffffffLL) bytes = 0xffffffffLL;
+  return {m + sb_offset<SR>(r0, k0, K), 4096u, (uint32_t)(SR * 128), (uint32_t)bytes};
+}
+
+// One operand tile of ROWS rows, loaded in blocks of RPB rows (1 KB): one
+// direct-to-LDS load (64 lanes x 16 bytes) fills block b. Row-major: lane l
+// the 16 bytes at physical chunk l % CPR of row RPB * b + l / CPR, which is
+// that row's logical chunk (l % CPR) ^ swz(row). Slab: lane l the 16 bytes
+// at 1024 b + 16 l of the slab, copied as they are. Every wave issues
 // NI = ceil(blocks / waves) loads per K step, load i of wave w covering block
 // (waves * i + w) mod blocks; when the blocks do not divide evenly the extra
 // loads repeat a block, writing the same bytes to the same place. The
 // per-lane byte offsets are fixed; the K step enters as the scalar offset.
-template <int ROWS, int BK>
+template <int ROWS, int BK, int LAY>
 struct DmaTile {
   using S = Swz<BK>;
   static constexpr int NB = ROWS / S::RPB;
   static constexpr int NI = (NB + kGemmWaves - 1) / kGemmWaves;
   static_assert(ROWS % S::RPB == 0, "rows");
+  static_assert(LAY == kRowMajor || (BK == 64 && ROWS % 32 == 0), "slab tiles");
   uint32_t voff[NI];
   int block[NI];
   uint32_t step_bytes;
@@ -195,7 +223,8 @@ struct DmaTile {
       block[i] = (kGemmWaves * i + wave) % NB;
       const int row = block[i] * S::RPB + lane / S::CPR;
       const int kc = (lane % S::CPR) ^ S::swz(row);
-      voff[i] = (uint32_t)row * op.row_bytes + kc * 16;
+      voff[i] = LAY == kSlab ? (uint32_t)block[i] * 1024 + lane * 16
+                             : (uint32_t)row * op.row_bytes + kc * 16;
     }
   }
   __device__ __forceinline__ void issue(u16* lds_region, int kt) const {
@@ -252,9 +281,26 @@ __device__ __forceinline__ TileIdx tile_index(int tiles_m, int tiles_n, int grou
   return t;
 }
 
+// A K-step hook: called with the accumulators at the start of a K step,
+// returns whether it issued stores, and then issued exactly kStores vector
+// memory instructions in every wave (the pipeline's waits count them).
 struct NoHook {
-  __device__ __forceinline__ void operator()(int, const f32x16*) const {}
+  static constexpr int kStores = 0;
+  __device__ __forceinline__ bool operator()(int, const f32x16*) const { return false; }
 };
+
+// Waits as wait_and_barrier<BASE + c * STEP> for a runtime c in [0, C].
+template <int BASE, int STEP, int C>
+__device__ __forceinline__ void wait_and_barrier_var(int c) {
+  if constexpr (C == 0) {
+    wait_and_barrier<BASE>();
+  } else {
+    if (c == C)
+      wait_and_barrier<BASE + C * STEP>();
+    else
+      wait_and_barrier_var<BASE, STEP, C - 1>(c);
+  }
+}
 
 template <int TM, int TN>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM][TN]) {
@@ -281,13 +327,17 @@ struct Layout {
 // SPLITB: the B tile is BN/2 rows of B0 followed by BN/2 rows of B1 (the
 // gate and up projections); wave wn then owns the same TN/2 * 32 columns of
 // each, in acc[.][0, TN/2) (B0) and acc[.][TN/2, TN) (B1).
-// hook(kt, acc) runs at the start of K step kt, when acc holds steps < kt.
+// hook(kt, acc) runs at the start of K step kt, when acc holds steps < kt;
+// from step 1 on, after that step's stage loads are issued, so that its
+// stores need to be complete only R steps later (the waits in between allow
+// for them).
 // nk is the number of BK-wide K steps; lds holds NST stages, each
 // (BM + BN) * BK elements. Step kt reads K block (kt + k0) mod nk (k0 in
 // [0, nk)): tiles that share an operand slab but start at different k0 reach
 // it at different times, so one of them misses in L2 and the others then
 // hit, instead of all waiting on the same miss. A hook needs k0 = 0.
-template <int BM, int BN, int WGM, int BK, int NST, class Op, bool SPLITB, class Hook>
+template <int BM, int BN, int WGM, int BK, int NST, class Op, bool SPLITB, int ALAY, int BLAY,
+          class Hook>
 __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, const Operand& B1,
                                           int nk, f32x16* acc, u16* lds, const Hook& hook,
                                           int k0 = 0) {
@@ -301,9 +351,9 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
   const int wm = w / WGN, wn = w % WGN;
   if (nk <= 0) return;
 
-  DmaTile<BM, BK> ta;
-  DmaTile<BROWS, BK> tb0;
-  DmaTile<SPLITB ? BN / 2 : Swz<BK>::RPB, BK> tb1;
+  DmaTile<BM, BK, ALAY> ta;
+  DmaTile<BROWS, BK, BLAY> tb0;
+  DmaTile<SPLITB ? BN / 2 : 32, BK, BLAY> tb1;  // unused unless SPLITB
   ta.init(A, w, lane);
   tb0.init(B0, w, lane);
   if constexpr (SPLITB) tb1.init(B1, w, lane);
@@ -344,9 +394,10 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
   uint4 fa[2][TM], fb[2][TN];
   auto load_sub = [&](const u16* st, int sub, int set) {
 #pragma unroll
-    for (int m = 0; m < TM; ++m) fa[set][m] = lds_frag<BK>(st, arow[m], 2 * sub + khalf);
+    for (int m = 0; m < TM; ++m) fa[set][m] = lds_frag<BK, ALAY>(st, arow[m], 2 * sub + khalf);
 #pragma unroll
-    for (int n = 0; n < TN; ++n) fb[set][n] = lds_frag<BK>(st, brow[n], 2 * sub + khalf);
+    for (int n = 0; n < TN; ++n)
+      fb[set][n] = lds_frag<BK, BLAY>(st + BM * BK, brow[n] - BM, 2 * sub + khalf);
   };
   auto mma_sub = [&](int set) {
 #pragma unroll
@@ -355,12 +406,17 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
       for (int n = 0; n < TN; ++n)
         acc[m * TN + n] = Op::mma(fa[set][m], fb[set][n], acc[m * TN + n]);
   };
-  constexpr int NPS =
-      DmaTile<BM, BK>::NI + (SPLITB ? 2 * DmaTile<BN / 2, BK>::NI : DmaTile<BN, BK>::NI);
+  constexpr int NPS = DmaTile<BM, BK, ALAY>::NI +
+                      (SPLITB ? 2 * DmaTile<BN / 2, BK, BLAY>::NI : DmaTile<BN, BK, BLAY>::NI);
   // The loads issued after those of stage kt + 1 are the (R - 1) stage
   // loads that follow it.
   constexpr int WAIT = (R - 1) * NPS;
-  static_assert(WAIT + NPS <= 63, "outstanding loads exceed the vmcnt range");
+  constexpr int NSH = Hook::kStores;
+  static_assert(WAIT + NPS + R * NSH <= 63, "outstanding operations exceed the vmcnt range");
+  // Bit i of `stored`: the hook stored at step kt - i. The waits of step kt
+  // let the stores of steps kt - R + 1 .. kt (issued after the loads of
+  // stage kt + 1) stay in flight.
+  unsigned stored = 0;
   // One MFMA, then one fragment read while reads remain, then loads.
   auto interleave = [&](int nvmem) {
 #pragma unroll
@@ -375,6 +431,10 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
   // step's MFMA section stays one basic block; nothing uses their results.
   auto step = [&](const u16* cur, const u16* nxt, u16* refill, int kt) {
     issue(refill, min(kt + R, nk - 1));
+    if constexpr (NSH > 0) {
+      asm volatile("" ::: "memory");  // the hook's stores go after the loads
+      stored = (stored << 1) | (kt > 0 && hook(kt, acc) ? 1u : 0u);
+    }
     load_sub(cur, 1, 1);
     mma_sub(0);
     interleave(NPS);
@@ -384,11 +444,14 @@ __device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, c
       mma_sub(sub & 1);
       interleave(0);
     }
-    wait_and_barrier<WAIT>();  // stage kt + 1 landed everywhere; stage kt released
+    // Stage kt + 1 landed everywhere; stage kt released.
+    if constexpr (NSH > 0)
+      wait_and_barrier_var<WAIT, NSH, R>(__builtin_popcount(stored & ((1u << R) - 1)));
+    else
+      wait_and_barrier<WAIT>();
     load_sub(nxt, 0, 0);
     mma_sub((KSUB - 1) & 1);
     interleave(0);
-    if (kt + 1 < nk) hook(kt + 1, acc);
   };
 
   hook(0, acc);
@@ -422,6 +485,62 @@ struct Frag {
   __device__ __forceinline__ int col(int n) const { return wn * L::TN * 32 + n * 32 + (lane & 31); }
 };
 
+// Stores one 32x32 MFMA accumulator tile `a` of this wave, as 16-bit
+// values, into an sb<SR> matrix m (K columns) transposed: tile row R
+// (R = 8q + 4(lane / 32) + e for register 4q + e) goes to column k_base + R
+// (k_base a multiple of 32), and the lane's tile column to matrix row r.
+// Lanes l and l ^ 32 hold the two halves of every 8 consecutive tile rows;
+// each gives the other the half it does not keep, so that lane l < 32 ends
+// with rows 16p .. 16p + 7 and lane l + 32 with rows 16p + 8 .. 16p + 15,
+// and each of the two store instructions writes one contiguous 1 KB block
+// (32 consecutive matrix rows from a multiple of 32). cvt(x, y) packs two
+// values; sink(element offset, value, ok) stores the lanes with ok (all
+// lanes must call this).
+template <int SR, class Cvt, class Sink>
+__device__ __forceinline__ void store_tile_sb(int64_t K, int r, int64_t k_base, const f32x16& a,
+                                              const Cvt& cvt, bool ok, const Sink& sink) {
+  const int h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t lo0 = cvt(a[8 * p + 0], a[8 * p + 1]), lo1 = cvt(a[8 * p + 2], a[8 * p + 3]);
+    const uint32_t hi0 = cvt(a[8 * p + 4], a[8 * p + 5]), hi1 = cvt(a[8 * p + 6], a[8 * p + 7]);
+    // q = 2p is (lo0, lo1), q = 2p + 1 is (hi0, hi1). Lane h = 0 keeps q = 2p
+    // and sends q = 2p + 1; lane h = 1 keeps q = 2p + 1 and sends q = 2p.
+    const uint32_t s0 = h ? lo0 : hi0, s1 = h ? lo1 : hi1;
+    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32), r1 = (uint32_t)__shfl_xor((int)s1, 32);
+    const uint4 v = h ? make_uint4(r0, r1, hi0, hi1) : make_uint4(lo0, lo1, r0, r1);
+    sink(sb_offset<SR>(r, k_base + 16 * p + 8 * h, K), v, ok);
+  }
+}
+
+// 16-byte streaming (non-temporal) stores, for outputs that the next
+// kernel reads: keeping them from displacing the operand stream in the
+// caches made gate/up 9% faster.
+__device__ __forceinline__ void store_stream(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
+// Streaming 16-byte stores of the lanes with ok into m.
+struct StreamSink {
+  u16* m;
+  __device__ __forceinline__ void operator()(int64_t off, const uint4& v, bool ok) const {
+    if (ok) store_stream(m + off, v);
+  }
+};
+
+struct CvtF16 {
+  float scale;
+  __device__ __forceinline__ uint32_t operator()(float x, float y) const {
+    return pack_f16(x * scale, y * scale);
+  }
+};
+struct CvtBf16 {
+  float scale;
+  __device__ __forceinline__ uint32_t operator()(float x, float y) const {
+    return pack_bf16(x * scale, y * scale);
+  }
+};
+
 // K-step rotation of the tile at absolute tile coordinates (tm, tn): the
 // workgroups resident on one XCD cover 4 tile rows x 8 tile columns (see
 // tile_index), and offsets that differ along both directions stagger every
@@ -453,7 +572,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
   zero_acc(acc);
   const int nk = d / K1_BK;
   const int64_t wslab = (int64_t)ti.tn * kWRows * d;  // tile tn's packed rows
-  gemm_core<K1_BM, K1_BN, K1_WGM, K1_BK, K1_NST, Bf16Mma, true>(
+  gemm_core<K1_BM, K1_BN, K1_WGM, K1_BK, K1_NST, Bf16Mma, true, kRowMajor, kRowMajor>(
       row_major<K1_BK>(H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0)),
       blocked<K1_BK>(Wgp + wslab, kWRows, nk), blocked<K1_BK>(Wup + wslab, kWRows, nk), nk,
       &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, ti.tn, nk));
@@ -464,23 +583,23 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
 #pragma unroll
-    for (int n = 0; n < NG; ++n)
+    for (int n = 0; n < NG; ++n) {
+      const int jl = fr.wn * NG * 32 + n * 32 + (fr.lane & 31);
+      const int j = j0 + jl;
+      f32x16 z;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[r] = silu(acc[m][n][r]) * acc[m][n + NG][r];
+      if (ZT != nullptr)
+        store_tile_sb<kZtSlab>(g.T_pad, j, t0 + fr.wm * WROWS + m * 32, z, CvtF16{1.0f}, j < f,
+                               StreamSink{ZT + ti.b * sb_elems<kZtSlab>(f, g.T_pad)});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = fr.wm * WROWS + m * 32 + 8 * q + 4 * (fr.lane >> 5);  // tile row
-        const int jl = fr.wn * NG * 32 + n * 32 + (fr.lane & 31);
-        const int j = j0 + jl;
-        float z[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = silu(acc[m][n][4 * q + e]) * acc[m][n + NG][4 * q + e];
-        const int t = t0 + row;
-        if (ZT != nullptr && j < f)
-          *reinterpret_cast<uint2*>(ZT + zt_offset(g, ti.b, j, t)) =
-              make_uint2(pack_f16(z[0], z[1]), pack_f16(z[2], z[3]));
         u16* sZ = lds + row * K1_LDZ + jl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sZ[e * K1_LDZ] = bf16_rne(z[e]);
+        for (int e = 0; e < 4; ++e) sZ[e * K1_LDZ] = bf16_rne(z[4 * q + e]);
       }
+    }
   if (Z == nullptr) return;
   __syncthreads();
   constexpr int CHUNKS = K1_BM * (K1_BN / 2) / 8;  // 16-byte row segments in the tile
@@ -491,8 +610,8 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
     const u16* src = lds + row * K1_LDZ + cc * 8;
     const int t = t0 + row, jj = j0 + cc * 8;
     if (t < g.T && jj < f)
-      *reinterpret_cast<uint4*>(Z + ((int64_t)ti.b * g.T + t) * g.ld_z + jj) =
-          *reinterpret_cast<const uint4*>(src);
+      store_stream(Z + ((int64_t)ti.b * g.T + t) * g.ld_z + jj,
+                   *reinterpret_cast<const uint4*>(src));
   }
 }
 
@@ -512,31 +631,30 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
   zero_acc(acc);
   const Operand wt = row_major<K2_BK>(WtT + (int64_t)c0 * g.ld_y, g.ld_y, min(K2_BN, d - c0));
   const int nk = d / K2_BK;
-  gemm_core<K2_BM, K2_BN, K2_WGM, K2_BK, K2_NST, F16Mma, false>(
+  gemm_core<K2_BM, K2_BN, K2_WGM, K2_BK, K2_NST, F16Mma, false, kRowMajor, kRowMajor>(
       row_major<K2_BK>(Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM), wt, wt, nk,
       &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, ti.tn, nk));
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
 #pragma unroll
-    for (int n = 0; n < L::TN; ++n)
+    for (int n = 0; n < L::TN; ++n) {
+      const int c = c0 + fr.col(n);
+      if (VT != nullptr)
+        store_tile_sb<kVtSlab>(g.T_pad, c, t0 + fr.wm * L::TM * 32 + m * 32, acc[m][n],
+                               CvtF16{vscale}, c < d,
+                               StreamSink{VT + ti.b * sb_elems<kVtSlab>(d, g.T_pad)});
+      if (Vtok != nullptr && c < d) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = t0 + fr.row(m, q);
-        const int c = c0 + fr.col(n);
-        if (c >= d) continue;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[m][n][4 * q + e] * vscale;
-        if (VT != nullptr)
-          *reinterpret_cast<uint2*>(VT + vt_offset(g, ti.b, c, t)) =
-              make_uint2(pack_f16(v[0], v[1]), pack_f16(v[2], v[3]));
-        if (Vtok != nullptr) {
+        for (int q = 0; q < 4; ++q) {
+          const int t = t0 + fr.row(m, q);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (t + e < g.T) Vtok[((int64_t)ti.b * g.T + t + e) * d + c] = bf16_rne(v[e]);
+            if (t + e < g.T)
+              Vtok[((int64_t)ti.b * g.T + t + e) * d + c] = bf16_rne(acc[m][n][4 * q + e] * vscale);
         }
       }
+    }
 }
 
 // ------------------------------------------ fast-weight update (K3)
@@ -544,32 +662,56 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 // at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
 // time; at every chunk start the state before that chunk is stored as a
 // bf16 snapshot (the exclusive prefix).
-constexpr int K3_BM = kZtRows, K3_BN = kVtRows, K3_WGM = kGemmWaves == 8 ? 4 : 2,
-              K3_BK = kTokStep, K3_NST = 3;
+constexpr int K3_BM = 256, K3_BN = 128, K3_WGM = kGemmWaves == 8 ? 4 : 2, K3_BK = 64,
+              K3_NST = 3;
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
-// into a [d][ld] bf16 matrix (row c = d_model index, column j = d_ff index).
+// into an sb<256> d x f bf16 matrix of `bytes` bytes (row c = d_model index,
+// column j = d_ff index). Buffer stores: a lane outside the matrix stores
+// at offset `bytes`, which the buffer bound drops, so every wave issues
+// exactly kStores of them. They are streaming, system-scope stores (nt sc1):
+// the apply reads the snapshots only after this kernel, and keeping them out
+// of the way of the operand stream measured 4% faster.
 template <class L>
 struct SnapshotStore {
+  static constexpr int kStores = L::TM * L::TN * 2;
   int j0, c0, d, f;
-  int64_t ld;
   float out_scale;
+  uint32_t bytes;
   __device__ __forceinline__ void operator()(u16* dst, const f32x16* acc) const {
     const Frag<L> fr;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(dst, 0, (int)bytes, kRsrcWord3);
+    const uint32_t drop = bytes;
+    auto sink = [&](int64_t off, const uint4& v, bool ok) {
+      const u32x4 w = {v.x, v.y, v.z, v.w};
+      __builtin_amdgcn_raw_buffer_store_b128(w, rsrc, ok ? (int)(off * 2) : (int)drop, 0,
+                                             kCpolNt | kCpolSc1);
+    };
 #pragma unroll
     for (int m = 0; m < L::TM; ++m)
 #pragma unroll
-      for (int n = 0; n < L::TN; ++n)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = j0 + fr.row(m, q);
-          const int c = c0 + fr.col(n);
-          const f32x16& a = acc[m * L::TN + n];
-          if (c < d && j < f)
-            *reinterpret_cast<uint2*>(dst + (int64_t)c * ld + j) =
-                make_uint2(pack_bf16(a[4 * q] * out_scale, a[4 * q + 1] * out_scale),
-                           pack_bf16(a[4 * q + 2] * out_scale, a[4 * q + 3] * out_scale));
-        }
+      for (int n = 0; n < L::TN; ++n) {
+        const int jb = j0 + fr.wm * L::TM * 32 + m * 32;  // first d_ff index of the tile
+        const int c = c0 + fr.col(n);
+        store_tile_sb<kSnapSlab>(f, c, jb, acc[m * L::TN + n], CvtBf16{out_scale},
+                                 c < d && jb < f, sink);
+      }
+  }
+};
+
+// The update's hook: the exclusive-prefix snapshot at every chunk start.
+template <class L>
+struct ChunkSnapshots {
+  static constexpr int kStores = SnapshotStore<L>::kStores;
+  SnapshotStore<L> store;
+  u16* snap;  // this sequence's snapshots, or null
+  int64_t chunk_stride;
+  int steps_per_chunk;
+  __device__ __forceinline__ bool operator()(int kt, const f32x16* acc) const {
+    if (snap == nullptr || kt % steps_per_chunk != 0) return false;
+    store(snap + (int64_t)(kt / steps_per_chunk) * chunk_stride, acc);
+    return true;
   }
 };
 
@@ -586,7 +728,7 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
   const int j0 = ti.tm * K3_BM, c0 = ti.tn * K3_BN;
   const int d = g.d, f = g.f;
   const Frag<L> fr;
-  const int64_t chunk_stride = (int64_t)d * g.ld_s;
+  const int64_t chunk_stride = snap_elems(g);
   const float out_scale = 1.0f / acc_scale;
 
   f32x16 acc[TM][TN];
@@ -616,18 +758,17 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
         for (int e = 0; e < 4; ++e) acc[m][n][4 * q + e] = v[e] * acc_scale;
       }
 
-  SnapshotStore<L> snapshot{j0, c0, d, f, g.ld_s, out_scale};
-  u16* snap_b = snap ? snap + ti.b * snap_bstride : nullptr;
-  auto hook = [=](int kt, const f32x16* a) {
-    if (snap_b != nullptr && kt % steps_per_chunk == 0)
-      snapshot(snap_b + (int64_t)(kt / steps_per_chunk) * chunk_stride, a);
-  };
+  const SnapshotStore<L> snapshot{j0, c0, d, f, out_scale, (uint32_t)(chunk_stride * 2)};
+  const ChunkSnapshots<L> hook{snapshot, snap ? snap + ti.b * snap_bstride : nullptr,
+                               chunk_stride, steps_per_chunk};
   // Rows past d_ff / d_model in the last slabs are never written; they only
   // feed output rows / columns that are not stored.
-  const Operand vt = blocked<K3_BK>(VT + vt_offset(g, ti.b, c0, tok_begin), K3_BN, nk);
-  gemm_core<K3_BM, K3_BN, K3_WGM, K3_BK, K3_NST, F16Mma, false>(
-      blocked<K3_BK>(ZT + zt_offset(g, ti.b, j0, tok_begin), K3_BM, nk), vt, vt, nk, &acc[0][0],
-      lds, hook);
+  static_assert(K3_BM == kZtSlab && K3_BN == kVtSlab && K3_BK == 64, "update tile = slabs");
+  const Operand vt =
+      slab_blocked<kVtSlab>(VT + ti.b * sb_elems<kVtSlab>(d, g.T_pad), g.T_pad, c0, tok_begin);
+  gemm_core<K3_BM, K3_BN, K3_WGM, K3_BK, K3_NST, F16Mma, false, kSlab, kSlab>(
+      slab_blocked<kZtSlab>(ZT + ti.b * sb_elems<kZtSlab>(f, g.T_pad), g.T_pad, j0, tok_begin),
+      vt, vt, nk, &acc[0][0], lds, hook);
 
   float* wf_b = Wf + (int64_t)ti.b * d * f;
 #pragma unroll
@@ -662,8 +803,9 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
     int64_t snap_cstride, void* __restrict__ O, Dims g, int tok_begin, int chunk, int tiles_m,
     int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int BM = 256, WGM = ApplyCfg<BN>::WGM, BK = ApplyCfg<BN>::BK,
+  constexpr int BM = kSnapSlab, WGM = ApplyCfg<BN>::WGM, BK = ApplyCfg<BN>::BK,
                 NST = ApplyCfg<BN>::NST;
+  static_assert(BK == 64, "the snapshot slab is one K step");
   using L = Layout<BM, BN, WGM>;
   TTT_GEMM_LDS(lds, BM, BN, BK, NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
@@ -677,10 +819,9 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
   // The rotation uses the absolute token tile, so that every schedule runs
   // the same tile with the same summation order.
   const int nk = f / BK;
-  gemm_core<BM, BN, WGM, BK, NST, Bf16Mma, false>(
-      row_major<BK>(snap + ti.b * snap_bstride + i * snap_cstride + (int64_t)c0 * g.ld_s,
-                    g.ld_s, min(BM, d - c0)),
-      z, z, nk, &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, t0 / BN, nk));
+  gemm_core<BM, BN, WGM, BK, NST, Bf16Mma, false, kSlab, kRowMajor>(
+      slab_blocked<kSnapSlab>(snap + ti.b * snap_bstride + i * snap_cstride, f, c0, 0), z, z, nk,
+      &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, t0 / BN, nk));
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -898,6 +1039,8 @@ hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Win
                          uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
                          int chunk, hipStream_t s) {
   const int nk = (tok_count + K3_BK - 1) / K3_BK, steps_per_chunk = chunk / K3_BK;
+  // Token offsets and counts are whole K steps, so that the pair-blocked
+  // operands are read from a 16-token boundary.
   const int tiles_m = ceil_div(g.f, K3_BM), tiles_n = ceil_div(g.d, K3_BN);
   const int grid = tiles_m * tiles_n * g.B;
   if (winit_f32)

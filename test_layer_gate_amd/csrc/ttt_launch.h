@@ -1,19 +1,26 @@
 // Host-side launchers of the gfx950 kernels (internal to libttt_layer).
 // Every launcher enqueues one kernel on `s` and returns hipGetLastError().
 //
-// Workspace layouts (row-major; the *_ld row strides are padded so that a
-// row is an odd number of 128-byte lines, which spreads the rows of a tile
-// over the L2's sets instead of stacking them in one):
+// Workspace layouts. Row-major ones have their *_ld row strides padded so
+// that a row is an odd number of 128-byte lines, which spreads the rows of a
+// tile over the L2's sets instead of stacking them in one.
+// "sb<SR>" is the slab-blocked layout of a rows x K matrix (K a multiple of
+// 64): the matrix is cut into SR-row x 64-column slabs, stored
+// [ceil(rows/SR)][K/64] as contiguous SR * 128-byte blocks, so that one K
+// step of one GEMM tile of SR rows is one slab. Inside a slab, 1 KB blocks
+// [SR/32][4][2][32][8] hold 32 rows x 16 columns as two halves of 8 column
+// values per row. A wave stores an MFMA accumulator tile into it transposed
+// (the tile's M index becomes the column) with one contiguous 1 KB store per
+// instruction, and the GEMM core reads a slab back with K contiguous in
+// 16-byte pieces. Rows past `rows` in the last slab row are never written;
+// they only feed GEMM outputs that are not stored.
 //   Y   fp16 [B][T_pad][ld_y]   conv(X0); rows >= T are zero
 //   WtT fp16 [d][ld_y]          W_target transposed: WtT[o][i] = W_target[i][o]
 //   Z   bf16 [B][T][ld_z]       gated activation, token-major (the apply reads it)
-//   ZT  fp16 [B][f/256][T_pad/S][256][S]   the same, feature-major and blocked
-//                               for the update: each (256 d_ff rows x S tokens)
-//                               block is one contiguous slab, S = kTokStep, the
-//                               update's K step; tokens >= T are zero
-//   VT  fp16 [B][d/128][T_pad/S][128][S]   vscale * V, blocked the same way
-//                               (128 d_model rows per slab); tokens >= T zero
-//   S   bf16 [B][k][d][ld_s]    per-chunk snapshots of the state
+//   ZT  fp16 [B] x sb<256>(f x T_pad)   the same, feature-major, for the
+//                               update; tokens >= T are zero
+//   VT  fp16 [B] x sb<128>(d x T_pad)   vscale * V, feature-major; tokens >= T zero
+//   S   bf16 [B][k] x sb<256>(d x f)    per-chunk snapshots of the state
 //   Wgp, Wup  bf16 [f_pad/128][d/64][128][64]   W_g and W_u packed for the
 //                               gate/up GEMM: each (128 rows x 64 columns) block
 //                               is one contiguous 16 KB slab, one K step of one
@@ -27,9 +34,9 @@
 namespace tttk {
 
 constexpr int kTokenPad = 256;
-constexpr int kZtRows = 256;  // d_ff rows per ZT slab = the update tile's M
-constexpr int kVtRows = 128;  // d_model rows per VT slab = the update tile's N
-constexpr int kTokStep = 64;  // tokens per slab = one K step of the update
+constexpr int kZtSlab = 256;    // ZT slab rows = the update tile's M
+constexpr int kVtSlab = 128;    // VT slab rows = the update tile's N
+constexpr int kSnapSlab = 256;  // snapshot slab rows = the apply tile's M
 constexpr int kWRows = 128;   // W_g / W_u rows per packed slab = half the gate/up tile's N
 constexpr int kGateBK = 64;   // d_model elements per packed slab = one K step of gate/up
 
@@ -39,8 +46,7 @@ inline int64_t pad_ld(int64_t n) { return ((n / 64) % 2 == 0) ? n + 64 : n; }
 
 struct Dims {
   int B, T, T_pad, d, f;
-  int nts, nfb, ndb;  // token steps, ZT row blocks, VT row blocks
-  int64_t ld_y, ld_z, ld_s;
+  int64_t ld_y, ld_z;
 };
 
 inline Dims make_dims(int B, int T, int d, int f) {
@@ -50,29 +56,33 @@ inline Dims make_dims(int B, int T, int d, int f) {
   g.T_pad = (T + kTokenPad - 1) / kTokenPad * kTokenPad;
   g.d = d;
   g.f = f;
-  g.nts = g.T_pad / kTokStep;
-  g.nfb = (f + kZtRows - 1) / kZtRows;
-  g.ndb = (d + kVtRows - 1) / kVtRows;
   g.ld_y = pad_ld(d);
   g.ld_z = pad_ld(f);
-  g.ld_s = pad_ld(f);
   return g;
 }
 
-// Element offsets in the blocked ZT / VT buffers.
-__host__ __device__ inline int64_t zt_offset(const Dims& g, int b, int j, int t) {
-  return (((int64_t)b * g.nfb + j / kZtRows) * g.nts + t / kTokStep) * (kZtRows * kTokStep) +
-         (int64_t)(j % kZtRows) * kTokStep + t % kTokStep;
+// Element offset of (r, k) in an sb<SR> matrix with K columns.
+template <int SR>
+__host__ __device__ inline int64_t sb_offset(int64_t r, int64_t k, int64_t K) {
+  static_assert(SR % 32 == 0, "slab rows");
+  const int64_t slab = (r / SR) * (K >> 6) + (k >> 6);
+  const int64_t rr = r % SR;
+  return slab * (SR * 64) + ((rr >> 5) * 4 + ((k & 63) >> 4)) * 512 +
+         (((k >> 3) & 1) * 32 + (rr & 31)) * 8 + (k & 7);
 }
-__host__ __device__ inline int64_t vt_offset(const Dims& g, int b, int c, int t) {
-  return (((int64_t)b * g.ndb + c / kVtRows) * g.nts + t / kTokStep) * (kVtRows * kTokStep) +
-         (int64_t)(c % kVtRows) * kTokStep + t % kTokStep;
+// Elements of an sb<SR> matrix of `rows` rows and K columns.
+template <int SR>
+__host__ __device__ inline int64_t sb_elems(int64_t rows, int64_t K) {
+  return (rows + SR - 1) / SR * SR * K;
 }
-inline int64_t zt_elems(const Dims& g) { return (int64_t)g.B * g.nfb * kZtRows * g.T_pad; }
+inline int64_t zt_elems(const Dims& g) { return (int64_t)g.B * sb_elems<kZtSlab>(g.f, g.T_pad); }
+inline int64_t vt_elems(const Dims& g) { return (int64_t)g.B * sb_elems<kVtSlab>(g.d, g.T_pad); }
+__host__ __device__ inline int64_t snap_elems(const Dims& g) {
+  return sb_elems<kSnapSlab>(g.d, g.f);
+}
 inline int64_t wpack_elems(const Dims& g) {
   return (int64_t)((g.f + kWRows - 1) / kWRows) * kWRows * g.d;
 }
-inline int64_t vt_elems(const Dims& g) { return (int64_t)g.B * g.ndb * kVtRows * g.T_pad; }
 
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 
@@ -102,14 +112,16 @@ hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
                          float vscale, const Dims& g, hipStream_t s);
 
-// Fast-weight update over tokens [tok_begin, tok_begin + tok_count), in
-// kTokStep-token steps (columns past T read as zero). acc = acc_scale * Winit;
-// before each step that starts a chunk (every chunk / kTokStep steps), if snap !=
-// null, that chunk's snapshot = bf16(acc / acc_scale); then acc += the
-// step's ZT x VT contraction over tokens. Finally Wf = acc / acc_scale and,
-// if shadow != null, shadow = bf16(acc / acc_scale). tok_count may be 0.
-// Winit element (b, c, j) is at b * winit_bstride + c * winit_ld + j.
-// acc_scale must be a power of two (the scalings are then exact). nk may be 0.
+// Fast-weight update over tokens [tok_begin, tok_begin + tok_count) (a
+// multiple of 64), in 64-token steps (columns past T read as zero). acc =
+// acc_scale * Winit; before each step that starts a chunk (every chunk / 64
+// steps), if snap != null, that chunk's snapshot (sb<256>(d x f), at snap +
+// b * snap_bstride + chunk * snap_elems) = bf16(acc / acc_scale); then acc
+// += the step's ZT x VT contraction over tokens. Finally Wf = acc /
+// acc_scale (row-major [B][d][f]) and, if shadow != null, shadow =
+// bf16(acc / acc_scale) (sb<256>(d x f) per sequence). tok_count may be 0. Winit element
+// (b, c, j) is at b * winit_bstride + c * winit_ld + j. acc_scale must be a
+// power of two (the scalings are then exact).
 hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
                          bool winit_f32, int64_t winit_bstride, int64_t winit_ld,
                          float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
@@ -117,8 +129,8 @@ hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Win
                          int chunk, hipStream_t s);
 
 // O[b][t] = Z[b][t] W_i^T for tokens t in [tok_begin, tok_end), where W_i is
-// the bf16 state at snap + b * snap_bstride + (t / chunk) * snap_cstride,
-// with row stride ld_s.
+// the bf16 state (sb<256>(d x f)) at snap + b * snap_bstride + (t / chunk) *
+// snap_cstride.
 hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bstride,
                         int64_t snap_cstride, void* O, bool out_f32, const Dims& g,
                         int tok_begin, int tok_end, int chunk, hipStream_t s);

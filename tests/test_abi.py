@@ -67,10 +67,12 @@ def test_workspace_size_matches_layout(L):
     def pad(x):  # rows padded to an odd number of 128-byte lines
         return x + 64 if (x // 64) % 2 == 0 else x
     ld_y, ld_f = pad(d), pad(f)
-    # Y, W_target^T, Z, blocked Z^T and V^T (whole 256- / 128-row slabs), snapshots,
-    # packed W_g and W_u (whole 128-row slabs)
-    expect = (B * T * ld_y * 2 + d * ld_y * 2 + B * T * ld_f * 2 + B * (-(-f // 256) * 256) * T * 2
-              + B * (-(-d // 128) * 128) * T * 2 + B * k * d * ld_f * 2
+    def sb(rows, K, SR):  # slab-blocked: whole SR-row slabs
+        return -(-rows // SR) * SR * K
+    # Y, W_target^T, Z, Z^T and V^T, snapshots, packed W_g and W_u (whole
+    # 128-row slabs)
+    expect = (B * T * ld_y * 2 + d * ld_y * 2 + B * T * ld_f * 2 + B * sb(f, T, 256) * 2
+              + B * sb(d, T, 128) * 2 + B * k * sb(d, f, 256) * 2
               + 2 * (-(-f // 128) * 128) * d * 2)
     assert expect <= n <= expect + 16 * 256
     st, n_run = ws_size(L, qwen_desc(flags=bnd.FLAG_SCHED_RUNNING), 1024)
