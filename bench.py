@@ -130,15 +130,31 @@ def summarize(args):
     """Write a markdown summary of rocprofv3 results (and, with --fetch and
     --write, the per-launch HBM traffic record used by the bench line)."""
     stats = _read_csv(_find(args.summarize, "kernel_stats.csv"))
+    # Per-dispatch durations, to average the timed steps alone: the profiled
+    # command runs prof_warmup + prof_steps steps of the same launches.
+    durs = {}
+    for r in _read_csv(_find(args.summarize, "kernel_trace.csv")):
+        durs.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    n_steps = args.prof_steps + args.prof_warmup
     lines = [f"# rocprofv3 kernel summary: {args.title}", "",
              f"Command: `{args.command}`", "",
              f"Kernel source sha256[:16]: `{source_hash()}`", "",
-             "| kernel | calls | avg us | min us | max us | total ms | share |",
-             "|---|---|---|---|---|---|---|"]
+             f"\"timed avg\" leaves out the dispatches of the {args.prof_warmup} warm-up "
+             f"step(s) (kernels launched once per step of the {n_steps}).", "",
+             "| kernel | calls | avg us | timed avg us | min us | max us | total ms | share |",
+             "|---|---|---|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append("| {} | {} | {:.1f} | {:.1f} | {:.1f} | {:.3f} | {:.1f}% |".format(
-            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-            float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+        d = [x[1] for x in sorted(durs.get(r["Name"], []))]
+        timed = "-"
+        if d and len(d) % n_steps == 0:
+            per = len(d) // n_steps
+            rest = d[per * args.prof_warmup:]
+            timed = f"{sum(rest) / len(rest) / 1e3:.1f}"
+        lines.append("| {} | {} | {:.1f} | {} | {:.1f} | {:.1f} | {:.3f} | {:.1f}% |".format(
+            r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, timed,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
     if args.fetch and args.write:
         per = {}
         for which, d in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
@@ -192,6 +208,8 @@ def main():
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory")
     ap.add_argument("--summary-out")
+    ap.add_argument("--prof-steps", type=int, default=5, help="--steps of the profiled command")
+    ap.add_argument("--prof-warmup", type=int, default=1, help="--warmup of the profiled command")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", default="")
     ap.add_argument("--fetch-command", default="")

@@ -541,12 +541,14 @@ struct CvtBf16 {
   }
 };
 
-// K-step rotation of the tile at absolute tile coordinates (tm, tn): the
-// workgroups resident on one XCD cover 4 tile rows x 8 tile columns (see
-// tile_index), and offsets that differ along both directions stagger every
-// shared A and B slab.
+// K-step rotation of the tile at absolute tile coordinates (tm, tn) when the
+// workgroups resident on one XCD cover GM tile rows x 32 / GM tile columns
+// (tile_index with group_m = GM): offsets that differ along both directions
+// stagger every shared A and B slab.
+template <int GM>
 __device__ __forceinline__ int k_rotation(int tm, int tn, int nk) {
-  return ((tm & 3) + (tn & 7)) % nk;
+  static_assert(GM >= 1 && 32 % GM == 0, "group");
+  return ((tm % GM) + (tn % (32 / GM))) % nk;
 }
 
 // ------------------------------------------------ gate/up + SiLU*mul (K1)
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
   gemm_core<K1_BM, K1_BN, K1_WGM, K1_BK, K1_NST, Bf16Mma, true, kRowMajor, kRowMajor>(
       row_major<K1_BK>(H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0)),
       blocked<K1_BK>(Wgp + wslab, kWRows, nk), blocked<K1_BK>(Wup + wslab, kWRows, nk), nk,
-      &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, ti.tn, nk));
+      &acc[0][0], lds, NoHook{}, k_rotation<4>(ti.tm, ti.tn, nk));
   const Frag<L> fr;
   // Token-major Z goes through LDS so that its stores are whole 16-byte row
   // segments.
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
   const int nk = d / K2_BK;
   gemm_core<K2_BM, K2_BN, K2_WGM, K2_BK, K2_NST, F16Mma, false, kRowMajor, kRowMajor>(
       row_major<K2_BK>(Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM), wt, wt, nk,
-      &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, ti.tn, nk));
+      &acc[0][0], lds, NoHook{}, k_rotation<4>(ti.tm, ti.tn, nk));
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -790,6 +792,10 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
 // ------------------------------------------------------------ apply (K4)
 // M = d_model (256), N = tokens (BN, which divides the chunk), K = d_ff.
 // The tile's tokens all lie in one chunk i and read snapshot i.
+// The XCD's resident apply tiles: 8 d_model tiles x 4 token tiles, which
+// (with 256-token tiles) share one chunk's snapshot slabs.
+constexpr int kApplyGroupM = 8;
+
 template <int BN>
 struct ApplyCfg {
   static constexpr int WGM =
@@ -808,7 +814,7 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
   static_assert(BK == 64, "the snapshot slab is one K step");
   using L = Layout<BM, BN, WGM>;
   TTT_GEMM_LDS(lds, BM, BN, BK, NST)
-  const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
+  const TileIdx ti = tile_index(tiles_m, tiles_n, kApplyGroupM);
   const int c0 = ti.tm * BM, t0 = tok_begin + ti.tn * BN;
   const int i = t0 / chunk;
   const int d = g.d, f = g.f, T = g.T;
@@ -821,7 +827,7 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
   const int nk = f / BK;
   gemm_core<BM, BN, WGM, BK, NST, Bf16Mma, false, kSlab, kRowMajor>(
       slab_blocked<kSnapSlab>(snap + ti.b * snap_bstride + i * snap_cstride, f, c0, 0), z, z, nk,
-      &acc[0][0], lds, NoHook{}, k_rotation(ti.tm, t0 / BN, nk));
+      &acc[0][0], lds, NoHook{}, k_rotation<kApplyGroupM>(ti.tm, t0 / BN, nk));
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
