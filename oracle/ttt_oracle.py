@@ -31,13 +31,19 @@ tested by the pins in tests/test_oracle.py):
   * Each sequence of the batch has its own state, starting from W_down0.
   * A last chunk shorter than C is allowed. The returned final state includes
     the last chunk's update.
+  * Packed documents ([iplex] §6, document boundaries): a sequence may hold
+    several documents back to back, given by their start offsets. At each
+    document start the state returns to W_down0 and the chunking restarts,
+    and the conv reads nothing past the token's own document (nor past its
+    chunk, with chunk padding). The returned final state is the one after
+    the last document.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["silu", "gated_activation", "conv_target_input", "lm_target",
-           "ttt_prefill", "activation_rows", "target_rows",
+           "ttt_prefill", "ttt_prefill_packed", "activation_rows", "target_rows",
            "final_state_entries"]
 
 
@@ -135,6 +141,71 @@ def ttt_prefill(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
             W = W + eta * (V[rows].T @ Z[rows])        # then update
         W_final[b] = W
     return O, W_final
+
+
+def ttt_prefill_packed(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
+                       doc_starts, pad="sequence"):
+    """Prefill of one packed sequence holding several documents.
+
+    [iplex] §6: the fast weight is reset to the pretrained W_down at every
+    document boundary, so documents do not leak into each other; the conv
+    target stops at the boundary as it does at the end of a sequence.
+    Written token by token over the packed sequence: each token is assigned
+    its document r (doc_starts[r] <= t < doc_starts[r + 1], the last one
+    running to T) and its chunk, counted from the document's start; the
+    state is set to W_down0 when a document begins and stepped at the end of
+    each chunk.
+
+    H [T, d]; X0 [T, d]; Wg, Wu [f, d]; W_down0 [d, f]; taps [K, d];
+    W_target [d, d]; doc_starts: increasing offsets, the first 0. Returns
+    O [T, d] and the state after the last document [d, f], float64.
+    """
+    H, X0, taps = _f64(H), _f64(X0), _f64(taps)
+    W0, Wt = _f64(W_down0), _f64(W_target)
+    T, d = H.shape
+    K = taps.shape[0]
+    starts = [int(s) for s in doc_starts]
+    if not starts or starts[0] != 0 or any(b <= a for a, b in zip(starts, starts[1:])) \
+            or starts[-1] >= T:
+        raise ValueError("doc_starts must increase from 0 and stay below T")
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    bounds = starts + [T]
+    doc_end = np.zeros(T, dtype=np.int64)     # first token after t's document
+    chunk_end = np.zeros(T, dtype=np.int64)   # first token after t's chunk
+    chunk_id = np.zeros(T, dtype=np.int64)    # running chunk index over documents
+    n_chunks = 0
+    for r in range(len(starts)):
+        a, e = bounds[r], bounds[r + 1]
+        for t in range(a, e):
+            c = (t - a) // chunk
+            doc_end[t] = e
+            chunk_end[t] = min(e, a + (c + 1) * chunk)
+            chunk_id[t] = n_chunks + c
+        n_chunks += -(-(e - a) // chunk)
+    # Target: Y[t] = sum_k taps[k] * X0[t + k] over reads before the bound.
+    limit = doc_end if pad == "sequence" else chunk_end
+    if pad not in ("sequence", "chunk"):
+        raise ValueError(pad)
+    Y = np.zeros((T, d))
+    for t in range(T):
+        for k in range(K):
+            if t + k < limit[t]:
+                Y[t] += taps[k] * X0[t + k]
+    V = Y @ Wt
+    Z = gated_activation(H, Wg, Wu)
+    O = np.zeros((T, d))
+    W = W0.copy()
+    t = 0
+    while t < T:
+        if t in starts:
+            W = W0.copy()                       # document start: reset
+        rows = slice(t, int(chunk_end[t]))
+        O[rows] = Z[rows] @ W.T                 # apply with the pre-update state
+        W = W + eta * (V[rows].T @ Z[rows])     # then update
+        t = int(chunk_end[t])
+    assert n_chunks == int(chunk_id[-1]) + 1
+    return O, W
 
 
 # ---------------------------------------------------------------------------

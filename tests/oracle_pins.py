@@ -335,7 +335,68 @@ def pin_golden_ntp_fixture():
     assert np.array_equal(V, np.array(blocks["V_expected"])), "golden NTP"
 
 
+# ---- packed documents ([iplex] §6, reset at document boundaries) ----------
+
+PACKED_DOCS = ([0, 13, 30, 31], [0, 8, 24], [0, 20])  # lengths below, at and above C = 8
+
+
+def run_packed(x, starts, pad="sequence", b=0):
+    return ora.ttt_prefill_packed(x["H"][b], x["X0"][b], x["Wg"], x["Wu"], x["W_down0"],
+                                  x["taps"], x["W_target"], x["eta"], x["chunk"], starts,
+                                  pad=pad)
+
+
+def pin_packed_single_document():
+    """One document covering the sequence is the plain prefill of that
+    sequence (the packed form is written token by token, the plain one chunk
+    by chunk)."""
+    x = small_case(seed=21, B=1, T=29)
+    for pad in ("sequence", "chunk"):
+        O, W = run_packed(x, [0], pad)
+        O_ref, W_ref = run(x, pad=pad)
+        _close(O, O_ref[0], what=f"packed single O ({pad})")
+        _close(W, W_ref[0], what=f"packed single W ({pad})")
+
+
+def pin_packed_equals_documents():
+    """[iplex] §6: a packed sequence equals its documents run one by one from
+    W_down0, each on its own tokens only (no look-ahead into the next
+    document); the returned state is the last document's."""
+    x = small_case(seed=22, B=1, T=40)
+    for starts in PACKED_DOCS:
+        for pad in ("sequence", "chunk"):
+            O, W = run_packed(x, starts, pad)
+            bounds = list(starts) + [40]
+            for a, e in zip(bounds, bounds[1:]):
+                sub = dict(x, H=x["H"][:, a:e], X0=x["X0"][:, a:e])
+                O_ref, W_ref = run(sub, pad=pad)
+                _close(O[a:e], O_ref[0], what=f"document [{a},{e}) O ({pad})")
+            _close(W, W_ref[0], what=f"final state after {starts} ({pad})")
+
+
+def pin_packed_isolation():
+    """No information crosses a document boundary in either direction:
+    changing the tokens of one document changes no output of another (a
+    missing reset leaks forwards; a conv read past the boundary leaks
+    backwards)."""
+    x = small_case(seed=23, B=1, T=40)
+    starts = [0, 13, 30]
+    O, _ = run_packed(x, starts)
+    rng = np.random.default_rng(5)
+    for a, e in ((0, 13), (13, 30), (30, 40)):
+        y = dict(x, H=x["H"].copy(), X0=x["X0"].copy())
+        y["H"][0, a:e] += rng.standard_normal((e - a, x["H"].shape[2]))
+        y["X0"][0, a:e] += rng.standard_normal((e - a, x["X0"].shape[2]))
+        O2, _ = run_packed(y, starts)
+        keep = np.ones(40, bool)
+        keep[a:e] = False
+        assert np.array_equal(O[keep], O2[keep]), f"document [{a},{e}) leaked"
+        assert not np.allclose(O[a:e], O2[a:e]), f"document [{a},{e}) ignored its input"
+
+
 ALL_PINS = [pin_reduces_to_plain_mlp, pin_prefix_scan_form, pin_state_free_form,
             pin_next_token_target, pin_conv_library, pin_linear_in_eta,
             pin_chunk_causality, pin_batch_independence, pin_split_resume,
-            pin_brute_force_scalars, pin_sampled_forms, pin_golden_ntp_fixture]
+            pin_brute_force_scalars, pin_sampled_forms, pin_golden_ntp_fixture,
+            pin_packed_single_document, pin_packed_equals_documents,
+            pin_packed_isolation]

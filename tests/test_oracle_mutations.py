@@ -69,7 +69,55 @@ def _conv_ignores_chunk(X0, taps, pad="sequence", chunk=None, n_out=None):
     return _real_conv(X0, taps, "sequence", chunk, n_out)
 
 
+_real_packed = ora.ttt_prefill_packed
+
+
+def _packed_variant(reset=True, conv_stops=True, chunks_from_doc=True):
+    """A copy of the packed recurrence with one knob turned away from the
+    pages: no state reset at a document start, a conv that reads across the
+    boundary, or chunks counted from token 0 instead of the document start."""
+    def packed(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk, doc_starts,
+               pad="sequence"):
+        H, X0, taps = (np.asarray(a, np.float64) for a in (H, X0, taps))
+        W0 = np.asarray(W_down0, np.float64)
+        T, d = H.shape
+        starts = list(doc_starts)
+        bounds = starts + [T]
+        cuts = set()
+        for a, e in zip(bounds, bounds[1:]):
+            base = a if chunks_from_doc else 0
+            cuts.update(c for c in range(base, e, chunk) if c >= a)
+            cuts.add(a)
+        cuts = sorted(cuts) + [T]
+        doc_end = np.zeros(T, int)
+        for a, e in zip(bounds, bounds[1:]):
+            doc_end[a:e] = e
+        chunk_end = np.zeros(T, int)
+        for a, e in zip(cuts, cuts[1:]):
+            chunk_end[a:e] = e
+        lim = (doc_end if conv_stops else np.full(T, T)) if pad == "sequence" else chunk_end
+        Y = np.zeros((T, d))
+        for t in range(T):
+            for k in range(taps.shape[0]):
+                if t + k < lim[t]:
+                    Y[t] += taps[k] * X0[t + k]
+        V = Y @ np.asarray(W_target, np.float64)
+        Z = ora.gated_activation(H, Wg, Wu)
+        O = np.zeros((T, d))
+        W = W0.copy()
+        for a, e in zip(cuts, cuts[1:]):
+            if reset and a in starts:
+                W = W0.copy()
+            O[a:e] = Z[a:e] @ W.T
+            W = W + eta * (V[a:e].T @ Z[a:e])
+        return O, W
+    return packed
+
+
 MUTATIONS = {
+    "packed_no_reset": ("ttt_prefill_packed", _packed_variant(reset=False)),
+    "packed_conv_crosses_documents": ("ttt_prefill_packed", _packed_variant(conv_stops=False)),
+    "packed_chunks_from_token_0": ("ttt_prefill_packed", _packed_variant(chunks_from_doc=False)),
     "inclusive_prefix_leak": ("ttt_prefill", _prefill_variant(order="update_first")),
     "skip_update": ("ttt_prefill", _prefill_variant(scale=0.0)),
     "normalise_by_chunk": ("ttt_prefill", _prefill_variant(scale=1.0 / 8)),
