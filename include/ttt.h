@@ -118,6 +118,34 @@ ttt_status ttt_layer_forward(const ttt_desc* desc,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Packed documents: one sequence (batch must be 1) holding n_docs
+ * documents back to back, document r starting at token doc_starts[r]
+ * (iplexlaw explainer §6: the fast weight returns to the pretrained W_down
+ * at every document boundary, so documents do not leak into each other).
+ * Each document is processed as its own sequence: the state starts from
+ * W_down0, the chunks of C tokens are counted from the document's start
+ * (its last chunk may be shorter), and the conv reads no row past the
+ * document's end (nor past the chunk's end with TTT_FLAG_PAD_CHUNK).
+ *   doc_starts  host array of n_docs int32: 0 = doc_starts[0] < doc_starts[1]
+ *               < ... < seq_len, every entry a multiple of 64
+ *               (TTT_ERR_UNSUPPORTED otherwise); read during the call only
+ *   W_down_final [d, f] float32 out: the state after the last document
+ * Everything else as ttt_layer_forward; the workspace also holds a small
+ * per-64-token table, copied from the host with hipMemcpyAsync on the
+ * stream (staged from pageable memory before the call returns). */
+ttt_status ttt_packed_workspace_size(const ttt_desc* desc, int32_t chunk,
+                                     const int32_t* doc_starts, int32_t n_docs,
+                                     size_t* bytes);
+ttt_status ttt_layer_forward_packed(const ttt_desc* desc,
+                                    const void* H, const void* X0,
+                                    const void* Wg, const void* Wu,
+                                    const void* W_down0, const void* conv_taps,
+                                    const void* W_target, float eta, int32_t chunk,
+                                    const int32_t* doc_starts, int32_t n_docs,
+                                    void* O, float* W_down_final,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Step entry points: one step of the layer each, for per-step checks.
  * ttt_gated_activation writes Z [B, T, d_ff] in bf16.
  * ttt_lm_target writes V [B, T, d_model] in bf16 (unscaled, eta not applied).

@@ -14,15 +14,18 @@ from ._binding import (  # noqa: F401
     copy_calibration,
     gated_activation,
     layer_forward,
+    layer_forward_packed,
     lib,
     lm_target,
     make_desc,
+    packed_workspace_size,
     profile_enable,
     profile_read,
     workspace_size,
 )
 
-__all__ = ["layer_forward", "gated_activation", "lm_target", "workspace_size",
+__all__ = ["layer_forward", "layer_forward_packed", "packed_workspace_size",
+           "gated_activation", "lm_target", "workspace_size",
            "copy_calibration",
            "make_desc", "profile_enable", "profile_read", "TTTError", "lib",
            "LIB_PATH"]

@@ -61,9 +61,16 @@ def lib() -> ctypes.CDLL:
     L.ttt_step_workspace_size.argtypes = [DP, ctypes.POINTER(_S)]
     L.ttt_layer_forward.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                     ctypes.c_int32, _P, _P, _P, _S, _P]
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    L.ttt_packed_workspace_size.argtypes = [DP, ctypes.c_int32, I32P, ctypes.c_int32,
+                                            ctypes.POINTER(_S)]
+    L.ttt_layer_forward_packed.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                           ctypes.c_int32, I32P, ctypes.c_int32, _P, _P, _P,
+                                           _S, _P]
     L.ttt_gated_activation.argtypes = [DP, _P, _P, _P, _P, _P, _S, _P]
     L.ttt_lm_target.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _S, _P]
     for fn in ("ttt_workspace_size", "ttt_step_workspace_size", "ttt_layer_forward",
+               "ttt_packed_workspace_size", "ttt_layer_forward_packed",
                "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
         getattr(L, fn).restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int32]
@@ -183,6 +190,66 @@ def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
         _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk),
         _ptr(O), _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream)))
     return O, Wf
+
+
+def _doc_array(doc_starts):
+    starts = [int(v) for v in doc_starts]
+    return (ctypes.c_int32 * max(len(starts), 1))(*starts), len(starts)
+
+
+def packed_workspace_size(desc: Desc, chunk: int, doc_starts) -> int:
+    arr, n_docs = _doc_array(doc_starts)
+    n = _S(0)
+    _check(lib().ttt_packed_workspace_size(ctypes.byref(desc), chunk, arr, n_docs,
+                                           ctypes.byref(n)))
+    return n.value
+
+
+def layer_forward_packed(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk,
+                         doc_starts, *, schedule=None, pad="sequence", out=None,
+                         W_down_final=None, workspace=None, stream=None):
+    """O, W_final for one packed sequence of documents (include/ttt.h,
+    ttt_layer_forward_packed). H, X0 [T, d] or [1, T, d]; doc_starts: the
+    documents' first tokens, increasing from 0, multiples of 64. O has H's
+    shape; W_final is [d, f] (or [1, d, f] for 3-D H): the state after the
+    last document."""
+    _require_cuda(H, X0, Wg, Wu, W_down0, conv_taps, W_target)
+    squeeze = H.dim() == 2
+    H3 = H.unsqueeze(0) if squeeze else H
+    X3 = X0.unsqueeze(0) if X0.dim() == 2 else X0
+    if H3.dim() != 3 or H3.shape[0] != 1 or X3.shape != H3.shape:
+        raise ValueError("H and X0 must both be [T, d] or [1, T, d]")
+    _, T, d = H3.shape
+    f = Wg.shape[0]
+    K = conv_taps.shape[0]
+    if Wg.shape != (f, d) or Wu.shape != (f, d) or W_down0.shape != (d, f):
+        raise ValueError("Wg, Wu must be [d_ff, d_model] and W_down0 [d_model, d_ff]")
+    if conv_taps.shape != (K, d) or W_target.shape != (d, d):
+        raise ValueError("conv_taps must be [K, d_model] and W_target [d_model, d_model]")
+    act = _dtype_code(H3, "H")
+    wt = _dtype_code(Wg, "Wg")
+    if X3.dtype != H3.dtype:
+        raise TypeError("X0 must have H's dtype")
+    for t, n in ((Wu, "Wu"), (W_down0, "W_down0"), (conv_taps, "conv_taps"),
+                 (W_target, "W_target")):
+        if t.dtype != Wg.dtype:
+            raise TypeError(f"{n} must have Wg's dtype")
+    if not math.isfinite(float(eta)):
+        raise ValueError("eta must be finite")
+    desc = make_desc(1, T, d, f, K, act, wt, 0, _flags(schedule, pad))
+    arr, n_docs = _doc_array(doc_starts)
+    ws_bytes = packed_workspace_size(desc, int(chunk), doc_starts)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
+    O = torch.empty_like(H3) if out is None else out.view(1, T, d)
+    Wf = (torch.empty((1, d, f), dtype=torch.float32, device=H.device)
+          if W_down_final is None else W_down_final.view(1, d, f))
+    _require_cuda(O, Wf, workspace)
+    _check(lib().ttt_layer_forward_packed(
+        ctypes.byref(desc), _ptr(H3), _ptr(X3), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
+        _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk), arr, n_docs,
+        _ptr(O), _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return (O[0], Wf[0]) if squeeze else (O, Wf)
 
 
 def _step_ws(desc, device):

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -68,17 +69,27 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
 
 // ------------------------------------------------------------ geometry
 
+// A chunk of the schedule: tokens [t0, t1), and whether it starts a document.
+struct Chunk {
+  int t0, t1;
+  bool doc_start;
+};
+
 struct Geo {
   int64_t B, T, d, f, K, C, T_pad, nchunks;
   bool act_f32, w_f32, pad_chunk, running;
   int64_t w0_stride;  // elements
   tttk::Dims dims;
+  std::vector<Chunk> chunks;
+  std::vector<tttk::BlockInfo> blocks;     // packed documents only: per 64-token block
+  std::vector<tttk::ApplyTile> tiles;      // packed documents only: the apply's token tiles
   size_t act_bytes() const { return act_f32 ? 4 : 2; }
   size_t w_bytes() const { return w_f32 ? 4 : 2; }
 };
 
 struct Layout {
-  size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgp = 0, wup = 0;
+  size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgp = 0, wup = 0,
+         blk = 0;
   size_t total = 0;
 };
 
@@ -106,6 +117,9 @@ Layout forward_layout(const Geo& g) {
   }
   L.wgp = take(tttk::wpack_elems(D) * 2);
   L.wup = take(tttk::wpack_elems(D) * 2);
+  if (!g.blocks.empty())
+    L.blk = take(g.blocks.size() * sizeof(tttk::BlockInfo) +
+                 g.tiles.size() * sizeof(tttk::ApplyTile));
   L.total = off;
   return L;
 }
@@ -189,6 +203,55 @@ ttt_status check_chunk(int32_t chunk, Geo* g) {
   if (chunk % 64 != 0) return fail(TTT_ERR_UNSUPPORTED, "chunk must be a multiple of 64");
   g->C = chunk;
   g->nchunks = (g->T + chunk - 1) / chunk;
+  g->chunks.clear();
+  for (int64_t t = 0; t < g->T; t += chunk)
+    g->chunks.push_back({(int)t, (int)std::min<int64_t>(g->T, t + chunk), t == 0});
+  return TTT_OK;
+}
+
+// Packed documents: one sequence holding n_docs documents that start at
+// doc_starts[r]. Chunks restart at every document start; builds the chunk
+// list and the per-64-token block table the kernels read.
+ttt_status check_docs(const int32_t* doc_starts, int32_t n_docs, Geo* g) {
+  if (g->B != 1) return fail(TTT_ERR_UNSUPPORTED, "packed documents need batch == 1");
+  if (doc_starts == nullptr) return fail(TTT_ERR_INVALID_ARG, "doc_starts is NULL");
+  if (n_docs < 1) return fail(TTT_ERR_INVALID_ARG, "n_docs must be >= 1");
+  if (doc_starts[0] != 0) return fail(TTT_ERR_INVALID_ARG, "doc_starts[0] must be 0");
+  for (int32_t r = 1; r < n_docs; ++r) {
+    if (doc_starts[r] <= doc_starts[r - 1] || doc_starts[r] >= g->T)
+      return fail(TTT_ERR_INVALID_ARG,
+                  "doc_starts must increase and stay below seq_len (entry " +
+                      std::to_string(r) + ")");
+    if (doc_starts[r] % 64 != 0)
+      return fail(TTT_ERR_UNSUPPORTED, "document starts must be multiples of 64 (entry " +
+                                           std::to_string(r) + ")");
+  }
+  const int C = (int)g->C;
+  const int64_t nblk = g->T_pad / 64;
+  g->chunks.clear();
+  g->blocks.assign(nblk, tttk::BlockInfo{0, 0, (int32_t)g->T, (int32_t)g->T});
+  for (int32_t r = 0; r < n_docs; ++r) {
+    const int a = doc_starts[r], e = r + 1 < n_docs ? doc_starts[r + 1] : (int)g->T;
+    for (int t0 = a; t0 < e; t0 += C) {
+      const int t1 = std::min(e, t0 + C);
+      const int32_t idx = (int32_t)g->chunks.size();
+      g->chunks.push_back({t0, t1, t0 == a});
+      for (int t = t0; t < t1; t += 64)
+        g->blocks[t / 64] = {idx,
+                             (t == t0 ? tttk::kBlockChunkStart : 0) |
+                                 (t == a ? tttk::kBlockDocStart : 0),
+                             e, t1};
+    }
+  }
+  g->nchunks = (int64_t)g->chunks.size();
+  for (int64_t b = (g->T + 63) / 64; b < nblk; ++b) g->blocks[b].chunk = (int32_t)g->nchunks - 1;
+  // The apply's token tiles start at every chunk start; a chunk's last tile
+  // may be partial.
+  const int bn = tttk::apply_tile_width(C);
+  g->tiles.clear();
+  for (size_t i = 0; i < g->chunks.size(); ++i)
+    for (int t = g->chunks[i].t0; t < g->chunks[i].t1; t += bn)
+      g->tiles.push_back({t, std::min(g->chunks[i].t1, t + bn), (int32_t)i, 0});
   return TTT_OK;
 }
 
@@ -279,14 +342,16 @@ ttt_status ttt_step_workspace_size(const ttt_desc* desc, size_t* bytes) {
   return TTT_OK;
 }
 
-ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0,
-                             const void* Wg, const void* Wu, const void* W_down0,
-                             const void* conv_taps, const void* W_target, float eta,
-                             int32_t chunk, void* O, float* W_down_final, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  Geo g;
-  TTT_TRY(check_desc(desc, &g));
-  TTT_TRY(check_chunk(chunk, &g));
+}  // extern "C"
+
+namespace {
+
+// Everything after the descriptor, chunk (or document) checks: pointer and
+// workspace checks, then the launches of the whole layer.
+ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void* Wg,
+                        const void* Wu, const void* W_down0, const void* conv_taps,
+                        const void* W_target, float eta, void* O, float* W_down_final,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
   TTT_TRY(check_ptr(H, "H"));
   TTT_TRY(check_ptr(X0, "X0"));
@@ -321,6 +386,32 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
   hipStream_t s = static_cast<hipStream_t>(stream);
   const tttk::Dims& D = g.dims;
   const int64_t df = g.d * g.f;
+
+  // Packed documents: the block table and the apply's tile list go to the
+  // workspace first, in one asynchronous copy. Its host buffer must outlive
+  // the copy, which may run after this call returns: a host function
+  // enqueued behind the copy frees it.
+  const tttk::BlockInfo* blocks = nullptr;
+  const tttk::ApplyTile* tiles = nullptr;
+  if (!g.blocks.empty()) {
+    const size_t nb = g.blocks.size() * sizeof(tttk::BlockInfo);
+    const size_t nt = g.tiles.size() * sizeof(tttk::ApplyTile);
+    char* host = static_cast<char*>(std::malloc(nb + nt));
+    if (host == nullptr) return fail(TTT_ERR_HIP, "document table: host allocation failed");
+    std::memcpy(host, g.blocks.data(), nb);
+    std::memcpy(host + nb, g.tiles.data(), nt);
+    char* dst = at<char>(workspace, L.blk);
+    hipError_t e = hipMemcpyAsync(dst, host, nb + nt, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipLaunchHostFunc(s, [](void* p) { std::free(p); }, host);
+    if (e != hipSuccess) {
+      // The copy may be queued: let the stream drain before freeing.
+      (void)hipStreamSynchronize(s);
+      std::free(host);
+      return fail(TTT_ERR_HIP, std::string("document table copy: ") + hipGetErrorString(e));
+    }
+    blocks = reinterpret_cast<const tttk::BlockInfo*>(dst);
+    tiles = reinterpret_cast<const tttk::ApplyTile*>(dst + nb);
+  }
 
   // bf16 operands
   const uint16_t* Hb = static_cast<const uint16_t*>(H);
@@ -359,7 +450,8 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
   TTT_LAUNCH("transpose_w_target", s,
              tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, D.ld_y, s));
   TTT_LAUNCH("conv", s,
-             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, D, (int)g.K, (int)g.C, g.pad_chunk, s));
+             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, D, (int)g.K, (int)g.C, g.pad_chunk,
+                               blocks, s));
   TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, s));
   TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, vscale, D, s));
 
@@ -370,26 +462,72 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
     TTT_LAUNCH("update_prefix", s,
                tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale, snap,
                                    g.nchunks * snap_cstride, W_down_final, nullptr, D, 0,
-                                   (int)g.T, (int)g.C, s));
+                                   (int)g.T, (int)g.C, blocks, (int)g.nchunks, s));
     TTT_LAUNCH("apply", s,
                tttk::launch_apply(Z, snap, g.nchunks * snap_cstride, snap_cstride, O, g.act_f32,
-                                  D, 0, (int)g.T, (int)g.C, s));
+                                  D, 0, (int)g.T, (int)g.C, tiles, (int)g.tiles.size(),
+                                  (int)g.nchunks, s));
   } else {
-    // Running state: W_down_final holds W^(i) in fp32, `snap` its bf16 copy.
-    TTT_LAUNCH("update_running", s,
-               tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale,
-                                   nullptr, 0, W_down_final, snap, D, 0, 0, (int)g.C, s));
-    for (int64_t i = 0; i < g.nchunks; ++i) {
-      const int t0 = (int)(i * g.C), t1 = (int)std::min<int64_t>(g.T, (i + 1) * g.C);
+    // Running state: W_down_final holds W^(i) in fp32, `snap` its bf16 copy;
+    // both start from W_down0 at every document start.
+    for (const Chunk& c : g.chunks) {
+      if (c.doc_start)
+        TTT_LAUNCH("update_running", s,
+                   tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale,
+                                       nullptr, 0, W_down_final, snap, D, 0, 0, (int)g.C,
+                                       nullptr, 1, s));
       TTT_LAUNCH("apply", s,
-                 tttk::launch_apply(Z, snap, snap_cstride, 0, O, g.act_f32, D, t0, t1, (int)g.C,
-                                    s));
+                 tttk::launch_apply(Z, snap, snap_cstride, 0, O, g.act_f32, D, c.t0, c.t1,
+                                    (int)g.C, nullptr, 0, 1, s));
       TTT_LAUNCH("update_running", s,
                  tttk::launch_update(ZT, VT, W_down_final, true, df, g.f, acc_scale, nullptr, 0,
-                                     W_down_final, snap, D, t0, t1 - t0, (int)g.C, s));
+                                     W_down_final, snap, D, c.t0, c.t1 - c.t0, (int)g.C,
+                                     nullptr, 1, s));
     }
   }
   return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0,
+                             const void* Wg, const void* Wu, const void* W_down0,
+                             const void* conv_taps, const void* W_target, float eta,
+                             int32_t chunk, void* O, float* W_down_final, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  return forward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, O, W_down_final,
+                      workspace, workspace_bytes, stream);
+}
+
+ttt_status ttt_packed_workspace_size(const ttt_desc* desc, int32_t chunk,
+                                     const int32_t* doc_starts, int32_t n_docs,
+                                     size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  TTT_TRY(check_docs(doc_starts, n_docs, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = forward_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_forward_packed(const ttt_desc* desc, const void* H, const void* X0,
+                                    const void* Wg, const void* Wu, const void* W_down0,
+                                    const void* conv_taps, const void* W_target, float eta,
+                                    int32_t chunk, const int32_t* doc_starts, int32_t n_docs,
+                                    void* O, float* W_down_final, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  TTT_TRY(check_docs(doc_starts, n_docs, &g));
+  return forward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, O, W_down_final,
+                      workspace, workspace_bytes, stream);
 }
 
 ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void* Wg,
@@ -465,7 +603,7 @@ ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0, const void* conv_
                                         s));
   TTT_LAUNCH("conv", s,
              tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, g.dims, (int)g.K, (int)g.C,
-                               g.pad_chunk, s));
+                               g.pad_chunk, nullptr, s));
   TTT_LAUNCH("target", s,
              tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), 1.0f, g.dims, s));
   return TTT_OK;

@@ -286,7 +286,7 @@ __device__ __forceinline__ TileIdx tile_index(int tiles_m, int tiles_n, int grou
 // memory instructions in every wave (the pipeline's waits count them).
 struct NoHook {
   static constexpr int kStores = 0;
-  __device__ __forceinline__ bool operator()(int, const f32x16*) const { return false; }
+  __device__ __forceinline__ bool operator()(int, f32x16*) const { return false; }
 };
 
 // Waits as wait_and_barrier<BASE + c * STEP> for a runtime c in [0, C].
@@ -702,27 +702,87 @@ struct SnapshotStore {
   }
 };
 
-// The update's hook: the exclusive-prefix snapshot at every chunk start.
-template <class L>
+// acc = acc_scale * W for the wave's part of a [d_ff tile] x [d_model tile]
+// state block, W element (c, j) at W + c * ld + j (bf16 or fp32).
+template <class L, bool F32>
+struct StateLoad {
+  const void* W;
+  int64_t ld;
+  int j0, c0, d, f;
+  float acc_scale;
+  __device__ __forceinline__ void operator()(f32x16* acc) const {
+    const Frag<L> fr;
+#pragma unroll
+    for (int m = 0; m < L::TM; ++m)
+#pragma unroll
+      for (int n = 0; n < L::TN; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = j0 + fr.row(m, q);
+          const int c = c0 + fr.col(n);
+          float v[4] = {0.f, 0.f, 0.f, 0.f};
+          if (c < d && j < f) {
+            const int64_t o = (int64_t)c * ld + j;
+            if constexpr (F32) {
+              const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + o);
+              v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+            } else {
+              const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const u16*>(W) + o);
+              v[0] = __uint_as_float(x.x << 16);
+              v[1] = __uint_as_float(x.x & 0xffff0000u);
+              v[2] = __uint_as_float(x.y << 16);
+              v[3] = __uint_as_float(x.y & 0xffff0000u);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[m * L::TN + n][4 * q + e] = v[e] * acc_scale;
+        }
+  }
+};
+
+// The update's hook: the exclusive-prefix snapshot at every chunk start and,
+// for packed documents (PACKED), the reset to the initial state at every
+// document start after the first ([iplex] §6), with chunk starts taken from
+// the block table. The reset's loads are waited for at once; they only
+// lengthen the pipeline's waits that follow. The plain kernel is compiled
+// without the reset, which would otherwise keep its addresses live across
+// the K loop.
+template <class L, bool F32, bool PACKED>
 struct ChunkSnapshots {
   static constexpr int kStores = SnapshotStore<L>::kStores;
   SnapshotStore<L> store;
+  StateLoad<L, F32> reset;
   u16* snap;  // this sequence's snapshots, or null
   int64_t chunk_stride;
   int steps_per_chunk;
-  __device__ __forceinline__ bool operator()(int kt, const f32x16* acc) const {
-    if (snap == nullptr || kt % steps_per_chunk != 0) return false;
-    store(snap + (int64_t)(kt / steps_per_chunk) * chunk_stride, acc);
+  const BlockInfo* blocks;  // PACKED: per K step of this launch
+  int n_chunks;             // PACKED: snapshot slots (table values are clamped to them)
+  __device__ __forceinline__ bool operator()(int kt, f32x16* acc) const {
+    int slot;
+    if constexpr (PACKED) {
+      // A vector load: its vmcnt wait also waits for the stage loads in
+      // flight, which costs the packed update time at every step.
+      const BlockInfo info = blocks[kt];
+      const int flags = info.flags;
+      slot = min(max(info.chunk, 0), n_chunks - 1);
+      if ((flags & kBlockDocStart) && kt > 0) reset(acc);
+      if (snap == nullptr || !(flags & kBlockChunkStart)) return false;
+    } else {
+      if (snap == nullptr || kt % steps_per_chunk != 0) return false;
+      slot = kt / steps_per_chunk;
+    }
+    store(snap + (int64_t)slot * chunk_stride, acc);
     return true;
   }
 };
 
-template <bool WINIT_F32>
+template <bool WINIT_F32, bool PACKED>
 __global__ __launch_bounds__(kGemmThreads) void update_kernel(
     const u16* __restrict__ ZT, const u16* __restrict__ VT, const void* __restrict__ Winit,
     int64_t winit_bstride, int64_t winit_ld, float acc_scale, u16* __restrict__ snap,
     int64_t snap_bstride, float* __restrict__ Wf, u16* __restrict__ shadow, Dims g,
-    int tok_begin, int nk, int steps_per_chunk, int tiles_m, int tiles_n) {
+    int tok_begin, int nk, int steps_per_chunk, const BlockInfo* __restrict__ blocks,
+    int n_chunks, int tiles_m, int tiles_n) {
   using L = Layout<K3_BM, K3_BN, K3_WGM>;
   constexpr int TM = L::TM, TN = L::TN;
   TTT_GEMM_LDS(lds, K3_BM, K3_BN, K3_BK, K3_NST)
@@ -733,36 +793,17 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
   const int64_t chunk_stride = snap_elems(g);
   const float out_scale = 1.0f / acc_scale;
 
+  const void* winit_b =
+      WINIT_F32 ? (const void*)(static_cast<const float*>(Winit) + ti.b * winit_bstride)
+                : (const void*)(static_cast<const u16*>(Winit) + ti.b * winit_bstride);
+  const StateLoad<L, WINIT_F32> init{winit_b, winit_ld, j0, c0, d, f, acc_scale};
   f32x16 acc[TM][TN];
-#pragma unroll
-  for (int m = 0; m < TM; ++m)
-#pragma unroll
-    for (int n = 0; n < TN; ++n)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = j0 + fr.row(m, q);
-        const int c = c0 + fr.col(n);
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        if (c < d && j < f) {
-          const int64_t o = ti.b * winit_bstride + (int64_t)c * winit_ld + j;
-          if constexpr (WINIT_F32) {
-            const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(Winit) + o);
-            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-          } else {
-            const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const u16*>(Winit) + o);
-            v[0] = __uint_as_float(x.x << 16);
-            v[1] = __uint_as_float(x.x & 0xffff0000u);
-            v[2] = __uint_as_float(x.y << 16);
-            v[3] = __uint_as_float(x.y & 0xffff0000u);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[m][n][4 * q + e] = v[e] * acc_scale;
-      }
+  init(&acc[0][0]);
 
   const SnapshotStore<L> snapshot{j0, c0, d, f, out_scale, (uint32_t)(chunk_stride * 2)};
-  const ChunkSnapshots<L> hook{snapshot, snap ? snap + ti.b * snap_bstride : nullptr,
-                               chunk_stride, steps_per_chunk};
+  const ChunkSnapshots<L, WINIT_F32, PACKED> hook{
+      snapshot, init, snap ? snap + ti.b * snap_bstride : nullptr, chunk_stride,
+      steps_per_chunk, blocks ? blocks + tok_begin / K3_BK : nullptr, n_chunks};
   // Rows past d_ff / d_model in the last slabs are never written; they only
   // feed output rows / columns that are not stored.
   static_assert(K3_BM == kZtSlab && K3_BN == kVtSlab && K3_BK == 64, "update tile = slabs");
@@ -787,6 +828,7 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
                           acc[m][n][4 * q + 2] * out_scale, acc[m][n][4 * q + 3] * out_scale);
       }
   if (shadow != nullptr) snapshot(shadow + (int64_t)ti.b * chunk_stride, &acc[0][0]);
+  (void)fr;
 }
 
 // ------------------------------------------------------------ apply (K4)
@@ -806,8 +848,8 @@ struct ApplyCfg {
 template <int BN, bool OUT_F32>
 __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
     const u16* __restrict__ Z, const u16* __restrict__ snap, int64_t snap_bstride,
-    int64_t snap_cstride, void* __restrict__ O, Dims g, int tok_begin, int chunk, int tiles_m,
-    int tiles_n) {
+    int64_t snap_cstride, void* __restrict__ O, Dims g, int tok_begin, int tok_end, int chunk,
+    const ApplyTile* __restrict__ tiles, int n_chunks, int tiles_m, int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int BM = kSnapSlab, WGM = ApplyCfg<BN>::WGM, BK = ApplyCfg<BN>::BK,
                 NST = ApplyCfg<BN>::NST;
@@ -815,8 +857,18 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
   using L = Layout<BM, BN, WGM>;
   TTT_GEMM_LDS(lds, BM, BN, BK, NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, kApplyGroupM);
-  const int c0 = ti.tm * BM, t0 = tok_begin + ti.tn * BN;
-  const int i = t0 / chunk;
+  const int c0 = ti.tm * BM;
+  int t0, t1, i;
+  if (tiles != nullptr) {
+    const ApplyTile tl = tiles[ti.tn];
+    t0 = min(max(tl.t0, 0), g.T);
+    t1 = min(max(tl.t1, t0), g.T);
+    i = min(max(tl.chunk, 0), n_chunks - 1);
+  } else {
+    t0 = tok_begin + ti.tn * BN;
+    t1 = min(tok_end, t0 + BN);
+    i = t0 / chunk;
+  }
   const int d = g.d, f = g.f, T = g.T;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
@@ -837,7 +889,7 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
       for (int q = 0; q < 4; ++q) {
         const int c = c0 + fr.row(m, q);
         const int t = t0 + fr.col(n);
-        if (t >= T || c >= d) continue;
+        if (t >= t1 || c >= d) continue;  // past the tile's chunk: another snapshot's
         const int64_t o = ((int64_t)ti.b * T + t) * d + c;
         if constexpr (OUT_F32) {
           *reinterpret_cast<float4*>(static_cast<float*>(O) + o) =
@@ -889,7 +941,9 @@ template <bool TAPS_F32>
 __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ X0,
                                                         const void* __restrict__ taps,
                                                         u16* __restrict__ Y, Dims g, int K,
-                                                        int chunk, int pad_chunk, int64_t total) {
+                                                        int chunk, int pad_chunk,
+                                                        const BlockInfo* __restrict__ blocks,
+                                                        int64_t total) {
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (gid >= total) return;
   const int d = g.d, T = g.T;
@@ -899,7 +953,9 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
   const int t = (int)(bt % g.T_pad);
   const int b = (int)(bt / g.T_pad);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int end = pad_chunk ? min(T, (t / chunk + 1) * chunk) : T;
+  const int end = blocks != nullptr
+                      ? min(T, pad_chunk ? blocks[t >> 6].chunk_end : blocks[t >> 6].doc_end)
+                      : (pad_chunk ? min(T, (t / chunk + 1) * chunk) : T);
   for (int k = 0; k < K && t + k < end; ++k) {
     const uint4 xv = *reinterpret_cast<const uint4*>(X0 + ((int64_t)b * T + t + k) * d + c);
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -1000,15 +1056,16 @@ hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, in
 }
 
 hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint16_t* Y,
-                       const Dims& g, int K, int chunk, bool pad_chunk, hipStream_t s) {
+                       const Dims& g, int K, int chunk, bool pad_chunk,
+                       const BlockInfo* blocks, hipStream_t s) {
   const int64_t total = (int64_t)g.B * g.T_pad * (g.d / 8);
-  const int blocks = ceil_div(total, kThreads);
+  const int grid = ceil_div(total, kThreads);
   if (taps_f32)
-    conv_kernel<true><<<blocks, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
-                                                  total);
+    conv_kernel<true><<<grid, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
+                                                blocks, total);
   else
-    conv_kernel<false><<<blocks, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
-                                                   total);
+    conv_kernel<false><<<grid, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
+                                                 blocks, total);
   return hipGetLastError();
 }
 
@@ -1039,57 +1096,85 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
   return hipGetLastError();
 }
 
+template <bool F32, bool PACKED>
+static void update_launch(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
+                          int64_t winit_bstride, int64_t winit_ld, float acc_scale,
+                          uint16_t* snap, int64_t snap_bstride, float* Wf, uint16_t* shadow,
+                          const Dims& g, int tok_begin, int nk, int steps_per_chunk,
+                          const BlockInfo* blocks, int n_chunks, hipStream_t s) {
+  const int tiles_m = ceil_div(g.f, K3_BM), tiles_n = ceil_div(g.d, K3_BN);
+  update_kernel<F32, PACKED><<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(
+      ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap, snap_bstride, Wf, shadow, g,
+      tok_begin, nk, steps_per_chunk, blocks, n_chunks, tiles_m, tiles_n);
+}
+
 hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
                          bool winit_f32, int64_t winit_bstride, int64_t winit_ld,
                          float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
                          uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
-                         int chunk, hipStream_t s) {
+                         int chunk, const BlockInfo* blocks, int n_chunks, hipStream_t s) {
+  // Token offsets and counts are whole K steps, so that the slab operands are
+  // read from a slab boundary.
   const int nk = (tok_count + K3_BK - 1) / K3_BK, steps_per_chunk = chunk / K3_BK;
-  // Token offsets and counts are whole K steps, so that the pair-blocked
-  // operands are read from a 16-token boundary.
-  const int tiles_m = ceil_div(g.f, K3_BM), tiles_n = ceil_div(g.d, K3_BN);
-  const int grid = tiles_m * tiles_n * g.B;
-  if (winit_f32)
-    update_kernel<true><<<grid, kGemmThreads, 0, s>>>(ZT, VT, Winit, winit_bstride, winit_ld,
-                                                  acc_scale, snap, snap_bstride, Wf, shadow, g,
-                                                  tok_begin, nk, steps_per_chunk, tiles_m,
-                                                  tiles_n);
-  else
-    update_kernel<false><<<grid, kGemmThreads, 0, s>>>(ZT, VT, Winit, winit_bstride, winit_ld,
-                                                   acc_scale, snap, snap_bstride, Wf, shadow, g,
-                                                   tok_begin, nk, steps_per_chunk, tiles_m,
-                                                   tiles_n);
+  if (blocks != nullptr) {
+    if (winit_f32)
+      update_launch<true, true>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
+                                snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
+                                blocks, n_chunks, s);
+    else
+      update_launch<false, true>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
+                                 snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
+                                 blocks, n_chunks, s);
+  } else {
+    if (winit_f32)
+      update_launch<true, false>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
+                                 snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
+                                 nullptr, n_chunks, s);
+    else
+      update_launch<false, false>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
+                                  snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
+                                  nullptr, n_chunks, s);
+  }
   return hipGetLastError();
 }
 
 template <int BN>
 static void apply_dispatch(const uint16_t* Z, const uint16_t* snap, int64_t sb, int64_t sc,
                            void* O, bool out_f32, const Dims& g, int tok_begin, int tok_end,
-                           int chunk, hipStream_t s) {
-  const int tiles_m = ceil_div(g.d, 256), tiles_n = ceil_div(tok_end - tok_begin, BN);
+                           int chunk, const ApplyTile* tiles, int n_tiles, int n_chunks,
+                           hipStream_t s) {
+  const int tiles_m = ceil_div(g.d, 256);
+  const int tiles_n = tiles != nullptr ? n_tiles : ceil_div(tok_end - tok_begin, BN);
   const int grid = tiles_m * tiles_n * g.B;
   if (out_f32)
-    apply_kernel<BN, true><<<grid, kGemmThreads, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin, chunk,
-                                                     tiles_m, tiles_n);
+    apply_kernel<BN, true><<<grid, kGemmThreads, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin,
+                                                     tok_end, chunk, tiles, n_chunks, tiles_m,
+                                                     tiles_n);
   else
-    apply_kernel<BN, false><<<grid, kGemmThreads, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin, chunk,
-                                                      tiles_m, tiles_n);
+    apply_kernel<BN, false><<<grid, kGemmThreads, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin,
+                                                      tok_end, chunk, tiles, n_chunks, tiles_m,
+                                                      tiles_n);
 }
 
 hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bstride,
                         int64_t snap_cstride, void* O, bool out_f32, const Dims& g,
-                        int tok_begin, int tok_end, int chunk, hipStream_t s) {
-  // The token tile must not straddle a chunk: take the largest of 256, 128,
-  // 64 that divides the chunk (the chunk is a multiple of 64).
-  if (chunk % 256 == 0)
-    apply_dispatch<256>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
-                        chunk, s);
-  else if (chunk % 128 == 0)
-    apply_dispatch<128>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
-                        chunk, s);
-  else
-    apply_dispatch<64>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
-                       chunk, s);
+                        int tok_begin, int tok_end, int chunk, const ApplyTile* tiles,
+                        int n_tiles, int n_chunks, hipStream_t s) {
+  // A token tile must not straddle a chunk (it reads one snapshot): tiles
+  // start at chunk starts and are apply_tile_width(chunk) wide.
+  switch (apply_tile_width(chunk)) {
+    case 256:
+      apply_dispatch<256>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
+                          chunk, tiles, n_tiles, n_chunks, s);
+      break;
+    case 128:
+      apply_dispatch<128>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
+                          chunk, tiles, n_tiles, n_chunks, s);
+      break;
+    default:
+      apply_dispatch<64>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
+                         chunk, tiles, n_tiles, n_chunks, s);
+  }
   return hipGetLastError();
 }
 

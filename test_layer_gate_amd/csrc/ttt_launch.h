@@ -40,6 +40,29 @@ constexpr int kSnapSlab = 256;  // snapshot slab rows = the apply tile's M
 constexpr int kWRows = 128;   // W_g / W_u rows per packed slab = half the gate/up tile's N
 constexpr int kGateBK = 64;   // d_model elements per packed slab = one K step of gate/up
 
+// One 64-token block of a packed sequence (documents back to back, each
+// starting at a multiple of 64 tokens; chunks restart at every document
+// start). Blocks at or past T carry the last chunk, no flags and ends T.
+struct BlockInfo {
+  int32_t chunk;      // index of the chunk holding the block = its snapshot
+  int32_t flags;      // kBlockChunkStart | kBlockDocStart
+  int32_t doc_end;    // first token after the block's document
+  int32_t chunk_end;  // first token after the block's chunk
+};
+constexpr int32_t kBlockChunkStart = 1, kBlockDocStart = 2;
+
+// One token tile of the apply: tokens [t0, t1) of chunk `chunk`, t1 - t0 at
+// most the apply's tile width (apply_tile_width).
+struct ApplyTile {
+  int32_t t0, t1, chunk, reserved;
+};
+
+// The apply's token-tile width for a chunk of `chunk` tokens: the largest of
+// 256, 128 and 64 that divides it (the chunk is a multiple of 64).
+inline int apply_tile_width(int chunk) {
+  return chunk % 256 == 0 ? 256 : (chunk % 128 == 0 ? 128 : 64);
+}
+
 // n (a multiple of 64) padded so that n * 2 bytes is an odd number of
 // 128-byte lines.
 inline int64_t pad_ld(int64_t n) { return ((n / 64) % 2 == 0) ? n + 64 : n; }
@@ -94,9 +117,12 @@ hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, in
                                 int cols, int64_t ld_dst, hipStream_t s);
 
 // Y[b][t][c] = fp16(sum_k taps[k][c] * X0[b][t + k][c]) over reads inside the
-// sequence (or inside t's chunk when pad_chunk), for t < T_pad.
+// sequence (or inside t's chunk when pad_chunk), for t < T_pad. With blocks
+// (packed documents, B = 1) the reads stop at t's document end (or chunk
+// end) instead.
 hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint16_t* Y,
-                       const Dims& g, int K, int chunk, bool pad_chunk, hipStream_t s);
+                       const Dims& g, int K, int chunk, bool pad_chunk,
+                       const BlockInfo* blocks, hipStream_t s);
 
 // dst = W ([f][d], bf16 or fp32, rounded to bf16) in the packed Wgp layout.
 hipError_t launch_pack_weight(const void* W, bool w_f32, uint16_t* dst, const Dims& g,
@@ -115,9 +141,11 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
 // Fast-weight update over tokens [tok_begin, tok_begin + tok_count) (a
 // multiple of 64), in 64-token steps (columns past T read as zero). acc =
 // acc_scale * Winit; before each step that starts a chunk (every chunk / 64
-// steps), if snap != null, that chunk's snapshot (sb<256>(d x f), at snap +
-// b * snap_bstride + chunk * snap_elems) = bf16(acc / acc_scale); then acc
-// += the step's ZT x VT contraction over tokens. Finally Wf = acc /
+// steps; with blocks, the blocks flagged kBlockChunkStart, after resetting
+// acc to acc_scale * Winit at a kBlockDocStart), if snap != null, that
+// chunk's snapshot (sb<256>(d x f), at snap + b * snap_bstride + chunk *
+// snap_elems) = bf16(acc / acc_scale); then acc += the step's ZT x VT
+// contraction over tokens. Finally Wf = acc /
 // acc_scale (row-major [B][d][f]) and, if shadow != null, shadow =
 // bf16(acc / acc_scale) (sb<256>(d x f) per sequence). tok_count may be 0. Winit element
 // (b, c, j) is at b * winit_bstride + c * winit_ld + j. acc_scale must be a
@@ -126,13 +154,17 @@ hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Win
                          bool winit_f32, int64_t winit_bstride, int64_t winit_ld,
                          float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
                          uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
-                         int chunk, hipStream_t s);
+                         int chunk, const BlockInfo* blocks, int n_chunks, hipStream_t s);
 
-// O[b][t] = Z[b][t] W_i^T for tokens t in [tok_begin, tok_end), where W_i is
-// the bf16 state (sb<256>(d x f)) at snap + b * snap_bstride + (t / chunk) *
-// snap_cstride.
+// O[b][t] = Z[b][t] W_i^T, where W_i is the bf16 state (sb<256>(d x f)) at
+// snap + b * snap_bstride + i * snap_cstride. Without tiles: for tokens t in
+// [tok_begin, tok_end), tok_begin a multiple of apply_tile_width(chunk), i =
+// t / chunk. With tiles: for the n_tiles token tiles listed, i = the tile's
+// chunk. Table entries (blocks, tiles) are clamped to [0, n_chunks) and to
+// the sequence, so a wrong table gives wrong values, never a wild address.
 hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bstride,
                         int64_t snap_cstride, void* O, bool out_f32, const Dims& g,
-                        int tok_begin, int tok_end, int chunk, hipStream_t s);
+                        int tok_begin, int tok_end, int chunk, const ApplyTile* tiles,
+                        int n_tiles, int n_chunks, hipStream_t s);
 
 }  // namespace tttk

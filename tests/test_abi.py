@@ -177,3 +177,59 @@ def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         bnd.lib()
+
+
+# ---- packed documents --------------------------------------------------------
+
+def packed_ws(L, desc, chunk, starts):
+    arr = (ctypes.c_int32 * max(len(starts), 1))(*starts) if starts is not None else None
+    n = ctypes.c_size_t(0)
+    st = L.ttt_packed_workspace_size(ctypes.byref(desc), chunk, arr,
+                                     len(starts) if starts is not None else 1, ctypes.byref(n))
+    return st, n.value
+
+
+def test_packed_workspace_size(L):
+    desc = qwen_desc()
+    starts = [0, 1024 * 10, 1024 * 10 + 64, 40000 - 40000 % 64]
+    st, n = packed_ws(L, desc, 1024, starts)
+    assert st == OK, L.ttt_last_error()
+    _, plain = ws_size(L, desc, 1024)
+    T, d, f = 65536, 2560, 9728
+    ends = starts[1:] + [T]
+    k = sum(-(-(e - a) // 1024) for a, e in zip(starts, ends))
+    snap = -(-d // 256) * 256 * f * 2
+    chunks = [(t, min(e, t + 1024)) for a, e in zip(starts, ends) for t in range(a, e, 1024)]
+    n_tiles = sum(-(-(t1 - t0) // 256) for t0, t1 in chunks)
+    assert len(chunks) == k
+    # more chunks, plus the block table and the apply's tile list
+    extra = (k - 64) * snap + T // 64 * 16 + n_tiles * 16
+    assert plain + extra <= n <= plain + extra + 4 * 256
+
+
+@pytest.mark.parametrize("starts,code", [
+    ([0], OK), ([0, 64, 128], OK), ([64], INVALID), ([0, 128, 128], INVALID),
+    ([0, 256, 128], INVALID), ([0, 65536], INVALID), ([0, 100], UNSUPPORTED),
+    ([], INVALID), (None, INVALID)])
+def test_packed_document_validation(L, starts, code):
+    st, _ = packed_ws(L, qwen_desc(), 1024, starts)
+    assert st == code, (starts, st, L.ttt_last_error())
+
+
+def test_packed_needs_batch_one(L):
+    st, _ = packed_ws(L, qwen_desc(batch=2), 1024, [0, 64])
+    assert st == UNSUPPORTED
+
+
+def test_packed_forward_validates_before_launch(L):
+    desc = qwen_desc()
+    p = good_ptrs()
+    starts = (ctypes.c_int32 * 2)(0, 100)
+    st = L.ttt_layer_forward_packed(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3), 1024,
+                                    starts, 2, p[7], p[8], p[9], ctypes.c_size_t(1 << 62), None)
+    assert st == UNSUPPORTED
+    starts = (ctypes.c_int32 * 2)(0, 128)
+    _, need = packed_ws(L, desc, 1024, [0, 128])
+    st = L.ttt_layer_forward_packed(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3), 1024,
+                                    starts, 2, p[7], p[8], p[9], ctypes.c_size_t(need - 1), None)
+    assert st == WORKSPACE
