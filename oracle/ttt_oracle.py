@@ -31,6 +31,11 @@ tested by the pins in tests/test_oracle.py):
   * Each sequence of the batch has its own state, starting from W_down0.
   * A last chunk shorter than C is allowed. The returned final state includes
     the last chunk's update.
+  * Update-norm clipping ([iplex] §6, §8: the Frobenius norm of the update
+    delta is limited to a threshold): optionally, each chunk's delta
+    eta * V_i^T Z_i is scaled by min(1, clip / ||eta * V_i^T Z_i||_F). The
+    threshold the pages print (1e-5) reads as garbled, so it is a parameter;
+    clip = None (the default) applies no clipping.
   * Packed documents ([iplex] §6, document boundaries): a sequence may hold
     several documents back to back, given by their start offsets. At each
     document start the state returns to W_down0 and the chunking restarts,
@@ -107,7 +112,7 @@ def lm_target(X0, taps, W_target, pad="sequence", chunk=None, n_out=None):
 
 
 def ttt_prefill(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
-                pad="sequence"):
+                pad="sequence", clip=None):
     """The layer's prefill: per-chunk apply, then update, over the sequence.
 
     [notes] "Chunk-Wise 更新机制": the sequence is cut into non-overlapping
@@ -120,7 +125,8 @@ def ttt_prefill(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
     H [B, T, d]; X0 [B, T + L, d] (L >= 0 look-ahead rows, read by the conv
     only); Wg, Wu [f, d]; W_down0 [d, f] shared, or [B, d, f] per sequence;
     taps [K, d]; W_target [d, d]. Returns O [B, T, d] and the final state
-    W [B, d, f], float64.
+    W [B, d, f], float64. clip: None, or the Frobenius-norm limit of each
+    chunk's update delta ([iplex] §6 norm clipping).
     """
     H, X0, W_down0 = _f64(H), _f64(X0), _f64(W_down0)
     B, T, d = H.shape
@@ -138,7 +144,12 @@ def ttt_prefill(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
         for start in range(0, T, chunk):
             rows = slice(start, min(start + chunk, T))
             O[b, rows] = Z[rows] @ W.T                 # apply: pre-update state
-            W = W + eta * (V[rows].T @ Z[rows])        # then update
+            delta = eta * (V[rows].T @ Z[rows])
+            if clip is not None:
+                norm = np.linalg.norm(delta)           # Frobenius norm of the delta
+                if norm > clip:
+                    delta = delta * (clip / norm)
+            W = W + delta                              # then update
         W_final[b] = W
     return O, W_final
 

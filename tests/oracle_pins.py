@@ -51,9 +51,10 @@ def small_case(seed=0, B=2, T=37, d=6, f=10, K=3, C=8, eta=0.05,
 def run(x, **over):
     a = dict(x)
     a.update(over)
+    kw = {"clip": a["clip"]} if a.get("clip") is not None else {}
     return ora.ttt_prefill(a["H"], a["X0"], a["Wg"], a["Wu"], a["W_down0"],
                            a["taps"], a["W_target"], a["eta"], a["chunk"],
-                           pad=a.get("pad", "sequence"))
+                           pad=a.get("pad", "sequence"), **kw)
 
 
 # ---- library-routine references (torch, CPU, float64) ----------------------
@@ -335,6 +336,39 @@ def pin_golden_ntp_fixture():
     assert np.array_equal(V, np.array(blocks["V_expected"])), "golden NTP"
 
 
+# ---- update-norm clipping ([iplex] §6) ---------------------------------------
+
+def pin_clip_loose_is_plain():
+    """A limit no chunk's update reaches changes nothing."""
+    x = small_case(seed=31)
+    O, W = run(x)
+    O2, W2 = run(x, clip=1e12)
+    assert np.array_equal(O, O2) and np.array_equal(W, W2), "loose clip changed the result"
+
+
+def pin_clip_each_delta():
+    """Each chunk's applied update, read off the states after successive
+    chunks (the prefill of the first j chunks, with the conv's K - 1
+    look-ahead rows), is the torch-computed eta V_j^T Z_j scaled to norm
+    min(||eta V_j^T Z_j||_F, clip): same direction, clipped length."""
+    x = small_case(seed=32, B=1, T=40, C=8, eta=0.3)
+    K, C, T = x["taps"].shape[0], x["chunk"], 40
+    Z = torch_z(x["H"][0], x["Wg"], x["Wu"])
+    V = torch_target(x["X0"][0], x["taps"], x["W_target"])
+    raw = [x["eta"] * (_t(V[a:a + C]).T @ _t(Z[a:a + C])).numpy() for a in range(0, T, C)]
+    norms = [float(np.linalg.norm(r)) for r in raw]
+    clip = float(np.median(norms))            # clips about half of the chunks
+    prev = np.asarray(x["W_down0"], np.float64)
+    for j, a in enumerate(range(0, T, C)):
+        n = min(a + C, T)
+        sub = dict(x, H=x["H"][:, :n], X0=x["X0"][:, :n + K - 1])
+        _, Wj = run(sub, clip=clip)
+        delta = Wj[0] - prev
+        want = raw[j] * min(1.0, clip / norms[j])
+        _close(delta, want, tol=1e-9, what=f"clipped delta of chunk {j}")
+        prev = Wj[0]
+
+
 # ---- packed documents ([iplex] §6, reset at document boundaries) ----------
 
 PACKED_DOCS = ([0, 13, 30, 31], [0, 8, 24], [0, 20])  # lengths below, at and above C = 8
@@ -399,4 +433,4 @@ ALL_PINS = [pin_reduces_to_plain_mlp, pin_prefix_scan_form, pin_state_free_form,
             pin_chunk_causality, pin_batch_independence, pin_split_resume,
             pin_brute_force_scalars, pin_sampled_forms, pin_golden_ntp_fixture,
             pin_packed_single_document, pin_packed_equals_documents,
-            pin_packed_isolation]
+            pin_packed_isolation, pin_clip_loose_is_plain, pin_clip_each_delta]

@@ -14,10 +14,12 @@ _real_conv = ora.conv_target_input
 
 
 def _prefill_variant(order="apply_first", scale=1.0, skip_last=False,
-                     shared_state=False, sign=1.0, chunk_extra=0):
-    """A copy of the recurrence with one knob turned away from the pages."""
+                     shared_state=False, sign=1.0, chunk_extra=0, clip_mode="delta"):
+    """A copy of the recurrence with one knob turned away from the pages.
+    clip_mode: "delta" (the pages), "no_eta" (the norm of V^T Z without
+    eta), "inverted" (scale norm / clip), "state" (clip the whole state)."""
     def prefill(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
-                pad="sequence"):
+                pad="sequence", clip=None):
         H, X0, W_down0 = (np.asarray(a, np.float64) for a in (H, X0, W_down0))
         B, T, d = H.shape
         f = Wg.shape[0]
@@ -34,6 +36,16 @@ def _prefill_variant(order="apply_first", scale=1.0, skip_last=False,
             for n, s in enumerate(starts):
                 r = slice(s, min(s + step, T))
                 upd = sign * eta * scale * (V[r].T @ Z[r])
+                if clip is not None:
+                    if clip_mode == "delta":
+                        nrm = np.linalg.norm(upd)
+                        upd = upd * min(1.0, clip / nrm) if nrm > 0 else upd
+                    elif clip_mode == "no_eta":
+                        nrm = np.linalg.norm(V[r].T @ Z[r])
+                        upd = upd * min(1.0, clip / nrm) if nrm > 0 else upd
+                    elif clip_mode == "inverted":
+                        nrm = np.linalg.norm(upd)
+                        upd = upd * min(1.0, nrm / clip)
                 if skip_last and n == len(starts) - 1:
                     upd = 0.0
                 if order == "update_first":
@@ -42,6 +54,9 @@ def _prefill_variant(order="apply_first", scale=1.0, skip_last=False,
                 else:
                     O[b, r] = Z[r] @ W.T
                     W = W + upd
+                if clip is not None and clip_mode == "state":
+                    nrm = np.linalg.norm(W)
+                    W = W * min(1.0, clip / nrm)
             Wf[b] = W
         return O, Wf
     return prefill
@@ -115,6 +130,9 @@ def _packed_variant(reset=True, conv_stops=True, chunks_from_doc=True):
 
 
 MUTATIONS = {
+    "clip_norm_without_eta": ("ttt_prefill", _prefill_variant(clip_mode="no_eta")),
+    "clip_scale_inverted": ("ttt_prefill", _prefill_variant(clip_mode="inverted")),
+    "clip_whole_state": ("ttt_prefill", _prefill_variant(clip_mode="state")),
     "packed_no_reset": ("ttt_prefill_packed", _packed_variant(reset=False)),
     "packed_conv_crosses_documents": ("ttt_prefill_packed", _packed_variant(conv_stops=False)),
     "packed_chunks_from_token_0": ("ttt_prefill_packed", _packed_variant(chunks_from_doc=False)),
