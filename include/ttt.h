@@ -118,6 +118,27 @@ ttt_status ttt_layer_forward(const ttt_desc* desc,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Update-norm clipping (iplexlaw explainer §6: the Frobenius norm of the
+ * update delta is limited to a threshold): as ttt_layer_forward, except that
+ * every chunk's update eta * V_i^T Z_i is first scaled by
+ * min(1, clip_norm / ||eta * V_i^T Z_i||_F).
+ *   clip_norm   > 0 and finite (TTT_ERR_INVALID_ARG otherwise)
+ * The norms come from the chunk's C x C Gram matrices of Z (bf16) and V
+ * (fp16), so each scale carries their rounding (relative ~1e-3). The
+ * workspace (ttt_clipped_workspace_size) also holds a token-major copy of V
+ * and the per-chunk norms. Every other argument, layout and convention is
+ * ttt_layer_forward's. */
+ttt_status ttt_clipped_workspace_size(const ttt_desc* desc, int32_t chunk, float clip_norm,
+                                      size_t* bytes);
+ttt_status ttt_layer_forward_clipped(const ttt_desc* desc,
+                                     const void* H, const void* X0,
+                                     const void* Wg, const void* Wu,
+                                     const void* W_down0, const void* conv_taps,
+                                     const void* W_target, float eta, int32_t chunk,
+                                     float clip_norm, void* O, float* W_down_final,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* Packed documents: one sequence (batch must be 1) holding n_docs
  * documents back to back, document r starting at token doc_starts[r]
  * (iplexlaw explainer §6: the fast weight returns to the pretrained W_down

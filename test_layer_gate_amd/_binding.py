@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.ttt_layer_forward.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                     ctypes.c_int32, _P, _P, _P, _S, _P]
     I32P = ctypes.POINTER(ctypes.c_int32)
+    L.ttt_clipped_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.c_float,
+                                             ctypes.POINTER(_S)]
+    L.ttt_layer_forward_clipped.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                            ctypes.c_int32, ctypes.c_float, _P, _P, _P, _S, _P]
     L.ttt_packed_workspace_size.argtypes = [DP, ctypes.c_int32, I32P, ctypes.c_int32,
                                             ctypes.POINTER(_S)]
     L.ttt_layer_forward_packed.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
@@ -71,6 +75,7 @@ def lib() -> ctypes.CDLL:
     L.ttt_lm_target.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _S, _P]
     for fn in ("ttt_workspace_size", "ttt_step_workspace_size", "ttt_layer_forward",
                "ttt_packed_workspace_size", "ttt_layer_forward_packed",
+               "ttt_clipped_workspace_size", "ttt_layer_forward_clipped",
                "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
         getattr(L, fn).restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int32]
@@ -146,13 +151,15 @@ def workspace_size(desc: Desc, chunk: int) -> int:
 
 
 def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
-                  schedule=None, pad="sequence", out=None, W_down_final=None,
+                  schedule=None, pad="sequence", clip=None, out=None, W_down_final=None,
                   workspace=None, stream=None):
     """O, W_final for H, X0 [B, T, d]; Wg, Wu [f, d]; W_down0 [d, f] or
     [B, d, f]; conv_taps [K, d]; W_target [d, d] (see include/ttt.h).
 
     schedule: None (library default), "prefix" or "running". pad:
-    "sequence" (conv reads zero past the sequence end) or "chunk".
+    "sequence" (conv reads zero past the sequence end) or "chunk". clip:
+    None, or the Frobenius-norm limit of every chunk's update
+    (ttt_layer_forward_clipped).
     """
     _require_cuda(H, X0, Wg, Wu, W_down0, conv_taps, W_target)
     if H.dim() != 3 or X0.shape != H.shape:
@@ -178,17 +185,26 @@ def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
         raise ValueError("eta must be finite")
     stride = d * f if W_down0.dim() == 3 else 0
     desc = make_desc(B, T, d, f, K, act, wt, stride, _flags(schedule, pad))
-    ws_bytes = workspace_size(desc, int(chunk))
+    if clip is None:
+        ws_bytes = workspace_size(desc, int(chunk))
+    else:
+        n = _S(0)
+        _check(lib().ttt_clipped_workspace_size(ctypes.byref(desc), int(chunk),
+                                                ctypes.c_float(float(clip)), ctypes.byref(n)))
+        ws_bytes = n.value
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
     O = torch.empty_like(H) if out is None else out
     Wf = (torch.empty((B, d, f), dtype=torch.float32, device=H.device)
           if W_down_final is None else W_down_final)
     _require_cuda(O, Wf, workspace)
-    _check(lib().ttt_layer_forward(
-        ctypes.byref(desc), _ptr(H), _ptr(X0), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
-        _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk),
-        _ptr(O), _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream)))
+    args = [ctypes.byref(desc), _ptr(H), _ptr(X0), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
+            _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk)]
+    tail = [_ptr(O), _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream)]
+    if clip is None:
+        _check(lib().ttt_layer_forward(*args, *tail))
+    else:
+        _check(lib().ttt_layer_forward_clipped(*args, ctypes.c_float(float(clip)), *tail))
     return O, Wf
 
 

@@ -83,13 +83,14 @@ struct Geo {
   std::vector<Chunk> chunks;
   std::vector<tttk::BlockInfo> blocks;     // packed documents only: per 64-token block
   std::vector<tttk::ApplyTile> tiles;      // packed documents only: the apply's token tiles
+  float clip = 0.0f;                       // > 0: update-norm clipping limit
   size_t act_bytes() const { return act_f32 ? 4 : 2; }
   size_t w_bytes() const { return w_f32 ? 4 : 2; }
 };
 
 struct Layout {
   size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgp = 0, wup = 0,
-         blk = 0;
+         blk = 0, vrow = 0, partial = 0, scale = 0;
   size_t total = 0;
 };
 
@@ -120,6 +121,11 @@ Layout forward_layout(const Geo& g) {
   if (!g.blocks.empty())
     L.blk = take(g.blocks.size() * sizeof(tttk::BlockInfo) +
                  g.tiles.size() * sizeof(tttk::ApplyTile));
+  if (g.clip > 0.0f) {
+    L.vrow = take(g.B * g.T_pad * D.ld_y * 2);
+    L.partial = take(g.B * g.nchunks * tttk::clip_pairs((int)g.C) * 4);
+    L.scale = take(g.B * g.nchunks * 4);
+  }
   L.total = off;
   return L;
 }
@@ -212,6 +218,14 @@ ttt_status check_chunk(int32_t chunk, Geo* g) {
 // Packed documents: one sequence holding n_docs documents that start at
 // doc_starts[r]. Chunks restart at every document start; builds the chunk
 // list and the per-64-token block table the kernels read.
+// Update-norm clipping: the limit on each chunk's update norm.
+ttt_status check_clip(float clip_norm, Geo* g) {
+  if (!(clip_norm > 0.0f) || !std::isfinite(clip_norm))
+    return fail(TTT_ERR_INVALID_ARG, "clip_norm must be finite and > 0");
+  g->clip = clip_norm;
+  return TTT_OK;
+}
+
 ttt_status check_docs(const int32_t* doc_starts, int32_t n_docs, Geo* g) {
   if (g->B != 1) return fail(TTT_ERR_UNSUPPORTED, "packed documents need batch == 1");
   if (doc_starts == nullptr) return fail(TTT_ERR_INVALID_ARG, "doc_starts is NULL");
@@ -453,7 +467,18 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
              tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, D, (int)g.K, (int)g.C, g.pad_chunk,
                                blocks, s));
   TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, s));
-  TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, vscale, D, s));
+  const bool clip = g.clip > 0.0f && eta != 0.0f;
+  uint16_t* Vrow = clip ? at<uint16_t>(workspace, L.vrow) : nullptr;
+  TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, Vrow, vscale, D, s));
+  if (clip) {
+    // Every chunk's update eta V_i^T Z_i is scaled to a Frobenius norm of at
+    // most g.clip by scaling its columns of VT; the norm comes from the rows
+    // of vscale * V, hence the factor |eta| / vscale.
+    TTT_LAUNCH("clip_scale", s,
+               tttk::launch_clip_scale(Z, Vrow, at<float>(workspace, L.partial),
+                                       at<float>(workspace, L.scale), VT, D, (int)g.C,
+                                       (int)g.nchunks, std::fabs(eta) / vscale, g.clip, s));
+  }
 
   const int64_t snap_cstride = tttk::snap_elems(D);
   if (!g.running) {
@@ -500,6 +525,31 @@ ttt_status ttt_layer_forward(const ttt_desc* desc, const void* H, const void* X0
   Geo g;
   TTT_TRY(check_desc(desc, &g));
   TTT_TRY(check_chunk(chunk, &g));
+  return forward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, O, W_down_final,
+                      workspace, workspace_bytes, stream);
+}
+
+ttt_status ttt_clipped_workspace_size(const ttt_desc* desc, int32_t chunk, float clip_norm,
+                                      size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  TTT_TRY(check_clip(clip_norm, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = forward_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_forward_clipped(const ttt_desc* desc, const void* H, const void* X0,
+                                     const void* Wg, const void* Wu, const void* W_down0,
+                                     const void* conv_taps, const void* W_target, float eta,
+                                     int32_t chunk, float clip_norm, void* O,
+                                     float* W_down_final, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  TTT_TRY(check_clip(clip_norm, &g));
   return forward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, O, W_down_final,
                       workspace, workspace_bytes, stream);
 }
@@ -605,7 +655,8 @@ ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0, const void* conv_
              tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, g.dims, (int)g.K, (int)g.C,
                                g.pad_chunk, nullptr, s));
   TTT_LAUNCH("target", s,
-             tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), 1.0f, g.dims, s));
+             tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), nullptr, 1.0f,
+                                 g.dims, s));
   return TTT_OK;
 }
 

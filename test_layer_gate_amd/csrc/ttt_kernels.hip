@@ -623,7 +623,8 @@ constexpr int K2_BM = 256, K2_BN = 256, K2_WGM = 2, K2_BK = 64, K2_NST = 2;
 
 __global__ __launch_bounds__(kGemmThreads) void target_kernel(
     const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
-    u16* __restrict__ Vtok, float vscale, Dims g, int tiles_m, int tiles_n) {
+    u16* __restrict__ Vtok, u16* __restrict__ Vrow, float vscale, Dims g, int tiles_m,
+    int tiles_n) {
   using L = Layout<K2_BM, K2_BN, K2_WGM>;
   TTT_GEMM_LDS(lds, K2_BM, K2_BN, K2_BK, K2_NST)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
@@ -657,6 +658,140 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
         }
       }
     }
+  if (Vrow == nullptr) return;
+  // Token-major fp16 vscale * V ([B][T_pad][ld_y]) through LDS, 128 tile
+  // rows per pass (the rows of one wave row), so that its stores are whole
+  // 16-byte row segments.
+  constexpr int LDV = K2_BN + 8;
+  static_assert(K2_BM / K2_WGM == 128 && 128 * LDV <= K2_NST * (K2_BM + K2_BN) * K2_BK, "staging");
+#pragma unroll
+  for (int pass = 0; pass < K2_WGM; ++pass) {
+    __syncthreads();
+    if (fr.wm == pass) {
+#pragma unroll
+      for (int m = 0; m < L::TM; ++m)
+#pragma unroll
+        for (int n = 0; n < L::TN; ++n)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = m * 32 + 8 * q + 4 * (fr.lane >> 5);
+            u16* sv = lds + row * LDV + fr.col(n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[e * LDV] = f16_rne(acc[m][n][4 * q + e] * vscale);
+          }
+    }
+    __syncthreads();
+    constexpr int SEG = 128 * (K2_BN / 8);  // 16-byte row segments per pass
+#pragma unroll
+    for (int k = 0; k < SEG / kGemmThreads; ++k) {
+      const int sidx = threadIdx.x + k * kGemmThreads;
+      const int row = sidx / (K2_BN / 8), cc = sidx % (K2_BN / 8);
+      const int t = t0 + pass * 128 + row, c = c0 + cc * 8;
+      if (c < d)
+        store_stream(Vrow + ((int64_t)ti.b * g.T_pad + t) * g.ld_y + c,
+                     *reinterpret_cast<const uint4*>(lds + row * LDV + cc * 8));
+    }
+  }
+}
+
+// ------------------------------------------------- update-norm clipping
+// For clipping each chunk's update eta V_i^T Z_i to a Frobenius norm
+// ([iplex] §6), the norm comes from two C x C Gram matrices instead of the
+// d x f delta: ||V_i^T Z_i||_F^2 = sum_{s,t in chunk i} (V_s . V_t)(Z_s . Z_t).
+// One workgroup per pair (sb <= tb) of 128-token blocks of a chunk computes
+// the Z Gram tile (K = d_ff, bf16) and the V Gram tile (K = d_model, fp16,
+// on vscale * V) with the GEMM core, and writes the sum of their elementwise
+// product (twice for sb < tb) to partial[b][chunk][pair].
+constexpr int KG_B = 128, KG_WGM = 2;
+
+__global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
+    const u16* __restrict__ Z, const u16* __restrict__ Vrow, float* __restrict__ partial,
+    Dims g, int chunk, int nblk, int npair, int nchunks) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using L = Layout<KG_B, KG_B, KG_WGM>;
+  TTT_GEMM_LDS(lds, KG_B, KG_B, 64, 2)
+  __shared__ float wsum[kGemmWaves];
+  const int pair = blockIdx.x % npair, rest = blockIdx.x / npair;
+  const int i = rest % nchunks, b = rest / nchunks;
+  int sb = 0, tb = pair;  // pair -> (sb, tb), sb <= tb, upper triangle row by row
+  while (tb >= nblk - sb) {
+    tb -= nblk - sb;
+    ++sb;
+  }
+  tb += sb;
+  const int c0 = i * chunk, c1 = min(g.T, c0 + chunk);
+  const int s0 = c0 + sb * KG_B, u0 = c0 + tb * KG_B;
+  float sum = 0.f;
+  if (u0 < c1) {  // uniform: blocks past a short last chunk add nothing
+    f32x16 az[L::TM][L::TN], av[L::TM][L::TN];
+    zero_acc(az);
+    zero_acc(av);
+    const Operand zs = row_major<64>(Z + ((int64_t)b * g.T + s0) * g.ld_z, g.ld_z, c1 - s0);
+    const Operand zu = row_major<64>(Z + ((int64_t)b * g.T + u0) * g.ld_z, g.ld_z, c1 - u0);
+    gemm_core<KG_B, KG_B, KG_WGM, 64, 2, Bf16Mma, false, kRowMajor, kRowMajor>(
+        zs, zu, zu, g.f / 64, &az[0][0], lds, NoHook{});
+    const Operand vs =
+        row_major<64>(Vrow + ((int64_t)b * g.T_pad + s0) * g.ld_y, g.ld_y, c1 - s0);
+    const Operand vu =
+        row_major<64>(Vrow + ((int64_t)b * g.T_pad + u0) * g.ld_y, g.ld_y, c1 - u0);
+    gemm_core<KG_B, KG_B, KG_WGM, 64, 2, F16Mma, false, kRowMajor, kRowMajor>(
+        vs, vu, vu, g.d / 64, &av[0][0], lds, NoHook{});
+#pragma unroll
+    for (int m = 0; m < L::TM; ++m)
+#pragma unroll
+      for (int n = 0; n < L::TN; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum = fmaf(az[m][n][r], av[m][n][r], sum);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGemmWaves; ++w) tot += wsum[w];
+    partial[((int64_t)b * nchunks + i) * npair + pair] = (sb == tb ? 1.f : 2.f) * tot;
+  }
+#endif
+}
+
+// scale[b][i] = min(1, clip / ||eta V_i^T Z_i||_F), the norm being
+// norm_factor * sqrt(sum of chunk i's partials), summed in a fixed order.
+__global__ __launch_bounds__(kThreads) void clip_scale_kernel(const float* __restrict__ partial,
+                                                             float* __restrict__ scale, int npair,
+                                                             int n, float norm_factor,
+                                                             float clip) {
+  const int idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= n) return;
+  double s2 = 0.0;
+  for (int p = 0; p < npair; ++p) s2 += (double)partial[(int64_t)idx * npair + p];
+  const double nrm = (double)norm_factor * sqrt(s2 > 0.0 ? s2 : 0.0);
+  scale[idx] = nrm > (double)clip ? (float)((double)clip / nrm) : 1.0f;
+}
+
+// VT *= scale of each token's chunk (a 64-token slab lies in one chunk).
+__global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT,
+                                                           const float* __restrict__ scale,
+                                                           Dims g, int chunk, int nchunks,
+                                                           int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n16) return;
+  const int64_t e = i * 8, per_b = sb_elems<kVtSlab>(g.d, g.T_pad);
+  const int b = (int)(e / per_b);
+  const int64_t slab = (e % per_b) / (kVtSlab * 64);
+  const int tok = (int)(slab % (g.T_pad / 64)) * 64;
+  const float sc = scale[(int64_t)b * nchunks + min(tok / chunk, nchunks - 1)];
+  if (sc == 1.0f) return;
+  uint4 v = reinterpret_cast<uint4*>(VT)[i];
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = (float)__builtin_bit_cast(_Float16, (u16)(w[k] & 0xffffu));
+    const float hi = (float)__builtin_bit_cast(_Float16, (u16)(w[k] >> 16));
+    w[k] = pack_f16(lo * sc, hi * sc);
+  }
+  reinterpret_cast<uint4*>(VT)[i] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ------------------------------------------ fast-weight update (K3)
@@ -1089,10 +1224,33 @@ hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t
 }
 
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
-                         float vscale, const Dims& g, hipStream_t s) {
+                         uint16_t* Vrow, float vscale, const Dims& g, hipStream_t s) {
   const int tiles_m = g.T_pad / K2_BM, tiles_n = ceil_div(g.d, K2_BN);
-  target_kernel<<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(Y, WtT, VT, Vtok, vscale, g, tiles_m,
-                                                             tiles_n);
+  target_kernel<<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(Y, WtT, VT, Vtok, Vrow, vscale,
+                                                             g, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+int clip_pairs(int chunk) {
+  const int nblk = ceil_div(chunk, KG_B);
+  return nblk * (nblk + 1) / 2;
+}
+
+hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* partial,
+                             float* scale, uint16_t* VT, const Dims& g, int chunk, int nchunks,
+                             float norm_factor, float clip, hipStream_t s) {
+  const int nblk = ceil_div(chunk, KG_B), npair = clip_pairs(chunk);
+  gram_norm_kernel<<<g.B * nchunks * npair, kGemmThreads, 0, s>>>(Z, Vrow, partial, g, chunk,
+                                                                 nblk, npair, nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = g.B * nchunks;
+  clip_scale_kernel<<<ceil_div(n, kThreads), kThreads, 0, s>>>(partial, scale, npair, n,
+                                                               norm_factor, clip);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n16 = vt_elems(g) / 8;
+  vt_scale_kernel<<<ceil_div(n16, kThreads), kThreads, 0, s>>>(VT, scale, g, chunk, nchunks, n16);
   return hipGetLastError();
 }
 

@@ -133,10 +133,20 @@ hipError_t launch_pack_weight(const void* W, bool w_f32, uint16_t* dst, const Di
 hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
                           uint16_t* Z, uint16_t* ZT, const Dims& g, hipStream_t s);
 
-// V = Y WtT^T (conv(X0) W_target): fp16 VT = vscale * V (feature-major) and
-// bf16 Vtok = vscale * V ([B][T][d]); either may be null.
+// V = Y WtT^T (conv(X0) W_target): fp16 VT = vscale * V (feature-major),
+// bf16 Vtok = vscale * V ([B][T][d]) and fp16 Vrow = vscale * V ([B][T_pad]
+// [ld_y]); any may be null.
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
-                         float vscale, const Dims& g, hipStream_t s);
+                         uint16_t* Vrow, float vscale, const Dims& g, hipStream_t s);
+
+// Update-norm clipping: per chunk i of `chunk` tokens (uniform chunks),
+// scale[b][i] = min(1, clip / (norm_factor * ||Vrow_i^T Z_i||_F)) from the
+// Gram form (partial: B * nchunks * clip_pairs(chunk) floats), then VT *=
+// the scale of each token's chunk.
+int clip_pairs(int chunk);
+hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* partial,
+                             float* scale, uint16_t* VT, const Dims& g, int chunk, int nchunks,
+                             float norm_factor, float clip, hipStream_t s);
 
 // Fast-weight update over tokens [tok_begin, tok_begin + tok_count) (a
 // multiple of 64), in 64-token steps (columns past T read as zero). acc =

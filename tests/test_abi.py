@@ -233,3 +233,43 @@ def test_packed_forward_validates_before_launch(L):
     st = L.ttt_layer_forward_packed(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3), 1024,
                                     starts, 2, p[7], p[8], p[9], ctypes.c_size_t(need - 1), None)
     assert st == WORKSPACE
+
+
+# ---- update-norm clipping ----------------------------------------------------
+
+def clipped_ws(L, desc, chunk, clip):
+    n = ctypes.c_size_t(0)
+    st = L.ttt_clipped_workspace_size(ctypes.byref(desc), chunk, ctypes.c_float(clip),
+                                      ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("clip,code", [(1.0, OK), (1e-6, OK), (0.0, INVALID), (-1.0, INVALID),
+                                       (float("inf"), INVALID), (float("nan"), INVALID)])
+def test_clip_validation(L, clip, code):
+    st, _ = clipped_ws(L, qwen_desc(), 1024, clip)
+    assert st == code, (clip, st)
+
+
+def test_clipped_workspace_size(L):
+    st, n = clipped_ws(L, qwen_desc(), 1024, 1.0)
+    assert st == OK
+    _, plain = ws_size(L, qwen_desc(), 1024)
+    T, d, k = 65536, 2560, 64
+    ld_y = d + 64 if (d // 64) % 2 == 0 else d
+    pairs = 8 * 9 // 2                              # 128-token blocks of a 1024-token chunk
+    extra = T * ld_y * 2 + k * pairs * 4 + k * 4    # token-major V, Gram partials, scales
+    assert plain + extra <= n <= plain + extra + 4 * 256
+
+
+def test_clipped_forward_validates_before_launch(L):
+    p = good_ptrs()
+    st = L.ttt_layer_forward_clipped(ctypes.byref(qwen_desc()), *p[:7], ctypes.c_float(1e-3),
+                                     1024, ctypes.c_float(0.0), p[7], p[8], p[9],
+                                     ctypes.c_size_t(1 << 62), None)
+    assert st == INVALID
+    _, need = clipped_ws(L, qwen_desc(), 1024, 1.0)
+    st = L.ttt_layer_forward_clipped(ctypes.byref(qwen_desc()), *p[:7], ctypes.c_float(1e-3),
+                                     1024, ctypes.c_float(1.0), p[7], p[8], p[9],
+                                     ctypes.c_size_t(need - 1), None)
+    assert st == WORKSPACE
