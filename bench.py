@@ -47,15 +47,17 @@ KERNEL_NAMES = {"gate_up": "gate_up_kernel", "target": "target_kernel",
 
 
 def kernel_work(name, cfg, T_pad):
-    """(bound, algorithmic amount per launch, unit) of each kernel of one
-    step: FLOPs of the contraction (2 per multiply-add) for MFMA kernels,
-    bytes moved once for the bandwidth-bound ones."""
+    """(bound, algorithmic amount per step) of each kernel of one step:
+    FLOPs of the contraction (2 per multiply-add) for MFMA kernels, bytes
+    moved once for the bandwidth-bound ones. A kernel launched several times
+    per step (the running schedule's per-chunk apply and update) shares the
+    amount over its launches."""
     B, T, d, f, K = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.conv_k
     if name == "gate_up":
         return "mfma", 4.0 * B * T * d * f
     if name == "target":
         return "mfma", 2.0 * B * T * d * d
-    if name in ("update_prefix", "apply"):
+    if name in ("update_prefix", "update_running", "apply"):
         return "mfma", 2.0 * B * T * d * f
     if name == "conv":
         return "hbm", 2.0 * B * T * d + 2.0 * B * T_pad * d + 2.0 * K * d
@@ -284,6 +286,8 @@ def main():
                for n, (c, ms) in kstats.items()}
     dom = max(kstats, key=lambda n: kstats[n][1])
     bound, work = kernel_work(dom, cfg, T_pad)
+    launches_per_step = kstats[dom][0] / args.steps
+    work = work / launches_per_step          # per launch
     avg_s = kstats[dom][1] / kstats[dom][0] / 1e3
     if bound == "mfma":
         achieved = work / avg_s / 1e12
