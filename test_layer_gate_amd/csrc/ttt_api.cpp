@@ -228,6 +228,8 @@ ttt_status check_clip(float clip_norm, Geo* g) {
 
 ttt_status check_docs(const int32_t* doc_starts, int32_t n_docs, Geo* g) {
   if (g->B != 1) return fail(TTT_ERR_UNSUPPORTED, "packed documents need batch == 1");
+  if (g->T_pad / 64 > 2048)
+    return fail(TTT_ERR_UNSUPPORTED, "packed documents support up to 131072 tokens");
   if (doc_starts == nullptr) return fail(TTT_ERR_INVALID_ARG, "doc_starts is NULL");
   if (n_docs < 1) return fail(TTT_ERR_INVALID_ARG, "n_docs must be >= 1");
   if (doc_starts[0] != 0) return fail(TTT_ERR_INVALID_ARG, "doc_starts[0] must be 0");

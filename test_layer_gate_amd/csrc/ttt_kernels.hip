@@ -838,8 +838,12 @@ struct SnapshotStore {
 };
 
 // acc = acc_scale * W for the wave's part of a [d_ff tile] x [d_model tile]
-// state block, W element (c, j) at W + c * ld + j (bf16 or fp32).
-template <class L, bool F32>
+// state block, W element (c, j) at W + c * ld + j (bf16 or fp32). BATCHED:
+// the loads are unconditional (lanes outside the matrix read element 0 and
+// drop it), so that they are issued back to back and waited for once; this
+// needs registers for all of them, so inside the K loop (the packed
+// update's reset) the per-element conditional form is used instead.
+template <class L, bool F32, bool BATCHED = true>
 struct StateLoad {
   const void* W;
   int64_t ld;
@@ -855,22 +859,24 @@ struct StateLoad {
         for (int q = 0; q < 4; ++q) {
           const int j = j0 + fr.row(m, q);
           const int c = c0 + fr.col(n);
+          const bool in = c < d && j < f;
+          const int64_t o = in ? (int64_t)c * ld + j : 0;
+          const float keep = in ? acc_scale : 0.0f;
           float v[4] = {0.f, 0.f, 0.f, 0.f};
-          if (c < d && j < f) {
-            const int64_t o = (int64_t)c * ld + j;
-            if constexpr (F32) {
-              const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + o);
-              v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-            } else {
-              const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const u16*>(W) + o);
-              v[0] = __uint_as_float(x.x << 16);
-              v[1] = __uint_as_float(x.x & 0xffff0000u);
-              v[2] = __uint_as_float(x.y << 16);
-              v[3] = __uint_as_float(x.y & 0xffff0000u);
-            }
+          if (!BATCHED && !in) {
+            // no load
+          } else if constexpr (F32) {
+            const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + o);
+            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+          } else {
+            const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const u16*>(W) + o);
+            v[0] = __uint_as_float(x.x << 16);
+            v[1] = __uint_as_float(x.x & 0xffff0000u);
+            v[2] = __uint_as_float(x.y << 16);
+            v[3] = __uint_as_float(x.y & 0xffff0000u);
           }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[m * L::TN + n][4 * q + e] = v[e] * acc_scale;
+          for (int e = 0; e < 4; ++e) acc[m * L::TN + n][4 * q + e] = v[e] * keep;
         }
   }
 };
@@ -886,20 +892,20 @@ template <class L, bool F32, bool PACKED>
 struct ChunkSnapshots {
   static constexpr int kStores = SnapshotStore<L>::kStores;
   SnapshotStore<L> store;
-  StateLoad<L, F32> reset;
+  StateLoad<L, F32, false> reset;
   u16* snap;  // this sequence's snapshots, or null
   int64_t chunk_stride;
   int steps_per_chunk;
-  const BlockInfo* blocks;  // PACKED: per K step of this launch
-  int n_chunks;             // PACKED: snapshot slots (table values are clamped to them)
+  const uint32_t* steps;  // PACKED: per K step of this launch, in LDS (step_word)
+  int n_chunks;           // PACKED: snapshot slots (table values are clamped to them)
   __device__ __forceinline__ bool operator()(int kt, f32x16* acc) const {
     int slot;
     if constexpr (PACKED) {
-      // A vector load: its vmcnt wait also waits for the stage loads in
-      // flight, which costs the packed update time at every step.
-      const BlockInfo info = blocks[kt];
-      const int flags = info.flags;
-      slot = min(max(info.chunk, 0), n_chunks - 1);
+      // An LDS read (lgkmcnt): a global load here would need a vmcnt wait,
+      // which also waits for the stage loads in flight.
+      const uint32_t w = steps[kt];
+      const int flags = (int)(w >> 30);
+      slot = min((int)(w & 0x3fffffffu), n_chunks - 1);
       if ((flags & kBlockDocStart) && kt > 0) reset(acc);
       if (snap == nullptr || !(flags & kBlockChunkStart)) return false;
     } else {
@@ -911,6 +917,12 @@ struct ChunkSnapshots {
   }
 };
 
+// A block's {chunk, flags} in one word, for the packed update's LDS copy.
+__device__ __forceinline__ uint32_t step_word(const BlockInfo& b) {
+  return ((uint32_t)b.chunk & 0x3fffffffu) | ((uint32_t)(b.flags & 3) << 30);
+}
+constexpr int kMaxPackedSteps = 2048;  // K steps of a packed update launch (131072 tokens)
+
 template <bool WINIT_F32, bool PACKED>
 __global__ __launch_bounds__(kGemmThreads) void update_kernel(
     const u16* __restrict__ ZT, const u16* __restrict__ VT, const void* __restrict__ Winit,
@@ -921,6 +933,14 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
   using L = Layout<K3_BM, K3_BN, K3_WGM>;
   constexpr int TM = L::TM, TN = L::TN;
   TTT_GEMM_LDS(lds, K3_BM, K3_BN, K3_BK, K3_NST)
+  __shared__ uint32_t steps[PACKED ? kMaxPackedSteps : 1];
+  if constexpr (PACKED) {
+    // This launch's block table, one word per K step (nk <= kMaxPackedSteps,
+    // checked on the host); the pipeline's first barrier publishes it.
+    for (int k = threadIdx.x; k < nk; k += kGemmThreads)
+      steps[k] = step_word(blocks[tok_begin / K3_BK + k]);
+    __syncthreads();
+  }
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int j0 = ti.tm * K3_BM, c0 = ti.tn * K3_BN;
   const int d = g.d, f = g.f;
@@ -932,13 +952,14 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
       WINIT_F32 ? (const void*)(static_cast<const float*>(Winit) + ti.b * winit_bstride)
                 : (const void*)(static_cast<const u16*>(Winit) + ti.b * winit_bstride);
   const StateLoad<L, WINIT_F32> init{winit_b, winit_ld, j0, c0, d, f, acc_scale};
+  const StateLoad<L, WINIT_F32, false> reset{winit_b, winit_ld, j0, c0, d, f, acc_scale};
   f32x16 acc[TM][TN];
   init(&acc[0][0]);
 
   const SnapshotStore<L> snapshot{j0, c0, d, f, out_scale, (uint32_t)(chunk_stride * 2)};
   const ChunkSnapshots<L, WINIT_F32, PACKED> hook{
-      snapshot, init, snap ? snap + ti.b * snap_bstride : nullptr, chunk_stride,
-      steps_per_chunk, blocks ? blocks + tok_begin / K3_BK : nullptr, n_chunks};
+      snapshot, reset, snap ? snap + ti.b * snap_bstride : nullptr, chunk_stride,
+      steps_per_chunk, steps, n_chunks};
   // Rows past d_ff / d_model in the last slabs are never written; they only
   // feed output rows / columns that are not stored.
   static_assert(K3_BM == kZtSlab && K3_BN == kVtSlab && K3_BK == 64, "update tile = slabs");
