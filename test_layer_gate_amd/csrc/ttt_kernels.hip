@@ -261,12 +261,18 @@ struct TileIdx {
   int b, tm, tn;
 };
 
-__device__ __forceinline__ TileIdx tile_index(int tiles_m, int tiles_n, int group_m) {
+// The workgroup id renumbered so that the workgroups of one XCD form one
+// contiguous range of ids.
+__device__ __forceinline__ int xcd_contiguous_id() {
   const int nblk = gridDim.x;
-  int lin = blockIdx.x;
+  const int lin = blockIdx.x;
   const int xcd = lin & 7, idx = lin >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
-  lin = xcd * per + min(xcd, rem) + idx;
+  return xcd * per + min(xcd, rem) + idx;
+}
+
+__device__ __forceinline__ TileIdx tile_index(int tiles_m, int tiles_n, int group_m) {
+  int lin = xcd_contiguous_id();
   const int per_batch = tiles_m * tiles_n;
   TileIdx t;
   t.b = lin / per_batch;
@@ -1093,6 +1099,18 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const void* __restr
   }
 }
 
+// Depthwise conv, kConvRows consecutive tokens x 8 channels per thread: a
+// window of kConvRows X0 rows slides down one row per tap, so each row is
+// loaded once per thread instead of once per tap. Output t sums tap k over
+// k = 0, 1, ... in order while t + k is before its bound (the sequence, the
+// chunk or the document end).
+constexpr int kConvRows = 8;
+static_assert(kTokenPad % kConvRows == 0, "row windows tile the padded sequence");
+
+__device__ __forceinline__ uint4 load_row8(const u16* X0, int64_t row_off, bool ok) {
+  return ok ? *reinterpret_cast<const uint4*>(X0 + row_off) : make_uint4(0u, 0u, 0u, 0u);
+}
+
 template <bool TAPS_F32>
 __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ X0,
                                                         const void* __restrict__ taps,
@@ -1100,21 +1118,33 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
                                                         int chunk, int pad_chunk,
                                                         const BlockInfo* __restrict__ blocks,
                                                         int64_t total) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // Neighbouring row windows overlap by K - 1 rows; keeping them on one XCD
+  // lets the overlap come from that XCD's L2.
+  const int64_t gid = (int64_t)xcd_contiguous_id() * kThreads + threadIdx.x;
   if (gid >= total) return;
   const int d = g.d, T = g.T;
   const int d8 = d >> 3;
   const int c = (int)(gid % d8) * 8;
   const int64_t bt = gid / d8;
-  const int t = (int)(bt % g.T_pad);
-  const int b = (int)(bt / g.T_pad);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int end = blocks != nullptr
-                      ? min(T, pad_chunk ? blocks[t >> 6].chunk_end : blocks[t >> 6].doc_end)
-                      : (pad_chunk ? min(T, (t / chunk + 1) * chunk) : T);
-  for (int k = 0; k < K && t + k < end; ++k) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(X0 + ((int64_t)b * T + t + k) * d + c);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const int groups = g.T_pad / kConvRows;
+  const int t = (int)(bt % groups) * kConvRows;
+  const int b = (int)(bt / groups);
+  const u16* xb = X0 + (int64_t)b * T * d + c;
+  int end[kConvRows];
+  int last = 0;
+#pragma unroll
+  for (int r = 0; r < kConvRows; ++r) {
+    const int tr = t + r;
+    end[r] = blocks != nullptr
+                 ? min(T, pad_chunk ? blocks[tr >> 6].chunk_end : blocks[tr >> 6].doc_end)
+                 : (pad_chunk ? min(T, (tr / chunk + 1) * chunk) : T);
+    last = max(last, end[r]);
+  }
+  float acc[kConvRows][8] = {};
+  uint4 win[kConvRows];
+#pragma unroll
+  for (int r = 0; r < kConvRows; ++r) win[r] = load_row8(xb, (int64_t)(t + r) * d, t + r < T);
+  for (int k = 0; k < K && t + k < last; ++k) {
     float tp[8];
     if constexpr (TAPS_F32) {
       const float4* p =
@@ -1133,14 +1163,27 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] = fmaf(tp[2 * e], __uint_as_float(xw[e] << 16), acc[2 * e]);
-      acc[2 * e + 1] = fmaf(tp[2 * e + 1], __uint_as_float(xw[e] & 0xffff0000u), acc[2 * e + 1]);
+    for (int r = 0; r < kConvRows; ++r) {
+      if (t + r + k < end[r]) {
+        const uint32_t xw[4] = {win[r].x, win[r].y, win[r].z, win[r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[r][2 * e] = fmaf(tp[2 * e], __uint_as_float(xw[e] << 16), acc[r][2 * e]);
+          acc[r][2 * e + 1] =
+              fmaf(tp[2 * e + 1], __uint_as_float(xw[e] & 0xffff0000u), acc[r][2 * e + 1]);
+        }
+      }
     }
+#pragma unroll
+    for (int r = 0; r + 1 < kConvRows; ++r) win[r] = win[r + 1];
+    const int nr = t + kConvRows + k;
+    win[kConvRows - 1] = load_row8(xb, (int64_t)nr * d, nr < T);
   }
-  *reinterpret_cast<uint4*>(Y + ((int64_t)b * g.T_pad + t) * g.ld_y + c) =
-      make_uint4(pack_f16(acc[0], acc[1]), pack_f16(acc[2], acc[3]), pack_f16(acc[4], acc[5]),
-                 pack_f16(acc[6], acc[7]));
+#pragma unroll
+  for (int r = 0; r < kConvRows; ++r)
+    *reinterpret_cast<uint4*>(Y + ((int64_t)b * g.T_pad + t + r) * g.ld_y + c) =
+        make_uint4(pack_f16(acc[r][0], acc[r][1]), pack_f16(acc[r][2], acc[r][3]),
+                   pack_f16(acc[r][4], acc[r][5]), pack_f16(acc[r][6], acc[r][7]));
 }
 
 // One thread per 8 packed elements, in packed (destination) order: row
@@ -1214,7 +1257,7 @@ hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, in
 hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint16_t* Y,
                        const Dims& g, int K, int chunk, bool pad_chunk,
                        const BlockInfo* blocks, hipStream_t s) {
-  const int64_t total = (int64_t)g.B * g.T_pad * (g.d / 8);
+  const int64_t total = (int64_t)g.B * (g.T_pad / kConvRows) * (g.d / 8);
   const int grid = ceil_div(total, kThreads);
   if (taps_f32)
     conv_kernel<true><<<grid, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
