@@ -251,11 +251,12 @@ def final_state_entries(H_b, X0_b, Wg, Wu, W0_b, taps, W_target, eta, cs, js,
     Summing the update equation over all chunks gives
     W_final = W_down0 + eta * sum_i V_i^T Z_i = W_down0 + eta * V^T Z, since
     the chunks partition the tokens; each entry needs only column j of Z and
-    column c of V over all tokens.
+    column c of V over all tokens. X0_b may carry look-ahead rows past the
+    T = len(H_b) tokens (read by the conv only).
     """
     H_b, Wg, Wu = _f64(H_b), _f64(Wg), _f64(Wu)
     cs, js = np.asarray(cs), np.asarray(js)
     Zc = silu(H_b @ Wg[js].T) * (H_b @ Wu[js].T)                  # [T, |js|]
-    Y = conv_target_input(X0_b, taps, pad, chunk)                  # [T, d]
+    Y = conv_target_input(X0_b, taps, pad, chunk, n_out=H_b.shape[0])  # [T, d]
     Vc = Y @ _f64(W_target)[:, cs]                                  # [T, |cs|]
     return _f64(W0_b)[np.ix_(cs, js)] + eta * (Vc.T @ Zc)

@@ -311,6 +311,14 @@ def pin_sampled_forms():
                                    pad=pad, chunk=8),
                    torch_target(x["X0"][b], x["taps"], x["W_target"], pad, 8)[rows],
                    what=f"target rows ({pad})")
+    # a segment whose X0 carries two look-ahead rows past its 24 tokens
+    _, W1 = run(x, H=x["H"][:, :24], X0=x["X0"][:, :26])
+    for b in range(2):
+        got = ora.final_state_entries(x["H"][b, :24], x["X0"][b, :26], x["Wg"], x["Wu"],
+                                      x["W_down0"], x["taps"], x["W_target"], x["eta"],
+                                      [0, 3, 5], [1, 2, 9])
+        _close(got, W1[b][np.ix_([0, 3, 5], [1, 2, 9])], tol=1e-12,
+               what="final entries (look-ahead)")
     _close(ora.activation_rows(x["H"][0], x["Wg"], x["Wu"], [2, 30]),
            torch_z(x["H"][0], x["Wg"], x["Wu"])[[2, 30]], what="Z rows")
 
