@@ -167,6 +167,35 @@ ttt_status ttt_layer_forward_packed(const ttt_desc* desc,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* Continuation: the next segment of sequences whose earlier tokens went
+ * through a previous call. The fast weight keeps changing over a whole
+ * document and is reset only at its end (iplexlaw explainer §6 and §8), so
+ * a long document may be prefilled in segments: each segment starts from the
+ * state the previous one ended with, and its conv reads the first rows of
+ * the next segment exactly as one call over the whole document would. Split
+ * at a multiple of C, two calls give the one-call result.
+ *   X0_next   [B, n_next, d] act_dtype: X0 rows T .. T + n_next - 1 of each
+ *             sequence (the next segment's first tokens); 0 <= n_next <=
+ *             K - 1 (TTT_ERR_INVALID_ARG otherwise). Ignored, and may be
+ *             NULL, when n_next is 0. The conv reads rows past T + n_next as
+ *             zero (with TTT_FLAG_PAD_CHUNK it never reads past T).
+ *   W_state   [B, d, f] float32 in/out: the state before the segment (for
+ *             the first segment, W_down0 widened to fp32, one per sequence),
+ *             overwritten in place with the state after its last chunk. It
+ *             must not overlap any other argument (TTT_ERR_ALIAS).
+ *   desc->w0_batch_stride must be 0 (W_state is always [B, d, f]).
+ * The workspace size comes from ttt_continue_workspace_size(). Every other
+ * argument, layout and convention is ttt_layer_forward's. */
+ttt_status ttt_continue_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes);
+ttt_status ttt_layer_forward_continue(const ttt_desc* desc,
+                                      const void* H, const void* X0,
+                                      const void* X0_next, int32_t n_next,
+                                      const void* Wg, const void* Wu,
+                                      float* W_state, const void* conv_taps,
+                                      const void* W_target, float eta, int32_t chunk,
+                                      void* O, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 /* Step entry points: one step of the layer each, for per-step checks.
  * ttt_gated_activation writes Z [B, T, d_ff] in bf16.
  * ttt_lm_target writes V [B, T, d_model] in bf16 (unscaled, eta not applied).

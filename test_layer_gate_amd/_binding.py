@@ -71,11 +71,16 @@ def lib() -> ctypes.CDLL:
     L.ttt_layer_forward_packed.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                            ctypes.c_int32, I32P, ctypes.c_int32, _P, _P, _P,
                                            _S, _P]
+    L.ttt_continue_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
+    L.ttt_layer_forward_continue.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
+                                             _P, ctypes.c_float, ctypes.c_int32, _P, _P, _S,
+                                             _P]
     L.ttt_gated_activation.argtypes = [DP, _P, _P, _P, _P, _P, _S, _P]
     L.ttt_lm_target.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _S, _P]
     for fn in ("ttt_workspace_size", "ttt_step_workspace_size", "ttt_layer_forward",
                "ttt_packed_workspace_size", "ttt_layer_forward_packed",
                "ttt_clipped_workspace_size", "ttt_layer_forward_clipped",
+               "ttt_continue_workspace_size", "ttt_layer_forward_continue",
                "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
         getattr(L, fn).restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int32]
@@ -266,6 +271,63 @@ def layer_forward_packed(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk
         _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk), arr, n_docs,
         _ptr(O), _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream)))
     return (O[0], Wf[0]) if squeeze else (O, Wf)
+
+
+def continue_workspace_size(desc: Desc, chunk: int) -> int:
+    n = _S(0)
+    _check(lib().ttt_continue_workspace_size(ctypes.byref(desc), chunk, ctypes.byref(n)))
+    return n.value
+
+
+def layer_forward_continue(H, X0, X0_next, Wg, Wu, W_state, conv_taps, W_target, eta,
+                           chunk, *, schedule=None, pad="sequence", out=None,
+                           workspace=None, stream=None):
+    """O for the next segment of B sequences (include/ttt.h,
+    ttt_layer_forward_continue). H, X0 [B, T, d]; X0_next [B, L, d] with
+    0 <= L <= K - 1 (the X0 rows that follow the segment), or None; W_state
+    [B, d, f] float32, read as the state before the segment and overwritten
+    in place with the state after it. Returns O."""
+    _require_cuda(H, X0, Wg, Wu, W_state, conv_taps, W_target)
+    if H.dim() != 3 or X0.shape != H.shape:
+        raise ValueError("H and X0 must both be [B, T, d]")
+    B, T, d = H.shape
+    f = Wg.shape[0]
+    K = conv_taps.shape[0]
+    if Wg.shape != (f, d) or Wu.shape != (f, d):
+        raise ValueError("Wg and Wu must be [d_ff, d_model]")
+    if W_state.shape != (B, d, f) or W_state.dtype != torch.float32:
+        raise ValueError("W_state must be float32 [B, d_model, d_ff]")
+    if conv_taps.shape != (K, d) or W_target.shape != (d, d):
+        raise ValueError("conv_taps must be [K, d_model] and W_target [d_model, d_model]")
+    act = _dtype_code(H, "H")
+    wt = _dtype_code(Wg, "Wg")
+    if X0.dtype != H.dtype:
+        raise TypeError("X0 must have H's dtype")
+    for t, n in ((Wu, "Wu"), (conv_taps, "conv_taps"), (W_target, "W_target")):
+        if t.dtype != Wg.dtype:
+            raise TypeError(f"{n} must have Wg's dtype")
+    n_next = 0
+    if X0_next is not None:
+        _require_cuda(X0_next)
+        if X0_next.dim() != 3 or X0_next.shape[0] != B or X0_next.shape[2] != d:
+            raise ValueError("X0_next must be [B, L, d]")
+        if X0_next.dtype != H.dtype:
+            raise TypeError("X0_next must have H's dtype")
+        n_next = X0_next.shape[1]
+    if not math.isfinite(float(eta)):
+        raise ValueError("eta must be finite")
+    desc = make_desc(B, T, d, f, K, act, wt, 0, _flags(schedule, pad))
+    ws_bytes = continue_workspace_size(desc, int(chunk))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
+    O = torch.empty_like(H) if out is None else out
+    _require_cuda(O, workspace)
+    _check(lib().ttt_layer_forward_continue(
+        ctypes.byref(desc), _ptr(H), _ptr(X0),
+        _ptr(X0_next) if n_next > 0 else ctypes.c_void_p(0), int(n_next), _ptr(Wg), _ptr(Wu),
+        _ptr(W_state), _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)),
+        int(chunk), _ptr(O), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return O
 
 
 def _step_ws(desc, device):

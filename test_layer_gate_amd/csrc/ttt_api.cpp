@@ -84,13 +84,14 @@ struct Geo {
   std::vector<tttk::BlockInfo> blocks;     // packed documents only: per 64-token block
   std::vector<tttk::ApplyTile> tiles;      // packed documents only: the apply's token tiles
   float clip = 0.0f;                       // > 0: update-norm clipping limit
+  bool resume = false;                     // continuation: fp32 state in place, look-ahead rows
   size_t act_bytes() const { return act_f32 ? 4 : 2; }
   size_t w_bytes() const { return w_f32 ? 4 : 2; }
 };
 
 struct Layout {
   size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgp = 0, wup = 0,
-         blk = 0, vrow = 0, partial = 0, scale = 0;
+         blk = 0, vrow = 0, partial = 0, scale = 0, x0n = 0;
   size_t total = 0;
 };
 
@@ -115,6 +116,7 @@ Layout forward_layout(const Geo& g) {
   if (g.act_f32) {
     L.hb = take(g.B * g.T * g.d * 2);
     L.x0b = take(g.B * g.T * g.d * 2);
+    if (g.resume) L.x0n = take(g.B * (g.K - 1) * g.d * 2);  // bf16 look-ahead rows
   }
   L.wgp = take(tttk::wpack_elems(D) * 2);
   L.wup = take(tttk::wpack_elems(D) * 2);
@@ -363,14 +365,19 @@ ttt_status ttt_step_workspace_size(const ttt_desc* desc, size_t* bytes) {
 namespace {
 
 // Everything after the descriptor, chunk (or document) checks: pointer and
-// workspace checks, then the launches of the whole layer.
+// workspace checks, then the launches of the whole layer. For a continuation
+// (g.resume) W_down0 and W_down_final are the same fp32 [B, d, f] state,
+// read as the initial state and overwritten with the final one, and X0_next
+// holds n_next look-ahead rows per sequence.
 ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void* Wg,
                         const void* Wu, const void* W_down0, const void* conv_taps,
                         const void* W_target, float eta, void* O, float* W_down_final,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        const void* X0_next = nullptr, int n_next = 0) {
   if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
   TTT_TRY(check_ptr(H, "H"));
   TTT_TRY(check_ptr(X0, "X0"));
+  if (n_next > 0) TTT_TRY(check_ptr(X0_next, "X0_next"));
   TTT_TRY(check_ptr(Wg, "Wg"));
   TTT_TRY(check_ptr(Wu, "Wu"));
   TTT_TRY(check_ptr(W_down0, "W_down0"));
@@ -386,18 +393,25 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
   const size_t ab = g.act_bytes(), wb = g.w_bytes();
   const size_t w0_bytes =
       g.w0_stride == 0 ? g.d * g.f * wb : ((g.B - 1) * g.w0_stride + g.d * g.f) * wb;
-  const std::vector<Range> inputs = {
+  std::vector<Range> inputs = {
       range_of("H", H, g.B * g.T * g.d * ab),
       range_of("X0", X0, g.B * g.T * g.d * ab),
       range_of("Wg", Wg, g.f * g.d * wb),
       range_of("Wu", Wu, g.f * g.d * wb),
-      range_of("W_down0", W_down0, w0_bytes),
       range_of("conv_taps", conv_taps, g.K * g.d * wb),
       range_of("W_target", W_target, g.d * g.d * wb)};
-  const std::vector<Range> outputs = {range_of("O", O, g.B * g.T * g.d * ab),
-                                      range_of("W_down_final", W_down_final, g.B * g.d * g.f * 4),
-                                      range_of("workspace", workspace, L.total)};
+  // The continuation's state is both read and written, by the same tiles of
+  // the same kernels: it is an output here.
+  if (!g.resume) inputs.push_back(range_of("W_down0", W_down0, w0_bytes));
+  if (n_next > 0) inputs.push_back(range_of("X0_next", X0_next, g.B * n_next * g.d * ab));
+  const std::vector<Range> outputs = {
+      range_of("O", O, g.B * g.T * g.d * ab),
+      range_of(g.resume ? "W_state" : "W_down_final", W_down_final, g.B * g.d * g.f * 4),
+      range_of("workspace", workspace, L.total)};
   TTT_TRY(check_aliasing(inputs, outputs));
+  // Initial state: the caller's W_down0, or the continuation's fp32 state.
+  const bool w0_f32 = g.resume || g.w_f32;
+  const int64_t w0_stride = g.resume ? g.d * g.f : g.w0_stride;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const tttk::Dims& D = g.dims;
@@ -432,6 +446,7 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
   // bf16 operands
   const uint16_t* Hb = static_cast<const uint16_t*>(H);
   const uint16_t* X0b = static_cast<const uint16_t*>(X0);
+  const uint16_t* X0nb = static_cast<const uint16_t*>(X0_next);
   if (g.act_f32) {
     TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(H),
                                                       at<uint16_t>(workspace, L.hb), g.B * g.T * g.d, s));
@@ -439,6 +454,12 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
                                                       at<uint16_t>(workspace, L.x0b), g.B * g.T * g.d, s));
     Hb = at<uint16_t>(workspace, L.hb);
     X0b = at<uint16_t>(workspace, L.x0b);
+    if (n_next > 0) {
+      TTT_LAUNCH("cast_bf16", s,
+                 tttk::launch_cast_bf16(static_cast<const float*>(X0_next),
+                                        at<uint16_t>(workspace, L.x0n), g.B * n_next * g.d, s));
+      X0nb = at<uint16_t>(workspace, L.x0n);
+    }
   }
   uint16_t* Wgp = at<uint16_t>(workspace, L.wgp);
   uint16_t* Wup = at<uint16_t>(workspace, L.wup);
@@ -466,8 +487,8 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
   TTT_LAUNCH("transpose_w_target", s,
              tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, D.ld_y, s));
   TTT_LAUNCH("conv", s,
-             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, D, (int)g.K, (int)g.C, g.pad_chunk,
-                               blocks, s));
+             tttk::launch_conv(X0b, X0nb, n_next, conv_taps, g.w_f32, Y, D, (int)g.K, (int)g.C,
+                               g.pad_chunk, blocks, s));
   TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, s));
   const bool clip = g.clip > 0.0f && eta != 0.0f;
   uint16_t* Vrow = clip ? at<uint16_t>(workspace, L.vrow) : nullptr;
@@ -487,7 +508,7 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
     // Materialised exclusive prefix: snapshot i = bf16(W^(i)) for every chunk,
     // W_down_final = W^(k); then every chunk's output in one launch.
     TTT_LAUNCH("update_prefix", s,
-               tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale, snap,
+               tttk::launch_update(ZT, VT, W_down0, w0_f32, w0_stride, g.f, acc_scale, snap,
                                    g.nchunks * snap_cstride, W_down_final, nullptr, D, 0,
                                    (int)g.T, (int)g.C, blocks, (int)g.nchunks, s));
     TTT_LAUNCH("apply", s,
@@ -500,7 +521,7 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
     for (const Chunk& c : g.chunks) {
       if (c.doc_start)
         TTT_LAUNCH("update_running", s,
-                   tttk::launch_update(ZT, VT, W_down0, g.w_f32, g.w0_stride, g.f, acc_scale,
+                   tttk::launch_update(ZT, VT, W_down0, w0_f32, w0_stride, g.f, acc_scale,
                                        nullptr, 0, W_down_final, snap, D, 0, 0, (int)g.C,
                                        nullptr, 1, s));
       TTT_LAUNCH("apply", s,
@@ -582,6 +603,35 @@ ttt_status ttt_layer_forward_packed(const ttt_desc* desc, const void* H, const v
                       workspace, workspace_bytes, stream);
 }
 
+ttt_status ttt_continue_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  g.resume = true;
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = forward_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_forward_continue(const ttt_desc* desc, const void* H, const void* X0,
+                                      const void* X0_next, int32_t n_next, const void* Wg,
+                                      const void* Wu, float* W_state, const void* conv_taps,
+                                      const void* W_target, float eta, int32_t chunk, void* O,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  g.resume = true;
+  if (desc->w0_batch_stride != 0)
+    return fail(TTT_ERR_INVALID_ARG,
+                "w0_batch_stride must be 0: the continued state is [batch, d_model, d_ff]");
+  if (n_next < 0 || n_next > g.K - 1)
+    return fail(TTT_ERR_INVALID_ARG, "n_next must be in [0, conv_k - 1]");
+  TTT_TRY(check_ptr(W_state, "W_state"));
+  return forward_impl(g, H, X0, Wg, Wu, W_state, conv_taps, W_target, eta, O, W_state,
+                      workspace, workspace_bytes, stream, X0_next, n_next);
+}
+
 ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void* Wg,
                                 const void* Wu, void* Z, void* workspace, size_t workspace_bytes,
                                 void* stream) {
@@ -654,8 +704,8 @@ ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0, const void* conv_
              tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, g.dims.ld_y,
                                         s));
   TTT_LAUNCH("conv", s,
-             tttk::launch_conv(X0b, conv_taps, g.w_f32, Y, g.dims, (int)g.K, (int)g.C,
-                               g.pad_chunk, nullptr, s));
+             tttk::launch_conv(X0b, nullptr, 0, conv_taps, g.w_f32, Y, g.dims, (int)g.K,
+                               (int)g.C, g.pad_chunk, nullptr, s));
   TTT_LAUNCH("target", s,
              tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), nullptr, 1.0f,
                                  g.dims, s));

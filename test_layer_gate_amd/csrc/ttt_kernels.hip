@@ -1102,17 +1102,23 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const void* __restr
 // Depthwise conv, kConvRows consecutive tokens x 8 channels per thread: a
 // window of kConvRows X0 rows slides down one row per tap, so each row is
 // loaded once per thread instead of once per tap. Output t sums tap k over
-// k = 0, 1, ... in order while t + k is before its bound (the sequence, the
-// chunk or the document end).
+// k = 0, 1, ... in order while t + k is before its bound (the sequence end,
+// or the end of the n_next look-ahead rows that follow it; the chunk end; the
+// document end). Row r of the sequence is X0 row r for r < T and look-ahead
+// row r - T of Xn after that.
 constexpr int kConvRows = 8;
 static_assert(kTokenPad % kConvRows == 0, "row windows tile the padded sequence");
 
-__device__ __forceinline__ uint4 load_row8(const u16* X0, int64_t row_off, bool ok) {
-  return ok ? *reinterpret_cast<const uint4*>(X0 + row_off) : make_uint4(0u, 0u, 0u, 0u);
+__device__ __forceinline__ uint4 load_row8(const u16* X0, const u16* Xn, int r, int T,
+                                           int n_next, int d) {
+  if (r < T) return *reinterpret_cast<const uint4*>(X0 + (int64_t)r * d);
+  if (r < T + n_next) return *reinterpret_cast<const uint4*>(Xn + (int64_t)(r - T) * d);
+  return make_uint4(0u, 0u, 0u, 0u);
 }
 
 template <bool TAPS_F32>
 __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ X0,
+                                                        const u16* __restrict__ X0n, int n_next,
                                                         const void* __restrict__ taps,
                                                         u16* __restrict__ Y, Dims g, int K,
                                                         int chunk, int pad_chunk,
@@ -1130,6 +1136,7 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
   const int t = (int)(bt % groups) * kConvRows;
   const int b = (int)(bt / groups);
   const u16* xb = X0 + (int64_t)b * T * d + c;
+  const u16* xn = X0n + (int64_t)b * n_next * d + c;  // not read when n_next == 0
   int end[kConvRows];
   int last = 0;
 #pragma unroll
@@ -1137,13 +1144,14 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
     const int tr = t + r;
     end[r] = blocks != nullptr
                  ? min(T, pad_chunk ? blocks[tr >> 6].chunk_end : blocks[tr >> 6].doc_end)
-                 : (pad_chunk ? min(T, (tr / chunk + 1) * chunk) : T);
+                 : (pad_chunk ? min(T, (tr / chunk + 1) * chunk) : T + n_next);
+    if (tr >= T) end[r] = 0;  // padding rows of Y stay zero
     last = max(last, end[r]);
   }
   float acc[kConvRows][8] = {};
   uint4 win[kConvRows];
 #pragma unroll
-  for (int r = 0; r < kConvRows; ++r) win[r] = load_row8(xb, (int64_t)(t + r) * d, t + r < T);
+  for (int r = 0; r < kConvRows; ++r) win[r] = load_row8(xb, xn, t + r, T, n_next, d);
   for (int k = 0; k < K && t + k < last; ++k) {
     float tp[8];
     if constexpr (TAPS_F32) {
@@ -1176,8 +1184,7 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
     }
 #pragma unroll
     for (int r = 0; r + 1 < kConvRows; ++r) win[r] = win[r + 1];
-    const int nr = t + kConvRows + k;
-    win[kConvRows - 1] = load_row8(xb, (int64_t)nr * d, nr < T);
+    win[kConvRows - 1] = load_row8(xb, xn, t + kConvRows + k, T, n_next, d);
   }
 #pragma unroll
   for (int r = 0; r < kConvRows; ++r)
@@ -1254,17 +1261,18 @@ hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, in
   return hipGetLastError();
 }
 
-hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint16_t* Y,
-                       const Dims& g, int K, int chunk, bool pad_chunk,
-                       const BlockInfo* blocks, hipStream_t s) {
+hipError_t launch_conv(const uint16_t* X0, const uint16_t* X0_next, int n_next,
+                       const void* taps, bool taps_f32, uint16_t* Y, const Dims& g, int K,
+                       int chunk, bool pad_chunk, const BlockInfo* blocks, hipStream_t s) {
   const int64_t total = (int64_t)g.B * (g.T_pad / kConvRows) * (g.d / 8);
   const int grid = ceil_div(total, kThreads);
+  if (n_next == 0) X0_next = X0;  // never read
   if (taps_f32)
-    conv_kernel<true><<<grid, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
-                                                blocks, total);
+    conv_kernel<true><<<grid, kThreads, 0, s>>>(X0, X0_next, n_next, taps, Y, g, K, chunk,
+                                                pad_chunk ? 1 : 0, blocks, total);
   else
-    conv_kernel<false><<<grid, kThreads, 0, s>>>(X0, taps, Y, g, K, chunk, pad_chunk ? 1 : 0,
-                                                 blocks, total);
+    conv_kernel<false><<<grid, kThreads, 0, s>>>(X0, X0_next, n_next, taps, Y, g, K, chunk,
+                                                 pad_chunk ? 1 : 0, blocks, total);
   return hipGetLastError();
 }
 

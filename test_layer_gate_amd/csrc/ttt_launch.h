@@ -117,12 +117,14 @@ hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, in
                                 int cols, int64_t ld_dst, hipStream_t s);
 
 // Y[b][t][c] = fp16(sum_k taps[k][c] * X0[b][t + k][c]) over reads inside the
-// sequence (or inside t's chunk when pad_chunk), for t < T_pad. With blocks
-// (packed documents, B = 1) the reads stop at t's document end (or chunk
+// sequence (or inside t's chunk when pad_chunk), for t < T_pad. The sequence
+// may continue past T with n_next look-ahead rows, X0_next [B][n_next][d],
+// which the reads of the sequence-padded conv reach. With blocks (packed
+// documents, B = 1, n_next = 0) the reads stop at t's document end (or chunk
 // end) instead.
-hipError_t launch_conv(const uint16_t* X0, const void* taps, bool taps_f32, uint16_t* Y,
-                       const Dims& g, int K, int chunk, bool pad_chunk,
-                       const BlockInfo* blocks, hipStream_t s);
+hipError_t launch_conv(const uint16_t* X0, const uint16_t* X0_next, int n_next,
+                       const void* taps, bool taps_f32, uint16_t* Y, const Dims& g, int K,
+                       int chunk, bool pad_chunk, const BlockInfo* blocks, hipStream_t s);
 
 // dst = W ([f][d], bf16 or fp32, rounded to bf16) in the packed Wgp layout.
 hipError_t launch_pack_weight(const void* W, bool w_f32, uint16_t* dst, const Dims& g,

@@ -273,3 +273,60 @@ def test_clipped_forward_validates_before_launch(L):
                                      1024, ctypes.c_float(1.0), p[7], p[8], p[9],
                                      ctypes.c_size_t(need - 1), None)
     assert st == WORKSPACE
+
+
+# ---- continuation ------------------------------------------------------------
+
+def continue_ws(L, desc, chunk):
+    n = ctypes.c_size_t(0)
+    st = L.ttt_continue_workspace_size(ctypes.byref(desc), chunk, ctypes.byref(n))
+    return st, n.value
+
+
+def test_continue_workspace_size(L):
+    st, n = continue_ws(L, qwen_desc(), 1024)
+    assert st == OK
+    _, plain = ws_size(L, qwen_desc(), 1024)
+    assert n == plain                       # bf16 look-ahead rows are read in place
+    f32 = dict(act_dtype=bnd.TTT_F32, seq_len=4096)
+    st, n = continue_ws(L, qwen_desc(**f32), 1024)
+    _, plain = ws_size(L, qwen_desc(**f32), 1024)
+    extra = 3 * 2560 * 2                    # K - 1 rows cast to bf16
+    assert st == OK and plain + extra <= n <= plain + extra + 256
+
+
+def continue_fwd(L, desc, p, x0n, n_next, ws_bytes=1 << 62, eta=1e-3):
+    # H, X0, X0_next, n_next, Wg, Wu, W_state, taps, W_target, eta, chunk, O, ws
+    return L.ttt_layer_forward_continue(ctypes.byref(desc), p[0], p[1], x0n, n_next, p[2],
+                                        p[3], p[4], p[5], p[6], ctypes.c_float(eta), 1024,
+                                        p[7], p[9], ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("n_next,code", [(-1, INVALID), (4, INVALID), (64, INVALID)])
+def test_continue_rejects_lookahead_count(L, n_next, code):
+    p = good_ptrs()
+    assert continue_fwd(L, qwen_desc(), p, p[8], n_next) == code
+
+
+def test_continue_validates_before_launch(L):
+    p = good_ptrs()
+    # X0_next is required when rows are promised, not when n_next is 0
+    assert continue_fwd(L, qwen_desc(), p, None, 3) == INVALID
+    # the state layout is fixed: no W_down0 stride
+    assert continue_fwd(L, qwen_desc(w0_batch_stride=2560 * 9728), p, p[8], 3) == INVALID
+    # NULL / misaligned state
+    q = list(p)
+    q[4] = None
+    assert continue_fwd(L, qwen_desc(), q, p[8], 3) == INVALID
+    q[4] = ctypes.c_void_p(p[4].value + 4)
+    assert continue_fwd(L, qwen_desc(), q, p[8], 3) == INVALID
+    # the in-place state may not overlap an input or the other outputs
+    q = list(p)
+    q[4] = p[1]
+    assert continue_fwd(L, qwen_desc(), q, p[8], 3) == ALIAS
+    assert continue_fwd(L, qwen_desc(), p, p[4], 3) == ALIAS     # X0_next is the state
+    assert continue_fwd(L, qwen_desc(), p, p[7], 3) == ALIAS     # X0_next is O
+    assert continue_fwd(L, qwen_desc(), p, p[8], 3, eta=float("nan")) == INVALID
+    _, need = continue_ws(L, qwen_desc(), 1024)
+    assert continue_fwd(L, qwen_desc(), p, p[8], 3, ws_bytes=need - 1) == WORKSPACE
+    assert continue_fwd(L, qwen_desc(), p, None, 0, ws_bytes=need - 1) == WORKSPACE
