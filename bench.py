@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule prefix|running] [--no-cpu-baseline]
+                    [--variant plain|packed|clipped|continue]
     python bench.py --summarize DIR [--fetch DIR2 --write DIR3]
                     --summary-out FILE.md --command "..."
 
@@ -11,6 +12,11 @@ text summaries kept under profiles/.
 
 One step is one call of ttt_layer_forward on the whole workload (gate/up,
 target, update with per-chunk snapshots, apply), with inputs resident in HBM.
+--variant times the other entry points on the same workload instead: packed
+(ttt_layer_forward_packed, the sequence cut into --docs equal documents),
+clipped (ttt_layer_forward_clipped, limit --clip) or continue
+(ttt_layer_forward_continue: an fp32 state updated in place and K - 1
+look-ahead rows).
 Prints one JSON line: tokens/s for the step, the per-kernel device times
 (HIP events recorded by the library around each launch, on the stream it
 launches on), the roofline of the dominant kernel, and the CPU oracle timed
@@ -87,9 +93,12 @@ def measured_traffic(kernel, workload):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, x, budget_s=15.0):
+def cpu_baseline(cfg, x, budget_s=15.0, variant="plain", clip=None, doc_len=None):
     """The float64 oracle on the first j chunks of the workload (plus the
-    conv's K-1 look-ahead rows), j chosen so the sample takes ~budget_s."""
+    conv's K-1 look-ahead rows), j chosen so the sample takes ~budget_s.
+    For the packed variant the sample is the first j chunks' worth of whole
+    documents, run through the packed oracle; for the clipped one the oracle
+    clips; a continued segment is the plain recurrence from a given state."""
     import oracle.ttt_oracle as ora
     try:
         from threadpoolctl import threadpool_info
@@ -101,8 +110,15 @@ def cpu_baseline(cfg, x, budget_s=15.0):
     def run(j):
         n = j * C
         t0 = time.perf_counter()
-        ora.ttt_prefill(x["H"][:1, :n], x["X0"][:1, :n + K - 1], x["Wg"], x["Wu"],
-                        x["W_down0"], x["taps"], x["W_target"], cfg.eta, C)
+        if variant == "packed":
+            n = max(doc_len, n // doc_len * doc_len)
+            ora.ttt_prefill_packed(x["H"][0, :n], x["X0"][0, :n], x["Wg"], x["Wu"],
+                                   x["W_down0"], x["taps"], x["W_target"], cfg.eta, C,
+                                   list(range(0, n, doc_len)))
+        else:
+            ora.ttt_prefill(x["H"][:1, :n], x["X0"][:1, :n + K - 1], x["Wg"], x["Wu"],
+                            x["W_down0"], x["taps"], x["W_target"], cfg.eta, C,
+                            clip=clip if variant == "clipped" else None)
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -206,6 +222,9 @@ def main():
     ap.add_argument("--workload", default=synth.BENCH_CONFIG, choices=sorted(synth.CONFIGS))
     ap.add_argument("--schedule", default="prefix", choices=["prefix", "running"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", default="plain", choices=["plain", "packed", "clipped", "continue"])
+    ap.add_argument("--docs", type=int, default=64, help="packed variant: equal documents")
+    ap.add_argument("--clip", type=float, default=1e-3, help="clipped variant: norm limit")
     ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory")
@@ -242,12 +261,39 @@ def main():
     desc = ttt.make_desc(B, T, d, f, cfg.conv_k, 0 if cfg.dtype == "bf16" else 1,
                          0 if cfg.dtype == "bf16" else 1, 0,
                          2 if args.schedule == "running" else 4)
-    ws = torch.empty(ttt.workspace_size(desc, cfg.chunk), dtype=torch.uint8, device=dev)
+    doc_len = None
+    if args.variant == "packed":
+        if B != 1 or T % args.docs or (T // args.docs) % 64:
+            raise SystemExit("--variant packed needs batch 1 and documents of a multiple of 64 tokens")
+        doc_len = T // args.docs
+        starts = list(range(0, T, doc_len))
+        ws_bytes = ttt.packed_workspace_size(desc, cfg.chunk, starts)
+    elif args.variant == "clipped":
+        ws_bytes = ttt.clipped_workspace_size(desc, cfg.chunk, args.clip)
+    elif args.variant == "continue":
+        ws_bytes = ttt.continue_workspace_size(desc, cfg.chunk)
+        # the segment continues a document: its state is fp32 and K - 1 rows follow it
+        W_state = t["W_down0"].float().expand(B, d, f).contiguous()
+        X0_next = t["X0"][:, :cfg.conv_k - 1].contiguous()
+    else:
+        ws_bytes = ttt.workspace_size(desc, cfg.chunk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step():
-        ttt.layer_forward(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
-                          t["W_target"], cfg.eta, cfg.chunk, schedule=args.schedule,
-                          out=O, W_down_final=Wf, workspace=ws)
+        if args.variant == "packed":
+            ttt.layer_forward_packed(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
+                                     t["W_target"], cfg.eta, cfg.chunk, starts,
+                                     schedule=args.schedule, out=O, W_down_final=Wf,
+                                     workspace=ws)
+        elif args.variant == "continue":
+            ttt.layer_forward_continue(t["H"], t["X0"], X0_next, t["Wg"], t["Wu"], W_state,
+                                       t["taps"], t["W_target"], cfg.eta, cfg.chunk,
+                                       schedule=args.schedule, out=O, workspace=ws)
+        else:
+            ttt.layer_forward(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
+                              t["W_target"], cfg.eta, cfg.chunk, schedule=args.schedule,
+                              clip=args.clip if args.variant == "clipped" else None,
+                              out=O, W_down_final=Wf, workspace=ws)
 
     # A plain copy of known size, outside the timed region: the reference that
     # converts hardware traffic counters to bytes in profiled runs.
@@ -308,7 +354,7 @@ def main():
         "dtype": "bf16+fp16", "data": "synthetic",
         "config": {"workload": cfg.name, "batch": B, "seq_len": T, "chunk": cfg.chunk,
                    "d_model": d, "d_ff": f, "conv_k": cfg.conv_k, "eta": cfg.eta,
-                   "schedule": args.schedule},
+                   "schedule": args.schedule, "variant": args.variant},
         "layer_tflops": round(tflops, 1),
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
@@ -317,7 +363,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(cfg, x)
+        line["cpu_baseline"] = cpu_baseline(cfg, x, variant=args.variant, clip=args.clip,
+                                            doc_len=doc_len)
     print(json.dumps(line), flush=True)
 
 

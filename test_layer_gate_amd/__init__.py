@@ -11,6 +11,7 @@ built, or a call fails, an exception is raised.
 from ._binding import (  # noqa: F401
     LIB_PATH,
     TTTError,
+    clipped_workspace_size,
     continue_workspace_size,
     copy_calibration,
     gated_activation,
@@ -27,7 +28,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["layer_forward", "layer_forward_packed", "packed_workspace_size",
-           "layer_forward_continue", "continue_workspace_size",
+           "layer_forward_continue", "continue_workspace_size", "clipped_workspace_size",
            "gated_activation", "lm_target", "workspace_size",
            "copy_calibration",
            "make_desc", "profile_enable", "profile_read", "TTTError", "lib",

@@ -155,6 +155,13 @@ def workspace_size(desc: Desc, chunk: int) -> int:
     return n.value
 
 
+def clipped_workspace_size(desc: Desc, chunk: int, clip: float) -> int:
+    n = _S(0)
+    _check(lib().ttt_clipped_workspace_size(ctypes.byref(desc), int(chunk),
+                                            ctypes.c_float(float(clip)), ctypes.byref(n)))
+    return n.value
+
+
 def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
                   schedule=None, pad="sequence", clip=None, out=None, W_down_final=None,
                   workspace=None, stream=None):
@@ -193,10 +200,7 @@ def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
     if clip is None:
         ws_bytes = workspace_size(desc, int(chunk))
     else:
-        n = _S(0)
-        _check(lib().ttt_clipped_workspace_size(ctypes.byref(desc), int(chunk),
-                                                ctypes.c_float(float(clip)), ctypes.byref(n)))
-        ws_bytes = n.value
+        ws_bytes = clipped_workspace_size(desc, int(chunk), clip)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
     O = torch.empty_like(H) if out is None else out
