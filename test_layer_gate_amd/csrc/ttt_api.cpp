@@ -91,7 +91,7 @@ struct Geo {
 
 struct Layout {
   size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgp = 0, wup = 0,
-         blk = 0, vrow = 0, partial = 0, scale = 0, x0n = 0;
+         blk = 0, vrow = 0, gram = 0, partial = 0, scale = 0, x0n = 0;
   size_t total = 0;
 };
 
@@ -125,6 +125,7 @@ Layout forward_layout(const Geo& g) {
                  g.tiles.size() * sizeof(tttk::ApplyTile));
   if (g.clip > 0.0f) {
     L.vrow = take(g.B * g.T_pad * D.ld_y * 2);
+    L.gram = take(g.B * g.nchunks * tttk::clip_gram_floats((int)g.C) * 4);
     L.partial = take(g.B * g.nchunks * tttk::clip_pairs((int)g.C) * 4);
     L.scale = take(g.B * g.nchunks * 4);
   }
@@ -498,7 +499,8 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
     // most g.clip by scaling its columns of VT; the norm comes from the rows
     // of vscale * V, hence the factor |eta| / vscale.
     TTT_LAUNCH("clip_scale", s,
-               tttk::launch_clip_scale(Z, Vrow, at<float>(workspace, L.partial),
+               tttk::launch_clip_scale(Z, Vrow, at<float>(workspace, L.gram),
+                                       at<float>(workspace, L.partial),
                                        at<float>(workspace, L.scale), VT, D, (int)g.C,
                                        (int)g.nchunks, std::fabs(eta) / vscale, g.clip, s));
   }

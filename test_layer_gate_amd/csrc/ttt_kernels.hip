@@ -766,50 +766,111 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 // For clipping each chunk's update eta V_i^T Z_i to a Frobenius norm
 // ([iplex] §6), the norm comes from two C x C Gram matrices instead of the
 // d x f delta: ||V_i^T Z_i||_F^2 = sum_{s,t in chunk i} (V_s . V_t)(Z_s . Z_t).
-// One workgroup per pair (sb <= tb) of 128-token blocks of a chunk computes
-// the Z Gram tile (K = d_ff, bf16) and the V Gram tile (K = d_model, fp16,
-// on vscale * V) with the GEMM core, and writes the sum of their elementwise
-// product (twice for sb < tb) to partial[b][chunk][pair].
-constexpr int KG_B = 128, KG_WGM = 2;
+// Both Grams are symmetric, so only the tiles of pairs (sb <= tb) of
+// 256-token blocks of a chunk are formed, and an off-diagonal tile counts
+// twice. Two passes over the same tiles: the first forms the V Gram tile
+// (K = d_model, fp16, on vscale * V) and keeps it in the gram buffer, each
+// lane its own accumulator registers; the second forms the Z Gram tile
+// (K = d_ff, bf16) in KG_SPLIT parts of d_ff and writes the sum of its
+// elementwise product with the kept V tile to partial[b][chunk][pair][part]
+// (the sum is linear in the Z Gram, so the parts add up).
+constexpr int KG_B = 256, KG_WGM = 2, KG_SPLIT = 2;
 
-__global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
-    const u16* __restrict__ Z, const u16* __restrict__ Vrow, float* __restrict__ partial,
-    Dims g, int chunk, int nblk, int npair, int nchunks) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  using L = Layout<KG_B, KG_B, KG_WGM>;
-  TTT_GEMM_LDS(lds, KG_B, KG_B, 64, 2)
-  __shared__ float wsum[kGemmWaves];
-  const int pair = blockIdx.x % npair, rest = blockIdx.x / npair;
-  const int i = rest % nchunks, b = rest / nchunks;
-  int sb = 0, tb = pair;  // pair -> (sb, tb), sb <= tb, upper triangle row by row
+struct GramTile {
+  int b, i, pair, part, s0, u0, c1, weight;
+};
+
+__device__ __forceinline__ GramTile gram_tile(const Dims& g, int chunk, int nblk, int npair,
+                                              int nchunks, int parts) {
+  GramTile t;
+  int rest = blockIdx.x;
+  t.part = rest % parts;
+  rest /= parts;
+  t.pair = rest % npair;
+  rest /= npair;
+  t.i = rest % nchunks;
+  t.b = rest / nchunks;
+  int sb = 0, tb = t.pair;  // pair -> (sb, tb), sb <= tb, upper triangle row by row
   while (tb >= nblk - sb) {
     tb -= nblk - sb;
     ++sb;
   }
   tb += sb;
-  const int c0 = i * chunk, c1 = min(g.T, c0 + chunk);
-  const int s0 = c0 + sb * KG_B, u0 = c0 + tb * KG_B;
+  const int c0 = t.i * chunk;
+  t.c1 = min(g.T, c0 + chunk);
+  t.s0 = c0 + sb * KG_B;
+  t.u0 = c0 + tb * KG_B;
+  t.weight = sb == tb ? 1 : 2;
+  return t;
+}
+
+// One Gram tile X[s0..] X[u0..]^T over K columns [k0, k0 + nk * 64) of the
+// row-major X (row stride ld, rows_b rows per sequence), rows at or past c1
+// reading as zero.
+template <class Op>
+__device__ __forceinline__ void gram_tile_acc(const u16* X, int64_t ld, int64_t rows_b,
+                                              const GramTile& t, int k0, int nk, f32x16* acc,
+                                              u16* lds) {
+  const Operand xs = row_major<64>(X + ((int64_t)t.b * rows_b + t.s0) * ld + k0, ld, t.c1 - t.s0);
+  const Operand xu = row_major<64>(X + ((int64_t)t.b * rows_b + t.u0) * ld + k0, ld, t.c1 - t.u0);
+  gemm_core<KG_B, KG_B, KG_WGM, 64, 2, Op, false, kRowMajor, kRowMajor>(xs, xu, xu, nk, acc, lds,
+                                                                       NoHook{});
+}
+
+__global__ __launch_bounds__(kGemmThreads) void gram_v_kernel(const u16* __restrict__ Vrow,
+                                                              float* __restrict__ gram, Dims g,
+                                                              int chunk, int nblk, int npair,
+                                                              int nchunks) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using L = Layout<KG_B, KG_B, KG_WGM>;
+  constexpr int NR = L::TM * L::TN * 16;  // accumulator registers per lane
+  TTT_GEMM_LDS(lds, KG_B, KG_B, 64, 2)
+  const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, 1);
+  if (t.u0 >= t.c1) return;  // uniform: blocks past a short last chunk add nothing
+  f32x16 acc[L::TM][L::TN];
+  zero_acc(acc);
+  gram_tile_acc<F16Mma>(Vrow, g.ld_y, g.T_pad, t, 0, g.d / 64, &acc[0][0], lds);
+  // Lane-private layout [tile][register][thread]: each register's stores are
+  // 256 contiguous bytes per wave; the second pass reads them in the same
+  // lanes.
+  float* dst = gram + (((int64_t)t.b * nchunks + t.i) * npair + t.pair) * NR * kGemmThreads +
+               threadIdx.x;
+#pragma unroll
+  for (int m = 0; m < L::TM; ++m)
+#pragma unroll
+    for (int n = 0; n < L::TN; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        dst[((m * L::TN + n) * 16 + r) * kGemmThreads] = acc[m][n][r];
+#endif
+}
+
+__global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
+    const u16* __restrict__ Z, const float* __restrict__ gram, float* __restrict__ partial,
+    Dims g, int chunk, int nblk, int npair, int nchunks) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using L = Layout<KG_B, KG_B, KG_WGM>;
+  constexpr int NR = L::TM * L::TN * 16;
+  TTT_GEMM_LDS(lds, KG_B, KG_B, 64, 2)
+  __shared__ float wsum[kGemmWaves];
+  const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, KG_SPLIT);
+  const int steps = g.f / 64, per = (steps + KG_SPLIT - 1) / KG_SPLIT;
+  const int k_first = t.part * per, nk = min(steps, k_first + per) - k_first;
   float sum = 0.f;
-  if (u0 < c1) {  // uniform: blocks past a short last chunk add nothing
-    f32x16 az[L::TM][L::TN], av[L::TM][L::TN];
-    zero_acc(az);
-    zero_acc(av);
-    const Operand zs = row_major<64>(Z + ((int64_t)b * g.T + s0) * g.ld_z, g.ld_z, c1 - s0);
-    const Operand zu = row_major<64>(Z + ((int64_t)b * g.T + u0) * g.ld_z, g.ld_z, c1 - u0);
-    gemm_core<KG_B, KG_B, KG_WGM, 64, 2, Bf16Mma, false, kRowMajor, kRowMajor>(
-        zs, zu, zu, g.f / 64, &az[0][0], lds, NoHook{});
-    const Operand vs =
-        row_major<64>(Vrow + ((int64_t)b * g.T_pad + s0) * g.ld_y, g.ld_y, c1 - s0);
-    const Operand vu =
-        row_major<64>(Vrow + ((int64_t)b * g.T_pad + u0) * g.ld_y, g.ld_y, c1 - u0);
-    gemm_core<KG_B, KG_B, KG_WGM, 64, 2, F16Mma, false, kRowMajor, kRowMajor>(
-        vs, vu, vu, g.d / 64, &av[0][0], lds, NoHook{});
+  if (t.u0 < t.c1 && nk > 0) {  // uniform
+    f32x16 acc[L::TM][L::TN];
+    zero_acc(acc);
+    gram_tile_acc<Bf16Mma>(Z, g.ld_z, g.T, t, k_first * 64, nk, &acc[0][0], lds);
+    const float* src = gram +
+                       (((int64_t)t.b * nchunks + t.i) * npair + t.pair) * NR * kGemmThreads +
+                       threadIdx.x;
 #pragma unroll
     for (int m = 0; m < L::TM; ++m)
 #pragma unroll
       for (int n = 0; n < L::TN; ++n)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum = fmaf(az[m][n][r], av[m][n][r], sum);
+        for (int r = 0; r < 16; ++r)
+          sum = fmaf(acc[m][n][r], src[((m * L::TN + n) * 16 + r) * kGemmThreads], sum);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
@@ -819,13 +880,15 @@ __global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < kGemmWaves; ++w) tot += wsum[w];
-    partial[((int64_t)b * nchunks + i) * npair + pair] = (sb == tb ? 1.f : 2.f) * tot;
+    partial[(((int64_t)t.b * nchunks + t.i) * npair + t.pair) * KG_SPLIT + t.part] =
+        (float)t.weight * tot;
   }
 #endif
 }
 
 // scale[b][i] = min(1, clip / ||eta V_i^T Z_i||_F), the norm being
-// norm_factor * sqrt(sum of chunk i's partials), summed in a fixed order.
+// norm_factor * sqrt(sum of chunk i's npair partials), summed in a fixed
+// order.
 __global__ __launch_bounds__(kThreads) void clip_scale_kernel(const float* __restrict__ partial,
                                                              float* __restrict__ scale, int npair,
                                                              int n, float norm_factor,
@@ -1371,20 +1434,30 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
 
 int clip_pairs(int chunk) {
   const int nblk = ceil_div(chunk, KG_B);
-  return nblk * (nblk + 1) / 2;
+  return nblk * (nblk + 1) / 2 * KG_SPLIT;
 }
 
-hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* partial,
-                             float* scale, uint16_t* VT, const Dims& g, int chunk, int nchunks,
-                             float norm_factor, float clip, hipStream_t s) {
-  const int nblk = ceil_div(chunk, KG_B), npair = clip_pairs(chunk);
-  gram_norm_kernel<<<g.B * nchunks * npair, kGemmThreads, 0, s>>>(Z, Vrow, partial, g, chunk,
-                                                                 nblk, npair, nchunks);
+int64_t clip_gram_floats(int chunk) {
+  const int nblk = ceil_div(chunk, KG_B);
+  return (int64_t)(nblk * (nblk + 1) / 2) * KG_B * KG_B;
+}
+
+hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gram,
+                             float* partial, float* scale, uint16_t* VT, const Dims& g,
+                             int chunk, int nchunks, float norm_factor, float clip,
+                             hipStream_t s) {
+  const int nblk = ceil_div(chunk, KG_B), npair = nblk * (nblk + 1) / 2;
+  gram_v_kernel<<<g.B * nchunks * npair, kGemmThreads, 0, s>>>(Vrow, gram, g, chunk, nblk, npair,
+                                                               nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  gram_norm_kernel<<<g.B * nchunks * npair * KG_SPLIT, kGemmThreads, 0, s>>>(
+      Z, gram, partial, g, chunk, nblk, npair, nchunks);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int n = g.B * nchunks;
-  clip_scale_kernel<<<ceil_div(n, kThreads), kThreads, 0, s>>>(partial, scale, npair, n,
-                                                               norm_factor, clip);
+  clip_scale_kernel<<<ceil_div(n, kThreads), kThreads, 0, s>>>(partial, scale, clip_pairs(chunk),
+                                                               n, norm_factor, clip);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n16 = vt_elems(g) / 8;

@@ -143,12 +143,15 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
 
 // Update-norm clipping: per chunk i of `chunk` tokens (uniform chunks),
 // scale[b][i] = min(1, clip / (norm_factor * ||Vrow_i^T Z_i||_F)) from the
-// Gram form (partial: B * nchunks * clip_pairs(chunk) floats), then VT *=
-// the scale of each token's chunk.
+// Gram form (gram: B * nchunks * clip_gram_floats(chunk) floats of V Gram
+// tiles; partial: B * nchunks * clip_pairs(chunk) floats), then VT *= the
+// scale of each token's chunk.
 int clip_pairs(int chunk);
-hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* partial,
-                             float* scale, uint16_t* VT, const Dims& g, int chunk, int nchunks,
-                             float norm_factor, float clip, hipStream_t s);
+int64_t clip_gram_floats(int chunk);
+hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gram,
+                             float* partial, float* scale, uint16_t* VT, const Dims& g,
+                             int chunk, int nchunks, float norm_factor, float clip,
+                             hipStream_t s);
 
 // Fast-weight update over tokens [tok_begin, tok_begin + tok_count) (a
 // multiple of 64), in 64-token steps (columns past T read as zero). acc =

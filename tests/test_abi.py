@@ -257,9 +257,10 @@ def test_clipped_workspace_size(L):
     _, plain = ws_size(L, qwen_desc(), 1024)
     T, d, k = 65536, 2560, 64
     ld_y = d + 64 if (d // 64) % 2 == 0 else d
-    pairs = 8 * 9 // 2                              # 128-token blocks of a 1024-token chunk
-    extra = T * ld_y * 2 + k * pairs * 4 + k * 4    # token-major V, Gram partials, scales
-    assert plain + extra <= n <= plain + extra + 4 * 256
+    pairs = 4 * 5 // 2                              # 256-token blocks of a 1024-token chunk
+    # token-major V, the V Gram tiles, Gram partials (two parts of d_ff), scales
+    extra = T * ld_y * 2 + k * pairs * 256 * 256 * 4 + k * pairs * 2 * 4 + k * 4
+    assert plain + extra <= n <= plain + extra + 5 * 256
 
 
 def test_clipped_forward_validates_before_launch(L):
