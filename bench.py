@@ -223,7 +223,7 @@ def main():
     ap.add_argument("--schedule", default="prefix", choices=["prefix", "running"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", default="plain", choices=["plain", "packed", "clipped", "continue"])
-    ap.add_argument("--docs", type=int, default=64, help="packed variant: equal documents")
+    ap.add_argument("--docs", type=int, default=32, help="packed variant: equal documents")
     ap.add_argument("--clip", type=float, default=1e-3, help="clipped variant: norm limit")
     ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")

@@ -141,3 +141,41 @@ def test_packed_full_size_sampled(ttt):
     ew, edw = rel(W_s, W_ref), rel(W_s - W0s, W_ref - W0s)
     print(f"final state after the last document: W {ew:.2e} dW {edw:.2e}", flush=True)
     assert ew <= W_TOL and edw <= DW_TOL
+
+
+@pytest.mark.timeout(900)
+def test_packed_full_size_equal_documents_sampled(ttt):
+    """Qwen3-4B shape at 64k tokens as 32 documents of 2048 tokens (two
+    chunks each), the layout bench.py --variant packed times. Checked on
+    whole documents the oracle runs alone (the first, one in the middle and
+    the last: each second chunk sees its own first chunk's update and nothing
+    of the document before) and on sampled entries of the final state (the
+    last document's update on top of W_down0)."""
+    cfg = synth.CONFIGS["qwen3_4b_64k"]
+    x = synth.make_inputs(cfg)
+    C, eta, L = cfg.chunk, cfg.eta, 2048
+    starts = list(range(0, cfg.seq_len, L))
+    t = to_dev(x, cfg.dtype)
+    O, Wf = run_packed_gpu(ttt, t, eta, C, starts)
+    del t
+    torch.cuda.empty_cache()
+    one = {k: x[k] for k in ("Wg", "Wu", "W_down0", "taps", "W_target")}
+    for a in (0, 13 * L, starts[-1]):
+        O_ref, _ = ora.ttt_prefill(x["H"][:, a:a + L], x["X0"][:, a:a + L], one["Wg"],
+                                   one["Wu"], one["W_down0"], one["taps"], one["W_target"],
+                                   eta, C)
+        eo = rel(O[a:a + L], O_ref[0])
+        e2 = rel(O[a + C:a + L], O_ref[0, C:])
+        print(f"document [{a}, {a + L}): O {eo:.2e}, second chunk {e2:.2e}", flush=True)
+        assert eo <= O_TOL and e2 <= O_TOL
+    rng = np.random.default_rng(98)
+    cs = np.unique(np.concatenate([[0, cfg.d_model - 1], rng.integers(0, cfg.d_model, 14)]))
+    js = np.unique(np.concatenate([[0, cfg.d_ff - 1], rng.integers(0, cfg.d_ff, 14)]))
+    a = starts[-1]
+    W_ref = ora.final_state_entries(x["H"][0, a:], x["X0"][0, a:], one["Wg"], one["Wu"],
+                                    one["W_down0"], one["taps"], one["W_target"], eta, cs, js)
+    W0s = x["W_down0"][np.ix_(cs, js)].astype(np.float64)
+    W_s = Wf[np.ix_(cs, js)]
+    ew, edw = rel(W_s, W_ref), rel(W_s - W0s, W_ref - W0s)
+    print(f"final state after the last document: W {ew:.2e} dW {edw:.2e}", flush=True)
+    assert ew <= W_TOL and edw <= DW_TOL
