@@ -5,12 +5,13 @@
 //   C[M][N] = sum_k A[m][k] * B[n][k],  both operands K-contiguous in HBM.
 // A workgroup is 8 wave64s (two per SIMD) in a WGM x WGN grid; each wave
 // owns a block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}, fp32
-// accumulation). K advances BK elements (32 or 64) per step through NST LDS
-// stages: buffer_load ... lds moves each 16-byte chunk from HBM straight
-// into LDS (no VGPR staging), bounds-checked by the buffer descriptor (rows
-// past the tile's valid rows read as zero), while the MFMAs run on a stage
-// that has landed; NST - 1 stages are in flight at once. Fragments are read
-// with ds_read_b128 one K-substep ahead of the MFMAs that use them.
+// accumulation). K advances BK elements (32 or 64) per step through LDS
+// stages, NSTA of the A tile and NSTB of the B tile: buffer_load ... lds
+// moves each 16-byte chunk from HBM straight into LDS (no VGPR staging),
+// bounds-checked by the buffer descriptor (rows past the tile's valid rows
+// read as zero), while the MFMAs run on a stage that has landed; each
+// operand has all but one of its stages in flight. Fragments are read with
+// ds_read_b128 one K-substep ahead of the MFMAs that use them.
 //
 // Method sources: "论文精读：In-Place Test-Time Training" reading notes —
 // "In-Place 设计" (gated MLP), "Chunk-Wise 更新机制" (update equation),
@@ -37,7 +38,7 @@ constexpr int kThreads = 256;      // small kernels
 #endif
 constexpr int kGemmWaves = TTT_GEMM_WAVES;  // wave64s per GEMM workgroup (4 or 8)
 constexpr int kGemmThreads = 64 * kGemmWaves;
-constexpr int kMaxStages = 6;      // LDS stages per workgroup (all but one in flight)
+constexpr int kMaxStages = 6;      // LDS stages of one operand (all but one in flight)
 constexpr int kRsrcWord3 = 0x00020000;
 enum { kRowMajor = 0, kSlab = 1 };  // LDS / HBM layouts of a GEMM operand (see Operand)
 constexpr int kCpolNt = 2, kCpolSc1 = 16;  // cache-policy bits of buffer instructions
