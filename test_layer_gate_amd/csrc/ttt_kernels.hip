@@ -1166,12 +1166,13 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
   zero_acc(acc);
   const Operand z =
       row_major<BK>(Z + ((int64_t)ti.b * T + t0) * g.ld_z, g.ld_z, min(BN, T - t0));
-  // The rotation uses the absolute token tile, so that every schedule runs
-  // the same tile with the same summation order.
+  // The rotation follows the absolute 256-token block, whatever the tile
+  // width, so that every schedule and width sums each output in the same
+  // order.
   const int nk = f / BK;
   gemm_core_ab<BM, BN, WGM, BK, NSTA, NSTB, Bf16Mma, false, kSlab, kRowMajor>(
       slab_blocked<kSnapSlab>(snap + ti.b * snap_bstride + i * snap_cstride, f, c0, 0), z, z, nk,
-      &acc[0][0], lds, NoHook{}, k_rotation<kApplyGroupM>(ti.tm, t0 / BN, nk));
+      &acc[0][0], lds, NoHook{}, k_rotation<kApplyGroupM>(ti.tm, t0 / 256, nk));
   const Frag<L> fr;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -1531,8 +1532,16 @@ hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bs
                         int tok_begin, int tok_end, int chunk, const ApplyTile* tiles,
                         int n_tiles, int n_chunks, hipStream_t s) {
   // A token tile must not straddle a chunk (it reads one snapshot): tiles
-  // start at chunk starts and are apply_tile_width(chunk) wide.
-  switch (apply_tile_width(chunk)) {
+  // start at chunk starts and are apply_tile_width(chunk) wide, or narrower
+  // (down to 64 tokens) when a launch without a tile list would otherwise
+  // leave compute units idle, as the running schedule's one-chunk launches
+  // do.
+  int width = apply_tile_width(chunk);
+  if (tiles == nullptr)
+    while (width > 64 &&
+           (int64_t)g.B * ceil_div(g.d, 256) * ceil_div(tok_end - tok_begin, width) < 256)
+      width /= 2;
+  switch (width) {
     case 256:
       apply_dispatch<256>(Z, snap, snap_bstride, snap_cstride, O, out_f32, g, tok_begin, tok_end,
                           chunk, tiles, n_tiles, n_chunks, s);
