@@ -775,7 +775,7 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 // (K = d_ff, bf16) in KG_SPLIT parts of d_ff and writes the sum of its
 // elementwise product with the kept V tile to partial[b][chunk][pair][part]
 // (the sum is linear in the Z Gram, so the parts add up).
-constexpr int KG_B = 256, KG_WGM = 2, KG_SPLIT = 2;
+constexpr int KG_B = 256, KG_WGM = 2, KG_SPLIT = 2, KG_NSTA = 2, KG_NSTB = 3;
 
 struct GramTile {
   int b, i, pair, part, s0, u0, c1, weight;
@@ -814,8 +814,8 @@ __device__ __forceinline__ void gram_tile_acc(const u16* X, int64_t ld, int64_t 
                                               u16* lds) {
   const Operand xs = row_major<64>(X + ((int64_t)t.b * rows_b + t.s0) * ld + k0, ld, t.c1 - t.s0);
   const Operand xu = row_major<64>(X + ((int64_t)t.b * rows_b + t.u0) * ld + k0, ld, t.c1 - t.u0);
-  gemm_core<KG_B, KG_B, KG_WGM, 64, 2, Op, false, kRowMajor, kRowMajor>(xs, xu, xu, nk, acc, lds,
-                                                                       NoHook{});
+  gemm_core_ab<KG_B, KG_B, KG_WGM, 64, KG_NSTA, KG_NSTB, Op, false, kRowMajor, kRowMajor>(
+      xs, xu, xu, nk, acc, lds, NoHook{});
 }
 
 __global__ __launch_bounds__(kGemmThreads) void gram_v_kernel(const u16* __restrict__ Vrow,
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(kGemmThreads) void gram_v_kernel(const u16* __restr
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using L = Layout<KG_B, KG_B, KG_WGM>;
   constexpr int NR = L::TM * L::TN * 16;  // accumulator registers per lane
-  TTT_GEMM_LDS(lds, KG_B, KG_B, 64, 2)
+  TTT_GEMM_LDS_AB(lds, KG_B, KG_B, 64, KG_NSTA, KG_NSTB)
   const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, 1);
   if (t.u0 >= t.c1) return;  // uniform: blocks past a short last chunk add nothing
   f32x16 acc[L::TM][L::TN];
@@ -852,8 +852,8 @@ __global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using L = Layout<KG_B, KG_B, KG_WGM>;
   constexpr int NR = L::TM * L::TN * 16;
-  TTT_GEMM_LDS(lds, KG_B, KG_B, 64, 2)
-  __shared__ float wsum[kGemmWaves];
+  TTT_GEMM_LDS_AB(lds, KG_B, KG_B, 64, KG_NSTA, KG_NSTB)
+  float* wsum = reinterpret_cast<float*>(lds);  // per-wave sums, once the core is done
   const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, KG_SPLIT);
   const int steps = g.f / 64, per = (steps + KG_SPLIT - 1) / KG_SPLIT;
   const int k_first = t.part * per, nk = min(steps, k_first + per) - k_first;
