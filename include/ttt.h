@@ -125,9 +125,10 @@ ttt_status ttt_layer_forward(const ttt_desc* desc,
  *   clip_norm   > 0 and finite (TTT_ERR_INVALID_ARG otherwise)
  * The norms come from the chunk's C x C Gram matrices of Z (bf16) and V
  * (fp16), so each scale carries their rounding (relative ~1e-3). The
- * workspace (ttt_clipped_workspace_size) also holds a token-major copy of V
- * and the per-chunk norms. Every other argument, layout and convention is
- * ttt_layer_forward's. */
+ * workspace (ttt_clipped_workspace_size) also holds a token-major copy of V,
+ * the V Gram tiles (256 KB per pair of 256-token blocks of a chunk: 2.5 MB a
+ * chunk at C = 1024) and the per-chunk norms. Every other argument, layout
+ * and convention is ttt_layer_forward's. */
 ttt_status ttt_clipped_workspace_size(const ttt_desc* desc, int32_t chunk, float clip_norm,
                                       size_t* bytes);
 ttt_status ttt_layer_forward_clipped(const ttt_desc* desc,
