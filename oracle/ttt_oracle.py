@@ -42,14 +42,18 @@ tested by the pins in tests/test_oracle.py):
     and the conv reads nothing past the token's own document (nor past its
     chunk, with chunk padding). The returned final state is the one after
     the last document.
+  * Decode (ttt_decode): one token at a time, with chunk-local conv padding
+    only, the state stepped as soon as a chunk's last token is processed.
+    With that padding it is the prefill computed token by token; the pages
+    say decode was not evaluated and give no rule for sequence padding.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["silu", "gated_activation", "conv_target_input", "lm_target",
-           "ttt_prefill", "ttt_prefill_packed", "activation_rows", "target_rows",
-           "final_state_entries"]
+           "ttt_prefill", "ttt_prefill_packed", "ttt_decode", "activation_rows",
+           "target_rows", "final_state_entries"]
 
 
 def _f64(a) -> np.ndarray:
@@ -217,6 +221,66 @@ def ttt_prefill_packed(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
         t = int(chunk_end[t])
     assert n_chunks == int(chunk_id[-1]) + 1
     return O, W
+
+
+def ttt_decode(H, X0, Wg, Wu, W_state, taps, W_target, eta, chunk, start=0):
+    """Token-by-token decode of B sequences, with chunk-local conv padding.
+
+    [iplex] §3 and §6: within a chunk every output uses the state from before
+    the chunk's update, and the chunk's update is taken once the chunk is
+    complete; with the [iplex] §6 chunk-boundary padding the target of a
+    chunk reads only that chunk's tokens, so the update needs no token past
+    the chunk's end and a decoder can take it as soon as the chunk's last
+    token has been processed. (With sequence padding the last K - 1 targets
+    of a chunk read tokens that are not decoded yet; the pages give no rule
+    for that case, so it is not defined here.)
+
+    Processes tokens one at a time: token i of the call is document position
+    start + i (start counts tokens already processed, chunks being counted
+    from the document start). For each token: z = phi(h Wg^T) * (h Wu^T) and
+    o = z W^T with the current state; (z, x0) join the current chunk; when
+    the position closes a chunk, its target Y[t] = sum_k taps[k] X0[t + k]
+    over reads inside the chunk, V = Y W_target, and W += eta V^T Z.
+
+    H, X0 [B, n, d]; W_state [d, f] (shared start) or [B, d, f]; returns
+    O [B, n, d], the state [B, d, f] after the last complete chunk, and the
+    number of tokens of the incomplete chunk left pending (not yet applied to
+    the state), all float64. `start` must be a multiple of `chunk` (a call
+    begins at a chunk boundary).
+    """
+    H, X0, taps = _f64(H), _f64(X0), _f64(taps)
+    Wg, Wu, Wt = _f64(Wg), _f64(Wu), _f64(W_target)
+    Ws = _f64(W_state)
+    B, n, d = H.shape
+    f = Wg.shape[0]
+    K = taps.shape[0]
+    if chunk < 1 or start % chunk != 0:
+        raise ValueError("start must be a multiple of chunk")
+    O = np.zeros((B, n, d))
+    W_out = np.zeros((B, d, f))
+    pending = 0
+    for b in range(B):
+        W = (Ws[b] if Ws.ndim == 3 else Ws).copy()
+        zs, xs = [], []
+        for i in range(n):
+            h = H[b, i]
+            z = silu(Wg @ h) * (Wu @ h)                 # [f]
+            O[b, i] = W @ z                             # o = z W^T, pre-update state
+            zs.append(z)
+            xs.append(X0[b, i])
+            if (start + i + 1) % chunk == 0:            # the chunk is complete
+                L = len(zs)
+                Y = np.zeros((L, d))
+                for t in range(L):
+                    for k in range(K):
+                        if t + k < L:                   # reads stay inside the chunk
+                            Y[t] += taps[k] * xs[t + k]
+                V = Y @ Wt
+                W = W + eta * (V.T @ np.array(zs))
+                zs, xs = [], []
+        W_out[b] = W
+        pending = len(zs)
+    return O, W_out, pending
 
 
 # ---------------------------------------------------------------------------

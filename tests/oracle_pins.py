@@ -436,9 +436,54 @@ def pin_packed_isolation():
         assert not np.allclose(O[a:e], O2[a:e]), f"document [{a},{e}) ignored its input"
 
 
+def decode(x, **over):
+    a = dict(x)
+    a.update(over)
+    return ora.ttt_decode(a["H"], a["X0"], a["Wg"], a["Wu"], a["W_down0"], a["taps"],
+                          a["W_target"], a["eta"], a["chunk"], start=a.get("start", 0))
+
+
+def pin_decode_is_chunk_padded_prefill():
+    """Token-by-token decode equals the chunk-padded prefill: every output,
+    and the state after whole chunks (the sequence is 4 chunks long)."""
+    x = small_case(seed=21, T=32, C=8)
+    O, Wf = run(x, pad="chunk")
+    Od, Wd, pending = decode(x)
+    assert pending == 0
+    _close(Od, O, tol=1e-12, what="decode O")
+    _close(Wd, Wf, tol=1e-12, what="decode W")
+
+
+def pin_decode_pending_chunk():
+    """A ragged end: the outputs still match the prefill, but the state is
+    the one after the last whole chunk (the prefill of those tokens alone)
+    and the 5 tokens of the open chunk are pending."""
+    x = small_case(seed=22, T=37, C=8)
+    O, _ = run(x, pad="chunk")
+    _, W32 = run(x, H=x["H"][:, :32], X0=x["X0"][:, :32], pad="chunk")
+    Od, Wd, pending = decode(x)
+    assert pending == 5
+    _close(Od, O, tol=1e-12, what="ragged decode O")
+    _close(Wd, W32, tol=1e-12, what="ragged decode W")
+
+
+def pin_decode_resumes_prefill():
+    """Prefill of the first two chunks, then decode from the state it
+    returned, reproduces the single chunk-padded prefill."""
+    x = small_case(seed=23, T=40, C=8)
+    O, Wf = run(x, pad="chunk")
+    O1, W1 = run(x, H=x["H"][:, :16], X0=x["X0"][:, :16], pad="chunk")
+    O2, W2, pending = decode(x, H=x["H"][:, 16:], X0=x["X0"][:, 16:], W_down0=W1, start=16)
+    assert pending == 0
+    _close(np.concatenate([O1, O2], axis=1), O, tol=1e-12, what="prefill + decode O")
+    _close(W2, Wf, tol=1e-12, what="prefill + decode W")
+
+
 ALL_PINS = [pin_reduces_to_plain_mlp, pin_prefix_scan_form, pin_state_free_form,
             pin_next_token_target, pin_conv_library, pin_linear_in_eta,
             pin_chunk_causality, pin_batch_independence, pin_split_resume,
             pin_brute_force_scalars, pin_sampled_forms, pin_golden_ntp_fixture,
             pin_packed_single_document, pin_packed_equals_documents,
-            pin_packed_isolation, pin_clip_loose_is_plain, pin_clip_each_delta]
+            pin_packed_isolation, pin_clip_loose_is_plain, pin_clip_each_delta,
+            pin_decode_is_chunk_padded_prefill, pin_decode_pending_chunk,
+            pin_decode_resumes_prefill]

@@ -129,7 +129,68 @@ def _packed_variant(reset=True, conv_stops=True, chunks_from_doc=True):
     return packed
 
 
+_real_decode = ora.ttt_decode
+
+
+def _decode_variant(late=0, update_first=False, conv_past_chunk=False):
+    """A copy of the decode loop with one knob turned: the chunk's update
+    taken `late` tokens after the chunk closes, taken before the closing
+    token's output, or a chunk target that reads the next chunk's tokens."""
+    def decode(H, X0, Wg, Wu, W_state, taps, W_target, eta, chunk, start=0):
+        H, X0, taps = (np.asarray(a, np.float64) for a in (H, X0, taps))
+        Ws = np.asarray(W_state, np.float64)
+        B, n, d = H.shape
+        f = np.asarray(Wg).shape[0]
+        K = taps.shape[0]
+        O = np.zeros((B, n, d))
+        W_out = np.zeros((B, d, f))
+        pend = 0
+        for b in range(B):
+            W = (Ws[b] if Ws.ndim == 3 else Ws).copy()
+            Z = ora.gated_activation(H[b], Wg, Wu)
+            queue = []                  # (token index when due, delta)
+            c0 = 0
+            for i in range(n):
+                closes = (start + i + 1) % chunk == 0
+                if closes and update_first:
+                    pass
+                for due, dl in [q for q in queue if q[0] <= i]:
+                    W = W + dl
+                queue = [q for q in queue if q[0] > i]
+                rows = slice(c0, i + 1)
+                if closes:
+                    L = i + 1 - c0
+                    lim = min(n, c0 + L + K - 1) if conv_past_chunk else c0 + L
+                    Y = np.zeros((L, d))
+                    for t in range(L):
+                        for k in range(K):
+                            if c0 + t + k < lim:
+                                Y[t] += taps[k] * X0[b, c0 + t + k]
+                    dl = eta * ((Y @ np.asarray(W_target, np.float64)).T @ Z[rows])
+                    if update_first:
+                        W = W + dl
+                        O[b, i] = W @ Z[i]
+                    else:
+                        O[b, i] = W @ Z[i]
+                        if late == 0:
+                            W = W + dl
+                        else:
+                            queue.append((i + 1 + late, dl))
+                    c0 = i + 1
+                else:
+                    O[b, i] = W @ Z[i]
+            for _, dl in queue:
+                W = W + dl
+            W_out[b] = W
+            pend = n - c0
+        return O, W_out, pend
+    return decode
+
+
 MUTATIONS = {
+    "decode_update_one_token_late": ("ttt_decode", _decode_variant(late=1)),
+    "decode_update_before_last_output": ("ttt_decode", _decode_variant(update_first=True)),
+    "decode_target_reads_next_chunk": ("ttt_decode", _decode_variant(conv_past_chunk=True)),
     "clip_norm_without_eta": ("ttt_prefill", _prefill_variant(clip_mode="no_eta")),
     "clip_scale_inverted": ("ttt_prefill", _prefill_variant(clip_mode="inverted")),
     "clip_whole_state": ("ttt_prefill", _prefill_variant(clip_mode="state")),
