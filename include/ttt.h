@@ -197,6 +197,44 @@ ttt_status ttt_layer_forward_continue(const ttt_desc* desc,
                                       void* O, void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+/* Decode: the layer one token at a time, for B sequences together.
+ * Within a chunk every output uses the state from before the chunk's update
+ * (iplexlaw explainer §3); with the chunk-boundary padding of §6 a chunk's
+ * target reads only the chunk's own tokens, so the update is taken as soon
+ * as the chunk's last token has been processed, and decoding a document
+ * token by token gives the prefill's outputs and states. Sequence padding
+ * would need tokens not decoded yet, so the decode entry points require
+ * TTT_FLAG_PAD_CHUNK (TTT_ERR_UNSUPPORTED otherwise).
+ *   desc       seq_len must be 1 (one token per sequence per step);
+ *              w0_batch_stride must be 0
+ *   decode_state  device buffer of ttt_decode_state_size() bytes, 256-byte
+ *              aligned, owned by the caller: the bf16 copy of each state the
+ *              apply reads, the open chunk's activations and X0 rows, and
+ *              scratch. One buffer per group of B sequences decoded together.
+ *   W_state    [B, d, f] float32, in/out, the fast weight of each sequence.
+ * ttt_decode_begin starts decoding at a chunk boundary (a document start, or
+ * after ttt_layer_forward_continue on a prefix whose length is a multiple
+ * of C): it writes the bf16 copy of W_state into decode_state.
+ * ttt_decode_step processes the token at document position pos (the same
+ * for every sequence; positions must follow one another from the boundary
+ * ttt_decode_begin was called at, as the open chunk's rows are kept in
+ * decode_state):
+ *   h, x0      [B, d] act_dtype, the token's hidden state and embedding
+ *   Wg, Wu, conv_taps, W_target   as in ttt_layer_forward
+ *   o          [B, d] act_dtype out: z W^T with the current state
+ * When pos closes a chunk (pos % C == C - 1), the step also takes the
+ * chunk's update: W_state is updated in place and its bf16 copy refreshed.
+ * Arguments are checked as in ttt_layer_forward; o, W_state and
+ * decode_state may not overlap an input or each other (TTT_ERR_ALIAS). */
+ttt_status ttt_decode_state_size(const ttt_desc* desc, int32_t chunk, size_t* bytes);
+ttt_status ttt_decode_begin(const ttt_desc* desc, int32_t chunk, float* W_state,
+                            void* decode_state, size_t decode_state_bytes, void* stream);
+ttt_status ttt_decode_step(const ttt_desc* desc, const void* h, const void* x0,
+                           const void* Wg, const void* Wu, const void* conv_taps,
+                           const void* W_target, float eta, int32_t chunk, int32_t pos,
+                           float* W_state, void* decode_state, size_t decode_state_bytes,
+                           void* o, void* stream);
+
 /* Step entry points: one step of the layer each, for per-step checks.
  * ttt_gated_activation writes Z [B, T, d_ff] in bf16.
  * ttt_lm_target writes V [B, T, d_model] in bf16 (unscaled, eta not applied).

@@ -14,6 +14,9 @@ from ._binding import (  # noqa: F401
     clipped_workspace_size,
     continue_workspace_size,
     copy_calibration,
+    decode_begin,
+    decode_state_size,
+    decode_step,
     gated_activation,
     layer_forward,
     layer_forward_continue,
@@ -29,6 +32,7 @@ from ._binding import (  # noqa: F401
 
 __all__ = ["layer_forward", "layer_forward_packed", "packed_workspace_size",
            "layer_forward_continue", "continue_workspace_size", "clipped_workspace_size",
+           "decode_state_size", "decode_begin", "decode_step",
            "gated_activation", "lm_target", "workspace_size",
            "copy_calibration",
            "make_desc", "profile_enable", "profile_read", "TTTError", "lib",

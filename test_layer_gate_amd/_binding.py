@@ -75,12 +75,17 @@ def lib() -> ctypes.CDLL:
     L.ttt_layer_forward_continue.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
                                              _P, ctypes.c_float, ctypes.c_int32, _P, _P, _S,
                                              _P]
+    L.ttt_decode_state_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
+    L.ttt_decode_begin.argtypes = [DP, ctypes.c_int32, _P, _P, _S, _P]
+    L.ttt_decode_step.argtypes = [DP, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
+                                  ctypes.c_int32, _P, _P, _S, _P, _P]
     L.ttt_gated_activation.argtypes = [DP, _P, _P, _P, _P, _P, _S, _P]
     L.ttt_lm_target.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _S, _P]
     for fn in ("ttt_workspace_size", "ttt_step_workspace_size", "ttt_layer_forward",
                "ttt_packed_workspace_size", "ttt_layer_forward_packed",
                "ttt_clipped_workspace_size", "ttt_layer_forward_clipped",
                "ttt_continue_workspace_size", "ttt_layer_forward_continue",
+               "ttt_decode_state_size", "ttt_decode_begin", "ttt_decode_step",
                "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
         getattr(L, fn).restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int32]
@@ -332,6 +337,61 @@ def layer_forward_continue(H, X0, X0_next, Wg, Wu, W_state, conv_taps, W_target,
         _ptr(W_state), _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)),
         int(chunk), _ptr(O), _ptr(workspace), workspace.numel(), _stream(stream)))
     return O
+
+
+def _decode_desc(h, Wg, conv_taps):
+    B, d = h.shape
+    return make_desc(B, 1, d, Wg.shape[0], conv_taps.shape[0], _dtype_code(h, "h"),
+                     _dtype_code(Wg, "Wg"), 0, FLAG_PAD_CHUNK)
+
+
+def decode_state_size(desc: Desc, chunk: int) -> int:
+    n = _S(0)
+    _check(lib().ttt_decode_state_size(ctypes.byref(desc), int(chunk), ctypes.byref(n)))
+    return n.value
+
+
+def decode_begin(W_state, chunk, decode_state, *, act_dtype=torch.bfloat16,
+                 weight_dtype=torch.bfloat16, conv_k=1, stream=None):
+    """Start decoding B sequences at a chunk boundary from W_state [B, d, f]
+    float32 (include/ttt.h, ttt_decode_begin): writes the bf16 copy of the
+    states into decode_state (uint8, decode_state_size bytes)."""
+    _require_cuda(W_state, decode_state)
+    if W_state.dim() != 3 or W_state.dtype != torch.float32:
+        raise ValueError("W_state must be float32 [B, d_model, d_ff]")
+    B, d, f = W_state.shape
+    act = TTT_F32 if act_dtype == torch.float32 else TTT_BF16
+    wt = TTT_F32 if weight_dtype == torch.float32 else TTT_BF16
+    desc = make_desc(B, 1, d, f, conv_k, act, wt, 0, FLAG_PAD_CHUNK)
+    _check(lib().ttt_decode_begin(ctypes.byref(desc), int(chunk), _ptr(W_state),
+                                  _ptr(decode_state), decode_state.numel(), _stream(stream)))
+
+
+def decode_step(h, x0, Wg, Wu, conv_taps, W_target, eta, chunk, pos, W_state, decode_state,
+                *, out=None, stream=None):
+    """One token per sequence (include/ttt.h, ttt_decode_step): h, x0 [B, d]
+    at document position pos; W_state [B, d, f] float32 is updated in place
+    when pos closes a chunk. Returns o [B, d]."""
+    _require_cuda(h, x0, Wg, Wu, conv_taps, W_target, W_state, decode_state)
+    if h.dim() != 2 or x0.shape != h.shape or x0.dtype != h.dtype:
+        raise ValueError("h and x0 must both be [B, d_model] of one dtype")
+    B, d = h.shape
+    f = Wg.shape[0]
+    if W_state.shape != (B, d, f) or W_state.dtype != torch.float32:
+        raise ValueError("W_state must be float32 [B, d_model, d_ff]")
+    for t, n in ((Wu, "Wu"), (conv_taps, "conv_taps"), (W_target, "W_target")):
+        if t.dtype != Wg.dtype:
+            raise TypeError(f"{n} must have Wg's dtype")
+    if not math.isfinite(float(eta)):
+        raise ValueError("eta must be finite")
+    desc = _decode_desc(h, Wg, conv_taps)
+    o = torch.empty_like(h) if out is None else out
+    _require_cuda(o)
+    _check(lib().ttt_decode_step(ctypes.byref(desc), _ptr(h), _ptr(x0), _ptr(Wg), _ptr(Wu),
+                                 _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)),
+                                 int(chunk), int(pos), _ptr(W_state), _ptr(decode_state),
+                                 decode_state.numel(), _ptr(o), _stream(stream)))
+    return o
 
 
 def _step_ws(desc, device):

@@ -365,6 +365,21 @@ ttt_status ttt_step_workspace_size(const ttt_desc* desc, size_t* bytes) {
 
 namespace {
 
+// The update's operands are fp16 with the target scaled by vscale = eta *
+// 2^p, p = round(-log2 |eta|), so that eta * V sits at V's own magnitude;
+// the state is carried as 2^p * W in fp32 and every output is multiplied
+// back by 2^-p. Powers of two make both scalings exact.
+void update_scales(float eta, float* vscale, float* acc_scale) {
+  *vscale = 0.0f;
+  *acc_scale = 1.0f;
+  if (eta != 0.0f) {
+    long p = std::lround(-std::log2(std::fabs((double)eta)));
+    p = std::max(-60L, std::min(60L, p));
+    *acc_scale = std::ldexp(1.0f, (int)p);
+    *vscale = eta * *acc_scale;
+  }
+}
+
 // Everything after the descriptor, chunk (or document) checks: pointer and
 // workspace checks, then the launches of the whole layer. For a continuation
 // (g.resume) W_down0 and W_down_final are the same fp32 [B, d, f] state,
@@ -473,17 +488,8 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
   uint16_t* VT = at<uint16_t>(workspace, L.vt);
   uint16_t* snap = at<uint16_t>(workspace, L.snap);
 
-  // The update's operands are fp16 with the target scaled by vscale = eta *
-  // 2^p, p = round(-log2 |eta|), so that eta * V sits at V's own magnitude;
-  // the state is carried as 2^p * W in fp32 and every output is multiplied
-  // back by 2^-p. Powers of two make both scalings exact.
-  float vscale = 0.0f, acc_scale = 1.0f;
-  if (eta != 0.0f) {
-    long p = std::lround(-std::log2(std::fabs((double)eta)));
-    p = std::max(-60L, std::min(60L, p));
-    acc_scale = std::ldexp(1.0f, (int)p);
-    vscale = eta * acc_scale;
-  }
+  float vscale, acc_scale;
+  update_scales(eta, &vscale, &acc_scale);
 
   TTT_LAUNCH("transpose_w_target", s,
              tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, D.ld_y, s));
@@ -632,6 +638,164 @@ ttt_status ttt_layer_forward_continue(const ttt_desc* desc, const void* H, const
   TTT_TRY(check_ptr(W_state, "W_state"));
   return forward_impl(g, H, X0, Wg, Wu, W_state, conv_taps, W_target, eta, O, W_state,
                       workspace, workspace_bytes, stream, X0_next, n_next);
+}
+
+// ------------------------------------------------------------ decode
+
+}  // extern "C"
+
+namespace {
+
+// The decode state of B sequences: the bf16 copy of each state the apply
+// reads, the open chunk's Z^T and X0 rows, and the chunk-end scratch (Y,
+// W_target^T, V^T) and per-token scratch (z, the apply's partial sums).
+struct DecodeLayout {
+  size_t shadow = 0, zt = 0, x0c = 0, zb = 0, part = 0, y = 0, wtt = 0, vt = 0, total = 0;
+};
+
+DecodeLayout decode_layout(const Geo& g, const tttk::Dims& Dc) {
+  DecodeLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.shadow = take(g.B * tttk::snap_elems(Dc) * 2);
+  L.zt = take(tttk::zt_elems(Dc) * 2);
+  L.x0c = take(g.B * g.C * g.d * 2);
+  L.zb = take(g.B * g.f * 2);
+  L.part = take(tttk::decode_apply_part_floats((int)g.B, (int)g.d) * 4);
+  L.y = take(g.B * Dc.T_pad * Dc.ld_y * 2);
+  L.wtt = take(g.d * Dc.ld_y * 2);
+  L.vt = take(tttk::vt_elems(Dc) * 2);
+  L.total = off;
+  return L;
+}
+
+// Descriptor checks of the decode entry points: one token per sequence,
+// chunk-local padding, states [B, d, f]. Dc: the dims of one chunk.
+ttt_status check_decode(const ttt_desc* desc, int32_t chunk, Geo* g, tttk::Dims* Dc) {
+  TTT_TRY(check_desc(desc, g));
+  TTT_TRY(check_chunk(chunk, g));
+  if (desc->seq_len != 1)
+    return fail(TTT_ERR_INVALID_ARG, "decode takes one token per sequence: seq_len must be 1");
+  if (!(desc->flags & TTT_FLAG_PAD_CHUNK))
+    return fail(TTT_ERR_UNSUPPORTED,
+                "decode needs TTT_FLAG_PAD_CHUNK: with sequence padding a chunk's targets read "
+                "tokens that are not decoded yet");
+  if (desc->w0_batch_stride != 0)
+    return fail(TTT_ERR_INVALID_ARG, "w0_batch_stride must be 0: W_state is [batch, d, f]");
+  *Dc = tttk::make_dims((int)g->B, chunk, (int)g->d, (int)g->f);
+  return TTT_OK;
+}
+
+ttt_status check_dstate(void* dstate, size_t bytes, const DecodeLayout& L) {
+  TTT_TRY(check_ptr(dstate, "decode_state", 256));
+  if (bytes < L.total)
+    return fail(TTT_ERR_WORKSPACE, "decode state has " + std::to_string(bytes) +
+                                       " bytes, needs " + std::to_string(L.total));
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status ttt_decode_state_size(const ttt_desc* desc, int32_t chunk, size_t* bytes) {
+  Geo g;
+  tttk::Dims Dc;
+  TTT_TRY(check_decode(desc, chunk, &g, &Dc));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = decode_layout(g, Dc).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_decode_begin(const ttt_desc* desc, int32_t chunk, float* W_state,
+                            void* decode_state, size_t decode_state_bytes, void* stream) {
+  Geo g;
+  tttk::Dims Dc;
+  TTT_TRY(check_decode(desc, chunk, &g, &Dc));
+  TTT_TRY(check_ptr(W_state, "W_state"));
+  const DecodeLayout L = decode_layout(g, Dc);
+  TTT_TRY(check_dstate(decode_state, decode_state_bytes, L));
+  TTT_TRY(check_aliasing({}, {range_of("W_state", W_state, g.B * g.d * g.f * 4),
+                              range_of("decode_state", decode_state, L.total)}));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // An update over no tokens: W_state is stored back unchanged and its bf16
+  // copy written.
+  TTT_LAUNCH("decode_begin", s,
+             tttk::launch_update(at<uint16_t>(decode_state, L.zt),
+                                 at<uint16_t>(decode_state, L.vt), W_state, true, g.d * g.f,
+                                 g.f, 1.0f, nullptr, 0, W_state,
+                                 at<uint16_t>(decode_state, L.shadow), Dc, 0, 0, (int)g.C,
+                                 nullptr, 1, s));
+  return TTT_OK;
+}
+
+ttt_status ttt_decode_step(const ttt_desc* desc, const void* h, const void* x0, const void* Wg,
+                           const void* Wu, const void* conv_taps, const void* W_target,
+                           float eta, int32_t chunk, int32_t pos, float* W_state,
+                           void* decode_state, size_t decode_state_bytes, void* o,
+                           void* stream) {
+  Geo g;
+  tttk::Dims Dc;
+  TTT_TRY(check_decode(desc, chunk, &g, &Dc));
+  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
+  if (pos < 0) return fail(TTT_ERR_INVALID_ARG, "pos must be >= 0");
+  TTT_TRY(check_ptr(h, "h"));
+  TTT_TRY(check_ptr(x0, "x0"));
+  TTT_TRY(check_ptr(Wg, "Wg"));
+  TTT_TRY(check_ptr(Wu, "Wu"));
+  TTT_TRY(check_ptr(conv_taps, "conv_taps"));
+  TTT_TRY(check_ptr(W_target, "W_target"));
+  TTT_TRY(check_ptr(W_state, "W_state"));
+  TTT_TRY(check_ptr(o, "o"));
+  const DecodeLayout L = decode_layout(g, Dc);
+  TTT_TRY(check_dstate(decode_state, decode_state_bytes, L));
+  const size_t ab = g.act_bytes(), wb = g.w_bytes();
+  TTT_TRY(check_aliasing({range_of("h", h, g.B * g.d * ab), range_of("x0", x0, g.B * g.d * ab),
+                          range_of("Wg", Wg, g.f * g.d * wb), range_of("Wu", Wu, g.f * g.d * wb),
+                          range_of("conv_taps", conv_taps, g.K * g.d * wb),
+                          range_of("W_target", W_target, g.d * g.d * wb)},
+                         {range_of("o", o, g.B * g.d * ab),
+                          range_of("W_state", W_state, g.B * g.d * g.f * 4),
+                          range_of("decode_state", decode_state, L.total)}));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int C = (int)g.C, r = pos % C;
+  uint16_t* shadow = at<uint16_t>(decode_state, L.shadow);
+  uint16_t* zt = at<uint16_t>(decode_state, L.zt);
+  uint16_t* x0c = at<uint16_t>(decode_state, L.x0c);
+  uint16_t* zb = at<uint16_t>(decode_state, L.zb);
+  TTT_LAUNCH("decode_gate_up", s,
+             tttk::launch_decode_gate_up(h, x0, g.act_f32, Wg, Wu, g.w_f32, (int)g.B, (int)g.d,
+                                         (int)g.f, zb, zt,
+                                         tttk::sb_elems<tttk::kZtSlab>(g.f, Dc.T_pad),
+                                         (int)Dc.T_pad, x0c, C, r, s));
+  TTT_LAUNCH("decode_apply", s,
+             tttk::launch_decode_apply(zb, shadow, tttk::snap_elems(Dc), (int)g.B, (int)g.d,
+                                       (int)g.f, at<float>(decode_state, L.part), o, g.act_f32,
+                                       s));
+  if (r == C - 1) {
+    // The chunk is complete: its target (reads inside the chunk only), then
+    // its update, in place, with the bf16 copy refreshed for the next chunk.
+    float vscale, acc_scale;
+    update_scales(eta, &vscale, &acc_scale);
+    uint16_t* y = at<uint16_t>(decode_state, L.y);
+    uint16_t* wtt = at<uint16_t>(decode_state, L.wtt);
+    uint16_t* vt = at<uint16_t>(decode_state, L.vt);
+    TTT_LAUNCH("transpose_w_target", s,
+               tttk::launch_transpose_f16(W_target, g.w_f32, wtt, (int)g.d, (int)g.d, Dc.ld_y,
+                                          s));
+    TTT_LAUNCH("conv", s,
+               tttk::launch_conv(x0c, nullptr, 0, conv_taps, g.w_f32, y, Dc, (int)g.K, C, true,
+                                 nullptr, s));
+    TTT_LAUNCH("target", s, tttk::launch_target(y, wtt, vt, nullptr, nullptr, vscale, Dc, s));
+    TTT_LAUNCH("update_running", s,
+               tttk::launch_update(zt, vt, W_state, true, g.d * g.f, g.f, acc_scale, nullptr, 0,
+                                   W_state, shadow, Dc, 0, C, C, nullptr, 1, s));
+  }
+  return TTT_OK;
 }
 
 ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void* Wg,

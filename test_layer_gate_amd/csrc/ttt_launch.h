@@ -171,6 +171,22 @@ hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Win
                          uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
                          int chunk, const BlockInfo* blocks, int n_chunks, hipStream_t s);
 
+// Decode step, gated activation: for one token per sequence (h, x0: [B][d],
+// act dtype), zb[b][j] = bf16(z), column col of the chunk's Z^T (sb<256>, f
+// rows, zt_cols columns, zt_bstride elements per sequence) = fp16(z), with
+// z = SiLU(h_b Wg[j]) * (h_b Wu[j]); and x0 (as bf16) into row col of x0c
+// [B][chunk][d].
+hipError_t launch_decode_gate_up(const void* h, const void* x0, bool act_f32, const void* Wg,
+                                 const void* Wu, bool w_f32, int B, int d, int f, uint16_t* zb,
+                                 uint16_t* zt, int64_t zt_bstride, int zt_cols, uint16_t* x0c,
+                                 int chunk, int col, hipStream_t s);
+// Decode step, apply: o[b] = zb[b] S_b^T (S_b the bf16 state of sequence b,
+// sb<256> d x f, s_bstride elements apart), through part
+// (decode_apply_part_floats(B, d) floats); o is [B][d], bf16 or fp32.
+int64_t decode_apply_part_floats(int B, int d);
+hipError_t launch_decode_apply(const uint16_t* zb, const uint16_t* S, int64_t s_bstride, int B,
+                               int d, int f, float* part, void* o, bool out_f32, hipStream_t s);
+
 // O[b][t] = Z[b][t] W_i^T, where W_i is the bf16 state (sb<256>(d x f)) at
 // snap + b * snap_bstride + i * snap_cstride. Without tiles: for tokens t in
 // [tok_begin, tok_end), tok_begin a multiple of apply_tile_width(chunk), i =

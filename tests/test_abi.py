@@ -331,3 +331,73 @@ def test_continue_validates_before_launch(L):
     _, need = continue_ws(L, qwen_desc(), 1024)
     assert continue_fwd(L, qwen_desc(), p, p[8], 3, ws_bytes=need - 1) == WORKSPACE
     assert continue_fwd(L, qwen_desc(), p, None, 0, ws_bytes=need - 1) == WORKSPACE
+
+
+# ---- decode --------------------------------------------------------------------
+
+def decode_desc(**kw):
+    a = dict(batch=1, seq_len=1, d_model=2560, d_ff=9728, conv_k=4, flags=bnd.FLAG_PAD_CHUNK)
+    a.update(kw)
+    return bnd.make_desc(**a)
+
+
+def decode_size(L, desc, chunk=1024):
+    n = ctypes.c_size_t(0)
+    st = L.ttt_decode_state_size(ctypes.byref(desc), chunk, ctypes.byref(n))
+    return st, n.value
+
+
+def test_decode_state_size(L):
+    st, n = decode_size(L, decode_desc(batch=2))
+    assert st == OK, L.ttt_last_error()
+    B, d, f, C = 2, 2560, 9728, 1024
+
+    def pad(x):
+        return x + 64 if (x // 64) % 2 == 0 else x
+    ld_y = pad(d)
+    expect = (B * d * f * 2            # bf16 copies of the states (d rows: whole 256-row slabs)
+              + B * f * C * 2          # the open chunk's Z^T (f rows: whole slabs)
+              + B * C * d * 2          # the open chunk's X0 rows
+              + B * f * 2 + B * 4 * d * 4      # z and the apply's partial sums
+              + B * C * ld_y * 2 + d * ld_y * 2 + B * d * C * 2)   # Y, W_target^T, V^T
+    expect += B * ((-(-f // 256) * 256) - f) * C * 2   # f's last slab is whole
+    assert expect <= n <= expect + 9 * 256
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=0), UNSUPPORTED),                       # sequence padding
+    (dict(seq_len=2), INVALID),                         # one token per step
+    (dict(w0_batch_stride=2560 * 9728), INVALID),       # W_state is [B, d, f]
+    (dict(conv_k=0), INVALID)])
+def test_decode_descriptor_checks(L, kw, code):
+    st, _ = decode_size(L, decode_desc(**kw))
+    assert st == code, (kw, st, L.ttt_last_error())
+
+
+def decode_step(L, desc, p, pos=0, eta=1e-3, bytes_=1 << 62):
+    # h, x0, Wg, Wu, taps, W_target, eta, chunk, pos, W_state, dstate, bytes, o
+    return L.ttt_decode_step(ctypes.byref(desc), p[0], p[1], p[2], p[3], p[4], p[5],
+                             ctypes.c_float(eta), 1024, pos, p[6], p[9],
+                             ctypes.c_size_t(bytes_), p[7], None)
+
+
+def test_decode_step_validates_before_launch(L):
+    p = good_ptrs()
+    desc = decode_desc()
+    assert decode_step(L, desc, p, pos=-1) == INVALID
+    assert decode_step(L, desc, p, eta=float("nan")) == INVALID
+    _, need = decode_size(L, desc)
+    assert decode_step(L, desc, p, bytes_=need - 1) == WORKSPACE
+    q = list(p)
+    q[7] = p[0]                                         # o is h
+    assert decode_step(L, desc, q) == ALIAS
+    q = list(p)
+    q[6] = p[2]                                         # W_state is Wg
+    assert decode_step(L, desc, q) == ALIAS
+    q = list(p)
+    q[6] = None
+    assert decode_step(L, desc, q) == INVALID
+    assert L.ttt_decode_begin(ctypes.byref(desc), 1024, p[6], p[9], ctypes.c_size_t(need - 1),
+                              None) == WORKSPACE
+    assert L.ttt_decode_begin(ctypes.byref(decode_desc(flags=0)), 1024, p[6], p[9],
+                              ctypes.c_size_t(1 << 62), None) == UNSUPPORTED
