@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule prefix|running] [--no-cpu-baseline]
-                    [--variant plain|packed|clipped|continue]
+                    [--variant plain|packed|clipped|continue|decode]
     python bench.py --summarize DIR [--fetch DIR2 --write DIR3]
                     --summary-out FILE.md --command "..."
 
@@ -16,7 +16,8 @@ target, update with per-chunk snapshots, apply), with inputs resident in HBM.
 (ttt_layer_forward_packed, the sequence cut into --docs equal documents),
 clipped (ttt_layer_forward_clipped, limit --clip) or continue
 (ttt_layer_forward_continue: an fp32 state updated in place and K - 1
-look-ahead rows).
+look-ahead rows) or decode (ttt_decode_step token by token with chunk-local
+padding; one step is one chunk of C tokens, the chunk's update included).
 Prints one JSON line: tokens/s for the step, the per-kernel device times
 (HIP events recorded by the library around each launch, on the stream it
 launches on), the roofline of the dominant kernel, and the CPU oracle timed
@@ -71,6 +72,12 @@ def kernel_work(name, cfg, T_pad):
         return "hbm", 4.0 * d * d
     if name == "pack_weights":  # one of W_g / W_u per launch: read d*f, write the packed copy
         return "hbm", 2.0 * d * f + 2.0 * d * (-(-f // 128) * 128)
+    # decode, one launch per token, C tokens per step: W_g and W_u read once
+    # per token; each state's bf16 copy read once per token
+    if name == "decode_gate_up":
+        return "hbm", cfg.chunk * (2.0 * 2 * f * d + B * (4.0 * d + 4.0 * f))
+    if name == "decode_apply":
+        return "hbm", cfg.chunk * B * (2.0 * d * f + 2.0 * f + 2.0 * d)
     return None, None
 
 
@@ -110,7 +117,10 @@ def cpu_baseline(cfg, x, budget_s=15.0, variant="plain", clip=None, doc_len=None
     def run(j):
         n = j * C
         t0 = time.perf_counter()
-        if variant == "packed":
+        if variant == "decode":
+            ora.ttt_decode(x["H"][:1, :n], x["X0"][:1, :n], x["Wg"], x["Wu"], x["W_down0"],
+                           x["taps"], x["W_target"], cfg.eta, C)
+        elif variant == "packed":
             n = max(doc_len, n // doc_len * doc_len)
             ora.ttt_prefill_packed(x["H"][0, :n], x["X0"][0, :n], x["Wg"], x["Wu"],
                                    x["W_down0"], x["taps"], x["W_target"], cfg.eta, C,
@@ -222,7 +232,8 @@ def main():
     ap.add_argument("--workload", default=synth.BENCH_CONFIG, choices=sorted(synth.CONFIGS))
     ap.add_argument("--schedule", default="prefix", choices=["prefix", "running"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", default="plain", choices=["plain", "packed", "clipped", "continue"])
+    ap.add_argument("--variant", default="plain",
+                    choices=["plain", "packed", "clipped", "continue", "decode"])
     ap.add_argument("--docs", type=int, default=32, help="packed variant: equal documents")
     ap.add_argument("--clip", type=float, default=1e-3, help="clipped variant: norm limit")
     ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
@@ -262,7 +273,18 @@ def main():
                          0 if cfg.dtype == "bf16" else 1, 0,
                          2 if args.schedule == "running" else 4)
     doc_len = None
-    if args.variant == "packed":
+    if args.variant == "decode":
+        if (args.warmup + args.steps) * cfg.chunk > T:
+            raise SystemExit("--variant decode: (warmup + steps) chunks must fit the workload")
+        ddesc = ttt.make_desc(B, 1, d, f, cfg.conv_k, 0 if cfg.dtype == "bf16" else 1,
+                              0 if cfg.dtype == "bf16" else 1, 0, 1)
+        ws_bytes = ttt.decode_state_size(ddesc, cfg.chunk)
+        W_state = t["W_down0"].float().expand(B, d, f).contiguous()
+        O_tok = torch.empty((B, d), dtype=t["H"].dtype, device=dev)
+        H_tok = t["H"].transpose(0, 1).contiguous()     # [T, B, d]: each token's rows together
+        X0_tok = t["X0"].transpose(0, 1).contiguous()
+        pos = [0]
+    elif args.variant == "packed":
         if B != 1 or T % args.docs or (T // args.docs) % 64:
             raise SystemExit("--variant packed needs batch 1 and documents of a multiple of 64 tokens")
         doc_len = T // args.docs
@@ -279,8 +301,18 @@ def main():
         ws_bytes = ttt.workspace_size(desc, cfg.chunk)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
+    if args.variant == "decode":
+        ttt.decode_begin(W_state, cfg.chunk, ws, act_dtype=t["H"].dtype,
+                         weight_dtype=t["Wg"].dtype, conv_k=cfg.conv_k)
+
     def step():
-        if args.variant == "packed":
+        if args.variant == "decode":
+            for _ in range(cfg.chunk):
+                p = pos[0]
+                ttt.decode_step(H_tok[p], X0_tok[p], t["Wg"], t["Wu"], t["taps"],
+                                t["W_target"], cfg.eta, cfg.chunk, p, W_state, ws, out=O_tok)
+                pos[0] = p + 1
+        elif args.variant == "packed":
             ttt.layer_forward_packed(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
                                      t["W_target"], cfg.eta, cfg.chunk, starts,
                                      schedule=args.schedule, out=O, W_down_final=Wf,
@@ -324,8 +356,8 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.3f} s)",
           file=sys.stderr, flush=True)
 
-    tokens = B * T
-    flops = synth.algorithmic_flops(cfg)
+    tokens = B * (cfg.chunk if args.variant == "decode" else T)
+    flops = synth.algorithmic_flops(cfg) * tokens / (B * T)
     value = tokens / (ms_per_step / 1e3)
     tflops = flops / (ms_per_step / 1e3) / 1e12
     kernels = {n: {"launches_per_step": c / args.steps, "avg_ms": ms / c}

@@ -112,8 +112,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gate_up_kernel(
 // part[b][s][c] = sum over split s of the d_ff columns of z[b][j] * S_b[c][j].
 // A workgroup takes 32 rows and one split; its 4 waves share the split's
 // 16-column groups, each wave reading one 1 KB block of the slab per group
-// (32 rows x 16 columns), and the waves' sums meet in LDS.
-constexpr int kApplySplit = 4;
+// (32 rows x 16 columns), four groups at a time so that four loads are in
+// flight, and the waves' sums meet in LDS.
+constexpr int kApplySplit = 8;
 
 __global__ __launch_bounds__(kDecThreads) void decode_apply_kernel(
     const u16* __restrict__ zb, const u16* __restrict__ S, int64_t s_bstride, int d, int f,
@@ -127,17 +128,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_apply_kernel(
   const int g0 = split * per, g1 = min(groups, g0 + per);
   const u16* Sb = S + (int64_t)b * s_bstride;
   const u16* zr = zb + (int64_t)b * f;
-  float acc = 0.f;
-  for (int q = g0 + w; q < g1; q += 4) {
-    const int k = q * 16 + half * 8;
-    float sv[8], zv[8];
-    load8_bf16<false>(Sb, sb_offset<kSnapSlab>(row, k, f), sv);
-    load8_bf16<false>(zr, k, zv);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int q0 = g0 + w; q0 < g1; q0 += 16) {
+    float sv[4][8], zv[4][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(zv[e], sv[e], acc);
+    for (int u = 0; u < 4; ++u) {
+      const int q = min(q0 + 4 * u, g1 - 1);  // in bounds; a repeat adds nothing (below)
+      const int k = q * 16 + half * 8;
+      load8_bf16<false>(Sb, sb_offset<kSnapSlab>(row, k, f), sv[u]);
+      load8_bf16<false>(zr, k, zv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q0 + 4 * u < g1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u] = fmaf(zv[u][e], sv[u][e], acc[u]);
+      }
   }
-  acc += __shfl_xor(acc, 32);  // the two halves of the 16 columns
-  if (half == 0) red[w][lane] = acc;
+  float tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  tot += __shfl_xor(tot, 32);  // the two halves of the 16 columns
+  if (half == 0) red[w][lane] = tot;
   __syncthreads();
   if (threadIdx.x < 32) {
     const float s = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] +

@@ -358,7 +358,7 @@ def test_decode_state_size(L):
     expect = (B * d * f * 2            # bf16 copies of the states (d rows: whole 256-row slabs)
               + B * f * C * 2          # the open chunk's Z^T (f rows: whole slabs)
               + B * C * d * 2          # the open chunk's X0 rows
-              + B * f * 2 + B * 4 * d * 4      # z and the apply's partial sums
+              + B * f * 2 + B * 8 * d * 4      # z and the apply's partial sums (8 splits)
               + B * C * ld_y * 2 + d * ld_y * 2 + B * d * C * 2)   # Y, W_target^T, V^T
     expect += B * ((-(-f // 256) * 256) - f) * C * 2   # f's last slab is whole
     assert expect <= n <= expect + 9 * 256
