@@ -154,6 +154,43 @@ def _find(d, suffix):
     return hits[-1]
 
 
+N_XCD, SIMD_NUM = 8, 1024      # MI355X: GRBM counters sum over the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def mfma_section(args):
+    """MFMA utilisation per MFMA kernel from the counter run's last dispatch
+    of each: SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles of the dispatch
+    (GRBM_GUI_ACTIVE per XCD x SIMD_NUM), the clock those cycles imply over
+    the dispatch's duration, and the MFMA work (MOPS x 512 FLOPs)."""
+    last = {}
+    for r in _read_csv(_find(args.mfma, "counter_collection.csv")):
+        key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+        e = last.setdefault(key, {"dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+    per = {}
+    for (name, disp), e in sorted(last.items(), key=lambda kv: kv[0][1]):
+        if e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) > 0:
+            per[name] = e                     # the later dispatch wins
+    out = ["", "## MFMA utilisation (rocprofv3 --pmc)", "",
+           f"Command: `{args.mfma_command}`", "",
+           "Busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); the "
+           "clock is GRBM_GUI_ACTIVE / 8 over the dispatch's duration; FLOPs = MFMA MOPS x 512. "
+           "Last dispatch of each kernel (a timed step).", "",
+           "| kernel | ms | MFMA busy | clock GHz | MFMA TFLOP | TFLOP/s | of 2.5 PF at 2.4 GHz | of peak at that clock |",
+           "|---|---|---|---|---|---|---|---|"]
+    for name, e in per.items():
+        cyc = e["GRBM_GUI_ACTIVE"] / N_XCD
+        busy = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMD_NUM)
+        clk = cyc / (e["dur"] * 1e-9) / 1e9
+        flops = (e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) +
+                 e.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)) * 512
+        tfs = flops / (e["dur"] * 1e-9) / 1e12
+        out.append(f"| {name} | {e['dur'] / 1e6:.3f} | {busy * 100:.1f}% | {clk:.2f} | "
+                   f"{flops / 1e12:.3f} | {tfs:.0f} | {tfs / PEAK_BF16_TFLOPS * 100:.1f}% | "
+                   f"{tfs / (PEAK_BF16_TFLOPS * clk / 2.4) * 100:.1f}% |")
+    return out
+
+
 def summarize(args):
     """Write a markdown summary of rocprofv3 results (and, with --fetch and
     --write, the per-launch HBM traffic record used by the bench line)."""
@@ -218,6 +255,8 @@ def summarize(args):
                         "write_bytes": wr * w_fac}
         with open(TRAFFIC_FILE, "w") as fh:
             json.dump(rec, fh, indent=1)
+    if args.mfma:
+        lines += mfma_section(args)
     os.makedirs(os.path.dirname(args.summary_out) or ".", exist_ok=True)
     with open(args.summary_out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -239,6 +278,10 @@ def main():
     ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory")
+    ap.add_argument("--mfma", help="rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+                                   "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 "
+                                   "output directory")
+    ap.add_argument("--mfma-command", default="")
     ap.add_argument("--summary-out")
     ap.add_argument("--prof-steps", type=int, default=5, help="--steps of the profiled command")
     ap.add_argument("--prof-warmup", type=int, default=1, help="--warmup of the profiled command")
