@@ -78,3 +78,36 @@ def test_loose_clip_is_the_plain_layer(ttt):
     torch.cuda.synchronize()
     assert np.array_equal(O1, O2.float().cpu().numpy())
     assert np.array_equal(W1, W2.cpu().numpy())
+
+
+@pytest.mark.timeout(900)
+def test_clip_full_size_sampled(ttt):
+    """Qwen3-4B shape at 64k tokens with a limit of half the first chunk's
+    update norm (so it clips): the first three chunks' outputs against the
+    oracle's clipped run of those chunks (plus the conv's look-ahead rows);
+    the third sees two clipped updates. eta is 10x the config's, so that the
+    fast-weight term (about 3% of O at the config's eta) is large enough for
+    the check to tell clipped from unclipped. A limit above every update
+    norm gives the unclipped layer bit for bit."""
+    cfg = synth.CONFIGS["qwen3_4b_64k"]
+    x = synth.make_inputs(cfg)
+    C, eta, K, n = cfg.chunk, 10 * cfg.eta, cfg.conv_k, 3 * cfg.chunk
+    head = {k: (v[:, :n + K - 1] if k == "X0" else v[:, :n] if k == "H" else v)
+            for k, v in x.items()}
+    norms = chunk_update_norms(dict(head, X0=x["X0"][:, :n]), eta, C)
+    clip = 0.5 * norms[0]
+    O, _ = run_clip(ttt, x, cfg.dtype, eta, C, clip)
+    O_ref, _ = ora.ttt_prefill(head["H"], head["X0"], x["Wg"], x["Wu"], x["W_down0"],
+                               x["taps"], x["W_target"], eta, C, clip=clip)
+    O_free, _ = ora.ttt_prefill(head["H"], head["X0"], x["Wg"], x["Wu"], x["W_down0"],
+                                x["taps"], x["W_target"], eta, C)
+    e_o = rel(O[:, :n], O_ref)
+    gap = rel(O_free[:, 2 * C:n], O_ref[:, 2 * C:n])
+    e3 = rel(O[:, 2 * C:n], O_ref[:, 2 * C:n])
+    print(f"64k clipped: first chunks O {e_o:.2e}; third chunk {e3:.2e} "
+          f"(clipping moves it by {gap:.2e})", flush=True)
+    assert e_o <= O_TOL and e3 <= O_TOL
+    assert gap >= 5 * e3, "the check cannot tell the clipped outputs from the unclipped ones"
+    O_loose, W_loose = run_clip(ttt, x, cfg.dtype, eta, C, 1e30)
+    O_plain, W_plain = run_clip(ttt, x, cfg.dtype, eta, C, None)
+    assert np.array_equal(O_loose, O_plain) and np.array_equal(W_loose, W_plain)
