@@ -146,6 +146,20 @@ def test_schedules_agree_bitwise(ttt):
     assert np.array_equal(Op, Or) and np.array_equal(Wp, Wr)
 
 
+@pytest.mark.timeout(600)
+def test_schedules_agree_bitwise_full_size(ttt):
+    """The same at the Qwen3-4B 64k shape, where the running schedule's
+    per-chunk apply uses 64-token tiles and the prefix schedule's 256-token
+    ones: the tile width changes no sum."""
+    cfg = synth.CONFIGS["qwen3_4b_64k"]
+    x = synth.make_inputs(cfg)
+    t = to_dev(x, cfg.dtype)
+    del x
+    Op, Wp = run_gpu(ttt, t, cfg.eta, cfg.chunk, schedule="prefix")
+    Or, Wr = run_gpu(ttt, t, cfg.eta, cfg.chunk, schedule="running")
+    assert np.array_equal(Op, Or) and np.array_equal(Wp, Wr)
+
+
 def test_deterministic(ttt):
     cfg = synth.CONFIGS["mid_amp"]
     x = synth.make_inputs(cfg)
