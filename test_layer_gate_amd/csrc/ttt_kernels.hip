@@ -33,10 +33,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;      // small kernels
-#ifndef TTT_GEMM_WAVES
-#define TTT_GEMM_WAVES 8
-#endif
-constexpr int kGemmWaves = TTT_GEMM_WAVES;  // wave64s per GEMM workgroup (4 or 8)
+constexpr int kGemmWaves = 8;  // wave64s per GEMM workgroup, two per SIMD
 constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kMaxStages = 6;      // LDS stages of one operand (all but one in flight)
 constexpr int kRsrcWord3 = 0x00020000;
@@ -593,7 +590,6 @@ constexpr int K1_BM = 256, K1_BN = 2 * kWRows, K1_WGM = 2, K1_BK = kGateBK, K1_N
 constexpr int K1_LDZ = K1_BN / 2 + 8;  // row stride of the Z staging tile in LDS
 static_assert(K1_BM * K1_LDZ <= (K1_NSTA * K1_BM + K1_NSTB * K1_BN) * K1_BK,
               "Z staging fits the stages");
-static_assert(kGemmWaves == 4 || kGemmWaves == 8, "wave count");
 
 __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
     const u16* __restrict__ H, const u16* __restrict__ Wgp, const u16* __restrict__ Wup,
@@ -902,7 +898,7 @@ __global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT
 // at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
 // time; at every chunk start the state before that chunk is stored as a
 // bf16 snapshot (the exclusive prefix).
-constexpr int K3_BM = 256, K3_BN = 128, K3_WGM = kGemmWaves == 8 ? 4 : 2, K3_BK = 64,
+constexpr int K3_BM = 256, K3_BN = 128, K3_WGM = 4, K3_BK = 64,
               K3_NSTA = 4, K3_NSTB = 2;  // Z^T four stages deep, V^T two (160 KB)
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
@@ -1102,7 +1098,7 @@ constexpr int kApplyGroupM = 8;
 template <int BN>
 struct ApplyCfg {
   static constexpr int WGM =
-      kGemmWaves == 8 ? (BN == 256 ? 2 : (BN == 128 ? 4 : 8)) : (BN == 64 ? 4 : 2);
+      BN == 256 ? 2 : (BN == 128 ? 4 : 8);
   // With 256-token tiles, Z's stages run one step deeper than the
   // snapshot's (160 KB of LDS): 10% faster. Narrower tiles keep two each.
   static constexpr int BK = 64, NSTA = 2, NSTB = BN == 256 ? 3 : 2;
