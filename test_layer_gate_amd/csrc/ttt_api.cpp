@@ -687,6 +687,9 @@ ttt_status check_decode(const ttt_desc* desc, int32_t chunk, Geo* g, tttk::Dims*
   if (desc->w0_batch_stride != 0)
     return fail(TTT_ERR_INVALID_ARG, "w0_batch_stride must be 0: W_state is [batch, d, f]");
   *Dc = tttk::make_dims((int)g->B, chunk, (int)g->d, (int)g->f);
+  // A closing chunk runs the prefill kernels over the chunk's tokens.
+  if ((int64_t)g->B * (Dc->T_pad / 256) * (g->f / 64 + 1) >= (int64_t)1 << 31)
+    return fail(TTT_ERR_UNSUPPORTED, "chunk too large for one launch");
   return TTT_OK;
 }
 
