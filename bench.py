@@ -5,8 +5,11 @@
                     [--variant plain|packed|clipped|continue|decode]
     python bench.py --summarize DIR [--fetch DIR2 --write DIR3]
                     --summary-out FILE.md --command "..."
+    python bench.py --vendor-gemm
 
-The second form turns rocprofv3 output (a --kernel-trace --stats run, and
+The third form times torch.matmul (hipBLASLt) on the plain GEMM shapes of
+the layer's four contractions, as a vendor-library reference point (run
+only). The second form turns rocprofv3 output (a --kernel-trace --stats run, and
 optionally --pmc FETCH_SIZE / WRITE_SIZE runs) of the first form into the
 text summaries kept under profiles/.
 
@@ -263,6 +266,36 @@ def summarize(args):
     print("\n".join(lines))
 
 
+def vendor_gemm(cfg):
+    """torch.matmul (hipBLASLt) on the plain GEMMs with the layer's shapes
+    (bf16, fp32 accumulation): gate/up as one [T, d] x [2f, d]^T product, the
+    target, the apply with one weight for all chunks, and the update over
+    all tokens. Context only: the layer's kernels also fuse SiLU, write Z in
+    two layouts, read one state per chunk and store the snapshots."""
+    import torch
+    T, d, f = cfg.batch * cfg.seq_len, cfg.d_model, cfg.d_ff
+    out = {}
+    for name, M, N, K in [("gate_up", T, 2 * f, d), ("target", T, d, d), ("apply", T, d, f),
+                          ("update", f, d, T)]:
+        A = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        B = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+        for _ in range(2):
+            torch.matmul(A, B.t())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(A, B.t())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        out[name] = {"M": M, "N": N, "K": K, "ms": round(ms, 4),
+                     "tflops": round(2.0 * M * N * K / ms / 1e9, 1)}
+        del A, B
+    print(json.dumps({"vendor_gemm": "torch.matmul (hipBLASLt), bf16", "workload": cfg.name,
+                      "shapes": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +311,8 @@ def main():
     ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output directory")
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output directory")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time torch.matmul on the layer's GEMM shapes instead")
     ap.add_argument("--mfma", help="rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
                                    "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 "
                                    "output directory")
@@ -299,10 +334,14 @@ def main():
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
+    cfg = synth.CONFIGS[args.workload]
+    if args.vendor_gemm:
+        vendor_gemm(cfg)
+        return
+
     import torch
     import test_layer_gate_amd as ttt
 
-    cfg = synth.CONFIGS[args.workload]
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     x = synth.make_inputs(cfg)
     dev = torch.device("cuda:0")
