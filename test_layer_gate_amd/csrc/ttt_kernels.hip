@@ -33,8 +33,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;      // small kernels
-constexpr int kGemmWaves = 8;  // wave64s per GEMM workgroup, two per SIMD
-constexpr int kGemmThreads = 64 * kGemmWaves;
 constexpr int kMaxStages = 6;      // LDS stages of one operand (all but one in flight)
 constexpr int kRsrcWord3 = 0x00020000;
 enum { kRowMajor = 0, kSlab = 1 };  // LDS / HBM layouts of a GEMM operand (see Operand)
@@ -173,34 +171,50 @@ __device__ __forceinline__ Operand slab_blocked(const u16* m, int64_t K, int r0,
 // (waves * i + w) mod blocks; when the blocks do not divide evenly the extra
 // loads repeat a block, writing the same bytes to the same place. The
 // per-lane byte offsets are fixed; the K step enters as the scalar offset.
-template <int ROWS, int BK, int LAY>
+// The LDS side is all scalar: the stage's 32-bit LDS byte address plus the
+// wave's block offsets, so that setting M0 for a load is one scalar add
+// (no per-load conversion of a generic pointer, which cost two
+// readfirstlanes and a null check per load, issued ahead of the MFMAs).
+template <int ROWS, int BK, int LAY, int NW>
 struct DmaTile {
   using S = Swz<BK>;
   static constexpr int NB = ROWS / S::RPB;
-  static constexpr int NI = (NB + kGemmWaves - 1) / kGemmWaves;
+  static constexpr int NI = (NB + NW - 1) / NW;
+  static constexpr uint32_t kBlockBytes = S::RPB * BK * 2;  // 1 KB
   static_assert(ROWS % S::RPB == 0, "rows");
   static_assert(LAY == kRowMajor || (BK == 64 && ROWS % 32 == 0), "slab tiles");
   uint32_t voff[NI];
-  int block[NI];
+  uint32_t loff[NI];  // wave-uniform: LDS byte offset of load i within a stage
   uint32_t step_bytes;
   u32x4 rsrc;
+  // wave must be the same in every lane of the wave (a scalar).
   __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
     rsrc = make_rsrc(op.base, op.bytes);
     step_bytes = op.step_bytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      block[i] = (kGemmWaves * i + wave) % NB;
-      const int row = block[i] * S::RPB + lane / S::CPR;
+      const int block = (NW * i + wave) % NB;
+      loff[i] = (uint32_t)block * kBlockBytes;
+      const int row = block * S::RPB + lane / S::CPR;
       const int kc = (lane % S::CPR) ^ S::swz(row);
-      voff[i] = LAY == kSlab ? (uint32_t)block[i] * 1024 + lane * 16
+      voff[i] = LAY == kSlab ? (uint32_t)block * 1024 + lane * 16
                              : (uint32_t)row * op.row_bytes + kc * 16;
     }
   }
-  __device__ __forceinline__ void issue(u16* lds_region, int kt) const {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)kt * step_bytes);
+  // The scalar byte offset of K step kt.
+  __device__ __forceinline__ uint32_t soff(int kt) const {
+    return __builtin_amdgcn_readfirstlane((uint32_t)kt * step_bytes);
+  }
+  // Load i of K step kt (scalar offset so) into the stage at LDS byte
+  // address lds_stage.
+  __device__ __forceinline__ void issue_one(uint32_t lds_stage, uint32_t so, int i) const {
+    lds_dma_b128(rsrc, lds_stage + loff[i], voff[i], so);
+  }
+  // All loads of K step kt.
+  __device__ __forceinline__ void issue(uint32_t lds_stage, int kt) const {
+    const uint32_t so = soff(kt);
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      lds_dma_b128(rsrc, lds_addr_of(lds_region + block[i] * S::RPB * BK), voff[i], soff);
+    for (int i = 0; i < NI; ++i) issue_one(lds_stage, so, i);
   }
 };
 
@@ -291,11 +305,12 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TM][TN]) {
     for (int n = 0; n < TN; ++n) acc[m][n] = f32x16{};
 }
 
-// Wave layout of a BM x BN GEMM tile: WGM x WGN waves (WGM * WGN = 8), each
+// Wave layout of a BM x BN GEMM tile: WGM x WGN waves (WGM * WGN = NW), each
 // owning TM x TN MFMA tiles of 32 x 32.
-template <int BM, int BN, int WGM>
+template <int BM, int BN, int WGM, int NW>
 struct Layout {
-  static constexpr int WGN = kGemmWaves / WGM;
+  static constexpr int NWAVES = NW;
+  static constexpr int WGN = NW / WGM;
   static constexpr int TM = BM / (32 * WGM);
   static constexpr int TN = BN / (32 * WGN);
   static_assert(TM >= 1 && TN >= 1 && TM * 32 * WGM == BM && TN * 32 * WGN == BN, "layout");
@@ -321,12 +336,12 @@ struct Layout {
 // different k0 reach it at different times, so one of them misses in L2 and
 // the others then hit, instead of all waiting on the same miss. A hook
 // needs k0 = 0.
-template <int BM, int BN, int WGM, int BK, int NSTA, int NSTB, class Op, bool SPLITB, int ALAY,
-          int BLAY, class Hook>
+template <int NW, int BM, int BN, int WGM, int BK, int NSTA, int NSTB, class Op, bool SPLITB,
+          int ALAY, int BLAY, class Hook>
 __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0,
                                              const Operand& B1, int nk, f32x16* acc, u16* lds,
                                              const Hook& hook, int k0 = 0) {
-  using Lay = Layout<BM, BN, WGM>;
+  using Lay = Layout<BM, BN, WGM, NW>;
   constexpr int TM = Lay::TM, TN = Lay::TN, WGN = Lay::WGN;
   constexpr int BROWS = SPLITB ? BN / 2 : BN;
   constexpr int KSUB = BK / 16;  // MFMA K-substeps per stage
@@ -336,24 +351,30 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
   const int wm = w / WGN, wn = w % WGN;
   if (nk <= 0) return;
 
-  DmaTile<BM, BK, ALAY> ta;
-  DmaTile<BROWS, BK, BLAY> tb0;
-  DmaTile<SPLITB ? BN / 2 : 32, BK, BLAY> tb1;  // unused unless SPLITB
-  ta.init(A, w, lane);
-  tb0.init(B0, w, lane);
-  if constexpr (SPLITB) tb1.init(B1, w, lane);
+  // The wave index as a scalar, so that the loads' LDS offsets are scalars.
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  DmaTile<BM, BK, ALAY, NW> ta;
+  DmaTile<BROWS, BK, BLAY, NW> tb0;
+  DmaTile<SPLITB ? BN / 2 : 32, BK, BLAY, NW> tb1;  // unused unless SPLITB
+  ta.init(A, ws, lane);
+  tb0.init(B0, ws, lane);
+  if constexpr (SPLITB) tb1.init(B1, ws, lane);
 
   u16* const ldsb = lds + NSTA * BM * BK;
   auto stage_a = [&](int i) { return lds + i * (BM * BK); };
   auto stage_b = [&](int i) { return ldsb + i * (BN * BK); };
+  // The same stages as LDS byte addresses, for the loads.
+  const uint32_t lds0 = lds_addr_of(lds);
+  auto addr_a = [&](int i) { return lds0 + (uint32_t)(i * (BM * BK * 2)); };
+  auto addr_b = [&](int i) { return lds0 + (uint32_t)((NSTA * BM + i * BN) * BK * 2); };
   auto kblock = [&](int kt) {
     kt += k0;
     return kt >= nk ? kt - nk : kt;
   };
-  auto issue_a = [&](u16* st, int kt) { ta.issue(st, kblock(kt)); };
-  auto issue_b = [&](u16* st, int kt) {
-    tb0.issue(st, kblock(kt));
-    if constexpr (SPLITB) tb1.issue(st + (BN / 2) * BK, kblock(kt));
+  auto issue_a = [&](int st, int kt) { ta.issue(addr_a(st), kblock(kt)); };
+  auto issue_b = [&](int st, int kt) {
+    tb0.issue(addr_b(st), kblock(kt));
+    if constexpr (SPLITB) tb1.issue(addr_b(st) + (uint32_t)((BN / 2) * BK * 2), kblock(kt));
   };
 
   // Rows of this lane's fragments within the A and B stages.
@@ -387,15 +408,9 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
 #pragma unroll
     for (int n = 0; n < TN; ++n) fb[set][n] = lds_frag<BK, BLAY>(sb, brow[n], 2 * sub + khalf);
   };
-  auto mma_sub = [&](int set) {
-#pragma unroll
-    for (int m = 0; m < TM; ++m)
-#pragma unroll
-      for (int n = 0; n < TN; ++n)
-        acc[m * TN + n] = Op::mma(fa[set][m], fb[set][n], acc[m * TN + n]);
-  };
-  constexpr int NPA = DmaTile<BM, BK, ALAY>::NI;
-  constexpr int NPB = SPLITB ? 2 * DmaTile<BN / 2, BK, BLAY>::NI : DmaTile<BN, BK, BLAY>::NI;
+  constexpr int NPA = DmaTile<BM, BK, ALAY, NW>::NI;
+  constexpr int NPB =
+      SPLITB ? 2 * DmaTile<BN / 2, BK, BLAY, NW>::NI : DmaTile<BN, BK, BLAY, NW>::NI;
   constexpr int NPS = NPA + NPB;
   // Each step issues the loads of the operand with the shorter distance
   // first (A first when they agree). Stage kt + 1 is complete once the last
@@ -411,57 +426,81 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
   // let the stores of steps kt - R + 1 .. kt (issued after the loads of
   // stage kt + 1) stay in flight.
   unsigned stored = 0;
-  // One MFMA, then one fragment read while reads remain, then loads.
-  auto interleave = [&](int nvmem) {
-#pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < TM + TN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i < nvmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-  };
-  // The loads of one step, the shorter-distance operand's first.
-  auto issue_step = [&](int u, int kt) {
-    u16* ra = stage_a((u + RA) % NSTA);
-    u16* rb = stage_b((u + RB) % NSTB);
-    if constexpr (RA > RB) {
-      issue_b(rb, min(kt + RB, nk - 1));
-      issue_a(ra, min(kt + RA, nk - 1));
-    } else {
-      issue_a(ra, min(kt + RA, nk - 1));
-      issue_b(rb, min(kt + RB, nk - 1));
-    }
-  };
   // Loads and reads past the last stage are unconditional (clamped to the
   // last stage, in bounds, into released stages; reads of stale LDS) so a
   // step's MFMA section stays one basic block; nothing uses their results.
   // kt + 1 is taken mod the stage counts, so u (kt mod U) is compile-time.
   constexpr int U = NSTA == NSTB ? NSTA : NSTA * NSTB;
+
+  // The step is laid out by hand, in the order the waves issue it: after
+  // every MFMA one fragment read for the next substep and one load, with
+  // scheduling fences in between, so that neither the loads nor the reads
+  // bunch up between MFMAs and the MFMAs ahead of the stage barrier stay
+  // ahead of it (the barrier's LDS wait is then covered). The loads of step
+  // kt + 1 (A stage kt + 1 + RA, B stage kt + 1 + RB) go out right after the
+  // barrier of step kt, which released their stages, between the MFMAs of
+  // its last substep; the hook's stores of step kt + 1 follow them.
+  constexpr int NPB0 = DmaTile<BROWS, BK, BLAY, NW>::NI;
+  // Load j (in issue order) of the loads of step kt: A stage kt + RA and B
+  // stage kt + RB, the shorter-distance operand's first.
+  auto issue_load = [&](int u, int kt, int j) {
+    const int ra = (u + RA) % NSTA, rb = (u + RB) % NSTB;
+    auto a_load = [&](int i) { ta.issue_one(addr_a(ra), ta.soff(kblock(min(kt + RA, nk - 1))), i); };
+    auto b_load = [&](int i) {
+      const int kb = kblock(min(kt + RB, nk - 1));
+      if (i < NPB0)
+        tb0.issue_one(addr_b(rb), tb0.soff(kb), i);
+      else if constexpr (SPLITB)
+        tb1.issue_one(addr_b(rb) + (uint32_t)((BN / 2) * BK * 2), tb1.soff(kb), i - NPB0);
+    };
+    if constexpr (RA > RB) {
+      if (j < NPB) b_load(j); else a_load(j - NPB);
+    } else {
+      if (j < NPA) a_load(j); else b_load(j - NPA);
+    }
+  };
+  // Fragment read r (A fragments first, then B) of substep sub of the stage
+  // (sa, sb) into set.
+  auto read_frag = [&](const u16* sa, const u16* sb, int sub, int set, int r) {
+    if (r < TM)
+      fa[set][r] = lds_frag<BK, ALAY>(sa, arow[r], 2 * sub + khalf);
+    else
+      fb[set][r - TM] = lds_frag<BK, BLAY>(sb, brow[r - TM], 2 * sub + khalf);
+  };
+  // The MFMAs of fragment set `set`, each followed by one read of substep
+  // rsub of (sa, sb) into rset and, while nload remain, one load of step
+  // lkt (lu = lkt mod U).
+  auto mma_sub_sched = [&](int set, const u16* sa, const u16* sb, int rsub, int rset, int lu,
+                           int lkt, int nload) {
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {
+      acc[i] = Op::mma(fa[set][i / TN], fb[set][i % TN], acc[i]);
+      if (i < TM + TN) read_frag(sa, sb, rsub, rset, i);
+      if (i < nload) issue_load(lu, lkt, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = TM * TN; i < TM + TN; ++i) read_frag(sa, sb, rsub, rset, i);
+#pragma unroll
+    for (int i = TM * TN; i < nload; ++i) issue_load(lu, lkt, i);
+  };
   auto step = [&](int u, int kt) {
     const u16* ca = stage_a(u % NSTA);
     const u16* cb = stage_b(u % NSTB);
-    issue_step(u, kt);
     if constexpr (NSH > 0) {
       asm volatile("" ::: "memory");  // the hook's stores go after the loads
       stored = (stored << 1) | (kt > 0 && hook(kt, acc) ? 1u : 0u);
     }
-    load_sub(ca, cb, 1, 1);
-    mma_sub(0);
-    interleave(NPS);
 #pragma unroll
-    for (int sub = 1; sub + 1 < KSUB; ++sub) {
-      load_sub(ca, cb, sub + 1, (sub + 1) & 1);
-      mma_sub(sub & 1);
-      interleave(0);
-    }
+    for (int sub = 0; sub + 1 < KSUB; ++sub)
+      mma_sub_sched(sub & 1, ca, cb, sub + 1, (sub + 1) & 1, 0, 0, 0);
     // Stage kt + 1 landed everywhere; stage kt released.
     if constexpr (NSH > 0)
       wait_and_barrier_var<WAIT, NSH, R>(__builtin_popcount(stored & ((1u << R) - 1)));
     else
       wait_and_barrier<WAIT>();
-    load_sub(stage_a((u + 1) % NSTA), stage_b((u + 1) % NSTB), 0, 0);
-    mma_sub((KSUB - 1) & 1);
-    interleave(0);
+    mma_sub_sched((KSUB - 1) & 1, stage_a((u + 1) % NSTA), stage_b((u + 1) % NSTB), 0, 0,
+                  (u + 1) % U, kt + 1, NPS);
   };
 
   hook(0, acc);
@@ -470,15 +509,18 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
 #pragma unroll
   for (int j = -RMAX; j < 0; ++j) {
     if constexpr (RA > RB) {
-      if (j + RB >= 0) issue_b(stage_b(j + RB), min(j + RB, nk - 1));
-      issue_a(stage_a(j + RA), min(j + RA, nk - 1));
+      if (j + RB >= 0) issue_b(j + RB, min(j + RB, nk - 1));
+      issue_a(j + RA, min(j + RA, nk - 1));
     } else {
-      if (j + RA >= 0) issue_a(stage_a(j + RA), min(j + RA, nk - 1));
-      if (j + RB >= 0) issue_b(stage_b(j + RB), min(j + RB, nk - 1));
+      if (j + RA >= 0) issue_a(j + RA, min(j + RA, nk - 1));
+      if (j + RB >= 0) issue_b(j + RB, min(j + RB, nk - 1));
     }
   }
   wait_and_barrier<WAIT>();
   load_sub(stage_a(0), stage_b(0), 0, 0);
+  // Step 0's loads; each later step's go out after the previous barrier.
+#pragma unroll
+  for (int j = 0; j < NPS; ++j) issue_load(0, 0, j);
   for (int kt = 0; kt < nk; kt += U) {
 #pragma unroll
     for (int i = 0; i < U; ++i)
@@ -486,15 +528,6 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
   }
   // Drain the trailing loads before the caller reuses LDS.
   wait_and_barrier<0>();
-}
-
-template <int BM, int BN, int WGM, int BK, int NST, class Op, bool SPLITB, int ALAY, int BLAY,
-          class Hook>
-__device__ __forceinline__ void gemm_core(const Operand& A, const Operand& B0, const Operand& B1,
-                                          int nk, f32x16* acc, u16* lds, const Hook& hook,
-                                          int k0 = 0) {
-  gemm_core_ab<BM, BN, WGM, BK, NST, NST, Op, SPLITB, ALAY, BLAY>(A, B0, B1, nk, acc, lds, hook,
-                                                                  k0);
 }
 
 // Output coordinates of register group q (registers 4q..4q+3) of MFMA tile
@@ -585,16 +618,16 @@ __device__ __forceinline__ int k_rotation(int tm, int tn, int nk) {
 // Waves 2 x 4: each wave owns 128 tokens x 32 columns of Wg and of Wu. The
 // weights come packed (Wgp / Wup: one contiguous slab per tile and K step).
 // The weights' stages run one step deeper than H's (160 KB of LDS): 1% faster.
-constexpr int K1_BM = 256, K1_BN = 2 * kWRows, K1_WGM = 2, K1_BK = kGateBK, K1_NSTA = 2,
-              K1_NSTB = 3;
+constexpr int K1_NW = 8, K1_BM = 256, K1_BN = 2 * kWRows, K1_WGM = 2, K1_BK = kGateBK,
+              K1_NSTA = 2, K1_NSTB = 3;
 constexpr int K1_LDZ = K1_BN / 2 + 8;  // row stride of the Z staging tile in LDS
 static_assert(K1_BM * K1_LDZ <= (K1_NSTA * K1_BM + K1_NSTB * K1_BN) * K1_BK,
               "Z staging fits the stages");
 
-__global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
+__global__ __launch_bounds__(64 * K1_NW) void gate_up_kernel(
     const u16* __restrict__ H, const u16* __restrict__ Wgp, const u16* __restrict__ Wup,
     u16* __restrict__ Z, u16* __restrict__ ZT, Dims g, int tiles_m, int tiles_n) {
-  using L = Layout<K1_BM, K1_BN, K1_WGM>;
+  using L = Layout<K1_BM, K1_BN, K1_WGM, K1_NW>;
   constexpr int NG = L::TN / 2;  // gate tiles per wave (and as many up tiles)
   static_assert(NG >= 1 && L::TN == 2 * NG, "gate and up tiles pair up");
   TTT_GEMM_LDS_AB(lds, K1_BM, K1_BN, K1_BK, K1_NSTA, K1_NSTB)
@@ -605,7 +638,7 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
   zero_acc(acc);
   const int nk = d / K1_BK;
   const int64_t wslab = (int64_t)ti.tn * kWRows * d;  // tile tn's packed rows
-  gemm_core_ab<K1_BM, K1_BN, K1_WGM, K1_BK, K1_NSTA, K1_NSTB, Bf16Mma, true, kRowMajor,
+  gemm_core_ab<K1_NW, K1_BM, K1_BN, K1_WGM, K1_BK, K1_NSTA, K1_NSTB, Bf16Mma, true, kRowMajor,
                kRowMajor>(
       row_major<K1_BK>(H + ((int64_t)ti.b * g.T + t0) * d, d, min(K1_BM, g.T - t0)),
       blocked<K1_BK>(Wgp + wslab, kWRows, nk), blocked<K1_BK>(Wup + wslab, kWRows, nk), nk,
@@ -638,8 +671,8 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
   __syncthreads();
   constexpr int CHUNKS = K1_BM * (K1_BN / 2) / 8;  // 16-byte row segments in the tile
 #pragma unroll
-  for (int i = 0; i < CHUNKS / kGemmThreads; ++i) {
-    const int c = threadIdx.x + i * kGemmThreads;
+  for (int i = 0; i < CHUNKS / (64 * K1_NW); ++i) {
+    const int c = threadIdx.x + i * (64 * K1_NW);
     const int row = c >> 4, cc = c & 15;
     const u16* src = lds + row * K1_LDZ + cc * 8;
     const int t = t0 + row, jj = j0 + cc * 8;
@@ -652,13 +685,14 @@ __global__ __launch_bounds__(kGemmThreads) void gate_up_kernel(
 // ------------------------------------------------------ target GEMM (K2)
 // M = tokens (256), N = output channels (256), K = d; fp16 operands.
 // Y's stages run one step deeper than W_target's (160 KB of LDS): 5% faster.
-constexpr int K2_BM = 256, K2_BN = 256, K2_WGM = 2, K2_BK = 64, K2_NSTA = 3, K2_NSTB = 2;
+constexpr int K2_NW = 8, K2_BM = 256, K2_BN = 256, K2_WGM = 2, K2_BK = 64, K2_NSTA = 3,
+              K2_NSTB = 2;
 
-__global__ __launch_bounds__(kGemmThreads) void target_kernel(
+__global__ __launch_bounds__(64 * K2_NW) void target_kernel(
     const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
     u16* __restrict__ Vtok, u16* __restrict__ Vrow, float vscale, Dims g, int tiles_m,
     int tiles_n) {
-  using L = Layout<K2_BM, K2_BN, K2_WGM>;
+  using L = Layout<K2_BM, K2_BN, K2_WGM, K2_NW>;
   TTT_GEMM_LDS_AB(lds, K2_BM, K2_BN, K2_BK, K2_NSTA, K2_NSTB)
   const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K2_BM, c0 = ti.tn * K2_BN;
@@ -667,7 +701,7 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
   zero_acc(acc);
   const Operand wt = row_major<K2_BK>(WtT + (int64_t)c0 * g.ld_y, g.ld_y, min(K2_BN, d - c0));
   const int nk = d / K2_BK;
-  gemm_core_ab<K2_BM, K2_BN, K2_WGM, K2_BK, K2_NSTA, K2_NSTB, F16Mma, false, kRowMajor,
+  gemm_core_ab<K2_NW, K2_BM, K2_BN, K2_WGM, K2_BK, K2_NSTA, K2_NSTB, F16Mma, false, kRowMajor,
                kRowMajor>(
       row_major<K2_BK>(Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM), wt, wt, nk,
       &acc[0][0], lds, NoHook{}, k_rotation<4>(ti.tm, ti.tn, nk));
@@ -719,8 +753,8 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
     __syncthreads();
     constexpr int SEG = 128 * (K2_BN / 8);  // 16-byte row segments per pass
 #pragma unroll
-    for (int k = 0; k < SEG / kGemmThreads; ++k) {
-      const int sidx = threadIdx.x + k * kGemmThreads;
+    for (int k = 0; k < SEG / (64 * K2_NW); ++k) {
+      const int sidx = threadIdx.x + k * (64 * K2_NW);
       const int row = sidx / (K2_BN / 8), cc = sidx % (K2_BN / 8);
       const int t = t0 + pass * 128 + row, c = c0 + cc * 8;
       if (c < d)
@@ -742,7 +776,8 @@ __global__ __launch_bounds__(kGemmThreads) void target_kernel(
 // (K = d_ff, bf16) in KG_SPLIT parts of d_ff and writes the sum of its
 // elementwise product with the kept V tile to partial[b][chunk][pair][part]
 // (the sum is linear in the Z Gram, so the parts add up).
-constexpr int KG_B = 256, KG_WGM = 2, KG_SPLIT = 2, KG_NSTA = 2, KG_NSTB = 3;
+constexpr int KG_NW = 8, KG_B = 256, KG_WGM = 2, KG_SPLIT = 2, KG_NSTA = 2, KG_NSTB = 3;
+constexpr int KG_THREADS = 64 * KG_NW;
 
 struct GramTile {
   int b, i, pair, part, s0, u0, c1, weight;
@@ -781,16 +816,16 @@ __device__ __forceinline__ void gram_tile_acc(const u16* X, int64_t ld, int64_t 
                                               u16* lds) {
   const Operand xs = row_major<64>(X + ((int64_t)t.b * rows_b + t.s0) * ld + k0, ld, t.c1 - t.s0);
   const Operand xu = row_major<64>(X + ((int64_t)t.b * rows_b + t.u0) * ld + k0, ld, t.c1 - t.u0);
-  gemm_core_ab<KG_B, KG_B, KG_WGM, 64, KG_NSTA, KG_NSTB, Op, false, kRowMajor, kRowMajor>(
+  gemm_core_ab<KG_NW, KG_B, KG_B, KG_WGM, 64, KG_NSTA, KG_NSTB, Op, false, kRowMajor, kRowMajor>(
       xs, xu, xu, nk, acc, lds, NoHook{});
 }
 
-__global__ __launch_bounds__(kGemmThreads) void gram_v_kernel(const u16* __restrict__ Vrow,
+__global__ __launch_bounds__(KG_THREADS) void gram_v_kernel(const u16* __restrict__ Vrow,
                                                               float* __restrict__ gram, Dims g,
                                                               int chunk, int nblk, int npair,
                                                               int nchunks) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  using L = Layout<KG_B, KG_B, KG_WGM>;
+  using L = Layout<KG_B, KG_B, KG_WGM, KG_NW>;
   constexpr int NR = L::TM * L::TN * 16;  // accumulator registers per lane
   TTT_GEMM_LDS_AB(lds, KG_B, KG_B, 64, KG_NSTA, KG_NSTB)
   const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, 1);
@@ -801,7 +836,7 @@ __global__ __launch_bounds__(kGemmThreads) void gram_v_kernel(const u16* __restr
   // Lane-private layout [tile][register][thread]: each register's stores are
   // 256 contiguous bytes per wave; the second pass reads them in the same
   // lanes.
-  float* dst = gram + (((int64_t)t.b * nchunks + t.i) * npair + t.pair) * NR * kGemmThreads +
+  float* dst = gram + (((int64_t)t.b * nchunks + t.i) * npair + t.pair) * NR * KG_THREADS +
                threadIdx.x;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
@@ -809,15 +844,15 @@ __global__ __launch_bounds__(kGemmThreads) void gram_v_kernel(const u16* __restr
     for (int n = 0; n < L::TN; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        dst[((m * L::TN + n) * 16 + r) * kGemmThreads] = acc[m][n][r];
+        dst[((m * L::TN + n) * 16 + r) * KG_THREADS] = acc[m][n][r];
 #endif
 }
 
-__global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
+__global__ __launch_bounds__(KG_THREADS) void gram_norm_kernel(
     const u16* __restrict__ Z, const float* __restrict__ gram, float* __restrict__ partial,
     Dims g, int chunk, int nblk, int npair, int nchunks) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  using L = Layout<KG_B, KG_B, KG_WGM>;
+  using L = Layout<KG_B, KG_B, KG_WGM, KG_NW>;
   constexpr int NR = L::TM * L::TN * 16;
   TTT_GEMM_LDS_AB(lds, KG_B, KG_B, 64, KG_NSTA, KG_NSTB)
   float* wsum = reinterpret_cast<float*>(lds);  // per-wave sums, once the core is done
@@ -830,7 +865,7 @@ __global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
     zero_acc(acc);
     gram_tile_acc<Bf16Mma>(Z, g.ld_z, g.T, t, k_first * 64, nk, &acc[0][0], lds);
     const float* src = gram +
-                       (((int64_t)t.b * nchunks + t.i) * npair + t.pair) * NR * kGemmThreads +
+                       (((int64_t)t.b * nchunks + t.i) * npair + t.pair) * NR * KG_THREADS +
                        threadIdx.x;
 #pragma unroll
     for (int m = 0; m < L::TM; ++m)
@@ -838,7 +873,7 @@ __global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
       for (int n = 0; n < L::TN; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          sum = fmaf(acc[m][n][r], src[((m * L::TN + n) * 16 + r) * kGemmThreads], sum);
+          sum = fmaf(acc[m][n][r], src[((m * L::TN + n) * 16 + r) * KG_THREADS], sum);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
@@ -847,7 +882,7 @@ __global__ __launch_bounds__(kGemmThreads) void gram_norm_kernel(
   if (threadIdx.x == 0) {
     float tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < kGemmWaves; ++w) tot += wsum[w];
+    for (int w = 0; w < KG_NW; ++w) tot += wsum[w];
     partial[(((int64_t)t.b * nchunks + t.i) * npair + t.pair) * KG_SPLIT + t.part] =
         (float)t.weight * tot;
   }
@@ -898,7 +933,7 @@ __global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT
 // at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
 // time; at every chunk start the state before that chunk is stored as a
 // bf16 snapshot (the exclusive prefix).
-constexpr int K3_BM = 256, K3_BN = 128, K3_WGM = 4, K3_BK = 64,
+constexpr int K3_NW = 8, K3_BM = 256, K3_BN = 128, K3_WGM = 4, K3_BK = 64,
               K3_NSTA = 4, K3_NSTB = 2;  // Z^T four stages deep, V^T two (160 KB)
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
@@ -1023,13 +1058,13 @@ __device__ __forceinline__ uint32_t step_word(const BlockInfo& b) {
 constexpr int kMaxPackedSteps = 2048;  // K steps of a packed update launch (131072 tokens)
 
 template <bool WINIT_F32, bool PACKED>
-__global__ __launch_bounds__(kGemmThreads) void update_kernel(
+__global__ __launch_bounds__(64 * K3_NW) void update_kernel(
     const u16* __restrict__ ZT, const u16* __restrict__ VT, const void* __restrict__ Winit,
     int64_t winit_bstride, int64_t winit_ld, float acc_scale, u16* __restrict__ snap,
     int64_t snap_bstride, float* __restrict__ Wf, u16* __restrict__ shadow, Dims g,
     int tok_begin, int nk, int steps_per_chunk, const BlockInfo* __restrict__ blocks,
     int n_chunks, int tiles_m, int tiles_n) {
-  using L = Layout<K3_BM, K3_BN, K3_WGM>;
+  using L = Layout<K3_BM, K3_BN, K3_WGM, K3_NW>;
   constexpr int TM = L::TM, TN = L::TN;
   // The packed variant's step table takes 8 KB of LDS: three stages each.
   constexpr int NSTA = PACKED ? 3 : K3_NSTA, NSTB = PACKED ? 3 : K3_NSTB;
@@ -1038,7 +1073,7 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
   if constexpr (PACKED) {
     // This launch's block table, one word per K step (nk <= kMaxPackedSteps,
     // checked on the host); the pipeline's first barrier publishes it.
-    for (int k = threadIdx.x; k < nk; k += kGemmThreads)
+    for (int k = threadIdx.x; k < nk; k += 64 * K3_NW)
       steps[k] = step_word(blocks[tok_begin / K3_BK + k]);
     __syncthreads();
   }
@@ -1066,7 +1101,7 @@ __global__ __launch_bounds__(kGemmThreads) void update_kernel(
   static_assert(K3_BM == kZtSlab && K3_BN == kVtSlab && K3_BK == 64, "update tile = slabs");
   const Operand vt =
       slab_blocked<kVtSlab>(VT + ti.b * sb_elems<kVtSlab>(d, g.T_pad), g.T_pad, c0, tok_begin);
-  gemm_core_ab<K3_BM, K3_BN, K3_WGM, K3_BK, NSTA, NSTB, F16Mma, false, kSlab, kSlab>(
+  gemm_core_ab<K3_NW, K3_BM, K3_BN, K3_WGM, K3_BK, NSTA, NSTB, F16Mma, false, kSlab, kSlab>(
       slab_blocked<kZtSlab>(ZT + ti.b * sb_elems<kZtSlab>(f, g.T_pad), g.T_pad, j0, tok_begin),
       vt, vt, nk, &acc[0][0], lds, hook);
 
@@ -1097,6 +1132,7 @@ constexpr int kApplyGroupM = 8;
 
 template <int BN>
 struct ApplyCfg {
+  static constexpr int NW = 8;
   static constexpr int WGM =
       BN == 256 ? 2 : (BN == 128 ? 4 : 8);
   // With 256-token tiles, Z's stages run one step deeper than the
@@ -1105,7 +1141,7 @@ struct ApplyCfg {
 };
 
 template <int BN, bool OUT_F32>
-__global__ __launch_bounds__(kGemmThreads) void apply_kernel(
+__global__ __launch_bounds__(64 * ApplyCfg<BN>::NW) void apply_kernel(
     const u16* __restrict__ Z, const u16* __restrict__ snap, int64_t snap_bstride,
     int64_t snap_cstride, void* __restrict__ O, Dims g, int tok_begin, int tok_end, int chunk,
     const ApplyTile* __restrict__ tiles, int n_chunks, int tiles_m, int tiles_n) {
@@ -1113,7 +1149,7 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
   constexpr int BM = kSnapSlab, WGM = ApplyCfg<BN>::WGM, BK = ApplyCfg<BN>::BK,
                 NSTA = ApplyCfg<BN>::NSTA, NSTB = ApplyCfg<BN>::NSTB;
   static_assert(BK == 64, "the snapshot slab is one K step");
-  using L = Layout<BM, BN, WGM>;
+  using L = Layout<BM, BN, WGM, ApplyCfg<BN>::NW>;
   TTT_GEMM_LDS_AB(lds, BM, BN, BK, NSTA, NSTB)
   const TileIdx ti = tile_index(tiles_m, tiles_n, kApplyGroupM);
   const int c0 = ti.tm * BM;
@@ -1137,7 +1173,7 @@ __global__ __launch_bounds__(kGemmThreads) void apply_kernel(
   // width, so that every schedule and width sums each output in the same
   // order.
   const int nk = f / BK;
-  gemm_core_ab<BM, BN, WGM, BK, NSTA, NSTB, Bf16Mma, false, kSlab, kRowMajor>(
+  gemm_core_ab<ApplyCfg<BN>::NW, BM, BN, WGM, BK, NSTA, NSTB, Bf16Mma, false, kSlab, kRowMajor>(
       slab_blocked<kSnapSlab>(snap + ti.b * snap_bstride + i * snap_cstride, f, c0, 0), z, z, nk,
       &acc[0][0], lds, NoHook{}, k_rotation<kApplyGroupM>(ti.tm, t0 / 256, nk));
   const Frag<L> fr;
@@ -1388,7 +1424,7 @@ hipError_t launch_pack_weight(const void* W, bool w_f32, uint16_t* dst, const Di
 hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
                           uint16_t* Z, uint16_t* ZT, const Dims& g, hipStream_t s) {
   const int tiles_m = g.T_pad / K1_BM, tiles_n = ceil_div(g.f, K1_BN / 2);
-  gate_up_kernel<<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(H, Wgp, Wup, Z, ZT, g, tiles_m,
+  gate_up_kernel<<<tiles_m * tiles_n * g.B, 64 * K1_NW, 0, s>>>(H, Wgp, Wup, Z, ZT, g, tiles_m,
                                                               tiles_n);
   return hipGetLastError();
 }
@@ -1396,7 +1432,7 @@ hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
                          uint16_t* Vrow, float vscale, const Dims& g, hipStream_t s) {
   const int tiles_m = g.T_pad / K2_BM, tiles_n = ceil_div(g.d, K2_BN);
-  target_kernel<<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(Y, WtT, VT, Vtok, Vrow, vscale,
+  target_kernel<<<tiles_m * tiles_n * g.B, 64 * K2_NW, 0, s>>>(Y, WtT, VT, Vtok, Vrow, vscale,
                                                              g, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -1416,11 +1452,11 @@ hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gra
                              int chunk, int nchunks, float norm_factor, float clip,
                              hipStream_t s) {
   const int nblk = ceil_div(chunk, KG_B), npair = nblk * (nblk + 1) / 2;
-  gram_v_kernel<<<g.B * nchunks * npair, kGemmThreads, 0, s>>>(Vrow, gram, g, chunk, nblk, npair,
+  gram_v_kernel<<<g.B * nchunks * npair, KG_THREADS, 0, s>>>(Vrow, gram, g, chunk, nblk, npair,
                                                                nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  gram_norm_kernel<<<g.B * nchunks * npair * KG_SPLIT, kGemmThreads, 0, s>>>(
+  gram_norm_kernel<<<g.B * nchunks * npair * KG_SPLIT, KG_THREADS, 0, s>>>(
       Z, gram, partial, g, chunk, nblk, npair, nchunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1441,7 +1477,7 @@ static void update_launch(const uint16_t* ZT, const uint16_t* VT, const void* Wi
                           const Dims& g, int tok_begin, int nk, int steps_per_chunk,
                           const BlockInfo* blocks, int n_chunks, hipStream_t s) {
   const int tiles_m = ceil_div(g.f, K3_BM), tiles_n = ceil_div(g.d, K3_BN);
-  update_kernel<F32, PACKED><<<tiles_m * tiles_n * g.B, kGemmThreads, 0, s>>>(
+  update_kernel<F32, PACKED><<<tiles_m * tiles_n * g.B, 64 * K3_NW, 0, s>>>(
       ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap, snap_bstride, Wf, shadow, g,
       tok_begin, nk, steps_per_chunk, blocks, n_chunks, tiles_m, tiles_n);
 }
@@ -1485,11 +1521,11 @@ static void apply_dispatch(const uint16_t* Z, const uint16_t* snap, int64_t sb, 
   const int tiles_n = tiles != nullptr ? n_tiles : ceil_div(tok_end - tok_begin, BN);
   const int grid = tiles_m * tiles_n * g.B;
   if (out_f32)
-    apply_kernel<BN, true><<<grid, kGemmThreads, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin,
+    apply_kernel<BN, true><<<grid, 64 * ApplyCfg<BN>::NW, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin,
                                                      tok_end, chunk, tiles, n_chunks, tiles_m,
                                                      tiles_n);
   else
-    apply_kernel<BN, false><<<grid, kGemmThreads, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin,
+    apply_kernel<BN, false><<<grid, 64 * ApplyCfg<BN>::NW, 0, s>>>(Z, snap, sb, sc, O, g, tok_begin,
                                                       tok_end, chunk, tiles, n_chunks, tiles_m,
                                                       tiles_n);
 }
