@@ -250,18 +250,24 @@ struct TileIdx {
   int b, tm, tn;
 };
 
-// The workgroup id renumbered so that the workgroups of one XCD form one
-// contiguous range of ids.
-__device__ __forceinline__ int xcd_contiguous_id() {
-  const int nblk = gridDim.x;
-  const int lin = blockIdx.x;
-  const int xcd = lin & 7, idx = lin >> 3;
-  const int per = nblk >> 3, rem = nblk & 7;
+// Position p of a range of `count` workgroups that starts at a multiple of
+// 8 renumbered so that the workgroups of one XCD form one contiguous range
+// (workgroup ids go to the XCDs in turn, so p & 7 is the XCD).
+__device__ __forceinline__ int xcd_contiguous(int p, int count) {
+  const int xcd = p & 7, idx = p >> 3;
+  const int per = count >> 3, rem = count & 7;
   return xcd * per + min(xcd, rem) + idx;
 }
 
-__device__ __forceinline__ TileIdx tile_index(int tiles_m, int tiles_n, int group_m) {
-  int lin = xcd_contiguous_id();
+// The workgroup id renumbered so that the workgroups of one XCD form one
+// contiguous range of ids.
+__device__ __forceinline__ int xcd_contiguous_id() {
+  return xcd_contiguous(blockIdx.x, gridDim.x);
+}
+
+// Tile coordinates of the linear tile id lin: batch-major, then groups of
+// group_m tile rows, M fastest within a group.
+__device__ __forceinline__ TileIdx tile_coords(int lin, int tiles_m, int tiles_n, int group_m) {
   const int per_batch = tiles_m * tiles_n;
   TileIdx t;
   t.b = lin / per_batch;
@@ -274,6 +280,10 @@ __device__ __forceinline__ TileIdx tile_index(int tiles_m, int tiles_n, int grou
   t.tm = first_m + r % gm;
   t.tn = r / gm;
   return t;
+}
+
+__device__ __forceinline__ TileIdx tile_index(int tiles_m, int tiles_n, int group_m) {
+  return tile_coords(xcd_contiguous_id(), tiles_m, tiles_n, group_m);
 }
 
 // A K-step hook: called with the accumulators at the start of a K step,
@@ -929,12 +939,30 @@ __global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT
 }
 
 // ------------------------------------------ fast-weight update (K3)
-// M = d_ff (256), N = d_model (128), K = tokens; fp16 operands. acc starts
-// at acc_scale * state and absorbs (vscale V)^T Z one 64-token step at a
-// time; at every chunk start the state before that chunk is stored as a
-// bf16 snapshot (the exclusive prefix).
-constexpr int K3_NW = 8, K3_BM = 256, K3_BN = 128, K3_WGM = 4, K3_BK = 64,
-              K3_NSTA = 4, K3_NSTB = 2;  // Z^T four stages deep, V^T two (160 KB)
+// M = d_ff (256), N = d_model (256 or 128), K = tokens; fp16 operands. acc
+// starts at acc_scale * state and absorbs (vscale V)^T Z one 64-token step
+// at a time; at every chunk start the state before that chunk is stored as
+// a bf16 snapshot (the exclusive prefix).
+// A launch covers the state in 256 x 256 regions. It runs whole rounds (one
+// tile per compute unit) of wide 256 x 256 tiles and, when the regions left
+// over would fill at most half a round, splits each of them into two narrow
+// 256 x 128 tiles, so that the last round is one of narrow tiles instead of
+// a part-empty round of wide ones. Wide tiles read half the operand bytes per
+// MFMA that narrow ones do.
+constexpr int K3_NW = 8, K3_BM = 256, K3_BK = 64, K3_WIDE = 256, K3_NARROW = 128;
+template <int BN, bool PACKED>
+struct UpdCfg {
+  static constexpr int WGM = BN == K3_WIDE ? 2 : 4;
+  // Wide: Z^T three stages, V^T two; narrow: Z^T four, V^T two (160 KB
+  // each). The packed variant (narrow only) keeps 8 KB of LDS for its step
+  // table: three stages each.
+  static constexpr int NSTA = PACKED ? 3 : (BN == K3_WIDE ? 3 : 4);
+  static constexpr int NSTB = PACKED ? 3 : 2;
+};
+template <bool PACKED>
+constexpr int upd_lds_elems() {  // the stages of either width
+  return PACKED ? (3 * K3_BM + 3 * K3_NARROW) * K3_BK : 160 * 1024 / 2;
+}
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
 // into an sb<256> d x f bf16 matrix of `bytes` bytes (row c = d_model index,
@@ -1057,36 +1085,27 @@ __device__ __forceinline__ uint32_t step_word(const BlockInfo& b) {
 }
 constexpr int kMaxPackedSteps = 2048;  // K steps of a packed update launch (131072 tokens)
 
-template <bool WINIT_F32, bool PACKED>
-__global__ __launch_bounds__(64 * K3_NW) void update_kernel(
-    const u16* __restrict__ ZT, const u16* __restrict__ VT, const void* __restrict__ Winit,
-    int64_t winit_bstride, int64_t winit_ld, float acc_scale, u16* __restrict__ snap,
-    int64_t snap_bstride, float* __restrict__ Wf, u16* __restrict__ shadow, Dims g,
-    int tok_begin, int nk, int steps_per_chunk, const BlockInfo* __restrict__ blocks,
-    int n_chunks, int tiles_m, int tiles_n) {
-  using L = Layout<K3_BM, K3_BN, K3_WGM, K3_NW>;
-  constexpr int TM = L::TM, TN = L::TN;
-  // The packed variant's step table takes 8 KB of LDS: three stages each.
-  constexpr int NSTA = PACKED ? 3 : K3_NSTA, NSTB = PACKED ? 3 : K3_NSTB;
-  TTT_GEMM_LDS_AB(lds, K3_BM, K3_BN, K3_BK, NSTA, NSTB)
-  __shared__ uint32_t steps[PACKED ? kMaxPackedSteps : 1];
-  if constexpr (PACKED) {
-    // This launch's block table, one word per K step (nk <= kMaxPackedSteps,
-    // checked on the host); the pipeline's first barrier publishes it.
-    for (int k = threadIdx.x; k < nk; k += 64 * K3_NW)
-      steps[k] = step_word(blocks[tok_begin / K3_BK + k]);
-    __syncthreads();
-  }
-  const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
-  const int j0 = ti.tm * K3_BM, c0 = ti.tn * K3_BN;
+// One update tile: d_ff rows [j0, j0 + 256) and d_model columns
+// [c0, c0 + BN) of sequence b's state.
+template <int BN, bool WINIT_F32, bool PACKED>
+__device__ __forceinline__ void update_tile(
+    u16* lds, const uint32_t* steps, int b, int j0, int c0, const u16* __restrict__ ZT,
+    const u16* __restrict__ VT, const void* __restrict__ Winit, int64_t winit_bstride,
+    int64_t winit_ld, float acc_scale, u16* __restrict__ snap, int64_t snap_bstride,
+    float* __restrict__ Wf, u16* __restrict__ shadow, const Dims& g, int tok_begin, int nk,
+    int steps_per_chunk, int n_chunks) {
+  using C = UpdCfg<BN, PACKED>;
+  using L = Layout<K3_BM, BN, C::WGM, K3_NW>;
+  constexpr int TM = L::TM, TN = L::TN, NSTA = C::NSTA, NSTB = C::NSTB;
+  static_assert((NSTA * K3_BM + NSTB * BN) * K3_BK <= upd_lds_elems<PACKED>(), "stages fit");
   const int d = g.d, f = g.f;
   const Frag<L> fr;
   const int64_t chunk_stride = snap_elems(g);
   const float out_scale = 1.0f / acc_scale;
 
   const void* winit_b =
-      WINIT_F32 ? (const void*)(static_cast<const float*>(Winit) + ti.b * winit_bstride)
-                : (const void*)(static_cast<const u16*>(Winit) + ti.b * winit_bstride);
+      WINIT_F32 ? (const void*)(static_cast<const float*>(Winit) + b * winit_bstride)
+                : (const void*)(static_cast<const u16*>(Winit) + b * winit_bstride);
   const StateLoad<L, WINIT_F32> init{winit_b, winit_ld, j0, c0, d, f, acc_scale};
   const StateLoad<L, WINIT_F32, false> reset{winit_b, winit_ld, j0, c0, d, f, acc_scale};
   f32x16 acc[TM][TN];
@@ -1094,18 +1113,21 @@ __global__ __launch_bounds__(64 * K3_NW) void update_kernel(
 
   const SnapshotStore<L> snapshot{j0, c0, d, f, out_scale, (uint32_t)(chunk_stride * 2)};
   const ChunkSnapshots<L, WINIT_F32, PACKED> hook{
-      snapshot, reset, snap ? snap + ti.b * snap_bstride : nullptr, chunk_stride,
+      snapshot, reset, snap ? snap + b * snap_bstride : nullptr, chunk_stride,
       steps_per_chunk, steps, n_chunks};
   // Rows past d_ff / d_model in the last slabs are never written; they only
-  // feed output rows / columns that are not stored.
-  static_assert(K3_BM == kZtSlab && K3_BN == kVtSlab && K3_BK == 64, "update tile = slabs");
+  // feed output rows / columns that are not stored. A narrow tile reads the
+  // first or second 128 rows of a 256-row V^T slab: 16 contiguous KB per K
+  // step.
+  static_assert(K3_BM == kZtSlab && kVtSlab == K3_WIDE && BN <= kVtSlab && K3_BK == 64,
+                "update tile rows = slab rows");
   const Operand vt =
-      slab_blocked<kVtSlab>(VT + ti.b * sb_elems<kVtSlab>(d, g.T_pad), g.T_pad, c0, tok_begin);
-  gemm_core_ab<K3_NW, K3_BM, K3_BN, K3_WGM, K3_BK, NSTA, NSTB, F16Mma, false, kSlab, kSlab>(
-      slab_blocked<kZtSlab>(ZT + ti.b * sb_elems<kZtSlab>(f, g.T_pad), g.T_pad, j0, tok_begin),
+      slab_blocked<kVtSlab>(VT + b * sb_elems<kVtSlab>(d, g.T_pad), g.T_pad, c0, tok_begin);
+  gemm_core_ab<K3_NW, K3_BM, BN, C::WGM, K3_BK, NSTA, NSTB, F16Mma, false, kSlab, kSlab>(
+      slab_blocked<kZtSlab>(ZT + b * sb_elems<kZtSlab>(f, g.T_pad), g.T_pad, j0, tok_begin),
       vt, vt, nk, &acc[0][0], lds, hook);
 
-  float* wf_b = Wf + (int64_t)ti.b * d * f;
+  float* wf_b = Wf + (int64_t)b * d * f;
 #pragma unroll
   for (int m = 0; m < TM; ++m)
 #pragma unroll
@@ -1119,8 +1141,48 @@ __global__ __launch_bounds__(64 * K3_NW) void update_kernel(
               make_float4(acc[m][n][4 * q] * out_scale, acc[m][n][4 * q + 1] * out_scale,
                           acc[m][n][4 * q + 2] * out_scale, acc[m][n][4 * q + 3] * out_scale);
       }
-  if (shadow != nullptr) snapshot(shadow + (int64_t)ti.b * chunk_stride, &acc[0][0]);
-  (void)fr;
+  if (shadow != nullptr) snapshot(shadow + (int64_t)b * chunk_stride, &acc[0][0]);
+}
+
+// Workgroups [0, n_wide) take the wide tiles of regions [0, n_wide); the
+// rest take the two narrow halves of each remaining region (regions in
+// tile_coords order over regions_m x regions_n 256 x 256 regions per
+// sequence, group 4).
+template <bool WINIT_F32, bool PACKED>
+__global__ __launch_bounds__(64 * K3_NW) void update_kernel(
+    const u16* __restrict__ ZT, const u16* __restrict__ VT, const void* __restrict__ Winit,
+    int64_t winit_bstride, int64_t winit_ld, float acc_scale, u16* __restrict__ snap,
+    int64_t snap_bstride, float* __restrict__ Wf, u16* __restrict__ shadow, Dims g,
+    int tok_begin, int nk, int steps_per_chunk, const BlockInfo* __restrict__ blocks,
+    int n_chunks, int regions_m, int regions_n, int n_wide) {
+  __shared__ __attribute__((aligned(16))) u16 lds[upd_lds_elems<PACKED>()];
+  __shared__ uint32_t steps[PACKED ? kMaxPackedSteps : 1];
+  if constexpr (PACKED) {
+    // This launch's block table, one word per K step (nk <= kMaxPackedSteps,
+    // checked on the host); the pipeline's first barrier publishes it.
+    for (int k = threadIdx.x; k < nk; k += 64 * K3_NW)
+      steps[k] = step_word(blocks[tok_begin / K3_BK + k]);
+    __syncthreads();
+  }
+  if constexpr (!PACKED) {
+    if ((int)blockIdx.x < n_wide) {
+      const TileIdx t = tile_coords(xcd_contiguous(blockIdx.x, n_wide), regions_m, regions_n, 4);
+      update_tile<K3_WIDE, WINIT_F32, PACKED>(
+          lds, steps, t.b, t.tm * K3_BM, t.tn * K3_WIDE, ZT, VT, Winit, winit_bstride,
+          winit_ld, acc_scale, snap, snap_bstride, Wf, shadow, g, tok_begin, nk,
+          steps_per_chunk, n_chunks);
+      return;
+    }
+  }
+  // n_wide is a multiple of 8 whenever narrow tiles follow, so the XCD of a
+  // workgroup is that of its position in the narrow range.
+  const int id = xcd_contiguous(blockIdx.x - n_wide, gridDim.x - n_wide);
+  const TileIdx t = tile_coords(n_wide + id / 2, regions_m, regions_n, 4);
+  const int c0 = t.tn * K3_WIDE + (id & 1) * K3_NARROW;
+  if (c0 >= g.d) return;  // uniform: the half of a region past d_model
+  update_tile<K3_NARROW, WINIT_F32, PACKED>(
+      lds, steps, t.b, t.tm * K3_BM, c0, ZT, VT, Winit, winit_bstride, winit_ld, acc_scale,
+      snap, snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk, n_chunks);
 }
 
 // ------------------------------------------------------------ apply (K4)
@@ -1476,10 +1538,27 @@ static void update_launch(const uint16_t* ZT, const uint16_t* VT, const void* Wi
                           uint16_t* snap, int64_t snap_bstride, float* Wf, uint16_t* shadow,
                           const Dims& g, int tok_begin, int nk, int steps_per_chunk,
                           const BlockInfo* blocks, int n_chunks, hipStream_t s) {
-  const int tiles_m = ceil_div(g.f, K3_BM), tiles_n = ceil_div(g.d, K3_BN);
-  update_kernel<F32, PACKED><<<tiles_m * tiles_n * g.B, 64 * K3_NW, 0, s>>>(
+  // Wide tiles in whole rounds of one per compute unit; the regions left
+  // over become narrow tiles when they fill at most half a round (two narrow
+  // tiles then take about as long as one wide round would, with every
+  // compute unit busy). The packed variant uses narrow tiles only.
+  const int regions_m = ceil_div(g.f, K3_BM), regions_n = ceil_div(g.d, K3_WIDE);
+  const int regions = regions_m * regions_n * g.B;
+  int n_wide = 0;
+  if (!PACKED) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+      cus = 256;
+    cus &= ~7;  // whole XCD rounds
+    const int rem = regions % cus;
+    n_wide = (rem == 0 || 2 * rem > cus) ? regions : regions - rem;
+  }
+  const int grid = n_wide + 2 * (regions - n_wide);
+  update_kernel<F32, PACKED><<<grid, 64 * K3_NW, 0, s>>>(
       ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap, snap_bstride, Wf, shadow, g,
-      tok_begin, nk, steps_per_chunk, blocks, n_chunks, tiles_m, tiles_n);
+      tok_begin, nk, steps_per_chunk, blocks, n_chunks, regions_m, regions_n, n_wide);
 }
 
 hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Winit,

@@ -19,7 +19,7 @@
 //   Z   bf16 [B][T][ld_z]       gated activation, token-major (the apply reads it)
 //   ZT  fp16 [B] x sb<256>(f x T_pad)   the same, feature-major, for the
 //                               update; tokens >= T are zero
-//   VT  fp16 [B] x sb<128>(d x T_pad)   vscale * V, feature-major; tokens >= T zero
+//   VT  fp16 [B] x sb<256>(d x T_pad)   vscale * V, feature-major; tokens >= T zero
 //   S   bf16 [B][k] x sb<256>(d x f)    per-chunk snapshots of the state
 //   Wgp, Wup  bf16 [f_pad/128][d/64][128][64]   W_g and W_u packed for the
 //                               gate/up GEMM: each (128 rows x 64 columns) block
@@ -35,7 +35,7 @@ namespace tttk {
 
 constexpr int kTokenPad = 256;
 constexpr int kZtSlab = 256;    // ZT slab rows = the update tile's M
-constexpr int kVtSlab = 128;    // VT slab rows = the update tile's N
+constexpr int kVtSlab = 256;    // VT slab rows = the wide update tile's N
 constexpr int kSnapSlab = 256;  // snapshot slab rows = the apply tile's M
 constexpr int kWRows = 128;   // W_g / W_u rows per packed slab = half the gate/up tile's N
 constexpr int kGateBK = 64;   // d_model elements per packed slab = one K step of gate/up

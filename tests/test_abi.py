@@ -72,7 +72,7 @@ def test_workspace_size_matches_layout(L):
     # Y, W_target^T, Z, Z^T and V^T, snapshots, packed W_g and W_u (whole
     # 128-row slabs)
     expect = (B * T * ld_y * 2 + d * ld_y * 2 + B * T * ld_f * 2 + B * sb(f, T, 256) * 2
-              + B * sb(d, T, 128) * 2 + B * k * sb(d, f, 256) * 2
+              + B * sb(d, T, 256) * 2 + B * k * sb(d, f, 256) * 2
               + 2 * (-(-f // 128) * 128) * d * 2)
     assert expect <= n <= expect + 16 * 256
     st, n_run = ws_size(L, qwen_desc(flags=bnd.FLAG_SCHED_RUNNING), 1024)
