@@ -545,11 +545,17 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
 template <class L>
 struct Frag {
   int wm, wn, lane;
-  __device__ __forceinline__ Frag() {
-    const int w = threadIdx.x >> 6;
+  // opaque: the thread index goes through an empty asm statement, so that
+  // the coordinates, and the addresses derived from them, are computed where
+  // they are used instead of being kept live across the K loop (for the
+  // update's hooks, which run inside it).
+  __device__ __forceinline__ explicit Frag(bool opaque = false) {
+    int t = threadIdx.x;
+    if (opaque) asm volatile("" : "+v"(t));
+    const int w = t >> 6;
     wm = w / L::WGN;
     wn = w % L::WGN;
-    lane = threadIdx.x & 63;
+    lane = t & 63;
   }
   __device__ __forceinline__ int row(int m, int q) const {
     return wm * L::TM * 32 + m * 32 + 8 * q + 4 * (lane >> 5);
@@ -948,16 +954,16 @@ __global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT
 // over would fill at most half a round, splits each of them into two narrow
 // 256 x 128 tiles, so that the last round is one of narrow tiles instead of
 // a part-empty round of wide ones. Wide tiles read half the operand bytes per
-// MFMA that narrow ones do.
+// MFMA that narrow ones do. Both the plain and the packed variant do this.
 constexpr int K3_NW = 8, K3_BM = 256, K3_BK = 64, K3_WIDE = 256, K3_NARROW = 128;
 template <int BN, bool PACKED>
 struct UpdCfg {
   static constexpr int WGM = BN == K3_WIDE ? 2 : 4;
   // Wide: Z^T three stages, V^T two; narrow: Z^T four, V^T two (160 KB
-  // each). The packed variant (narrow only) keeps 8 KB of LDS for its step
-  // table: three stages each.
-  static constexpr int NSTA = PACKED ? 3 : (BN == K3_WIDE ? 3 : 4);
-  static constexpr int NSTB = PACKED ? 3 : 2;
+  // each). The packed variant keeps 8 KB of LDS for its step table: two
+  // stages each when wide (128 KB), three each when narrow (144 KB).
+  static constexpr int NSTA = PACKED ? (BN == K3_WIDE ? 2 : 3) : (BN == K3_WIDE ? 3 : 4);
+  static constexpr int NSTB = PACKED ? (BN == K3_WIDE ? 2 : 3) : 2;
 };
 template <bool PACKED>
 constexpr int upd_lds_elems() {  // the stages of either width
@@ -971,14 +977,16 @@ constexpr int upd_lds_elems() {  // the stages of either width
 // exactly kStores of them. They are streaming, system-scope stores (nt sc1):
 // the apply reads the snapshots only after this kernel, and keeping them out
 // of the way of the operand stream measured 4% faster.
-template <class L>
+// OPQ: the addresses are computed at each call (Frag opaque), for the
+// packed update, whose hook otherwise keeps them live across the K loop.
+template <class L, bool OPQ = false>
 struct SnapshotStore {
   static constexpr int kStores = L::TM * L::TN * 2;
   int j0, c0, d, f;
   float out_scale;
   uint32_t bytes;
   __device__ __forceinline__ void operator()(u16* dst, const f32x16* acc) const {
-    const Frag<L> fr;
+    const Frag<L> fr(OPQ);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(dst, 0, (int)bytes, kRsrcWord3);
     const uint32_t drop = bytes;
@@ -1005,14 +1013,14 @@ struct SnapshotStore {
 // drop it), so that they are issued back to back and waited for once; this
 // needs registers for all of them, so inside the K loop (the packed
 // update's reset) the per-element conditional form is used instead.
-template <class L, bool F32, bool BATCHED = true>
+template <class L, bool F32, bool BATCHED = true, bool OPQ = false>
 struct StateLoad {
   const void* W;
   int64_t ld;
   int j0, c0, d, f;
   float acc_scale;
   __device__ __forceinline__ void operator()(f32x16* acc) const {
-    const Frag<L> fr;
+    const Frag<L> fr(OPQ);
 #pragma unroll
     for (int m = 0; m < L::TM; ++m)
 #pragma unroll
@@ -1052,9 +1060,9 @@ struct StateLoad {
 // the K loop.
 template <class L, bool F32, bool PACKED>
 struct ChunkSnapshots {
-  static constexpr int kStores = SnapshotStore<L>::kStores;
-  SnapshotStore<L> store;
-  StateLoad<L, F32, false> reset;
+  static constexpr int kStores = SnapshotStore<L, PACKED>::kStores;
+  SnapshotStore<L, PACKED> store;
+  StateLoad<L, F32, false, PACKED> reset;
   u16* snap;  // this sequence's snapshots, or null
   int64_t chunk_stride;
   int steps_per_chunk;
@@ -1107,11 +1115,13 @@ __device__ __forceinline__ void update_tile(
       WINIT_F32 ? (const void*)(static_cast<const float*>(Winit) + b * winit_bstride)
                 : (const void*)(static_cast<const u16*>(Winit) + b * winit_bstride);
   const StateLoad<L, WINIT_F32> init{winit_b, winit_ld, j0, c0, d, f, acc_scale};
-  const StateLoad<L, WINIT_F32, false> reset{winit_b, winit_ld, j0, c0, d, f, acc_scale};
+  const StateLoad<L, WINIT_F32, false, PACKED> reset{winit_b, winit_ld, j0, c0, d, f,
+                                                     acc_scale};
   f32x16 acc[TM][TN];
   init(&acc[0][0]);
 
-  const SnapshotStore<L> snapshot{j0, c0, d, f, out_scale, (uint32_t)(chunk_stride * 2)};
+  const SnapshotStore<L, PACKED> snapshot{j0, c0, d, f, out_scale,
+                                          (uint32_t)(chunk_stride * 2)};
   const ChunkSnapshots<L, WINIT_F32, PACKED> hook{
       snapshot, reset, snap ? snap + b * snap_bstride : nullptr, chunk_stride,
       steps_per_chunk, steps, n_chunks};
@@ -1164,15 +1174,13 @@ __global__ __launch_bounds__(64 * K3_NW) void update_kernel(
       steps[k] = step_word(blocks[tok_begin / K3_BK + k]);
     __syncthreads();
   }
-  if constexpr (!PACKED) {
-    if ((int)blockIdx.x < n_wide) {
-      const TileIdx t = tile_coords(xcd_contiguous(blockIdx.x, n_wide), regions_m, regions_n, 4);
-      update_tile<K3_WIDE, WINIT_F32, PACKED>(
-          lds, steps, t.b, t.tm * K3_BM, t.tn * K3_WIDE, ZT, VT, Winit, winit_bstride,
-          winit_ld, acc_scale, snap, snap_bstride, Wf, shadow, g, tok_begin, nk,
-          steps_per_chunk, n_chunks);
-      return;
-    }
+  if ((int)blockIdx.x < n_wide) {
+    const TileIdx t = tile_coords(xcd_contiguous(blockIdx.x, n_wide), regions_m, regions_n, 4);
+    update_tile<K3_WIDE, WINIT_F32, PACKED>(
+        lds, steps, t.b, t.tm * K3_BM, t.tn * K3_WIDE, ZT, VT, Winit, winit_bstride, winit_ld,
+        acc_scale, snap, snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
+        n_chunks);
+    return;
   }
   // n_wide is a multiple of 8 whenever narrow tiles follow, so the XCD of a
   // workgroup is that of its position in the narrow range.
@@ -1541,20 +1549,17 @@ static void update_launch(const uint16_t* ZT, const uint16_t* VT, const void* Wi
   // Wide tiles in whole rounds of one per compute unit; the regions left
   // over become narrow tiles when they fill at most half a round (two narrow
   // tiles then take about as long as one wide round would, with every
-  // compute unit busy). The packed variant uses narrow tiles only.
+  // compute unit busy).
   const int regions_m = ceil_div(g.f, K3_BM), regions_n = ceil_div(g.d, K3_WIDE);
   const int regions = regions_m * regions_n * g.B;
-  int n_wide = 0;
-  if (!PACKED) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 8)
-      cus = 256;
-    cus &= ~7;  // whole XCD rounds
-    const int rem = regions % cus;
-    n_wide = (rem == 0 || 2 * rem > cus) ? regions : regions - rem;
-  }
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 8)
+    cus = 256;
+  cus &= ~7;  // whole XCD rounds
+  const int rem = regions % cus;
+  const int n_wide = (rem == 0 || 2 * rem > cus) ? regions : regions - rem;
   const int grid = n_wide + 2 * (regions - n_wide);
   update_kernel<F32, PACKED><<<grid, 64 * K3_NW, 0, s>>>(
       ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap, snap_bstride, Wf, shadow, g,
