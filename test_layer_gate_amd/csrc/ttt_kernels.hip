@@ -3,15 +3,17 @@
 // The four dense contractions (gate/up projection, target projection, the
 // fast-weight update and the apply) share one MFMA GEMM core:
 //   C[M][N] = sum_k A[m][k] * B[n][k],  both operands K-contiguous in HBM.
-// A workgroup is 8 wave64s (two per SIMD) in a WGM x WGN grid; each wave
-// owns a block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}, fp32
-// accumulation). K advances BK elements (32 or 64) per step through LDS
-// stages, NSTA of the A tile and NSTB of the B tile: buffer_load ... lds
-// moves each 16-byte chunk from HBM straight into LDS (no VGPR staging),
-// bounds-checked by the buffer descriptor (rows past the tile's valid rows
-// read as zero), while the MFMAs run on a stage that has landed; each
-// operand has all but one of its stages in flight. Fragments are read with
-// ds_read_b128 one K-substep ahead of the MFMAs that use them.
+// A workgroup is NW wave64s (8 in every kernel here, two per SIMD) in a
+// WGM x WGN grid; each wave owns a block of 32x32 MFMA tiles
+// (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation). K advances BK
+// elements (32 or 64) per step through LDS stages, NSTA of the A tile and
+// NSTB of the B tile: buffer_load ... lds moves each 16-byte chunk from HBM
+// straight into LDS (no VGPR staging), bounds-checked by the buffer
+// descriptor (rows past the tile's valid rows read as zero), while the MFMAs
+// run on a stage that has landed; each operand has all but one of its stages
+// in flight. Fragments are read with ds_read_b128 one K-substep ahead of the
+// MFMAs that use them; each step is laid out by hand (one read and one load
+// after each MFMA).
 //
 // Method sources: "论文精读：In-Place Test-Time Training" reading notes —
 // "In-Place 设计" (gated MLP), "Chunk-Wise 更新机制" (update equation),
