@@ -481,14 +481,38 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
   };
   // The MFMAs of fragment set `set`, each followed by one read of substep
   // rsub of (sa, sb) into rset and, while nload remain, one load of step
-  // lkt (lu = lkt mod U).
+  // lkt (lu = lkt mod U). sub >= 0: this is substep sub of step skt
+  // (su = skt mod U), which also issues that step's spread loads.
+  // Without a hook, and when the distances differ, the loads of step kt
+  // of the longer-distance operand do not go out after the barrier with the
+  // others: they are spread over the MFMAs of step kt's first KSUB - 1
+  // substeps, one every SPREAD MFMAs. Their stages were released by the
+  // barrier ending step kt - 1, the issue order (the shorter-distance
+  // operand's loads of step kt, then these) is unchanged and so are the
+  // waits. With the loads in one burst the waves stalled on issuing them
+  // (with 4 waves, one per SIMD, the MFMA units were 60% busy with the loads
+  // and 72% without); spread, gate/up, the target and the apply run 3-4%
+  // faster.
+  constexpr int NFIRST = (RA > RB ? NPB : NPA);
+  constexpr int NSECOND = NPS - NFIRST;
+  constexpr bool SPREADING = NSH == 0 && RA != RB;
+  constexpr int SLOTS = (KSUB - 1) * TM * TN;
+  constexpr int SPREAD =
+      SPREADING && NSECOND > 0 ? (SLOTS / NSECOND > 0 ? SLOTS / NSECOND : 1) : 1;
   auto mma_sub_sched = [&](int set, const u16* sa, const u16* sb, int rsub, int rset, int lu,
-                           int lkt, int nload) {
+                           int lkt, int nload, int sub = -1, int su = 0, int skt = 0) {
 #pragma unroll
     for (int i = 0; i < TM * TN; ++i) {
       acc[i] = Op::mma(fa[set][i / TN], fb[set][i % TN], acc[i]);
       if (i < TM + TN) read_frag(sa, sb, rsub, rset, i);
       if (i < nload) issue_load(lu, lkt, i);
+      if constexpr (SPREADING) {
+        if (sub >= 0) {
+          const int slot = sub * TM * TN + i;
+          if (slot % SPREAD == 0 && slot / SPREAD < NSECOND)
+            issue_load(su, skt, NFIRST + slot / SPREAD);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -505,14 +529,14 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
     }
 #pragma unroll
     for (int sub = 0; sub + 1 < KSUB; ++sub)
-      mma_sub_sched(sub & 1, ca, cb, sub + 1, (sub + 1) & 1, 0, 0, 0);
+      mma_sub_sched(sub & 1, ca, cb, sub + 1, (sub + 1) & 1, 0, 0, 0, sub, u, kt);
     // Stage kt + 1 landed everywhere; stage kt released.
     if constexpr (NSH > 0)
       wait_and_barrier_var<WAIT, NSH, R>(__builtin_popcount(stored & ((1u << R) - 1)));
     else
       wait_and_barrier<WAIT>();
     mma_sub_sched((KSUB - 1) & 1, stage_a((u + 1) % NSTA), stage_b((u + 1) % NSTB), 0, 0,
-                  (u + 1) % U, kt + 1, NPS);
+                  (u + 1) % U, kt + 1, SPREADING ? NFIRST : NPS);
   };
 
   hook(0, acc);
@@ -532,7 +556,7 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
   load_sub(stage_a(0), stage_b(0), 0, 0);
   // Step 0's loads; each later step's go out after the previous barrier.
 #pragma unroll
-  for (int j = 0; j < NPS; ++j) issue_load(0, 0, j);
+  for (int j = 0; j < (SPREADING ? NFIRST : NPS); ++j) issue_load(0, 0, j);
   for (int kt = 0; kt < nk; kt += U) {
 #pragma unroll
     for (int i = 0; i < U; ++i)
