@@ -483,19 +483,19 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
   // rsub of (sa, sb) into rset and, while nload remain, one load of step
   // lkt (lu = lkt mod U). sub >= 0: this is substep sub of step skt
   // (su = skt mod U), which also issues that step's spread loads.
-  // Without a hook, and when the distances differ, the loads of step kt
-  // of the longer-distance operand do not go out after the barrier with the
-  // others: they are spread over the MFMAs of step kt's first KSUB - 1
-  // substeps, one every SPREAD MFMAs. Their stages were released by the
-  // barrier ending step kt - 1, the issue order (the shorter-distance
-  // operand's loads of step kt, then these) is unchanged and so are the
-  // waits. With the loads in one burst the waves stalled on issuing them
-  // (with 4 waves, one per SIMD, the MFMA units were 60% busy with the loads
-  // and 72% without); spread, gate/up, the target and the apply run 3-4%
-  // faster.
+  // When the distances differ, the loads of step kt of the longer-distance
+  // operand do not go out after the barrier with the others: they are
+  // spread over the MFMAs of step kt's first KSUB - 1 substeps, one every
+  // SPREAD MFMAs. Their stages were released by the barrier ending step
+  // kt - 1. They follow the shorter-distance operand's loads of step kt and
+  // the hook's stores of step kt, so what a step's wait allows in flight
+  // (those stores and these loads) is the same set as with all loads in one
+  // burst. In one burst the waves stalled on issuing them (with 4 waves, one
+  // per SIMD, the MFMA units were 60% busy with the loads and 72% without);
+  // spread, gate/up, the target, the apply and the update run 3-5% faster.
   constexpr int NFIRST = (RA > RB ? NPB : NPA);
   constexpr int NSECOND = NPS - NFIRST;
-  constexpr bool SPREADING = NSH == 0 && RA != RB;
+  constexpr bool SPREADING = RA != RB;
   constexpr int SLOTS = (KSUB - 1) * TM * TN;
   constexpr int SPREAD =
       SPREADING && NSECOND > 0 ? (SLOTS / NSECOND > 0 ? SLOTS / NSECOND : 1) : 1;
