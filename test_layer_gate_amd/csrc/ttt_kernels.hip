@@ -111,7 +111,10 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
 // LDS read, which serialises the pipeline. They have no register results;
 // completion is tracked only by the explicit vmcnt waits in the pipeline.
 // M0 holds the LDS byte address of lane 0; one wait state separates the M0
-// write from the load.
+// write from the load. The compiler warns that M0 is a reserved register in
+// the clobber list; no compiler-generated code in these kernels reads or
+// writes M0 (every M0 access in their assembly is one of these loads'), so
+// there is nothing for the clobber to protect.
 __device__ __forceinline__ void lds_dma_b128(const u32x4& rsrc, uint32_t lds_addr,
                                              uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
