@@ -68,6 +68,7 @@ def check(x, O, W, eta, chunk, what, raw_w=True, a=0, W_in=None):
 
 
 @pytest.mark.parametrize("name,B,T", [("mid_amp", 1, 1024), ("mid_amp", 2, 1000),
+                                      ("mid_amp", 10, 300),  # past one pass of 8 sequences
                                       ("tiny", 2, 256), ("tiny_amp", 1, 200)])
 def test_decode_matches_oracle(ttt, name, B, T):
     """Whole sequences decoded token by token: every output, and the state
