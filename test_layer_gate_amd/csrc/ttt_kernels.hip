@@ -339,9 +339,10 @@ struct Layout {
 // gate and up projections); wave wn then owns the same TN/2 * 32 columns of
 // each, in acc[.][0, TN/2) (B0) and acc[.][TN/2, TN) (B1).
 // hook(kt, acc) runs at the start of K step kt, when acc holds steps < kt;
-// from step 1 on, after that step's stage loads are issued, so that its
-// stores need to be complete only R steps later (the waits in between allow
-// for them).
+// from step 1 on, after that step's loads of the shorter-distance operand
+// (issued right after the previous barrier) and before its spread loads of
+// the other operand, so that its stores need to be complete only R steps
+// later (the waits in between allow for them).
 // nk is the number of BK-wide K steps. lds holds NSTA stages of the A tile
 // (BM * BK elements each) followed by NSTB stages of the B tile (BN * BK);
 // the A loads run NSTA - 1 steps ahead and the B loads NSTB - 1, so the LDS
