@@ -1,0 +1,50 @@
+"""CPU checks of bench.py's host logic: the multi-GPU refusal, the
+algorithmic work it divides by the measured times, and the rule that a
+traffic record is only used for the kernel source it was taken on."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_layer_flops_match_the_method():
+    """The MFMA kernels of one step add up to 2*B*T*(4*d*f + d^2): gate/up
+    4*B*T*d*f, the target 2*B*T*d^2, the update and the apply 2*B*T*d*f
+    each (13.92 TFLOP at the Qwen3-4B 64k shape)."""
+    cfg = synth.CONFIGS["qwen3_4b_64k"]
+    B, T, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
+    total = 0.0
+    for k in ("gate_up", "target", "update_prefix", "apply"):
+        bound, work = bench.kernel_work(k, cfg, T)
+        assert bound == "mfma"
+        total += work
+    assert total == 2.0 * B * T * (4 * d * f + d * d)
+    assert abs(total / 1e12 - 13.92) < 0.01
+
+
+def test_traffic_record_is_tied_to_the_source(tmp_path, monkeypatch):
+    rec = {"kernel_source_sha256_16": bench.source_hash(), "workload": "w",
+           "kernels": {"w": {"gate_up": {"hbm_bytes_per_launch": 123.0}}}}
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
+    assert bench.measured_traffic("gate_up", "w") == 123.0
+    rec["kernel_source_sha256_16"] = "0" * 16
+    p.write_text(json.dumps(rec))
+    assert bench.measured_traffic("gate_up", "w") is None
+
