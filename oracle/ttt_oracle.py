@@ -40,8 +40,9 @@ tested by the pins in tests/test_oracle.py):
     several documents back to back, given by their start offsets. At each
     document start the state returns to W_down0 and the chunking restarts,
     and the conv reads nothing past the token's own document (nor past its
-    chunk, with chunk padding). The returned final state is the one after
-    the last document.
+    chunk, with chunk padding). Clipping, when asked for, acts on each chunk
+    of each document. The returned final state is the one after the last
+    document.
   * Decode (ttt_decode): one token at a time, with chunk-local conv padding
     only, the state stepped as soon as a chunk's last token is processed.
     With that padding it is the prefill computed token by token; the pages
@@ -159,7 +160,7 @@ def ttt_prefill(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
 
 
 def ttt_prefill_packed(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
-                       doc_starts, pad="sequence"):
+                       doc_starts, pad="sequence", clip=None):
     """Prefill of one packed sequence holding several documents.
 
     [iplex] §6: the fast weight is reset to the pretrained W_down at every
@@ -172,8 +173,11 @@ def ttt_prefill_packed(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
     each chunk.
 
     H [T, d]; X0 [T, d]; Wg, Wu [f, d]; W_down0 [d, f]; taps [K, d];
-    W_target [d, d]; doc_starts: increasing offsets, the first 0. Returns
-    O [T, d] and the state after the last document [d, f], float64.
+    W_target [d, d]; doc_starts: increasing offsets, the first 0. clip: None,
+    or the Frobenius-norm limit of each chunk's update delta, as in
+    ttt_prefill ([iplex] §6 norm clipping; a chunk here never spans two
+    documents). Returns O [T, d] and the state after the last document
+    [d, f], float64.
     """
     H, X0, taps = _f64(H), _f64(X0), _f64(taps)
     W0, Wt = _f64(W_down0), _f64(W_target)
@@ -217,7 +221,12 @@ def ttt_prefill_packed(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk,
             W = W0.copy()                       # document start: reset
         rows = slice(t, int(chunk_end[t]))
         O[rows] = Z[rows] @ W.T                 # apply with the pre-update state
-        W = W + eta * (V[rows].T @ Z[rows])     # then update
+        delta = eta * (V[rows].T @ Z[rows])
+        if clip is not None:
+            norm = np.linalg.norm(delta)        # Frobenius norm of the delta
+            if norm > clip:
+                delta = delta * (clip / norm)
+        W = W + delta                           # then update
         t = int(chunk_end[t])
     assert n_chunks == int(chunk_id[-1]) + 1
     return O, W

@@ -382,10 +382,11 @@ def pin_clip_each_delta():
 PACKED_DOCS = ([0, 13, 30, 31], [0, 8, 24], [0, 20])  # lengths below, at and above C = 8
 
 
-def run_packed(x, starts, pad="sequence", b=0):
+def run_packed(x, starts, pad="sequence", b=0, clip=None):
+    kw = {"clip": clip} if clip is not None else {}
     return ora.ttt_prefill_packed(x["H"][b], x["X0"][b], x["Wg"], x["Wu"], x["W_down0"],
                                   x["taps"], x["W_target"], x["eta"], x["chunk"], starts,
-                                  pad=pad)
+                                  pad=pad, **kw)
 
 
 def pin_packed_single_document():
@@ -414,6 +415,35 @@ def pin_packed_equals_documents():
                 O_ref, W_ref = run(sub, pad=pad)
                 _close(O[a:e], O_ref[0], what=f"document [{a},{e}) O ({pad})")
             _close(W, W_ref[0], what=f"final state after {starts} ({pad})")
+
+
+def pin_packed_clip_equals_documents():
+    """Packed documents with update-norm clipping equal the documents run one
+    by one through the clipped prefill (itself pinned chunk by chunk by
+    pin_clip_each_delta), at a limit between the chunks' update norms (the
+    median of the torch-computed norms), so that some chunks are clipped and
+    some are not."""
+    x = small_case(seed=24, B=1, T=40, eta=0.3)
+    C = x["chunk"]
+    starts = [0, 13, 30]
+    bounds = starts + [40]
+    norms = []
+    for a, e in zip(bounds, bounds[1:]):
+        Z = torch_z(x["H"][0, a:e], x["Wg"], x["Wu"])
+        V = torch_target(x["X0"][0, a:e], x["taps"], x["W_target"])
+        for c in range(0, e - a, C):
+            norms.append(x["eta"] * float(torch.linalg.matrix_norm(
+                _t(V[c:c + C]).T @ _t(Z[c:c + C]))))
+    clip = float(np.median(norms))
+    assert min(norms) < clip < max(norms)
+    O, W = run_packed(x, starts, clip=clip)
+    for a, e in zip(bounds, bounds[1:]):
+        sub = dict(x, H=x["H"][:, a:e], X0=x["X0"][:, a:e])
+        O_ref, W_ref = run(sub, clip=clip)
+        _close(O[a:e], O_ref[0], what=f"clipped document [{a},{e}) O")
+    _close(W, W_ref[0], what="clipped final state")
+    _, W_free = run_packed(x, starts)
+    assert not np.allclose(W, W_free), "the limit changed nothing"
 
 
 def pin_packed_isolation():
@@ -484,6 +514,6 @@ ALL_PINS = [pin_reduces_to_plain_mlp, pin_prefix_scan_form, pin_state_free_form,
             pin_chunk_causality, pin_batch_independence, pin_split_resume,
             pin_brute_force_scalars, pin_sampled_forms, pin_golden_ntp_fixture,
             pin_packed_single_document, pin_packed_equals_documents,
-            pin_packed_isolation, pin_clip_loose_is_plain, pin_clip_each_delta,
+            pin_packed_isolation, pin_packed_clip_equals_documents, pin_clip_loose_is_plain, pin_clip_each_delta,
             pin_decode_is_chunk_padded_prefill, pin_decode_pending_chunk,
             pin_decode_resumes_prefill]

@@ -87,12 +87,13 @@ def _conv_ignores_chunk(X0, taps, pad="sequence", chunk=None, n_out=None):
 _real_packed = ora.ttt_prefill_packed
 
 
-def _packed_variant(reset=True, conv_stops=True, chunks_from_doc=True):
+def _packed_variant(reset=True, conv_stops=True, chunks_from_doc=True, clips=True):
     """A copy of the packed recurrence with one knob turned away from the
     pages: no state reset at a document start, a conv that reads across the
-    boundary, or chunks counted from token 0 instead of the document start."""
+    boundary, chunks counted from token 0 instead of the document start, or
+    a clipping limit that is ignored."""
     def packed(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk, doc_starts,
-               pad="sequence"):
+               pad="sequence", clip=None):
         H, X0, taps = (np.asarray(a, np.float64) for a in (H, X0, taps))
         W0 = np.asarray(W_down0, np.float64)
         T, d = H.shape
@@ -124,7 +125,11 @@ def _packed_variant(reset=True, conv_stops=True, chunks_from_doc=True):
             if reset and a in starts:
                 W = W0.copy()
             O[a:e] = Z[a:e] @ W.T
-            W = W + eta * (V[a:e].T @ Z[a:e])
+            delta = eta * (V[a:e].T @ Z[a:e])
+            norm = np.linalg.norm(delta)
+            if clips and clip is not None and norm > clip:
+                delta = delta * (clip / norm)
+            W = W + delta
         return O, W
     return packed
 
@@ -197,6 +202,7 @@ MUTATIONS = {
     "packed_no_reset": ("ttt_prefill_packed", _packed_variant(reset=False)),
     "packed_conv_crosses_documents": ("ttt_prefill_packed", _packed_variant(conv_stops=False)),
     "packed_chunks_from_token_0": ("ttt_prefill_packed", _packed_variant(chunks_from_doc=False)),
+    "packed_clip_ignored": ("ttt_prefill_packed", _packed_variant(clips=False)),
     "inclusive_prefix_leak": ("ttt_prefill", _prefill_variant(order="update_first")),
     "skip_update": ("ttt_prefill", _prefill_variant(scale=0.0)),
     "normalise_by_chunk": ("ttt_prefill", _prefill_variant(scale=1.0 / 8)),
