@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule prefix|running] [--no-cpu-baseline]
-                    [--variant plain|packed|clipped|continue|decode]
+                    [--variant plain|packed|clipped|packed_clipped|continue|decode]
     python bench.py --summarize DIR [--fetch DIR2 --write DIR3]
                     --summary-out FILE.md --command "..."
     python bench.py --vendor-gemm
@@ -17,7 +17,8 @@ One step is one call of ttt_layer_forward on the whole workload (gate/up,
 target, update with per-chunk snapshots, apply), with inputs resident in HBM.
 --variant times the other entry points on the same workload instead: packed
 (ttt_layer_forward_packed, the sequence cut into --docs equal documents),
-clipped (ttt_layer_forward_clipped, limit --clip) or continue
+clipped (ttt_layer_forward_clipped, limit --clip), packed_clipped
+(ttt_layer_forward_packed_clipped: both at once), continue
 (ttt_layer_forward_continue: an fp32 state updated in place and K - 1
 look-ahead rows) or decode (ttt_decode_step token by token with chunk-local
 padding; one step is one chunk of C tokens, the chunk's update included).
@@ -123,11 +124,12 @@ def cpu_baseline(cfg, x, budget_s=15.0, variant="plain", clip=None, doc_len=None
         if variant == "decode":
             ora.ttt_decode(x["H"][:1, :n], x["X0"][:1, :n], x["Wg"], x["Wu"], x["W_down0"],
                            x["taps"], x["W_target"], cfg.eta, C)
-        elif variant == "packed":
+        elif variant in ("packed", "packed_clipped"):
             n = max(doc_len, n // doc_len * doc_len)
             ora.ttt_prefill_packed(x["H"][0, :n], x["X0"][0, :n], x["Wg"], x["Wu"],
                                    x["W_down0"], x["taps"], x["W_target"], cfg.eta, C,
-                                   list(range(0, n, doc_len)))
+                                   list(range(0, n, doc_len)),
+                                   clip=clip if variant == "packed_clipped" else None)
         else:
             ora.ttt_prefill(x["H"][:1, :n], x["X0"][:1, :n + K - 1], x["Wg"], x["Wu"],
                             x["W_down0"], x["taps"], x["W_target"], cfg.eta, C,
@@ -305,7 +307,8 @@ def main():
     ap.add_argument("--schedule", default="prefix", choices=["prefix", "running"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", default="plain",
-                    choices=["plain", "packed", "clipped", "continue", "decode"])
+                    choices=["plain", "packed", "clipped", "packed_clipped", "continue",
+                             "decode"])
     ap.add_argument("--docs", type=int, default=32, help="packed variant: equal documents")
     ap.add_argument("--clip", type=float, default=1e-3, help="clipped variant: norm limit")
     ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
@@ -366,12 +369,13 @@ def main():
         H_tok = t["H"].transpose(0, 1).contiguous()     # [T, B, d]: each token's rows together
         X0_tok = t["X0"].transpose(0, 1).contiguous()
         pos = [0]
-    elif args.variant == "packed":
+    elif args.variant in ("packed", "packed_clipped"):
         if B != 1 or T % args.docs or (T // args.docs) % 64:
             raise SystemExit("--variant packed needs batch 1 and documents of a multiple of 64 tokens")
         doc_len = T // args.docs
         starts = list(range(0, T, doc_len))
-        ws_bytes = ttt.packed_workspace_size(desc, cfg.chunk, starts)
+        pclip = args.clip if args.variant == "packed_clipped" else None
+        ws_bytes = ttt.packed_workspace_size(desc, cfg.chunk, starts, pclip)
     elif args.variant == "clipped":
         ws_bytes = ttt.clipped_workspace_size(desc, cfg.chunk, args.clip)
     elif args.variant == "continue":
@@ -394,10 +398,10 @@ def main():
                 ttt.decode_step(H_tok[p], X0_tok[p], t["Wg"], t["Wu"], t["taps"],
                                 t["W_target"], cfg.eta, cfg.chunk, p, W_state, ws, out=O_tok)
                 pos[0] = p + 1
-        elif args.variant == "packed":
+        elif args.variant in ("packed", "packed_clipped"):
             ttt.layer_forward_packed(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
                                      t["W_target"], cfg.eta, cfg.chunk, starts,
-                                     schedule=args.schedule, out=O, W_down_final=Wf,
+                                     schedule=args.schedule, clip=pclip, out=O, W_down_final=Wf,
                                      workspace=ws)
         elif args.variant == "continue":
             ttt.layer_forward_continue(t["H"], t["X0"], X0_next, t["Wg"], t["Wu"], W_state,

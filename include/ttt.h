@@ -168,6 +168,28 @@ ttt_status ttt_layer_forward_packed(const ttt_desc* desc,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* Packed documents with update-norm clipping (iplexlaw explainer §6, both
+ * the document reset and the norm clipping): ttt_layer_forward_packed,
+ * where each chunk's update is first scaled as in ttt_layer_forward_clipped.
+ * A chunk never spans two documents, so each document's chunks are clipped
+ * as they would be if that document ran alone.
+ *   clip_norm   > 0 and finite (TTT_ERR_INVALID_ARG otherwise)
+ * Arguments, layout, errors and workspace use as ttt_layer_forward_packed;
+ * the workspace (ttt_packed_clipped_workspace_size) adds the clipped path's
+ * buffers. */
+ttt_status ttt_packed_clipped_workspace_size(const ttt_desc* desc, int32_t chunk,
+                                             const int32_t* doc_starts, int32_t n_docs,
+                                             float clip_norm, size_t* bytes);
+ttt_status ttt_layer_forward_packed_clipped(const ttt_desc* desc,
+                                            const void* H, const void* X0,
+                                            const void* Wg, const void* Wu,
+                                            const void* W_down0, const void* conv_taps,
+                                            const void* W_target, float eta, int32_t chunk,
+                                            const int32_t* doc_starts, int32_t n_docs,
+                                            float clip_norm, void* O, float* W_down_final,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
 /* Continuation: the next segment of sequences whose earlier tokens went
  * through a previous call. The fast weight keeps changing over a whole
  * document and is reset only at its end (iplexlaw explainer §6 and §8), so

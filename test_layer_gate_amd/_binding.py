@@ -71,6 +71,12 @@ def lib() -> ctypes.CDLL:
     L.ttt_layer_forward_packed.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                            ctypes.c_int32, I32P, ctypes.c_int32, _P, _P, _P,
                                            _S, _P]
+    L.ttt_packed_clipped_workspace_size.argtypes = [DP, ctypes.c_int32, I32P, ctypes.c_int32,
+                                                    ctypes.c_float, ctypes.POINTER(_S)]
+    L.ttt_layer_forward_packed_clipped.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P,
+                                                   ctypes.c_float, ctypes.c_int32, I32P,
+                                                   ctypes.c_int32, ctypes.c_float, _P, _P, _P,
+                                                   _S, _P]
     L.ttt_continue_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
     L.ttt_layer_forward_continue.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
                                              _P, ctypes.c_float, ctypes.c_int32, _P, _P, _S,
@@ -84,6 +90,7 @@ def lib() -> ctypes.CDLL:
     for fn in ("ttt_workspace_size", "ttt_step_workspace_size", "ttt_layer_forward",
                "ttt_packed_workspace_size", "ttt_layer_forward_packed",
                "ttt_clipped_workspace_size", "ttt_layer_forward_clipped",
+               "ttt_packed_clipped_workspace_size", "ttt_layer_forward_packed_clipped",
                "ttt_continue_workspace_size", "ttt_layer_forward_continue",
                "ttt_decode_state_size", "ttt_decode_begin", "ttt_decode_step",
                "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
@@ -227,22 +234,28 @@ def _doc_array(doc_starts):
     return (ctypes.c_int32 * max(len(starts), 1))(*starts), len(starts)
 
 
-def packed_workspace_size(desc: Desc, chunk: int, doc_starts) -> int:
+def packed_workspace_size(desc: Desc, chunk: int, doc_starts, clip=None) -> int:
     arr, n_docs = _doc_array(doc_starts)
     n = _S(0)
-    _check(lib().ttt_packed_workspace_size(ctypes.byref(desc), chunk, arr, n_docs,
-                                           ctypes.byref(n)))
+    if clip is None:
+        _check(lib().ttt_packed_workspace_size(ctypes.byref(desc), chunk, arr, n_docs,
+                                               ctypes.byref(n)))
+    else:
+        _check(lib().ttt_packed_clipped_workspace_size(ctypes.byref(desc), chunk, arr, n_docs,
+                                                       ctypes.c_float(float(clip)),
+                                                       ctypes.byref(n)))
     return n.value
 
 
 def layer_forward_packed(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk,
-                         doc_starts, *, schedule=None, pad="sequence", out=None,
+                         doc_starts, *, schedule=None, pad="sequence", clip=None, out=None,
                          W_down_final=None, workspace=None, stream=None):
     """O, W_final for one packed sequence of documents (include/ttt.h,
     ttt_layer_forward_packed). H, X0 [T, d] or [1, T, d]; doc_starts: the
-    documents' first tokens, increasing from 0, multiples of 64. O has H's
-    shape; W_final is [d, f] (or [1, d, f] for 3-D H): the state after the
-    last document."""
+    documents' first tokens, increasing from 0, multiples of 64. clip: None
+    or each chunk's update-norm limit (ttt_layer_forward_packed_clipped). O
+    has H's shape; W_final is [d, f] (or [1, d, f] for 3-D H): the state
+    after the last document."""
     _require_cuda(H, X0, Wg, Wu, W_down0, conv_taps, W_target)
     squeeze = H.dim() == 2
     H3 = H.unsqueeze(0) if squeeze else H
@@ -268,17 +281,21 @@ def layer_forward_packed(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk
         raise ValueError("eta must be finite")
     desc = make_desc(1, T, d, f, K, act, wt, 0, _flags(schedule, pad))
     arr, n_docs = _doc_array(doc_starts)
-    ws_bytes = packed_workspace_size(desc, int(chunk), doc_starts)
+    ws_bytes = packed_workspace_size(desc, int(chunk), doc_starts, clip)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
     O = torch.empty_like(H3) if out is None else out.view(1, T, d)
     Wf = (torch.empty((1, d, f), dtype=torch.float32, device=H.device)
           if W_down_final is None else W_down_final.view(1, d, f))
     _require_cuda(O, Wf, workspace)
-    _check(lib().ttt_layer_forward_packed(
-        ctypes.byref(desc), _ptr(H3), _ptr(X3), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
-        _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk), arr, n_docs,
-        _ptr(O), _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream)))
+    args = (ctypes.byref(desc), _ptr(H3), _ptr(X3), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
+            _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk), arr, n_docs)
+    tail = (_ptr(O), _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream))
+    if clip is None:
+        _check(lib().ttt_layer_forward_packed(*args, *tail))
+    else:
+        _check(lib().ttt_layer_forward_packed_clipped(*args, ctypes.c_float(float(clip)),
+                                                      *tail))
     return (O[0], Wf[0]) if squeeze else (O, Wf)
 
 

@@ -58,10 +58,10 @@ template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   if (!g_timing.on) return launch();
   hipEvent_t a = take_event(), b = take_event();
-  if (a && b) hipEventRecord(a, s);
+  if (a && b) (void)hipEventRecord(a, s);
   hipError_t e = launch();
   if (a && b) {
-    hipEventRecord(b, s);
+    (void)hipEventRecord(b, s);
     g_timing.recs.push_back({name, a, b});
   }
   return e;
@@ -83,6 +83,7 @@ struct Geo {
   std::vector<Chunk> chunks;
   std::vector<tttk::BlockInfo> blocks;     // packed documents only: per 64-token block
   std::vector<tttk::ApplyTile> tiles;      // packed documents only: the apply's token tiles
+  std::vector<tttk::ChunkSpan> spans;      // packed documents only: each chunk's tokens
   float clip = 0.0f;                       // > 0: update-norm clipping limit
   bool resume = false;                     // continuation: fp32 state in place, look-ahead rows
   size_t act_bytes() const { return act_f32 ? 4 : 2; }
@@ -122,7 +123,8 @@ Layout forward_layout(const Geo& g) {
   L.wup = take(tttk::wpack_elems(D) * 2);
   if (!g.blocks.empty())
     L.blk = take(g.blocks.size() * sizeof(tttk::BlockInfo) +
-                 g.tiles.size() * sizeof(tttk::ApplyTile));
+                 g.tiles.size() * sizeof(tttk::ApplyTile) +
+                 g.spans.size() * sizeof(tttk::ChunkSpan));
   if (g.clip > 0.0f) {
     L.vrow = take(g.B * g.T_pad * D.ld_y * 2);
     L.gram = take(g.B * g.nchunks * tttk::clip_gram_floats((int)g.C) * 4);
@@ -264,6 +266,8 @@ ttt_status check_docs(const int32_t* doc_starts, int32_t n_docs, Geo* g) {
   }
   g->nchunks = (int64_t)g->chunks.size();
   for (int64_t b = (g->T + 63) / 64; b < nblk; ++b) g->blocks[b].chunk = (int32_t)g->nchunks - 1;
+  g->spans.clear();
+  for (const Chunk& c : g->chunks) g->spans.push_back({c.t0, c.t1});
   // The apply's token tiles start at every chunk start; a chunk's last tile
   // may be partial.
   const int bn = tttk::apply_tile_width(C);
@@ -433,21 +437,24 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
   const tttk::Dims& D = g.dims;
   const int64_t df = g.d * g.f;
 
-  // Packed documents: the block table and the apply's tile list go to the
-  // workspace first, in one asynchronous copy. Its host buffer must outlive
-  // the copy, which may run after this call returns: a host function
-  // enqueued behind the copy frees it.
+  // Packed documents: the block table, the apply's tile list and the chunk
+  // spans go to the workspace first, in one asynchronous copy. Its host
+  // buffer must outlive the copy, which may run after this call returns: a
+  // host function enqueued behind the copy frees it.
   const tttk::BlockInfo* blocks = nullptr;
   const tttk::ApplyTile* tiles = nullptr;
+  const tttk::ChunkSpan* spans = nullptr;
   if (!g.blocks.empty()) {
     const size_t nb = g.blocks.size() * sizeof(tttk::BlockInfo);
     const size_t nt = g.tiles.size() * sizeof(tttk::ApplyTile);
-    char* host = static_cast<char*>(std::malloc(nb + nt));
+    const size_t ns = g.spans.size() * sizeof(tttk::ChunkSpan);
+    char* host = static_cast<char*>(std::malloc(nb + nt + ns));
     if (host == nullptr) return fail(TTT_ERR_HIP, "document table: host allocation failed");
     std::memcpy(host, g.blocks.data(), nb);
     std::memcpy(host + nb, g.tiles.data(), nt);
+    std::memcpy(host + nb + nt, g.spans.data(), ns);
     char* dst = at<char>(workspace, L.blk);
-    hipError_t e = hipMemcpyAsync(dst, host, nb + nt, hipMemcpyHostToDevice, s);
+    hipError_t e = hipMemcpyAsync(dst, host, nb + nt + ns, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipLaunchHostFunc(s, [](void* p) { std::free(p); }, host);
     if (e != hipSuccess) {
       // The copy may be queued: let the stream drain before freeing.
@@ -457,6 +464,7 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
     }
     blocks = reinterpret_cast<const tttk::BlockInfo*>(dst);
     tiles = reinterpret_cast<const tttk::ApplyTile*>(dst + nb);
+    spans = reinterpret_cast<const tttk::ChunkSpan*>(dst + nb + nt);
   }
 
   // bf16 operands
@@ -508,7 +516,8 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
                tttk::launch_clip_scale(Z, Vrow, at<float>(workspace, L.gram),
                                        at<float>(workspace, L.partial),
                                        at<float>(workspace, L.scale), VT, D, (int)g.C,
-                                       (int)g.nchunks, std::fabs(eta) / vscale, g.clip, s));
+                                       (int)g.nchunks, spans, blocks, std::fabs(eta) / vscale,
+                                       g.clip, s));
   }
 
   const int64_t snap_cstride = tttk::snap_elems(D);
@@ -607,6 +616,35 @@ ttt_status ttt_layer_forward_packed(const ttt_desc* desc, const void* H, const v
   TTT_TRY(check_desc(desc, &g));
   TTT_TRY(check_chunk(chunk, &g));
   TTT_TRY(check_docs(doc_starts, n_docs, &g));
+  return forward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, O, W_down_final,
+                      workspace, workspace_bytes, stream);
+}
+
+ttt_status ttt_packed_clipped_workspace_size(const ttt_desc* desc, int32_t chunk,
+                                             const int32_t* doc_starts, int32_t n_docs,
+                                             float clip_norm, size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  TTT_TRY(check_docs(doc_starts, n_docs, &g));
+  TTT_TRY(check_clip(clip_norm, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = forward_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_forward_packed_clipped(const ttt_desc* desc, const void* H, const void* X0,
+                                            const void* Wg, const void* Wu, const void* W_down0,
+                                            const void* conv_taps, const void* W_target,
+                                            float eta, int32_t chunk, const int32_t* doc_starts,
+                                            int32_t n_docs, float clip_norm, void* O,
+                                            float* W_down_final, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  TTT_TRY(check_docs(doc_starts, n_docs, &g));
+  TTT_TRY(check_clip(clip_norm, &g));
   return forward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, O, W_down_final,
                       workspace, workspace_bytes, stream);
 }

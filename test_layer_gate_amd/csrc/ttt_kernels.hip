@@ -830,7 +830,8 @@ struct GramTile {
 };
 
 __device__ __forceinline__ GramTile gram_tile(const Dims& g, int chunk, int nblk, int npair,
-                                              int nchunks, int parts) {
+                                              int nchunks, int parts,
+                                              const ChunkSpan* __restrict__ spans) {
   GramTile t;
   int rest = blockIdx.x;
   t.part = rest % parts;
@@ -845,8 +846,8 @@ __device__ __forceinline__ GramTile gram_tile(const Dims& g, int chunk, int nblk
     ++sb;
   }
   tb += sb;
-  const int c0 = t.i * chunk;
-  t.c1 = min(g.T, c0 + chunk);
+  const int c0 = spans ? spans[t.i].t0 : t.i * chunk;
+  t.c1 = spans ? spans[t.i].t1 : min(g.T, c0 + chunk);
   t.s0 = c0 + sb * KG_B;
   t.u0 = c0 + tb * KG_B;
   t.weight = sb == tb ? 1 : 2;
@@ -866,15 +867,14 @@ __device__ __forceinline__ void gram_tile_acc(const u16* X, int64_t ld, int64_t 
       xs, xu, xu, nk, acc, lds, NoHook{});
 }
 
-__global__ __launch_bounds__(KG_THREADS) void gram_v_kernel(const u16* __restrict__ Vrow,
-                                                              float* __restrict__ gram, Dims g,
-                                                              int chunk, int nblk, int npair,
-                                                              int nchunks) {
+__global__ __launch_bounds__(KG_THREADS) void gram_v_kernel(
+    const u16* __restrict__ Vrow, float* __restrict__ gram, Dims g, int chunk, int nblk,
+    int npair, int nchunks, const ChunkSpan* __restrict__ spans) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using L = Layout<KG_B, KG_B, KG_WGM, KG_NW>;
   constexpr int NR = L::TM * L::TN * 16;  // accumulator registers per lane
   TTT_GEMM_LDS_AB(lds, KG_B, KG_B, 64, KG_NSTA, KG_NSTB)
-  const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, 1);
+  const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, 1, spans);
   if (t.u0 >= t.c1) return;  // uniform: blocks past a short last chunk add nothing
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
@@ -896,13 +896,13 @@ __global__ __launch_bounds__(KG_THREADS) void gram_v_kernel(const u16* __restric
 
 __global__ __launch_bounds__(KG_THREADS) void gram_norm_kernel(
     const u16* __restrict__ Z, const float* __restrict__ gram, float* __restrict__ partial,
-    Dims g, int chunk, int nblk, int npair, int nchunks) {
+    Dims g, int chunk, int nblk, int npair, int nchunks, const ChunkSpan* __restrict__ spans) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using L = Layout<KG_B, KG_B, KG_WGM, KG_NW>;
   constexpr int NR = L::TM * L::TN * 16;
   TTT_GEMM_LDS_AB(lds, KG_B, KG_B, 64, KG_NSTA, KG_NSTB)
   float* wsum = reinterpret_cast<float*>(lds);  // per-wave sums, once the core is done
-  const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, KG_SPLIT);
+  const GramTile t = gram_tile(g, chunk, nblk, npair, nchunks, KG_SPLIT, spans);
   const int steps = g.f / 64, per = (steps + KG_SPLIT - 1) / KG_SPLIT;
   const int k_first = t.part * per, nk = min(steps, k_first + per) - k_first;
   float sum = 0.f;
@@ -950,10 +950,12 @@ __global__ __launch_bounds__(kThreads) void clip_scale_kernel(const float* __res
   scale[idx] = nrm > (double)clip ? (float)((double)clip / nrm) : 1.0f;
 }
 
-// VT *= scale of each token's chunk (a 64-token slab lies in one chunk).
+// VT *= scale of each token's chunk (a 64-token slab lies in one chunk: the
+// block table's entry for a packed sequence, else token / chunk).
 __global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT,
                                                            const float* __restrict__ scale,
                                                            Dims g, int chunk, int nchunks,
+                                                           const BlockInfo* __restrict__ blocks,
                                                            int64_t n16) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n16) return;
@@ -961,7 +963,8 @@ __global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT
   const int b = (int)(e / per_b);
   const int64_t slab = (e % per_b) / (kVtSlab * 64);
   const int tok = (int)(slab % (g.T_pad / 64)) * 64;
-  const float sc = scale[(int64_t)b * nchunks + min(tok / chunk, nchunks - 1)];
+  const int ci = blocks ? blocks[tok / 64].chunk : min(tok / chunk, nchunks - 1);
+  const float sc = scale[(int64_t)b * nchunks + ci];
   if (sc == 1.0f) return;
   uint4 v = reinterpret_cast<uint4*>(VT)[i];
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -1549,15 +1552,16 @@ int64_t clip_gram_floats(int chunk) {
 
 hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gram,
                              float* partial, float* scale, uint16_t* VT, const Dims& g,
-                             int chunk, int nchunks, float norm_factor, float clip,
+                             int chunk, int nchunks, const ChunkSpan* spans,
+                             const BlockInfo* blocks, float norm_factor, float clip,
                              hipStream_t s) {
   const int nblk = ceil_div(chunk, KG_B), npair = nblk * (nblk + 1) / 2;
   gram_v_kernel<<<g.B * nchunks * npair, KG_THREADS, 0, s>>>(Vrow, gram, g, chunk, nblk, npair,
-                                                               nchunks);
+                                                               nchunks, spans);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   gram_norm_kernel<<<g.B * nchunks * npair * KG_SPLIT, KG_THREADS, 0, s>>>(
-      Z, gram, partial, g, chunk, nblk, npair, nchunks);
+      Z, gram, partial, g, chunk, nblk, npair, nchunks, spans);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = g.B * nchunks;
@@ -1566,7 +1570,8 @@ hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gra
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n16 = vt_elems(g) / 8;
-  vt_scale_kernel<<<ceil_div(n16, kThreads), kThreads, 0, s>>>(VT, scale, g, chunk, nchunks, n16);
+  vt_scale_kernel<<<ceil_div(n16, kThreads), kThreads, 0, s>>>(VT, scale, g, chunk, nchunks,
+                                                               blocks, n16);
   return hipGetLastError();
 }
 

@@ -57,6 +57,11 @@ struct ApplyTile {
   int32_t t0, t1, chunk, reserved;
 };
 
+// The tokens [t0, t1) of one chunk of a packed sequence, in chunk order.
+struct ChunkSpan {
+  int32_t t0, t1;
+};
+
 // The apply's token-tile width for a chunk of `chunk` tokens: the largest of
 // 256, 128 and 64 that divides it (the chunk is a multiple of 64).
 inline int apply_tile_width(int chunk) {
@@ -141,16 +146,20 @@ hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
                          uint16_t* Vrow, float vscale, const Dims& g, hipStream_t s);
 
-// Update-norm clipping: per chunk i of `chunk` tokens (uniform chunks),
-// scale[b][i] = min(1, clip / (norm_factor * ||Vrow_i^T Z_i||_F)) from the
-// Gram form (gram: B * nchunks * clip_gram_floats(chunk) floats of V Gram
-// tiles; partial: B * nchunks * clip_pairs(chunk) floats), then VT *= the
-// scale of each token's chunk.
+// Update-norm clipping: per chunk i, scale[b][i] = min(1, clip /
+// (norm_factor * ||Vrow_i^T Z_i||_F)) from the Gram form (gram: B * nchunks
+// * clip_gram_floats(chunk) floats of V Gram tiles; partial: B * nchunks *
+// clip_pairs(chunk) floats), then VT *= the scale of each token's chunk.
+// Chunks are uniform (chunk i = tokens [i * chunk, min(T, (i + 1) * chunk)))
+// when spans and blocks are null; a packed sequence (B = 1) passes its chunk
+// spans (each at most `chunk` tokens) and its block table, which give each
+// 64-token slab's chunk.
 int clip_pairs(int chunk);
 int64_t clip_gram_floats(int chunk);
 hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gram,
                              float* partial, float* scale, uint16_t* VT, const Dims& g,
-                             int chunk, int nchunks, float norm_factor, float clip,
+                             int chunk, int nchunks, const ChunkSpan* spans,
+                             const BlockInfo* blocks, float norm_factor, float clip,
                              hipStream_t s);
 
 // Fast-weight update over tokens [tok_begin, tok_begin + tok_count) (a

@@ -202,8 +202,8 @@ def test_packed_workspace_size(L):
     chunks = [(t, min(e, t + 1024)) for a, e in zip(starts, ends) for t in range(a, e, 1024)]
     n_tiles = sum(-(-(t1 - t0) // 256) for t0, t1 in chunks)
     assert len(chunks) == k
-    # more chunks, plus the block table and the apply's tile list
-    extra = (k - 64) * snap + T // 64 * 16 + n_tiles * 16
+    # more chunks, plus the block table, the apply's tile list and the chunk spans
+    extra = (k - 64) * snap + T // 64 * 16 + n_tiles * 16 + k * 8
     assert plain + extra <= n <= plain + extra + 4 * 256
 
 
@@ -273,6 +273,56 @@ def test_clipped_forward_validates_before_launch(L):
     st = L.ttt_layer_forward_clipped(ctypes.byref(qwen_desc()), *p[:7], ctypes.c_float(1e-3),
                                      1024, ctypes.c_float(1.0), p[7], p[8], p[9],
                                      ctypes.c_size_t(need - 1), None)
+    assert st == WORKSPACE
+
+
+# ---- packed documents with clipping -------------------------------------------
+
+def packed_clipped_ws(L, desc, chunk, starts, clip):
+    arr = (ctypes.c_int32 * len(starts))(*starts)
+    n = ctypes.c_size_t(0)
+    st = L.ttt_packed_clipped_workspace_size(ctypes.byref(desc), chunk, arr, len(starts),
+                                             ctypes.c_float(clip), ctypes.byref(n))
+    return st, n.value
+
+
+def test_packed_clipped_workspace_size(L):
+    """The packed layout plus the clipped path's buffers, sized by the packed
+    chunk count (chunks restart at every document)."""
+    desc = qwen_desc()
+    starts = [0, 1024 * 10, 1024 * 10 + 64, 40000 - 40000 % 64]
+    st, n = packed_clipped_ws(L, desc, 1024, starts, 1.0)
+    assert st == OK, L.ttt_last_error()
+    _, packed = packed_ws(L, desc, 1024, starts)
+    T, d = 65536, 2560
+    ends = starts[1:] + [T]
+    k = sum(-(-(e - a) // 1024) for a, e in zip(starts, ends))
+    ld_y = d + 64 if (d // 64) % 2 == 0 else d
+    pairs = 4 * 5 // 2
+    extra = T * ld_y * 2 + k * pairs * 256 * 256 * 4 + k * pairs * 2 * 4 + k * 4
+    assert packed + extra <= n <= packed + extra + 5 * 256
+
+
+@pytest.mark.parametrize("starts,clip,code", [
+    ([0, 128], 1.0, OK), ([0, 128], 0.0, INVALID), ([0, 128], float("nan"), INVALID),
+    ([0, 100], 1.0, UNSUPPORTED), ([64], 1.0, INVALID)])
+def test_packed_clipped_validation(L, starts, clip, code):
+    st, _ = packed_clipped_ws(L, qwen_desc(), 1024, starts, clip)
+    assert st == code, (starts, clip, st, L.ttt_last_error())
+
+
+def test_packed_clipped_forward_validates_before_launch(L):
+    desc = qwen_desc()
+    p = good_ptrs()
+    starts = (ctypes.c_int32 * 2)(0, 128)
+    st = L.ttt_layer_forward_packed_clipped(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3),
+                                            1024, starts, 2, ctypes.c_float(-1.0), p[7], p[8],
+                                            p[9], ctypes.c_size_t(1 << 62), None)
+    assert st == INVALID
+    _, need = packed_clipped_ws(L, desc, 1024, [0, 128], 1.0)
+    st = L.ttt_layer_forward_packed_clipped(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3),
+                                            1024, starts, 2, ctypes.c_float(1.0), p[7], p[8],
+                                            p[9], ctypes.c_size_t(need - 1), None)
     assert st == WORKSPACE
 
 
