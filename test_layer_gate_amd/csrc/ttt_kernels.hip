@@ -846,8 +846,10 @@ __device__ __forceinline__ GramTile gram_tile(const Dims& g, int chunk, int nblk
     ++sb;
   }
   tb += sb;
-  const int c0 = spans ? spans[t.i].t0 : t.i * chunk;
-  t.c1 = spans ? spans[t.i].t1 : min(g.T, c0 + chunk);
+  // A span table's values are clamped to the sequence, so a wrong table
+  // gives wrong norms, never a read outside the operands.
+  const int c0 = spans ? min(max(spans[t.i].t0, 0), g.T) : t.i * chunk;
+  t.c1 = spans ? min(max(spans[t.i].t1, c0), g.T) : min(g.T, c0 + chunk);
   t.s0 = c0 + sb * KG_B;
   t.u0 = c0 + tb * KG_B;
   t.weight = sb == tb ? 1 : 2;
@@ -963,7 +965,8 @@ __global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT
   const int b = (int)(e / per_b);
   const int64_t slab = (e % per_b) / (kVtSlab * 64);
   const int tok = (int)(slab % (g.T_pad / 64)) * 64;
-  const int ci = blocks ? blocks[tok / 64].chunk : min(tok / chunk, nchunks - 1);
+  const int ci = blocks ? min(max(blocks[tok / 64].chunk, 0), nchunks - 1)
+                        : min(tok / chunk, nchunks - 1);
   const float sc = scale[(int64_t)b * nchunks + ci];
   if (sc == 1.0f) return;
   uint4 v = reinterpret_cast<uint4*>(VT)[i];
