@@ -992,19 +992,16 @@ __global__ __launch_bounds__(kThreads) void vt_scale_kernel(u16* __restrict__ VT
 // a part-empty round of wide ones. Wide tiles read half the operand bytes per
 // MFMA that narrow ones do. Both the plain and the packed variant do this.
 constexpr int K3_NW = 8, K3_BM = 256, K3_BK = 64, K3_WIDE = 256, K3_NARROW = 128;
-template <int BN, bool PACKED>
+template <int BN>
 struct UpdCfg {
   static constexpr int WGM = BN == K3_WIDE ? 2 : 4;
   // Wide: Z^T three stages, V^T two; narrow: Z^T four, V^T two (160 KB
-  // each). The packed variant keeps 8 KB of LDS for its step table: two
-  // stages each when wide (128 KB), three each when narrow (144 KB).
-  static constexpr int NSTA = PACKED ? (BN == K3_WIDE ? 2 : 3) : (BN == K3_WIDE ? 3 : 4);
-  static constexpr int NSTB = PACKED ? (BN == K3_WIDE ? 2 : 3) : 2;
+  // each, the whole LDS; the packed variant keeps its step table in
+  // registers).
+  static constexpr int NSTA = BN == K3_WIDE ? 3 : 4;
+  static constexpr int NSTB = 2;
 };
-template <bool PACKED>
-constexpr int upd_lds_elems() {  // the stages of either width
-  return PACKED ? (3 * K3_BM + 3 * K3_NARROW) * K3_BK : 160 * 1024 / 2;
-}
+constexpr int kUpdLdsElems = 160 * 1024 / 2;  // the stages of either width
 
 // Stores bf16(acc * out_scale) of a [d_ff tile] x [d_model tile] state block
 // into an sb<256> d x f bf16 matrix of `bytes` bytes (row c = d_model index,
@@ -1087,6 +1084,19 @@ struct StateLoad {
   }
 };
 
+// A packed launch's block table, reduced to what the update's hook reads
+// and held in three registers per lane: lane l covers K steps [32 l,
+// 32 l + 32) (2048 steps = 131072 tokens in all), bit i of chunk_start /
+// doc_start flags step 32 l + i, and base is the chunk of step 32 l. The
+// chunk of step kt is base + the chunk starts in (32 l, kt]. Registers
+// instead of an LDS copy leave the whole LDS to the pipeline's stages; a
+// global read in the loop would need a vmcnt wait, which also waits for the
+// stage loads in flight.
+struct StepBits {
+  uint32_t chunk_start, doc_start;
+  int base;
+};
+
 // The update's hook: the exclusive-prefix snapshot at every chunk start and,
 // for packed documents (PACKED), the reset to the initial state at every
 // document start after the first ([iplex] §6), with chunk starts taken from
@@ -1102,18 +1112,20 @@ struct ChunkSnapshots {
   u16* snap;  // this sequence's snapshots, or null
   int64_t chunk_stride;
   int steps_per_chunk;
-  const uint32_t* steps;  // PACKED: per K step of this launch, in LDS (step_word)
-  int n_chunks;           // PACKED: snapshot slots (table values are clamped to them)
+  StepBits bits;  // PACKED: this launch's steps
+  int n_chunks;   // PACKED: snapshot slots (table values are clamped to them)
   __device__ __forceinline__ bool operator()(int kt, f32x16* acc) const {
     int slot;
     if constexpr (PACKED) {
-      // An LDS read (lgkmcnt): a global load here would need a vmcnt wait,
-      // which also waits for the stage loads in flight.
-      const uint32_t w = steps[kt];
-      const int flags = (int)(w >> 30);
-      slot = min((int)(w & 0x3fffffffu), n_chunks - 1);
-      if ((flags & kBlockDocStart) && kt > 0) reset(acc);
-      if (snap == nullptr || !(flags & kBlockChunkStart)) return false;
+      // kt is uniform, so these are scalar reads of one lane's registers.
+      const int lane = kt >> 5, bit = kt & 31;
+      const uint32_t cs = (uint32_t)__builtin_amdgcn_readlane((int)bits.chunk_start, lane);
+      const uint32_t ds = (uint32_t)__builtin_amdgcn_readlane((int)bits.doc_start, lane);
+      if (((ds >> bit) & 1u) && kt > 0) reset(acc);
+      if (snap == nullptr || !((cs >> bit) & 1u)) return false;
+      const uint32_t later = ((2u << bit) - 1u) & ~1u;  // steps 32 l + 1 .. kt
+      slot = min(__builtin_amdgcn_readlane(bits.base, lane) + __builtin_popcount(cs & later),
+                 n_chunks - 1);
     } else {
       if (snap == nullptr || kt % steps_per_chunk != 0) return false;
       slot = kt / steps_per_chunk;
@@ -1129,19 +1141,46 @@ __device__ __forceinline__ uint32_t step_word(const BlockInfo& b) {
 }
 constexpr int kMaxPackedSteps = 2048;  // K steps of a packed update launch (131072 tokens)
 
+// Every lane's StepBits from this launch's block table, staged through the
+// LDS stage memory (free until the pipeline's first loads; the barrier at the
+// end keeps them from overwriting it while a wave still reads). Table
+// values are clamped, so a wrong table gives wrong numbers, never a wild
+// address.
+__device__ __forceinline__ StepBits load_step_bits(u16* lds, const BlockInfo* __restrict__ blocks,
+                                                   int first_block, int nk, int n_chunks) {
+  uint32_t* words = reinterpret_cast<uint32_t*>(lds);
+  for (int k = threadIdx.x; k < nk; k += 64 * K3_NW) words[k] = step_word(blocks[first_block + k]);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  StepBits sb{0u, 0u, 0};
+#pragma unroll 4
+  for (int jj = 0; jj < 32; ++jj) {
+    const int j = (jj + lane) & 31;  // skewed, so the lanes read different banks
+    const int k = lane * 32 + j;
+    if (k < nk) {
+      const uint32_t w = words[k];
+      sb.chunk_start |= ((w >> 30) & (uint32_t)kBlockChunkStart ? 1u : 0u) << j;
+      sb.doc_start |= ((w >> 30) & (uint32_t)kBlockDocStart ? 1u : 0u) << j;
+      if (j == 0) sb.base = min((int)(w & 0x3fffffffu), n_chunks - 1);
+    }
+  }
+  __syncthreads();
+  return sb;
+}
+
 // One update tile: d_ff rows [j0, j0 + 256) and d_model columns
 // [c0, c0 + BN) of sequence b's state.
 template <int BN, bool WINIT_F32, bool PACKED>
 __device__ __forceinline__ void update_tile(
-    u16* lds, const uint32_t* steps, int b, int j0, int c0, const u16* __restrict__ ZT,
+    u16* lds, StepBits bits, int b, int j0, int c0, const u16* __restrict__ ZT,
     const u16* __restrict__ VT, const void* __restrict__ Winit, int64_t winit_bstride,
     int64_t winit_ld, float acc_scale, u16* __restrict__ snap, int64_t snap_bstride,
     float* __restrict__ Wf, u16* __restrict__ shadow, const Dims& g, int tok_begin, int nk,
     int steps_per_chunk, int n_chunks) {
-  using C = UpdCfg<BN, PACKED>;
+  using C = UpdCfg<BN>;
   using L = Layout<K3_BM, BN, C::WGM, K3_NW>;
   constexpr int TM = L::TM, TN = L::TN, NSTA = C::NSTA, NSTB = C::NSTB;
-  static_assert((NSTA * K3_BM + NSTB * BN) * K3_BK <= upd_lds_elems<PACKED>(), "stages fit");
+  static_assert((NSTA * K3_BM + NSTB * BN) * K3_BK <= kUpdLdsElems, "stages fit");
   const int d = g.d, f = g.f;
   const Frag<L> fr;
   const int64_t chunk_stride = snap_elems(g);
@@ -1160,7 +1199,7 @@ __device__ __forceinline__ void update_tile(
                                           (uint32_t)(chunk_stride * 2)};
   const ChunkSnapshots<L, WINIT_F32, PACKED> hook{
       snapshot, reset, snap ? snap + b * snap_bstride : nullptr, chunk_stride,
-      steps_per_chunk, steps, n_chunks};
+      steps_per_chunk, bits, n_chunks};
   // Rows past d_ff / d_model in the last slabs are never written; they only
   // feed output rows / columns that are not stored. A narrow tile reads the
   // first or second 128 rows of a 256-row V^T slab: 16 contiguous KB per K
@@ -1201,19 +1240,14 @@ __global__ __launch_bounds__(64 * K3_NW) void update_kernel(
     int64_t snap_bstride, float* __restrict__ Wf, u16* __restrict__ shadow, Dims g,
     int tok_begin, int nk, int steps_per_chunk, const BlockInfo* __restrict__ blocks,
     int n_chunks, int regions_m, int regions_n, int n_wide) {
-  __shared__ __attribute__((aligned(16))) u16 lds[upd_lds_elems<PACKED>()];
-  __shared__ uint32_t steps[PACKED ? kMaxPackedSteps : 1];
-  if constexpr (PACKED) {
-    // This launch's block table, one word per K step (nk <= kMaxPackedSteps,
-    // checked on the host); the pipeline's first barrier publishes it.
-    for (int k = threadIdx.x; k < nk; k += 64 * K3_NW)
-      steps[k] = step_word(blocks[tok_begin / K3_BK + k]);
-    __syncthreads();
-  }
+  __shared__ __attribute__((aligned(16))) u16 lds[kUpdLdsElems];
+  StepBits bits{0u, 0u, 0};
+  // nk <= kMaxPackedSteps for a packed launch (checked on the host).
+  if constexpr (PACKED) bits = load_step_bits(lds, blocks, tok_begin / K3_BK, nk, n_chunks);
   if ((int)blockIdx.x < n_wide) {
     const TileIdx t = tile_coords(xcd_contiguous(blockIdx.x, n_wide), regions_m, regions_n, 4);
     update_tile<K3_WIDE, WINIT_F32, PACKED>(
-        lds, steps, t.b, t.tm * K3_BM, t.tn * K3_WIDE, ZT, VT, Winit, winit_bstride, winit_ld,
+        lds, bits, t.b, t.tm * K3_BM, t.tn * K3_WIDE, ZT, VT, Winit, winit_bstride, winit_ld,
         acc_scale, snap, snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
         n_chunks);
     return;
@@ -1225,7 +1259,7 @@ __global__ __launch_bounds__(64 * K3_NW) void update_kernel(
   const int c0 = t.tn * K3_WIDE + (id & 1) * K3_NARROW;
   if (c0 >= g.d) return;  // uniform: the half of a region past d_model
   update_tile<K3_NARROW, WINIT_F32, PACKED>(
-      lds, steps, t.b, t.tm * K3_BM, c0, ZT, VT, Winit, winit_bstride, winit_ld, acc_scale,
+      lds, bits, t.b, t.tm * K3_BM, c0, ZT, VT, Winit, winit_bstride, winit_ld, acc_scale,
       snap, snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk, n_chunks);
 }
 
@@ -1613,6 +1647,7 @@ hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Win
   // read from a slab boundary.
   const int nk = (tok_count + K3_BK - 1) / K3_BK, steps_per_chunk = chunk / K3_BK;
   if (blocks != nullptr) {
+    if (nk > kMaxPackedSteps) return hipErrorInvalidValue;  // StepBits holds 2048 steps
     if (winit_f32)
       update_launch<true, true>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
                                 snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
