@@ -269,12 +269,16 @@ ttt_status check_docs(const int32_t* doc_starts, int32_t n_docs, Geo* g) {
   g->spans.clear();
   for (const Chunk& c : g->chunks) g->spans.push_back({c.t0, c.t1});
   // The apply's token tiles start at every chunk start; a chunk's last tile
-  // may be partial.
+  // may be partial. A document's first chunk starts from W_down0, whose
+  // snapshot is slot 0 (the first document's first chunk): its tiles read
+  // that slot, and the update stores no copy of it.
   const int bn = tttk::apply_tile_width(C);
   g->tiles.clear();
-  for (size_t i = 0; i < g->chunks.size(); ++i)
+  for (size_t i = 0; i < g->chunks.size(); ++i) {
+    const int32_t slot = g->chunks[i].doc_start ? 0 : (int32_t)i;
     for (int t = g->chunks[i].t0; t < g->chunks[i].t1; t += bn)
-      g->tiles.push_back({t, std::min(g->chunks[i].t1, t + bn), (int32_t)i, 0});
+      g->tiles.push_back({t, std::min(g->chunks[i].t1, t + bn), slot, 0});
+  }
   return TTT_OK;
 }
 

@@ -1121,8 +1121,12 @@ struct ChunkSnapshots {
       const int lane = kt >> 5, bit = kt & 31;
       const uint32_t cs = (uint32_t)__builtin_amdgcn_readlane((int)bits.chunk_start, lane);
       const uint32_t ds = (uint32_t)__builtin_amdgcn_readlane((int)bits.doc_start, lane);
-      if (((ds >> bit) & 1u) && kt > 0) reset(acc);
-      if (snap == nullptr || !((cs >> bit) & 1u)) return false;
+      const bool doc = ((ds >> bit) & 1u) && kt > 0;
+      if (doc) reset(acc);
+      // After a reset the state is W_down0 again, whose snapshot is slot 0:
+      // a later document's first chunk reads that slot (the apply's tile
+      // list says so), and nothing is stored here.
+      if (snap == nullptr || doc || !((cs >> bit) & 1u)) return false;
       const uint32_t later = ((2u << bit) - 1u) & ~1u;  // steps 32 l + 1 .. kt
       slot = min(__builtin_amdgcn_readlane(bits.base, lane) + __builtin_popcount(cs & later),
                  n_chunks - 1);
