@@ -103,9 +103,9 @@ def test_documents_do_not_leak(ttt):
 
 
 @pytest.mark.skip(reason="this 64k five-document layout faulted the GPU through a scalar "
-                         "table read whose address was sign-extended; the read is reverted "
-                         "to the vector load and the case is held off the GPU until it is "
-                         "re-tested")
+                         "table read whose address was sign-extended; that read is removed "
+                         "(the hook now reads per-lane step registers) and the case is held "
+                         "off the GPU until it is re-tested")
 @pytest.mark.timeout(900)
 def test_packed_full_size_sampled(ttt):
     """Qwen3-4B shape at 64k tokens, five documents of uneven lengths (some
