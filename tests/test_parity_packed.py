@@ -179,3 +179,17 @@ def test_packed_full_size_equal_documents_sampled(ttt):
     ew, edw = rel(W_s, W_ref), rel(W_s - W0s, W_ref - W0s)
     print(f"final state after the last document: W {ew:.2e} dW {edw:.2e}", flush=True)
     assert ew <= W_TOL and edw <= DW_TOL
+
+
+def test_packed_at_the_step_limit(ttt):
+    """131072 tokens, the longest packed sequence (2048 update steps of 64
+    tokens, the last one held by the last bit of the update's per-lane step
+    registers), with documents that put a chunk start inside a document at
+    step 2044 and a document start on step 2047; mid_amp widths, chunk 256.
+    Every output against the oracle, and the final state, which is the last
+    one-step document's update on W_down0."""
+    cfg = synth.CONFIGS["mid_amp"]
+    x = synth.make_inputs(cfg, batch=1, seq_len=131072, seed=59)
+    starts = [0, 640, 65536, 130560, 131008]
+    O, Wf = run_packed_gpu(ttt, to_dev(x, cfg.dtype), cfg.eta, cfg.chunk, starts)
+    check_packed(x, O, Wf, cfg.eta, cfg.chunk, starts, raw_w=False)
