@@ -168,6 +168,34 @@ ttt_status ttt_layer_forward_packed(const ttt_desc* desc,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* The tables ttt_layer_forward_packed builds on the host for a layout and
+ * copies to its workspace (host only: no GPU call, nothing launched). For
+ * inspecting and testing a layout; the same checks as
+ * ttt_packed_workspace_size apply.
+ *   blocks  out, one entry per 64-token block of the sequence padded to 256
+ *           tokens: the chunk holding the block (chunks counted over all
+ *           documents, in order), flags (TTT_BLOCK_CHUNK_START when a chunk
+ *           starts at the block, TTT_BLOCK_DOC_START when a document does),
+ *           and the first token after the block's document and after its
+ *           chunk. Blocks at or past seq_len carry the last chunk, no flags
+ *           and ends seq_len.
+ *   tiles   out, the apply's token tiles: tokens [t0, t1) of one chunk, read
+ *           against snapshot slot `snapshot` (0 for a document's first chunk,
+ *           whose state is W_down0 like the first document's).
+ *   counts  out, 3 int32: entries of blocks, entries of tiles, chunks.
+ * At most max_blocks / max_tiles entries are written (counts has the full
+ * numbers either way); blocks / tiles may be NULL when their max is 0. */
+enum { TTT_BLOCK_CHUNK_START = 1, TTT_BLOCK_DOC_START = 2 };
+typedef struct ttt_packed_block {
+  int32_t chunk, flags, doc_end, chunk_end;
+} ttt_packed_block;
+typedef struct ttt_packed_tile {
+  int32_t t0, t1, snapshot, reserved;
+} ttt_packed_tile;
+ttt_status ttt_packed_tables(const ttt_desc* desc, int32_t chunk, const int32_t* doc_starts,
+                             int32_t n_docs, ttt_packed_block* blocks, int32_t max_blocks,
+                             ttt_packed_tile* tiles, int32_t max_tiles, int32_t* counts);
+
 /* Packed documents with update-norm clipping (iplexlaw explainer §6, both
  * the document reset and the norm clipping): ttt_layer_forward_packed,
  * where each chunk's update is first scaled as in ttt_layer_forward_clipped.
@@ -272,8 +300,14 @@ ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0,
                          void* V, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* The name of a status code ("TTT_OK", "TTT_ERR_INVALID_ARG", ...; codes
+ * outside ttt_status give "TTT_ERR_UNKNOWN"). The string is static. */
 const char* ttt_status_string(int32_t status);
+/* The reason for the most recent failed call on the calling thread
+ * (thread-local; valid until that thread's next call into the library).
+ * ttt_last_error_message is the same function under a second name. */
 const char* ttt_last_error(void);
+const char* ttt_last_error_message(void);
 
 /* Optional per-launch timing. While enabled, every kernel the library
  * launches is bracketed by HIP events on its stream. ttt_profile_read()

@@ -24,13 +24,14 @@ from ._binding import (  # noqa: F401
     lib,
     lm_target,
     make_desc,
+    packed_tables,
     packed_workspace_size,
     profile_enable,
     profile_read,
     workspace_size,
 )
 
-__all__ = ["layer_forward", "layer_forward_packed", "packed_workspace_size",
+__all__ = ["layer_forward", "layer_forward_packed", "packed_workspace_size", "packed_tables",
            "layer_forward_continue", "continue_workspace_size", "clipped_workspace_size",
            "decode_state_size", "decode_begin", "decode_step",
            "gated_activation", "lm_target", "workspace_size",

@@ -37,6 +37,16 @@ class Desc(ctypes.Structure):
                 ("reserved2", ctypes.c_uint32)]
 
 
+class PackedBlock(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("doc_end", ctypes.c_int32), ("chunk_end", ctypes.c_int32)]
+
+
+class PackedTile(ctypes.Structure):
+    _fields_ = [("t0", ctypes.c_int32), ("t1", ctypes.c_int32),
+                ("snapshot", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class KernelStat(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
                 ("total_ms", ctypes.c_double)]
@@ -77,6 +87,9 @@ def lib() -> ctypes.CDLL:
                                                    ctypes.c_float, ctypes.c_int32, I32P,
                                                    ctypes.c_int32, ctypes.c_float, _P, _P, _P,
                                                    _S, _P]
+    L.ttt_packed_tables.argtypes = [DP, ctypes.c_int32, I32P, ctypes.c_int32,
+                                    ctypes.POINTER(PackedBlock), ctypes.c_int32,
+                                    ctypes.POINTER(PackedTile), ctypes.c_int32, I32P]
     L.ttt_continue_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
     L.ttt_layer_forward_continue.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P,
                                              _P, ctypes.c_float, ctypes.c_int32, _P, _P, _S,
@@ -91,6 +104,7 @@ def lib() -> ctypes.CDLL:
                "ttt_packed_workspace_size", "ttt_layer_forward_packed",
                "ttt_clipped_workspace_size", "ttt_layer_forward_clipped",
                "ttt_packed_clipped_workspace_size", "ttt_layer_forward_packed_clipped",
+               "ttt_packed_tables",
                "ttt_continue_workspace_size", "ttt_layer_forward_continue",
                "ttt_decode_state_size", "ttt_decode_begin", "ttt_decode_step",
                "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
@@ -297,6 +311,24 @@ def layer_forward_packed(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk
         _check(lib().ttt_layer_forward_packed_clipped(*args, ctypes.c_float(float(clip)),
                                                       *tail))
     return (O[0], Wf[0]) if squeeze else (O, Wf)
+
+
+def packed_tables(desc: Desc, chunk: int, doc_starts):
+    """The block table and apply tiles ttt_layer_forward_packed builds for a
+    layout (include/ttt.h, ttt_packed_tables; host only): (blocks, tiles,
+    n_chunks), blocks as (chunk, flags, doc_end, chunk_end) tuples and tiles
+    as (t0, t1, snapshot) tuples."""
+    arr, n_docs = _doc_array(doc_starts)
+    counts = (ctypes.c_int32 * 3)()
+    _check(lib().ttt_packed_tables(ctypes.byref(desc), int(chunk), arr, n_docs, None, 0, None,
+                                   0, counts))
+    nb, nt = counts[0], counts[1]
+    blocks = (PackedBlock * max(nb, 1))()
+    tiles = (PackedTile * max(nt, 1))()
+    _check(lib().ttt_packed_tables(ctypes.byref(desc), int(chunk), arr, n_docs, blocks, nb,
+                                   tiles, nt, counts))
+    return ([(b.chunk, b.flags, b.doc_end, b.chunk_end) for b in blocks[:nb]],
+            [(t.t0, t.t1, t.snapshot) for t in tiles[:nt]], counts[2])
 
 
 def continue_workspace_size(desc: Desc, chunk: int) -> int:

@@ -351,6 +351,7 @@ const char* ttt_status_string(int32_t s) {
 }
 
 const char* ttt_last_error(void) { return g_err.c_str(); }
+const char* ttt_last_error_message(void) { return g_err.c_str(); }
 
 ttt_status ttt_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes) {
   Geo g;
@@ -622,6 +623,38 @@ ttt_status ttt_layer_forward_packed(const ttt_desc* desc, const void* H, const v
   TTT_TRY(check_docs(doc_starts, n_docs, &g));
   return forward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, O, W_down_final,
                       workspace, workspace_bytes, stream);
+}
+
+static_assert(sizeof(ttt_packed_block) == sizeof(tttk::BlockInfo) &&
+                  TTT_BLOCK_CHUNK_START == tttk::kBlockChunkStart &&
+                  TTT_BLOCK_DOC_START == tttk::kBlockDocStart,
+              "the exported block table is the kernels' table");
+static_assert(sizeof(ttt_packed_tile) == sizeof(tttk::ApplyTile), "tile entries");
+
+ttt_status ttt_packed_tables(const ttt_desc* desc, int32_t chunk, const int32_t* doc_starts,
+                             int32_t n_docs, ttt_packed_block* blocks, int32_t max_blocks,
+                             ttt_packed_tile* tiles, int32_t max_tiles, int32_t* counts) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  TTT_TRY(check_docs(doc_starts, n_docs, &g));
+  if (counts == nullptr) return fail(TTT_ERR_INVALID_ARG, "counts is NULL");
+  if (max_blocks < 0 || max_tiles < 0)
+    return fail(TTT_ERR_INVALID_ARG, "max_blocks / max_tiles must be >= 0");
+  if ((max_blocks > 0 && blocks == nullptr) || (max_tiles > 0 && tiles == nullptr))
+    return fail(TTT_ERR_INVALID_ARG, "blocks / tiles is NULL");
+  counts[0] = (int32_t)g.blocks.size();
+  counts[1] = (int32_t)g.tiles.size();
+  counts[2] = (int32_t)g.nchunks;
+  for (int32_t i = 0; i < max_blocks && i < counts[0]; ++i) {
+    const tttk::BlockInfo& b = g.blocks[i];
+    blocks[i] = {b.chunk, b.flags, b.doc_end, b.chunk_end};
+  }
+  for (int32_t i = 0; i < max_tiles && i < counts[1]; ++i) {
+    const tttk::ApplyTile& t = g.tiles[i];
+    tiles[i] = {t.t0, t.t1, t.chunk, 0};
+  }
+  return TTT_OK;
 }
 
 ttt_status ttt_packed_clipped_workspace_size(const ttt_desc* desc, int32_t chunk,

@@ -41,6 +41,47 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), f"{n} declared in ttt.h but not exported"
 
 
+# The boundary the survey sketched (its names) and the exported function
+# that serves each; where the name differs, the design doc's boundary table gives
+# the reason (the survey's debug calls took no workspace, and its size call
+# had no way to report an invalid descriptor).
+SURVEY_BOUNDARY = {
+    "ttt_workspace_size": "ttt_workspace_size",
+    "ttt_layer_forward": "ttt_layer_forward",
+    "ttt_status_string": "ttt_status_string",
+    "ttt_last_error_message": "ttt_last_error_message",
+    "ttt_debug_gate_up": "ttt_gated_activation",
+    "ttt_debug_target": "ttt_lm_target",
+}
+
+
+def header_constants():
+    src = open(HEADER).read()
+    return {k: v for k, v in re.findall(r"\b(TTT_[A-Z0-9_]+)\s*=\s*([-0-9a-fx<u ]+?)\s*[,}\n/]",
+                                          src)}
+
+
+def test_survey_boundary_is_served(L):
+    declared = set(declared_functions())
+    for survey_name, ours in SURVEY_BOUNDARY.items():
+        assert ours in declared, f"{survey_name}: {ours} is not declared in ttt.h"
+        assert hasattr(L, ours), f"{survey_name}: {ours} is not exported"
+    c = header_constants()
+    want = {"TTT_OK": "0", "TTT_ERR_INVALID_ARG": "-1", "TTT_ERR_UNSUPPORTED": "-2",
+            "TTT_ERR_WORKSPACE": "-3", "TTT_ERR_ALIAS": "-4", "TTT_ERR_HIP": "-5",
+            "TTT_BF16": "0", "TTT_F32": "1", "TTT_FLAG_PAD_CHUNK": "1u << 0",
+            "TTT_FLAG_SCHED_RUNNING": "1u << 1", "TTT_FLAG_SCHED_PREFIX": "1u << 2"}
+    for k, v in want.items():
+        assert c.get(k, "").strip() == v, (k, c.get(k))
+
+
+def test_last_error_message_is_last_error(L):
+    L.ttt_last_error_message.restype = ctypes.c_char_p
+    st, _ = ws_size(L, qwen_desc(batch=0), 1024)
+    assert st == INVALID
+    assert L.ttt_last_error_message() == L.ttt_last_error() == b"batch must be >= 1"
+
+
 def test_status_strings(L):
     for code, name in [(0, "TTT_OK"), (-1, "TTT_ERR_INVALID_ARG"), (-2, "TTT_ERR_UNSUPPORTED"),
                        (-3, "TTT_ERR_WORKSPACE"), (-4, "TTT_ERR_ALIAS"), (-5, "TTT_ERR_HIP")]:

@@ -7,11 +7,14 @@ W check alone would hide a wrong update). The bf16 path rounds Z, V, the
 state snapshots and O to bf16 (relative error 2^-9 each), which puts the
 expected error near 4e-3 for O and 3e-3 for dW.
 
-Sizes: the small configurations run the whole oracle. The full-size
-configurations run exactly what the benchmark times, and are checked on
-outputs the oracle can compute directly: rows of Z and V, every output of
-the first chunks (the oracle runs those chunks with the conv's look-ahead
-rows), and sampled entries of the final state.
+Sizes: the small configurations run the whole oracle at once. The
+full-size configurations run exactly what the benchmark times and are
+checked over the whole sequence: the oracle runs it in segments of whole
+chunks, each segment starting from the previous one's final state and
+reading the conv's K - 1 look-ahead rows past its end (the split/resume
+form pinned in oracle_pins.py), so that every output of every chunk and
+every entry of the final state are compared, with the oracle's memory
+bounded by one segment. Rows of Z and V are also compared on their own.
 """
 import numpy as np
 import pytest
@@ -68,6 +71,89 @@ def check_full(x, O, Wf, eta, chunk, pad="sequence", W0=None, raw_w=True):
     return e_o, e_w, e_dw
 
 
+def oracle_segments(x, eta, chunk, seg_chunks=8, pad="sequence", clip=None):
+    """The oracle's prefill over the whole sequence in segments of seg_chunks
+    chunks: yields (a, e, O[:, a:e]) per segment, float64, and returns the
+    final state [B, d, f] (as the generator's return value). Each segment
+    continues the previous one's state and reads K - 1 look-ahead rows of
+    X0 past its end, which reproduces the single run (split/resume pin)."""
+    H, X0 = x["H"], x["X0"]
+    B, T, _ = H.shape
+    K = x["taps"].shape[0]
+    W = np.broadcast_to(np.asarray(x["W_down0"], np.float64),
+                        (B,) + x["W_down0"].shape[-2:]).copy()
+    for a in range(0, T, seg_chunks * chunk):
+        e = min(T, a + seg_chunks * chunk)
+        la = min(K - 1, T - e)
+        O, W = ora.ttt_prefill(H[:, a:e], X0[:, a:e + la], x["Wg"], x["Wu"], W, x["taps"],
+                               x["W_target"], eta, chunk, pad=pad, clip=clip)
+        yield a, e, O
+    return W
+
+
+class SegmentErrors:
+    """max|err| / max|ref| of O over the whole sequence, per batch row, and
+    the same over the last chunk alone, accumulated segment by segment."""
+
+    def __init__(self, B, T, chunk):
+        self.err = np.zeros(B)
+        self.ref = np.zeros(B)
+        self.last_err = np.zeros(B)
+        self.last_ref = np.zeros(B)
+        self.last0 = (T - 1) // chunk * chunk
+
+    def add(self, a, e, O_gpu, O_ref):
+        for b in range(O_ref.shape[0]):
+            d = np.abs(O_gpu[b].astype(np.float64) - O_ref[b])
+            self.err[b] = max(self.err[b], d.max())
+            self.ref[b] = max(self.ref[b], np.abs(O_ref[b]).max())
+            if e > self.last0:
+                lo = max(self.last0, a) - a
+                self.last_err[b] = max(self.last_err[b], d[lo:].max())
+                self.last_ref[b] = max(self.last_ref[b], np.abs(O_ref[b, lo:]).max())
+
+    def rel(self):
+        return self.err / np.maximum(self.ref, 1e-30), \
+            self.last_err / np.maximum(self.last_ref, 1e-30)
+
+
+def check_whole_sequence(x, O_gpu, Wf_gpu, eta, chunk, what, pad="sequence", clip=None,
+                         seg_chunks=8, raw_w=True, check_state=True):
+    """Every output and every final-state entry of a full-size run against the
+    oracle run over the whole sequence in segments. O_gpu: host float32
+    [B, T, d]; Wf_gpu: host float32 [B, d, f] (not compared unless
+    check_state)."""
+    B, T, _ = x["H"].shape
+    acc = SegmentErrors(B, T, chunk)
+    gen = oracle_segments(x, eta, chunk, seg_chunks, pad=pad, clip=clip)
+    while True:
+        try:
+            a, e, O_ref = next(gen)
+        except StopIteration as stop:
+            W_ref = stop.value
+            break
+        acc.add(a, e, O_gpu[:, a:e], O_ref)
+    e_o, e_last = acc.rel()
+    W0 = np.broadcast_to(np.asarray(x["W_down0"], np.float64), W_ref.shape)
+    out = []
+    for b in range(B):
+        msg = f"{what}[{b}]: O (all {-(-T // chunk)} chunks) {e_o[b]:.2e}, last chunk {e_last[b]:.2e}"
+        if not check_state:
+            print(msg, flush=True)
+            assert e_o[b] <= O_TOL and e_last[b] <= O_TOL, f"O error {e_o[b]:.3e} / {e_last[b]:.3e}"
+            out.append((e_o[b], e_last[b]))
+            continue
+        e_w = rel(Wf_gpu[b], W_ref[b])
+        e_dw = rel(Wf_gpu[b] - W0[b], W_ref[b] - W0[b])
+        print(f"{msg}; W (every entry) {e_w:.2e} dW {e_dw:.2e}", flush=True)
+        assert e_o[b] <= O_TOL and e_last[b] <= O_TOL, f"O error {e_o[b]:.3e} / {e_last[b]:.3e}"
+        assert e_dw <= DW_TOL, f"dW error {e_dw:.3e}"
+        if raw_w:
+            assert e_w <= W_TOL, f"W error {e_w:.3e}"
+        out.append((e_o[b], e_last[b], e_w, e_dw))
+    return out
+
+
 SMALL = ["tiny", "tiny_amp", "mid_amp"]
 
 
@@ -92,9 +178,7 @@ def test_forward_small(ttt, name, schedule, pad):
     cfg = synth.CONFIGS[name]
     x = synth.make_inputs(cfg)
     O, Wf = run_gpu(ttt, to_dev(x, cfg.dtype), cfg.eta, cfg.chunk, schedule=schedule, pad=pad)
-    # Raw W check only where the update is small next to W (the amplified
-    # configs make the update comparable to W on purpose).
-    check_full(x, O, Wf, cfg.eta, cfg.chunk, pad=pad, raw_w=name == "tiny")
+    check_full(x, O, Wf, cfg.eta, cfg.chunk, pad=pad)
 
 
 def test_ragged_batched_per_sequence_state(ttt):
@@ -107,7 +191,7 @@ def test_ragged_batched_per_sequence_state(ttt):
     t["W_down0"] = torch.from_numpy(W0).to("cuda").to(torch.bfloat16)
     for schedule in ("prefix", "running"):
         O, Wf = run_gpu(ttt, t, cfg.eta, cfg.chunk, schedule=schedule)
-        check_full(x, O, Wf, cfg.eta, cfg.chunk, W0=W0, raw_w=False)
+        check_full(x, O, Wf, cfg.eta, cfg.chunk, W0=W0)
 
 
 @pytest.mark.parametrize("T,C", [(1, 64), (63, 64), (65, 64), (300, 128), (257, 256)])
@@ -115,7 +199,7 @@ def test_edge_lengths(ttt, T, C):
     cfg = synth.CONFIGS["tiny_amp"]
     x = synth.make_inputs(cfg, seq_len=T, seed=T)
     O, Wf = run_gpu(ttt, to_dev(x, cfg.dtype), cfg.eta, C)
-    check_full(x, O, Wf, cfg.eta, C, raw_w=False)
+    check_full(x, O, Wf, cfg.eta, C)
 
 
 def test_special_cases_reduce_to_plain_mlp(ttt):
@@ -209,19 +293,23 @@ def test_qwen3_4b_8k_full(ttt):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["qwen3_4b_64k", "llama31_8b_32k", "qwen3_14b_128k"])
-def test_full_size_sampled(ttt, name):
+def test_full_size_whole_sequence(ttt, name):
+    """The full-size configurations exactly as the benchmark runs them:
+    sampled rows of Z and V, then every output of every chunk of every batch
+    row and every entry of the final state against the oracle's whole run
+    (in segments). The late chunks read snapshot slots up to k - 1 and depend
+    on every earlier update."""
     cfg = synth.CONFIGS[name]
     x = synth.make_inputs(cfg)
-    C, K, eta = cfg.chunk, cfg.conv_k, cfg.eta
+    C, eta = cfg.chunk, cfg.eta
     t = to_dev(x, cfg.dtype)
+    print(f"[{name}] GPU layer", flush=True)
     O, Wf = ttt.layer_forward(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
                               t["W_target"], eta, C)
-    n_chunks = 3 if name == "qwen3_4b_64k" else 2
-    O_head = O[:, :n_chunks * C].float().cpu().numpy()
+    O_h = O.float().cpu().numpy()
+    Wf_h = Wf.cpu().numpy()
+    del O, Wf
     rng = np.random.default_rng(1234)
-    cs = np.unique(np.concatenate([[0, cfg.d_model - 1], rng.integers(0, cfg.d_model, 14)]))
-    js = np.unique(np.concatenate([[0, cfg.d_ff - 1], rng.integers(0, cfg.d_ff, 14)]))
-    W_s = Wf[:, cs][:, :, js].cpu().numpy()
     rows = np.unique(np.concatenate([[0, 1, C - 1, C, cfg.seq_len - 2, cfg.seq_len - 1],
                                      rng.integers(0, cfg.seq_len, 10)]))
     Z = ttt.gated_activation(t["H"], t["Wg"], t["Wu"])
@@ -229,21 +317,12 @@ def test_full_size_sampled(ttt, name):
     del Z
     V = ttt.lm_target(t["X0"], t["taps"], t["W_target"], chunk=C)
     V_s = V[:, rows].float().cpu().numpy()
-    del V, O, Wf, t
+    del V, t
     torch.cuda.empty_cache()
     for b in range(cfg.batch):
         ez = rel(Z_s[b], ora.activation_rows(x["H"][b], x["Wg"], x["Wu"], rows))
         ev = rel(V_s[b], ora.target_rows(x["X0"][b], x["taps"], x["W_target"], rows))
-        n = n_chunks * C
-        O_ref, _ = ora.ttt_prefill(x["H"][b:b + 1, :n], x["X0"][b:b + 1, :n + K - 1], x["Wg"],
-                                   x["Wu"], x["W_down0"], x["taps"], x["W_target"], eta, C)
-        eo = rel(O_head[b], O_ref[0])
-        W_ref = ora.final_state_entries(x["H"][b], x["X0"][b], x["Wg"], x["Wu"],
-                                        x["W_down0"], x["taps"], x["W_target"], eta, cs, js)
-        W0s = x["W_down0"][np.ix_(cs, js)].astype(np.float64)
-        ew = rel(W_s[b], W_ref)
-        edw = rel(W_s[b] - W0s, W_ref - W0s)
-        print(f"{name}[{b}]: Z {ez:.2e} V {ev:.2e} O(first {n_chunks} chunks) {eo:.2e} "
-              f"W {ew:.2e} dW {edw:.2e}", flush=True)
+        print(f"{name}[{b}]: Z rows {ez:.2e} V rows {ev:.2e}", flush=True)
         assert ez <= STEP_TOL and ev <= STEP_TOL
-        assert eo <= O_TOL and ew <= W_TOL and edw <= DW_TOL
+    print(f"[{name}] oracle over the whole sequence", flush=True)
+    check_whole_sequence(x, O_h, Wf_h, eta, C, name)

@@ -82,7 +82,7 @@ def test_segments_match_one_oracle_run(ttt, case, pad, schedule):
     t = to_dev(x, cfg.dtype)
     O, Wf = run_segments(ttt, t, cfg.eta, cfg.chunk, [0] + cuts + [T], cfg.conv_k,
                          schedule=schedule, pad=pad)
-    check(x, O, Wf, cfg.eta, cfg.chunk, pad=pad, raw_w=name == "tiny", what=case)
+    check(x, O, Wf, cfg.eta, cfg.chunk, pad=pad, what=case)
 
 
 def test_segment_from_the_gpu_state(ttt):

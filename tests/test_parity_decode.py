@@ -78,8 +78,7 @@ def test_decode_matches_oracle(ttt, name, B, T):
     t = to_dev(x, cfg.dtype)
     W = state0(t, B)
     O = decode_gpu(ttt, t, cfg.eta, cfg.chunk, 0, T, W)
-    pending = check(x, O, W.cpu().numpy(), cfg.eta, cfg.chunk, f"{name} B={B} T={T}",
-                    raw_w=name == "tiny")
+    pending = check(x, O, W.cpu().numpy(), cfg.eta, cfg.chunk, f"{name} B={B} T={T}")
     assert pending == T % cfg.chunk
 
 
