@@ -118,6 +118,31 @@ ttt_status ttt_layer_forward(const ttt_desc* desc,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* The prefill without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc). It is ttt_layer_forward with its
+ * workspace in a static device array of TTT_NOALLOC_SCRATCH_BYTES bytes that
+ * the library's code object reserves on every device it runs on, for the
+ * life of the process; the call itself allocates nothing.
+ *   Arguments, layouts, flags and results are ttt_layer_forward's, minus
+ *   the workspace. Problems whose ttt_workspace_size exceeds the scratch
+ *   return TTT_ERR_WORKSPACE before anything is launched (64 MiB holds, for
+ *   instance, 2048 tokens at d_model 256 / d_ff 1024; the Qwen3-4B shapes
+ *   need the caller-workspace entry point).
+ *   Every call on one GPU uses that GPU's one scratch array, which keeps
+ *   the previous call's contents (nothing in it needs to start at zero):
+ *   calls that overlap in time on one GPU (on different streams, or from
+ *   different threads) race on it and must be serialised by the caller.
+ * The device address of each GPU's array is looked up on the first call on
+ * that device (TTT_ERR_HIP if the lookup fails). */
+#define TTT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ttt_status ttt_layer_forward_noalloc(const ttt_desc* desc,
+                                     const void* H, const void* X0,
+                                     const void* Wg, const void* Wu,
+                                     const void* W_down0, const void* conv_taps,
+                                     const void* W_target, float eta, int32_t chunk,
+                                     void* O, float* W_down_final, void* stream);
+
 /* Update-norm clipping (iplexlaw explainer §6: the Frobenius norm of the
  * update delta is limited to a threshold): as ttt_layer_forward, except that
  * every chunk's update eta * V_i^T Z_i is first scaled by

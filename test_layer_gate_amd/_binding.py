@@ -98,9 +98,12 @@ def lib() -> ctypes.CDLL:
     L.ttt_decode_begin.argtypes = [DP, ctypes.c_int32, _P, _P, _S, _P]
     L.ttt_decode_step.argtypes = [DP, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
                                   ctypes.c_int32, _P, _P, _S, _P, _P]
+    L.ttt_layer_forward_noalloc.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                            ctypes.c_int32, _P, _P, _P]
     L.ttt_gated_activation.argtypes = [DP, _P, _P, _P, _P, _P, _S, _P]
     L.ttt_lm_target.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _S, _P]
     for fn in ("ttt_workspace_size", "ttt_step_workspace_size", "ttt_layer_forward",
+               "ttt_layer_forward_noalloc",
                "ttt_packed_workspace_size", "ttt_layer_forward_packed",
                "ttt_clipped_workspace_size", "ttt_layer_forward_clipped",
                "ttt_packed_clipped_workspace_size", "ttt_layer_forward_packed_clipped",

@@ -336,6 +336,13 @@ T* at(void* base, size_t off) {
 
 }  // namespace
 
+namespace tttk_api {
+// The error record of the other translation units' entry points.
+__attribute__((visibility("hidden"))) ttt_status set_error(ttt_status s, const std::string& msg) {
+  return fail(s, msg);
+}
+}  // namespace tttk_api
+
 extern "C" {
 
 const char* ttt_status_string(int32_t s) {

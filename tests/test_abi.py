@@ -492,3 +492,22 @@ def test_decode_step_validates_before_launch(L):
                               None) == WORKSPACE
     assert L.ttt_decode_begin(ctypes.byref(decode_desc(flags=0)), 1024, p[6], p[9],
                               ctypes.c_size_t(1 << 62), None) == UNSUPPORTED
+
+
+# ---- the no-allocation entry point ------------------------------------------
+
+def test_noalloc_rejects_problems_beyond_its_scratch(L):
+    """A workload whose workspace exceeds the static scratch is refused with
+    TTT_ERR_WORKSPACE on the host, before any HIP call (this runs without a
+    GPU)."""
+    p = good_ptrs()
+    desc = qwen_desc()
+    st = L.ttt_layer_forward_noalloc(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3), 1024,
+                                     p[7], p[8], None)
+    assert st == WORKSPACE
+    msg = L.ttt_last_error().decode()
+    assert "static scratch" in msg and str(64 << 20) in msg
+    desc = qwen_desc(batch=0)
+    st = L.ttt_layer_forward_noalloc(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3), 1024,
+                                     p[7], p[8], None)
+    assert st == INVALID
