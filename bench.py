@@ -54,7 +54,10 @@ KERNEL_NAMES = {"gate_up": "gate_up_kernel", "target": "target_kernel",
                 "apply": "apply_kernel", "conv": "conv_kernel",
                 "transpose_w_target": "transpose_kernel", "cast_bf16": "cast_kernel",
                 "pack_weights": "pack_weight_kernel",
-                "calibration_copy": "calibration_copy_kernel"}
+                "calibration_copy": "calibration_copy_kernel",
+                "range_clear": "range_clear_kernel", "amax": "amax_kernel",
+                "conv_repair": "conv_repair_kernel", "gate_up_repair": "gate_up_repair_kernel",
+                "target_repair": "target_repair_kernel"}
 
 
 def kernel_work(name, cfg, T_pad):

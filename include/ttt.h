@@ -106,9 +106,17 @@ ttt_status ttt_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes
  *   O         [B, T, d]  act_dtype   out
  *   W_down_final [B, d, f] float32   out, the state after the last chunk
  *   workspace            >= ttt_workspace_size() bytes, 256-byte aligned
- * Every pointer must be 16-byte aligned. Arithmetic: bf16 operands with
- * fp32 accumulation; Z and V are stored in bf16, the state in fp32, and the
- * apply reads a bf16 copy of each chunk's state. */
+ * Every pointer must be 16-byte aligned. Arithmetic: every contraction
+ * accumulates in fp32. The gate/up projection and the apply take bf16
+ * operands: Z is stored in bf16 token-major for the apply, which reads a bf16
+ * copy of each chunk's state. The target and the update take fp16 operands
+ * (3 more mantissa bits, for the fp32 state's accuracy): conv(X0) and
+ * W_target^T for the target, a feature-major fp16 copy of Z and eta * V for
+ * the update. Those fp16 copies are kept in fp16's range whatever the
+ * inputs' magnitudes: each producer notes its largest |value|, and a copy
+ * whose maximum falls outside [2^-10, 65504] is written again times a power
+ * of two that brings it to [2^14, 2^15), which its consumers divide back out
+ * (exact). The state is fp32 throughout; O is act_dtype. */
 ttt_status ttt_layer_forward(const ttt_desc* desc,
                              const void* H, const void* X0,
                              const void* Wg, const void* Wu,

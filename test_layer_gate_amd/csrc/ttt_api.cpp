@@ -92,7 +92,7 @@ struct Geo {
 
 struct Layout {
   size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgp = 0, wup = 0,
-         blk = 0, vrow = 0, gram = 0, partial = 0, scale = 0, x0n = 0;
+         blk = 0, vrow = 0, gram = 0, partial = 0, scale = 0, x0n = 0, range = 0;
   size_t total = 0;
 };
 
@@ -107,6 +107,7 @@ Layout forward_layout(const Geo& g) {
     return o;
   };
   const tttk::Dims& D = g.dims;
+  L.range = take(tttk::kRangeWords * 4);
   L.y = take(g.B * g.T_pad * D.ld_y * 2);
   L.wtt = take(g.d * D.ld_y * 2);
   L.z = take(g.B * g.T * D.ld_z * 2);
@@ -145,6 +146,7 @@ Layout step_layout(const Geo& g) {
     off = align256(off + bytes);
     return o;
   };
+  L.range = take(tttk::kRangeWords * 4);
   L.y = take(g.B * g.T_pad * g.dims.ld_y * 2);
   L.wtt = take(g.d * g.dims.ld_y * 2);
   if (g.act_f32) {
@@ -383,16 +385,17 @@ namespace {
 
 // The update's operands are fp16 with the target scaled by vscale = eta *
 // 2^p, p = round(-log2 |eta|), so that eta * V sits at V's own magnitude;
-// the state is carried as 2^p * W in fp32 and every output is multiplied
-// back by 2^-p. Powers of two make both scalings exact.
-void update_scales(float eta, float* vscale, float* acc_scale) {
+// the state is carried as 2^p * W in fp32 (times the operands' own range
+// exponents, read on the device) and every output is multiplied back. Powers
+// of two make the scalings exact.
+void update_scales(float eta, float* vscale, int* p_out) {
   *vscale = 0.0f;
-  *acc_scale = 1.0f;
+  *p_out = 0;
   if (eta != 0.0f) {
     long p = std::lround(-std::log2(std::fabs((double)eta)));
     p = std::max(-60L, std::min(60L, p));
-    *acc_scale = std::ldexp(1.0f, (int)p);
-    *vscale = eta * *acc_scale;
+    *p_out = (int)p;
+    *vscale = eta * std::ldexp(1.0f, (int)p);
   }
 }
 
@@ -499,6 +502,8 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
   }
   uint16_t* Wgp = at<uint16_t>(workspace, L.wgp);
   uint16_t* Wup = at<uint16_t>(workspace, L.wup);
+  uint32_t* range = at<uint32_t>(workspace, L.range);
+  TTT_LAUNCH("range_clear", s, tttk::launch_range_clear(range, s));
   TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wg, g.w_f32, Wgp, D, s));
   TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wu, g.w_f32, Wup, D, s));
   uint16_t* Y = at<uint16_t>(workspace, L.y);
@@ -508,28 +513,45 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
   uint16_t* VT = at<uint16_t>(workspace, L.vt);
   uint16_t* snap = at<uint16_t>(workspace, L.snap);
 
-  float vscale, acc_scale;
-  update_scales(eta, &vscale, &acc_scale);
+  float vscale;
+  int p;
+  update_scales(eta, &vscale, &p);
 
+  // The fp16 copies (W_target^T, conv(X0), Z^T, V^T) keep their values in
+  // fp16's range: each producer notes its largest |value| and a repair launch
+  // rewrites the copy times 2^q when that maximum is out of range (it
+  // returns at once otherwise); the consumers divide 2^q back out.
+  TTT_LAUNCH("amax", s,
+             tttk::launch_amax(W_target, g.w_f32, g.d * g.d, range + tttk::kRangeWt * tttk::kRangeSlots, s));
   TTT_LAUNCH("transpose_w_target", s,
-             tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, D.ld_y, s));
+             tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, D.ld_y,
+                                        range + tttk::kRangeWt * tttk::kRangeSlots, s));
+  uint32_t* range_y = range + tttk::kRangeY * tttk::kRangeSlots;
   TTT_LAUNCH("conv", s,
              tttk::launch_conv(X0b, X0nb, n_next, conv_taps, g.w_f32, Y, D, (int)g.K, (int)g.C,
-                               g.pad_chunk, blocks, s));
-  TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, s));
+                               g.pad_chunk, blocks, range_y, s));
+  TTT_LAUNCH("conv_repair", s,
+             tttk::launch_conv_repair(X0b, X0nb, n_next, conv_taps, g.w_f32, Y, D, (int)g.K,
+                                      (int)g.C, g.pad_chunk, blocks, range_y, s));
+  uint32_t* range_z = range + tttk::kRangeZ * tttk::kRangeSlots;
+  TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, range_z, s));
+  TTT_LAUNCH("gate_up_repair", s, tttk::launch_gate_up_repair(Hb, Wgp, Wup, ZT, D, range_z, s));
   const bool clip = g.clip > 0.0f && eta != 0.0f;
   uint16_t* Vrow = clip ? at<uint16_t>(workspace, L.vrow) : nullptr;
-  TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, Vrow, vscale, D, s));
+  TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, Vrow, vscale, D, range, s));
+  TTT_LAUNCH("target_repair", s,
+             tttk::launch_target_repair(Y, WtT, VT, Vrow, vscale, p, D, range, s));
   if (clip) {
     // Every chunk's update eta V_i^T Z_i is scaled to a Frobenius norm of at
     // most g.clip by scaling its columns of VT; the norm comes from the rows
-    // of vscale * V, hence the factor |eta| / vscale.
+    // of vscale * V (times V's range exponent, which the kernel divides out),
+    // hence the factor |eta| / vscale.
     TTT_LAUNCH("clip_scale", s,
                tttk::launch_clip_scale(Z, Vrow, at<float>(workspace, L.gram),
                                        at<float>(workspace, L.partial),
                                        at<float>(workspace, L.scale), VT, D, (int)g.C,
                                        (int)g.nchunks, spans, blocks, std::fabs(eta) / vscale,
-                                       g.clip, s));
+                                       g.clip, range, p, s));
   }
 
   const int64_t snap_cstride = tttk::snap_elems(D);
@@ -537,7 +559,7 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
     // Materialised exclusive prefix: snapshot i = bf16(W^(i)) for every chunk,
     // W_down_final = W^(k); then every chunk's output in one launch.
     TTT_LAUNCH("update_prefix", s,
-               tttk::launch_update(ZT, VT, W_down0, w0_f32, w0_stride, g.f, acc_scale, snap,
+               tttk::launch_update(ZT, VT, W_down0, w0_f32, w0_stride, g.f, p, range, snap,
                                    g.nchunks * snap_cstride, W_down_final, nullptr, D, 0,
                                    (int)g.T, (int)g.C, blocks, (int)g.nchunks, s));
     TTT_LAUNCH("apply", s,
@@ -550,14 +572,14 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
     for (const Chunk& c : g.chunks) {
       if (c.doc_start)
         TTT_LAUNCH("update_running", s,
-                   tttk::launch_update(ZT, VT, W_down0, w0_f32, w0_stride, g.f, acc_scale,
+                   tttk::launch_update(ZT, VT, W_down0, w0_f32, w0_stride, g.f, p, range,
                                        nullptr, 0, W_down_final, snap, D, 0, 0, (int)g.C,
                                        nullptr, 1, s));
       TTT_LAUNCH("apply", s,
                  tttk::launch_apply(Z, snap, snap_cstride, 0, O, g.act_f32, D, c.t0, c.t1,
                                     (int)g.C, nullptr, 0, 1, s));
       TTT_LAUNCH("update_running", s,
-                 tttk::launch_update(ZT, VT, W_down_final, true, df, g.f, acc_scale, nullptr, 0,
+                 tttk::launch_update(ZT, VT, W_down_final, true, df, g.f, p, range, nullptr, 0,
                                      W_down_final, snap, D, c.t0, c.t1 - c.t0, (int)g.C,
                                      nullptr, 1, s));
     }
@@ -732,7 +754,8 @@ namespace {
 // reads, the open chunk's Z^T and X0 rows, and the chunk-end scratch (Y,
 // W_target^T, V^T) and per-token scratch (z, the apply's partial sums).
 struct DecodeLayout {
-  size_t shadow = 0, zt = 0, x0c = 0, zb = 0, part = 0, y = 0, wtt = 0, vt = 0, total = 0;
+  size_t shadow = 0, zt = 0, x0c = 0, zb = 0, part = 0, y = 0, wtt = 0, vt = 0, zc = 0,
+         range = 0, total = 0;
 };
 
 DecodeLayout decode_layout(const Geo& g, const tttk::Dims& Dc) {
@@ -751,6 +774,8 @@ DecodeLayout decode_layout(const Geo& g, const tttk::Dims& Dc) {
   L.y = take(g.B * Dc.T_pad * Dc.ld_y * 2);
   L.wtt = take(g.d * Dc.ld_y * 2);
   L.vt = take(tttk::vt_elems(Dc) * 2);
+  L.zc = take(g.B * g.C * g.f * 4);
+  L.range = take(tttk::kRangeWords * 4);
   L.total = off;
   return L;
 }
@@ -807,12 +832,13 @@ ttt_status ttt_decode_begin(const ttt_desc* desc, int32_t chunk, float* W_state,
   TTT_TRY(check_aliasing({}, {range_of("W_state", W_state, g.B * g.d * g.f * 4),
                               range_of("decode_state", decode_state, L.total)}));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // An update over no tokens: W_state is stored back unchanged and its bf16
-  // copy written.
+  // The open chunk's range buffer starts empty; an update over no tokens
+  // stores W_state back unchanged and writes its bf16 copy.
+  TTT_LAUNCH("range_clear", s, tttk::launch_range_clear(at<uint32_t>(decode_state, L.range), s));
   TTT_LAUNCH("decode_begin", s,
              tttk::launch_update(at<uint16_t>(decode_state, L.zt),
                                  at<uint16_t>(decode_state, L.vt), W_state, true, g.d * g.f,
-                                 g.f, 1.0f, nullptr, 0, W_state,
+                                 g.f, 0, nullptr, nullptr, 0, W_state,
                                  at<uint16_t>(decode_state, L.shadow), Dc, 0, 0, (int)g.C,
                                  nullptr, 1, s));
   return TTT_OK;
@@ -852,33 +878,51 @@ ttt_status ttt_decode_step(const ttt_desc* desc, const void* h, const void* x0, 
   uint16_t* zt = at<uint16_t>(decode_state, L.zt);
   uint16_t* x0c = at<uint16_t>(decode_state, L.x0c);
   uint16_t* zb = at<uint16_t>(decode_state, L.zb);
+  float* zc = at<float>(decode_state, L.zc);
+  uint32_t* range = at<uint32_t>(decode_state, L.range);
+  const int64_t zt_bstride = tttk::sb_elems<tttk::kZtSlab>(g.f, Dc.T_pad);
   TTT_LAUNCH("decode_gate_up", s,
              tttk::launch_decode_gate_up(h, x0, g.act_f32, Wg, Wu, g.w_f32, (int)g.B, (int)g.d,
-                                         (int)g.f, zb, zt,
-                                         tttk::sb_elems<tttk::kZtSlab>(g.f, Dc.T_pad),
-                                         (int)Dc.T_pad, x0c, C, r, s));
+                                         (int)g.f, zb, zc, zt, zt_bstride, (int)Dc.T_pad, x0c, C,
+                                         r, range, s));
   TTT_LAUNCH("decode_apply", s,
              tttk::launch_decode_apply(zb, shadow, tttk::snap_elems(Dc), (int)g.B, (int)g.d,
                                        (int)g.f, at<float>(decode_state, L.part), o, g.act_f32,
                                        s));
   if (r == C - 1) {
-    // The chunk is complete: its target (reads inside the chunk only), then
-    // its update, in place, with the bf16 copy refreshed for the next chunk.
-    float vscale, acc_scale;
-    update_scales(eta, &vscale, &acc_scale);
+    // The chunk is complete: its Z^T brought into fp16's range if needed, its
+    // target (reads inside the chunk only, with the same range guards as the
+    // prefill), then its update, in place, with the bf16 copy refreshed for
+    // the next chunk; the range buffer is cleared for the next chunk.
+    float vscale;
+    int p;
+    update_scales(eta, &vscale, &p);
     uint16_t* y = at<uint16_t>(decode_state, L.y);
     uint16_t* wtt = at<uint16_t>(decode_state, L.wtt);
     uint16_t* vt = at<uint16_t>(decode_state, L.vt);
+    uint32_t* range_wt = range + tttk::kRangeWt * tttk::kRangeSlots;
+    uint32_t* range_y = range + tttk::kRangeY * tttk::kRangeSlots;
+    TTT_LAUNCH("decode_zt_repair", s,
+               tttk::launch_decode_zt_repair(zc, zt, (int)g.B, (int)g.f, C, zt_bstride,
+                                             (int)Dc.T_pad, range, s));
+    TTT_LAUNCH("amax", s, tttk::launch_amax(W_target, g.w_f32, g.d * g.d, range_wt, s));
     TTT_LAUNCH("transpose_w_target", s,
                tttk::launch_transpose_f16(W_target, g.w_f32, wtt, (int)g.d, (int)g.d, Dc.ld_y,
-                                          s));
+                                          range_wt, s));
     TTT_LAUNCH("conv", s,
                tttk::launch_conv(x0c, nullptr, 0, conv_taps, g.w_f32, y, Dc, (int)g.K, C, true,
-                                 nullptr, s));
-    TTT_LAUNCH("target", s, tttk::launch_target(y, wtt, vt, nullptr, nullptr, vscale, Dc, s));
+                                 nullptr, range_y, s));
+    TTT_LAUNCH("conv_repair", s,
+               tttk::launch_conv_repair(x0c, nullptr, 0, conv_taps, g.w_f32, y, Dc, (int)g.K, C,
+                                        true, nullptr, range_y, s));
+    TTT_LAUNCH("target", s,
+               tttk::launch_target(y, wtt, vt, nullptr, nullptr, vscale, Dc, range, s));
+    TTT_LAUNCH("target_repair", s,
+               tttk::launch_target_repair(y, wtt, vt, nullptr, vscale, p, Dc, range, s));
     TTT_LAUNCH("update_running", s,
-               tttk::launch_update(zt, vt, W_state, true, g.d * g.f, g.f, acc_scale, nullptr, 0,
+               tttk::launch_update(zt, vt, W_state, true, g.d * g.f, g.f, p, range, nullptr, 0,
                                    W_state, shadow, Dc, 0, C, C, nullptr, 1, s));
+    TTT_LAUNCH("range_clear", s, tttk::launch_range_clear(range, s));
   }
   return TTT_OK;
 }
@@ -917,7 +961,7 @@ ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void*
   TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wg, g.w_f32, Wgp, D, s));
   TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wu, g.w_f32, Wup, D, s));
   TTT_LAUNCH("gate_up", s,
-             tttk::launch_gate_up(Hb, Wgp, Wup, static_cast<uint16_t*>(Z), nullptr, D, s));
+             tttk::launch_gate_up(Hb, Wgp, Wup, static_cast<uint16_t*>(Z), nullptr, D, nullptr, s));
   return TTT_OK;
 }
 
@@ -951,15 +995,23 @@ ttt_status ttt_lm_target(const ttt_desc* desc, const void* X0, const void* conv_
   }
   uint16_t* Y = at<uint16_t>(workspace, L.y);
   uint16_t* WtT = at<uint16_t>(workspace, L.wtt);
+  uint32_t* range = at<uint32_t>(workspace, L.range);
+  uint32_t* range_y = range + tttk::kRangeY * tttk::kRangeSlots;
+  TTT_LAUNCH("range_clear", s, tttk::launch_range_clear(range, s));
+  TTT_LAUNCH("amax", s,
+             tttk::launch_amax(W_target, g.w_f32, g.d * g.d, range + tttk::kRangeWt * tttk::kRangeSlots, s));
   TTT_LAUNCH("transpose_w_target", s,
              tttk::launch_transpose_f16(W_target, g.w_f32, WtT, (int)g.d, (int)g.d, g.dims.ld_y,
-                                        s));
+                                        range + tttk::kRangeWt * tttk::kRangeSlots, s));
   TTT_LAUNCH("conv", s,
              tttk::launch_conv(X0b, nullptr, 0, conv_taps, g.w_f32, Y, g.dims, (int)g.K,
-                               (int)g.C, g.pad_chunk, nullptr, s));
+                               (int)g.C, g.pad_chunk, nullptr, range_y, s));
+  TTT_LAUNCH("conv_repair", s,
+             tttk::launch_conv_repair(X0b, nullptr, 0, conv_taps, g.w_f32, Y, g.dims, (int)g.K,
+                                      (int)g.C, g.pad_chunk, nullptr, range_y, s));
   TTT_LAUNCH("target", s,
              tttk::launch_target(Y, WtT, nullptr, static_cast<uint16_t*>(V), nullptr, 1.0f,
-                                 g.dims, s));
+                                 g.dims, range, s));
   return TTT_OK;
 }
 

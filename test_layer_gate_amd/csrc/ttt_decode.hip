@@ -48,17 +48,19 @@ __device__ __forceinline__ void load8_bf16(const void* p, int64_t i, float (&v)[
 
 // Gated activation of one token per sequence: for row j of W_g and W_u
 // (one wave per row), z[b][j] = SiLU(h_b . Wg[j]) * (h_b . Wu[j]). z goes to
-// zb (bf16, the apply's operand) and, as fp16, to column `col` of the
-// chunk's Z^T (sb<256> rows j, zt_cols columns) for the chunk's update:
-// the same roundings as the prefill's Z and Z^T. The threads of the first
-// blocks also copy the token's X0 rows (as bf16) into row `col` of the
-// chunk's X0 buffer [B][chunk][d].
+// zb (bf16, the apply's operand) and to row `col` of the chunk's fp32 rows
+// zc [B][chunk][f], and, as fp16, to column `col` of the chunk's Z^T
+// (sb<256> rows j, zt_cols columns) for the chunk's update: the same
+// roundings as the prefill's Z and Z^T. The largest |z| goes to the Z group
+// of the chunk's range buffer (zrange), which the chunk's close checks. The
+// threads of the first blocks also copy the token's X0 rows (as bf16) into
+// row `col` of the chunk's X0 buffer [B][chunk][d].
 template <bool ACT_F32, bool W_F32>
 __global__ __launch_bounds__(kDecThreads) void decode_gate_up_kernel(
     const void* __restrict__ h, const void* __restrict__ x0, const void* __restrict__ Wg,
     const void* __restrict__ Wu, int B, int d, int f, u16* __restrict__ zb,
-    u16* __restrict__ zt, int64_t zt_bstride, int zt_cols, u16* __restrict__ x0c, int chunk,
-    int col) {
+    float* __restrict__ zc, u16* __restrict__ zt, int64_t zt_bstride, int zt_cols,
+    u16* __restrict__ x0c, int chunk, int col, uint32_t* __restrict__ zrange) {
   const int64_t gid = (int64_t)blockIdx.x * kDecThreads + threadIdx.x;
   if (gid < (int64_t)B * d / 8) {
     const int b = (int)(gid / (d / 8)), c = (int)(gid % (d / 8)) * 8;
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gate_up_kernel(
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * (kDecThreads / 64) + (threadIdx.x >> 6);
   if (j >= f) return;  // uniform per wave
+  float zmax = 0.0f;
   for (int b0 = 0; b0 < B; b0 += kDecMaxB) {
     const int nb = min(kDecMaxB, B - b0);
     float g[kDecMaxB], u[kDecMaxB];
@@ -99,11 +102,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_gate_up_kernel(
         const float gs = wave_sum(g[b]), us = wave_sum(u[b]);
         if (lane == 0) {
           const float z = silu(gs) * us;
+          zmax = fmaxf(zmax, fabsf(z));
           zb[(int64_t)(b0 + b) * f + j] = bf16_rne(z);
+          zc[((int64_t)(b0 + b) * chunk + col) * f + j] = z;
           zt[(int64_t)(b0 + b) * zt_bstride + sb_offset<kZtSlab>(j, col, zt_cols)] = f16_rne(z);
         }
       }
     }
+  }
+  range_note(zrange + kRangeZ * kRangeSlots, zmax);
+}
+
+// At a chunk's close: if the chunk's largest |z| is out of the fp16 range,
+// Z^T again from the chunk's fp32 rows, times 2^qz (the update divides it
+// out), as the prefill's repaired Z^T; otherwise returns at once.
+__global__ __launch_bounds__(kDecThreads) void decode_zt_repair_kernel(
+    const float* __restrict__ zc, u16* __restrict__ zt, int B, int f, int chunk, int64_t zt_bstride,
+    int zt_cols, const uint32_t* __restrict__ zrange) {
+  const int q = range_exp(range_read(zrange + kRangeZ * kRangeSlots));
+  if (q == 0) return;
+  const float sc = exp2i(q);
+  const int64_t n = (int64_t)B * chunk * f;
+  for (int64_t i = (int64_t)blockIdx.x * kDecThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kDecThreads) {
+    const int j = (int)(i % f);
+    const int64_t bc = i / f;
+    const int col = (int)(bc % chunk), b = (int)(bc / chunk);
+    zt[(int64_t)b * zt_bstride + sb_offset<kZtSlab>(j, col, zt_cols)] = f16_rne(zc[i] * sc);
   }
 }
 
@@ -180,13 +205,15 @@ int64_t decode_apply_part_floats(int B, int d) { return (int64_t)B * kApplySplit
 
 hipError_t launch_decode_gate_up(const void* h, const void* x0, bool act_f32, const void* Wg,
                                  const void* Wu, bool w_f32, int B, int d, int f, uint16_t* zb,
-                                 uint16_t* zt, int64_t zt_bstride, int zt_cols, uint16_t* x0c,
-                                 int chunk, int col, hipStream_t s) {
+                                 float* zc, uint16_t* zt, int64_t zt_bstride, int zt_cols,
+                                 uint16_t* x0c, int chunk, int col, uint32_t* zrange,
+                                 hipStream_t s) {
   // One wave per row of W_g / W_u, and enough threads for the X0 copy.
   const int grid = max(ceil_div_i(f, kDecThreads / 64), ceil_div_i((int64_t)B * d / 8, kDecThreads));
-#define TTT_DEC_GU(A, W)                                                                  \
-  decode_gate_up_kernel<A, W><<<grid, kDecThreads, 0, s>>>(h, x0, Wg, Wu, B, d, f, zb, zt, \
-                                                            zt_bstride, zt_cols, x0c, chunk, col)
+#define TTT_DEC_GU(A, W)                                                                     \
+  decode_gate_up_kernel<A, W><<<grid, kDecThreads, 0, s>>>(h, x0, Wg, Wu, B, d, f, zb, zc, zt, \
+                                                            zt_bstride, zt_cols, x0c, chunk, col, \
+                                                            zrange)
   if (act_f32 && w_f32)
     TTT_DEC_GU(true, true);
   else if (act_f32)
@@ -196,6 +223,15 @@ hipError_t launch_decode_gate_up(const void* h, const void* x0, bool act_f32, co
   else
     TTT_DEC_GU(false, false);
 #undef TTT_DEC_GU
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_zt_repair(const float* zc, uint16_t* zt, int B, int f, int chunk,
+                                  int64_t zt_bstride, int zt_cols, const uint32_t* zrange,
+                                  hipStream_t s) {
+  const int grid = min(ceil_div_i((int64_t)B * chunk * f, kDecThreads), 1024);
+  decode_zt_repair_kernel<<<grid, kDecThreads, 0, s>>>(zc, zt, B, f, chunk, zt_bstride, zt_cols,
+                                                       zrange);
   return hipGetLastError();
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ttt_launch.h"
+
 namespace tttk {
 
 typedef uint16_t u16;
@@ -35,5 +37,83 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
+
+// ---------------------------------------------------------------- ranges
+// Several operands are kept as fp16 copies (10 mantissa bits; normal values
+// from 2^-14 to 65504): the update's Z^T and V^T, and the target's conv(X0)
+// and W_target^T. Each producer notes the largest |value| it writes in
+// kRangeSlots words of a range group (the bits of the non-negative float,
+// combined with atomicMax, spread over the words so that atomics on one
+// address stay rare). When that maximum leaves [2^-10, 65504], the operand
+// is written again times 2^q, with q bringing the maximum into [2^14, 2^15),
+// and its consumers divide 2^q back out. Powers of two make both exact.
+// (kRangeSlots, the group indices and the exponent limits: ttt_launch.h)
+
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
+}
+
+// Notes m (this lane's largest |value|, >= 0) in a range group; every lane
+// of the wave must call it. One atomicMax per wave (for kernels with long
+// workgroups, where these are rare).
+__device__ __forceinline__ void range_note(uint32_t* group, float m) {
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) {
+    const uint32_t slot = (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) % kRangeSlots;
+    atomicMax(group + slot, __float_as_uint(m));
+  }
+}
+
+// The same with one atomicMax per workgroup of NT threads (for short
+// workgroups, whose per-wave atomics would queue on the words); every thread
+// of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ void range_note_block(uint32_t* group, float m) {
+  __shared__ float red[NT / 64];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+    atomicMax(group + blockIdx.x % kRangeSlots, __float_as_uint(m));
+  }
+}
+
+// The largest |value| noted in a range group; every lane of the wave must
+// call it.
+__device__ __forceinline__ float range_read(const uint32_t* group) {
+  static_assert(kRangeSlots % 64 == 0, "range words per lane");
+  uint32_t v = 0u;
+#pragma unroll
+  for (int i = 0; i < kRangeSlots / 64; ++i) v = max(v, group[i * 64 + (threadIdx.x & 63)]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return __uint_as_float(v);
+}
+
+// The exponent q that brings a maximum a into [2^14, 2^15), or 0 when a is
+// already in [2^-10, 65504], or is 0, NaN or infinite (those propagate).
+__device__ __forceinline__ int range_exp(float a) {
+  if (!(a > 0.0f) || !(a < __builtin_huge_valf())) return 0;
+  if (a >= 0x1p-10f && a <= 65504.0f) return 0;
+  int e = 0;
+  (void)frexpf(a, &e);  // a = m 2^e, m in [0.5, 1): floor(log2 a) = e - 1
+  return min(max(15 - e, -kRangeMaxExp), kRangeMaxExp);
+}
+
+// The exponents of the update's operands: Z^T holds Z 2^qz and V^T holds
+// eta 2^(p + qv) V, so the state is carried as 2^(p + qv + qz) W. qv is held
+// so that p + qv + qz stays within +-kStateMaxExp (p is eta's, within +-60,
+// and qz within +-40, so qv = 0 is always allowed).
+__device__ __forceinline__ void update_exps(const uint32_t* range, int p, int* qv, int* qz) {
+  *qz = range_exp(range_read(range + kRangeZ * kRangeSlots));
+  const int v = range_exp(range_read(range + kRangeV * kRangeSlots));
+  *qv = min(max(v, -kStateMaxExp - p - *qz), kStateMaxExp - p - *qz);
+}
+
+__device__ __forceinline__ float exp2i(int q) { return ldexpf(1.0f, q); }
 
 }  // namespace tttk

@@ -670,14 +670,16 @@ constexpr int K1_LDZ = K1_BN / 2 + 8;  // row stride of the Z staging tile in LD
 static_assert(K1_BM * K1_LDZ <= (K1_NSTA * K1_BM + K1_NSTB * K1_BN) * K1_BK,
               "Z staging fits the stages");
 
-__global__ __launch_bounds__(64 * K1_NW) void gate_up_kernel(
-    const u16* __restrict__ H, const u16* __restrict__ Wgp, const u16* __restrict__ Wup,
-    u16* __restrict__ Z, u16* __restrict__ ZT, Dims g, int tiles_m, int tiles_n) {
+// One gate/up tile: Z (bf16, token-major, unless null) and zscale * Z
+// (fp16, ZT, unless null). Returns the largest |Z| of this lane's values.
+__device__ __forceinline__ float gate_up_tile(const TileIdx& ti, u16* lds,
+                                              const u16* __restrict__ H,
+                                              const u16* __restrict__ Wgp,
+                                              const u16* __restrict__ Wup, u16* __restrict__ Z,
+                                              u16* __restrict__ ZT, const Dims& g, float zscale) {
   using L = Layout<K1_BM, K1_BN, K1_WGM, K1_NW>;
   constexpr int NG = L::TN / 2;  // gate tiles per wave (and as many up tiles)
   static_assert(NG >= 1 && L::TN == 2 * NG, "gate and up tiles pair up");
-  TTT_GEMM_LDS_AB(lds, K1_BM, K1_BN, K1_BK, K1_NSTA, K1_NSTB)
-  const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K1_BM, j0 = ti.tn * (K1_BN / 2);
   const int d = g.d, f = g.f;
   f32x16 acc[L::TM][L::TN];
@@ -690,6 +692,7 @@ __global__ __launch_bounds__(64 * K1_NW) void gate_up_kernel(
       blocked<K1_BK>(Wgp + wslab, kWRows, nk), blocked<K1_BK>(Wup + wslab, kWRows, nk), nk,
       &acc[0][0], lds, NoHook{}, k_rotation<4>(ti.tm, ti.tn, nk));
   const Frag<L> fr;
+  float zmax = 0.0f;
   // Token-major Z goes through LDS so that its stores are whole 16-byte row
   // segments.
   constexpr int WROWS = K1_BM / K1_WGM;  // tile rows per wave row
@@ -701,19 +704,24 @@ __global__ __launch_bounds__(64 * K1_NW) void gate_up_kernel(
       const int j = j0 + jl;
       f32x16 z;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) z[r] = silu(acc[m][n][r]) * acc[m][n + NG][r];
+      for (int r = 0; r < 16; ++r) {
+        z[r] = silu(acc[m][n][r]) * acc[m][n + NG][r];
+        zmax = fmaxf(zmax, fabsf(z[r]));
+      }
       if (ZT != nullptr)
-        store_tile_sb<kZtSlab>(g.T_pad, j, t0 + fr.wm * WROWS + m * 32, z, CvtF16{1.0f}, j < f,
+        store_tile_sb<kZtSlab>(g.T_pad, j, t0 + fr.wm * WROWS + m * 32, z, CvtF16{zscale}, j < f,
                                StreamSink{ZT + ti.b * sb_elems<kZtSlab>(f, g.T_pad)});
+      if (Z != nullptr) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = fr.wm * WROWS + m * 32 + 8 * q + 4 * (fr.lane >> 5);  // tile row
-        u16* sZ = lds + row * K1_LDZ + jl;
+        for (int q = 0; q < 4; ++q) {
+          const int row = fr.wm * WROWS + m * 32 + 8 * q + 4 * (fr.lane >> 5);  // tile row
+          u16* sZ = lds + row * K1_LDZ + jl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sZ[e * K1_LDZ] = bf16_rne(z[4 * q + e]);
+          for (int e = 0; e < 4; ++e) sZ[e * K1_LDZ] = bf16_rne(z[4 * q + e]);
+        }
       }
     }
-  if (Z == nullptr) return;
+  if (Z == nullptr) return zmax;
   __syncthreads();
   constexpr int CHUNKS = K1_BM * (K1_BN / 2) / 8;  // 16-byte row segments in the tile
 #pragma unroll
@@ -726,6 +734,36 @@ __global__ __launch_bounds__(64 * K1_NW) void gate_up_kernel(
       store_stream(Z + ((int64_t)ti.b * g.T + t) * g.ld_z + jj,
                    *reinterpret_cast<const uint4*>(src));
   }
+  return zmax;
+}
+
+// Z and ZT (fp16 at scale 1); the largest |Z| goes to the range group (if
+// not null; only when ZT is written, the fp16 copy it guards).
+__global__ __launch_bounds__(64 * K1_NW) void gate_up_kernel(
+    const u16* __restrict__ H, const u16* __restrict__ Wgp, const u16* __restrict__ Wup,
+    u16* __restrict__ Z, u16* __restrict__ ZT, Dims g, int tiles_m, int tiles_n,
+    uint32_t* __restrict__ range) {
+  TTT_GEMM_LDS_AB(lds, K1_BM, K1_BN, K1_BK, K1_NSTA, K1_NSTB)
+  const float m =
+      gate_up_tile(tile_index(tiles_m, tiles_n, 4), lds, H, Wgp, Wup, Z, ZT, g, 1.0f);
+  if (range != nullptr) range_note(range, m);
+}
+
+// ZT again, times 2^q, when Z's noted maximum is out of the fp16 range;
+// otherwise returns at once. Persistent: a grid of about one workgroup per
+// compute unit walks the tiles.
+__global__ __launch_bounds__(64 * K1_NW) void gate_up_repair_kernel(
+    const u16* __restrict__ H, const u16* __restrict__ Wgp, const u16* __restrict__ Wup,
+    u16* __restrict__ ZT, Dims g, int tiles_m, int tiles_n, const uint32_t* __restrict__ range) {
+  TTT_GEMM_LDS_AB(lds, K1_BM, K1_BN, K1_BK, K1_NSTA, K1_NSTB)
+  const int q = range_exp(range_read(range));
+  if (q == 0) return;
+  const float sc = exp2i(q);
+  for (int lin = blockIdx.x; lin < tiles_m * tiles_n * g.B; lin += gridDim.x) {
+    __syncthreads();  // the previous tile is done with the LDS
+    (void)gate_up_tile(tile_coords(lin, tiles_m, tiles_n, 4), lds, H, Wgp, Wup, nullptr, ZT, g,
+                       sc);
+  }
 }
 
 // ------------------------------------------------------ target GEMM (K2)
@@ -734,13 +772,15 @@ __global__ __launch_bounds__(64 * K1_NW) void gate_up_kernel(
 constexpr int K2_NW = 8, K2_BM = 256, K2_BN = 256, K2_WGM = 2, K2_BK = 64, K2_NSTA = 3,
               K2_NSTB = 2;
 
-__global__ __launch_bounds__(64 * K2_NW) void target_kernel(
-    const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
-    u16* __restrict__ Vtok, u16* __restrict__ Vrow, float vscale, Dims g, int tiles_m,
-    int tiles_n) {
+// One target tile, outputs times out_scale: fp16 VT (feature-major),
+// bf16 Vtok ([B][T][d]) and fp16 Vrow ([B][T_pad][ld_y]), each unless null.
+// Returns the largest |out_scale * V| of this lane's values.
+__device__ __forceinline__ float target_tile(const TileIdx& ti, u16* lds,
+                                             const u16* __restrict__ Y,
+                                             const u16* __restrict__ WtT, u16* __restrict__ VT,
+                                             u16* __restrict__ Vtok, u16* __restrict__ Vrow,
+                                             float out_scale, const Dims& g) {
   using L = Layout<K2_BM, K2_BN, K2_WGM, K2_NW>;
-  TTT_GEMM_LDS_AB(lds, K2_BM, K2_BN, K2_BK, K2_NSTA, K2_NSTB)
-  const TileIdx ti = tile_index(tiles_m, tiles_n, 4);
   const int t0 = ti.tm * K2_BM, c0 = ti.tn * K2_BN;
   const int d = g.d;
   f32x16 acc[L::TM][L::TN];
@@ -752,14 +792,17 @@ __global__ __launch_bounds__(64 * K2_NW) void target_kernel(
       row_major<K2_BK>(Y + ((int64_t)ti.b * g.T_pad + t0) * g.ld_y, g.ld_y, K2_BM), wt, wt, nk,
       &acc[0][0], lds, NoHook{}, k_rotation<4>(ti.tm, ti.tn, nk));
   const Frag<L> fr;
+  float vmax = 0.0f;
 #pragma unroll
   for (int m = 0; m < L::TM; ++m)
 #pragma unroll
     for (int n = 0; n < L::TN; ++n) {
       const int c = c0 + fr.col(n);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, fabsf(acc[m][n][r] * out_scale));
       if (VT != nullptr)
         store_tile_sb<kVtSlab>(g.T_pad, c, t0 + fr.wm * L::TM * 32 + m * 32, acc[m][n],
-                               CvtF16{vscale}, c < d,
+                               CvtF16{out_scale}, c < d,
                                StreamSink{VT + ti.b * sb_elems<kVtSlab>(d, g.T_pad)});
       if (Vtok != nullptr && c < d) {
 #pragma unroll
@@ -768,12 +811,13 @@ __global__ __launch_bounds__(64 * K2_NW) void target_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (t + e < g.T)
-              Vtok[((int64_t)ti.b * g.T + t + e) * d + c] = bf16_rne(acc[m][n][4 * q + e] * vscale);
+              Vtok[((int64_t)ti.b * g.T + t + e) * d + c] =
+                  bf16_rne(acc[m][n][4 * q + e] * out_scale);
         }
       }
     }
-  if (Vrow == nullptr) return;
-  // Token-major fp16 vscale * V ([B][T_pad][ld_y]) through LDS, 128 tile
+  if (Vrow == nullptr) return vmax;
+  // Token-major fp16 out_scale * V ([B][T_pad][ld_y]) through LDS, 128 tile
   // rows per pass (the rows of one wave row), so that its stores are whole
   // 16-byte row segments.
   constexpr int LDV = K2_BN + 8;
@@ -793,7 +837,7 @@ __global__ __launch_bounds__(64 * K2_NW) void target_kernel(
             const int row = m * 32 + 8 * q + 4 * (fr.lane >> 5);
             u16* sv = lds + row * LDV + fr.col(n);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sv[e * LDV] = f16_rne(acc[m][n][4 * q + e] * vscale);
+            for (int e = 0; e < 4; ++e) sv[e * LDV] = f16_rne(acc[m][n][4 * q + e] * out_scale);
           }
     }
     __syncthreads();
@@ -807,6 +851,46 @@ __global__ __launch_bounds__(64 * K2_NW) void target_kernel(
         store_stream(Vrow + ((int64_t)ti.b * g.T_pad + t) * g.ld_y + c,
                      *reinterpret_cast<const uint4*>(lds + row * LDV + cc * 8));
     }
+  }
+  return vmax;
+}
+
+// The exponents W_target^T and conv(X0) were scaled by (their range
+// groups), which the target divides out.
+__device__ __forceinline__ int target_in_exp(const uint32_t* range) {
+  return range_exp(range_read(range + kRangeWt * kRangeSlots)) +
+         range_exp(range_read(range + kRangeY * kRangeSlots));
+}
+
+// V = conv(X0) W_target: outputs at vscale * V; the largest |vscale * V|
+// goes to the range's V group when note_v (the fp16 V^T it guards is
+// written). range may be null (no scaled inputs).
+__global__ __launch_bounds__(64 * K2_NW) void target_kernel(
+    const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
+    u16* __restrict__ Vtok, u16* __restrict__ Vrow, float vscale, Dims g, int tiles_m,
+    int tiles_n, uint32_t* __restrict__ range, int note_v) {
+  TTT_GEMM_LDS_AB(lds, K2_BM, K2_BN, K2_BK, K2_NSTA, K2_NSTB)
+  const float sc = range != nullptr ? vscale * exp2i(-target_in_exp(range)) : vscale;
+  const float m = target_tile(tile_index(tiles_m, tiles_n, 4), lds, Y, WtT, VT, Vtok, Vrow, sc, g);
+  if (range != nullptr && note_v) range_note(range + kRangeV * kRangeSlots, m);
+}
+
+// VT and Vrow again, times 2^qv, when V's noted maximum is out of the fp16
+// range (qv from update_exps, with eta's exponent p); otherwise returns at
+// once. Persistent grid, as gate_up_repair_kernel.
+__global__ __launch_bounds__(64 * K2_NW) void target_repair_kernel(
+    const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
+    u16* __restrict__ Vrow, float vscale, int p, Dims g, int tiles_m, int tiles_n,
+    const uint32_t* __restrict__ range) {
+  TTT_GEMM_LDS_AB(lds, K2_BM, K2_BN, K2_BK, K2_NSTA, K2_NSTB)
+  int qv, qz;
+  update_exps(range, p, &qv, &qz);
+  if (qv == 0) return;
+  const float sc = vscale * exp2i(qv - target_in_exp(range));
+  for (int lin = blockIdx.x; lin < tiles_m * tiles_n * g.B; lin += gridDim.x) {
+    __syncthreads();  // the previous tile is done with the LDS
+    (void)target_tile(tile_coords(lin, tiles_m, tiles_n, 4), lds, Y, WtT, VT, nullptr, Vrow, sc,
+                      g);
   }
 }
 
@@ -938,12 +1022,20 @@ __global__ __launch_bounds__(KG_THREADS) void gram_norm_kernel(
 }
 
 // scale[b][i] = min(1, clip / ||eta V_i^T Z_i||_F), the norm being
-// norm_factor * sqrt(sum of chunk i's npair partials), summed in a fixed
-// order.
+// norm_factor * 2^-qv * sqrt(sum of chunk i's npair partials), summed in a
+// fixed order (the Gram tiles come from V at vscale * 2^qv; qv from the
+// range groups when range is not null).
 __global__ __launch_bounds__(kThreads) void clip_scale_kernel(const float* __restrict__ partial,
                                                              float* __restrict__ scale, int npair,
                                                              int n, float norm_factor,
-                                                             float clip) {
+                                                             float clip,
+                                                             const uint32_t* __restrict__ range,
+                                                             int p) {
+  if (range != nullptr) {
+    int qv, qz;
+    update_exps(range, p, &qv, &qz);
+    norm_factor *= exp2i(-qv);
+  }
   const int idx = blockIdx.x * kThreads + threadIdx.x;
   if (idx >= n) return;
   double s2 = 0.0;
@@ -1237,14 +1329,24 @@ __device__ __forceinline__ void update_tile(
 // rest take the two narrow halves of each remaining region (regions in
 // tile_coords order over regions_m x regions_n 256 x 256 regions per
 // sequence, group 4).
+// The state is carried as acc_scale * W, acc_scale = 2^(p + qv + qz): eta's
+// exponent p and the operands' range exponents (none when range is null).
 template <bool WINIT_F32, bool PACKED>
 __global__ __launch_bounds__(64 * K3_NW) void update_kernel(
     const u16* __restrict__ ZT, const u16* __restrict__ VT, const void* __restrict__ Winit,
-    int64_t winit_bstride, int64_t winit_ld, float acc_scale, u16* __restrict__ snap,
-    int64_t snap_bstride, float* __restrict__ Wf, u16* __restrict__ shadow, Dims g,
-    int tok_begin, int nk, int steps_per_chunk, const BlockInfo* __restrict__ blocks,
-    int n_chunks, int regions_m, int regions_n, int n_wide) {
+    int64_t winit_bstride, int64_t winit_ld, int p, const uint32_t* __restrict__ range,
+    u16* __restrict__ snap, int64_t snap_bstride, float* __restrict__ Wf,
+    u16* __restrict__ shadow, Dims g, int tok_begin, int nk, int steps_per_chunk,
+    const BlockInfo* __restrict__ blocks, int n_chunks, int regions_m, int regions_n,
+    int n_wide) {
   __shared__ __attribute__((aligned(16))) u16 lds[kUpdLdsElems];
+  int e = p;
+  if (range != nullptr) {
+    int qv, qz;
+    update_exps(range, p, &qv, &qz);
+    e += qv + qz;
+  }
+  const float acc_scale = exp2i(e);
   StepBits bits{0u, 0u, 0};
   // nk <= kMaxPackedSteps for a packed launch (checked on the host).
   if constexpr (PACKED) bits = load_step_bits(lds, blocks, tok_begin / K3_BK, nk, n_chunks);
@@ -1355,10 +1457,41 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const float* __restrict_
   }
 }
 
+__global__ __launch_bounds__(kThreads) void range_clear_kernel(uint32_t* __restrict__ range) {
+  for (int i = threadIdx.x; i < kRangeWords; i += kThreads) range[i] = 0u;
+}
+
+// Notes max |W| over n elements (bf16, or fp32; n a multiple of 8) in a
+// range group, 16 bytes per load.
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ W, int64_t n,
+                                                        uint32_t* __restrict__ group) {
+  float m = 0.0f;
+  const int64_t per = F32 ? 4 : 8;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n / per;
+       i += (int64_t)gridDim.x * kThreads) {
+    if constexpr (F32) {
+      const float4 x = reinterpret_cast<const float4*>(W)[i];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    } else {
+      const uint4 x = reinterpret_cast<const uint4*>(W)[i];
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[e] << 16)),
+                           fabsf(__uint_as_float(w[e] & 0xffff0000u))));
+    }
+  }
+  range_note_block<kThreads>(group, m);
+}
+
+// dst = fp16(src^T 2^q), q from the range group of src (null: q = 0).
 template <bool F32>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(const void* __restrict__ src,
                                                              u16* __restrict__ dst, int rows,
-                                                             int cols, int64_t ld_dst) {
+                                                             int cols, int64_t ld_dst,
+                                                             const uint32_t* __restrict__ range) {
+  const float sc = range != nullptr ? exp2i(range_exp(range_read(range))) : 1.0f;
   __shared__ float tile[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -1373,7 +1506,7 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(const void* __restr
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) dst[(int64_t)c * ld_dst + r] = f16_rne(tile[tx][i]);
+    if (c < cols && r < rows) dst[(int64_t)c * ld_dst + r] = f16_rne(tile[tx][i] * sc);
   }
 }
 
@@ -1394,18 +1527,15 @@ __device__ __forceinline__ uint4 load_row8(const u16* X0, const u16* Xn, int r, 
   return make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Rows t .. t + kConvRows - 1 and channels c .. c + 7 of sequence b for
+// thread index gid: Y = scale * conv(X0), written as fp16. Returns the
+// largest |conv(X0)| (before the scale) of the thread's outputs.
 template <bool TAPS_F32>
-__global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ X0,
-                                                        const u16* __restrict__ X0n, int n_next,
-                                                        const void* __restrict__ taps,
-                                                        u16* __restrict__ Y, Dims g, int K,
-                                                        int chunk, int pad_chunk,
-                                                        const BlockInfo* __restrict__ blocks,
-                                                        int64_t total) {
-  // Neighbouring row windows overlap by K - 1 rows; keeping them on one XCD
-  // lets the overlap come from that XCD's L2.
-  const int64_t gid = (int64_t)xcd_contiguous_id() * kThreads + threadIdx.x;
-  if (gid >= total) return;
+__device__ __forceinline__ float conv_rows(int64_t gid, const u16* __restrict__ X0,
+                                           const u16* __restrict__ X0n, int n_next,
+                                           const void* __restrict__ taps, u16* __restrict__ Y,
+                                           const Dims& g, int K, int chunk, int pad_chunk,
+                                           const BlockInfo* __restrict__ blocks, float scale) {
   const int d = g.d, T = g.T;
   const int d8 = d >> 3;
   const int c = (int)(gid % d8) * 8;
@@ -1464,11 +1594,53 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ 
     for (int r = 0; r + 1 < kConvRows; ++r) win[r] = win[r + 1];
     win[kConvRows - 1] = load_row8(xb, xn, t + kConvRows + k, T, n_next, d);
   }
+  float m = 0.0f;
 #pragma unroll
-  for (int r = 0; r < kConvRows; ++r)
+  for (int r = 0; r < kConvRows; ++r) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(acc[r][e]));
     *reinterpret_cast<uint4*>(Y + ((int64_t)b * g.T_pad + t + r) * g.ld_y + c) =
-        make_uint4(pack_f16(acc[r][0], acc[r][1]), pack_f16(acc[r][2], acc[r][3]),
-                   pack_f16(acc[r][4], acc[r][5]), pack_f16(acc[r][6], acc[r][7]));
+        make_uint4(pack_f16(acc[r][0] * scale, acc[r][1] * scale),
+                   pack_f16(acc[r][2] * scale, acc[r][3] * scale),
+                   pack_f16(acc[r][4] * scale, acc[r][5] * scale),
+                   pack_f16(acc[r][6] * scale, acc[r][7] * scale));
+  }
+  return m;
+}
+
+// The conv (scale 1), noting its largest |value| in the range group (if
+// not null).
+template <bool TAPS_F32>
+__global__ __launch_bounds__(kThreads) void conv_kernel(const u16* __restrict__ X0,
+                                                        const u16* __restrict__ X0n, int n_next,
+                                                        const void* __restrict__ taps,
+                                                        u16* __restrict__ Y, Dims g, int K,
+                                                        int chunk, int pad_chunk,
+                                                        const BlockInfo* __restrict__ blocks,
+                                                        int64_t total, uint32_t* __restrict__ range) {
+  // Neighbouring row windows overlap by K - 1 rows; keeping them on one XCD
+  // lets the overlap come from that XCD's L2.
+  const int64_t gid = (int64_t)xcd_contiguous_id() * kThreads + threadIdx.x;
+  float m = 0.0f;
+  if (gid < total)
+    m = conv_rows<TAPS_F32>(gid, X0, X0n, n_next, taps, Y, g, K, chunk, pad_chunk, blocks, 1.0f);
+  if (range != nullptr) range_note_block<kThreads>(range, m);
+}
+
+// Writes Y again times 2^q when the conv's noted maximum is out of the fp16
+// range (q from range_exp); otherwise returns at once. A small persistent
+// grid, so that the usual case costs one short launch.
+template <bool TAPS_F32>
+__global__ __launch_bounds__(kThreads) void conv_repair_kernel(
+    const u16* __restrict__ X0, const u16* __restrict__ X0n, int n_next,
+    const void* __restrict__ taps, u16* __restrict__ Y, Dims g, int K, int chunk, int pad_chunk,
+    const BlockInfo* __restrict__ blocks, int64_t total, const uint32_t* __restrict__ range) {
+  const int q = range_exp(range_read(range));
+  if (q == 0) return;
+  const float sc = exp2i(q);
+  for (int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x; gid < total;
+       gid += (int64_t)gridDim.x * kThreads)
+    (void)conv_rows<TAPS_F32>(gid, X0, X0n, n_next, taps, Y, g, K, chunk, pad_chunk, blocks, sc);
 }
 
 // One thread per 8 packed elements, in packed (destination) order: row
@@ -1529,28 +1701,70 @@ hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStrea
   return hipGetLastError();
 }
 
+hipError_t launch_range_clear(uint32_t* range, hipStream_t s) {
+  range_clear_kernel<<<1, kThreads, 0, s>>>(range);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const void* W, bool w_f32, int64_t n, uint32_t* group, hipStream_t s) {
+  const int64_t vecs = n / (w_f32 ? 4 : 8);
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(ceil_div(vecs, kThreads), 512));
+  if (w_f32)
+    amax_kernel<true><<<blocks, kThreads, 0, s>>>(W, n, group);
+  else
+    amax_kernel<false><<<blocks, kThreads, 0, s>>>(W, n, group);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, int rows, int cols,
-                                int64_t ld_dst, hipStream_t s) {
+                                int64_t ld_dst, const uint32_t* range, hipStream_t s) {
   dim3 grid(ceil_div(cols, 64), ceil_div(rows, 64));
   if (src_f32)
-    transpose_kernel<true><<<grid, kThreads, 0, s>>>(src, dst, rows, cols, ld_dst);
+    transpose_kernel<true><<<grid, kThreads, 0, s>>>(src, dst, rows, cols, ld_dst, range);
   else
-    transpose_kernel<false><<<grid, kThreads, 0, s>>>(src, dst, rows, cols, ld_dst);
+    transpose_kernel<false><<<grid, kThreads, 0, s>>>(src, dst, rows, cols, ld_dst, range);
   return hipGetLastError();
 }
 
 hipError_t launch_conv(const uint16_t* X0, const uint16_t* X0_next, int n_next,
                        const void* taps, bool taps_f32, uint16_t* Y, const Dims& g, int K,
-                       int chunk, bool pad_chunk, const BlockInfo* blocks, hipStream_t s) {
+                       int chunk, bool pad_chunk, const BlockInfo* blocks, uint32_t* range,
+                       hipStream_t s) {
   const int64_t total = (int64_t)g.B * (g.T_pad / kConvRows) * (g.d / 8);
   const int grid = ceil_div(total, kThreads);
   if (n_next == 0) X0_next = X0;  // never read
   if (taps_f32)
     conv_kernel<true><<<grid, kThreads, 0, s>>>(X0, X0_next, n_next, taps, Y, g, K, chunk,
-                                                pad_chunk ? 1 : 0, blocks, total);
+                                                pad_chunk ? 1 : 0, blocks, total, range);
   else
     conv_kernel<false><<<grid, kThreads, 0, s>>>(X0, X0_next, n_next, taps, Y, g, K, chunk,
-                                                 pad_chunk ? 1 : 0, blocks, total);
+                                                 pad_chunk ? 1 : 0, blocks, total, range);
+  return hipGetLastError();
+}
+
+int repair_grid() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  return cus;
+}
+
+hipError_t launch_conv_repair(const uint16_t* X0, const uint16_t* X0_next, int n_next,
+                              const void* taps, bool taps_f32, uint16_t* Y, const Dims& g, int K,
+                              int chunk, bool pad_chunk, const BlockInfo* blocks,
+                              const uint32_t* range, hipStream_t s) {
+  const int64_t total = (int64_t)g.B * (g.T_pad / kConvRows) * (g.d / 8);
+  const int grid = std::min<int64_t>(ceil_div(total, kThreads), 4 * repair_grid());
+  if (n_next == 0) X0_next = X0;  // never read
+  if (taps_f32)
+    conv_repair_kernel<true><<<grid, kThreads, 0, s>>>(X0, X0_next, n_next, taps, Y, g, K, chunk,
+                                                       pad_chunk ? 1 : 0, blocks, total, range);
+  else
+    conv_repair_kernel<false><<<grid, kThreads, 0, s>>>(X0, X0_next, n_next, taps, Y, g, K,
+                                                        chunk, pad_chunk ? 1 : 0, blocks, total,
+                                                        range);
   return hipGetLastError();
 }
 
@@ -1566,18 +1780,39 @@ hipError_t launch_pack_weight(const void* W, bool w_f32, uint16_t* dst, const Di
 }
 
 hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
-                          uint16_t* Z, uint16_t* ZT, const Dims& g, hipStream_t s) {
+                          uint16_t* Z, uint16_t* ZT, const Dims& g, uint32_t* range,
+                          hipStream_t s) {
   const int tiles_m = g.T_pad / K1_BM, tiles_n = ceil_div(g.f, K1_BN / 2);
   gate_up_kernel<<<tiles_m * tiles_n * g.B, 64 * K1_NW, 0, s>>>(H, Wgp, Wup, Z, ZT, g, tiles_m,
-                                                              tiles_n);
+                                                              tiles_n, range);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_repair(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
+                                 uint16_t* ZT, const Dims& g, const uint32_t* range,
+                                 hipStream_t s) {
+  const int tiles_m = g.T_pad / K1_BM, tiles_n = ceil_div(g.f, K1_BN / 2);
+  const int grid = std::min(tiles_m * tiles_n * g.B, repair_grid());
+  gate_up_repair_kernel<<<grid, 64 * K1_NW, 0, s>>>(H, Wgp, Wup, ZT, g, tiles_m, tiles_n, range);
   return hipGetLastError();
 }
 
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
-                         uint16_t* Vrow, float vscale, const Dims& g, hipStream_t s) {
+                         uint16_t* Vrow, float vscale, const Dims& g, uint32_t* range,
+                         hipStream_t s) {
   const int tiles_m = g.T_pad / K2_BM, tiles_n = ceil_div(g.d, K2_BN);
-  target_kernel<<<tiles_m * tiles_n * g.B, 64 * K2_NW, 0, s>>>(Y, WtT, VT, Vtok, Vrow, vscale,
-                                                             g, tiles_m, tiles_n);
+  target_kernel<<<tiles_m * tiles_n * g.B, 64 * K2_NW, 0, s>>>(
+      Y, WtT, VT, Vtok, Vrow, vscale, g, tiles_m, tiles_n, range, VT != nullptr ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_repair(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT,
+                                uint16_t* Vrow, float vscale, int p, const Dims& g,
+                                const uint32_t* range, hipStream_t s) {
+  const int tiles_m = g.T_pad / K2_BM, tiles_n = ceil_div(g.d, K2_BN);
+  const int grid = std::min(tiles_m * tiles_n * g.B, repair_grid());
+  target_repair_kernel<<<grid, 64 * K2_NW, 0, s>>>(Y, WtT, VT, Vrow, vscale, p, g, tiles_m,
+                                                   tiles_n, range);
   return hipGetLastError();
 }
 
@@ -1595,7 +1830,7 @@ hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gra
                              float* partial, float* scale, uint16_t* VT, const Dims& g,
                              int chunk, int nchunks, const ChunkSpan* spans,
                              const BlockInfo* blocks, float norm_factor, float clip,
-                             hipStream_t s) {
+                             const uint32_t* range, int p, hipStream_t s) {
   const int nblk = ceil_div(chunk, KG_B), npair = nblk * (nblk + 1) / 2;
   gram_v_kernel<<<g.B * nchunks * npair, KG_THREADS, 0, s>>>(Vrow, gram, g, chunk, nblk, npair,
                                                                nchunks, spans);
@@ -1607,7 +1842,7 @@ hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gra
   if (e != hipSuccess) return e;
   const int n = g.B * nchunks;
   clip_scale_kernel<<<ceil_div(n, kThreads), kThreads, 0, s>>>(partial, scale, clip_pairs(chunk),
-                                                               n, norm_factor, clip);
+                                                               n, norm_factor, clip, range, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n16 = vt_elems(g) / 8;
@@ -1618,7 +1853,7 @@ hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gra
 
 template <bool F32, bool PACKED>
 static void update_launch(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
-                          int64_t winit_bstride, int64_t winit_ld, float acc_scale,
+                          int64_t winit_bstride, int64_t winit_ld, int p, const uint32_t* range,
                           uint16_t* snap, int64_t snap_bstride, float* Wf, uint16_t* shadow,
                           const Dims& g, int tok_begin, int nk, int steps_per_chunk,
                           const BlockInfo* blocks, int n_chunks, hipStream_t s) {
@@ -1638,13 +1873,13 @@ static void update_launch(const uint16_t* ZT, const uint16_t* VT, const void* Wi
   const int n_wide = (rem == 0 || 2 * rem > cus) ? regions : regions - rem;
   const int grid = n_wide + 2 * (regions - n_wide);
   update_kernel<F32, PACKED><<<grid, 64 * K3_NW, 0, s>>>(
-      ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap, snap_bstride, Wf, shadow, g,
+      ZT, VT, Winit, winit_bstride, winit_ld, p, range, snap, snap_bstride, Wf, shadow, g,
       tok_begin, nk, steps_per_chunk, blocks, n_chunks, regions_m, regions_n, n_wide);
 }
 
 hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
-                         bool winit_f32, int64_t winit_bstride, int64_t winit_ld,
-                         float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
+                         bool winit_f32, int64_t winit_bstride, int64_t winit_ld, int p,
+                         const uint32_t* range, uint16_t* snap, int64_t snap_bstride, float* Wf,
                          uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
                          int chunk, const BlockInfo* blocks, int n_chunks, hipStream_t s) {
   // Token offsets and counts are whole K steps, so that the slab operands are
@@ -1653,20 +1888,20 @@ hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Win
   if (blocks != nullptr) {
     if (nk > kMaxPackedSteps) return hipErrorInvalidValue;  // StepBits holds 2048 steps
     if (winit_f32)
-      update_launch<true, true>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
+      update_launch<true, true>(ZT, VT, Winit, winit_bstride, winit_ld, p, range, snap,
                                 snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
                                 blocks, n_chunks, s);
     else
-      update_launch<false, true>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
+      update_launch<false, true>(ZT, VT, Winit, winit_bstride, winit_ld, p, range, snap,
                                  snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
                                  blocks, n_chunks, s);
   } else {
     if (winit_f32)
-      update_launch<true, false>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
+      update_launch<true, false>(ZT, VT, Winit, winit_bstride, winit_ld, p, range, snap,
                                  snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
                                  nullptr, n_chunks, s);
     else
-      update_launch<false, false>(ZT, VT, Winit, winit_bstride, winit_ld, acc_scale, snap,
+      update_launch<false, false>(ZT, VT, Winit, winit_bstride, winit_ld, p, range, snap,
                                   snap_bstride, Wf, shadow, g, tok_begin, nk, steps_per_chunk,
                                   nullptr, n_chunks, s);
   }

@@ -112,39 +112,78 @@ inline int64_t wpack_elems(const Dims& g) {
   return (int64_t)((g.f + kWRows - 1) / kWRows) * kWRows * g.d;
 }
 
+// Operand ranges of the fp16 copies (ttt_device.h has the device side): a
+// range buffer holds kRangeGroups groups of kRangeSlots words, each group the
+// largest |value| noted by one producer (W_target, conv(X0), V at vscale, Z).
+constexpr int kRangeSlots = 256;
+enum { kRangeWt = 0, kRangeY = 1, kRangeV = 2, kRangeZ = 3, kRangeGroups = 4 };
+constexpr int kRangeWords = kRangeGroups * kRangeSlots;
+constexpr int kRangeMaxExp = 40;   // |q| limit of one operand's exponent
+constexpr int kStateMaxExp = 100;  // |p + qv + qz| limit of the update's state scale
+
+// Zeroes a range buffer (kRangeWords words); every call that uses one starts
+// with it.
+hipError_t launch_range_clear(uint32_t* range, hipStream_t s);
+// Notes max |W| over n elements (bf16 or fp32, n a multiple of 8) in one
+// range group.
+hipError_t launch_amax(const void* W, bool w_f32, int64_t n, uint32_t* group, hipStream_t s);
+
 hipError_t launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 
 // dst[0, bytes) = src[0, bytes) with a plain 16-byte-per-thread copy.
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
-// dst[c * ld_dst + r] = fp16(src[r][c]) for a rows x cols matrix (bf16 or fp32).
+// dst[c * ld_dst + r] = fp16(src[r][c] 2^q) for a rows x cols matrix (bf16
+// or fp32), q from src's range group (range_exp of its noted maximum; 0 when
+// range is null).
 hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, int rows,
-                                int cols, int64_t ld_dst, hipStream_t s);
+                                int cols, int64_t ld_dst, const uint32_t* range, hipStream_t s);
 
 // Y[b][t][c] = fp16(sum_k taps[k][c] * X0[b][t + k][c]) over reads inside the
 // sequence (or inside t's chunk when pad_chunk), for t < T_pad. The sequence
 // may continue past T with n_next look-ahead rows, X0_next [B][n_next][d],
 // which the reads of the sequence-padded conv reach. With blocks (packed
 // documents, B = 1, n_next = 0) the reads stop at t's document end (or chunk
-// end) instead.
+// end) instead. The largest |Y| goes to the range group (if not null);
+// launch_conv_repair then writes Y again times 2^q if that maximum is out of
+// the fp16 range, and otherwise only reads the group.
 hipError_t launch_conv(const uint16_t* X0, const uint16_t* X0_next, int n_next,
                        const void* taps, bool taps_f32, uint16_t* Y, const Dims& g, int K,
-                       int chunk, bool pad_chunk, const BlockInfo* blocks, hipStream_t s);
+                       int chunk, bool pad_chunk, const BlockInfo* blocks, uint32_t* range,
+                       hipStream_t s);
+hipError_t launch_conv_repair(const uint16_t* X0, const uint16_t* X0_next, int n_next,
+                              const void* taps, bool taps_f32, uint16_t* Y, const Dims& g, int K,
+                              int chunk, bool pad_chunk, const BlockInfo* blocks,
+                              const uint32_t* range, hipStream_t s);
 
 // dst = W ([f][d], bf16 or fp32, rounded to bf16) in the packed Wgp layout.
 hipError_t launch_pack_weight(const void* W, bool w_f32, uint16_t* dst, const Dims& g,
                               hipStream_t s);
 
 // Z = SiLU(H Wg^T) * (H Wu^T) from packed Wgp / Wup: bf16 Z (token-major) and
-// fp16 ZT; either may be null.
+// fp16 ZT; either may be null. With ZT, the largest |Z| goes to the range's
+// Z group (if range is not null); launch_gate_up_repair then writes ZT again
+// times 2^qz (qz = range_exp of that maximum) if qz != 0.
 hipError_t launch_gate_up(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
-                          uint16_t* Z, uint16_t* ZT, const Dims& g, hipStream_t s);
+                          uint16_t* Z, uint16_t* ZT, const Dims& g, uint32_t* range,
+                          hipStream_t s);
+hipError_t launch_gate_up_repair(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
+                                 uint16_t* ZT, const Dims& g, const uint32_t* range,
+                                 hipStream_t s);
 
 // V = Y WtT^T (conv(X0) W_target): fp16 VT = vscale * V (feature-major),
 // bf16 Vtok = vscale * V ([B][T][d]) and fp16 Vrow = vscale * V ([B][T_pad]
-// [ld_y]); any may be null.
+// [ld_y]); any may be null. With a range buffer, the exponents Y and WtT
+// were scaled by (their groups) are divided out, and with VT the largest
+// |vscale * V| goes to the V group. launch_target_repair then writes VT and
+// Vrow again at vscale * 2^qv * V if qv != 0 (qv from the V and Z groups and
+// eta's exponent p: the update's exponents).
 hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
-                         uint16_t* Vrow, float vscale, const Dims& g, hipStream_t s);
+                         uint16_t* Vrow, float vscale, const Dims& g, uint32_t* range,
+                         hipStream_t s);
+hipError_t launch_target_repair(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT,
+                                uint16_t* Vrow, float vscale, int p, const Dims& g,
+                                const uint32_t* range, hipStream_t s);
 
 // Update-norm clipping: per chunk i, scale[b][i] = min(1, clip /
 // (norm_factor * ||Vrow_i^T Z_i||_F)) from the Gram form (gram: B * nchunks
@@ -156,11 +195,13 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
 // 64-token slab's chunk.
 int clip_pairs(int chunk);
 int64_t clip_gram_floats(int chunk);
+// With a range buffer, norm_factor is divided by 2^qv (Vrow holds V at
+// vscale * 2^qv).
 hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gram,
                              float* partial, float* scale, uint16_t* VT, const Dims& g,
                              int chunk, int nchunks, const ChunkSpan* spans,
                              const BlockInfo* blocks, float norm_factor, float clip,
-                             hipStream_t s);
+                             const uint32_t* range, int p, hipStream_t s);
 
 // Fast-weight update over tokens [tok_begin, tok_begin + tok_count) (a
 // multiple of 64), in 64-token steps (columns past T read as zero). acc =
@@ -172,23 +213,31 @@ hipError_t launch_clip_scale(const uint16_t* Z, const uint16_t* Vrow, float* gra
 // contraction over tokens. Finally Wf = acc /
 // acc_scale (row-major [B][d][f]) and, if shadow != null, shadow =
 // bf16(acc / acc_scale) (sb<256>(d x f) per sequence). tok_count may be 0. Winit element
-// (b, c, j) is at b * winit_bstride + c * winit_ld + j. acc_scale must be a
-// power of two (the scalings are then exact).
+// (b, c, j) is at b * winit_bstride + c * winit_ld + j. acc_scale = 2^(p +
+// qv + qz): eta's exponent and, with a range buffer, the exponents ZT and
+// VT carry (powers of two, so the scalings are exact).
 hipError_t launch_update(const uint16_t* ZT, const uint16_t* VT, const void* Winit,
-                         bool winit_f32, int64_t winit_bstride, int64_t winit_ld,
-                         float acc_scale, uint16_t* snap, int64_t snap_bstride, float* Wf,
+                         bool winit_f32, int64_t winit_bstride, int64_t winit_ld, int p,
+                         const uint32_t* range, uint16_t* snap, int64_t snap_bstride, float* Wf,
                          uint16_t* shadow, const Dims& g, int tok_begin, int tok_count,
                          int chunk, const BlockInfo* blocks, int n_chunks, hipStream_t s);
 
 // Decode step, gated activation: for one token per sequence (h, x0: [B][d],
-// act dtype), zb[b][j] = bf16(z), column col of the chunk's Z^T (sb<256>, f
-// rows, zt_cols columns, zt_bstride elements per sequence) = fp16(z), with
-// z = SiLU(h_b Wg[j]) * (h_b Wu[j]); and x0 (as bf16) into row col of x0c
-// [B][chunk][d].
+// act dtype), zb[b][j] = bf16(z), row col of zc [B][chunk][f] = z (fp32),
+// column col of the chunk's Z^T (sb<256>, f rows, zt_cols columns,
+// zt_bstride elements per sequence) = fp16(z), with z = SiLU(h_b Wg[j]) *
+// (h_b Wu[j]); the largest |z| goes to zrange's Z group; and x0 (as bf16)
+// into row col of x0c [B][chunk][d].
 hipError_t launch_decode_gate_up(const void* h, const void* x0, bool act_f32, const void* Wg,
                                  const void* Wu, bool w_f32, int B, int d, int f, uint16_t* zb,
-                                 uint16_t* zt, int64_t zt_bstride, int zt_cols, uint16_t* x0c,
-                                 int chunk, int col, hipStream_t s);
+                                 float* zc, uint16_t* zt, int64_t zt_bstride, int zt_cols,
+                                 uint16_t* x0c, int chunk, int col, uint32_t* zrange,
+                                 hipStream_t s);
+// At a chunk's close: Z^T = fp16(zc 2^qz) for the chunk's columns if qz (from
+// the Z group's maximum) is not 0; otherwise nothing.
+hipError_t launch_decode_zt_repair(const float* zc, uint16_t* zt, int B, int f, int chunk,
+                                  int64_t zt_bstride, int zt_cols, const uint32_t* zrange,
+                                  hipStream_t s);
 // Decode step, apply: o[b] = zb[b] S_b^T (S_b the bf16 state of sequence b,
 // sb<256> d x f, s_bstride elements apart), through part
 // (decode_apply_part_floats(B, d) floats); o is [B][d], bf16 or fp32.
