@@ -47,14 +47,22 @@ tested by the pins in tests/test_oracle.py):
     only, the state stepped as soon as a chunk's last token is processed.
     With that padding it is the prefill computed token by token; the pages
     say decode was not evaluated and give no rule for sequence padding.
+  * Backward (ttt_prefill_backward): the pages train the layer's slow
+    parameters by continual pretraining ([iplex] §2 and §7.1; [forum]
+    "Limitations"), and the conv taps and W_target reach the output only
+    through the fast-weight updates ([iplex] §6 initialises them so that the
+    first updates are near zero). So the backward is the exact gradient of
+    the prefill, taken through the chunk recurrence, with respect to every
+    input: H, X0, W_g, W_u, W_down0, the taps and W_target. eta is a fixed
+    scalar (the pages do not learn it) and gets no gradient.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["silu", "gated_activation", "conv_target_input", "lm_target",
-           "ttt_prefill", "ttt_prefill_packed", "ttt_decode", "activation_rows",
-           "target_rows", "final_state_entries"]
+           "ttt_prefill", "ttt_prefill_packed", "ttt_decode", "ttt_prefill_backward",
+           "activation_rows", "target_rows", "final_state_entries"]
 
 
 def _f64(a) -> np.ndarray:
@@ -290,6 +298,99 @@ def ttt_decode(H, X0, Wg, Wu, W_state, taps, W_target, eta, chunk, start=0):
         W_out[b] = W
         pending = len(zs)
     return O, W_out, pending
+
+
+def ttt_prefill_backward(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk, dO,
+                         dW_final=None, pad="sequence"):
+    """Gradients of the prefill: for L = <dO, O> + <dW_final, W_final> (the
+    upstream gradients of ttt_prefill's two outputs, dW_final zero if None),
+    the gradient of L with respect to every input of ttt_prefill.
+
+    The forward, per sequence ([notes] "In-Place 设计", "Chunk-Wise 更新机制",
+    "LM-Aligned 目标函数"; [iplex] §3): G = H Wg^T, U = H Wu^T, Z = phi(G) * U;
+    Y = conv(X0), V = Y W_target; W_0 = W_down0; for chunk i,
+    O_i = Z_i W_i^T, then W_{i+1} = W_i + eta V_i^T Z_i; W_final = W_k.
+
+    Reverse, chunk by chunk from the last: with Gbar = dL/dW_{i+1} (Gbar =
+    dW_final after the last chunk),
+        the update W_{i+1} = W_i + eta V_i^T Z_i gives
+            dV_i += eta Z_i Gbar^T,   dZ_i += eta V_i Gbar;
+        the apply O_i = Z_i W_i^T gives
+            dZ_i += dO_i W_i,         dL/dW_i = Gbar + dO_i^T Z_i;
+    and dW_down0 = dL/dW_0. Then V = Y W_target gives dY = dV W_target^T and
+    dW_target = Y^T dV; the conv Y[t] = sum_k taps[k] X0[t + k] (reads before
+    t's bound) gives dtaps[k] = sum_t dY[t] X0[t + k] and dX0[t + k] +=
+    taps[k] dY[t] over the same reads; Z = phi(G) U with phi(x) = x sigma(x),
+    phi'(x) = sigma(x) (1 + x (1 - sigma(x))), gives dG = dZ U phi'(G),
+    dU = dZ phi(G), dH = dG Wg + dU Wu, dWg = dG^T H, dWu = dU^T H.
+
+    Shapes as ttt_prefill (X0 may carry look-ahead rows past T; its gradient
+    has X0's shape). dO [B, T, d]; dW_final None or [B, d, f]. Returns a dict
+    of float64 arrays: dH, dX0, dWg, dWu, dW_down0 (the shape of W_down0:
+    summed over the batch when it is shared), dtaps, dW_target.
+    """
+    H, X0, W_down0 = _f64(H), _f64(X0), _f64(W_down0)
+    Wg, Wu, taps, Wt, dO = _f64(Wg), _f64(Wu), _f64(taps), _f64(W_target), _f64(dO)
+    B, T, d = H.shape
+    f = Wg.shape[0]
+    K = taps.shape[0]
+    T_in = X0.shape[1]
+    if dO.shape != (B, T, d):
+        raise ValueError("dO must be [B, T, d]")
+    dWf = np.zeros((B, d, f)) if dW_final is None else _f64(dW_final)
+    out = {"dH": np.zeros((B, T, d)), "dX0": np.zeros_like(X0), "dWg": np.zeros((f, d)),
+           "dWu": np.zeros((f, d)), "dW_down0": np.zeros_like(W_down0),
+           "dtaps": np.zeros((K, d)), "dW_target": np.zeros((d, d))}
+    # the conv's read bound of each output t (as conv_target_input)
+    t_idx = np.arange(T)
+    if pad == "sequence":
+        bound = np.full(T, T_in)
+    elif pad == "chunk":
+        bound = np.minimum((t_idx // chunk + 1) * chunk, T_in)
+    else:
+        raise ValueError(pad)
+    starts = list(range(0, T, chunk))
+    for b in range(B):
+        G = H[b] @ Wg.T
+        U = H[b] @ Wu.T
+        sig = 1.0 / (1.0 + np.exp(-G))
+        S = G * sig                                   # phi(G)
+        Z = S * U
+        Y = conv_target_input(X0[b], taps, pad, chunk, n_out=T)
+        V = Y @ Wt
+        # states before each chunk
+        W = (W_down0[b] if W_down0.ndim == 3 else W_down0).copy()
+        states = []
+        for a in starts:
+            r = slice(a, min(a + chunk, T))
+            states.append(W)
+            W = W + eta * (V[r].T @ Z[r])
+        # reverse over the chunks
+        Gbar = dWf[b].copy()
+        dZ = np.zeros((T, f))
+        dV = np.zeros((T, d))
+        for i in reversed(range(len(starts))):
+            r = slice(starts[i], min(starts[i] + chunk, T))
+            dV[r] = eta * (Z[r] @ Gbar.T)
+            dZ[r] = eta * (V[r] @ Gbar) + dO[b, r] @ states[i]
+            Gbar = Gbar + dO[b, r].T @ Z[r]
+        if W_down0.ndim == 3:
+            out["dW_down0"][b] = Gbar
+        else:
+            out["dW_down0"] += Gbar
+        dY = dV @ Wt.T
+        out["dW_target"] += Y.T @ dV
+        for k in range(K):
+            m = t_idx + k < bound                      # the reads the forward made
+            tt = t_idx[m]
+            out["dtaps"][k] += (dY[tt] * X0[b, tt + k]).sum(axis=0)
+            out["dX0"][b, tt + k] += taps[k] * dY[tt]
+        dG = dZ * U * (sig * (1.0 + G * (1.0 - sig)))
+        dU = dZ * S
+        out["dH"][b] = dG @ Wg + dU @ Wu
+        out["dWg"] += dG.T @ H[b]
+        out["dWu"] += dU.T @ H[b]
+    return out
 
 
 # ---------------------------------------------------------------------------

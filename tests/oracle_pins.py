@@ -509,6 +509,147 @@ def pin_decode_resumes_prefill():
     _close(W2, Wf, tol=1e-12, what="prefill + decode W")
 
 
+# ---- the backward pass -------------------------------------------------------
+
+BWD_KEYS = ("H", "X0", "Wg", "Wu", "W_down0", "taps", "W_target")
+GRAD_OF = {"H": "dH", "X0": "dX0", "Wg": "dWg", "Wu": "dWu", "W_down0": "dW_down0",
+           "taps": "dtaps", "W_target": "dW_target"}
+
+
+def backward_case(seed, per_seq=False, lookahead=0, **kw):
+    """A small case for the backward: a ragged sequence, a batch of two, the
+    upstream gradients dO and dW_final drawn too."""
+    x = small_case(seed=seed, **kw)
+    rng = np.random.default_rng(1000 + seed)
+    B, T, d = x["H"].shape
+    f = x["Wg"].shape[0]
+    if lookahead:
+        x["X0"] = np.concatenate([x["X0"], rng.standard_normal((B, lookahead, d))], axis=1)
+    if per_seq:
+        x["W_down0"] = rng.standard_normal((B, d, f)) / math.sqrt(f)
+    x["dO"] = rng.standard_normal((B, T, d))
+    x["dW_final"] = rng.standard_normal((B, d, f))
+    return x
+
+
+def backward(x, **over):
+    a = dict(x)
+    a.update(over)
+    return ora.ttt_prefill_backward(a["H"], a["X0"], a["Wg"], a["Wu"], a["W_down0"],
+                                    a["taps"], a["W_target"], a["eta"], a["chunk"], a["dO"],
+                                    a.get("dW_final"), pad=a.get("pad", "sequence"))
+
+
+def _loss(x, **over):
+    """<dO, O> + <dW_final, W_final> through the forward oracle."""
+    a = dict(x)
+    a.update(over)
+    O, Wf = run(a)
+    return float((O * a["dO"]).sum() + (Wf * a["dW_final"]).sum())
+
+
+def pin_backward_finite_differences():
+    """Each gradient's directional derivative equals the central difference of
+    the forward oracle's <dO, O> + <dW_final, W_final> along a random
+    direction (float64, step 1e-6): both paddings, a shared and a
+    per-sequence W_down0, look-ahead rows of X0, a ragged last chunk."""
+    for seed, pad, per_seq, la in ((30, "sequence", False, 2), (31, "chunk", True, 0),
+                                   (32, "sequence", True, 0)):
+        x = backward_case(seed, per_seq=per_seq, lookahead=la, T=29, C=8)
+        x["pad"] = pad
+        g = backward(x)
+        rng = np.random.default_rng(seed)
+        for key in BWD_KEYS:
+            v = rng.standard_normal(np.shape(x[key]))
+            eps = 1e-6
+            fd = (_loss(x, **{key: x[key] + eps * v}) - _loss(x, **{key: x[key] - eps * v})) \
+                / (2 * eps)
+            an = float((g[GRAD_OF[key]] * v).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), \
+                f"{key} ({pad}): finite difference {fd:.12g} vs gradient {an:.12g}"
+
+
+def _torch_prefill(t, eta, chunk, pad):
+    """The prefill restated in torch (float64), for autograd: per sequence,
+    the gated MLP with torch's silu, the conv as shifted sums over the reads
+    before each token's bound, the chunk loop of apply then update."""
+    H, X0, Wg, Wu, W0, taps, Wt = (t[k] for k in BWD_KEYS)
+    B, T, d = H.shape
+    T_in, K = X0.shape[1], taps.shape[0]
+    Os, Ws = [], []
+    for b in range(B):
+        Z = torch.nn.functional.silu(H[b] @ Wg.T) * (H[b] @ Wu.T)
+        rows = []
+        for i in range(T):
+            end = T_in if pad == "sequence" else min((i // chunk + 1) * chunk, T_in)
+            y = torch.zeros(d, dtype=torch.float64)
+            for k in range(K):
+                if i + k < end:
+                    y = y + taps[k] * X0[b, i + k]
+            rows.append(y)
+        V = torch.stack(rows) @ Wt
+        W = W0[b] if W0.dim() == 3 else W0
+        outs = []
+        for a in range(0, T, chunk):
+            outs.append(Z[a:a + chunk] @ W.T)
+            W = W + eta * (V[a:a + chunk].T @ Z[a:a + chunk])
+        Os.append(torch.cat(outs))
+        Ws.append(W)
+    return torch.stack(Os), torch.stack(Ws)
+
+
+def pin_backward_autograd():
+    """Every gradient equals torch autograd through a torch restatement of
+    the forward (float64): both paddings, shared and per-sequence W_down0,
+    look-ahead rows, a ragged last chunk."""
+    for seed, pad, per_seq, la in ((33, "sequence", False, 1), (34, "chunk", True, 0),
+                                   (35, "chunk", False, 2)):
+        x = backward_case(seed, per_seq=per_seq, lookahead=la, T=30, C=8)
+        g = backward(x, pad=pad)
+        t = {k: torch.tensor(np.asarray(x[k], np.float64), requires_grad=True)
+             for k in BWD_KEYS}
+        O, Wf = _torch_prefill(t, x["eta"], x["chunk"], pad)
+        loss = (O * torch.tensor(x["dO"])).sum() + (Wf * torch.tensor(x["dW_final"])).sum()
+        loss.backward()
+        for key in BWD_KEYS:
+            _close(g[GRAD_OF[key]], t[key].grad.numpy(), tol=1e-10,
+                   what=f"{GRAD_OF[key]} ({pad})")
+
+
+def pin_backward_plain_mlp():
+    """eta = 0: the layer is the plain gated MLP O = Z W_down0^T and W_final
+    = W_down0, so the target path gets no gradient (dX0, dtaps, dW_target
+    exactly zero), dW_down0 = sum over sequences of dO^T Z + dW_final, and
+    dH, dW_g, dW_u are the plain MLP's (torch autograd of silu and matmul)."""
+    x = backward_case(36, T=21, C=8)
+    g = backward(x, eta=0.0)
+    for key in ("dX0", "dtaps", "dW_target"):
+        assert not np.any(g[key]), f"{key} must be zero at eta = 0"
+    H = torch.tensor(x["H"], requires_grad=True)
+    Wg = torch.tensor(x["Wg"], requires_grad=True)
+    Wu = torch.tensor(x["Wu"], requires_grad=True)
+    W0 = torch.tensor(x["W_down0"], requires_grad=True)
+    Z = torch.nn.functional.silu(H @ Wg.T) * (H @ Wu.T)
+    loss = ((Z @ W0.T) * torch.tensor(x["dO"])).sum() + (torch.tensor(x["dW_final"]).sum(0) * W0).sum()
+    loss.backward()
+    _close(g["dH"], H.grad.numpy(), what="plain dH")
+    _close(g["dWg"], Wg.grad.numpy(), what="plain dWg")
+    _close(g["dWu"], Wu.grad.numpy(), what="plain dWu")
+    _close(g["dW_down0"], W0.grad.numpy(), what="plain dW_down0")
+
+
+def pin_backward_linear_in_upstream():
+    """The gradients are linear in (dO, dW_final) jointly."""
+    x = backward_case(37, T=19, C=8)
+    rng = np.random.default_rng(37)
+    dO2, dW2 = rng.standard_normal(x["dO"].shape), rng.standard_normal(x["dW_final"].shape)
+    g1 = backward(x)
+    g2 = backward(x, dO=dO2, dW_final=dW2)
+    g3 = backward(x, dO=x["dO"] - 3.0 * dO2, dW_final=x["dW_final"] - 3.0 * dW2)
+    for key in GRAD_OF.values():
+        _close(g3[key], g1[key] - 3.0 * g2[key], tol=1e-12, what=f"linear {key}")
+
+
 ALL_PINS = [pin_reduces_to_plain_mlp, pin_prefix_scan_form, pin_state_free_form,
             pin_next_token_target, pin_conv_library, pin_linear_in_eta,
             pin_chunk_causality, pin_batch_independence, pin_split_resume,
@@ -516,4 +657,5 @@ ALL_PINS = [pin_reduces_to_plain_mlp, pin_prefix_scan_form, pin_state_free_form,
             pin_packed_single_document, pin_packed_equals_documents,
             pin_packed_isolation, pin_packed_clip_equals_documents, pin_clip_loose_is_plain, pin_clip_each_delta,
             pin_decode_is_chunk_padded_prefill, pin_decode_pending_chunk,
-            pin_decode_resumes_prefill]
+            pin_decode_resumes_prefill, pin_backward_finite_differences,
+            pin_backward_autograd, pin_backward_plain_mlp, pin_backward_linear_in_upstream]

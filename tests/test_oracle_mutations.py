@@ -192,7 +192,78 @@ def _decode_variant(late=0, update_first=False, conv_past_chunk=False):
     return decode
 
 
+def _backward_variant(mistake):
+    """A copy of the backward with one plausible mistake planted: the apply's
+    gradient taken against the state after the chunk's update ("next_state"),
+    the update's term of dZ dropped ("no_update_term"), the chunk's own
+    apply folded into the state gradient before its update terms
+    ("inclusive_gbar"), dW_final ignored ("no_dw_final"), phi' taken as
+    sigma ("silu_prime"), dW_target transposed ("dwt_transposed"), the
+    conv's input gradient scattered backwards ("conv_backwards"), eta left
+    out of dV ("dv_no_eta")."""
+    def bwd(H, X0, Wg, Wu, W_down0, taps, W_target, eta, chunk, dO, dW_final=None,
+            pad="sequence"):
+        H, X0, W_down0 = (np.asarray(a, np.float64) for a in (H, X0, W_down0))
+        Wg, Wu, taps, Wt, dO = (np.asarray(a, np.float64) for a in (Wg, Wu, taps, W_target, dO))
+        B, T, d = H.shape
+        f, K, T_in = Wg.shape[0], taps.shape[0], X0.shape[1]
+        dWf = np.zeros((B, d, f)) if dW_final is None or mistake == "no_dw_final" \
+            else np.asarray(dW_final, np.float64)
+        out = {"dH": np.zeros((B, T, d)), "dX0": np.zeros_like(X0), "dWg": np.zeros((f, d)),
+               "dWu": np.zeros((f, d)), "dW_down0": np.zeros_like(W_down0),
+               "dtaps": np.zeros((K, d)), "dW_target": np.zeros((d, d))}
+        ti = np.arange(T)
+        bound = np.full(T, T_in) if pad == "sequence" else np.minimum((ti // chunk + 1) * chunk, T_in)
+        starts = list(range(0, T, chunk))
+        for b in range(B):
+            G, U = H[b] @ Wg.T, H[b] @ Wu.T
+            sig = 1.0 / (1.0 + np.exp(-G))
+            S = G * sig
+            Z = S * U
+            Y = _real_conv(X0[b], taps, pad, chunk, n_out=T)
+            V = Y @ Wt
+            W = (W_down0[b] if W_down0.ndim == 3 else W_down0).copy()
+            states = []
+            for a in starts:
+                states.append(W)
+                W = W + eta * (V[a:a + chunk].T @ Z[a:a + chunk])
+            states.append(W)
+            Gbar = dWf[b].copy()
+            dZ, dV = np.zeros((T, f)), np.zeros((T, d))
+            for i in reversed(range(len(starts))):
+                r = slice(starts[i], min(starts[i] + chunk, T))
+                if mistake == "inclusive_gbar":
+                    Gbar = Gbar + dO[b, r].T @ Z[r]
+                dV[r] = (1.0 if mistake == "dv_no_eta" else eta) * (Z[r] @ Gbar.T)
+                upd = 0.0 if mistake == "no_update_term" else eta * (V[r] @ Gbar)
+                dZ[r] = upd + dO[b, r] @ states[i + 1 if mistake == "next_state" else i]
+                if mistake != "inclusive_gbar":
+                    Gbar = Gbar + dO[b, r].T @ Z[r]
+            if W_down0.ndim == 3:
+                out["dW_down0"][b] = Gbar
+            else:
+                out["dW_down0"] += Gbar
+            dY = dV @ Wt.T
+            out["dW_target"] += (dV.T @ Y) if mistake == "dwt_transposed" else (Y.T @ dV)
+            for k in range(K):
+                m = ti + k < bound
+                tt = ti[m]
+                out["dtaps"][k] += (dY[tt] * X0[b, tt + k]).sum(axis=0)
+                dst = np.clip(tt - k, 0, T_in - 1) if mistake == "conv_backwards" else tt + k
+                out["dX0"][b, dst] += taps[k] * dY[tt]
+            dphi = sig if mistake == "silu_prime" else sig * (1.0 + G * (1.0 - sig))
+            dG, dU = dZ * U * dphi, dZ * S
+            out["dH"][b] = dG @ Wg + dU @ Wu
+            out["dWg"] += dG.T @ H[b]
+            out["dWu"] += dU.T @ H[b]
+        return out
+    return bwd
+
+
 MUTATIONS = {
+    **{f"backward_{m}": ("ttt_prefill_backward", _backward_variant(m))
+       for m in ("next_state", "no_update_term", "inclusive_gbar", "no_dw_final", "silu_prime",
+                 "dwt_transposed", "conv_backwards", "dv_no_eta")},
     "decode_update_one_token_late": ("ttt_decode", _decode_variant(late=1)),
     "decode_update_before_last_output": ("ttt_decode", _decode_variant(update_first=True)),
     "decode_target_reads_next_chunk": ("ttt_decode", _decode_variant(conv_past_chunk=True)),
