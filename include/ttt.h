@@ -318,6 +318,54 @@ ttt_status ttt_decode_step(const ttt_desc* desc, const void* h, const void* x0,
                            float* W_state, void* decode_state, size_t decode_state_bytes,
                            void* o, void* stream);
 
+/* The backward pass: the gradients of the prefill (ttt_layer_forward with
+ * the same arguments) for training the layer. The pages train it by
+ * continual pretraining (iplexlaw explainer §2 and §7.1; zhichai summary,
+ * "Limitations"), and the conv taps and W_target act on the output only
+ * through the fast-weight updates (§6 initialises them so that the first
+ * updates are near zero), so the gradients are taken through the chunk
+ * recurrence. For upstream gradients dO = dL/dO and dW_final = dL/dW_final,
+ * with Gbar = dL/dW^(i+1) (dW_final after the last chunk), chunk by chunk
+ * from the last:
+ *   dZ_i = dO_i W^(i) + eta V_i Gbar,  dV_i = eta Z_i Gbar^T,
+ *   dL/dW^(i) = Gbar + dO_i^T Z_i,     dW_down0 = dL/dW^(0);
+ * then dY = dV W_target^T, dW_target = Y^T dV (Y = conv(X0)), the conv's
+ * transpose for dX0 and dtaps, and dG = dZ U phi'(G), dU = dZ phi(G) (G, U
+ * the gate and up projections, phi = SiLU), dH = dG Wg + dU Wu,
+ * dWg = dG^T H, dWu = dU^T H. eta is a fixed scalar and gets no gradient.
+ *   H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk: as in
+ *             ttt_layer_forward (flags: TTT_FLAG_PAD_CHUNK as there; the
+ *             schedule flags are ignored). A per-sequence W_down0 must sit
+ *             at w0_batch_stride = d_model * d_ff (TTT_ERR_UNSUPPORTED
+ *             otherwise).
+ *   dO        [B, T, d]  act_dtype   upstream gradient of O
+ *   dW_final  [B, d, f]  float32     upstream gradient of W_down_final, or
+ *             NULL (zero)
+ *   dH, dX0   [B, T, d]  float32     out
+ *   dWg, dWu  [f, d]     float32     out, summed over the batch
+ *   dW_down0  float32 out: [d, f] summed over the batch for a shared
+ *             W_down0, [B, d, f] for per-sequence ones
+ *   dtaps     [K, d]     float32     out, summed over the batch
+ *   dW_target [d, d]     float32     out, summed over the batch
+ *   workspace >= ttt_backward_workspace_size() bytes, 256-byte aligned
+ * Arithmetic: the forward's activations are recomputed; every contraction
+ * of the backward takes bf16 operands with fp32 accumulation, and the
+ * states W^(i) and gradients Gbar of the chunks are kept as bf16 copies
+ * (each gradient carries bf16-level error, about 1e-3 relative). The
+ * workspace holds three sets of per-chunk d x f copies (6 k d f bytes per
+ * sequence) besides activation-sized buffers. Conventions (validation before
+ * any launch, asynchrony, no allocation, aliasing) as ttt_layer_forward. */
+ttt_status ttt_backward_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes);
+ttt_status ttt_layer_backward(const ttt_desc* desc,
+                              const void* H, const void* X0,
+                              const void* Wg, const void* Wu,
+                              const void* W_down0, const void* conv_taps,
+                              const void* W_target, float eta, int32_t chunk,
+                              const void* dO, const float* dW_final,
+                              float* dH, float* dX0, float* dWg, float* dWu,
+                              float* dW_down0, float* dtaps, float* dW_target,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Step entry points: one step of the layer each, for per-step checks.
  * ttt_gated_activation writes Z [B, T, d_ff] in bf16.
  * ttt_lm_target writes V [B, T, d_model] in bf16 (unscaled, eta not applied).

@@ -7,10 +7,13 @@ built, or a call fails, an exception is raised.
 
     O, W_final = layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target,
                                eta, chunk)
+    grads = layer_backward(H, X0, Wg, Wu, W_down0, conv_taps, W_target,
+                           eta, chunk, dO)
 """
 from ._binding import (  # noqa: F401
     LIB_PATH,
     TTTError,
+    backward_workspace_size,
     clipped_workspace_size,
     continue_workspace_size,
     copy_calibration,
@@ -18,6 +21,7 @@ from ._binding import (  # noqa: F401
     decode_state_size,
     decode_step,
     gated_activation,
+    layer_backward,
     layer_forward,
     layer_forward_continue,
     layer_forward_packed,
@@ -35,6 +39,7 @@ __all__ = ["layer_forward", "layer_forward_packed", "packed_workspace_size", "pa
            "layer_forward_continue", "continue_workspace_size", "clipped_workspace_size",
            "decode_state_size", "decode_begin", "decode_step",
            "gated_activation", "lm_target", "workspace_size",
+           "layer_backward", "backward_workspace_size",
            "copy_calibration",
            "make_desc", "profile_enable", "profile_read", "TTTError", "lib",
            "LIB_PATH"]

@@ -100,6 +100,10 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_int32, _P, _P, _S, _P, _P]
     L.ttt_layer_forward_noalloc.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                             ctypes.c_int32, _P, _P, _P]
+    L.ttt_backward_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
+    L.ttt_layer_backward.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                     ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _S, _P]
     L.ttt_gated_activation.argtypes = [DP, _P, _P, _P, _P, _P, _S, _P]
     L.ttt_lm_target.argtypes = [DP, _P, _P, _P, ctypes.c_int32, _P, _P, _S, _P]
     for fn in ("ttt_workspace_size", "ttt_step_workspace_size", "ttt_layer_forward",
@@ -110,6 +114,7 @@ def lib() -> ctypes.CDLL:
                "ttt_packed_tables",
                "ttt_continue_workspace_size", "ttt_layer_forward_continue",
                "ttt_decode_state_size", "ttt_decode_begin", "ttt_decode_step",
+               "ttt_backward_workspace_size", "ttt_layer_backward",
                "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
         getattr(L, fn).restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int32]
@@ -191,17 +196,8 @@ def clipped_workspace_size(desc: Desc, chunk: int, clip: float) -> int:
     return n.value
 
 
-def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
-                  schedule=None, pad="sequence", clip=None, out=None, W_down_final=None,
-                  workspace=None, stream=None):
-    """O, W_final for H, X0 [B, T, d]; Wg, Wu [f, d]; W_down0 [d, f] or
-    [B, d, f]; conv_taps [K, d]; W_target [d, d] (see include/ttt.h).
-
-    schedule: None (library default), "prefix" or "running". pad:
-    "sequence" (conv reads zero past the sequence end) or "chunk". clip:
-    None, or the Frobenius-norm limit of every chunk's update
-    (ttt_layer_forward_clipped).
-    """
+def _layer_desc(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, schedule, pad):
+    """The descriptor of a prefill call, after checking shapes and dtypes."""
     _require_cuda(H, X0, Wg, Wu, W_down0, conv_taps, W_target)
     if H.dim() != 3 or X0.shape != H.shape:
         raise ValueError("H and X0 must both be [B, T, d]")
@@ -225,7 +221,23 @@ def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
     if not math.isfinite(float(eta)):
         raise ValueError("eta must be finite")
     stride = d * f if W_down0.dim() == 3 else 0
-    desc = make_desc(B, T, d, f, K, act, wt, stride, _flags(schedule, pad))
+    return make_desc(B, T, d, f, K, act, wt, stride, _flags(schedule, pad))
+
+
+def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
+                  schedule=None, pad="sequence", clip=None, out=None, W_down_final=None,
+                  workspace=None, stream=None):
+    """O, W_final for H, X0 [B, T, d]; Wg, Wu [f, d]; W_down0 [d, f] or
+    [B, d, f]; conv_taps [K, d]; W_target [d, d] (see include/ttt.h).
+
+    schedule: None (library default), "prefix" or "running". pad:
+    "sequence" (conv reads zero past the sequence end) or "chunk". clip:
+    None, or the Frobenius-norm limit of every chunk's update
+    (ttt_layer_forward_clipped).
+    """
+    desc = _layer_desc(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, schedule, pad)
+    B, T, d = H.shape
+    f = Wg.shape[0]
     if clip is None:
         ws_bytes = workspace_size(desc, int(chunk))
     else:
@@ -244,6 +256,50 @@ def layer_forward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
     else:
         _check(lib().ttt_layer_forward_clipped(*args, ctypes.c_float(float(clip)), *tail))
     return O, Wf
+
+
+def backward_workspace_size(desc: Desc, chunk: int) -> int:
+    n = _S(0)
+    _check(lib().ttt_backward_workspace_size(ctypes.byref(desc), int(chunk), ctypes.byref(n)))
+    return n.value
+
+
+def layer_backward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, dO, *,
+                   dW_final=None, pad="sequence", workspace=None, stream=None):
+    """The prefill's gradients (ttt_layer_backward) for the upstream
+    gradients dO [B, T, d] (H's dtype) and dW_final [B, d, f] fp32 (None:
+    zero). Returns a dict of fp32 tensors: dH, dX0 [B, T, d]; dWg, dWu
+    [f, d]; dW_down0 [d, f] (shared W_down0) or [B, d, f]; dtaps [K, d];
+    dW_target [d, d]."""
+    desc = _layer_desc(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, None, pad)
+    B, T, d = H.shape
+    f, K = Wg.shape[0], conv_taps.shape[0]
+    _require_cuda(dO)
+    if dO.shape != H.shape or dO.dtype != H.dtype:
+        raise ValueError("dO must be [B, T, d] with H's dtype")
+    if dW_final is not None:
+        _require_cuda(dW_final)
+        if dW_final.shape != (B, d, f) or dW_final.dtype != torch.float32:
+            raise ValueError("dW_final must be [B, d_model, d_ff] float32")
+        if not dW_final.is_contiguous():
+            raise ValueError("dW_final must be contiguous")
+    ws_bytes = backward_workspace_size(desc, int(chunk))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
+    _require_cuda(workspace)
+    f32 = dict(dtype=torch.float32, device=H.device)
+    g = {"dH": torch.empty((B, T, d), **f32), "dX0": torch.empty((B, T, d), **f32),
+         "dWg": torch.empty((f, d), **f32), "dWu": torch.empty((f, d), **f32),
+         "dW_down0": torch.empty(tuple(W_down0.shape), **f32),
+         "dtaps": torch.empty((K, d), **f32), "dW_target": torch.empty((d, d), **f32)}
+    _check(lib().ttt_layer_backward(
+        ctypes.byref(desc), _ptr(H), _ptr(X0), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
+        _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk), _ptr(dO),
+        None if dW_final is None else _ptr(dW_final),
+        _ptr(g["dH"]), _ptr(g["dX0"]), _ptr(g["dWg"]), _ptr(g["dWu"]), _ptr(g["dW_down0"]),
+        _ptr(g["dtaps"]), _ptr(g["dW_target"]), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return g
 
 
 def _doc_array(doc_starts):

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libttt_layer.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["ttt_kernels.hip", "ttt_decode.hip", "ttt_noalloc.hip", "ttt_api.cpp"]
+SOURCES = ["ttt_kernels.hip", "ttt_decode.hip", "ttt_backward.hip", "ttt_noalloc.hip",
+           "ttt_api.cpp"]
 ARCH = "gfx950"
 
 

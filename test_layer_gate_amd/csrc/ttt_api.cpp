@@ -927,6 +927,249 @@ ttt_status ttt_decode_step(const ttt_desc* desc, const void* h, const void* x0, 
   return TTT_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The backward's workspace: the forward's recomputed activations (bf16 and
+// slab copies), the states W_i^T and state gradients Gbar (both
+// orientations) of every chunk, and the gradients' intermediates.
+struct BwdLayout {
+  size_t range = 0, wgp = 0, wup = 0, hb = 0, x0b = 0, dov = 0, y = 0, wtt = 0, yt = 0, z = 0,
+         zt = 0, sa = 0, vt = 0, dot = 0, ht = 0, wgt = 0, gs = 0, dw0 = 0, dgu = 0, dgt = 0,
+         dut = 0, dv = 0, dvt = 0, wgut = 0, wtb = 0, dy = 0, part = 0, total = 0;
+  int64_t ld_gu = 0, ld_ov = 0;
+};
+
+BwdLayout backward_layout(const Geo& g) {
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const tttk::Dims& D = g.dims;
+  const int64_t BT = g.B * g.T, BTp = g.B * g.T_pad;
+  const int64_t snap_df = tttk::sb_elems<256>(g.d, g.f), snap_f2d = tttk::sb_elems<256>(g.f, 2 * g.d);
+  L.ld_gu = tttk::pad_ld(2 * g.f);
+  L.ld_ov = tttk::pad_ld(2 * g.d);
+  L.range = take(tttk::kRangeWords * 4);
+  L.wgp = take(tttk::wpack_elems(D) * 2);
+  L.wup = take(tttk::wpack_elems(D) * 2);
+  if (g.act_f32) {
+    L.hb = take(BT * g.d * 2);
+    L.x0b = take(BT * g.d * 2);
+  }
+  L.dov = take(BT * L.ld_ov * 2);
+  L.y = take(BTp * D.ld_y * 2);
+  L.wtt = take(g.d * D.ld_y * 2);
+  L.yt = take(tttk::sb_elems<256>(g.d, BTp) * 2);
+  L.z = take(BT * D.ld_z * 2);
+  L.zt = take(tttk::zt_elems(D) * 2);
+  L.sa = take(BT * g.f * 4);
+  L.vt = take(tttk::vt_elems(D) * 2);
+  L.dot = take(tttk::vt_elems(D) * 2);
+  L.ht = take(tttk::sb_elems<256>(g.d, BTp) * 2);
+  L.wgt = take(g.B * g.nchunks * snap_f2d * 2);
+  L.gs = take(g.B * g.nchunks * snap_df * 2);
+  if (g.w0_stride == 0 && g.B > 1) L.dw0 = take(g.B * g.d * g.f * 4);
+  L.dgu = take(BT * L.ld_gu * 2);
+  L.dgt = take(tttk::sb_elems<256>(g.f, BTp) * 2);
+  L.dut = take(tttk::sb_elems<256>(g.f, BTp) * 2);
+  L.dv = take(BT * g.d * 2);
+  L.dvt = take(tttk::sb_elems<256>(g.d, BTp) * 2);
+  L.wgut = take(g.d * L.ld_gu * 2);
+  if (g.w_f32) L.wtb = take(g.d * g.d * 2);
+  L.dy = take(BT * g.d * 4);
+  L.part = take(tttk::conv_bwd_part_floats((int)g.B, (int)g.T, (int)g.K, (int)g.d) * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status ttt_backward_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = backward_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X0,
+                              const void* Wg, const void* Wu, const void* W_down0,
+                              const void* conv_taps, const void* W_target, float eta,
+                              int32_t chunk, const void* dO, const float* dW_final, float* dH,
+                              float* dX0, float* dWg, float* dWu, float* dW_down0, float* dtaps,
+                              float* dW_target, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
+  const char* names[] = {"H", "X0", "Wg", "Wu", "W_down0", "conv_taps", "W_target", "dO",
+                         "dH", "dX0", "dWg", "dWu", "dW_down0", "dtaps", "dW_target"};
+  const void* ptrs[] = {H, X0, Wg, Wu, W_down0, conv_taps, W_target, dO,
+                        dH, dX0, dWg, dWu, dW_down0, dtaps, dW_target};
+  for (int i = 0; i < 15; ++i) TTT_TRY(check_ptr(ptrs[i], names[i]));
+  if (dW_final != nullptr) TTT_TRY(check_ptr(dW_final, "dW_final"));
+  TTT_TRY(check_ptr(workspace, "workspace", 256));
+  if (g.w0_stride != 0 && g.w0_stride != g.d * g.f)
+    return fail(TTT_ERR_UNSUPPORTED,
+                "the backward needs per-sequence W_down0 at stride d_model * d_ff (or shared)");
+  const BwdLayout L = backward_layout(g);
+  if (workspace_bytes < L.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                       " bytes, needs " + std::to_string(L.total));
+  const size_t ab = g.act_bytes(), wb = g.w_bytes();
+  const int64_t df = g.d * g.f;
+  const size_t w0_bytes = g.w0_stride == 0 ? df * wb : g.B * df * wb;
+  std::vector<Range> inputs = {range_of("H", H, g.B * g.T * g.d * ab),
+                               range_of("X0", X0, g.B * g.T * g.d * ab),
+                               range_of("Wg", Wg, g.f * g.d * wb),
+                               range_of("Wu", Wu, g.f * g.d * wb),
+                               range_of("W_down0", W_down0, w0_bytes),
+                               range_of("conv_taps", conv_taps, g.K * g.d * wb),
+                               range_of("W_target", W_target, g.d * g.d * wb),
+                               range_of("dO", dO, g.B * g.T * g.d * ab)};
+  if (dW_final != nullptr) inputs.push_back(range_of("dW_final", dW_final, g.B * df * 4));
+  const std::vector<Range> outputs = {
+      range_of("dH", dH, g.B * g.T * g.d * 4), range_of("dX0", dX0, g.B * g.T * g.d * 4),
+      range_of("dWg", dWg, df * 4), range_of("dWu", dWu, df * 4),
+      range_of("dW_down0", dW_down0, (g.w0_stride == 0 ? 1 : g.B) * df * 4),
+      range_of("dtaps", dtaps, g.K * g.d * 4), range_of("dW_target", dW_target, g.d * g.d * 4),
+      range_of("workspace", workspace, L.total)};
+  TTT_TRY(check_aliasing(inputs, outputs));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const tttk::Dims& D = g.dims;
+  const int B = (int)g.B, T = (int)g.T, d = (int)g.d, f = (int)g.f, C = (int)g.C;
+  const int nch = (int)g.nchunks;
+  const int64_t snap_df = tttk::sb_elems<256>(g.d, g.f), snap_f2d = tttk::sb_elems<256>(g.f, 2 * g.d);
+  uint32_t* range = at<uint32_t>(workspace, L.range);
+  uint32_t* range_y = range + tttk::kRangeY * tttk::kRangeSlots;
+  uint32_t* range_wt = range + tttk::kRangeWt * tttk::kRangeSlots;
+  TTT_LAUNCH("range_clear", s, tttk::launch_range_clear(range, s));
+
+  // bf16 operands; dO goes to the first d columns of [dO | eta V]
+  const uint16_t* Hb = static_cast<const uint16_t*>(H);
+  const uint16_t* X0b = static_cast<const uint16_t*>(X0);
+  if (g.act_f32) {
+    const int64_t n = g.B * g.T * g.d;
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(H), at<uint16_t>(workspace, L.hb), n, s));
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(X0), at<uint16_t>(workspace, L.x0b), n, s));
+    Hb = at<uint16_t>(workspace, L.hb);
+    X0b = at<uint16_t>(workspace, L.x0b);
+  }
+  uint16_t* DOV = at<uint16_t>(workspace, L.dov);
+  TTT_LAUNCH("bwd_rows", s,
+             tttk::launch_rows_bf16(dO, g.act_f32, g.d, DOV, L.ld_ov, g.B * g.T, d, s));
+
+  // The forward's activations again (bf16 for the backward's contractions).
+  uint16_t* Wgp = at<uint16_t>(workspace, L.wgp);
+  uint16_t* Wup = at<uint16_t>(workspace, L.wup);
+  TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wg, g.w_f32, Wgp, D, s));
+  TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wu, g.w_f32, Wup, D, s));
+  uint16_t* Y = at<uint16_t>(workspace, L.y);
+  uint16_t* WtT = at<uint16_t>(workspace, L.wtt);
+  uint16_t* YT = at<uint16_t>(workspace, L.yt);
+  TTT_LAUNCH("amax", s, tttk::launch_amax(W_target, g.w_f32, g.d * g.d, range_wt, s));
+  TTT_LAUNCH("transpose_w_target", s,
+             tttk::launch_transpose_f16(W_target, g.w_f32, WtT, d, d, D.ld_y, range_wt, s));
+  TTT_LAUNCH("conv", s,
+             tttk::launch_conv(X0b, nullptr, 0, conv_taps, g.w_f32, Y, D, (int)g.K, C,
+                               g.pad_chunk, nullptr, range_y, s, YT));
+  TTT_LAUNCH("conv_repair", s,
+             tttk::launch_conv_repair(X0b, nullptr, 0, conv_taps, g.w_f32, Y, D, (int)g.K, C,
+                                      g.pad_chunk, nullptr, range_y, s));
+  uint16_t* Z = at<uint16_t>(workspace, L.z);
+  uint16_t* ZT = at<uint16_t>(workspace, L.zt);
+  uint32_t* SA = at<uint32_t>(workspace, L.sa);
+  TTT_LAUNCH("bwd_gate_up", s, tttk::launch_gate_up_bwd(Hb, Wgp, Wup, Z, ZT, SA, D, s));
+  uint16_t* VT = at<uint16_t>(workspace, L.vt);
+  TTT_LAUNCH("bwd_target", s,
+             tttk::launch_target_bwd(Y, WtT, VT, DOV + g.d, L.ld_ov, eta, D, range, s));
+  uint16_t* DOT = at<uint16_t>(workspace, L.dot);
+  uint16_t* HT = at<uint16_t>(workspace, L.ht);
+  TTT_LAUNCH("bwd_to_slab", s,
+             tttk::launch_to_slab(dO, g.act_f32, g.d, DOT, B, T, (int)g.T_pad, d, false, s));
+  TTT_LAUNCH("bwd_to_slab", s,
+             tttk::launch_to_slab(Hb, false, g.d, HT, B, T, (int)g.T_pad, d, true, s));
+
+  // The states W_i of every chunk, transposed (rows d_ff), into the first d
+  // columns of the chunk's [W_i^T | Gbar_{i+1}^T]: the forward's update
+  // with its operands swapped.
+  uint16_t* WGT = at<uint16_t>(workspace, L.wgt);
+  const tttk::Dims Dsw = tttk::make_dims(B, T, f, d);
+  TTT_LAUNCH("bwd_states", s,
+             tttk::launch_contract_bf16(VT, ZT, Dsw, W_down0, g.w_f32, true, g.w0_stride, g.f,
+                                        WGT, g.nchunks * snap_f2d, 2 * d, nullptr, false, C, s));
+  // The state gradients Gbar_{i+1} = dW_final + sum_{j > i} dO_j^T Z_j of
+  // every chunk, backwards over the tokens (the scan ends at dW_down0), and
+  // their transposes into the last d columns of [W_i^T | Gbar_{i+1}^T].
+  uint16_t* GS = at<uint16_t>(workspace, L.gs);
+  float* dw0_all = (g.w0_stride == 0 && g.B > 1) ? at<float>(workspace, L.dw0) : dW_down0;
+  TTT_LAUNCH("bwd_state_grads", s,
+             tttk::launch_contract_bf16(ZT, DOT, D, dW_final, true, false, df, g.f, GS,
+                                        g.nchunks * snap_df, f, dw0_all, true, C, s));
+  TTT_LAUNCH("bwd_transpose_grads", s,
+             tttk::launch_slab_transpose(GS, snap_df, WGT, snap_f2d, 2 * g.d, d, B * nch, d, f,
+                                         s));
+  if (dw0_all != dW_down0)
+    TTT_LAUNCH("bwd_sum", s, tttk::launch_sum_parts(dw0_all, df, B, dW_down0, df, s));
+
+  // dZ (and through the SiLU's backward, dG and dU), then dV.
+  uint16_t* DGU = at<uint16_t>(workspace, L.dgu);
+  uint16_t* DGT = at<uint16_t>(workspace, L.dgt);
+  uint16_t* DUT = at<uint16_t>(workspace, L.dut);
+  TTT_LAUNCH("bwd_dz", s,
+             tttk::launch_act_gemm_dz(DOV, L.ld_ov, WGT, g.nchunks * snap_f2d, snap_f2d, d, f, C,
+                                      nch, SA, DGU, L.ld_gu, DGT, DUT, D, s));
+  uint16_t* DV = at<uint16_t>(workspace, L.dv);
+  uint16_t* DVT = at<uint16_t>(workspace, L.dvt);
+  TTT_LAUNCH("bwd_dv", s,
+             tttk::launch_act_gemm_dv(Z, D.ld_z, GS, g.nchunks * snap_df, snap_df, d, f, C, nch,
+                                      eta, DV, g.d, DVT, D, s));
+
+  // The target's and the conv's backward.
+  const uint16_t* Wtb = static_cast<const uint16_t*>(W_target);
+  if (g.w_f32) {
+    TTT_LAUNCH("cast_bf16", s, tttk::launch_cast_bf16(static_cast<const float*>(W_target),
+                                                      at<uint16_t>(workspace, L.wtb), g.d * g.d, s));
+    Wtb = at<uint16_t>(workspace, L.wtb);
+  }
+  float* DY = at<float>(workspace, L.dy);
+  TTT_LAUNCH("bwd_dy", s, tttk::launch_nt_gemm(DV, g.d, Wtb, g.d, d, d, DY, g.d, D, s));
+  TTT_LAUNCH("bwd_conv", s,
+             tttk::launch_conv_bwd(DY, X0b, conv_taps, g.w_f32, dX0, dtaps,
+                                   at<float>(workspace, L.part), B, T, d, (int)g.K, C,
+                                   g.pad_chunk, s));
+  const tttk::Dims Dflat_dd = tttk::make_dims(1, (int)(g.B * g.T_pad), d, d);
+  TTT_LAUNCH("bwd_dw_target", s,
+             tttk::launch_contract_bf16(DVT, YT, Dflat_dd, nullptr, true, false, 0, 0, nullptr,
+                                        0, 0, dW_target, false, 64, s));
+
+  // The gated MLP's weight gradients and dH.
+  const tttk::Dims Dflat_fd = tttk::make_dims(1, (int)(g.B * g.T_pad), f, d);
+  TTT_LAUNCH("bwd_dw_gate_up", s,
+             tttk::launch_contract_bf16(HT, DGT, Dflat_fd, nullptr, true, false, 0, 0, nullptr,
+                                        0, 0, dWg, false, 64, s));
+  TTT_LAUNCH("bwd_dw_gate_up", s,
+             tttk::launch_contract_bf16(HT, DUT, Dflat_fd, nullptr, true, false, 0, 0, nullptr,
+                                        0, 0, dWu, false, 64, s));
+  uint16_t* WGUT = at<uint16_t>(workspace, L.wgut);
+  TTT_LAUNCH("bwd_transpose_w", s, tttk::launch_transpose_bf16(Wg, g.w_f32, WGUT, f, d, L.ld_gu, s));
+  TTT_LAUNCH("bwd_transpose_w", s,
+             tttk::launch_transpose_bf16(Wu, g.w_f32, WGUT + g.f, f, d, L.ld_gu, s));
+  TTT_LAUNCH("bwd_dh", s,
+             tttk::launch_nt_gemm(DGU, L.ld_gu, WGUT, L.ld_gu, d, 2 * f, dH, g.d, D, s));
+  return TTT_OK;
+}
+
 ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void* Wg,
                                 const void* Wu, void* Z, void* workspace, size_t workspace_bytes,
                                 void* stream) {

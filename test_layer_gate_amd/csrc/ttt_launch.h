@@ -150,7 +150,7 @@ hipError_t launch_transpose_f16(const void* src, bool src_f32, uint16_t* dst, in
 hipError_t launch_conv(const uint16_t* X0, const uint16_t* X0_next, int n_next,
                        const void* taps, bool taps_f32, uint16_t* Y, const Dims& g, int K,
                        int chunk, bool pad_chunk, const BlockInfo* blocks, uint32_t* range,
-                       hipStream_t s);
+                       hipStream_t s, uint16_t* yt = nullptr);
 hipError_t launch_conv_repair(const uint16_t* X0, const uint16_t* X0_next, int n_next,
                               const void* taps, bool taps_f32, uint16_t* Y, const Dims& g, int K,
                               int chunk, bool pad_chunk, const BlockInfo* blocks,
@@ -255,5 +255,85 @@ hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bs
                         int64_t snap_cstride, void* O, bool out_f32, const Dims& g,
                         int tok_begin, int tok_end, int chunk, const ApplyTile* tiles,
                         int n_tiles, int n_chunks, hipStream_t s);
+
+// ------------------------------------------------------------ backward
+// (ttt_backward.hip, and the prefill kernels' backward variants)
+
+// gate/up for the backward: Z (bf16, token-major [B][T][ld_z]), ZT as bf16
+// slabs (sb<256>(f x T_pad) per sequence), and sa [B][T][f]: per element the
+// bf16 pair (phi(G), U phi'(G)) in the low and high halves of a word.
+hipError_t launch_gate_up_bwd(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
+                              uint16_t* Z, uint16_t* ZT, uint32_t* sa, const Dims& g,
+                              hipStream_t s);
+// The target for the backward: eta * V as bf16 slabs (VT, sb<256>(d x T_pad)
+// per sequence) and token-major bf16 (Vtok [B][T] rows of vtok_ld), the
+// exponents of Y and WtT (range groups) divided out.
+hipError_t launch_target_bwd(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, uint16_t* Vtok,
+                             int64_t vtok_ld, float eta, const Dims& g, const uint32_t* range,
+                             hipStream_t s);
+// A contraction over tokens on the update kernel, bf16 operands: for each
+// sequence b, the state S[c][j] (j < g.f rows of the slab matrix A, c < g.d
+// rows of the slab matrix Bm, both sb<256>(rows x T_pad) per sequence)
+// starts at Winit (null: zero; element (c, j) at Winit + b * winit_bstride +
+// c * winit_ld + j, or j * winit_ld + c with winit_trans), accumulates
+// sum_t A[j][t] Bm[c][t] over the tokens (backwards with reverse), stores
+// bf16 snapshots at chunk boundaries as the prefill's update does (unless
+// snap is null; in reverse, chunk i's snapshot is the state after every
+// later chunk) and, unless Wout is null, the final fp32 state [B][g.d][g.f].
+// The snapshots are sb<256>(g.d x snap_k) matrices (snap_k >= g.f; the
+// state fills their first g.f columns), snap_bstride elements per sequence.
+hipError_t launch_contract_bf16(const uint16_t* A, const uint16_t* Bm, const Dims& g,
+                                const void* Winit, bool winit_f32, bool winit_trans,
+                                int64_t winit_bstride, int64_t winit_ld, uint16_t* snap,
+                                int64_t snap_bstride, int snap_k, float* Wout, bool reverse,
+                                int chunk, hipStream_t s);
+// dZ for every chunk as one contraction over K = 2d: dZ_i = [dO_i | eta V_i]
+// [W_i^T | Gbar_{i+1}^T]^T, the token-major bf16 operand [B][T][lda] holding
+// dO in columns [0, d) and eta V in [d, 2d), the chunk's bf16 state matrix
+// sb<256>(f x 2d) holding W_i^T in columns [0, d) and Gbar_{i+1}^T in
+// [d, 2d) (sequence stride sbs, chunk stride scs); the SiLU's backward in
+// the epilogue: dG = dZ U phi'(G), dU = dZ phi(G) from sa, written
+// token-major into dgu ([B][T][ld_gu]: dG then dU) and as bf16 slabs dgt, dut
+// (sb<256>(f x B T_pad), token b T_pad + t).
+hipError_t launch_act_gemm_dz(const uint16_t* dOV, int64_t lda, const uint16_t* WGT, int64_t sbs,
+                              int64_t scs, int d, int f, int chunk, int n_chunks,
+                              const uint32_t* sa, uint16_t* dgu, int64_t ld_gu, uint16_t* dgt,
+                              uint16_t* dut, const Dims& g, hipStream_t s);
+// dV_i = eta Z_i Gbar_{i+1}^T for every chunk, Gbar as bf16 sb<256>(d x f)
+// snapshots: token-major bf16 dv ([B][T][ld_dv]) and slabs dvt
+// (sb<256>(d x B T_pad)).
+hipError_t launch_act_gemm_dv(const uint16_t* Z, int64_t ldz, const uint16_t* G, int64_t sbs,
+                              int64_t scs, int d, int f, int chunk, int n_chunks, float eta,
+                              uint16_t* dv, int64_t ld_dv, uint16_t* dvt, const Dims& g,
+                              hipStream_t s);
+// out[b][t][n] = sum_k A[b][t][k] Bm[n][k], bf16 operands, fp32 output.
+hipError_t launch_nt_gemm(const uint16_t* A, int64_t lda, const uint16_t* Bm, int64_t ldb, int N,
+                          int K, float* out, int64_t ldo, const Dims& g, hipStream_t s);
+// Token-major [B][T][ld_src] (bf16 or fp32, D features) to bf16 slabs:
+// sb<256>(D x T_pad) per sequence, or with flat sb<256>(D x B T_pad).
+hipError_t launch_to_slab(const void* src, bool src_f32, int64_t ld_src, uint16_t* dst, int B,
+                          int T, int T_pad, int D, bool flat, hipStream_t s);
+// dst[c * ld_dst + r] = bf16(src[r][c]) for a rows x cols matrix.
+hipError_t launch_transpose_bf16(const void* src, bool src_f32, uint16_t* dst, int rows,
+                                 int cols, int64_t ld_dst, hipStream_t s);
+// nmat matrices sb<256>(R x C) to the columns [k0, k0 + R) of sb<256>(C x
+// dst_K) matrices, bf16.
+hipError_t launch_slab_transpose(const uint16_t* src, int64_t src_stride, uint16_t* dst,
+                                 int64_t dst_stride, int64_t dst_K, int k0, int nmat, int R,
+                                 int C, hipStream_t s);
+// dst[r][c] (row stride ld_dst) = bf16(src[r][c]) (row stride ld_src; bf16
+// or fp32) for rows x cols (cols a multiple of 8).
+hipError_t launch_rows_bf16(const void* src, bool src_f32, int64_t ld_src, uint16_t* dst,
+                            int64_t ld_dst, int64_t rows, int cols, hipStream_t s);
+// The conv's backward from dY (fp32 [B][T][d]) and the bf16 X0 [B][T][d]:
+// dX0 (fp32 [B][T][d]) and dtaps (fp32 [K][d], over the batch), through part
+// (conv_bwd_part_floats floats).
+int64_t conv_bwd_part_floats(int B, int T, int K, int d);
+hipError_t launch_conv_bwd(const float* dY, const uint16_t* X0, const void* taps, bool taps_f32,
+                           float* dX0, float* dtaps, float* part, int B, int T, int d, int K,
+                           int chunk, bool pad_chunk, hipStream_t s);
+// out[i] = sum over p < n_parts of in[p * stride + i], in order.
+hipError_t launch_sum_parts(const float* in, int64_t stride, int n_parts, float* out, int64_t n,
+                            hipStream_t s);
 
 }  // namespace tttk

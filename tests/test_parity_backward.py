@@ -1,0 +1,148 @@
+"""GPU parity of the prefill's backward pass (ttt_layer_backward) against
+the oracle's ttt_prefill_backward, every gradient element by element.
+
+The backward takes bf16 operands with fp32 accumulation and keeps every
+chunk's state W_i and state gradient Gbar_{i+1} as bf16 copies, so each
+gradient carries a few bf16 roundings of relative size 2^-9 along its chain
+(the state, the activation factors, the operand copies): the bar is
+max|err| / max|ref| <= 2e-2 per gradient, as for the forward's output.
+
+The amplified configurations make the fast-weight term dominate the output,
+so that a dropped or misplaced term of the chunk recurrence's reverse (the
+eta V Gbar term of dZ, the state before rather than after a chunk, dW_final)
+moves a gradient far past the bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.ttt_oracle as ora
+import synth
+from test_parity import rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+BWD_TOL = 2e-2
+GRADS = ("dH", "dX0", "dWg", "dWu", "dW_down0", "dtaps", "dW_target")
+
+
+@pytest.fixture(scope="module")
+def ttt():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU")
+    import test_layer_gate_amd as m
+    m.lib()
+    return m
+
+
+def upstream(x, dtype, seed, with_dwf=True):
+    """dO [B, T, d] (exact in the activation dtype) and dW_final [B, d, f]
+    fp32 (or None), both standard normal."""
+    B, T, d = x["H"].shape
+    f = x["Wg"].shape[0]
+    rng = np.random.default_rng(seed)
+    dO = rng.standard_normal((B, T, d)).astype(np.float32)
+    if dtype == "bf16":
+        dO = synth.round_to_bf16(dO)
+    dWf = rng.standard_normal((B, d, f)).astype(np.float32) if with_dwf else None
+    return dO, dWf
+
+
+def run_backward(ttt, x, dtype, eta, chunk, dO, dWf, pad="sequence", W0=None):
+    t = to_dev(x, dtype)
+    if W0 is not None:
+        t["W_down0"] = torch.from_numpy(W0).to("cuda").to(t["Wg"].dtype)
+    dO_t = torch.from_numpy(dO).to("cuda").to(t["H"].dtype)
+    dWf_t = None if dWf is None else torch.from_numpy(dWf).to("cuda")
+    g = ttt.layer_backward(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
+                           t["W_target"], eta, chunk, dO_t, dW_final=dWf_t, pad=pad)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in g.items()}
+
+
+def check(x, g, eta, chunk, dO, dWf, what, pad="sequence", W0=None):
+    W0 = x["W_down0"] if W0 is None else W0
+    ref = ora.ttt_prefill_backward(x["H"], x["X0"], x["Wg"], x["Wu"], W0, x["taps"],
+                                   x["W_target"], eta, chunk, dO, dW_final=dWf, pad=pad)
+    errs = {k: rel(g[k], ref[k]) for k in GRADS}
+    print(f"{what}: " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()), flush=True)
+    for k in GRADS:
+        assert g[k].shape == ref[k].shape, k
+        assert np.isfinite(g[k]).all(), k
+    bad = {k: e for k, e in errs.items() if not e <= BWD_TOL}
+    assert not bad, f"{what}: {bad}"
+    return errs
+
+
+@pytest.mark.parametrize("pad", ["sequence", "chunk"])
+@pytest.mark.parametrize("name", ["tiny_amp", "mid_amp"])
+def test_backward_matches_oracle(ttt, name, pad):
+    cfg = synth.CONFIGS[name]
+    x = synth.make_inputs(cfg, seed=200)
+    dO, dWf = upstream(x, cfg.dtype, seed=201)
+    g = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf, pad=pad)
+    check(x, g, cfg.eta, cfg.chunk, dO, dWf, f"{name} {pad}", pad=pad)
+
+
+def test_backward_fp32_operands(ttt):
+    """fp32 activations and weights (the tiny configuration): cast to bf16
+    inside, gradients still fp32."""
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.make_inputs(cfg, seed=202)
+    dO, dWf = upstream(x, cfg.dtype, seed=203)
+    g = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf)
+    check(x, g, cfg.eta, cfg.chunk, dO, dWf, "tiny fp32")
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_backward_ragged_batch(ttt, shared):
+    """B = 2, T = 1000 (a partial last chunk and a partial 256-token tile);
+    W_down0 shared (its gradient summed over the batch) or per sequence."""
+    cfg = synth.CONFIGS["mid_amp"]
+    x = synth.make_inputs(cfg, batch=2, seq_len=1000, seed=204)
+    W0 = None if shared else np.stack([x["W_down0"], synth.round_to_bf16(-0.5 * x["W_down0"])])
+    dO, dWf = upstream(x, cfg.dtype, seed=205)
+    g = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf, W0=W0)
+    check(x, g, cfg.eta, cfg.chunk, dO, dWf, f"ragged B=2 shared={shared}", W0=W0)
+
+
+def test_backward_without_state_gradient(ttt):
+    """dW_final = NULL is a zero upstream gradient of the final state."""
+    cfg = synth.CONFIGS["mid_amp"]
+    x = synth.make_inputs(cfg, seed=206)
+    dO, _ = upstream(x, cfg.dtype, seed=207, with_dwf=False)
+    g = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, None)
+    check(x, g, cfg.eta, cfg.chunk, dO, None, "dW_final none")
+
+
+@pytest.mark.parametrize("T,C", [(1, 64), (65, 64), (300, 128), (257, 256)])
+def test_backward_edge_lengths(ttt, T, C):
+    cfg = synth.CONFIGS["tiny_amp"]
+    x = synth.make_inputs(cfg, seq_len=T, seed=300 + T)
+    dO, dWf = upstream(x, cfg.dtype, seed=400 + T)
+    g = run_backward(ttt, x, cfg.dtype, cfg.eta, C, dO, dWf)
+    check(x, g, cfg.eta, C, dO, dWf, f"T={T} C={C}")
+
+
+def test_backward_state_gradient_only(ttt):
+    """dO = 0: every gradient flows from dW_final through the updates alone
+    (dZ = eta V Gbar, dV = eta Z Gbar^T with Gbar = dW_final in every
+    chunk, and dW_down0 = dW_final exactly)."""
+    cfg = synth.CONFIGS["mid_amp"]
+    x = synth.make_inputs(cfg, seed=208)
+    dO, dWf = upstream(x, cfg.dtype, seed=209)
+    dO = np.zeros_like(dO)
+    g = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf)
+    check(x, g, cfg.eta, cfg.chunk, dO, dWf, "dO zero")
+    assert np.array_equal(g["dW_down0"], dWf[0])
+
+
+def test_backward_deterministic(ttt):
+    cfg = synth.CONFIGS["mid_amp"]
+    x = synth.make_inputs(cfg, batch=2, seq_len=700, seed=210)
+    dO, dWf = upstream(x, cfg.dtype, seed=211)
+    a = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf)
+    b = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf)
+    for k in GRADS:
+        assert np.array_equal(a[k], b[k]), k
