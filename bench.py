@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule prefix|running] [--no-cpu-baseline]
-                    [--variant plain|packed|clipped|packed_clipped|continue|decode]
+                    [--variant plain|packed|clipped|packed_clipped|continue|decode|
+                               backward]
     python bench.py --summarize DIR [--fetch DIR2 --write DIR3]
                     --summary-out FILE.md --command "..."
     python bench.py --vendor-gemm
@@ -20,8 +21,10 @@ target, update with per-chunk snapshots, apply), with inputs resident in HBM.
 clipped (ttt_layer_forward_clipped, limit --clip), packed_clipped
 (ttt_layer_forward_packed_clipped: both at once), continue
 (ttt_layer_forward_continue: an fp32 state updated in place and K - 1
-look-ahead rows) or decode (ttt_decode_step token by token with chunk-local
-padding; one step is one chunk of C tokens, the chunk's update included).
+look-ahead rows), decode (ttt_decode_step token by token with chunk-local
+padding; one step is one chunk of C tokens, the chunk's update included) or
+backward (ttt_layer_backward: every gradient of the prefill for a random
+upstream dO and dW_final, the forward's activations recomputed inside).
 Prints one JSON line: tokens/s for the step, the per-kernel device times
 (HIP events recorded by the library around each launch, on the stream it
 launches on), the roofline of the dominant kernel, and the CPU oracle timed
@@ -45,7 +48,7 @@ import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "test_layer_gate_amd", "csrc", "ttt_kernels.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "test_layer_gate_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CALIB_BYTES = 256 << 20      # the known-size copy run before the timed region
 # library timing names -> kernel names in rocprofv3 traces
@@ -57,7 +60,25 @@ KERNEL_NAMES = {"gate_up": "gate_up_kernel", "target": "target_kernel",
                 "calibration_copy": "calibration_copy_kernel",
                 "range_clear": "range_clear_kernel", "amax": "amax_kernel",
                 "conv_repair": "conv_repair_kernel", "gate_up_repair": "gate_up_repair_kernel",
-                "target_repair": "target_repair_kernel"}
+                "target_repair": "target_repair_kernel",
+                "bwd_gate_up": "gate_up_bwd_kernel", "bwd_target": "target_bwd_kernel",
+                "bwd_states": "update_kernel", "bwd_state_grads": "update_kernel",
+                "bwd_dz": "dz_gemm_kernel", "bwd_dv": "dv_gemm_kernel",
+                "bwd_dy": "nt_gemm_kernel", "bwd_dh": "nt_gemm_kernel",
+                "bwd_dw_target": "update_kernel", "bwd_dw_gate_up": "update_kernel",
+                "bwd_conv": "conv_bwd", "bwd_rows": "rows_bf16_kernel",
+                "bwd_to_slab": "to_slab_kernel", "bwd_transpose_grads": "slab_transpose_kernel",
+                "bwd_transpose_w": "transpose_bf16_kernel", "bwd_sum": "sum_parts_kernel"}
+
+
+def backward_flops(cfg):
+    """Contraction FLOPs (2 per multiply-add) that one ttt_layer_backward
+    call executes: the recomputed gate/up (4 B T d f) and target (2 B T d^2),
+    the scans for the states and the state gradients (2 B T d f each), dZ
+    (4 B T d f: two products side by side), dV (2 B T d f), dY and dW_target
+    (2 B T d^2 each), dWg and dWu (4 B T d f) and dH (4 B T d f)."""
+    B, T, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
+    return 22.0 * B * T * d * f + 6.0 * B * T * d * d
 
 
 def kernel_work(name, cfg, T_pad):
@@ -73,6 +94,12 @@ def kernel_work(name, cfg, T_pad):
         return "mfma", 2.0 * B * T * d * d
     if name in ("update_prefix", "update_running", "apply"):
         return "mfma", 2.0 * B * T * d * f
+    if name in ("bwd_gate_up", "bwd_dz", "bwd_dw_gate_up", "bwd_dh"):
+        return "mfma", 4.0 * B * T * d * f
+    if name in ("bwd_states", "bwd_state_grads", "bwd_dv"):
+        return "mfma", 2.0 * B * T * d * f
+    if name in ("bwd_target", "bwd_dy", "bwd_dw_target"):
+        return "mfma", 2.0 * B * T * d * d
     if name == "conv":
         return "hbm", 2.0 * B * T * d + 2.0 * B * T_pad * d + 2.0 * K * d
     if name == "transpose_w_target":
@@ -89,13 +116,23 @@ def kernel_work(name, cfg, T_pad):
 
 
 def source_hash():
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """sha256[:16] over the kernel sources (.hip and .h files, by name)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_key(workload, variant):
+    return workload if variant == "plain" else f"{workload}/{variant}"
 
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
-    only if it was taken on the kernel source as it is now."""
+    only if it was taken on the kernel source as it is now and the kernel's
+    name in the trace belongs to this one timing name of the step."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
@@ -104,7 +141,9 @@ def measured_traffic(kernel, workload):
     if rec.get("kernel_source_sha256_16") != source_hash():
         return None
     ent = rec.get("kernels", {}).get(workload, {}).get(kernel)
-    return None if ent is None else ent.get("hbm_bytes_per_launch")
+    if ent is None or ent.get("shared_name"):
+        return None
+    return ent.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(cfg, x, budget_s=15.0, variant="plain", clip=None, doc_len=None):
@@ -124,7 +163,14 @@ def cpu_baseline(cfg, x, budget_s=15.0, variant="plain", clip=None, doc_len=None
     def run(j):
         n = j * C
         t0 = time.perf_counter()
-        if variant == "decode":
+        if variant == "backward":
+            B, T, d = x["H"].shape
+            dO = np.random.default_rng(1).standard_normal((1, n, d))
+            dWf = np.random.default_rng(2).standard_normal((1, d, x["Wg"].shape[0]))
+            ora.ttt_prefill_backward(x["H"][:1, :n], x["X0"][:1, :n], x["Wg"], x["Wu"],
+                                     x["W_down0"], x["taps"], x["W_target"], cfg.eta, C, dO,
+                                     dW_final=dWf)
+        elif variant == "decode":
             ora.ttt_decode(x["H"][:1, :n], x["X0"][:1, :n], x["Wg"], x["Wu"], x["W_down0"],
                            x["taps"], x["W_target"], cfg.eta, C)
         elif variant in ("packed", "packed_clipped"):
@@ -248,19 +294,35 @@ def summarize(args):
                   f"counter-to-byte factors: fetch {f_fac:.4f}, write {w_fac:.4f}.", "",
                   "| kernel | dispatches | fetch MB | write MB | HBM MB (scaled) |",
                   "|---|---|---|---|---|"]
-        rec = {"kernel_source_sha256_16": source_hash(), "workload": args.workload,
-               "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {args.workload: {}}}
+        # One record per kernel source; each workload (and variant) keeps its
+        # own entry, so profiling one does not drop another's.
+        key = traffic_key(args.workload, args.variant)
+        rec = {}
+        try:
+            with open(TRAFFIC_FILE) as fh:
+                rec = json.load(fh)
+        except (OSError, ValueError):
+            pass
+        if rec.get("kernel_source_sha256_16") != source_hash():
+            rec = {"kernel_source_sha256_16": source_hash(), "kernels": {}}
+        rec.pop("workload", None)
+        rec.setdefault("factors", {})[key] = {"fetch": f_fac, "write": w_fac}
+        rec.pop("fetch_factor", None)
+        rec.pop("write_factor", None)
+        rec["kernels"][key] = {}
+        names_in_step = [n for n in KERNEL_NAMES
+                         if n.startswith("bwd_") == (args.variant == "backward")]
         for name, v in sorted(per.items()):
             fe = sum(v.get("FETCH_SIZE", [0])) / max(len(v.get("FETCH_SIZE", [])), 1)
             wr = sum(v.get("WRITE_SIZE", [0])) / max(len(v.get("WRITE_SIZE", [])), 1)
             tot = fe * f_fac + wr * w_fac
             lines.append(f"| {name} | {len(v.get('FETCH_SIZE', []))} | {fe / 1e6:.1f} | "
                          f"{wr / 1e6:.1f} | {tot / 1e6:.1f} |")
-            for lib_name, kname in KERNEL_NAMES.items():
-                if kname == name:
-                    rec["kernels"][args.workload][lib_name] = {
-                        "hbm_bytes_per_launch": tot, "fetch_bytes": fe * f_fac,
-                        "write_bytes": wr * w_fac}
+            sharing = [n for n in names_in_step if KERNEL_NAMES[n] == name]
+            for lib_name in sharing:
+                rec["kernels"][key][lib_name] = {
+                    "hbm_bytes_per_launch": tot, "fetch_bytes": fe * f_fac,
+                    "write_bytes": wr * w_fac, "shared_name": len(sharing) > 1}
         with open(TRAFFIC_FILE, "w") as fh:
             json.dump(rec, fh, indent=1)
     if args.mfma:
@@ -311,7 +373,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", default="plain",
                     choices=["plain", "packed", "clipped", "packed_clipped", "continue",
-                             "decode"])
+                             "decode", "backward"])
     ap.add_argument("--docs", type=int, default=32, help="packed variant: equal documents")
     ap.add_argument("--clip", type=float, default=1e-3, help="clipped variant: norm limit")
     ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
@@ -386,6 +448,14 @@ def main():
         # the segment continues a document: its state is fp32 and K - 1 rows follow it
         W_state = t["W_down0"].float().expand(B, d, f).contiguous()
         X0_next = t["X0"][:, :cfg.conv_k - 1].contiguous()
+    elif args.variant == "backward":
+        ws_bytes = ttt.backward_workspace_size(desc, cfg.chunk)
+        gen = torch.Generator(device=dev).manual_seed(5)
+        dO = torch.randn(t["H"].shape, generator=gen, device=dev).to(tdt)
+        dWf_up = torch.randn((B, d, f), generator=gen, device=dev)
+        shapes = {"dH": (B, T, d), "dX0": (B, T, d), "dWg": (f, d), "dWu": (f, d),
+                  "dW_down0": (d, f), "dtaps": (cfg.conv_k, d), "dW_target": (d, d)}
+        grads = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
     else:
         ws_bytes = ttt.workspace_size(desc, cfg.chunk)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -406,6 +476,10 @@ def main():
                                      t["W_target"], cfg.eta, cfg.chunk, starts,
                                      schedule=args.schedule, clip=pclip, out=O, W_down_final=Wf,
                                      workspace=ws)
+        elif args.variant == "backward":
+            ttt.layer_backward(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
+                               t["W_target"], cfg.eta, cfg.chunk, dO, dW_final=dWf_up,
+                               out=grads, workspace=ws)
         elif args.variant == "continue":
             ttt.layer_forward_continue(t["H"], t["X0"], X0_next, t["Wg"], t["Wu"], W_state,
                                        t["taps"], t["W_target"], cfg.eta, cfg.chunk,
@@ -446,7 +520,8 @@ def main():
           file=sys.stderr, flush=True)
 
     tokens = B * (cfg.chunk if args.variant == "decode" else T)
-    flops = synth.algorithmic_flops(cfg) * tokens / (B * T)
+    flops = (backward_flops(cfg) if args.variant == "backward"
+             else synth.algorithmic_flops(cfg) * tokens / (B * T))
     value = tokens / (ms_per_step / 1e3)
     tflops = flops / (ms_per_step / 1e3) / 1e12
     kernels = {n: {"launches_per_step": c / args.steps, "avg_ms": ms / c}
@@ -465,7 +540,7 @@ def main():
         achieved = work / avg_s / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(dom, cfg.name)
+    roof["traffic"] = measured_traffic(dom, traffic_key(cfg.name, args.variant))
 
     line = {
         "metric": "TTT-MLP layer prefill tokens/s + MFMA util (Qwen3-4B shape, 64k ctx)",

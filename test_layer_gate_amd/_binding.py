@@ -265,12 +265,12 @@ def backward_workspace_size(desc: Desc, chunk: int) -> int:
 
 
 def layer_backward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, dO, *,
-                   dW_final=None, pad="sequence", workspace=None, stream=None):
+                   dW_final=None, pad="sequence", out=None, workspace=None, stream=None):
     """The prefill's gradients (ttt_layer_backward) for the upstream
     gradients dO [B, T, d] (H's dtype) and dW_final [B, d, f] fp32 (None:
     zero). Returns a dict of fp32 tensors: dH, dX0 [B, T, d]; dWg, dWu
     [f, d]; dW_down0 [d, f] (shared W_down0) or [B, d, f]; dtaps [K, d];
-    dW_target [d, d]."""
+    dW_target [d, d]. out: such a dict to write into instead of new tensors."""
     desc = _layer_desc(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, None, pad)
     B, T, d = H.shape
     f, K = Wg.shape[0], conv_taps.shape[0]
@@ -287,11 +287,16 @@ def layer_backward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, dO, 
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
     _require_cuda(workspace)
-    f32 = dict(dtype=torch.float32, device=H.device)
-    g = {"dH": torch.empty((B, T, d), **f32), "dX0": torch.empty((B, T, d), **f32),
-         "dWg": torch.empty((f, d), **f32), "dWu": torch.empty((f, d), **f32),
-         "dW_down0": torch.empty(tuple(W_down0.shape), **f32),
-         "dtaps": torch.empty((K, d), **f32), "dW_target": torch.empty((d, d), **f32)}
+    shapes = {"dH": (B, T, d), "dX0": (B, T, d), "dWg": (f, d), "dWu": (f, d),
+              "dW_down0": tuple(W_down0.shape), "dtaps": (K, d), "dW_target": (d, d)}
+    if out is None:
+        g = {k: torch.empty(v, dtype=torch.float32, device=H.device) for k, v in shapes.items()}
+    else:
+        g = out
+        for k, v in shapes.items():
+            if k not in g or tuple(g[k].shape) != v or g[k].dtype != torch.float32:
+                raise ValueError(f"out[{k!r}] must be a float32 tensor of shape {v}")
+            _require_cuda(g[k])
     _check(lib().ttt_layer_backward(
         ctypes.byref(desc), _ptr(H), _ptr(X0), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
         _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk), _ptr(dO),

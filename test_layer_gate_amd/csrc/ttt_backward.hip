@@ -91,8 +91,8 @@ struct PlainSink {
 };
 
 template <int BM, int MODE>
-__global__ __launch_bounds__(64 * KA_NW) void act_gemm_kernel(ActArgs a, Dims g, int tiles_m,
-                                                              int tiles_n) {
+__device__ __forceinline__ void act_gemm(const ActArgs& a, const Dims& g, int tiles_m,
+                                         int tiles_n) {
   using C = ActCfg<BM>;
   using L = Layout<BM, KA_BN, C::WGM, KA_NW>;
   TTT_GEMM_LDS_AB(lds, BM, KA_BN, KA_BK, C::NSTA, C::NSTB)
@@ -167,6 +167,18 @@ __global__ __launch_bounds__(64 * KA_NW) void act_gemm_kernel(ActArgs a, Dims g,
       store_tile_sb<256>(kt, col, kb, v, CvtBf16{1.0f}, cok, PlainSink{a.out_t});
     }
   });
+}
+
+// dZ and dV under kernel names of their own, for traces.
+template <int BM>
+__global__ __launch_bounds__(64 * KA_NW) void dz_gemm_kernel(ActArgs a, Dims g, int tiles_m,
+                                                             int tiles_n) {
+  act_gemm<BM, kActDZ>(a, g, tiles_m, tiles_n);
+}
+template <int BM>
+__global__ __launch_bounds__(64 * KA_NW) void dv_gemm_kernel(ActArgs a, Dims g, int tiles_m,
+                                                             int tiles_n) {
+  act_gemm<BM, kActDV>(a, g, tiles_m, tiles_n);
 }
 
 // ------------------------------------------------------- plain NT GEMM
@@ -532,10 +544,10 @@ hipError_t launch_act_gemm_dz(const uint16_t* dOV, int64_t lda, const uint16_t* 
   const int tiles_n = (f + KA_BN - 1) / KA_BN;
   if (bm == 256) {
     const int tiles_m = g.T_pad / 256;
-    act_gemm_kernel<256, kActDZ><<<tiles_m * tiles_n * g.B, 64 * KA_NW, 0, s>>>(a, g, tiles_m, tiles_n);
+    dz_gemm_kernel<256><<<tiles_m * tiles_n * g.B, 64 * KA_NW, 0, s>>>(a, g, tiles_m, tiles_n);
   } else {
     const int tiles_m = g.T_pad / 64;
-    act_gemm_kernel<64, kActDZ><<<tiles_m * tiles_n * g.B, 64 * KA_NW, 0, s>>>(a, g, tiles_m, tiles_n);
+    dz_gemm_kernel<64><<<tiles_m * tiles_n * g.B, 64 * KA_NW, 0, s>>>(a, g, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }
@@ -562,10 +574,10 @@ hipError_t launch_act_gemm_dv(const uint16_t* Z, int64_t ldz, const uint16_t* G,
   const int tiles_n = (d + KA_BN - 1) / KA_BN;
   if (bm == 256) {
     const int tiles_m = g.T_pad / 256;
-    act_gemm_kernel<256, kActDV><<<tiles_m * tiles_n * g.B, 64 * KA_NW, 0, s>>>(a, g, tiles_m, tiles_n);
+    dv_gemm_kernel<256><<<tiles_m * tiles_n * g.B, 64 * KA_NW, 0, s>>>(a, g, tiles_m, tiles_n);
   } else {
     const int tiles_m = g.T_pad / 64;
-    act_gemm_kernel<64, kActDV><<<tiles_m * tiles_n * g.B, 64 * KA_NW, 0, s>>>(a, g, tiles_m, tiles_n);
+    dv_gemm_kernel<64><<<tiles_m * tiles_n * g.B, 64 * KA_NW, 0, s>>>(a, g, tiles_m, tiles_n);
   }
   return hipGetLastError();
 }

@@ -17,7 +17,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "test_layer_gate_amd", "csrc")
-SOURCES = ["ttt_kernels.hip", "ttt_decode.hip"]
+SOURCES = ["ttt_kernels.hip", "ttt_decode.hip", "ttt_backward.hip"]
 
 # instructions that read M0 without naming it
 IMPLICIT_M0 = re.compile(r"^(s_sendmsg|s_sendmsghalt|s_movrel|v_movrel|v_interp|ds_gws|"
@@ -63,5 +63,5 @@ def test_m0_only_feeds_the_direct_to_lds_loads(tmp_path, src):
             n_loads += 1
             continue
         pytest.fail(f"compiler-generated M0 use: {i!r} (instruction {k})")
-    if src == "ttt_kernels.hip":
+    if src in ("ttt_kernels.hip", "ttt_backward.hip"):
         assert n_loads > 100, "the GEMM core's direct-to-LDS loads are missing"
