@@ -10,13 +10,12 @@ namespace tttk {
 
 typedef uint16_t u16;
 
-// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ u16 bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (u16)(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (NaN stays a NaN): gfx950's
+// v_cvt_pk_bf16_f32, one instruction for two values.
+__device__ __forceinline__ u16 bf16_rne(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
 
 __device__ __forceinline__ float bf16_f32(u16 h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -25,7 +24,7 @@ __device__ __forceinline__ u16 f16_rne(float x) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)bf16_rne(lo) | ((uint32_t)bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {

@@ -613,12 +613,15 @@ __device__ __forceinline__ void store_tile_sb(int64_t K, int r, int64_t k_base, 
   for (int p = 0; p < 2; ++p) {
     const uint32_t lo0 = cvt(a[8 * p + 0], a[8 * p + 1]), lo1 = cvt(a[8 * p + 2], a[8 * p + 3]);
     const uint32_t hi0 = cvt(a[8 * p + 4], a[8 * p + 5]), hi1 = cvt(a[8 * p + 6], a[8 * p + 7]);
-    // q = 2p is (lo0, lo1), q = 2p + 1 is (hi0, hi1). Lane h = 0 keeps q = 2p
-    // and sends q = 2p + 1; lane h = 1 keeps q = 2p + 1 and sends q = 2p.
-    const uint32_t s0 = h ? lo0 : hi0, s1 = h ? lo1 : hi1;
-    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32), r1 = (uint32_t)__shfl_xor((int)s1, 32);
-    const uint4 v = h ? make_uint4(r0, r1, hi0, hi1) : make_uint4(lo0, lo1, r0, r1);
-    sink(sb_offset<SR>(r, k_base + 16 * p + 8 * h, K), v, ok);
+    // q = 2p is (lo0, lo1), q = 2p + 1 is (hi0, hi1). v_permlane32_swap
+    // trades lanes 32..63 of its first operand for lanes 0..31 of its
+    // second: afterwards lane l < 32 holds its own q = 2p in the first and
+    // lane l + 32's q = 2p in the second, and lane l + 32 holds lane l's
+    // q = 2p + 1 in the first and its own in the second.
+    const auto x0 = __builtin_amdgcn_permlane32_swap(lo0, hi0, false, false);
+    const auto x1 = __builtin_amdgcn_permlane32_swap(lo1, hi1, false, false);
+    sink(sb_offset<SR>(r, k_base + 16 * p + 8 * h, K), make_uint4(x0[0], x1[0], x0[1], x1[1]),
+         ok);
   }
 }
 
