@@ -497,6 +497,61 @@ def test_decode_step_validates_before_launch(L):
                               ctypes.c_size_t(1 << 62), None) == UNSUPPORTED
 
 
+# ---- the backward pass ------------------------------------------------------
+
+def bwd_ws(L, desc, chunk=1024):
+    n = ctypes.c_size_t(0)
+    st = L.ttt_backward_workspace_size(ctypes.byref(desc), chunk, ctypes.byref(n))
+    return st, n.value
+
+
+def test_backward_workspace_size(L):
+    st, n = bwd_ws(L, qwen_desc())
+    assert st == OK
+    B, T, d, f, k = 1, 65536, 2560, 9728, 64
+    # at least the per-chunk bf16 states W_i^T and state gradients (both
+    # halves of [W_i^T | Gbar^T], and Gbar itself), Z, Z^T, the SiLU factors
+    # (fp32 words), [dG | dU] token-major, dG^T and dU^T
+    floor = 3 * k * d * f * 2 + B * T * f * (2 + 2 + 4 + 2 * 2 + 2 + 2)
+    assert floor <= n <= floor * 3 // 2
+    st2, n2 = bwd_ws(L, qwen_desc(batch=2, w0_batch_stride=2560 * 9728))
+    assert st2 == OK and n2 > n
+    assert bwd_ws(L, qwen_desc(), 100)[0] == UNSUPPORTED
+
+
+def backward(L, desc, p, dwf=True, eta=1e-3, chunk=1024, ws_bytes=1 << 62):
+    """p: the seven inputs, dO, dW_final, the seven outputs, the workspace."""
+    return L.ttt_layer_backward(ctypes.byref(desc), *p[:7], ctypes.c_float(eta), chunk, p[7],
+                                p[8] if dwf else None, *p[9:16], p[16],
+                                ctypes.c_size_t(ws_bytes), None)
+
+
+def test_backward_validates_before_launch(L):
+    fb = FakeBuffers()
+    p = [fb[i] for i in range(17)]
+    desc = qwen_desc()
+    assert backward(L, desc, p, eta=float("nan")) == INVALID
+    for i in list(range(8)) + list(range(9, 17)):
+        q = list(p)
+        q[i] = ctypes.c_void_p(0)
+        assert backward(L, desc, q) == INVALID, i
+        assert "NULL" in L.ttt_last_error().decode()
+    q = list(p)
+    q[8] = ctypes.c_void_p(p[8].value + 2)            # dW_final misaligned
+    assert backward(L, desc, q) == INVALID
+    _, need = bwd_ws(L, desc)
+    assert backward(L, desc, p, ws_bytes=need - 1) == WORKSPACE
+    q = list(p)
+    q[9] = ctypes.c_void_p(p[0].value + 4096)         # dH inside H
+    assert backward(L, desc, q) == ALIAS
+    q = list(p)
+    q[15] = ctypes.c_void_p(p[16].value + 4096)       # dW_target inside the workspace
+    assert backward(L, desc, q) == ALIAS
+    # per-sequence W_down0 at a stride other than d_model * d_ff
+    assert backward(L, qwen_desc(batch=2, w0_batch_stride=2 * 2560 * 9728), p) == UNSUPPORTED
+    assert "stride" in L.ttt_last_error().decode()
+
+
 # ---- the no-allocation entry point ------------------------------------------
 
 def test_noalloc_rejects_problems_beyond_its_scratch(L):

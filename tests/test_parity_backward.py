@@ -146,3 +146,63 @@ def test_backward_deterministic(ttt):
     b = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf)
     for k in GRADS:
         assert np.array_equal(a[k], b[k]), k
+
+
+def oracle_backward_segments(x, dO, dWf, eta, chunk, seg_chunks=8):
+    """The oracle's gradients of a long sequence (B = 1), in segments of
+    seg_chunks chunks so that its memory stays bounded. The chain rule
+    splits the backward exactly where the split/resume pin splits the
+    forward: a segment [a, b) is the prefill from the state W_a with X0's
+    K - 1 look-ahead rows, so its backward with dW_final = dL/dW_b returns
+    the segment's gradients and dL/dW_a; the look-ahead rows' gradient
+    belongs to the next segment's first rows."""
+    T = x["H"].shape[1]
+    K = x["taps"].shape[0]
+    L = seg_chunks * chunk
+    starts = list(range(0, T, L))
+    # forward: the state at every segment start
+    W = [np.asarray(x["W_down0"], np.float64)[None]]
+    for a in starts[:-1]:
+        b = min(a + L, T)
+        _, Wb = ora.ttt_prefill(x["H"][:, a:b], x["X0"][:, a:min(b + K - 1, T)], x["Wg"],
+                                x["Wu"], W[-1], x["taps"], x["W_target"], eta, chunk)
+        W.append(Wb)
+        print(f"  oracle forward to token {b}", flush=True)
+    d, f = x["Wg"].shape[1], x["Wg"].shape[0]
+    ref = {"dH": np.zeros(x["H"].shape), "dX0": np.zeros(x["X0"].shape),
+           "dWg": np.zeros((f, d)), "dWu": np.zeros((f, d)), "dtaps": np.zeros((K, d)),
+           "dW_target": np.zeros((d, d))}
+    gbar = np.zeros((1, d, f)) if dWf is None else np.asarray(dWf, np.float64)
+    for s in reversed(range(len(starts))):
+        a = starts[s]
+        b = min(a + L, T)
+        e = min(b + K - 1, T)
+        g = ora.ttt_prefill_backward(x["H"][:, a:b], x["X0"][:, a:e], x["Wg"], x["Wu"], W[s],
+                                     x["taps"], x["W_target"], eta, chunk, dO[:, a:b],
+                                     dW_final=gbar)
+        ref["dH"][:, a:b] = g["dH"]
+        ref["dX0"][:, a:e] += g["dX0"]
+        for k in ("dWg", "dWu", "dtaps", "dW_target"):
+            ref[k] += g[k]
+        gbar = g["dW_down0"]
+        print(f"  oracle backward from token {b}", flush=True)
+    ref["dW_down0"] = gbar[0]
+    return ref
+
+
+def test_backward_full_size_whole_sequence(ttt):
+    """The Qwen3-4B shape at T = 65536 (the benchmark's backward call): every
+    gradient over the whole sequence against the segmented oracle."""
+    cfg = synth.CONFIGS["qwen3_4b_64k"]
+    x = synth.make_inputs(cfg)
+    dO, dWf = upstream(x, cfg.dtype, seed=212)
+    g = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf)
+    print("  GPU backward done", flush=True)
+    ref = oracle_backward_segments(x, dO, dWf, cfg.eta, cfg.chunk)
+    errs = {k: rel(g[k], ref[k]) for k in GRADS}
+    print("qwen3_4b_64k: " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()), flush=True)
+    for k in GRADS:
+        assert np.isfinite(g[k]).all(), k
+    bad = {k: e for k, e in errs.items() if not e <= BWD_TOL}
+    assert not bad, bad
+
