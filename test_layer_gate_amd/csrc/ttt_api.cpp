@@ -967,7 +967,7 @@ BwdLayout backward_layout(const Geo& g) {
   L.yt = take(tttk::sb_elems<256>(g.d, BTp) * 2);
   L.z = take(BT * D.ld_z * 2);
   L.zt = take(tttk::zt_elems(D) * 2);
-  L.sa = take(BT * g.f * 4);
+  L.sa = take(BTp * g.f * 4);
   L.vt = take(tttk::vt_elems(D) * 2);
   L.dot = take(tttk::vt_elems(D) * 2);
   L.ht = take(tttk::sb_elems<256>(g.d, BTp) * 2);

@@ -70,9 +70,10 @@ struct ActArgs {
   int K;
   int N, chunk, n_chunks;
   float scale;
-  // dZ: the SiLU's derivative factors [B][T][N] (low half phi(G), high half
-  // U phi'(G), bf16), dG and dU token-major ([B][T][ld_gu]: dG in columns
-  // [0, N), dU in [N, 2N)) and as slabs sb<256>(N x B T_pad).
+  // dZ: the SiLU's derivative factors (low half phi(G), high half U phi'(G),
+  // bf16) in accumulator-fragment order (sa_frag_offset), dG and dU
+  // token-major ([B][T][ld_gu]: dG in columns [0, N), dU in [N, 2N)) and as
+  // slabs sb<256>(N x B T_pad).
   const uint32_t* sa;
   u16* dgu;
   int64_t ld_gu;
@@ -111,62 +112,116 @@ __device__ __forceinline__ void act_gemm(const ActArgs& a, const Dims& g, int ti
   }
   const int N = a.N;
   const int64_t kt = (int64_t)g.B * g.T_pad;
-  static_for<0, L::TM * L::TN>([&](auto I) __attribute__((always_inline)) {
-    constexpr int m = decltype(I)::value / L::TN, n = decltype(I)::value % L::TN;
-    // Coordinates (and the addresses made from them) per tile, through an
-    // opaque copy of the thread index: computed once for all tiles, the
-    // 64 row addresses of a lane would be held across the whole epilogue.
+  // dV's token-major output goes through LDS (free once the core has
+  // drained), so that its stores are whole 16-byte row segments: every wave
+  // writes its values as bf16 rows of a BM x 256 staging tile, then all
+  // threads copy the tile's rows out.
+  constexpr int LDG = KA_BN + 8;  // staging row stride (elements)
+  static_assert(BM * LDG <= (C::NSTA * BM + C::NSTB * KA_BN) * KA_BK, "staging fits");
+  auto stage = [&](int m, int n, const f32x16& v) {
     const Frag<L> fr(true);
-    const int col = n0 + fr.col(n);
-    const bool cok = col < N;
-    const int64_t kb = (int64_t)ti.b * g.T_pad + t0 + fr.wm * L::TM * 32 + m * 32;
-    if constexpr (MODE == kActDZ) {
-      // dG then dU, one temporary tile at a time (the factor words stay).
-      // Loads and stores go through buffer resources based at the tile's
-      // first row and sized to its rows inside the sequence, so that rows
-      // past it read as zero and are not written, with 32-bit offsets.
-      const int rows_ok = max(0, min(BM, g.T - t0));
-      const __amdgpu_buffer_rsrc_t sa_r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint32_t*>(a.sa) + ((int64_t)ti.b * g.T + t0) * N, 0, rows_ok * N * 4,
-          kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t gu_r = __builtin_amdgcn_make_buffer_rsrc(
-          a.dgu + ((int64_t)ti.b * g.T + t0) * a.ld_gu, 0, (int)(rows_ok * a.ld_gu * 2),
-          kRsrcWord3);
-      const int drop_sa = rows_ok * N * 4, drop_gu = (int)(rows_ok * a.ld_gu * 2);
-      uint32_t w[16];
+    const int cl = fr.col(n);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tr = fr.row(m, r / 4) + r % 4;  // row within the tile
-        w[r] = __builtin_amdgcn_raw_buffer_load_b32(sa_r, cok ? (tr * N + col) * 4 : drop_sa, 0, 0);
-      }
+    for (int q = 0; q < 4; ++q) {
+      u16* sr = lds + fr.row(m, q) * LDG + cl;
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        f32x16 v;
+      for (int e = 0; e < 4; ++e) sr[e * LDG] = bf16_rne(v[4 * q + e]);
+    }
+  };
+  auto flush = [&](u16* dst, int64_t ld) {
+    __syncthreads();
+    constexpr int SEGS = BM * (KA_BN / 8);
+    static_assert(SEGS % (64 * KA_NW) == 0, "whole rounds");
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float fac = part == 0 ? __uint_as_float(w[r] & 0xffff0000u)   // U phi'(G)
-                                      : __uint_as_float(w[r] << 16);          // phi(G)
-          v[r] = acc[m][n][r] * fac;
-          const int tr = fr.row(m, r / 4) + r % 4;
-          __builtin_amdgcn_raw_buffer_store_b16(
-              bf16_rne(v[r]), gu_r,
-              cok ? (int)((tr * a.ld_gu + part * N + col) * 2) : drop_gu, 0, 0);
+    for (int i = 0; i < SEGS / (64 * KA_NW); ++i) {
+      const int sgi = threadIdx.x + i * (64 * KA_NW);
+      const int row = sgi / (KA_BN / 8), cc = (sgi % (KA_BN / 8)) * 8;
+      const int t = t0 + row, c = n0 + cc;
+      if (t < g.T && c < N)
+        *reinterpret_cast<uint4*>(dst + ((int64_t)ti.b * g.T + t) * ld + c) =
+            *reinterpret_cast<const uint4*>(lds + row * LDG + cc);
+    }
+  };
+  if constexpr (MODE == kActDZ) {
+    // The factor words of two tiles at a time (a lane's four consecutive
+    // tokens are 16 bytes), then dG and dU of both tiles: the stores of a
+    // tile come before the next loads, and vmcnt completes in issue order,
+    // so each load batch waits for the stores ahead of it (one wait per two
+    // tiles; staging dG and dU through LDS instead took 7% longer). dG and
+    // dU go token-major with 2-byte stores through a buffer resource based
+    // at the tile's first row and sized to its rows inside the sequence
+    // (rows past it are dropped), and as slabs.
+    const int rows_ok = max(0, min(BM, g.T - t0));
+    const __amdgpu_buffer_rsrc_t gu_r = __builtin_amdgcn_make_buffer_rsrc(
+        a.dgu + ((int64_t)ti.b * g.T + t0) * a.ld_gu, 0, (int)(rows_ok * a.ld_gu * 2),
+        kRsrcWord3);
+    const int drop_gu = (int)(rows_ok * a.ld_gu * 2);
+    static_assert((L::TM * L::TN) % 2 == 0, "tiles pair up");
+    static_for<0, L::TM * L::TN / 2>([&](auto P) __attribute__((always_inline)) {
+      constexpr int I0 = 2 * decltype(P)::value;
+      // Coordinates (and the addresses made from them) per pair, through an
+      // opaque copy of the thread index: computed once for all tiles, they
+      // would be held across the whole epilogue.
+      const Frag<L> fr(true);
+      uint4 w4[2][4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int m = (I0 + k) / L::TN, n = (I0 + k) % L::TN;
+        const int col = n0 + fr.col(n);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w4[k][q] = make_uint4(0u, 0u, 0u, 0u);
+          if (col < N)
+            w4[k][q] = *reinterpret_cast<const uint4*>(
+                a.sa + sa_frag_offset(ti.b, t0 + fr.wm * L::TM * 32 + m * 32,
+                                      col - (fr.lane & 31), q, fr.lane, g));
         }
-        store_tile_sb<256>(kt, col, kb, v, CvtBf16{1.0f}, cok,
-                           PlainSink{part == 0 ? a.dgt : a.dut});
       }
-    } else {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int m = (I0 + k) / L::TN, n = (I0 + k) % L::TN;
+        const int col = n0 + fr.col(n);
+        const bool cok = col < N;
+        const int64_t kb = (int64_t)ti.b * g.T_pad + t0 + fr.wm * L::TM * 32 + m * 32;
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {  // dG, then dU
+          f32x16 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w[4] = {w4[k][q].x, w4[k][q].y, w4[k][q].z, w4[k][q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float fac = part == 0 ? __uint_as_float(w[e] & 0xffff0000u)  // U phi'(G)
+                                          : __uint_as_float(w[e] << 16);         // phi(G)
+              v[4 * q + e] = acc[m][n][4 * q + e] * fac;
+            }
+          }
+          store_tile_sb<256>(kt, col, kb, v, CvtBf16{1.0f}, cok,
+                             PlainSink{part == 0 ? a.dgt : a.dut});
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tr = fr.row(m, r / 4) + r % 4;  // row within the tile
+            __builtin_amdgcn_raw_buffer_store_b16(
+                bf16_rne(v[r]), gu_r,
+                cok ? (int)((tr * a.ld_gu + part * N + col) * 2) : drop_gu, 0, 0);
+          }
+        }
+      }
+    });
+  } else {
+    static_for<0, L::TM * L::TN>([&](auto I) __attribute__((always_inline)) {
+      constexpr int m = decltype(I)::value / L::TN, n = decltype(I)::value % L::TN;
+      const Frag<L> fr(true);
+      const int col = n0 + fr.col(n);
       f32x16 v;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = t0 + fr.row(m, r / 4) + r % 4;
-        v[r] = acc[m][n][r] * a.scale;
-        if (cok && t < g.T)
-          a.out_tok[((int64_t)ti.b * g.T + t) * a.ld_out + col] = bf16_rne(v[r]);
-      }
-      store_tile_sb<256>(kt, col, kb, v, CvtBf16{1.0f}, cok, PlainSink{a.out_t});
-    }
-  });
+      for (int r = 0; r < 16; ++r) v[r] = acc[m][n][r] * a.scale;
+      const int64_t kb = (int64_t)ti.b * g.T_pad + t0 + fr.wm * L::TM * 32 + m * 32;
+      store_tile_sb<256>(kt, col, kb, v, CvtBf16{1.0f}, col < N, PlainSink{a.out_t});
+      stage(m, n, v);
+    });
+    flush(a.out_tok, a.ld_out);
+  }
 }
 
 // dZ and dV under kernel names of their own, for traces.

@@ -31,6 +31,21 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return (uint32_t)f16_rne(lo) | ((uint32_t)f16_rne(hi) << 16);
 }
 
+// The backward's SiLU factor words (one per token and d_ff feature) in the
+// order a 32x32 MFMA accumulator holds them: each 32-token x 32-feature
+// block is 4 KB, laid out [q][feature][lane half][4 tokens], so the 16 bytes
+// of register group q of every lane sit side by side and one wave's access
+// is one contiguous 1 KB span. Blocks run over the features, then the
+// tokens (T_pad of them), then the batch. t32 and j32: the block's first
+// token and feature (multiples of 32); lane: the lane index (feature j32 +
+// lane % 32, tokens t32 + 8 q + 4 (lane / 32) .. + 3). Returns the word
+// offset of the lane's 16 bytes.
+__device__ __forceinline__ int64_t sa_frag_offset(int b, int t32, int j32, int q, int lane,
+                                                  const Dims& g) {
+  const int64_t blk = ((int64_t)b * (g.T_pad >> 5) + (t32 >> 5)) * (g.f >> 5) + (j32 >> 5);
+  return blk * 1024 + q * 256 + (lane & 31) * 8 + (lane >> 5) * 4;
+}
+
 // SiLU(x) = x * sigmoid(x), with the hardware reciprocal (1 ulp) in place of
 // a full division.
 __device__ __forceinline__ float silu(float x) {

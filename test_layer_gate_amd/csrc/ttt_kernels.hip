@@ -32,10 +32,10 @@ static_assert(K1_BM * K1_LDZ <= (K1_NSTA * K1_BM + K1_NSTB * K1_BN) * K1_BK,
 
 // One gate/up tile: Z (bf16, token-major, unless null) and zscale * Z
 // (fp16, or bf16 with ZT_BF16, ZT, unless null). With sa (the backward),
-// also the SiLU's derivative factors, token-major [B][T][f]: the low half
-// of each word bf16(phi(G)), the high half bf16(U phi'(G)), phi'(x) =
-// sigma(x) (1 + x (1 - sigma(x))). Returns the largest |Z| of this lane's
-// values.
+// also the SiLU's derivative factors in accumulator-fragment order
+// (sa_frag_offset; padding tokens get zero): the low half of each word
+// bf16(phi(G)), the high half bf16(U phi'(G)), phi'(x) = sigma(x) (1 + x
+// (1 - sigma(x))). Returns the largest |Z| of this lane's values.
 template <bool ZT_BF16 = false>
 __device__ __forceinline__ float gate_up_tile(const TileIdx& ti, u16* lds,
                                               const u16* __restrict__ H,
@@ -76,16 +76,18 @@ __device__ __forceinline__ float gate_up_tile(const TileIdx& ti, u16* lds,
       }
       if (sa != nullptr && j < f) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int t = t0 + fr.row(m, q) + e;
             const float gv = acc[m][n][4 * q + e], uv = acc[m][n + NG][4 * q + e];
             const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
-            if (t < g.T)
-              sa[((int64_t)ti.b * g.T + t) * f + j] =
-                  pack_bf16(gv * sig, uv * sig * (1.0f + gv * (1.0f - sig)));
+            w[e] = pack_bf16(gv * sig, uv * sig * (1.0f + gv * (1.0f - sig)));
           }
+          *reinterpret_cast<uint4*>(sa + sa_frag_offset(ti.b, t0 + fr.wm * L::TM * 32 + m * 32,
+                                                        j - (fr.lane & 31), q, fr.lane, g)) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+        }
       }
       if (ZT != nullptr) {
         if constexpr (ZT_BF16)
