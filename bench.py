@@ -28,7 +28,11 @@ upstream dO and dW_final, the forward's activations recomputed inside).
 Prints one JSON line: tokens/s for the step, the per-kernel device times
 (HIP events recorded by the library around each launch, on the stream it
 launches on), the roofline of the dominant kernel, and the CPU oracle timed
-on a bounded sample of the same workload.
+on a bounded sample of the same workload. The K timed steps run twice: the
+first pass, with no events around the launches, gives the step time and
+tokens/s; the second, the same K steps with the library's events around
+every launch, gives the per-kernel times (events between launches lengthen
+a step of short kernels, such as a decode step's).
 """
 from __future__ import annotations
 
@@ -250,12 +254,14 @@ def summarize(args):
     --write, the per-launch HBM traffic record used by the bench line)."""
     stats = _read_csv(_find(args.summarize, "kernel_stats.csv"))
     # Per-dispatch durations, to average the timed steps alone: the profiled
-    # command runs prof_warmup + prof_steps steps of the same launches.
+    # command runs prof_warmup + 2 x prof_steps steps of the same launches.
     durs = {}
     for r in _read_csv(_find(args.summarize, "kernel_trace.csv")):
         durs.setdefault(r["Kernel_Name"], []).append(
             (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    n_steps = args.prof_steps + args.prof_warmup
+    # bench.py runs warm-up steps, then the timed steps twice (without and
+    # with the library's per-launch events)
+    n_steps = 2 * args.prof_steps + args.prof_warmup
     lines = [f"# rocprofv3 kernel summary: {args.title}", "",
              f"Command: `{args.command}`", "",
              f"Kernel source sha256[:16]: `{source_hash()}`", "",
@@ -424,8 +430,8 @@ def main():
                          2 if args.schedule == "running" else 4)
     doc_len = None
     if args.variant == "decode":
-        if (args.warmup + args.steps) * cfg.chunk > T:
-            raise SystemExit("--variant decode: (warmup + steps) chunks must fit the workload")
+        if (args.warmup + 2 * args.steps) * cfg.chunk > T:
+            raise SystemExit("--variant decode: (warmup + 2 x steps) chunks must fit the workload")
         ddesc = ttt.make_desc(B, 1, d, f, cfg.conv_k, 0 if cfg.dtype == "bf16" else 1,
                               0 if cfg.dtype == "bf16" else 1, 0, 1)
         ws_bytes = ttt.decode_state_size(ddesc, cfg.chunk)
@@ -503,7 +509,6 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ttt.profile_enable(True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
@@ -512,9 +517,15 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    dev_ms = ev0.elapsed_time(ev1)
+    # the same steps again, with the library's events around every launch
+    ttt.profile_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     kstats = ttt.profile_read()
     ttt.profile_enable(False)
-    dev_ms = ev0.elapsed_time(ev1)
     ms_per_step = dev_ms / args.steps
     print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.3f} s)",
           file=sys.stderr, flush=True)
