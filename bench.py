@@ -521,9 +521,12 @@ def main():
     # the same steps again, with the library's events around every launch
     ttt.profile_enable(True)
     torch.cuda.synchronize()
+    ev0.record(stream)
     for _ in range(args.steps):
         step()
+    ev1.record(stream)
     torch.cuda.synchronize()
+    prof_ms = ev0.elapsed_time(ev1) / args.steps
     kstats = ttt.profile_read()
     ttt.profile_enable(False)
     ms_per_step = dev_ms / args.steps
@@ -567,6 +570,7 @@ def main():
         "roofline": roof,
         "kernels": {n: {k: round(v, 4) for k, v in s.items()} for n, s in kernels.items()},
         "wall_s": round(wall, 3),
+        "ms_per_step_with_launch_events": round(prof_ms, 4),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
