@@ -752,9 +752,9 @@ namespace {
 
 // The decode state of B sequences: the bf16 copy of each state the apply
 // reads, the open chunk's Z^T and X0 rows, and the chunk-end scratch (Y,
-// W_target^T, V^T) and per-token scratch (z, the apply's partial sums).
+// W_target^T, V^T) and per-token scratch (z).
 struct DecodeLayout {
-  size_t shadow = 0, zt = 0, x0c = 0, zb = 0, part = 0, y = 0, wtt = 0, vt = 0, zc = 0,
+  size_t shadow = 0, zt = 0, x0c = 0, zb = 0, y = 0, wtt = 0, vt = 0, zc = 0,
          range = 0, total = 0;
 };
 
@@ -770,7 +770,6 @@ DecodeLayout decode_layout(const Geo& g, const tttk::Dims& Dc) {
   L.zt = take(tttk::zt_elems(Dc) * 2);
   L.x0c = take(g.B * g.C * g.d * 2);
   L.zb = take(g.B * g.f * 2);
-  L.part = take(tttk::decode_apply_part_floats((int)g.B, (int)g.d) * 4);
   L.y = take(g.B * Dc.T_pad * Dc.ld_y * 2);
   L.wtt = take(g.d * Dc.ld_y * 2);
   L.vt = take(tttk::vt_elems(Dc) * 2);
@@ -887,8 +886,7 @@ ttt_status ttt_decode_step(const ttt_desc* desc, const void* h, const void* x0, 
                                          r, range, s));
   TTT_LAUNCH("decode_apply", s,
              tttk::launch_decode_apply(zb, shadow, tttk::snap_elems(Dc), (int)g.B, (int)g.d,
-                                       (int)g.f, at<float>(decode_state, L.part), o, g.act_f32,
-                                       s));
+                                       (int)g.f, o, g.act_f32, s));
   if (r == C - 1) {
     // The chunk is complete: its Z^T brought into fp16's range if needed, its
     // target (reads inside the chunk only, with the same range guards as the

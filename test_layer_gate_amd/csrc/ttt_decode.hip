@@ -133,75 +133,64 @@ __global__ __launch_bounds__(kDecThreads) void decode_zt_repair_kernel(
 }
 
 // The apply of one token per sequence against its own bf16 state copy S_b
-// (sb<256>, rows c = d_model index, columns j = d_ff index):
-// part[b][s][c] = sum over split s of the d_ff columns of z[b][j] * S_b[c][j].
-// A workgroup takes 32 rows and one split; its 4 waves share the split's
-// 16-column groups, each wave reading one 1 KB block of the slab per group
-// (32 rows x 16 columns), four groups at a time so that four loads are in
-// flight, and the waves' sums meet in LDS.
-constexpr int kApplySplit = 8;
+// (sb<256>, rows c = d_model index, columns j = d_ff index): o[b][c] = sum
+// over j of z[b][j] * S_b[c][j]. A workgroup takes 8 rows and all of d_ff;
+// its 8 waves take every 8th 64-column block, lane (r, s) reading row r's
+// columns 8s .. 8s + 7 of a block (the 8 rows' 8 columns are one 128-byte
+// piece of the slab), four blocks in flight. The lanes of a row, then the
+// waves (in LDS), add up in a fixed order.
+constexpr int kApRows = 8, kApWaves = 8, kApInFlight = 4;
 
-__global__ __launch_bounds__(kDecThreads) void decode_apply_kernel(
+template <bool OUT_F32>
+__global__ __launch_bounds__(64 * kApWaves) void decode_apply_kernel(
     const u16* __restrict__ zb, const u16* __restrict__ S, int64_t s_bstride, int d, int f,
-    float* __restrict__ part) {
-  __shared__ float red[4][32];
-  const int rg = blockIdx.x % (d / 32), rest = blockIdx.x / (d / 32);
-  const int split = rest % kApplySplit, b = rest / kApplySplit;
+    void* __restrict__ o) {
+  __shared__ float red[kApWaves][kApRows];
+  const int rg = blockIdx.x % (d / kApRows), b = blockIdx.x / (d / kApRows);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = rg * 32 + (lane & 31), half = lane >> 5;
-  const int groups = f / 16, per = (groups + kApplySplit - 1) / kApplySplit;
-  const int g0 = split * per, g1 = min(groups, g0 + per);
+  const int r = lane & 7, sg = lane >> 3;
+  const int row = rg * kApRows + r;
   const u16* Sb = S + (int64_t)b * s_bstride;
   const u16* zr = zb + (int64_t)b * f;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int q0 = g0 + w; q0 < g1; q0 += 16) {
-    float sv[4][8], zv[4][8];
+  const int nblk = f / 64;
+  float acc[kApInFlight] = {};
+  for (int q0 = w; q0 < nblk; q0 += kApWaves * kApInFlight) {
+    float sv[kApInFlight][8], zv[kApInFlight][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = min(q0 + 4 * u, g1 - 1);  // in bounds; a repeat adds nothing (below)
-      const int k = q * 16 + half * 8;
+    for (int u = 0; u < kApInFlight; ++u) {
+      const int q = min(q0 + u * kApWaves, nblk - 1);  // in bounds; a repeat adds nothing
+      const int k = q * 64 + sg * 8;
       load8_bf16<false>(Sb, sb_offset<kSnapSlab>(row, k, f), sv[u]);
       load8_bf16<false>(zr, k, zv[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (q0 + 4 * u < g1) {
+    for (int u = 0; u < kApInFlight; ++u)
+      if (q0 + u * kApWaves < nblk) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[u] = fmaf(zv[u][e], sv[u][e], acc[u]);
       }
   }
   float tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  tot += __shfl_xor(tot, 32);  // the two halves of the 16 columns
-  if (half == 0) red[w][lane] = tot;
+  tot += __shfl_xor(tot, 8);   // the 8 column groups of a row
+  tot += __shfl_xor(tot, 16);
+  tot += __shfl_xor(tot, 32);
+  if (sg == 0) red[w][r] = tot;
   __syncthreads();
-  if (threadIdx.x < 32) {
-    const float s = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] +
-                    red[3][threadIdx.x];
-    part[((int64_t)b * kApplySplit + split) * d + rg * 32 + threadIdx.x] = s;
-  }
-}
-
-// o[b][c] = sum of the splits' partial sums, in split order.
-template <bool OUT_F32>
-__global__ __launch_bounds__(kDecThreads) void decode_apply_sum_kernel(
-    const float* __restrict__ part, void* __restrict__ o, int B, int d) {
-  const int64_t i = (int64_t)blockIdx.x * kDecThreads + threadIdx.x;
-  if (i >= (int64_t)B * d) return;
-  const int64_t b = i / d, c = i % d;
-  float s = 0.f;
+  if (threadIdx.x < kApRows) {
+    float s = 0.f;
 #pragma unroll
-  for (int sp = 0; sp < kApplySplit; ++sp) s += part[(b * kApplySplit + sp) * d + c];
-  if constexpr (OUT_F32)
-    static_cast<float*>(o)[i] = s;
-  else
-    static_cast<u16*>(o)[i] = bf16_rne(s);
+    for (int v = 0; v < kApWaves; ++v) s += red[v][threadIdx.x];
+    const int64_t i = (int64_t)b * d + rg * kApRows + threadIdx.x;
+    if constexpr (OUT_F32)
+      static_cast<float*>(o)[i] = s;
+    else
+      static_cast<u16*>(o)[i] = bf16_rne(s);
+  }
 }
 
 int ceil_div_i(int64_t a, int b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
-
-int64_t decode_apply_part_floats(int B, int d) { return (int64_t)B * kApplySplit * d; }
 
 hipError_t launch_decode_gate_up(const void* h, const void* x0, bool act_f32, const void* Wg,
                                  const void* Wu, bool w_f32, int B, int d, int f, uint16_t* zb,
@@ -236,16 +225,12 @@ hipError_t launch_decode_zt_repair(const float* zc, uint16_t* zt, int B, int f, 
 }
 
 hipError_t launch_decode_apply(const uint16_t* zb, const uint16_t* S, int64_t s_bstride, int B,
-                               int d, int f, float* part, void* o, bool out_f32, hipStream_t s) {
-  decode_apply_kernel<<<B * kApplySplit * (d / 32), kDecThreads, 0, s>>>(zb, S, s_bstride, d, f,
-                                                                         part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int grid = ceil_div_i((int64_t)B * d, kDecThreads);
+                               int d, int f, void* o, bool out_f32, hipStream_t s) {
+  const int grid = B * (d / kApRows);
   if (out_f32)
-    decode_apply_sum_kernel<true><<<grid, kDecThreads, 0, s>>>(part, o, B, d);
+    decode_apply_kernel<true><<<grid, 64 * kApWaves, 0, s>>>(zb, S, s_bstride, d, f, o);
   else
-    decode_apply_sum_kernel<false><<<grid, kDecThreads, 0, s>>>(part, o, B, d);
+    decode_apply_kernel<false><<<grid, 64 * kApWaves, 0, s>>>(zb, S, s_bstride, d, f, o);
   return hipGetLastError();
 }
 

@@ -239,11 +239,9 @@ hipError_t launch_decode_zt_repair(const float* zc, uint16_t* zt, int B, int f, 
                                   int64_t zt_bstride, int zt_cols, const uint32_t* zrange,
                                   hipStream_t s);
 // Decode step, apply: o[b] = zb[b] S_b^T (S_b the bf16 state of sequence b,
-// sb<256> d x f, s_bstride elements apart), through part
-// (decode_apply_part_floats(B, d) floats); o is [B][d], bf16 or fp32.
-int64_t decode_apply_part_floats(int B, int d);
+// sb<256> d x f, s_bstride elements apart); o is [B][d], bf16 or fp32.
 hipError_t launch_decode_apply(const uint16_t* zb, const uint16_t* S, int64_t s_bstride, int B,
-                               int d, int f, float* part, void* o, bool out_f32, hipStream_t s);
+                               int d, int f, void* o, bool out_f32, hipStream_t s);
 
 // O[b][t] = Z[b][t] W_i^T, where W_i is the bf16 state (sb<256>(d x f)) at
 // snap + b * snap_bstride + i * snap_cstride. Without tiles: for tokens t in

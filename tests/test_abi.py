@@ -450,7 +450,7 @@ def test_decode_state_size(L):
     expect = (B * d * f * 2            # bf16 copies of the states (d rows: whole 256-row slabs)
               + B * f * C * 2          # the open chunk's Z^T (f rows: whole slabs)
               + B * C * d * 2          # the open chunk's X0 rows
-              + B * f * 2 + B * 8 * d * 4      # z and the apply's partial sums (8 splits)
+              + B * f * 2                      # z (bf16, the apply's operand)
               + B * C * ld_y * 2 + d * ld_y * 2 + B * d * C * 2   # Y, W_target^T, V^T
               + B * C * f * 4          # the open chunk's fp32 Z rows (fp16 range repair)
               + 4 * 256 * 4)           # the range buffer
