@@ -540,7 +540,9 @@ def main():
     tflops = flops / (ms_per_step / 1e3) / 1e12
     kernels = {n: {"launches_per_step": c / args.steps, "avg_ms": ms / c}
                for n, (c, ms) in kstats.items()}
-    dom = max(kstats, key=lambda n: kstats[n][1])
+    # the longest-running kernel that has an algorithmic work figure
+    dom = max((n for n in kstats if kernel_work(n, cfg, T_pad)[0] is not None),
+              key=lambda n: kstats[n][1])
     bound, work = kernel_work(dom, cfg, T_pad)
     launches_per_step = kstats[dom][0] / args.steps
     work = work / launches_per_step          # per launch

@@ -48,3 +48,35 @@ def test_traffic_record_is_tied_to_the_source(tmp_path, monkeypatch):
     p.write_text(json.dumps(rec))
     assert bench.measured_traffic("gate_up", "w") is None
 
+
+
+def test_backward_flops_match_its_kernels():
+    """The backward's kernels add up to the contractions it executes:
+    22*B*T*d*f + 6*B*T*d^2 (the recomputed gate/up and target, the state
+    and state-gradient scans, dZ over K = 2d, dV, dY, dW_target, dWg + dWu
+    and dH)."""
+    cfg = synth.CONFIGS["qwen3_4b_64k"]
+    total = 0.0
+    for k in ("bwd_gate_up", "bwd_target", "bwd_states", "bwd_state_grads", "bwd_dz", "bwd_dv",
+              "bwd_dy", "bwd_dw_target", "bwd_dw_gate_up", "bwd_dh"):
+        bound, work = bench.kernel_work(k, cfg, cfg.seq_len)
+        assert bound == "mfma", k
+        total += work
+    assert total == bench.backward_flops(cfg)
+
+
+def test_traffic_of_a_shared_kernel_name_is_not_used(tmp_path, monkeypatch):
+    """Timing names whose kernels share one trace name (the backward's
+    update-kernel contractions) get no traffic figure: the counters cannot
+    tell their launches apart."""
+    rec = {"kernel_source_sha256_16": bench.source_hash(),
+           "kernels": {"w/backward": {"bwd_states": {"hbm_bytes_per_launch": 5.0,
+                                                     "shared_name": True},
+                                      "bwd_dz": {"hbm_bytes_per_launch": 7.0,
+                                                 "shared_name": False}}}}
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
+    key = bench.traffic_key("w", "backward")
+    assert bench.measured_traffic("bwd_states", key) is None
+    assert bench.measured_traffic("bwd_dz", key) == 7.0
