@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule prefix|running] [--no-cpu-baseline]
                     [--variant plain|packed|clipped|packed_clipped|continue|decode|
-                               backward]
+                               backward|train]
     python bench.py --summarize DIR [--fetch DIR2 --write DIR3]
                     --summary-out FILE.md --command "..."
     python bench.py --vendor-gemm
@@ -24,7 +24,9 @@ clipped (ttt_layer_forward_clipped, limit --clip), packed_clipped
 look-ahead rows), decode (ttt_decode_step token by token with chunk-local
 padding; one step is one chunk of C tokens, the chunk's update included) or
 backward (ttt_layer_backward: every gradient of the prefill for a random
-upstream dO and dW_final, the forward's activations recomputed inside).
+upstream dO and dW_final, the forward's activations recomputed inside) or
+train (a training step: ttt_layer_forward_train, whose workspace keeps the
+activations, then ttt_layer_backward_saved on it).
 Prints one JSON line: tokens/s for the step, the per-kernel device times
 (HIP events recorded by the library around each launch, on the stream it
 launches on), the roofline of the dominant kernel, and the CPU oracle timed
@@ -72,7 +74,8 @@ KERNEL_NAMES = {"gate_up": "gate_up_kernel", "target": "target_kernel",
                 "bwd_dw_target": "update_kernel", "bwd_dw_gate_up": "update_kernel",
                 "bwd_conv": "conv_bwd", "bwd_rows": "rows_bf16_kernel",
                 "bwd_to_slab": "to_slab_kernel", "bwd_transpose_grads": "slab_transpose_kernel",
-                "bwd_transpose_w": "transpose_bf16_kernel", "bwd_sum": "sum_parts_kernel"}
+                "bwd_transpose_w": "transpose_bf16_kernel", "bwd_sum": "sum_parts_kernel",
+                "bwd_states_transpose": "slab_transpose_kernel"}
 
 
 def backward_flops(cfg):
@@ -83,6 +86,14 @@ def backward_flops(cfg):
     (2 B T d^2 each), dWg and dWu (4 B T d f) and dH (4 B T d f)."""
     B, T, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
     return 22.0 * B * T * d * f + 6.0 * B * T * d * d
+
+
+def train_flops(cfg):
+    """A training step's contraction FLOPs: the prefill (8 B T d f + 2 B T
+    d^2) and the saved backward, which skips the gate/up recompute (4 B T d
+    f) and the state scan (2 B T d f)."""
+    B, T, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
+    return synth.algorithmic_flops(cfg) + backward_flops(cfg) - 6.0 * B * T * d * f
 
 
 def kernel_work(name, cfg, T_pad):
@@ -104,6 +115,9 @@ def kernel_work(name, cfg, T_pad):
         return "mfma", 2.0 * B * T * d * f
     if name in ("bwd_target", "bwd_dy", "bwd_dw_target"):
         return "mfma", 2.0 * B * T * d * d
+    if name in ("bwd_states_transpose", "bwd_transpose_grads"):
+        # every chunk's bf16 d x f matrix read and written once
+        return "hbm", 2.0 * 2.0 * B * -(-T // cfg.chunk) * d * f
     if name == "conv":
         return "hbm", 2.0 * B * T * d + 2.0 * B * T_pad * d + 2.0 * K * d
     if name == "transpose_w_target":
@@ -167,8 +181,11 @@ def cpu_baseline(cfg, x, budget_s=15.0, variant="plain", clip=None, doc_len=None
     def run(j):
         n = j * C
         t0 = time.perf_counter()
-        if variant == "backward":
+        if variant in ("backward", "train"):
             B, T, d = x["H"].shape
+            if variant == "train":   # the step's forward, then its backward
+                ora.ttt_prefill(x["H"][:1, :n], x["X0"][:1, :n], x["Wg"], x["Wu"],
+                                x["W_down0"], x["taps"], x["W_target"], cfg.eta, C)
             dO = np.random.default_rng(1).standard_normal((1, n, d))
             dWf = np.random.default_rng(2).standard_normal((1, d, x["Wg"].shape[0]))
             ora.ttt_prefill_backward(x["H"][:1, :n], x["X0"][:1, :n], x["Wg"], x["Wu"],
@@ -317,7 +334,8 @@ def summarize(args):
         rec.pop("write_factor", None)
         rec["kernels"][key] = {}
         names_in_step = [n for n in KERNEL_NAMES
-                         if n.startswith("bwd_") == (args.variant == "backward")]
+                         if args.variant == "train" or
+                         n.startswith("bwd_") == (args.variant == "backward")]
         for name, v in sorted(per.items()):
             fe = sum(v.get("FETCH_SIZE", [0])) / max(len(v.get("FETCH_SIZE", [])), 1)
             wr = sum(v.get("WRITE_SIZE", [0])) / max(len(v.get("WRITE_SIZE", [])), 1)
@@ -379,7 +397,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", default="plain",
                     choices=["plain", "packed", "clipped", "packed_clipped", "continue",
-                             "decode", "backward"])
+                             "decode", "backward", "train"])
     ap.add_argument("--docs", type=int, default=32, help="packed variant: equal documents")
     ap.add_argument("--clip", type=float, default=1e-3, help="clipped variant: norm limit")
     ap.add_argument("--summarize", help="rocprofv3 --kernel-trace --stats output directory")
@@ -454,8 +472,11 @@ def main():
         # the segment continues a document: its state is fp32 and K - 1 rows follow it
         W_state = t["W_down0"].float().expand(B, d, f).contiguous()
         X0_next = t["X0"][:, :cfg.conv_k - 1].contiguous()
-    elif args.variant == "backward":
-        ws_bytes = ttt.backward_workspace_size(desc, cfg.chunk)
+    elif args.variant in ("backward", "train"):
+        ws_bytes = (ttt.backward_workspace_size(desc, cfg.chunk) if args.variant == "backward"
+                    else ttt.backward_saved_workspace_size(desc, cfg.chunk))
+        saved = (torch.empty(ttt.train_workspace_size(desc, cfg.chunk), dtype=torch.uint8,
+                             device=dev) if args.variant == "train" else None)
         gen = torch.Generator(device=dev).manual_seed(5)
         dO = torch.randn(t["H"].shape, generator=gen, device=dev).to(tdt)
         dWf_up = torch.randn((B, d, f), generator=gen, device=dev)
@@ -482,10 +503,14 @@ def main():
                                      t["W_target"], cfg.eta, cfg.chunk, starts,
                                      schedule=args.schedule, clip=pclip, out=O, W_down_final=Wf,
                                      workspace=ws)
-        elif args.variant == "backward":
+        elif args.variant in ("backward", "train"):
+            if saved is not None:
+                ttt.layer_forward_train(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"],
+                                        t["taps"], t["W_target"], cfg.eta, cfg.chunk, out=O,
+                                        W_down_final=Wf, workspace=saved)
             ttt.layer_backward(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
                                t["W_target"], cfg.eta, cfg.chunk, dO, dW_final=dWf_up,
-                               out=grads, workspace=ws)
+                               saved=saved, out=grads, workspace=ws)
         elif args.variant == "continue":
             ttt.layer_forward_continue(t["H"], t["X0"], X0_next, t["Wg"], t["Wu"], W_state,
                                        t["taps"], t["W_target"], cfg.eta, cfg.chunk,
@@ -534,8 +559,12 @@ def main():
           file=sys.stderr, flush=True)
 
     tokens = B * (cfg.chunk if args.variant == "decode" else T)
-    flops = (backward_flops(cfg) if args.variant == "backward"
-             else synth.algorithmic_flops(cfg) * tokens / (B * T))
+    if args.variant == "backward":
+        flops = backward_flops(cfg)
+    elif args.variant == "train":
+        flops = train_flops(cfg)
+    else:
+        flops = synth.algorithmic_flops(cfg) * tokens / (B * T)
     value = tokens / (ms_per_step / 1e3)
     tflops = flops / (ms_per_step / 1e3) / 1e12
     kernels = {n: {"launches_per_step": c / args.steps, "avg_ms": ms / c}

@@ -366,6 +366,41 @@ ttt_status ttt_layer_backward(const ttt_desc* desc,
                               float* dW_down0, float* dtaps, float* dW_target,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Training: the prefill that keeps what its backward reads, and that
+ * backward. A training step recomputes nothing: ttt_layer_forward_train is
+ * ttt_layer_forward (prefix schedule only: TTT_ERR_UNSUPPORTED with
+ * TTT_FLAG_SCHED_RUNNING) whose workspace of ttt_train_workspace_size()
+ * bytes, once the call has run, holds the chunks' states W^(i) (bf16), Z,
+ * Z^T and the SiLU factors; ttt_layer_backward_saved takes that workspace
+ * as `saved` (saved_bytes >= ttt_train_workspace_size()) with the same
+ * descriptor, chunk and inputs, and returns what ttt_layer_backward
+ * returns, without the gate/up recompute and the state scan (W^(i) comes
+ * from the forward's snapshots: the forward's update precision, so its
+ * gradients differ from ttt_layer_backward's in the last bf16 bits). The
+ * caller keeps `saved` unchanged between the two calls; the backward only
+ * reads it. Its own workspace is ttt_backward_saved_workspace_size() bytes.
+ * Other conventions as ttt_layer_forward and ttt_layer_backward. */
+ttt_status ttt_train_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes);
+ttt_status ttt_layer_forward_train(const ttt_desc* desc,
+                                   const void* H, const void* X0,
+                                   const void* Wg, const void* Wu,
+                                   const void* W_down0, const void* conv_taps,
+                                   const void* W_target, float eta, int32_t chunk,
+                                   void* O, float* W_down_final,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+ttt_status ttt_backward_saved_workspace_size(const ttt_desc* desc, int32_t chunk,
+                                             size_t* bytes);
+ttt_status ttt_layer_backward_saved(const ttt_desc* desc,
+                                    const void* H, const void* X0,
+                                    const void* Wg, const void* Wu,
+                                    const void* W_down0, const void* conv_taps,
+                                    const void* W_target, float eta, int32_t chunk,
+                                    const void* saved, size_t saved_bytes,
+                                    const void* dO, const float* dW_final,
+                                    float* dH, float* dX0, float* dWg, float* dWu,
+                                    float* dW_down0, float* dtaps, float* dW_target,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Step entry points: one step of the layer each, for per-step checks.
  * ttt_gated_activation writes Z [B, T, d_ff] in bf16.
  * ttt_lm_target writes V [B, T, d_model] in bf16 (unscaled, eta not applied).

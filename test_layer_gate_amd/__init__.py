@@ -13,6 +13,7 @@ built, or a call fails, an exception is raised.
 from ._binding import (  # noqa: F401
     LIB_PATH,
     TTTError,
+    backward_saved_workspace_size,
     backward_workspace_size,
     clipped_workspace_size,
     continue_workspace_size,
@@ -25,6 +26,7 @@ from ._binding import (  # noqa: F401
     layer_forward,
     layer_forward_continue,
     layer_forward_packed,
+    layer_forward_train,
     lib,
     lm_target,
     make_desc,
@@ -32,6 +34,7 @@ from ._binding import (  # noqa: F401
     packed_workspace_size,
     profile_enable,
     profile_read,
+    train_workspace_size,
     workspace_size,
 )
 
@@ -39,7 +42,8 @@ __all__ = ["layer_forward", "layer_forward_packed", "packed_workspace_size", "pa
            "layer_forward_continue", "continue_workspace_size", "clipped_workspace_size",
            "decode_state_size", "decode_begin", "decode_step",
            "gated_activation", "lm_target", "workspace_size",
-           "layer_backward", "backward_workspace_size",
+           "layer_backward", "backward_workspace_size", "layer_forward_train",
+           "train_workspace_size", "backward_saved_workspace_size",
            "copy_calibration",
            "make_desc", "profile_enable", "profile_read", "TTTError", "lib",
            "LIB_PATH"]

@@ -101,6 +101,13 @@ def lib() -> ctypes.CDLL:
     L.ttt_layer_forward_noalloc.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                             ctypes.c_int32, _P, _P, _P]
     L.ttt_backward_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
+    L.ttt_train_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
+    L.ttt_backward_saved_workspace_size.argtypes = [DP, ctypes.c_int32, ctypes.POINTER(_S)]
+    L.ttt_layer_forward_train.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                          ctypes.c_int32, _P, _P, _P, _S, _P]
+    L.ttt_layer_backward_saved.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                           ctypes.c_int32, _P, _S, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _S, _P]
     L.ttt_layer_backward.argtypes = [DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                      ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _S, _P]
@@ -115,6 +122,8 @@ def lib() -> ctypes.CDLL:
                "ttt_continue_workspace_size", "ttt_layer_forward_continue",
                "ttt_decode_state_size", "ttt_decode_begin", "ttt_decode_step",
                "ttt_backward_workspace_size", "ttt_layer_backward",
+               "ttt_train_workspace_size", "ttt_layer_forward_train",
+               "ttt_backward_saved_workspace_size", "ttt_layer_backward_saved",
                "ttt_gated_activation", "ttt_lm_target", "ttt_profile_enable"):
         getattr(L, fn).restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int32]
@@ -264,13 +273,52 @@ def backward_workspace_size(desc: Desc, chunk: int) -> int:
     return n.value
 
 
+def train_workspace_size(desc: Desc, chunk: int) -> int:
+    n = _S(0)
+    _check(lib().ttt_train_workspace_size(ctypes.byref(desc), int(chunk), ctypes.byref(n)))
+    return n.value
+
+
+def backward_saved_workspace_size(desc: Desc, chunk: int) -> int:
+    n = _S(0)
+    _check(lib().ttt_backward_saved_workspace_size(ctypes.byref(desc), int(chunk),
+                                                   ctypes.byref(n)))
+    return n.value
+
+
+def layer_forward_train(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, *,
+                        pad="sequence", out=None, W_down_final=None, workspace=None,
+                        stream=None):
+    """ttt_layer_forward_train: the prefill (prefix schedule) that keeps in its
+    workspace what the backward reads. Returns O, W_final and that workspace,
+    to pass unchanged to layer_backward(..., saved=...)."""
+    desc = _layer_desc(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, None, pad)
+    B, T, d = H.shape
+    f = Wg.shape[0]
+    ws_bytes = train_workspace_size(desc, int(chunk))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
+    O = torch.empty_like(H) if out is None else out
+    Wf = (torch.empty((B, d, f), dtype=torch.float32, device=H.device)
+          if W_down_final is None else W_down_final)
+    _require_cuda(O, Wf, workspace)
+    _check(lib().ttt_layer_forward_train(
+        ctypes.byref(desc), _ptr(H), _ptr(X0), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
+        _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk), _ptr(O),
+        _ptr(Wf), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return O, Wf, workspace
+
+
 def layer_backward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, dO, *,
-                   dW_final=None, pad="sequence", out=None, workspace=None, stream=None):
+                   dW_final=None, pad="sequence", saved=None, out=None, workspace=None,
+                   stream=None):
     """The prefill's gradients (ttt_layer_backward) for the upstream
     gradients dO [B, T, d] (H's dtype) and dW_final [B, d, f] fp32 (None:
     zero). Returns a dict of fp32 tensors: dH, dX0 [B, T, d]; dWg, dWu
     [f, d]; dW_down0 [d, f] (shared W_down0) or [B, d, f]; dtaps [K, d];
-    dW_target [d, d]. out: such a dict to write into instead of new tensors."""
+    dW_target [d, d]. out: such a dict to write into instead of new tensors.
+    saved: the workspace layer_forward_train returned for the same arguments
+    (ttt_layer_backward_saved: no recompute of gate/up and the states)."""
     desc = _layer_desc(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, None, pad)
     B, T, d = H.shape
     f, K = Wg.shape[0], conv_taps.shape[0]
@@ -283,7 +331,11 @@ def layer_backward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, dO, 
             raise ValueError("dW_final must be [B, d_model, d_ff] float32")
         if not dW_final.is_contiguous():
             raise ValueError("dW_final must be contiguous")
-    ws_bytes = backward_workspace_size(desc, int(chunk))
+    if saved is not None:
+        _require_cuda(saved)
+        ws_bytes = backward_saved_workspace_size(desc, int(chunk))
+    else:
+        ws_bytes = backward_workspace_size(desc, int(chunk))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=H.device)
     _require_cuda(workspace)
@@ -297,13 +349,16 @@ def layer_backward(H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, chunk, dO, 
             if k not in g or tuple(g[k].shape) != v or g[k].dtype != torch.float32:
                 raise ValueError(f"out[{k!r}] must be a float32 tensor of shape {v}")
             _require_cuda(g[k])
-    _check(lib().ttt_layer_backward(
-        ctypes.byref(desc), _ptr(H), _ptr(X0), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
-        _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk), _ptr(dO),
-        None if dW_final is None else _ptr(dW_final),
-        _ptr(g["dH"]), _ptr(g["dX0"]), _ptr(g["dWg"]), _ptr(g["dWu"]), _ptr(g["dW_down0"]),
-        _ptr(g["dtaps"]), _ptr(g["dW_target"]), _ptr(workspace), workspace.numel(),
-        _stream(stream)))
+    head = [ctypes.byref(desc), _ptr(H), _ptr(X0), _ptr(Wg), _ptr(Wu), _ptr(W_down0),
+            _ptr(conv_taps), _ptr(W_target), ctypes.c_float(float(eta)), int(chunk)]
+    tail = [_ptr(dO), None if dW_final is None else _ptr(dW_final),
+            _ptr(g["dH"]), _ptr(g["dX0"]), _ptr(g["dWg"]), _ptr(g["dWu"]), _ptr(g["dW_down0"]),
+            _ptr(g["dtaps"]), _ptr(g["dW_target"]), _ptr(workspace), workspace.numel(),
+            _stream(stream)]
+    if saved is None:
+        _check(lib().ttt_layer_backward(*head, *tail))
+    else:
+        _check(lib().ttt_layer_backward_saved(*head, _ptr(saved), saved.numel(), *tail))
     return g
 
 

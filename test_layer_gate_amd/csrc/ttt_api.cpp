@@ -86,13 +86,15 @@ struct Geo {
   std::vector<tttk::ChunkSpan> spans;      // packed documents only: each chunk's tokens
   float clip = 0.0f;                       // > 0: update-norm clipping limit
   bool resume = false;                     // continuation: fp32 state in place, look-ahead rows
+  bool train = false;                      // training forward: keeps what the backward reads
   size_t act_bytes() const { return act_f32 ? 4 : 2; }
   size_t w_bytes() const { return w_f32 ? 4 : 2; }
 };
 
 struct Layout {
   size_t y = 0, wtt = 0, z = 0, zt = 0, vt = 0, snap = 0, hb = 0, x0b = 0, wgp = 0, wup = 0,
-         blk = 0, vrow = 0, gram = 0, partial = 0, scale = 0, x0n = 0, range = 0;
+         blk = 0, vrow = 0, gram = 0, partial = 0, scale = 0, x0n = 0, range = 0, ztb = 0,
+         sa = 0;
   size_t total = 0;
 };
 
@@ -131,6 +133,12 @@ Layout forward_layout(const Geo& g) {
     L.gram = take(g.B * g.nchunks * tttk::clip_gram_floats((int)g.C) * 4);
     L.partial = take(g.B * g.nchunks * tttk::clip_pairs((int)g.C) * 4);
     L.scale = take(g.B * g.nchunks * 4);
+  }
+  if (g.train) {
+    // kept for the backward (with Z and the snapshots above): Z^T in bf16
+    // and the SiLU factors
+    L.ztb = take(tttk::zt_elems(D) * 2);
+    L.sa = take(g.B * g.T_pad * g.f * 4);
   }
   L.total = off;
   return L;
@@ -534,7 +542,12 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
              tttk::launch_conv_repair(X0b, X0nb, n_next, conv_taps, g.w_f32, Y, D, (int)g.K,
                                       (int)g.C, g.pad_chunk, blocks, range_y, s));
   uint32_t* range_z = range + tttk::kRangeZ * tttk::kRangeSlots;
-  TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, range_z, s));
+  if (g.train)
+    TTT_LAUNCH("gate_up", s,
+               tttk::launch_gate_up_train(Hb, Wgp, Wup, Z, ZT, at<uint16_t>(workspace, L.ztb),
+                                          at<uint32_t>(workspace, L.sa), D, range_z, s));
+  else
+    TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, range_z, s));
   TTT_LAUNCH("gate_up_repair", s, tttk::launch_gate_up_repair(Hb, Wgp, Wup, ZT, D, range_z, s));
   const bool clip = g.clip > 0.0f && eta != 0.0f;
   uint16_t* Vrow = clip ? at<uint16_t>(workspace, L.vrow) : nullptr;
@@ -939,7 +952,9 @@ struct BwdLayout {
   int64_t ld_gu = 0, ld_ov = 0;
 };
 
-BwdLayout backward_layout(const Geo& g) {
+// With `saved` (the training forward's workspace holds Z, Z^T, the SiLU
+// factors and the states) the recompute's buffers are not needed.
+BwdLayout backward_layout(const Geo& g, bool saved = false) {
   BwdLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -953,8 +968,10 @@ BwdLayout backward_layout(const Geo& g) {
   L.ld_gu = tttk::pad_ld(2 * g.f);
   L.ld_ov = tttk::pad_ld(2 * g.d);
   L.range = take(tttk::kRangeWords * 4);
-  L.wgp = take(tttk::wpack_elems(D) * 2);
-  L.wup = take(tttk::wpack_elems(D) * 2);
+  if (!saved) {
+    L.wgp = take(tttk::wpack_elems(D) * 2);
+    L.wup = take(tttk::wpack_elems(D) * 2);
+  }
   if (g.act_f32) {
     L.hb = take(BT * g.d * 2);
     L.x0b = take(BT * g.d * 2);
@@ -963,9 +980,11 @@ BwdLayout backward_layout(const Geo& g) {
   L.y = take(BTp * D.ld_y * 2);
   L.wtt = take(g.d * D.ld_y * 2);
   L.yt = take(tttk::sb_elems<256>(g.d, BTp) * 2);
-  L.z = take(BT * D.ld_z * 2);
-  L.zt = take(tttk::zt_elems(D) * 2);
-  L.sa = take(BTp * g.f * 4);
+  if (!saved) {
+    L.z = take(BT * D.ld_z * 2);
+    L.zt = take(tttk::zt_elems(D) * 2);
+    L.sa = take(BTp * g.f * 4);
+  }
   L.vt = take(tttk::vt_elems(D) * 2);
   L.dot = take(tttk::vt_elems(D) * 2);
   L.ht = take(tttk::sb_elems<256>(g.d, BTp) * 2);
@@ -985,29 +1004,30 @@ BwdLayout backward_layout(const Geo& g) {
   return L;
 }
 
-}  // namespace
-
-extern "C" {
-
-ttt_status ttt_backward_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes) {
-  Geo g;
-  TTT_TRY(check_desc(desc, &g));
-  TTT_TRY(check_chunk(chunk, &g));
-  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = backward_layout(g).total;
+// The training forward and its backward: the descriptor and chunk checks of
+// the prefill; the prefix schedule only (its per-chunk snapshots are what
+// the backward reads).
+ttt_status check_train_desc(const ttt_desc* desc, int32_t chunk, Geo* g) {
+  TTT_TRY(check_desc(desc, g));
+  TTT_TRY(check_chunk(chunk, g));
+  if (g->running)
+    return fail(TTT_ERR_UNSUPPORTED,
+                "the training forward keeps every chunk's state: prefix schedule only");
+  g->train = true;
   return TTT_OK;
 }
 
-ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X0,
-                              const void* Wg, const void* Wu, const void* W_down0,
-                              const void* conv_taps, const void* W_target, float eta,
-                              int32_t chunk, const void* dO, const float* dW_final, float* dH,
-                              float* dX0, float* dWg, float* dWu, float* dW_down0, float* dtaps,
-                              float* dW_target, void* workspace, size_t workspace_bytes,
-                              void* stream) {
-  Geo g;
-  TTT_TRY(check_desc(desc, &g));
-  TTT_TRY(check_chunk(chunk, &g));
+// The backward of a prefill (see ttt_layer_backward). With `saved` (the
+// workspace of ttt_layer_forward_train on the same arguments, g.train set),
+// Z, Z^T, the SiLU factors and the states W_i come from it: the gate/up
+// recompute and the state scan are skipped, and W_i^T is the transpose of
+// the forward's bf16 snapshots.
+ttt_status backward_impl(const Geo& g, const void* H, const void* X0, const void* Wg,
+                         const void* Wu, const void* W_down0, const void* conv_taps,
+                         const void* W_target, float eta, const void* saved, size_t saved_bytes,
+                         const void* dO, const float* dW_final, float* dH, float* dX0,
+                         float* dWg, float* dWu, float* dW_down0, float* dtaps, float* dW_target,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
   const char* names[] = {"H", "X0", "Wg", "Wu", "W_down0", "conv_taps", "W_target", "dO",
                          "dH", "dX0", "dWg", "dWu", "dW_down0", "dtaps", "dW_target"};
@@ -1016,10 +1036,20 @@ ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X
   for (int i = 0; i < 15; ++i) TTT_TRY(check_ptr(ptrs[i], names[i]));
   if (dW_final != nullptr) TTT_TRY(check_ptr(dW_final, "dW_final"));
   TTT_TRY(check_ptr(workspace, "workspace", 256));
+  const bool sv = saved != nullptr;
+  Layout F;
+  if (sv) {
+    TTT_TRY(check_ptr(saved, "saved", 256));
+    F = forward_layout(g);
+    if (saved_bytes < F.total)
+      return fail(TTT_ERR_WORKSPACE, "saved has " + std::to_string(saved_bytes) +
+                                         " bytes, the training forward's workspace is " +
+                                         std::to_string(F.total));
+  }
   if (g.w0_stride != 0 && g.w0_stride != g.d * g.f)
     return fail(TTT_ERR_UNSUPPORTED,
                 "the backward needs per-sequence W_down0 at stride d_model * d_ff (or shared)");
-  const BwdLayout L = backward_layout(g);
+  const BwdLayout L = backward_layout(g, sv);
   if (workspace_bytes < L.total)
     return fail(TTT_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
                                        " bytes, needs " + std::to_string(L.total));
@@ -1035,6 +1065,7 @@ ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X
                                range_of("W_target", W_target, g.d * g.d * wb),
                                range_of("dO", dO, g.B * g.T * g.d * ab)};
   if (dW_final != nullptr) inputs.push_back(range_of("dW_final", dW_final, g.B * df * 4));
+  if (sv) inputs.push_back(range_of("saved", saved, F.total));
   const std::vector<Range> outputs = {
       range_of("dH", dH, g.B * g.T * g.d * 4), range_of("dX0", dX0, g.B * g.T * g.d * 4),
       range_of("dWg", dWg, df * 4), range_of("dWu", dWu, df * 4),
@@ -1067,11 +1098,15 @@ ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X
   TTT_LAUNCH("bwd_rows", s,
              tttk::launch_rows_bf16(dO, g.act_f32, g.d, DOV, L.ld_ov, g.B * g.T, d, s));
 
-  // The forward's activations again (bf16 for the backward's contractions).
-  uint16_t* Wgp = at<uint16_t>(workspace, L.wgp);
-  uint16_t* Wup = at<uint16_t>(workspace, L.wup);
-  TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wg, g.w_f32, Wgp, D, s));
-  TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wu, g.w_f32, Wup, D, s));
+  // The forward's activations again (bf16 for the backward's contractions);
+  // Z, Z^T and the SiLU factors from the training forward when it saved them.
+  auto saved_at = [&](size_t off) { return reinterpret_cast<const char*>(saved) + off; };
+  uint16_t* Wgp = sv ? nullptr : at<uint16_t>(workspace, L.wgp);
+  uint16_t* Wup = sv ? nullptr : at<uint16_t>(workspace, L.wup);
+  if (!sv) {
+    TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wg, g.w_f32, Wgp, D, s));
+    TTT_LAUNCH("pack_weights", s, tttk::launch_pack_weight(Wu, g.w_f32, Wup, D, s));
+  }
   uint16_t* Y = at<uint16_t>(workspace, L.y);
   uint16_t* WtT = at<uint16_t>(workspace, L.wtt);
   uint16_t* YT = at<uint16_t>(workspace, L.yt);
@@ -1084,10 +1119,22 @@ ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X
   TTT_LAUNCH("conv_repair", s,
              tttk::launch_conv_repair(X0b, nullptr, 0, conv_taps, g.w_f32, Y, D, (int)g.K, C,
                                       g.pad_chunk, nullptr, range_y, s));
-  uint16_t* Z = at<uint16_t>(workspace, L.z);
-  uint16_t* ZT = at<uint16_t>(workspace, L.zt);
-  uint32_t* SA = at<uint32_t>(workspace, L.sa);
-  TTT_LAUNCH("bwd_gate_up", s, tttk::launch_gate_up_bwd(Hb, Wgp, Wup, Z, ZT, SA, D, s));
+  const uint16_t* Z;
+  const uint16_t* ZT;
+  const uint32_t* SA;
+  if (sv) {
+    Z = reinterpret_cast<const uint16_t*>(saved_at(F.z));
+    ZT = reinterpret_cast<const uint16_t*>(saved_at(F.ztb));
+    SA = reinterpret_cast<const uint32_t*>(saved_at(F.sa));
+  } else {
+    uint16_t* z = at<uint16_t>(workspace, L.z);
+    uint16_t* zt = at<uint16_t>(workspace, L.zt);
+    uint32_t* sa = at<uint32_t>(workspace, L.sa);
+    TTT_LAUNCH("bwd_gate_up", s, tttk::launch_gate_up_bwd(Hb, Wgp, Wup, z, zt, sa, D, s));
+    Z = z;
+    ZT = zt;
+    SA = sa;
+  }
   uint16_t* VT = at<uint16_t>(workspace, L.vt);
   TTT_LAUNCH("bwd_target", s,
              tttk::launch_target_bwd(Y, WtT, VT, DOV + g.d, L.ld_ov, eta, D, range, s));
@@ -1103,9 +1150,16 @@ ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X
   // with its operands swapped.
   uint16_t* WGT = at<uint16_t>(workspace, L.wgt);
   const tttk::Dims Dsw = tttk::make_dims(B, T, f, d);
-  TTT_LAUNCH("bwd_states", s,
-             tttk::launch_contract_bf16(VT, ZT, Dsw, W_down0, g.w_f32, true, g.w0_stride, g.f,
-                                        WGT, g.nchunks * snap_f2d, 2 * d, nullptr, false, C, s));
+  if (sv)
+    // the training forward's snapshots W_i (sb<256>(d x f), bf16), transposed
+    TTT_LAUNCH("bwd_states_transpose", s,
+               tttk::launch_slab_transpose(reinterpret_cast<const uint16_t*>(saved_at(F.snap)),
+                                           snap_df, WGT, snap_f2d, 2 * g.d, 0, B * nch, d, f, s));
+  else
+    TTT_LAUNCH("bwd_states", s,
+               tttk::launch_contract_bf16(VT, ZT, Dsw, W_down0, g.w_f32, true, g.w0_stride, g.f,
+                                          WGT, g.nchunks * snap_f2d, 2 * d, nullptr, false, C,
+                                          s));
   // The state gradients Gbar_{i+1} = dW_final + sum_{j > i} dO_j^T Z_j of
   // every chunk, backwards over the tokens (the scan ends at dW_down0), and
   // their transposes into the last d columns of [W_i^T | Gbar_{i+1}^T].
@@ -1166,6 +1220,78 @@ ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X
   TTT_LAUNCH("bwd_dh", s,
              tttk::launch_nt_gemm(DGU, L.ld_gu, WGUT, L.ld_gu, d, 2 * f, dH, g.d, D, s));
   return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttt_status ttt_backward_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = backward_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_backward(const ttt_desc* desc, const void* H, const void* X0,
+                              const void* Wg, const void* Wu, const void* W_down0,
+                              const void* conv_taps, const void* W_target, float eta,
+                              int32_t chunk, const void* dO, const float* dW_final, float* dH,
+                              float* dX0, float* dWg, float* dWu, float* dW_down0, float* dtaps,
+                              float* dW_target, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Geo g;
+  TTT_TRY(check_desc(desc, &g));
+  TTT_TRY(check_chunk(chunk, &g));
+  return backward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, nullptr, 0, dO,
+                       dW_final, dH, dX0, dWg, dWu, dW_down0, dtaps, dW_target, workspace,
+                       workspace_bytes, stream);
+}
+
+ttt_status ttt_train_workspace_size(const ttt_desc* desc, int32_t chunk, size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_train_desc(desc, chunk, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = forward_layout(g).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_forward_train(const ttt_desc* desc, const void* H, const void* X0,
+                                   const void* Wg, const void* Wu, const void* W_down0,
+                                   const void* conv_taps, const void* W_target, float eta,
+                                   int32_t chunk, void* O, float* W_down_final, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  Geo g;
+  TTT_TRY(check_train_desc(desc, chunk, &g));
+  return forward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, O, W_down_final,
+                      workspace, workspace_bytes, stream);
+}
+
+ttt_status ttt_backward_saved_workspace_size(const ttt_desc* desc, int32_t chunk,
+                                             size_t* bytes) {
+  Geo g;
+  TTT_TRY(check_train_desc(desc, chunk, &g));
+  if (bytes == nullptr) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = backward_layout(g, true).total;
+  return TTT_OK;
+}
+
+ttt_status ttt_layer_backward_saved(const ttt_desc* desc, const void* H, const void* X0,
+                                    const void* Wg, const void* Wu, const void* W_down0,
+                                    const void* conv_taps, const void* W_target, float eta,
+                                    int32_t chunk, const void* saved, size_t saved_bytes,
+                                    const void* dO, const float* dW_final, float* dH, float* dX0,
+                                    float* dWg, float* dWu, float* dW_down0, float* dtaps,
+                                    float* dW_target, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  Geo g;
+  TTT_TRY(check_train_desc(desc, chunk, &g));
+  TTT_TRY(check_ptr(saved, "saved", 256));
+  return backward_impl(g, H, X0, Wg, Wu, W_down0, conv_taps, W_target, eta, saved, saved_bytes,
+                       dO, dW_final, dH, dX0, dWg, dWu, dW_down0, dtaps, dW_target, workspace,
+                       workspace_bytes, stream);
 }
 
 ttt_status ttt_gated_activation(const ttt_desc* desc, const void* H, const void* Wg,

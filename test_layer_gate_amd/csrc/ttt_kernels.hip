@@ -35,14 +35,17 @@ static_assert(K1_BM * K1_LDZ <= (K1_NSTA * K1_BM + K1_NSTB * K1_BN) * K1_BK,
 // also the SiLU's derivative factors in accumulator-fragment order
 // (sa_frag_offset; padding tokens get zero): the low half of each word
 // bf16(phi(G)), the high half bf16(U phi'(G)), phi'(x) = sigma(x) (1 + x
-// (1 - sigma(x))). Returns the largest |Z| of this lane's values.
+// (1 - sigma(x))); with ZTb, also Z^T as bf16 at scale 1 (the training
+// forward keeps both for the backward). Returns the largest |Z| of this
+// lane's values.
 template <bool ZT_BF16 = false>
 __device__ __forceinline__ float gate_up_tile(const TileIdx& ti, u16* lds,
                                               const u16* __restrict__ H,
                                               const u16* __restrict__ Wgp,
                                               const u16* __restrict__ Wup, u16* __restrict__ Z,
                                               u16* __restrict__ ZT, const Dims& g, float zscale,
-                                              uint32_t* __restrict__ sa = nullptr) {
+                                              uint32_t* __restrict__ sa = nullptr,
+                                              u16* __restrict__ ZTb = nullptr) {
   using L = Layout<K1_BM, K1_BN, K1_WGM, K1_NW>;
   constexpr int NG = L::TN / 2;  // gate tiles per wave (and as many up tiles)
   static_assert(NG >= 1 && L::TN == 2 * NG, "gate and up tiles pair up");
@@ -89,6 +92,9 @@ __device__ __forceinline__ float gate_up_tile(const TileIdx& ti, u16* lds,
               make_uint4(w[0], w[1], w[2], w[3]);
         }
       }
+      if (ZTb != nullptr)
+        store_tile_sb<kZtSlab>(g.T_pad, j, t0 + fr.wm * WROWS + m * 32, z, CvtBf16{1.0f}, j < f,
+                               StreamSink{ZTb + ti.b * sb_elems<kZtSlab>(f, g.T_pad)});
       if (ZT != nullptr) {
         if constexpr (ZT_BF16)
           store_tile_sb<kZtSlab>(g.T_pad, j, t0 + fr.wm * WROWS + m * 32, z, CvtBf16{zscale},
@@ -133,6 +139,19 @@ __global__ __launch_bounds__(64 * K1_NW) void gate_up_kernel(
   const float m =
       gate_up_tile(tile_index(tiles_m, tiles_n, 4), lds, H, Wgp, Wup, Z, ZT, g, 1.0f);
   if (range != nullptr) range_note(range, m);
+}
+
+// The training forward's gate/up: gate_up_kernel's Z and fp16 Z^T (with its
+// range note), and for the backward Z^T as bf16 slabs and the SiLU's
+// derivative factors (gate_up_tile's ZTb and sa).
+__global__ __launch_bounds__(64 * K1_NW) void gate_up_train_kernel(
+    const u16* __restrict__ H, const u16* __restrict__ Wgp, const u16* __restrict__ Wup,
+    u16* __restrict__ Z, u16* __restrict__ ZT, u16* __restrict__ ZTb, uint32_t* __restrict__ sa,
+    Dims g, int tiles_m, int tiles_n, uint32_t* __restrict__ range) {
+  TTT_GEMM_LDS_AB(lds, K1_BM, K1_BN, K1_BK, K1_NSTA, K1_NSTB)
+  const float m = gate_up_tile(tile_index(tiles_m, tiles_n, 4), lds, H, Wgp, Wup, Z, ZT, g, 1.0f,
+                               sa, ZTb);
+  range_note(range, m);
 }
 
 // The backward's recompute of gate/up: Z (bf16, token-major), Z^T as bf16
@@ -1265,6 +1284,15 @@ hipError_t launch_gate_up_bwd(const uint16_t* H, const uint16_t* Wgp, const uint
   const int tiles_m = g.T_pad / K1_BM, tiles_n = ceil_div(g.f, K1_BN / 2);
   gate_up_bwd_kernel<<<tiles_m * tiles_n * g.B, 64 * K1_NW, 0, s>>>(H, Wgp, Wup, Z, ZT, sa, g,
                                                                   tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_train(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
+                                uint16_t* Z, uint16_t* ZT, uint16_t* ZTb, uint32_t* sa,
+                                const Dims& g, uint32_t* range, hipStream_t s) {
+  const int tiles_m = g.T_pad / K1_BM, tiles_n = ceil_div(g.f, K1_BN / 2);
+  gate_up_train_kernel<<<tiles_m * tiles_n * g.B, 64 * K1_NW, 0, s>>>(H, Wgp, Wup, Z, ZT, ZTb, sa,
+                                                                    g, tiles_m, tiles_n, range);
   return hipGetLastError();
 }
 

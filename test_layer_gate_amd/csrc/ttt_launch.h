@@ -257,9 +257,16 @@ hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bs
 // ------------------------------------------------------------ backward
 // (ttt_backward.hip, and the prefill kernels' backward variants)
 
+// The training forward's gate/up: Z and fp16 Z^T as launch_gate_up (range
+// noted in range, not null), plus Z^T as bf16 slabs (ZTb) and the SiLU
+// factors as launch_gate_up_bwd writes them (sa, B T_pad f words).
+hipError_t launch_gate_up_train(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
+                                uint16_t* Z, uint16_t* ZT, uint16_t* ZTb, uint32_t* sa,
+                                const Dims& g, uint32_t* range, hipStream_t s);
 // gate/up for the backward: Z (bf16, token-major [B][T][ld_z]), ZT as bf16
-// slabs (sb<256>(f x T_pad) per sequence), and sa [B][T][f]: per element the
-// bf16 pair (phi(G), U phi'(G)) in the low and high halves of a word.
+// slabs (sb<256>(f x T_pad) per sequence), and sa (B T_pad f words in
+// accumulator-fragment order, sa_frag_offset): per element the bf16 pair
+// (phi(G), U phi'(G)) in the low and high halves of a word.
 hipError_t launch_gate_up_bwd(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
                               uint16_t* Z, uint16_t* ZT, uint32_t* sa, const Dims& g,
                               hipStream_t s);

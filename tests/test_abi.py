@@ -552,6 +552,61 @@ def test_backward_validates_before_launch(L):
     assert "stride" in L.ttt_last_error().decode()
 
 
+# ---- training: the forward that keeps its activations, and its backward ----
+
+def train_sizes(L, desc, chunk=1024):
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st1 = L.ttt_train_workspace_size(ctypes.byref(desc), chunk, ctypes.byref(a))
+    st2 = L.ttt_backward_saved_workspace_size(ctypes.byref(desc), chunk, ctypes.byref(b))
+    return st1, a.value, st2, b.value
+
+
+def test_train_workspace_sizes(L):
+    desc = qwen_desc()
+    st1, fwd_train, st2, bwd_saved = train_sizes(L, desc)
+    assert st1 == OK and st2 == OK
+    _, fwd = ws_size(L, desc, 1024)
+    _, bwd = bwd_ws(L, desc)
+    B, T, d, f = 1, 65536, 2560, 9728
+    # the training forward keeps a bf16 Z^T and the SiLU factors besides
+    assert fwd_train - fwd >= B * T * f * (2 + 4)
+    # the saved backward needs no Z, Z^T, SiLU factors or packed weights
+    assert bwd - bwd_saved >= B * T * f * (2 + 2 + 4)
+    running = qwen_desc(flags=bnd.FLAG_SCHED_RUNNING)
+    st1, _, st2, _ = train_sizes(L, running)
+    assert st1 == UNSUPPORTED and st2 == UNSUPPORTED
+    assert "prefix" in L.ttt_last_error().decode()
+
+
+def test_train_entry_points_validate_before_launch(L):
+    fb = FakeBuffers()
+    p = [fb[i] for i in range(18)]
+    desc = qwen_desc()
+    st1, need_fwd, _, need_bwd = train_sizes(L, desc)
+    st = L.ttt_layer_forward_train(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3), 1024, p[7],
+                                   p[8], p[9], ctypes.c_size_t(need_fwd - 1), None)
+    assert st == WORKSPACE
+    st = L.ttt_layer_forward_train(ctypes.byref(qwen_desc(flags=bnd.FLAG_SCHED_RUNNING)),
+                                   *p[:7], ctypes.c_float(1e-3), 1024, p[7], p[8], p[9],
+                                   ctypes.c_size_t(1 << 62), None)
+    assert st == UNSUPPORTED
+
+    def bwd(saved, saved_bytes, ws_bytes=1 << 62):
+        return L.ttt_layer_backward_saved(ctypes.byref(desc), *p[:7], ctypes.c_float(1e-3), 1024,
+                                          saved, ctypes.c_size_t(saved_bytes), p[8], p[9],
+                                          *p[10:17], p[17], ctypes.c_size_t(ws_bytes), None)
+    assert bwd(ctypes.c_void_p(0), need_fwd) == INVALID
+    assert bwd(p[7], need_fwd - 1) == WORKSPACE
+    assert "saved" in L.ttt_last_error().decode()
+    assert bwd(p[7], need_fwd, ws_bytes=need_bwd - 1) == WORKSPACE
+    q = list(p)
+    q[10] = ctypes.c_void_p(p[7].value + 4096)        # dH inside saved
+    st = L.ttt_layer_backward_saved(ctypes.byref(desc), *q[:7], ctypes.c_float(1e-3), 1024,
+                                    q[7], ctypes.c_size_t(need_fwd), q[8], q[9], *q[10:17],
+                                    q[17], ctypes.c_size_t(1 << 62), None)
+    assert st == ALIAS
+
+
 # ---- the no-allocation entry point ------------------------------------------
 
 def test_noalloc_rejects_problems_beyond_its_scratch(L):

@@ -80,3 +80,11 @@ def test_traffic_of_a_shared_kernel_name_is_not_used(tmp_path, monkeypatch):
     key = bench.traffic_key("w", "backward")
     assert bench.measured_traffic("bwd_states", key) is None
     assert bench.measured_traffic("bwd_dz", key) == 7.0
+
+
+def test_train_flops():
+    """A training step: the prefill's contractions plus the backward's, less
+    the backward's gate/up recompute and state scan."""
+    cfg = synth.CONFIGS["qwen3_4b_64k"]
+    B, T, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
+    assert bench.train_flops(cfg) == 24.0 * B * T * d * f + 8.0 * B * T * d * d

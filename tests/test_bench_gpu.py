@@ -26,7 +26,7 @@ def run_bench(*args):
     return json.loads(lines[0])
 
 
-@pytest.mark.parametrize("variant", ["plain", "backward", "decode"])
+@pytest.mark.parametrize("variant", ["plain", "backward", "train", "decode"])
 def test_bench_line(variant):
     extra = [] if variant == "plain" else ["--no-cpu-baseline"]
     d = run_bench("--variant", variant, *extra)

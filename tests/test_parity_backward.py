@@ -206,3 +206,69 @@ def test_backward_full_size_whole_sequence(ttt):
     bad = {k: e for k, e in errs.items() if not e <= BWD_TOL}
     assert not bad, bad
 
+
+
+# ---- training: ttt_layer_forward_train, then ttt_layer_backward_saved ----
+
+def run_train(ttt, x, dtype, eta, chunk, dO, dWf, pad="sequence", W0=None):
+    t = to_dev(x, dtype)
+    if W0 is not None:
+        t["W_down0"] = torch.from_numpy(W0).to("cuda").to(t["Wg"].dtype)
+    O, Wf, saved = ttt.layer_forward_train(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"],
+                                           t["taps"], t["W_target"], eta, chunk, pad=pad)
+    dO_t = torch.from_numpy(dO).to("cuda").to(t["H"].dtype)
+    dWf_t = None if dWf is None else torch.from_numpy(dWf).to("cuda")
+    g = ttt.layer_backward(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
+                           t["W_target"], eta, chunk, dO_t, dW_final=dWf_t, pad=pad, saved=saved)
+    O2, Wf2 = ttt.layer_forward(t["H"], t["X0"], t["Wg"], t["Wu"], t["W_down0"], t["taps"],
+                                t["W_target"], eta, chunk, pad=pad, schedule="prefix")
+    torch.cuda.synchronize()
+    # the training forward's outputs are the prefill's, bit for bit
+    assert torch.equal(O, O2) and torch.equal(Wf, Wf2)
+    return {k: v.cpu().numpy() for k, v in g.items()}
+
+
+@pytest.mark.parametrize("pad", ["sequence", "chunk"])
+@pytest.mark.parametrize("name", ["tiny_amp", "mid_amp"])
+def test_saved_backward_matches_oracle(ttt, name, pad):
+    cfg = synth.CONFIGS[name]
+    x = synth.make_inputs(cfg, seed=220)
+    dO, dWf = upstream(x, cfg.dtype, seed=221)
+    g = run_train(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf, pad=pad)
+    check(x, g, cfg.eta, cfg.chunk, dO, dWf, f"saved {name} {pad}", pad=pad)
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_saved_backward_ragged_batch(ttt, shared):
+    cfg = synth.CONFIGS["mid_amp"]
+    x = synth.make_inputs(cfg, batch=2, seq_len=1000, seed=222)
+    W0 = None if shared else np.stack([x["W_down0"], synth.round_to_bf16(-0.5 * x["W_down0"])])
+    dO, dWf = upstream(x, cfg.dtype, seed=223)
+    g = run_train(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf, W0=W0)
+    check(x, g, cfg.eta, cfg.chunk, dO, dWf, f"saved ragged B=2 shared={shared}", W0=W0)
+
+
+def test_saved_backward_fp32_and_no_state_gradient(ttt):
+    cfg = synth.CONFIGS["tiny"]
+    x = synth.make_inputs(cfg, seed=224)
+    dO, _ = upstream(x, cfg.dtype, seed=225, with_dwf=False)
+    g = run_train(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, None)
+    check(x, g, cfg.eta, cfg.chunk, dO, None, "saved tiny fp32, dW_final none")
+
+
+def test_saved_backward_full_size_whole_sequence(ttt):
+    """The training step at the Qwen3-4B shape, T = 65536: the saved
+    backward's gradients over the whole sequence against the segmented
+    oracle."""
+    cfg = synth.CONFIGS["qwen3_4b_64k"]
+    x = synth.make_inputs(cfg)
+    dO, dWf = upstream(x, cfg.dtype, seed=226)
+    g = run_train(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf)
+    print("  GPU training step done", flush=True)
+    ref = oracle_backward_segments(x, dO, dWf, cfg.eta, cfg.chunk)
+    errs = {k: rel(g[k], ref[k]) for k in GRADS}
+    print("saved qwen3_4b_64k: " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()), flush=True)
+    for k in GRADS:
+        assert np.isfinite(g[k]).all(), k
+    bad = {k: e for k, e in errs.items() if not e <= BWD_TOL}
+    assert not bad, bad
