@@ -72,9 +72,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_gate_up_kernel(
   }
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * (kDecThreads / 64) + (threadIdx.x >> 6);
-  if (j >= f) return;  // uniform per wave
   float zmax = 0.0f;
-  for (int b0 = 0; b0 < B; b0 += kDecMaxB) {
+  // Waves past the last row skip the product but still reach the range
+  // note's barrier (one atomic per workgroup: one per wave, a row each,
+  // queued on the range words).
+  for (int b0 = 0; j < f && b0 < B; b0 += kDecMaxB) {
     const int nb = min(kDecMaxB, B - b0);
     float g[kDecMaxB], u[kDecMaxB];
 #pragma unroll
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gate_up_kernel(
       }
     }
   }
-  range_note(zrange + kRangeZ * kRangeSlots, zmax);
+  range_note_block<kDecThreads>(zrange + kRangeZ * kRangeSlots, zmax);
 }
 
 // At a chunk's close: if the chunk's largest |z| is out of the fp16 range,
