@@ -17,7 +17,8 @@ namespace tttk {
 namespace {
 
 constexpr int kDecThreads = 256;   // 4 waves
-constexpr int kDecMaxB = 8;        // sequences per pass of the gate/up product
+constexpr int kDecMaxB = 4;        // sequences per pass of the gate/up product
+constexpr int kDecRows = 2;        // W_g / W_u rows per wave of the gate/up product
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -47,7 +48,8 @@ __device__ __forceinline__ void load8_bf16(const void* p, int64_t i, float (&v)[
 }
 
 // Gated activation of one token per sequence: for row j of W_g and W_u
-// (one wave per row), z[b][j] = SiLU(h_b . Wg[j]) * (h_b . Wu[j]). z goes to
+// (two rows per wave, so that all of a Qwen3-4B-sized d_ff's waves are
+// resident at once), z[b][j] = SiLU(h_b . Wg[j]) * (h_b . Wu[j]). z goes to
 // zb (bf16, the apply's operand) and to row `col` of the chunk's fp32 rows
 // zc [B][chunk][f], and, as fp16, to column `col` of the chunk's Z^T
 // (sb<256> rows j, zt_cols columns) for the chunk's update: the same
@@ -71,43 +73,56 @@ __global__ __launch_bounds__(kDecThreads) void decode_gate_up_kernel(
                    pack_bf16(v[6], v[7]));
   }
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * (kDecThreads / 64) + (threadIdx.x >> 6);
+  const int j0 = (blockIdx.x * (kDecThreads / 64) + (threadIdx.x >> 6)) * kDecRows;
   float zmax = 0.0f;
   // Waves past the last row skip the product but still reach the range
-  // note's barrier (one atomic per workgroup: one per wave, a row each,
-  // queued on the range words).
-  for (int b0 = 0; j < f && b0 < B; b0 += kDecMaxB) {
+  // note's barrier (one atomic per workgroup: per wave, the notes queued on
+  // the range words).
+  for (int b0 = 0; j0 < f && b0 < B; b0 += kDecMaxB) {
     const int nb = min(kDecMaxB, B - b0);
-    float g[kDecMaxB], u[kDecMaxB];
+    float g[kDecRows][kDecMaxB], u[kDecRows][kDecMaxB];
 #pragma unroll
-    for (int b = 0; b < kDecMaxB; ++b) g[b] = u[b] = 0.f;
+    for (int r = 0; r < kDecRows; ++r)
+#pragma unroll
+      for (int b = 0; b < kDecMaxB; ++b) g[r][b] = u[r][b] = 0.f;
     for (int c = lane * 8; c < d; c += 64 * 8) {
-      float wg[8], wu[8];
-      load8_bf16<W_F32>(Wg, (int64_t)j * d + c, wg);
-      load8_bf16<W_F32>(Wu, (int64_t)j * d + c, wu);
+      float wg[kDecRows][8], wu[kDecRows][8];
+#pragma unroll
+      for (int r = 0; r < kDecRows; ++r) {
+        const int j = min(j0 + r, f - 1);  // in bounds; a clamped row is not stored (below)
+        load8_bf16<W_F32>(Wg, (int64_t)j * d + c, wg[r]);
+        load8_bf16<W_F32>(Wu, (int64_t)j * d + c, wu[r]);
+      }
 #pragma unroll
       for (int b = 0; b < kDecMaxB; ++b) {
         if (b < nb) {
           float hv[8];
           load8_bf16<ACT_F32>(h, (int64_t)(b0 + b) * d + c, hv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            g[b] = fmaf(hv[e], wg[e], g[b]);
-            u[b] = fmaf(hv[e], wu[e], u[b]);
-          }
+          for (int r = 0; r < kDecRows; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              g[r][b] = fmaf(hv[e], wg[r][e], g[r][b]);
+              u[r][b] = fmaf(hv[e], wu[r][e], u[r][b]);
+            }
         }
       }
     }
 #pragma unroll
-    for (int b = 0; b < kDecMaxB; ++b) {
-      if (b < nb) {
-        const float gs = wave_sum(g[b]), us = wave_sum(u[b]);
-        if (lane == 0) {
-          const float z = silu(gs) * us;
-          zmax = fmaxf(zmax, fabsf(z));
-          zb[(int64_t)(b0 + b) * f + j] = bf16_rne(z);
-          zc[((int64_t)(b0 + b) * chunk + col) * f + j] = z;
-          zt[(int64_t)(b0 + b) * zt_bstride + sb_offset<kZtSlab>(j, col, zt_cols)] = f16_rne(z);
+    for (int r = 0; r < kDecRows; ++r) {
+      const int j = j0 + r;
+#pragma unroll
+      for (int b = 0; b < kDecMaxB; ++b) {
+        if (b < nb) {
+          const float gs = wave_sum(g[r][b]), us = wave_sum(u[r][b]);
+          if (lane == 0 && j < f) {
+            const float z = silu(gs) * us;
+            zmax = fmaxf(zmax, fabsf(z));
+            zb[(int64_t)(b0 + b) * f + j] = bf16_rne(z);
+            zc[((int64_t)(b0 + b) * chunk + col) * f + j] = z;
+            zt[(int64_t)(b0 + b) * zt_bstride + sb_offset<kZtSlab>(j, col, zt_cols)] =
+                f16_rne(z);
+          }
         }
       }
     }
@@ -199,8 +214,9 @@ hipError_t launch_decode_gate_up(const void* h, const void* x0, bool act_f32, co
                                  float* zc, uint16_t* zt, int64_t zt_bstride, int zt_cols,
                                  uint16_t* x0c, int chunk, int col, uint32_t* zrange,
                                  hipStream_t s) {
-  // One wave per row of W_g / W_u, and enough threads for the X0 copy.
-  const int grid = max(ceil_div_i(f, kDecThreads / 64), ceil_div_i((int64_t)B * d / 8, kDecThreads));
+  // kDecRows rows of W_g / W_u per wave, and enough threads for the X0 copy.
+  const int grid = max(ceil_div_i(f, kDecThreads / 64 * kDecRows),
+                       ceil_div_i((int64_t)B * d / 8, kDecThreads));
 #define TTT_DEC_GU(A, W)                                                                     \
   decode_gate_up_kernel<A, W><<<grid, kDecThreads, 0, s>>>(h, x0, Wg, Wu, B, d, f, zb, zc, zt, \
                                                             zt_bstride, zt_cols, x0c, chunk, col, \
