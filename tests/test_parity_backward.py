@@ -272,3 +272,35 @@ def test_saved_backward_full_size_whole_sequence(ttt):
         assert np.isfinite(g[k]).all(), k
     bad = {k: e for k, e in errs.items() if not e <= BWD_TOL}
     assert not bad, bad
+
+
+def test_backward_full_size_two_sequences(ttt):
+    """The LLaMA-3.1-8B shape (B = 2, T = 32768, d 4096, d_ff 14336, one
+    shared W_down0): every gradient over both whole sequences against the
+    segmented oracle, run per sequence (the sequences share only W_down0,
+    W_g, W_u, the taps and W_target, whose gradients add up)."""
+    cfg = synth.CONFIGS["llama31_8b_32k"]
+    x = synth.make_inputs(cfg)
+    dO, dWf = upstream(x, cfg.dtype, seed=227)
+    g = run_backward(ttt, x, cfg.dtype, cfg.eta, cfg.chunk, dO, dWf)
+    print("  GPU backward done", flush=True)
+    ref = None
+    for b in range(cfg.batch):
+        xb = {k: (v[b:b + 1] if k in ("H", "X0") else v) for k, v in x.items()}
+        rb = oracle_backward_segments(xb, dO[b:b + 1], dWf[b:b + 1], cfg.eta, cfg.chunk)
+        if ref is None:
+            ref = {k: (np.zeros((cfg.batch,) + v.shape[1:]) if k in ("dH", "dX0") else v)
+                   for k, v in rb.items()}
+        else:
+            for k in ("dWg", "dWu", "dtaps", "dW_target", "dW_down0"):
+                ref[k] = ref[k] + rb[k]
+        ref["dH"][b] = rb["dH"][0]
+        ref["dX0"][b] = rb["dX0"][0]
+        print(f"  oracle sequence {b} done", flush=True)
+    errs = {k: rel(g[k], ref[k]) for k in GRADS}
+    print("llama31_8b_32k: " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()), flush=True)
+    for k in GRADS:
+        assert g[k].shape == ref[k].shape, k
+        assert np.isfinite(g[k]).all(), k
+    bad = {k: e for k, e in errs.items() if not e <= BWD_TOL}
+    assert not bad, bad
