@@ -304,3 +304,16 @@ def test_backward_full_size_two_sequences(ttt):
         assert np.isfinite(g[k]).all(), k
     bad = {k: e for k, e in errs.items() if not e <= BWD_TOL}
     assert not bad, bad
+
+
+def test_backward_eta_zero(ttt):
+    """eta = 0: the layer is the plain gated MLP (O = Z W_down0^T), so no
+    gradient reaches the target path (dX0, dtaps and dW_target exactly
+    zero) and the rest matches the oracle."""
+    cfg = synth.CONFIGS["mid_amp"]
+    x = synth.make_inputs(cfg, seed=228)
+    dO, dWf = upstream(x, cfg.dtype, seed=229)
+    g = run_backward(ttt, x, cfg.dtype, 0.0, cfg.chunk, dO, dWf)
+    for k in ("dX0", "dtaps", "dW_target"):
+        assert not np.any(g[k]), k
+    check(x, g, 0.0, cfg.chunk, dO, dWf, "eta 0")
