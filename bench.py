@@ -73,9 +73,8 @@ KERNEL_NAMES = {"gate_up": "gate_up_kernel", "target": "target_kernel",
                 "bwd_dy": "nt_gemm_kernel", "bwd_dh": "nt_gemm_kernel",
                 "bwd_dw_target": "update_kernel", "bwd_dw_gate_up": "update_kernel",
                 "bwd_conv": "conv_bwd", "bwd_rows": "rows_bf16_kernel",
-                "bwd_to_slab": "to_slab_kernel", "bwd_transpose_grads": "slab_transpose_kernel",
-                "bwd_transpose_w": "transpose_bf16_kernel", "bwd_sum": "sum_parts_kernel",
-                "bwd_states_transpose": "slab_transpose_kernel"}
+                "bwd_to_slab": "to_slab_kernel",
+                "bwd_transpose_w": "transpose_bf16_kernel", "bwd_sum": "sum_parts_kernel"}
 
 
 def backward_flops(cfg):
@@ -115,9 +114,6 @@ def kernel_work(name, cfg, T_pad):
         return "mfma", 2.0 * B * T * d * f
     if name in ("bwd_target", "bwd_dy", "bwd_dw_target"):
         return "mfma", 2.0 * B * T * d * d
-    if name in ("bwd_states_transpose", "bwd_transpose_grads"):
-        # every chunk's bf16 d x f matrix read and written once
-        return "hbm", 2.0 * 2.0 * B * -(-T // cfg.chunk) * d * f
     if name == "conv":
         return "hbm", 2.0 * B * T * d + 2.0 * B * T_pad * d + 2.0 * K * d
     if name == "transpose_w_target":

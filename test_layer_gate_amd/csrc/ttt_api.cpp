@@ -947,7 +947,7 @@ namespace {
 // orientations) of every chunk, and the gradients' intermediates.
 struct BwdLayout {
   size_t range = 0, wgp = 0, wup = 0, hb = 0, x0b = 0, dov = 0, y = 0, wtt = 0, yt = 0, z = 0,
-         zt = 0, sa = 0, vt = 0, dot = 0, ht = 0, wgt = 0, gs = 0, dw0 = 0, dgu = 0, dgt = 0,
+         zt = 0, sa = 0, vt = 0, dot = 0, ht = 0, ws = 0, gs = 0, dw0 = 0, dgu = 0, dgt = 0,
          dut = 0, dv = 0, dvt = 0, wgut = 0, wtb = 0, dy = 0, part = 0, total = 0;
   int64_t ld_gu = 0, ld_ov = 0;
 };
@@ -964,7 +964,7 @@ BwdLayout backward_layout(const Geo& g, bool saved = false) {
   };
   const tttk::Dims& D = g.dims;
   const int64_t BT = g.B * g.T, BTp = g.B * g.T_pad;
-  const int64_t snap_df = tttk::sb_elems<256>(g.d, g.f), snap_f2d = tttk::sb_elems<256>(g.f, 2 * g.d);
+  const int64_t snap_df = tttk::sb_elems<256>(g.d, g.f);
   L.ld_gu = tttk::pad_ld(2 * g.f);
   L.ld_ov = tttk::pad_ld(2 * g.d);
   L.range = take(tttk::kRangeWords * 4);
@@ -988,7 +988,7 @@ BwdLayout backward_layout(const Geo& g, bool saved = false) {
   L.vt = take(tttk::vt_elems(D) * 2);
   L.dot = take(tttk::vt_elems(D) * 2);
   L.ht = take(tttk::sb_elems<256>(g.d, BTp) * 2);
-  L.wgt = take(g.B * g.nchunks * snap_f2d * 2);
+  if (!saved) L.ws = take(g.B * g.nchunks * snap_df * 2);
   L.gs = take(g.B * g.nchunks * snap_df * 2);
   if (g.w0_stride == 0 && g.B > 1) L.dw0 = take(g.B * g.d * g.f * 4);
   L.dgu = take(BT * L.ld_gu * 2);
@@ -1078,7 +1078,7 @@ ttt_status backward_impl(const Geo& g, const void* H, const void* X0, const void
   const tttk::Dims& D = g.dims;
   const int B = (int)g.B, T = (int)g.T, d = (int)g.d, f = (int)g.f, C = (int)g.C;
   const int nch = (int)g.nchunks;
-  const int64_t snap_df = tttk::sb_elems<256>(g.d, g.f), snap_f2d = tttk::sb_elems<256>(g.f, 2 * g.d);
+  const int64_t snap_df = tttk::sb_elems<256>(g.d, g.f);
   uint32_t* range = at<uint32_t>(workspace, L.range);
   uint32_t* range_y = range + tttk::kRangeY * tttk::kRangeSlots;
   uint32_t* range_wt = range + tttk::kRangeWt * tttk::kRangeSlots;
@@ -1145,32 +1145,25 @@ ttt_status backward_impl(const Geo& g, const void* H, const void* X0, const void
   TTT_LAUNCH("bwd_to_slab", s,
              tttk::launch_to_slab(Hb, false, g.d, HT, B, T, (int)g.T_pad, d, true, s));
 
-  // The states W_i of every chunk, transposed (rows d_ff), into the first d
-  // columns of the chunk's [W_i^T | Gbar_{i+1}^T]: the forward's update
-  // with its operands swapped.
-  uint16_t* WGT = at<uint16_t>(workspace, L.wgt);
-  const tttk::Dims Dsw = tttk::make_dims(B, T, f, d);
-  if (sv)
-    // the training forward's snapshots W_i (sb<256>(d x f), bf16), transposed
-    TTT_LAUNCH("bwd_states_transpose", s,
-               tttk::launch_slab_transpose(reinterpret_cast<const uint16_t*>(saved_at(F.snap)),
-                                           snap_df, WGT, snap_f2d, 2 * g.d, 0, B * nch, d, f, s));
-  else
+  // The states W_i of every chunk (bf16 sb<256>(d x f)): the training
+  // forward's snapshots, or the forward's update again on bf16 operands.
+  const uint16_t* WS;
+  if (sv) {
+    WS = reinterpret_cast<const uint16_t*>(saved_at(F.snap));
+  } else {
+    uint16_t* ws = at<uint16_t>(workspace, L.ws);
     TTT_LAUNCH("bwd_states", s,
-               tttk::launch_contract_bf16(VT, ZT, Dsw, W_down0, g.w_f32, true, g.w0_stride, g.f,
-                                          WGT, g.nchunks * snap_f2d, 2 * d, nullptr, false, C,
-                                          s));
+               tttk::launch_contract_bf16(ZT, VT, D, W_down0, g.w_f32, false, g.w0_stride, g.f,
+                                          ws, g.nchunks * snap_df, f, nullptr, false, C, s));
+    WS = ws;
+  }
   // The state gradients Gbar_{i+1} = dW_final + sum_{j > i} dO_j^T Z_j of
-  // every chunk, backwards over the tokens (the scan ends at dW_down0), and
-  // their transposes into the last d columns of [W_i^T | Gbar_{i+1}^T].
+  // every chunk, backwards over the tokens (the scan ends at dW_down0).
   uint16_t* GS = at<uint16_t>(workspace, L.gs);
   float* dw0_all = (g.w0_stride == 0 && g.B > 1) ? at<float>(workspace, L.dw0) : dW_down0;
   TTT_LAUNCH("bwd_state_grads", s,
              tttk::launch_contract_bf16(ZT, DOT, D, dW_final, true, false, df, g.f, GS,
                                         g.nchunks * snap_df, f, dw0_all, true, C, s));
-  TTT_LAUNCH("bwd_transpose_grads", s,
-             tttk::launch_slab_transpose(GS, snap_df, WGT, snap_f2d, 2 * g.d, d, B * nch, d, f,
-                                         s));
   if (dw0_all != dW_down0)
     TTT_LAUNCH("bwd_sum", s, tttk::launch_sum_parts(dw0_all, df, B, dW_down0, df, s));
 
@@ -1179,8 +1172,9 @@ ttt_status backward_impl(const Geo& g, const void* H, const void* X0, const void
   uint16_t* DGT = at<uint16_t>(workspace, L.dgt);
   uint16_t* DUT = at<uint16_t>(workspace, L.dut);
   TTT_LAUNCH("bwd_dz", s,
-             tttk::launch_act_gemm_dz(DOV, L.ld_ov, WGT, g.nchunks * snap_f2d, snap_f2d, d, f, C,
-                                      nch, SA, DGU, L.ld_gu, DGT, DUT, D, s));
+             tttk::launch_act_gemm_dz(DOV, L.ld_ov, WS, g.nchunks * snap_df, snap_df, GS,
+                                      g.nchunks * snap_df, snap_df, d, f, C, nch, SA, DGU,
+                                      L.ld_gu, DGT, DUT, D, s));
   uint16_t* DV = at<uint16_t>(workspace, L.dv);
   uint16_t* DVT = at<uint16_t>(workspace, L.dvt);
   TTT_LAUNCH("bwd_dv", s,

@@ -48,11 +48,13 @@ __device__ __forceinline__ void static_for(const F& f) {
 
 // ------------------------------------------------ chunked activation GEMM
 // C[t][n] = sum_k A[t][k] S(i)[n][k] for the tokens t of one chunk i: A
-// token-major bf16 ([B][T][lda], K contiguous), S(i) chunk i's bf16 state
-// matrix (sb<256>, rows n, K columns) at S + b * sbs + i * scs. M = BM
-// tokens (a divisor of the chunk), N = 256. For dZ the K columns hold two
-// contractions side by side ([dO | eta V] against [W_i^T | Gbar^T]): one
-// pipeline over K = 2d.
+// token-major bf16 ([B][T][lda], K contiguous). M = BM tokens (a divisor of
+// the chunk), N = 256. dV: S(i) is chunk i's bf16 state gradient matrix
+// (sb<256>, rows n, K columns) at S + b * sbs + i * scs. dZ: two
+// contractions side by side in one pipeline over K = 2d, [dO | eta V]
+// against S(i) = [W_i^T | Gbar^T]; the chunk's state W_i (at S + b * sbs +
+// i * scs) and state gradient Gbar (at G + b * g_sbs + i * g_scs) are
+// sb<256>(d x f) matrices, read transposed (kSlabT) as they are.
 constexpr int KA_NW = 8, KA_BN = 256, KA_BK = 64;
 template <int BM>
 struct ActCfg {
@@ -67,6 +69,8 @@ struct ActArgs {
   int64_t lda;
   const u16* S;
   int64_t sbs, scs;
+  const u16* G;
+  int64_t g_sbs, g_scs;
   int K;
   int N, chunk, n_chunks;
   float scale;
@@ -106,9 +110,21 @@ __device__ __forceinline__ void act_gemm(const ActArgs& a, const Dims& g, int ti
   zero_acc(acc);
   {
     const Operand ao = row_major<KA_BK>(a.A + ((int64_t)ti.b * g.T + t0) * a.lda, a.lda, g.T - t0);
-    const Operand so = slab_blocked<256>(a.S + ti.b * a.sbs + i * a.scs, a.K, n0, 0);
-    gemm_core_ab<KA_NW, BM, KA_BN, C::WGM, KA_BK, C::NSTA, C::NSTB, Bf16Mma, false, kRowMajor,
-                 kSlab>(ao, so, so, a.K / KA_BK, &acc[0][0], lds, NoHook{});
+    if constexpr (MODE == kActDZ) {
+      // The tile's columns n0 .. n0 + 255 of both (d x f) matrices start in
+      // slab n0 / 64 of their first slab row.
+      const int64_t col0 = (int64_t)(n0 >> 6) * (256 * 64);
+      const uint32_t bytes = (uint32_t)((sb_elems<256>(g.d, g.f) - col0) * 2);
+      const OperandT so{a.S + ti.b * a.sbs + i * a.scs + col0,
+                        a.G + ti.b * a.g_sbs + i * a.g_scs + col0, bytes, bytes, g.d / KA_BK,
+                        (int64_t)g.f};
+      gemm_core_ab<KA_NW, BM, KA_BN, C::WGM, KA_BK, C::NSTA, C::NSTB, Bf16Mma, false, kRowMajor,
+                   kSlabT>(ao, so, so, a.K / KA_BK, &acc[0][0], lds, NoHook{});
+    } else {
+      const Operand so = slab_blocked<256>(a.S + ti.b * a.sbs + i * a.scs, a.K, n0, 0);
+      gemm_core_ab<KA_NW, BM, KA_BN, C::WGM, KA_BK, C::NSTA, C::NSTB, Bf16Mma, false, kRowMajor,
+                   kSlab>(ao, so, so, a.K / KA_BK, &acc[0][0], lds, NoHook{});
+    }
   }
   const int N = a.N;
   const int64_t kt = (int64_t)g.B * g.T_pad;
@@ -353,39 +369,6 @@ __global__ __launch_bounds__(kBwThreads) void transpose_bf16_kernel(const void* 
   }
 }
 
-// Each of nmat matrices sb<256>(R x C) (src + m * src_stride), transposed,
-// into the columns [k0, k0 + R) of an sb<256>(C x dst_K) matrix (dst + m *
-// dst_stride). R, C and k0 are multiples of 64; one block moves a 64 x 64
-// tile through LDS, 16 bytes (8 consecutive columns) per access.
-__global__ __launch_bounds__(kBwThreads) void slab_transpose_kernel(
-    const u16* __restrict__ src, int64_t src_stride, u16* __restrict__ dst, int64_t dst_stride,
-    int64_t dst_K, int k0, int R, int C) {
-  __shared__ u16 tile[64][72];
-  const int tiles_c = C / 64;
-  const int tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
-  const u16* sm = src + (int64_t)blockIdx.y * src_stride;
-  u16* dm = dst + (int64_t)blockIdx.y * dst_stride;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = threadIdx.x + i * kBwThreads;  // 64 rows x 8 pieces
-    const int r = piece >> 3, k8 = (piece & 7) * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(sm + sb_offset<256>(tr * 64 + r, tc * 64 + k8, C));
-    *reinterpret_cast<uint4*>(&tile[r][k8]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = threadIdx.x + i * kBwThreads;  // 64 columns x 8 pieces of rows
-    const int k = piece >> 3, r8 = (piece & 7) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)tile[r8 + 2 * e][k] | ((uint32_t)tile[r8 + 2 * e + 1][k] << 16);
-    *reinterpret_cast<uint4*>(dm + sb_offset<256>(tc * 64 + k, k0 + tr * 64 + r8, dst_K)) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // dst[r][c] = bf16(src[r][c]) with row strides ld_src and ld_dst, 8
 // columns per thread.
 template <bool F32>
@@ -575,16 +558,24 @@ int grid_of(int64_t threads) { return (int)((threads + kBwThreads - 1) / kBwThre
 
 // ------------------------------------------------------------ launchers
 
-hipError_t launch_act_gemm_dz(const uint16_t* dOV, int64_t lda, const uint16_t* WGT, int64_t sbs,
-                              int64_t scs, int d, int f, int chunk, int n_chunks,
-                              const uint32_t* sa, uint16_t* dgu, int64_t ld_gu, uint16_t* dgt,
-                              uint16_t* dut, const Dims& g, hipStream_t s) {
+hipError_t launch_act_gemm_dz(const uint16_t* dOV, int64_t lda, const uint16_t* W, int64_t w_sbs,
+                              int64_t w_scs, const uint16_t* Gs, int64_t g_sbs, int64_t g_scs,
+                              int d, int f, int chunk, int n_chunks, const uint32_t* sa,
+                              uint16_t* dgu, int64_t ld_gu, uint16_t* dgt, uint16_t* dut,
+                              const Dims& g, hipStream_t s) {
+  // The transposed reads address a state matrix with 32-bit offsets, the
+  // top bit reserved.
+  if (d != g.d || f != g.f || sb_elems<256>(d, f) * 2 >= (int64_t)1 << 31)
+    return hipErrorInvalidValue;
   ActArgs a{};
   a.A = dOV;
   a.lda = lda;
-  a.S = WGT;
-  a.sbs = sbs;
-  a.scs = scs;
+  a.S = W;
+  a.sbs = w_sbs;
+  a.scs = w_scs;
+  a.G = Gs;
+  a.g_sbs = g_sbs;
+  a.g_scs = g_scs;
   a.K = 2 * d;
   a.N = f;
   a.chunk = chunk;
@@ -662,15 +653,6 @@ hipError_t launch_transpose_bf16(const void* src, bool src_f32, uint16_t* dst, i
     transpose_bf16_kernel<true><<<grid, kBwThreads, 0, s>>>(src, dst, rows, cols, ld_dst);
   else
     transpose_bf16_kernel<false><<<grid, kBwThreads, 0, s>>>(src, dst, rows, cols, ld_dst);
-  return hipGetLastError();
-}
-
-hipError_t launch_slab_transpose(const uint16_t* src, int64_t src_stride, uint16_t* dst,
-                                 int64_t dst_stride, int64_t dst_K, int k0, int nmat, int R,
-                                 int C, hipStream_t s) {
-  dim3 grid((R / 64) * (C / 64), nmat);
-  slab_transpose_kernel<<<grid, kBwThreads, 0, s>>>(src, src_stride, dst, dst_stride, dst_K, k0,
-                                                    R, C);
   return hipGetLastError();
 }
 

@@ -34,7 +34,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kThreads = 256;      // small kernels
 constexpr int kMaxStages = 6;      // LDS stages of one operand (all but one in flight)
 constexpr int kRsrcWord3 = 0x00020000;
-enum { kRowMajor = 0, kSlab = 1 };  // LDS / HBM layouts of a GEMM operand (see Operand)
+// LDS / HBM layouts of a GEMM operand (see Operand; kSlabT: OperandT)
+enum { kRowMajor = 0, kSlab = 1, kSlabT = 2 };
 constexpr int kCpolNt = 2, kCpolSc1 = 16;  // cache-policy bits of buffer instructions
 
 struct Bf16Mma {
@@ -86,6 +87,19 @@ template <int BK, int LAY>
 __device__ __forceinline__ uint4 lds_frag(const u16* lds, int row, int kc) {
   return *reinterpret_cast<const uint4*>(lds + (LAY == kSlab ? slab_off(row, kc)
                                                              : Swz<BK>::off(row, kc)));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// A B fragment of a kSlabT stage: two LDS transpose reads at the lane's byte
+// offsets b0 (K values 0..3) and b1 (4..7) from the stage (slabt_tr_byte).
+__device__ __forceinline__ uint4 lds_frag_tr(const u16* lds, uint32_t b0, uint32_t b1) {
+  char* p = (char*)lds;
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + b0));
+  const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + b1));
+  const uint2 xu = __builtin_bit_cast(uint2, x), yu = __builtin_bit_cast(uint2, y);
+  return make_uint4(xu.x, xu.y, yu.x, yu.y);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -220,6 +234,57 @@ struct DmaTile {
   }
 };
 
+// A B operand read transposed from sb<256> matrices (kSlabT, BK = 64, tile
+// of 256 columns): B[n][k] = M0[k][n] for the K steps kt < ksplit and
+// M1[k - 64 ksplit][n] after them, both with K columns (slabt_* in
+// ttt_launch.h give the layouts). base0 / base1 point at the tile's first
+// column in slab row 0; reads at or past bytes0 / bytes1 from there return
+// zero. The step offsets must stay below 2^31 bytes.
+struct OperandT {
+  const u16* base0;
+  const u16* base1;
+  uint32_t bytes0, bytes1;
+  int ksplit;
+  int64_t K;
+};
+
+template <int ROWS, int NW>
+struct DmaTile<ROWS, 64, kSlabT, NW> {
+  static constexpr int NB = ROWS / 8;  // 1 KB blocks: 16 columns x 32 rows each
+  static constexpr int NI = (NB + NW - 1) / NW;
+  uint32_t voff[NI];
+  uint32_t loff[NI];
+  u32x4 rsrc0, rsrc1;
+  int ksplit;
+  int64_t K;
+  __device__ __forceinline__ void init(const OperandT& op, int wave, int lane) {
+    rsrc0 = make_rsrc(op.base0, op.bytes0);
+    rsrc1 = make_rsrc(op.base1, op.bytes1);
+    ksplit = op.ksplit;
+    K = op.K;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int block = (NW * i + wave) % NB;
+      loff[i] = (uint32_t)block * 1024;
+      voff[i] = slabt_piece_byte(block, lane);
+    }
+  }
+  // The scalar byte offset of K step kt, with bit 31 set when it reads M1.
+  __device__ __forceinline__ uint32_t soff(int kt) const {
+    const bool second = kt >= ksplit;
+    const uint32_t o = slabt_step_byte(second ? kt - ksplit : kt, K);
+    return __builtin_amdgcn_readfirstlane(o | (second ? 0x80000000u : 0u));
+  }
+  __device__ __forceinline__ void issue_one(uint32_t lds_stage, uint32_t so, int i) const {
+    lds_dma_b128((so >> 31) ? rsrc1 : rsrc0, lds_stage + loff[i], voff[i], so & 0x7fffffffu);
+  }
+  __device__ __forceinline__ void issue(uint32_t lds_stage, int kt) const {
+    const uint32_t so = soff(kt);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) issue_one(lds_stage, so, i);
+  }
+};
+
 // The LDS of a GEMM workgroup: NST stages of the A tile (BM * BK elements)
 // and NST of the B tile (BN * BK) (the epilogues reuse the whole array once
 // the core has returned).
@@ -343,6 +408,8 @@ struct Layout {
 // (issued right after the previous barrier) and before its spread loads of
 // the other operand, so that its stores need to be complete only R steps
 // later (the waits in between allow for them).
+// BLAY = kSlabT: B0 is an OperandT, read with LDS transpose reads (not with
+// SPLITB).
 // nk is the number of BK-wide K steps. lds holds NSTA stages of the A tile
 // (BM * BK elements each) followed by NSTB stages of the B tile (BN * BK);
 // the A loads run NSTA - 1 steps ahead and the B loads NSTB - 1, so the LDS
@@ -353,16 +420,17 @@ struct Layout {
 // the others then hit, instead of all waiting on the same miss. A hook
 // needs k0 = 0.
 template <int NW, int BM, int BN, int WGM, int BK, int NSTA, int NSTB, class Op, bool SPLITB,
-          int ALAY, int BLAY, class Hook>
-__device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0,
-                                             const Operand& B1, int nk, f32x16* acc, u16* lds,
-                                             const Hook& hook, int k0 = 0) {
+          int ALAY, int BLAY, class Hook, class OpB = Operand>
+__device__ __forceinline__ void gemm_core_ab(const Operand& A, const OpB& B0, const OpB& B1,
+                                             int nk, f32x16* acc, u16* lds, const Hook& hook,
+                                             int k0 = 0) {
   using Lay = Layout<BM, BN, WGM, NW>;
   constexpr int TM = Lay::TM, TN = Lay::TN, WGN = Lay::WGN;
   constexpr int BROWS = SPLITB ? BN / 2 : BN;
   constexpr int KSUB = BK / 16;  // MFMA K-substeps per stage
   static_assert(NSTA >= 2 && NSTB >= 2 && NSTA <= kMaxStages && NSTB <= kMaxStages && KSUB >= 2,
                 "pipeline");
+  static_assert(BLAY != kSlabT || (!SPLITB && BK == 64 && BN == 256), "transposed B tiles");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / WGN, wn = w % WGN;
   if (nk <= 0) return;
@@ -409,6 +477,21 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
     }
   }
   const int khalf = lane >> 5;
+  // kSlabT: the lane's LDS byte offsets of the two transpose reads of each
+  // B fragment in a stage's substep 0.
+  uint32_t btr[BLAY == kSlabT ? TN : 1][2];
+  if constexpr (BLAY == kSlabT) {
+#pragma unroll
+    for (int n = 0; n < TN; ++n)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd) btr[n][rd] = slabt_tr_lane(lane, wn * TN * 32 + n * 32, rd);
+  }
+  auto b_frag = [&](const u16* sb, int n, int sub) {
+    if constexpr (BLAY == kSlabT)
+      return lds_frag_tr(sb, btr[n][0] + slabt_tr_sub(sub), btr[n][1] + slabt_tr_sub(sub));
+    else
+      return lds_frag<BK, BLAY>(sb, brow[n], 2 * sub + khalf);
+  };
 
   // Software pipeline. While stage kt is read, the A loads of stages up to
   // kt + RA and the B loads up to kt + RB are in flight; each refill goes
@@ -423,7 +506,7 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
 #pragma unroll
     for (int m = 0; m < TM; ++m) fa[set][m] = lds_frag<BK, ALAY>(sa, arow[m], 2 * sub + khalf);
 #pragma unroll
-    for (int n = 0; n < TN; ++n) fb[set][n] = lds_frag<BK, BLAY>(sb, brow[n], 2 * sub + khalf);
+    for (int n = 0; n < TN; ++n) fb[set][n] = b_frag(sb, n, sub);
   };
   constexpr int NPA = DmaTile<BM, BK, ALAY, NW>::NI;
   constexpr int NPB =
@@ -482,7 +565,7 @@ __device__ __forceinline__ void gemm_core_ab(const Operand& A, const Operand& B0
     if (r < TM)
       fa[set][r] = lds_frag<BK, ALAY>(sa, arow[r], 2 * sub + khalf);
     else
-      fb[set][r - TM] = lds_frag<BK, BLAY>(sb, brow[r - TM], 2 * sub + khalf);
+      fb[set][r - TM] = b_frag(sb, r - TM, sub);
   };
   // The MFMAs of fragment set `set`, each followed by one read of substep
   // rsub of (sa, sb) into rset and, while nload remain, one load of step

@@ -103,6 +103,64 @@ template <int SR>
 __host__ __device__ inline int64_t sb_elems(int64_t rows, int64_t K) {
   return (rows + SR - 1) / SR * SR * K;
 }
+
+// Transposed reads of an sb<256> matrix M (R x K) as a GEMM B operand whose
+// N index runs over M's columns and whose K index over M's rows (B[n][k] =
+// M[k][n]). One K step is 64 rows of M (inside one 256-row slab row), one N
+// tile 256 columns (four slabs): 32 KB that the sb image holds as 32
+// contiguous 1 KB blocks of 32 rows x 16 columns. The direct-to-LDS loads
+// copy each block whole, with its 16-byte pieces permuted so that the LDS
+// transpose reads of a fragment fall on distinct banks.
+//
+// LDS image of one K step: element (k, n) (k < 64 the row within the step,
+// n < 256 the column within the tile) in 1 KB block 2 (n / 16) + k / 32, at
+// piece 32 h + ((k % 32) ^ 4 h ^ 8 ((n / 16) % 2)) with h = (n / 8) % 2,
+// 2 bytes per column n % 8.
+__host__ __device__ inline uint32_t slabt_lds_byte(int k, int n) {
+  const int f16 = n >> 4, h = (n >> 3) & 1;
+  const int pos = 32 * h + ((k & 31) ^ (4 * h) ^ (8 * (f16 & 1)));
+  return (uint32_t)((2 * f16 + (k >> 5)) * 1024 + pos * 16 + (n & 7) * 2);
+}
+// HBM byte offset, from the tile's first column in the K step's first slab,
+// of the 16-byte piece that lane `lane` of the load filling LDS block `blk`
+// copies: the sb piece of row 32 (blk % 2) + r, columns 16 (blk / 2) + 8 h
+// .. + 7, with h = lane / 32 and r = (lane % 32) ^ 4 h ^ 8 ((blk / 2) % 2),
+// so that it lands at the LDS piece slabt_lds_byte gives it.
+__host__ __device__ inline uint32_t slabt_piece_byte(int blk, int lane) {
+  const int f16 = blk >> 1, g = blk & 1, h = lane >> 5;
+  const int r = (lane & 31) ^ (4 * h) ^ (8 * (f16 & 1));
+  return (uint32_t)((f16 >> 2) * 32768 + (g * 4 + (f16 & 3)) * 1024 + (32 * h + r) * 16);
+}
+// Byte offset of K step kl (rows 64 kl .. 64 kl + 63) of an sb<256> matrix
+// with K columns from the matrix's first slab row.
+__host__ __device__ inline uint32_t slabt_step_byte(int kl, int64_t K) {
+  return (uint32_t)((int64_t)(kl >> 2) * (K >> 6) * 32768 + (kl & 3) * 8192);
+}
+// The LDS transpose read (ds_read_b64_tr_b16) gives lane i of each 16-lane
+// group, as its element e (e = 0..3), element i % 4 of the 8-byte piece that
+// lane 4e + i / 4 of the group addresses. The 32x32x16 MFMA B fragment of
+// columns nb .. nb + 31 (nb a multiple of 32) and K values 8 kc .. 8 kc + 7
+// (lanes 32-63 at kc + 1: kc = 2 sub + lane / 32 for the stage's K substep
+// sub) is two such reads, rd = 0 for K values + 0..3 and rd = 1 for + 4..7,
+// in which lane 4e + j of group G addresses row 8 kc + 4 rd + e, columns
+// nb + 16 (G % 2) + 4 j .. + 3.
+__host__ __device__ inline uint32_t slabt_tr_byte(int lane, int nb, int kc, int rd) {
+  const int G = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
+  return slabt_lds_byte(8 * kc + 4 * rd + e, nb + 16 * (G & 1) + 4 * j);
+}
+// slabt_tr_byte split into a per-lane part and a per-substep part:
+// slabt_tr_byte(lane, nb, 2 sub + lane / 32, rd) = slabt_tr_lane(lane, nb, rd)
+// + slabt_tr_sub(sub).
+__host__ __device__ inline uint32_t slabt_tr_lane(int lane, int nb, int rd) {
+  const int G = lane >> 4, e = (lane >> 2) & 3, j = lane & 3, h = j >> 1;
+  const int f16 = (nb >> 4) + (G & 1), kh = lane >> 5;
+  return (uint32_t)(f16 * 2048 + h * 512 + 128 * (kh ^ (f16 & 1)) + 64 * (rd ^ h) + 16 * e +
+                    8 * (j & 1));
+}
+__host__ __device__ inline uint32_t slabt_tr_sub(int sub) {
+  return (uint32_t)((sub >> 1) * 1024 + (sub & 1) * 256);
+}
+
 inline int64_t zt_elems(const Dims& g) { return (int64_t)g.B * sb_elems<kZtSlab>(g.f, g.T_pad); }
 inline int64_t vt_elems(const Dims& g) { return (int64_t)g.B * sb_elems<kVtSlab>(g.d, g.T_pad); }
 __host__ __device__ inline int64_t snap_elems(const Dims& g) {
@@ -294,16 +352,18 @@ hipError_t launch_contract_bf16(const uint16_t* A, const uint16_t* Bm, const Dim
                                 int chunk, hipStream_t s);
 // dZ for every chunk as one contraction over K = 2d: dZ_i = [dO_i | eta V_i]
 // [W_i^T | Gbar_{i+1}^T]^T, the token-major bf16 operand [B][T][lda] holding
-// dO in columns [0, d) and eta V in [d, 2d), the chunk's bf16 state matrix
-// sb<256>(f x 2d) holding W_i^T in columns [0, d) and Gbar_{i+1}^T in
-// [d, 2d) (sequence stride sbs, chunk stride scs); the SiLU's backward in
-// the epilogue: dG = dZ U phi'(G), dU = dZ phi(G) from sa, written
-// token-major into dgu ([B][T][ld_gu]: dG then dU) and as bf16 slabs dgt, dut
-// (sb<256>(f x B T_pad), token b T_pad + t).
-hipError_t launch_act_gemm_dz(const uint16_t* dOV, int64_t lda, const uint16_t* WGT, int64_t sbs,
-                              int64_t scs, int d, int f, int chunk, int n_chunks,
-                              const uint32_t* sa, uint16_t* dgu, int64_t ld_gu, uint16_t* dgt,
-                              uint16_t* dut, const Dims& g, hipStream_t s);
+// dO in columns [0, d) and eta V in [d, 2d); the chunk's bf16 state W_i and
+// state gradient Gbar_{i+1}, sb<256>(d x f) matrices as the update's
+// snapshots, at W + b * w_sbs + i * w_scs and Gs + b * g_sbs + i * g_scs,
+// read transposed as they are (d == g.d, f == g.f, and a matrix under
+// 2 GiB); the SiLU's backward in the epilogue: dG = dZ U phi'(G), dU = dZ
+// phi(G) from sa, written token-major into dgu ([B][T][ld_gu]: dG then dU)
+// and as bf16 slabs dgt, dut (sb<256>(f x B T_pad), token b T_pad + t).
+hipError_t launch_act_gemm_dz(const uint16_t* dOV, int64_t lda, const uint16_t* W, int64_t w_sbs,
+                              int64_t w_scs, const uint16_t* Gs, int64_t g_sbs, int64_t g_scs,
+                              int d, int f, int chunk, int n_chunks, const uint32_t* sa,
+                              uint16_t* dgu, int64_t ld_gu, uint16_t* dgt, uint16_t* dut,
+                              const Dims& g, hipStream_t s);
 // dV_i = eta Z_i Gbar_{i+1}^T for every chunk, Gbar as bf16 sb<256>(d x f)
 // snapshots: token-major bf16 dv ([B][T][ld_dv]) and slabs dvt
 // (sb<256>(d x B T_pad)).
@@ -321,11 +381,6 @@ hipError_t launch_to_slab(const void* src, bool src_f32, int64_t ld_src, uint16_
 // dst[c * ld_dst + r] = bf16(src[r][c]) for a rows x cols matrix.
 hipError_t launch_transpose_bf16(const void* src, bool src_f32, uint16_t* dst, int rows,
                                  int cols, int64_t ld_dst, hipStream_t s);
-// nmat matrices sb<256>(R x C) to the columns [k0, k0 + R) of sb<256>(C x
-// dst_K) matrices, bf16.
-hipError_t launch_slab_transpose(const uint16_t* src, int64_t src_stride, uint16_t* dst,
-                                 int64_t dst_stride, int64_t dst_K, int k0, int nmat, int R,
-                                 int C, hipStream_t s);
 // dst[r][c] (row stride ld_dst) = bf16(src[r][c]) (row stride ld_src; bf16
 // or fp32) for rows x cols (cols a multiple of 8).
 hipError_t launch_rows_bf16(const void* src, bool src_f32, int64_t ld_src, uint16_t* dst,
