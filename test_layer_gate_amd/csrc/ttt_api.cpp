@@ -1208,9 +1208,12 @@ ttt_status backward_impl(const Geo& g, const void* H, const void* X0, const void
              tttk::launch_contract_bf16(HT, DUT, Dflat_fd, nullptr, true, false, 0, 0, nullptr,
                                         0, 0, dWu, false, 64, s));
   uint16_t* WGUT = at<uint16_t>(workspace, L.wgut);
-  TTT_LAUNCH("bwd_transpose_w", s, tttk::launch_transpose_bf16(Wg, g.w_f32, WGUT, f, d, L.ld_gu, s));
+  // [Wg ; Wu] transposed with the rows of Wg and Wu interleaved, as dG and dU
+  // are in dgu.
   TTT_LAUNCH("bwd_transpose_w", s,
-             tttk::launch_transpose_bf16(Wu, g.w_f32, WGUT + g.f, f, d, L.ld_gu, s));
+             tttk::launch_transpose_bf16(Wg, g.w_f32, WGUT, f, d, L.ld_gu, 2, s));
+  TTT_LAUNCH("bwd_transpose_w", s,
+             tttk::launch_transpose_bf16(Wu, g.w_f32, WGUT + 1, f, d, L.ld_gu, 2, s));
   TTT_LAUNCH("bwd_dh", s,
              tttk::launch_nt_gemm(DGU, L.ld_gu, WGUT, L.ld_gu, d, 2 * f, dH, g.d, D, s));
   return TTT_OK;

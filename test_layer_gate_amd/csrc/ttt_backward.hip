@@ -76,8 +76,8 @@ struct ActArgs {
   float scale;
   // dZ: the SiLU's derivative factors (low half phi(G), high half U phi'(G),
   // bf16) in accumulator-fragment order (sa_frag_offset), dG and dU
-  // token-major ([B][T][ld_gu]: dG in columns [0, N), dU in [N, 2N)) and as
-  // slabs sb<256>(N x B T_pad).
+  // token-major ([B][T][ld_gu]: dG of feature c in column 2c, dU in 2c + 1)
+  // and as slabs sb<256>(N x B T_pad).
   const uint32_t* sa;
   u16* dgu;
   int64_t ld_gu;
@@ -163,10 +163,10 @@ __device__ __forceinline__ void act_gemm(const ActArgs& a, const Dims& g, int ti
     // tokens are 16 bytes), then dG and dU of both tiles: the stores of a
     // tile come before the next loads, and vmcnt completes in issue order,
     // so each load batch waits for the stores ahead of it (one wait per two
-    // tiles; staging dG and dU through LDS instead took 7% longer). dG and
-    // dU go token-major with 2-byte stores through a buffer resource based
-    // at the tile's first row and sized to its rows inside the sequence
-    // (rows past it are dropped), and as slabs.
+    // tiles; staging dG and dU through LDS instead took 7% longer). Each
+    // (dG, dU) pair goes token-major as one 4-byte store through a buffer
+    // resource based at the tile's first row and sized to its rows inside
+    // the sequence (rows past it are dropped), and dG and dU as slabs.
     const int rows_ok = max(0, min(BM, g.T - t0));
     const __amdgpu_buffer_rsrc_t gu_r = __builtin_amdgcn_make_buffer_rsrc(
         a.dgu + ((int64_t)ti.b * g.T + t0) * a.ld_gu, 0, (int)(rows_ok * a.ld_gu * 2),
@@ -199,28 +199,24 @@ __device__ __forceinline__ void act_gemm(const ActArgs& a, const Dims& g, int ti
         const int col = n0 + fr.col(n);
         const bool cok = col < N;
         const int64_t kb = (int64_t)ti.b * g.T_pad + t0 + fr.wm * L::TM * 32 + m * 32;
+        f32x16 vg, vu;
 #pragma unroll
-        for (int part = 0; part < 2; ++part) {  // dG, then dU
-          f32x16 v;
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w[4] = {w4[k][q].x, w4[k][q].y, w4[k][q].z, w4[k][q].w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t w[4] = {w4[k][q].x, w4[k][q].y, w4[k][q].z, w4[k][q].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float fac = part == 0 ? __uint_as_float(w[e] & 0xffff0000u)  // U phi'(G)
-                                          : __uint_as_float(w[e] << 16);         // phi(G)
-              v[4 * q + e] = acc[m][n][4 * q + e] * fac;
-            }
+          for (int e = 0; e < 4; ++e) {
+            vg[4 * q + e] = acc[m][n][4 * q + e] * __uint_as_float(w[e] & 0xffff0000u);  // U phi'(G)
+            vu[4 * q + e] = acc[m][n][4 * q + e] * __uint_as_float(w[e] << 16);          // phi(G)
           }
-          store_tile_sb<256>(kt, col, kb, v, CvtBf16{1.0f}, cok,
-                             PlainSink{part == 0 ? a.dgt : a.dut});
+        }
+        store_tile_sb<256>(kt, col, kb, vg, CvtBf16{1.0f}, cok, PlainSink{a.dgt});
+        store_tile_sb<256>(kt, col, kb, vu, CvtBf16{1.0f}, cok, PlainSink{a.dut});
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tr = fr.row(m, r / 4) + r % 4;  // row within the tile
-            __builtin_amdgcn_raw_buffer_store_b16(
-                bf16_rne(v[r]), gu_r,
-                cok ? (int)((tr * a.ld_gu + part * N + col) * 2) : drop_gu, 0, 0);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int tr = fr.row(m, r / 4) + r % 4;  // row within the tile
+          __builtin_amdgcn_raw_buffer_store_b32(
+              pack_bf16(vg[r], vu[r]), gu_r, cok ? (int)((tr * a.ld_gu + 2 * col) * 2) : drop_gu,
+              0, 0);
         }
       }
     });
@@ -344,13 +340,13 @@ __global__ __launch_bounds__(kBwThreads) void to_slab_kernel(const void* __restr
                    pack_bf16(v[4][e], v[5][e]), pack_bf16(v[6][e], v[7][e]));
 }
 
-// dst[c * ld_dst + r] = bf16(src[r][c]) for a rows x cols matrix (bf16 or
-// fp32).
+// dst[c * ld_dst + r * step] = bf16(src[r][c]) for a rows x cols matrix
+// (bf16 or fp32).
 template <bool F32>
 __global__ __launch_bounds__(kBwThreads) void transpose_bf16_kernel(const void* __restrict__ src,
                                                                     u16* __restrict__ dst,
                                                                     int rows, int cols,
-                                                                    int64_t ld_dst) {
+                                                                    int64_t ld_dst, int step) {
   __shared__ float tile[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -365,7 +361,7 @@ __global__ __launch_bounds__(kBwThreads) void transpose_bf16_kernel(const void* 
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) dst[(int64_t)c * ld_dst + r] = bf16_rne(tile[tx][i]);
+    if (c < cols && r < rows) dst[(int64_t)c * ld_dst + (int64_t)r * step] = bf16_rne(tile[tx][i]);
   }
 }
 
@@ -647,12 +643,12 @@ hipError_t launch_to_slab(const void* src, bool src_f32, int64_t ld_src, uint16_
 }
 
 hipError_t launch_transpose_bf16(const void* src, bool src_f32, uint16_t* dst, int rows,
-                                 int cols, int64_t ld_dst, hipStream_t s) {
+                                 int cols, int64_t ld_dst, int step, hipStream_t s) {
   dim3 grid((cols + 63) / 64, (rows + 63) / 64);
   if (src_f32)
-    transpose_bf16_kernel<true><<<grid, kBwThreads, 0, s>>>(src, dst, rows, cols, ld_dst);
+    transpose_bf16_kernel<true><<<grid, kBwThreads, 0, s>>>(src, dst, rows, cols, ld_dst, step);
   else
-    transpose_bf16_kernel<false><<<grid, kBwThreads, 0, s>>>(src, dst, rows, cols, ld_dst);
+    transpose_bf16_kernel<false><<<grid, kBwThreads, 0, s>>>(src, dst, rows, cols, ld_dst, step);
   return hipGetLastError();
 }
 

@@ -357,8 +357,9 @@ hipError_t launch_contract_bf16(const uint16_t* A, const uint16_t* Bm, const Dim
 // snapshots, at W + b * w_sbs + i * w_scs and Gs + b * g_sbs + i * g_scs,
 // read transposed as they are (d == g.d, f == g.f, and a matrix under
 // 2 GiB); the SiLU's backward in the epilogue: dG = dZ U phi'(G), dU = dZ
-// phi(G) from sa, written token-major into dgu ([B][T][ld_gu]: dG then dU)
-// and as bf16 slabs dgt, dut (sb<256>(f x B T_pad), token b T_pad + t).
+// phi(G) from sa, written token-major into dgu ([B][T][ld_gu]: dG of feature
+// c in column 2c, dU in 2c + 1) and as bf16 slabs dgt, dut (sb<256>(f x
+// B T_pad), token b T_pad + t).
 hipError_t launch_act_gemm_dz(const uint16_t* dOV, int64_t lda, const uint16_t* W, int64_t w_sbs,
                               int64_t w_scs, const uint16_t* Gs, int64_t g_sbs, int64_t g_scs,
                               int d, int f, int chunk, int n_chunks, const uint32_t* sa,
@@ -378,9 +379,9 @@ hipError_t launch_nt_gemm(const uint16_t* A, int64_t lda, const uint16_t* Bm, in
 // sb<256>(D x T_pad) per sequence, or with flat sb<256>(D x B T_pad).
 hipError_t launch_to_slab(const void* src, bool src_f32, int64_t ld_src, uint16_t* dst, int B,
                           int T, int T_pad, int D, bool flat, hipStream_t s);
-// dst[c * ld_dst + r] = bf16(src[r][c]) for a rows x cols matrix.
+// dst[c * ld_dst + r * step] = bf16(src[r][c]) for a rows x cols matrix.
 hipError_t launch_transpose_bf16(const void* src, bool src_f32, uint16_t* dst, int rows,
-                                 int cols, int64_t ld_dst, hipStream_t s);
+                                 int cols, int64_t ld_dst, int step, hipStream_t s);
 // dst[r][c] (row stride ld_dst) = bf16(src[r][c]) (row stride ld_src; bf16
 // or fp32) for rows x cols (cols a multiple of 8).
 hipError_t launch_rows_bf16(const void* src, bool src_f32, int64_t ld_src, uint16_t* dst,
