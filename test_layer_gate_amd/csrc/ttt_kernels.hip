@@ -552,24 +552,49 @@ struct SnapshotStore {
   int kdim;  // columns of the snapshot matrix (>= f; the state fills columns [0, f))
   float out_scale;
   uint32_t bytes;
+  // Where the accumulator tiles go. The tile's d_ff start j0 is a multiple
+  // of 256 and its d_model start c0 one of 128, and a wave's blocks stay
+  // inside one 256-row slab row (c) and start at a multiple of 64 columns
+  // (j), so every store of the wave lands at this lane's byte offset for
+  // tile (0, 0) plus a constant: tile (m, n) half p of sb<256> element
+  // (c, jb + 16 p + 8 h) is (m / 2) slabs (32 KB), (m % 2) column groups of
+  // 32 (2 KB), n 32-row blocks (4 KB) and p 16-column halves (1 KB) further
+  // on. The base is computed once per call instead of per tile.
   __device__ __forceinline__ void operator()(u16* dst, const f32x16* acc) const {
+    static_assert(L::WGN * L::TN * 32 <= 128 || L::WGN * L::TN * 32 == 256,
+                  "a wave's columns stay in one slab row");
     const Frag<L> fr(OPQ);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(dst, 0, (int)bytes, kRsrcWord3);
-    const uint32_t drop = bytes;
-    auto sink = [&](int64_t off, const uint4& v, bool ok) {
-      const u32x4 w = {v.x, v.y, v.z, v.w};
-      __builtin_amdgcn_raw_buffer_store_b128(w, rsrc, ok ? (int)(off * 2) : (int)drop, 0,
-                                             kCpolNt | kCpolSc1);
-    };
+    const uint32_t lane = (uint32_t)fr.lane;
+    const uint32_t jw = (uint32_t)(j0 + fr.wm * L::TM * 32);  // multiple of 64
+    const uint32_t cw = (uint32_t)(c0 + fr.wn * L::TN * 32);
+    const uint32_t base =
+        2u * ((((cw >> 8) * ((uint32_t)kdim >> 6) + (jw >> 6)) << 14) +
+              (((cw & 255u) >> 5) << 11) + ((((lane >> 5) & 1u) << 5) + (lane & 31u)) * 8u);
+    const CvtBf16 cvt{out_scale};
 #pragma unroll
     for (int m = 0; m < L::TM; ++m)
 #pragma unroll
       for (int n = 0; n < L::TN; ++n) {
-        const int jb = j0 + fr.wm * L::TM * 32 + m * 32;  // first d_ff index of the tile
-        const int c = c0 + fr.col(n);
-        store_tile_sb<kSnapSlab>(kdim, c, jb, acc[m * L::TN + n], CvtBf16{out_scale},
-                                 c < d && jb < f, sink);
+        const bool ok = cw + (uint32_t)(n * 32) + (lane & 31u) < (uint32_t)d &&
+                        jw + (uint32_t)(m * 32) < (uint32_t)f;
+        const uint32_t off =
+            ok ? base + (uint32_t)((m >> 1) * 32768 + (m & 1) * 2048 + n * 4096) : bytes;
+        const f32x16& a = acc[m * L::TN + n];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          // The two 16-byte pieces of store_tile_sb, lanes l and l ^ 32
+          // trading halves with v_permlane32_swap.
+          const uint32_t lo0 = cvt(a[8 * p + 0], a[8 * p + 1]), lo1 = cvt(a[8 * p + 2], a[8 * p + 3]);
+          const uint32_t hi0 = cvt(a[8 * p + 4], a[8 * p + 5]), hi1 = cvt(a[8 * p + 6], a[8 * p + 7]);
+          const auto x0 = __builtin_amdgcn_permlane32_swap(lo0, hi0, false, false);
+          const auto x1 = __builtin_amdgcn_permlane32_swap(lo1, hi1, false, false);
+          const u32x4 w = {x0[0], x1[0], x0[1], x1[1]};
+          // A dropped lane stores at `bytes` or 1 KB past it: out of bounds.
+          __builtin_amdgcn_raw_buffer_store_b128(w, rsrc, (int)(off + p * 1024u), 0,
+                                                 kCpolNt | kCpolSc1);
+        }
       }
   }
 };
