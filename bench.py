@@ -59,6 +59,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CALIB_BYTES = 256 << 20      # the known-size copy run before the timed region
 # library timing names -> kernel names in rocprofv3 traces
 KERNEL_NAMES = {"gate_up": "gate_up_kernel", "target": "target_kernel",
+                "gate_up_target": "gate_up_target_kernel",
                 "update_prefix": "update_kernel", "update_running": "update_kernel",
                 "apply": "apply_kernel", "conv": "conv_kernel",
                 "transpose_w_target": "transpose_kernel", "cast_bf16": "cast_kernel",
@@ -106,6 +107,8 @@ def kernel_work(name, cfg, T_pad):
         return "mfma", 4.0 * B * T * d * f
     if name == "target":
         return "mfma", 2.0 * B * T * d * d
+    if name == "gate_up_target":  # both in one launch, where that saves a round
+        return "mfma", 4.0 * B * T * d * f + 2.0 * B * T * d * d
     if name in ("update_prefix", "update_running", "apply"):
         return "mfma", 2.0 * B * T * d * f
     if name in ("bwd_gate_up", "bwd_dz", "bwd_dw_gate_up", "bwd_dh"):

@@ -542,16 +542,26 @@ ttt_status forward_impl(const Geo& g, const void* H, const void* X0, const void*
              tttk::launch_conv_repair(X0b, X0nb, n_next, conv_taps, g.w_f32, Y, D, (int)g.K,
                                       (int)g.C, g.pad_chunk, blocks, range_y, s));
   uint32_t* range_z = range + tttk::kRangeZ * tttk::kRangeSlots;
-  if (g.train)
-    TTT_LAUNCH("gate_up", s,
-               tttk::launch_gate_up_train(Hb, Wgp, Wup, Z, ZT, at<uint16_t>(workspace, L.ztb),
-                                          at<uint32_t>(workspace, L.sa), D, range_z, s));
-  else
-    TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, range_z, s));
-  TTT_LAUNCH("gate_up_repair", s, tttk::launch_gate_up_repair(Hb, Wgp, Wup, ZT, D, range_z, s));
   const bool clip = g.clip > 0.0f && eta != 0.0f;
   uint16_t* Vrow = clip ? at<uint16_t>(workspace, L.vrow) : nullptr;
-  TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, Vrow, vscale, D, range, s));
+  if (!g.train && tttk::gate_up_target_merges(D)) {
+    // Both part-empty last rounds in one: the target's tiles run in gate/up's.
+    TTT_LAUNCH("gate_up_target", s,
+               tttk::launch_gate_up_target(Hb, Wgp, Wup, Z, ZT, Y, WtT, VT, Vrow, vscale, D,
+                                           range, s));
+    TTT_LAUNCH("gate_up_repair", s,
+               tttk::launch_gate_up_repair(Hb, Wgp, Wup, ZT, D, range_z, s));
+  } else {
+    if (g.train)
+      TTT_LAUNCH("gate_up", s,
+                 tttk::launch_gate_up_train(Hb, Wgp, Wup, Z, ZT, at<uint16_t>(workspace, L.ztb),
+                                            at<uint32_t>(workspace, L.sa), D, range_z, s));
+    else
+      TTT_LAUNCH("gate_up", s, tttk::launch_gate_up(Hb, Wgp, Wup, Z, ZT, D, range_z, s));
+    TTT_LAUNCH("gate_up_repair", s,
+               tttk::launch_gate_up_repair(Hb, Wgp, Wup, ZT, D, range_z, s));
+    TTT_LAUNCH("target", s, tttk::launch_target(Y, WtT, VT, nullptr, Vrow, vscale, D, range, s));
+  }
   TTT_LAUNCH("target_repair", s,
              tttk::launch_target_repair(Y, WtT, VT, Vrow, vscale, p, D, range, s));
   if (clip) {

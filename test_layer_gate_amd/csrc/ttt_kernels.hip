@@ -303,6 +303,44 @@ __global__ __launch_bounds__(64 * K2_NW) void target_kernel(
   if (range != nullptr && note_v) range_note(range + kRangeV * kRangeSlots, m);
 }
 
+// gate/up and the target in one launch: workgroups [0, n_gu) take gate/up
+// tiles (as gate_up_kernel), the rest target tiles (as target_kernel, with
+// its V^T written and V's range noted). Both configurations hold 160 KB of
+// LDS and 8 waves. Used when the two launches' last rounds are part-empty
+// and the target's tiles fit into gate/up's last round, so the pair takes
+// one round fewer (the Qwen3-4B shape at 8k tokens: 2432 + 320 tiles, 11
+// rounds of 256 instead of 10 + 2). n_gu is gate/up's tile count rounded up
+// to a multiple of 8, so the XCD of a target workgroup is that of its
+// position in the target range; the gate/up workgroups whose renumbered
+// position is past the last tile return at once.
+__global__ __launch_bounds__(64 * K1_NW) void gate_up_target_kernel(
+    const u16* __restrict__ H, const u16* __restrict__ Wgp, const u16* __restrict__ Wup,
+    u16* __restrict__ Z, u16* __restrict__ ZT, int gu_tiles_m, int gu_tiles_n, int n_gu,
+    const u16* __restrict__ Y, const u16* __restrict__ WtT, u16* __restrict__ VT,
+    u16* __restrict__ Vrow, float vscale, int t_tiles_m, int t_tiles_n, Dims g,
+    uint32_t* __restrict__ range) {
+  static_assert((K1_NSTA * K1_BM + K1_NSTB * K1_BN) * K1_BK ==
+                    (K2_NSTA * K2_BM + K2_NSTB * K2_BN) * K2_BK && K1_NW == K2_NW,
+                "one LDS array and workgroup size for both tiles");
+  TTT_GEMM_LDS_AB(lds, K1_BM, K1_BN, K1_BK, K1_NSTA, K1_NSTB)
+  const int id = blockIdx.x;
+  if (id < n_gu) {
+    // The renumbering is a permutation of [0, n_gu): the positions past the
+    // last tile are the padding (not the ids past it).
+    const int lin = xcd_contiguous(id, n_gu);
+    if (lin >= gu_tiles_m * gu_tiles_n * g.B) return;
+    const float m = gate_up_tile(tile_coords(lin, gu_tiles_m, gu_tiles_n, 4), lds, H, Wgp, Wup,
+                                 Z, ZT, g, 1.0f);
+    range_note(range + kRangeZ * kRangeSlots, m);
+    return;
+  }
+  const float sc = vscale * exp2i(-target_in_exp(range));
+  const TileIdx t =
+      tile_coords(xcd_contiguous(id - n_gu, (int)gridDim.x - n_gu), t_tiles_m, t_tiles_n, 4);
+  const float m = target_tile(t, lds, Y, WtT, VT, nullptr, Vrow, sc, g);
+  range_note(range + kRangeV * kRangeSlots, m);
+}
+
 // The backward's recompute of the target: eta * V as bf16 slabs (VT) and
 // token-major bf16 (Vtok, row stride vtok_ld), the inputs' range exponents
 // divided out.
@@ -1336,6 +1374,29 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
   const int tiles_m = g.T_pad / K2_BM, tiles_n = ceil_div(g.d, K2_BN);
   target_kernel<<<tiles_m * tiles_n * g.B, 64 * K2_NW, 0, s>>>(
       Y, WtT, VT, Vtok, Vrow, vscale, g, tiles_m, tiles_n, range, VT != nullptr ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Rounds of `tiles` workgroups on `cus` compute units.
+static int rounds_of(int64_t tiles, int cus) { return (int)((tiles + cus - 1) / cus); }
+
+bool gate_up_target_merges(const Dims& g) {
+  const int cus = repair_grid();
+  const int64_t gu = (int64_t)(g.T_pad / K1_BM) * ceil_div(g.f, K1_BN / 2) * g.B;
+  const int64_t tg = (int64_t)(g.T_pad / K2_BM) * ceil_div(g.d, K2_BN) * g.B;
+  const int64_t gu8 = (gu + 7) / 8 * 8;
+  return rounds_of(gu8 + tg, cus) < rounds_of(gu, cus) + rounds_of(tg, cus);
+}
+
+hipError_t launch_gate_up_target(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
+                                 uint16_t* Z, uint16_t* ZT, const uint16_t* Y,
+                                 const uint16_t* WtT, uint16_t* VT, uint16_t* Vrow,
+                                 float vscale, const Dims& g, uint32_t* range, hipStream_t s) {
+  const int gtm = g.T_pad / K1_BM, gtn = ceil_div(g.f, K1_BN / 2);
+  const int ttm = g.T_pad / K2_BM, ttn = ceil_div(g.d, K2_BN);
+  const int n_gu = (gtm * gtn * g.B + 7) / 8 * 8;
+  gate_up_target_kernel<<<n_gu + ttm * ttn * g.B, 64 * K1_NW, 0, s>>>(
+      H, Wgp, Wup, Z, ZT, gtm, gtn, n_gu, Y, WtT, VT, Vrow, vscale, ttm, ttn, g, range);
   return hipGetLastError();
 }
 

@@ -243,6 +243,16 @@ hipError_t launch_target_repair(const uint16_t* Y, const uint16_t* WtT, uint16_t
                                 uint16_t* Vrow, float vscale, int p, const Dims& g,
                                 const uint32_t* range, hipStream_t s);
 
+// launch_gate_up (Z, ZT, range noted) and launch_target (VT, Vrow, range
+// noted) as one launch, gate/up's tiles first; worth it only when
+// gate_up_target_merges(g): the two launches' part-empty last rounds then
+// share one round (each repair launch still follows).
+bool gate_up_target_merges(const Dims& g);
+hipError_t launch_gate_up_target(const uint16_t* H, const uint16_t* Wgp, const uint16_t* Wup,
+                                 uint16_t* Z, uint16_t* ZT, const uint16_t* Y,
+                                 const uint16_t* WtT, uint16_t* VT, uint16_t* Vrow,
+                                 float vscale, const Dims& g, uint32_t* range, hipStream_t s);
+
 // Update-norm clipping: per chunk i, scale[b][i] = min(1, clip /
 // (norm_factor * ||Vrow_i^T Z_i||_F)) from the Gram form (gram: B * nchunks
 // * clip_gram_floats(chunk) floats of V Gram tiles; partial: B * nchunks *

@@ -35,6 +35,10 @@ def test_layer_flops_match_the_method():
         total += work
     assert total == 2.0 * B * T * (4 * d * f + d * d)
     assert abs(total / 1e12 - 13.92) < 0.01
+    # gate/up and the target in one launch count as both
+    merged = bench.kernel_work("gate_up_target", cfg, T)
+    assert merged == ("mfma", bench.kernel_work("gate_up", cfg, T)[1] +
+                      bench.kernel_work("target", cfg, T)[1])
 
 
 def test_traffic_record_is_tied_to_the_source(tmp_path, monkeypatch):
