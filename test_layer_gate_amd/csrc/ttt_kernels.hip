@@ -915,40 +915,34 @@ __global__ __launch_bounds__(64 * K3_NW) void update_kernel(
 // (with 256-token tiles) share one chunk's snapshot slabs.
 constexpr int kApplyGroupM = 8;
 
-template <int BN>
+template <int BN, bool TAIL = false>
 struct ApplyCfg {
   static constexpr int NW = 8;
   static constexpr int WGM =
       BN == 256 ? 2 : (BN == 128 ? 4 : 8);
   // With 256-token tiles, Z's stages run one step deeper than the
-  // snapshot's (160 KB of LDS): 10% faster. Narrower tiles keep two each.
-  static constexpr int BK = 64, NSTA = 2, NSTB = BN == 256 ? 3 : 2;
+  // snapshot's (160 KB of LDS): 10% faster. Narrower tiles keep two each,
+  // but for the 128-token halves of a whole-sequence launch's last round
+  // (TAIL), which have the launch's 160 KB: three snapshot stages and four
+  // of Z take that round at the 8k Qwen3-4B shape from 0.22 to 0.16 ms (two
+  // of each: the halves were bound by the load latency of every K step).
+  static constexpr int BK = 64, NSTA = TAIL ? 3 : 2, NSTB = TAIL ? 4 : (BN == 256 ? 3 : 2);
 };
 
-template <int BN, bool OUT_F32>
-__global__ __launch_bounds__(64 * ApplyCfg<BN>::NW) void apply_kernel(
-    const u16* __restrict__ Z, const u16* __restrict__ snap, int64_t snap_bstride,
-    int64_t snap_cstride, void* __restrict__ O, Dims g, int tok_begin, int tok_end, int chunk,
-    const ApplyTile* __restrict__ tiles, int n_chunks, int tiles_m, int tiles_n) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int BM = kSnapSlab, WGM = ApplyCfg<BN>::WGM, BK = ApplyCfg<BN>::BK,
-                NSTA = ApplyCfg<BN>::NSTA, NSTB = ApplyCfg<BN>::NSTB;
+// One apply tile: d_model rows [256 ti.tm, 256 ti.tm + 256) of sequence
+// ti.b for the tokens [t0, t1) (at most BN, all in chunk i), from snapshot i.
+template <int BN, bool OUT_F32, bool TAIL = false>
+__device__ __forceinline__ void apply_tile(u16* lds, const TileIdx& ti, int t0, int t1, int i,
+                                           const u16* __restrict__ Z,
+                                           const u16* __restrict__ snap, int64_t snap_bstride,
+                                           int64_t snap_cstride, void* __restrict__ O,
+                                           const Dims& g) {
+  using Cfg = ApplyCfg<BN, TAIL>;
+  constexpr int BM = kSnapSlab, WGM = Cfg::WGM, BK = Cfg::BK, NSTA = Cfg::NSTA,
+                NSTB = Cfg::NSTB;
   static_assert(BK == 64, "the snapshot slab is one K step");
-  using L = Layout<BM, BN, WGM, ApplyCfg<BN>::NW>;
-  TTT_GEMM_LDS_AB(lds, BM, BN, BK, NSTA, NSTB)
-  const TileIdx ti = tile_index(tiles_m, tiles_n, kApplyGroupM);
+  using L = Layout<BM, BN, WGM, Cfg::NW>;
   const int c0 = ti.tm * BM;
-  int t0, t1, i;
-  if (tiles != nullptr) {
-    const ApplyTile tl = tiles[ti.tn];
-    t0 = min(max(tl.t0, 0), g.T);
-    t1 = min(max(tl.t1, t0), g.T);
-    i = min(max(tl.chunk, 0), n_chunks - 1);
-  } else {
-    t0 = tok_begin + ti.tn * BN;
-    t1 = min(tok_end, t0 + BN);
-    i = t0 / chunk;
-  }
   const int d = g.d, f = g.f, T = g.T;
   f32x16 acc[L::TM][L::TN];
   zero_acc(acc);
@@ -958,7 +952,7 @@ __global__ __launch_bounds__(64 * ApplyCfg<BN>::NW) void apply_kernel(
   // width, so that every schedule and width sums each output in the same
   // order.
   const int nk = f / BK;
-  gemm_core_ab<ApplyCfg<BN>::NW, BM, BN, WGM, BK, NSTA, NSTB, Bf16Mma, false, kSlab, kRowMajor>(
+  gemm_core_ab<Cfg::NW, BM, BN, WGM, BK, NSTA, NSTB, Bf16Mma, false, kSlab, kRowMajor>(
       slab_blocked<kSnapSlab>(snap + ti.b * snap_bstride + i * snap_cstride, f, c0, 0), z, z, nk,
       &acc[0][0], lds, NoHook{}, k_rotation<kApplyGroupM>(ti.tm, t0 / 256, nk));
   const Frag<L> fr;
@@ -982,6 +976,66 @@ __global__ __launch_bounds__(64 * ApplyCfg<BN>::NW) void apply_kernel(
                          pack_bf16(acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]));
         }
       }
+}
+
+template <int BN, bool OUT_F32>
+__global__ __launch_bounds__(64 * ApplyCfg<BN>::NW) void apply_kernel(
+    const u16* __restrict__ Z, const u16* __restrict__ snap, int64_t snap_bstride,
+    int64_t snap_cstride, void* __restrict__ O, Dims g, int tok_begin, int tok_end, int chunk,
+    const ApplyTile* __restrict__ tiles, int n_chunks, int tiles_m, int tiles_n) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  TTT_GEMM_LDS_AB(lds, kSnapSlab, BN, ApplyCfg<BN>::BK, ApplyCfg<BN>::NSTA, ApplyCfg<BN>::NSTB)
+  const TileIdx ti = tile_index(tiles_m, tiles_n, kApplyGroupM);
+  int t0, t1, i;
+  if (tiles != nullptr) {
+    const ApplyTile tl = tiles[ti.tn];
+    t0 = min(max(tl.t0, 0), g.T);
+    t1 = min(max(tl.t1, t0), g.T);
+    i = min(max(tl.chunk, 0), n_chunks - 1);
+  } else {
+    t0 = tok_begin + ti.tn * BN;
+    t1 = min(tok_end, t0 + BN);
+    i = t0 / chunk;
+  }
+  apply_tile<BN, OUT_F32>(lds, ti, t0, t1, i, Z, snap, snap_bstride, snap_cstride, O, g);
+#endif
+}
+
+// The whole sequence's apply ([0, T), chunks a multiple of 256 tokens) when
+// its 256-token tiles leave a last round at most half full: workgroups
+// [0, n_wide) take whole rounds of 256-token tiles, the rest the two
+// 128-token halves of each tile left over (tile_coords order, as
+// apply_kernel). A half sums every output in the same order as the whole
+// tile would, so the results are the same bit for bit.
+template <bool OUT_F32>
+__global__ __launch_bounds__(64 * ApplyCfg<256>::NW) void apply_mixed_kernel(
+    const u16* __restrict__ Z, const u16* __restrict__ snap, int64_t snap_bstride,
+    int64_t snap_cstride, void* __restrict__ O, Dims g, int chunk, int tiles_m, int tiles_n,
+    int n_wide) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using Tail = ApplyCfg<128, true>;
+  static_assert(ApplyCfg<256>::NW == Tail::NW, "one workgroup size");
+  static_assert((Tail::NSTA * kSnapSlab + Tail::NSTB * 128) <=
+                    (ApplyCfg<256>::NSTA * kSnapSlab + ApplyCfg<256>::NSTB * 256),
+                "the narrow tile's stages fit the wide tile's LDS");
+  TTT_GEMM_LDS_AB(lds, kSnapSlab, 256, ApplyCfg<256>::BK, ApplyCfg<256>::NSTA,
+                  ApplyCfg<256>::NSTB)
+  if ((int)blockIdx.x < n_wide) {
+    const TileIdx ti =
+        tile_coords(xcd_contiguous(blockIdx.x, n_wide), tiles_m, tiles_n, kApplyGroupM);
+    const int t0 = ti.tn * 256;
+    apply_tile<256, OUT_F32>(lds, ti, t0, min(g.T, t0 + 256), t0 / chunk, Z, snap, snap_bstride,
+                             snap_cstride, O, g);
+    return;
+  }
+  // n_wide is a multiple of 8, so the XCD of a workgroup is that of its
+  // position in the narrow range.
+  const int id = xcd_contiguous(blockIdx.x - n_wide, (int)gridDim.x - n_wide);
+  const TileIdx ti = tile_coords(n_wide + id / 2, tiles_m, tiles_n, kApplyGroupM);
+  const int t0 = ti.tn * 256 + (id & 1) * 128;
+  if (t0 >= g.T) return;  // uniform: the half of a tile past the sequence
+  apply_tile<128, OUT_F32, true>(lds, ti, t0, min(g.T, t0 + 128), t0 / chunk, Z, snap,
+                                 snap_bstride, snap_cstride, O, g);
 #endif
 }
 
@@ -1562,6 +1616,25 @@ hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bs
   // leave compute units idle, as the running schedule's one-chunk launches
   // do.
   int width = apply_tile_width(chunk);
+  if (tiles == nullptr && tok_begin == 0 && tok_end == g.T && width == 256) {
+    // The whole sequence: whole rounds of 256-token tiles, and the tiles
+    // left over as 128-token halves when they fill at most half a round
+    // (as the update's wide and narrow tiles).
+    const int cus = repair_grid() & ~7;
+    const int tiles_m = ceil_div(g.d, 256), tiles_n = ceil_div(g.T, 256);
+    const int n = tiles_m * tiles_n * g.B;
+    const int rem = cus > 0 ? n % cus : 0;
+    if (rem != 0 && 2 * rem <= cus && n > rem) {
+      const int n_wide = n - rem, grid = n_wide + 2 * rem;
+      if (out_f32)
+        apply_mixed_kernel<true><<<grid, 64 * ApplyCfg<256>::NW, 0, s>>>(
+            Z, snap, snap_bstride, snap_cstride, O, g, chunk, tiles_m, tiles_n, n_wide);
+      else
+        apply_mixed_kernel<false><<<grid, 64 * ApplyCfg<256>::NW, 0, s>>>(
+            Z, snap, snap_bstride, snap_cstride, O, g, chunk, tiles_m, tiles_n, n_wide);
+      return hipGetLastError();
+    }
+  }
   if (tiles == nullptr)
     while (width > 64 &&
            (int64_t)g.B * ceil_div(g.d, 256) * ceil_div(tok_end - tok_begin, width) < 256)

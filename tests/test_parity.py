@@ -230,6 +230,24 @@ def test_schedules_agree_bitwise(ttt):
     assert np.array_equal(Op, Or) and np.array_equal(Wp, Wr)
 
 
+def test_apply_split_last_round(ttt):
+    """A whole-sequence apply whose 256-token tiles leave a last round at
+    most half full runs whole rounds of them and splits the tiles left over
+    into 128-token halves (B = 2, T = 6912, d_model = 1280: 270 tiles, 14
+    of them split, on 256 compute units). The halves sum every output in
+    the same order as whole tiles: the prefix schedule (which splits) and
+    the running one (one chunk per launch, narrower tiles) agree bit for
+    bit, and both match the oracle."""
+    cfg = synth.CONFIGS["mid_amp"].with_(name="apply_split", batch=2, seq_len=6912, chunk=256,
+                                         d_model=1280, d_ff=512)
+    x = synth.make_inputs(cfg, seed=29)
+    t = to_dev(x, cfg.dtype)
+    Op, Wp = run_gpu(ttt, t, cfg.eta, cfg.chunk, schedule="prefix")
+    Or, Wr = run_gpu(ttt, t, cfg.eta, cfg.chunk, schedule="running")
+    assert np.array_equal(Op, Or) and np.array_equal(Wp, Wr)
+    check_full(x, Op, Wp, cfg.eta, cfg.chunk)
+
+
 @pytest.mark.timeout(600)
 def test_schedules_agree_bitwise_full_size(ttt):
     """The same at the Qwen3-4B 64k shape, where the running schedule's
