@@ -1349,7 +1349,9 @@ hipError_t launch_conv(const uint16_t* X0, const uint16_t* X0_next, int n_next,
   return hipGetLastError();
 }
 
-int repair_grid() {
+// Compute units of the current device (256 if the query fails): the size of
+// the persistent repair grids and of a launch's rounds of tiles.
+int device_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -1363,7 +1365,7 @@ hipError_t launch_conv_repair(const uint16_t* X0, const uint16_t* X0_next, int n
                               int chunk, bool pad_chunk, const BlockInfo* blocks,
                               const uint32_t* range, hipStream_t s) {
   const int64_t total = (int64_t)g.B * (g.T_pad / kConvRows) * (g.d / 8);
-  const int grid = std::min<int64_t>(ceil_div(total, kThreads), 4 * repair_grid());
+  const int grid = std::min<int64_t>(ceil_div(total, kThreads), 4 * device_cus());
   if (n_next == 0) X0_next = X0;  // never read
   if (taps_f32)
     conv_repair_kernel<true><<<grid, kThreads, 0, s>>>(X0, X0_next, n_next, taps, Y, g, K, chunk,
@@ -1417,7 +1419,7 @@ hipError_t launch_gate_up_repair(const uint16_t* H, const uint16_t* Wgp, const u
                                  uint16_t* ZT, const Dims& g, const uint32_t* range,
                                  hipStream_t s) {
   const int tiles_m = g.T_pad / K1_BM, tiles_n = ceil_div(g.f, K1_BN / 2);
-  const int grid = std::min(tiles_m * tiles_n * g.B, repair_grid());
+  const int grid = std::min(tiles_m * tiles_n * g.B, device_cus());
   gate_up_repair_kernel<<<grid, 64 * K1_NW, 0, s>>>(H, Wgp, Wup, ZT, g, tiles_m, tiles_n, range);
   return hipGetLastError();
 }
@@ -1435,7 +1437,7 @@ hipError_t launch_target(const uint16_t* Y, const uint16_t* WtT, uint16_t* VT, u
 static int rounds_of(int64_t tiles, int cus) { return (int)((tiles + cus - 1) / cus); }
 
 bool gate_up_target_merges(const Dims& g) {
-  const int cus = repair_grid();
+  const int cus = device_cus();
   const int64_t gu = (int64_t)(g.T_pad / K1_BM) * ceil_div(g.f, K1_BN / 2) * g.B;
   const int64_t tg = (int64_t)(g.T_pad / K2_BM) * ceil_div(g.d, K2_BN) * g.B;
   const int64_t gu8 = (gu + 7) / 8 * 8;
@@ -1467,7 +1469,7 @@ hipError_t launch_target_repair(const uint16_t* Y, const uint16_t* WtT, uint16_t
                                 uint16_t* Vrow, float vscale, int p, const Dims& g,
                                 const uint32_t* range, hipStream_t s) {
   const int tiles_m = g.T_pad / K2_BM, tiles_n = ceil_div(g.d, K2_BN);
-  const int grid = std::min(tiles_m * tiles_n * g.B, repair_grid());
+  const int grid = std::min(tiles_m * tiles_n * g.B, device_cus());
   target_repair_kernel<<<grid, 64 * K2_NW, 0, s>>>(Y, WtT, VT, Vrow, vscale, p, g, tiles_m,
                                                    tiles_n, range);
   return hipGetLastError();
@@ -1620,7 +1622,7 @@ hipError_t launch_apply(const uint16_t* Z, const uint16_t* snap, int64_t snap_bs
     // The whole sequence: whole rounds of 256-token tiles, and the tiles
     // left over as 128-token halves when they fill at most half a round
     // (as the update's wide and narrow tiles).
-    const int cus = repair_grid() & ~7;
+    const int cus = device_cus() & ~7;
     const int tiles_m = ceil_div(g.d, 256), tiles_n = ceil_div(g.T, 256);
     const int n = tiles_m * tiles_n * g.B;
     const int rem = cus > 0 ? n % cus : 0;
